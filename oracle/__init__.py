@@ -1,0 +1,201 @@
+"""CPU oracle of the uzip v1 bitstream -- test infrastructure only.
+
+Only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product path (the HIP library and
+its binding) never does; the two implementations share no code and meet only
+through the bytes they produce.
+
+The arithmetic lives in ``uzip_oracle.c`` (plain single-threaded C, one step
+of the method per function, each citing the page passage it follows).  This
+module only marshals numpy arrays to it through ctypes.  Every function here
+is pinned by the ``-m "not gpu"`` tests in ``tests/test_oracle_*.py``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "uzip_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+BF16 = 1
+FP32 = 2
+OK, INVALID, CAPACITY, CORRUPT = 0, 1, 2, 3
+
+LANES = 32
+M = 4096
+L = 65536
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc -O2 (no hand vectorisation).
+
+    UZIP_ORACLE_LIB may name another build of this same source (used to run
+    the pins against deliberately broken copies when checking the tests)."""
+    if os.environ.get("UZIP_ORACLE_LIB"):
+        return os.environ["UZIP_ORACLE_LIB"]
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-Wall", "-shared", "-fPIC", "-o", tmp, _SRC])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        _lib = ctypes.CDLL(build())
+        u64, i32, vp = ctypes.c_uint64, ctypes.c_int, ctypes.c_void_p
+        _lib.orc_chunk_elems.restype = u64
+        _lib.orc_chunk_elems.argtypes = [i32, u64]
+        _lib.orc_split.restype = None
+        _lib.orc_split.argtypes = [i32, vp, u64, vp, vp]
+        _lib.orc_merge.restype = None
+        _lib.orc_merge.argtypes = [i32, vp, vp, u64, vp]
+        _lib.orc_histogram.restype = None
+        _lib.orc_histogram.argtypes = [vp, u64, vp]
+        _lib.orc_normalize.restype = i32
+        _lib.orc_normalize.argtypes = [vp, ctypes.c_uint32, vp]
+        _lib.orc_cumulative.restype = None
+        _lib.orc_cumulative.argtypes = [vp, vp]
+        _lib.orc_rans_encode.restype = u64
+        _lib.orc_rans_encode.argtypes = [vp, u64, i32, vp, vp, vp, vp]
+        _lib.orc_rans_decode.restype = i32
+        _lib.orc_rans_decode.argtypes = [vp, vp, u64, u64, i32, vp, vp, vp]
+        _lib.orc_max_compressed_size.restype = u64
+        _lib.orc_max_compressed_size.argtypes = [i32, u64, u64]
+        _lib.orc_compress.restype = i32
+        _lib.orc_compress.argtypes = [i32, vp, u64, u64, vp, u64, vp]
+        _lib.orc_decompress.restype = i32
+        _lib.orc_decompress.argtypes = [vp, u64, i32, u64, vp]
+    return _lib
+
+
+def _p(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _bits(dtype: int, values) -> np.ndarray:
+    """Bit patterns as a contiguous uint16 (bf16) or uint32 (fp32) array."""
+    a = np.ascontiguousarray(values)
+    want = np.uint16 if dtype == BF16 else np.uint32
+    if a.dtype.itemsize != np.dtype(want).itemsize:
+        raise ValueError("expected %d-byte elements, got %s" % (np.dtype(want).itemsize, a.dtype))
+    return a.view(want).reshape(-1)
+
+
+def raw_bytes_per_value(dtype: int) -> int:
+    return 1 if dtype == BF16 else 3
+
+
+def chunk_elems(dtype: int, chunk_bytes: int = 0) -> int:
+    return int(lib().orc_chunk_elems(dtype, chunk_bytes))
+
+
+def split(dtype: int, values):
+    """Exponent bytes (n,) and sign+mantissa bytes (r*n,) of each value."""
+    v = _bits(dtype, values)
+    n = v.size
+    e = np.empty(n, np.uint8)
+    sm = np.empty(n * raw_bytes_per_value(dtype), np.uint8)
+    lib().orc_split(dtype, _p(v), n, _p(e), _p(sm))
+    return e, sm
+
+
+def merge(dtype: int, e, sm) -> np.ndarray:
+    e = np.ascontiguousarray(e, np.uint8)
+    sm = np.ascontiguousarray(sm, np.uint8)
+    n = e.size
+    out = np.empty(n, np.uint16 if dtype == BF16 else np.uint32)
+    lib().orc_merge(dtype, _p(e), _p(sm), n, _p(out))
+    return out
+
+
+def histogram(e) -> np.ndarray:
+    e = np.ascontiguousarray(e, np.uint8)
+    c = np.empty(256, np.uint32)
+    lib().orc_histogram(_p(e), e.size, _p(c))
+    return c
+
+
+def normalize(counts):
+    """(f[256], nsym) for a histogram whose total is n = sum(counts)."""
+    c = np.ascontiguousarray(counts, np.uint32)
+    assert c.size == 256
+    f = np.empty(256, np.uint32)
+    nsym = lib().orc_normalize(_p(c), int(c.sum()), _p(f))
+    return f, int(nsym)
+
+
+def cumulative(f) -> np.ndarray:
+    f = np.ascontiguousarray(f, np.uint32)
+    c0 = np.empty(256, np.uint32)
+    lib().orc_cumulative(_p(f), _p(c0))
+    return c0
+
+
+def rans_encode(sym, f, c0, lanes: int = LANES):
+    """Interleaved rANS over `lanes` lanes with an explicit table.
+
+    Returns (states[lanes] uint32, words uint16 in decoder order)."""
+    s = np.ascontiguousarray(sym, np.uint8)
+    f = np.ascontiguousarray(f, np.uint32)
+    c0 = np.ascontiguousarray(c0, np.uint32)
+    states = np.empty(lanes, np.uint32)
+    words = np.empty(max(s.size, 1), np.uint16)
+    nw = lib().orc_rans_encode(_p(s), s.size, lanes, _p(f), _p(c0), _p(states), _p(words))
+    return states, words[:nw].copy()
+
+
+def rans_decode(states, words, n: int, f, c0, lanes: int = LANES):
+    """Returns (status, symbols[n])."""
+    st = np.ascontiguousarray(states, np.uint32)
+    w = np.ascontiguousarray(words, np.uint16)
+    if w.size == 0:
+        w = np.zeros(1, np.uint16)
+        nw = 0
+    else:
+        nw = w.size
+    f = np.ascontiguousarray(f, np.uint32)
+    c0 = np.ascontiguousarray(c0, np.uint32)
+    out = np.zeros(max(n, 1), np.uint8)
+    status = lib().orc_rans_decode(_p(st), _p(w), nw, n, lanes, _p(f), _p(c0), _p(out))
+    return int(status), out[:n]
+
+
+def max_compressed_size(dtype: int, n: int, chunk_bytes: int = 0) -> int:
+    return int(lib().orc_max_compressed_size(dtype, n, chunk_bytes))
+
+
+def compress(dtype: int, values, chunk_bytes: int = 0) -> np.ndarray:
+    """The whole compressed buffer as a uint8 array (exact size)."""
+    v = _bits(dtype, values)
+    cap = max_compressed_size(dtype, v.size, chunk_bytes)
+    if cap == 0:
+        raise ValueError("invalid chunk_bytes")
+    out = np.empty(cap, np.uint8)
+    size = ctypes.c_uint64(0)
+    st = lib().orc_compress(dtype, _p(v), v.size, chunk_bytes, _p(out), cap, ctypes.byref(size))
+    if st != OK:
+        raise ValueError("oracle compress failed with status %d" % st)
+    return out[: size.value].copy()
+
+
+def decompress(buf, dtype: int, n: int):
+    """Returns (status, bit patterns uint16/uint32 of length n)."""
+    b = np.ascontiguousarray(buf, np.uint8)
+    if b.size == 0:
+        b = np.zeros(1, np.uint8)
+        nbytes = 0
+    else:
+        nbytes = b.size
+    out = np.zeros(max(n, 1), np.uint16 if dtype == BF16 else np.uint32)
+    st = lib().orc_decompress(_p(b), nbytes, dtype, n, _p(out))
+    return int(st), out[:n]

@@ -1,0 +1,480 @@
+/*
+ * uzip_oracle.c -- plain, slow, single-threaded CPU oracle of the uzip v1
+ * bitstream (lossless bf16/fp32 compression by exponent/sign+mantissa split
+ * and 32-lane interleaved rANS of the exponent stream).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may link, load or
+ * call this file.  Only the test-suite, the smoke check and the CPU-baseline
+ * leg of the benchmark use it.  It shares no code, header, table or constant
+ * generator with the HIP implementation; the two meet only through the byte
+ * strings they produce.
+ *
+ * What the method is, and where each step comes from:
+ *  - UCCL-Zip: Lossless Compression Supercharged GPU Communication
+ *    (arXiv 2604.17172; review page on pith.science), Figure 2 and its body
+ *    text: the floating-point ANS pipeline separates every value's exponent
+ *    field from its sign and fraction bits and entropy-codes only the
+ *    exponents; the sign and fraction are left as they are.
+ *  - same page, Figure 5(b): each thread block builds its own local frequency
+ *    table, so there is no global table and no cross-block synchronisation.
+ *    Here: one table per fixed-size chunk, counted over the whole chunk.
+ *  - NCCLZ: Compression-Enabled GPU Collectives with Decoupled Quantization
+ *    and Entropy Coding (arXiv 2605.12396), Sec. IV-D2 "batch framing":
+ *    every coded unit is a self-describing header + payload (codec id, raw
+ *    size, payload size, codec parameters); Sec. IV-C / Algorithm 1: a RAW
+ *    frame is committed when coding does not pay; Algorithm 2: the receiver
+ *    validates the header before decoding.
+ *  - The pages give no formulas for the coder.  The textbook methods used
+ *    where they are silent: J. Duda, "Asymmetric numeral systems" (arXiv
+ *    1311.2540) for rANS with a 2^12 table, 32-bit state and 16-bit
+ *    renormalisation; F. Giesen, "Interleaved entropy coders" (arXiv
+ *    1402.3392) for the 32 interleaved lanes; largest-remainder (Hamilton)
+ *    apportionment for the frequency table.
+ *
+ * Parity pins: every exported function is pinned by the -m "not gpu" tests
+ * (hand-derived traces, closed forms, brute force, invariants, library
+ * routines); none is "parity unpinned".
+ *
+ * Build: gcc -O2 -std=c11 -shared -fPIC -o liboracle.so uzip_oracle.c
+ */
+#include <stddef.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ---- format constants of bitstream v1 --------------------------------- */
+#define ORC_PROB_BITS 12
+#define ORC_M 4096u            /* 2^PROB_BITS: total of the frequency table */
+#define ORC_LANES 32           /* interleaved rANS lanes per chunk */
+#define ORC_L 65536u           /* lower end of the normalised state interval */
+#define ORC_MAGIC 0x31505A55u  /* "UZP1" little-endian */
+#define ORC_VERSION 1
+#define ORC_HDR_BYTES 64
+#define ORC_REC_HDR 16
+#define ORC_MAX_CHUNK_ELEMS (1u << 20)
+
+#define ORC_DT_BF16 1
+#define ORC_DT_FP32 2
+
+enum { ORC_OK = 0, ORC_INVALID = 1, ORC_CAPACITY = 2, ORC_CORRUPT = 3 };
+
+static uint64_t orc_align16(uint64_t v) { return (v + 15u) & ~(uint64_t)15u; }
+static uint64_t orc_align4(uint64_t v) { return (v + 3u) & ~(uint64_t)3u; }
+
+/* little-endian stores / loads, byte by byte */
+static void put16(uint8_t *p, uint32_t v) { p[0] = (uint8_t)v; p[1] = (uint8_t)(v >> 8); }
+static void put32(uint8_t *p, uint32_t v) {
+    for (int k = 0; k < 4; ++k) p[k] = (uint8_t)(v >> (8 * k));
+}
+static void put64(uint8_t *p, uint64_t v) {
+    for (int k = 0; k < 8; ++k) p[k] = (uint8_t)(v >> (8 * k));
+}
+static uint32_t get16(const uint8_t *p) { return (uint32_t)p[0] | ((uint32_t)p[1] << 8); }
+static uint32_t get32(const uint8_t *p) {
+    uint32_t v = 0;
+    for (int k = 0; k < 4; ++k) v |= (uint32_t)p[k] << (8 * k);
+    return v;
+}
+static uint64_t get64(const uint8_t *p) {
+    uint64_t v = 0;
+    for (int k = 0; k < 8; ++k) v |= (uint64_t)p[k] << (8 * k);
+    return v;
+}
+
+/* bytes of sign+mantissa stored raw per value, and bytes per value */
+static int orc_raw_bytes(int dtype) { return dtype == ORC_DT_BF16 ? 1 : (dtype == ORC_DT_FP32 ? 3 : 0); }
+static int orc_elem_bytes(int dtype) { return dtype == ORC_DT_BF16 ? 2 : (dtype == ORC_DT_FP32 ? 4 : 0); }
+
+/* chunk_bytes 0 selects the per-dtype default (64 KiB bf16, 256 KiB fp32).
+ * Returns chunk_elems, or 0 when the chunk size is invalid. */
+uint64_t orc_chunk_elems(int dtype, uint64_t chunk_bytes) {
+    int eb = orc_elem_bytes(dtype);
+    if (eb == 0) return 0;
+    if (chunk_bytes == 0) chunk_bytes = dtype == ORC_DT_BF16 ? 65536u : 262144u;
+    if (chunk_bytes % (uint64_t)(32 * eb) != 0) return 0;
+    uint64_t ce = chunk_bytes / (uint64_t)eb;
+    if (ce == 0 || ce > ORC_MAX_CHUNK_ELEMS) return 0;
+    return ce;
+}
+
+/* ---- step 1: field split (UCCL-Zip Fig. 2) ------------------------------
+ * bf16 word v: exponent e = bits 14..7; sign+mantissa byte sm keeps the sign
+ * as its top bit and the 7 mantissa bits below it.
+ * fp32 word v: exponent e = bits 30..23; sm is 24 bits: sign at bit 23 and
+ * the 23 mantissa bits below, stored as 3 bytes little-endian. */
+void orc_split(int dtype, const void *in, uint64_t n, uint8_t *e_out, uint8_t *sm_out) {
+    if (dtype == ORC_DT_BF16) {
+        const uint16_t *v = (const uint16_t *)in;
+        for (uint64_t i = 0; i < n; ++i) {
+            uint32_t x = v[i];
+            e_out[i] = (uint8_t)((x >> 7) & 0xFFu);
+            sm_out[i] = (uint8_t)(((x >> 8) & 0x80u) | (x & 0x7Fu));
+        }
+    } else {
+        const uint32_t *v = (const uint32_t *)in;
+        for (uint64_t i = 0; i < n; ++i) {
+            uint32_t x = v[i];
+            uint32_t sm = ((x >> 8) & 0x800000u) | (x & 0x7FFFFFu);
+            e_out[i] = (uint8_t)((x >> 23) & 0xFFu);
+            sm_out[3 * i + 0] = (uint8_t)(sm & 0xFFu);
+            sm_out[3 * i + 1] = (uint8_t)((sm >> 8) & 0xFFu);
+            sm_out[3 * i + 2] = (uint8_t)(sm >> 16);
+        }
+    }
+}
+
+/* inverse of orc_split */
+void orc_merge(int dtype, const uint8_t *e, const uint8_t *sm, uint64_t n, void *out) {
+    if (dtype == ORC_DT_BF16) {
+        uint16_t *v = (uint16_t *)out;
+        for (uint64_t i = 0; i < n; ++i) {
+            uint32_t s = sm[i];
+            v[i] = (uint16_t)(((s & 0x80u) << 8) | ((uint32_t)e[i] << 7) | (s & 0x7Fu));
+        }
+    } else {
+        uint32_t *v = (uint32_t *)out;
+        for (uint64_t i = 0; i < n; ++i) {
+            uint32_t s = (uint32_t)sm[3 * i] | ((uint32_t)sm[3 * i + 1] << 8) | ((uint32_t)sm[3 * i + 2] << 16);
+            v[i] = ((s & 0x800000u) << 8) | ((uint32_t)e[i] << 23) | (s & 0x7FFFFFu);
+        }
+    }
+}
+
+/* ---- step 2: histogram of the chunk's exponents (UCCL-Zip Fig. 5(b)) ----
+ * A full count over every exponent of the chunk; no sampling. */
+void orc_histogram(const uint8_t *e, uint64_t n, uint32_t counts[256]) {
+    for (int s = 0; s < 256; ++s) counts[s] = 0;
+    for (uint64_t i = 0; i < n; ++i) counts[e[i]] += 1;
+}
+
+/* ---- step 3: normalise the counts to a table summing to M = 4096 --------
+ * Reserve one slot for each present symbol, share the remaining
+ * R = M - nsym slots in proportion to the counts (floor of the quota), and
+ * hand the d leftover slots to the symbols with the largest remainders,
+ * lower symbol first on equal remainders (Hamilton / largest remainder).
+ * n must equal the sum of the counts and be >= 1.  Returns nsym. */
+int orc_normalize(const uint32_t counts[256], uint32_t n, uint32_t f[256]) {
+    int nsym = 0;
+    for (int s = 0; s < 256; ++s) {
+        f[s] = 0;
+        if (counts[s] > 0) nsym += 1;
+    }
+    if (nsym == 0) return 0;
+    uint64_t R = ORC_M - (uint64_t)nsym;
+    uint64_t rem[256];
+    uint64_t given = 0;
+    for (int s = 0; s < 256; ++s) {
+        if (counts[s] == 0) continue;
+        uint64_t q = (uint64_t)counts[s] * R;
+        f[s] = 1u + (uint32_t)(q / n);
+        rem[s] = q % n;
+        given += q / n;
+    }
+    uint64_t d = R - given;
+    /* hand out d extra slots, one at a time, each to the present symbol with
+     * the largest remainder not yet served (lowest symbol on ties) */
+    int served[256];
+    for (int s = 0; s < 256; ++s) served[s] = 0;
+    for (uint64_t k = 0; k < d; ++k) {
+        int best = -1;
+        for (int s = 0; s < 256; ++s) {
+            if (counts[s] == 0 || served[s]) continue;
+            if (best < 0 || rem[s] > rem[best]) best = s;
+        }
+        served[best] = 1;
+        f[best] += 1;
+    }
+    return nsym;
+}
+
+/* cumulative frequencies in ascending symbol order */
+void orc_cumulative(const uint32_t f[256], uint32_t c0[256]) {
+    uint32_t acc = 0;
+    for (int s = 0; s < 256; ++s) {
+        c0[s] = acc;
+        acc += f[s];
+    }
+}
+
+/* ---- step 4: interleaved rANS encode (Duda; Giesen) ----------------------
+ * Value i belongs to lane i mod K and step i / K.  Every lane starts at
+ * x = L.  Steps run from the last one down to 0.  For each lane with a value
+ * at that step: if x >= f[s] * 2^20 the low 16 bits of x are emitted and x is
+ * shifted down by 16; then x = (x / f) * M + (x mod f) + c0[s].
+ * Words are returned in the order the decoder consumes them: step 0's words
+ * (lanes ascending), then step 1's, and so on.  The encoder meets the groups
+ * in the opposite order, so it fills its buffer from the end, one step group
+ * at a time, lanes ascending inside the group.
+ * words must hold n entries (at most one word per value).  Returns n_words. */
+uint64_t orc_rans_encode(const uint8_t *sym, uint64_t n, int K, const uint32_t f[256], const uint32_t c0[256],
+                         uint32_t *states, uint16_t *words) {
+    for (int j = 0; j < K; ++j) states[j] = ORC_L;
+    if (n == 0) return 0;
+    uint64_t T = (n + (uint64_t)K - 1) / (uint64_t)K;
+    uint16_t *group = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)K);
+    uint64_t end = n; /* words so far occupy words[end .. n) */
+    for (uint64_t t = T; t-- > 0;) {
+        int cnt = 0;
+        for (int j = 0; j < K; ++j) {
+            uint64_t i = t * (uint64_t)K + (uint64_t)j;
+            if (i >= n) continue;
+            uint32_t s = sym[i];
+            uint64_t x = states[j];
+            uint64_t fs = f[s];
+            if (x >= (fs << 20)) {
+                group[cnt++] = (uint16_t)(x & 0xFFFFu);
+                x >>= 16;
+            }
+            x = (x / fs) * ORC_M + (x % fs) + c0[s];
+            states[j] = (uint32_t)x;
+        }
+        end -= (uint64_t)cnt;
+        for (int k = 0; k < cnt; ++k) words[end + (uint64_t)k] = group[k];
+    }
+    free(group);
+    uint64_t n_words = n - end;
+    memmove(words, words + end, sizeof(uint16_t) * (size_t)n_words);
+    return n_words;
+}
+
+/* ---- inverse: interleaved rANS decode ------------------------------------
+ * For step t = 0, 1, ... and lanes ascending: slot = x mod M; s is the symbol
+ * with c0[s] <= slot < c0[s] + f[s]; x = f[s] * (x >> 12) + slot - c0[s];
+ * if x < L the next word is shifted in.  Returns ORC_OK, or ORC_CORRUPT when
+ * the word stream runs out, a slot maps to no symbol, or the end state is not
+ * L on every lane with every word consumed. */
+int orc_rans_decode(const uint32_t *states_in, const uint16_t *words, uint64_t n_words, uint64_t n, int K,
+                    const uint32_t f[256], const uint32_t c0[256], uint8_t *sym_out) {
+    uint32_t *x = (uint32_t *)malloc(sizeof(uint32_t) * (size_t)K);
+    int16_t slot_sym[ORC_M];
+    for (uint32_t k = 0; k < ORC_M; ++k) slot_sym[k] = -1;
+    for (int s = 0; s < 256; ++s)
+        for (uint32_t k = 0; k < f[s]; ++k)
+            if (c0[s] + k < ORC_M) slot_sym[c0[s] + k] = (int16_t)s;
+    for (int j = 0; j < K; ++j) x[j] = states_in[j];
+    uint64_t pos = 0;
+    int status = ORC_OK;
+    uint64_t T = n == 0 ? 0 : (n + (uint64_t)K - 1) / (uint64_t)K;
+    for (uint64_t t = 0; t < T && status == ORC_OK; ++t) {
+        for (int j = 0; j < K; ++j) {
+            uint64_t i = t * (uint64_t)K + (uint64_t)j;
+            if (i >= n) continue;
+            uint32_t slot = x[j] & (ORC_M - 1u);
+            int s = slot_sym[slot];
+            if (s < 0) { status = ORC_CORRUPT; break; }
+            uint32_t nx = f[s] * (x[j] >> ORC_PROB_BITS) + slot - c0[s];
+            if (nx < ORC_L) {
+                if (pos >= n_words) { status = ORC_CORRUPT; break; }
+                nx = (nx << 16) | words[pos++];
+            }
+            x[j] = nx;
+            sym_out[i] = (uint8_t)s;
+        }
+    }
+    if (status == ORC_OK) {
+        for (int j = 0; j < K; ++j)
+            if (x[j] != ORC_L) status = ORC_CORRUPT;
+        if (pos != n_words) status = ORC_CORRUPT;
+    }
+    free(x);
+    return status;
+}
+
+/* ---- buffer layout ------------------------------------------------------
+ * [0,64) header | [64, 64+8(C+1)) u64 rec_off[C+1] | pad | SM region at
+ * sm_off = align16(64+8(C+1)), r*N bytes in value order | pad | records from
+ * exp_off = align16(sm_off + r*N).  total = exp_off + rec_off[C]. */
+static void orc_layout(int dtype, uint64_t n, uint64_t ce, uint64_t *C, uint64_t *sm_off, uint64_t *exp_off) {
+    uint64_t c = (n + ce - 1) / ce;
+    *C = c;
+    *sm_off = orc_align16(ORC_HDR_BYTES + 8 * (c + 1));
+    *exp_off = orc_align16(*sm_off + (uint64_t)orc_raw_bytes(dtype) * n);
+}
+
+uint64_t orc_max_compressed_size(int dtype, uint64_t n, uint64_t chunk_bytes) {
+    uint64_t ce = orc_chunk_elems(dtype, chunk_bytes);
+    if (ce == 0) return 0;
+    uint64_t C, sm_off, exp_off;
+    orc_layout(dtype, n, ce, &C, &sm_off, &exp_off);
+    uint64_t total = exp_off;
+    for (uint64_t i = 0; i < C; ++i) {
+        uint64_t ni = (i + 1 < C) ? ce : n - i * ce;
+        total += orc_align16(ORC_REC_HDR + ni);
+    }
+    return total;
+}
+
+/* Encode one chunk's record (steps 2-4 plus the RANS/RAW choice) into rec,
+ * which must hold align16(16 + ni) bytes.  Returns the record size. */
+static uint64_t orc_encode_record(const uint8_t *e, uint64_t ni, uint8_t *rec) {
+    uint32_t counts[256], f[256], c0[256], states[ORC_LANES];
+    orc_histogram(e, ni, counts);
+    int nsym = orc_normalize(counts, (uint32_t)ni, f);
+    orc_cumulative(f, c0);
+    uint16_t *words = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)(ni ? ni : 1));
+    uint64_t n_words = orc_rans_encode(e, ni, ORC_LANES, f, c0, states, words);
+    uint64_t tab_end = orc_align4(ORC_REC_HDR + 32 + 2 * (uint64_t)nsym);
+    uint64_t words_at = tab_end + 4 * ORC_LANES;
+    uint64_t rans_bytes = orc_align16(words_at + 2 * n_words);
+    uint64_t raw_bytes = orc_align16(ORC_REC_HDR + ni);
+    uint64_t rec_bytes;
+    if (rans_bytes < raw_bytes) {
+        rec_bytes = rans_bytes;
+        memset(rec, 0, (size_t)rec_bytes);
+        rec[0] = 0; /* mode RANS */
+        put16(rec + 2, (uint32_t)nsym);
+        put32(rec + 4, (uint32_t)n_words);
+        put32(rec + 8, (uint32_t)ni);
+        put32(rec + 12, (uint32_t)rec_bytes);
+        int k = 0;
+        for (int s = 0; s < 256; ++s) {
+            if (f[s] == 0) continue;
+            rec[16 + (s >> 3)] |= (uint8_t)(1u << (s & 7));
+            put16(rec + 48 + 2 * k, f[s]);
+            k += 1;
+        }
+        for (int j = 0; j < ORC_LANES; ++j) put32(rec + tab_end + 4 * (uint64_t)j, states[j]);
+        for (uint64_t w = 0; w < n_words; ++w) put16(rec + words_at + 2 * w, words[w]);
+    } else {
+        rec_bytes = raw_bytes;
+        memset(rec, 0, (size_t)rec_bytes);
+        rec[0] = 1; /* mode RAW */
+        put32(rec + 8, (uint32_t)ni);
+        put32(rec + 12, (uint32_t)rec_bytes);
+        memcpy(rec + ORC_REC_HDR, e, (size_t)ni);
+    }
+    free(words);
+    return rec_bytes;
+}
+
+/* Whole-buffer compression.  out must hold cap >= orc_max_compressed_size
+ * bytes.  *out_size receives the exact compressed size. */
+int orc_compress(int dtype, const void *in, uint64_t n, uint64_t chunk_bytes, uint8_t *out, uint64_t cap,
+                 uint64_t *out_size) {
+    uint64_t ce = orc_chunk_elems(dtype, chunk_bytes);
+    if (ce == 0) return ORC_INVALID;
+    if (cap < orc_max_compressed_size(dtype, n, chunk_bytes)) return ORC_CAPACITY;
+    int r = orc_raw_bytes(dtype);
+    uint64_t C, sm_off, exp_off;
+    orc_layout(dtype, n, ce, &C, &sm_off, &exp_off);
+    uint8_t *e = (uint8_t *)malloc((size_t)(n ? n : 1));
+    uint8_t *sm = (uint8_t *)malloc((size_t)(n ? n * (uint64_t)r : 1));
+    orc_split(dtype, in, n, e, sm);
+    memset(out, 0, (size_t)exp_off);
+    memcpy(out + sm_off, sm, (size_t)(n * (uint64_t)r));
+    uint64_t off = 0;
+    put64(out + ORC_HDR_BYTES, 0);
+    for (uint64_t i = 0; i < C; ++i) {
+        uint64_t ni = (i + 1 < C) ? ce : n - i * ce;
+        off += orc_encode_record(e + i * ce, ni, out + exp_off + off);
+        put64(out + ORC_HDR_BYTES + 8 * (i + 1), off);
+    }
+    uint64_t total = exp_off + off;
+    put32(out + 0, ORC_MAGIC);
+    put16(out + 4, ORC_VERSION);
+    out[6] = (uint8_t)dtype;
+    out[7] = ORC_PROB_BITS;
+    out[8] = ORC_LANES;
+    out[9] = (uint8_t)r;
+    put16(out + 10, 0);
+    put32(out + 12, (uint32_t)ce);
+    put64(out + 16, n);
+    put64(out + 24, C);
+    put64(out + 32, sm_off);
+    put64(out + 40, exp_off);
+    put64(out + 48, total);
+    put64(out + 56, 0);
+    free(e);
+    free(sm);
+    *out_size = total;
+    return ORC_OK;
+}
+
+/* Decode one record into the chunk's exponents.  rec holds rec_len bytes
+ * (already known to lie inside the buffer).  Checks V6-V9. */
+static int orc_decode_record(const uint8_t *rec, uint64_t rec_len, uint64_t ni, uint8_t *e) {
+    if (rec_len < ORC_REC_HDR) return ORC_CORRUPT;
+    uint32_t mode = rec[0];
+    uint32_t nsym = get16(rec + 2);
+    uint64_t n_words = get32(rec + 4);
+    uint64_t n_values = get32(rec + 8);
+    uint64_t rec_bytes = get32(rec + 12);
+    if (mode > 1 || n_values != ni || rec_bytes != rec_len) return ORC_CORRUPT;
+    if (mode == 1) {
+        if (nsym != 0 || n_words != 0 || rec_len != orc_align16(ORC_REC_HDR + ni)) return ORC_CORRUPT;
+        memcpy(e, rec + ORC_REC_HDR, (size_t)ni);
+        return ORC_OK;
+    }
+    /* RANS: bitmap, frequencies, states, words */
+    if (rec_len < ORC_REC_HDR + 32) return ORC_CORRUPT;
+    uint32_t pop = 0;
+    for (int s = 0; s < 256; ++s) pop += (rec[16 + (s >> 3)] >> (s & 7)) & 1u;
+    if (pop != nsym || nsym < 1 || nsym > 256) return ORC_CORRUPT;
+    uint64_t tab_end = orc_align4(ORC_REC_HDR + 32 + 2 * (uint64_t)nsym);
+    uint64_t words_at = tab_end + 4 * ORC_LANES;
+    if (rec_len != orc_align16(words_at + 2 * n_words)) return ORC_CORRUPT;
+    uint32_t f[256], c0[256], states[ORC_LANES];
+    uint32_t sum = 0;
+    int k = 0;
+    for (int s = 0; s < 256; ++s) {
+        f[s] = 0;
+        if ((rec[16 + (s >> 3)] >> (s & 7)) & 1u) {
+            f[s] = get16(rec + 48 + 2 * k);
+            k += 1;
+            if (f[s] == 0) return ORC_CORRUPT;
+            sum += f[s];
+        }
+    }
+    if (sum != ORC_M) return ORC_CORRUPT;
+    orc_cumulative(f, c0);
+    for (int j = 0; j < ORC_LANES; ++j) {
+        states[j] = get32(rec + tab_end + 4 * (uint64_t)j);
+        if (states[j] < ORC_L) return ORC_CORRUPT;
+    }
+    uint16_t *words = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)(n_words ? n_words : 1));
+    for (uint64_t w = 0; w < n_words; ++w) words[w] = (uint16_t)get16(rec + words_at + 2 * w);
+    int st = orc_rans_decode(states, words, n_words, ni, ORC_LANES, f, c0, e);
+    free(words);
+    return st;
+}
+
+/* Whole-buffer decompression with validation V1-V9.  The caller states the
+ * dtype and element count, as a receiver does.  Returns ORC_OK, or
+ * ORC_CORRUPT for any inconsistency; never reads outside in[0, in_bytes). */
+int orc_decompress(const uint8_t *in, uint64_t in_bytes, int dtype, uint64_t n, void *out) {
+    int r = orc_raw_bytes(dtype);
+    if (r == 0) return ORC_INVALID;
+    if (in_bytes < ORC_HDR_BYTES) return ORC_CORRUPT;
+    /* V1: magic, version and the fixed coder parameters */
+    if (get32(in) != ORC_MAGIC || get16(in + 4) != ORC_VERSION) return ORC_CORRUPT;
+    if (in[7] != ORC_PROB_BITS || in[8] != ORC_LANES || in[9] != (uint8_t)r) return ORC_CORRUPT;
+    /* V2: dtype and element count as the caller states them */
+    if (in[6] != (uint8_t)dtype || get64(in + 16) != n) return ORC_CORRUPT;
+    /* V3: chunk size and chunk count */
+    uint64_t ce = get32(in + 12);
+    if (ce == 0 || ce % 32 != 0 || ce > ORC_MAX_CHUNK_ELEMS) return ORC_CORRUPT;
+    uint64_t C, sm_off, exp_off;
+    orc_layout(dtype, n, ce, &C, &sm_off, &exp_off);
+    if (get64(in + 24) != C) return ORC_CORRUPT;
+    /* V4: region offsets and total size */
+    uint64_t total = get64(in + 48);
+    if (get64(in + 32) != sm_off || get64(in + 40) != exp_off) return ORC_CORRUPT;
+    if (total > in_bytes || total < exp_off) return ORC_CORRUPT;
+    /* V5: the record index */
+    if (get64(in + ORC_HDR_BYTES) != 0) return ORC_CORRUPT;
+    if (get64(in + ORC_HDR_BYTES + 8 * C) != total - exp_off) return ORC_CORRUPT;
+    for (uint64_t i = 0; i < C; ++i) {
+        uint64_t a = get64(in + ORC_HDR_BYTES + 8 * i), b = get64(in + ORC_HDR_BYTES + 8 * (i + 1));
+        if (b < a || (a & 15u) != 0 || (b & 15u) != 0) return ORC_CORRUPT;
+    }
+    uint8_t *e = (uint8_t *)malloc((size_t)(n ? n : 1));
+    int st = ORC_OK;
+    for (uint64_t i = 0; i < C && st == ORC_OK; ++i) {
+        uint64_t ni = (i + 1 < C) ? ce : n - i * ce;
+        uint64_t a = get64(in + ORC_HDR_BYTES + 8 * i), b = get64(in + ORC_HDR_BYTES + 8 * (i + 1));
+        st = orc_decode_record(in + exp_off + a, b - a, ni, e + i * ce);
+    }
+    if (st == ORC_OK) orc_merge(dtype, e, in + sm_off, n, out);
+    free(e);
+    return st;
+}

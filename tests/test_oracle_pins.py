@@ -1,0 +1,559 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Each test pins one oracle function to something other than the oracle
+itself: a hand-derived trace (tests/golden, each with its derivation), a
+closed form, a library routine, brute force over tiny inputs, or an
+invariant of the method.  A plausible mistake in the oracle (a dropped term,
+a wrong sign or index, swapped lanes, a wrong word order, an off-by-one in
+the layout) fails at least one of them.
+"""
+import itertools
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle as orc
+import workloads
+
+GOLD = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _gold(name):
+    with open(os.path.join(GOLD, name)) as fh:
+        return json.load(fh)
+
+
+def _table(d):
+    f = np.zeros(256, np.uint32)
+    c0 = np.zeros(256, np.uint32)
+    for k, (fs, cs) in d.items():
+        f[int(k)] = fs
+        c0[int(k)] = cs
+    return f, c0
+
+
+# --------------------------------------------------------------------------
+# Record parsing helper (the v1 record layout read back byte by byte)
+# --------------------------------------------------------------------------
+def parse_buffer(buf):
+    b = bytes(buf)
+    hdr = dict(
+        magic=int.from_bytes(b[0:4], "little"), version=int.from_bytes(b[4:6], "little"), dtype=b[6],
+        prob_bits=b[7], lanes=b[8], r=b[9], chunk_elems=int.from_bytes(b[12:16], "little"),
+        n=int.from_bytes(b[16:24], "little"), C=int.from_bytes(b[24:32], "little"),
+        sm_off=int.from_bytes(b[32:40], "little"), exp_off=int.from_bytes(b[40:48], "little"),
+        total=int.from_bytes(b[48:56], "little"))
+    C = hdr["C"]
+    idx = [int.from_bytes(b[64 + 8 * i:72 + 8 * i], "little") for i in range(C + 1)]
+    recs = []
+    for i in range(C):
+        r = b[hdr["exp_off"] + idx[i]:hdr["exp_off"] + idx[i + 1]]
+        mode, nsym = r[0], int.from_bytes(r[2:4], "little")
+        n_words = int.from_bytes(r[4:8], "little")
+        n_values = int.from_bytes(r[8:12], "little")
+        rec = dict(mode=mode, nsym=nsym, n_words=n_words, n_values=n_values, bytes=len(r), raw=r)
+        if mode == 0:
+            bitmap = r[16:48]
+            syms = [s for s in range(256) if (bitmap[s >> 3] >> (s & 7)) & 1]
+            f = {s: int.from_bytes(r[48 + 2 * k:50 + 2 * k], "little") for k, s in enumerate(syms)}
+            tab_end = (48 + 2 * nsym + 3) // 4 * 4
+            states = [int.from_bytes(r[tab_end + 4 * j:tab_end + 4 * j + 4], "little") for j in range(32)]
+            rec.update(f=f, states=states)
+        recs.append(rec)
+    return hdr, idx, recs
+
+
+def entropy_bits(counts):
+    c = np.asarray(counts, np.float64)
+    c = c[c > 0]
+    n = c.sum()
+    return float(-(c * np.log2(c / n)).sum())
+
+
+# --------------------------------------------------------------------------
+# P1: field split -- a bijection, and it agrees with the float semantics
+# --------------------------------------------------------------------------
+def test_split_bf16_exhaustive_bijection():
+    v = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    e, sm = orc.split(orc.BF16, v)
+    assert np.array_equal(orc.merge(orc.BF16, e, sm), v)
+    assert np.unique(e.astype(np.uint32) * 256 + sm).size == 65536
+
+
+def _expected_fields(x, mant_bits, bias, emax):
+    """(exponent field, sign, mantissa field) from the float value itself."""
+    sign = np.signbit(x).astype(np.uint64)
+    ax = np.abs(x)
+    e = np.zeros(x.shape, np.uint64)
+    mant = np.zeros(x.shape, np.uint64)
+    finite = np.isfinite(x)
+    tiny = 2.0 ** (1 - bias)
+    normal = finite & (ax >= tiny)
+    m, ex = np.frexp(ax[normal])  # ax = m * 2^ex, m in [0.5, 1)
+    e[normal] = (ex - 1 + bias).astype(np.uint64)
+    mant[normal] = ((2 * m - 1) * 2.0 ** mant_bits).astype(np.uint64)
+    sub = finite & (ax < tiny)
+    mant[sub] = (ax[sub] / 2.0 ** (1 - bias - mant_bits)).astype(np.uint64)
+    e[~finite] = emax
+    return e, sign, mant, np.isnan(x)
+
+
+def test_split_bf16_matches_float_semantics():
+    v = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    x = (v.astype(np.uint32) << 16).view(np.float32).astype(np.float64)  # bf16 is the top half of fp32
+    e_exp, sign, mant, isnan = _expected_fields(x, 7, 127, 255)
+    e, sm = orc.split(orc.BF16, v)
+    assert np.array_equal(e.astype(np.uint64), e_exp)
+    assert np.array_equal((sm >> 7).astype(np.uint64), sign)
+    ok = ~isnan
+    assert np.array_equal((sm[ok] & 0x7F).astype(np.uint64), mant[ok])
+    assert np.all((sm[isnan] & 0x7F) != 0)  # NaN keeps a nonzero payload
+
+
+def test_split_fp32_all_exponents_and_special_classes():
+    rng = np.random.default_rng(11)
+    exps = np.repeat(np.arange(256, dtype=np.uint32), 64)
+    mants = rng.integers(0, 1 << 23, exps.size, dtype=np.uint32)
+    mants[::64] = 0
+    mants[1::64] = (1 << 23) - 1
+    mants[2::64] = 1
+    signs = rng.integers(0, 2, exps.size, dtype=np.uint32)
+    v = (signs << 31) | (exps << 23) | mants
+    special = np.array([0x00000000, 0x80000000, 0x7F800000, 0xFF800000, 0x7FC00000, 0xFFC00001, 0x7F800001,
+                        0x00000001, 0x807FFFFF, 0x00400000, 0x3F800000], np.uint32)
+    v = np.concatenate([v, special])
+    e, sm = orc.split(orc.FP32, v)
+    assert np.array_equal(orc.merge(orc.FP32, e, sm), v)
+    x = v.view(np.float32).astype(np.float64)
+    e_exp, sign, mant, isnan = _expected_fields(x, 23, 127, 255)
+    assert np.array_equal(e.astype(np.uint64), e_exp)
+    s24 = sm[0::3].astype(np.uint64) | (sm[1::3].astype(np.uint64) << 8) | (sm[2::3].astype(np.uint64) << 16)
+    assert np.array_equal(s24 >> 23, sign)
+    ok = ~isnan
+    assert np.array_equal((s24 & 0x7FFFFF)[ok], mant[ok])
+
+
+# --------------------------------------------------------------------------
+# P2: histogram == numpy.bincount
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_histogram_is_bincount(seed):
+    rng = np.random.default_rng(seed)
+    e = rng.geometric(0.3, 50_000).clip(0, 255).astype(np.uint8) if seed else rng.integers(0, 256, 50_000).astype(
+        np.uint8)
+    assert np.array_equal(orc.histogram(e), np.bincount(e, minlength=256).astype(np.uint32))
+
+
+# --------------------------------------------------------------------------
+# P3: normalisation to 4096
+# --------------------------------------------------------------------------
+def test_normalize_hand_trace_t2():
+    g = _gold("normalize_t2.json")
+    counts = np.zeros(256, np.uint32)
+    for k, v in g["counts"].items():
+        counts[int(k)] = v
+    f, nsym = orc.normalize(counts)
+    assert nsym == 4
+    for k, v in g["f"].items():
+        assert f[int(k)] == v
+    c0 = orc.cumulative(f)
+    for k, v in g["c0"].items():
+        assert c0[int(k)] == v
+
+
+@pytest.mark.parametrize("n", [1, 5, 4096, 32768, 1 << 20])
+def test_normalize_single_symbol_takes_whole_table(n):
+    for s in (0, 1, 127, 200, 255):
+        c = np.zeros(256, np.uint32)
+        c[s] = n
+        f, nsym = orc.normalize(c)
+        assert nsym == 1 and f[s] == 4096 and f.sum() == 4096
+
+
+@pytest.mark.parametrize("k", range(0, 9))
+def test_normalize_equiprobable_power_of_two(k):
+    syms = np.random.default_rng(k).choice(256, 1 << k, replace=False)
+    for per in (1, 3, 1000):
+        c = np.zeros(256, np.uint32)
+        c[syms] = per
+        f, nsym = orc.normalize(c)
+        assert nsym == 1 << k
+        assert np.all(f[syms] == 4096 >> k) and f.sum() == 4096
+
+
+def _hamilton(counts):
+    """Largest-remainder apportionment in exact rationals: reserve one slot
+    per present symbol, give each floor(quota) of the rest, then the leftover
+    slots to the largest fractional parts (lower symbol on ties)."""
+    present = [s for s in range(len(counts)) if counts[s] > 0]
+    n = sum(counts)
+    R = 4096 - len(present)
+    quota = {s: Fraction(counts[s] * R, n) for s in present}
+    f = {s: 1 + math.floor(quota[s]) for s in present}
+    left = R - sum(math.floor(q) for q in quota.values())
+    order = sorted(present, key=lambda s: (-(quota[s] - math.floor(quota[s])), s))
+    for s in order[:left]:
+        f[s] += 1
+    return f
+
+
+def test_normalize_all_tiny_histograms_match_rational_hamilton():
+    syms = [0, 7, 128, 255]
+    checked = 0
+    for n in range(1, 9):
+        for comp in itertools.product(range(n + 1), repeat=4):
+            if sum(comp) != n:
+                continue
+            c = np.zeros(256, np.uint32)
+            for s, v in zip(syms, comp):
+                c[s] = v
+            f, _ = orc.normalize(c)
+            want = _hamilton([int(x) for x in c])
+            assert {s: int(f[s]) for s in range(256) if f[s]} == want
+            checked += 1
+    assert checked == 494
+
+
+def test_normalize_random_histograms_invariants_and_quota_property():
+    rng = np.random.default_rng(5)
+    for trial in range(300):
+        nsym = int(rng.integers(1, 257))
+        syms = rng.choice(256, nsym, replace=False)
+        n = int(rng.integers(nsym, 1 << 20))
+        if trial % 3 == 0:  # adversarial: one dominant symbol, the rest singletons
+            cnt = np.ones(nsym, np.int64)
+            cnt[0] = n - (nsym - 1)
+        else:
+            cnt = rng.multinomial(n - nsym, rng.dirichlet(np.full(nsym, 0.3))) + 1
+        c = np.zeros(256, np.uint32)
+        c[syms] = cnt
+        f, k = orc.normalize(c)
+        assert k == nsym
+        assert int(f.sum()) == 4096
+        assert np.array_equal(f > 0, c > 0)
+        R = 4096 - nsym
+        quota = c[syms].astype(np.float64) * R / n
+        # Hamilton's quota property: every share is floor or ceil of the quota
+        assert np.all(np.abs(f[syms].astype(np.float64) - 1 - quota) < 1.0)
+        if trial % 50 == 0:
+            want = _hamilton([int(x) for x in c])
+            assert {s: int(f[s]) for s in range(256) if f[s]} == want
+
+
+# --------------------------------------------------------------------------
+# P4: rANS core -- hand traces, closed forms, brute force
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("name", ["rans_k1_trace.json", "interleave_k2_trace.json", "renorm_boundary_t5.json"])
+def test_rans_hand_traces(name):
+    g = _gold(name)
+    f, c0 = _table(g["table"])
+    sym = np.array(g["symbols"], np.uint8)
+    states, words = orc.rans_encode(sym, f, c0, lanes=g["lanes"])
+    assert states.tolist() == g["final_states"]
+    assert words.tolist() == g["words"]
+    st, back = orc.rans_decode(states, words, sym.size, f, c0, lanes=g["lanes"])
+    assert st == orc.OK and np.array_equal(back, sym)
+
+
+def test_rans_t2_encode_no_words():
+    g = _gold("normalize_t2.json")
+    f = np.zeros(256, np.uint32)
+    for k, v in g["f"].items():
+        f[int(k)] = v
+    c0 = orc.cumulative(f)
+    states, words = orc.rans_encode(np.array(g["symbols"], np.uint8), f, c0, lanes=1)
+    assert states.tolist() == g["final_states"] and words.tolist() == g["words"]
+
+
+def test_rans_one_symbol_per_lane_t3():
+    # four symbols with f = 1024: lane j ends at (65536/1024)*4096 + c0 = 262144 + 1024 j
+    f = np.zeros(256, np.uint32)
+    sy = [10, 20, 30, 40]
+    f[sy] = 1024
+    c0 = orc.cumulative(f)
+    states, words = orc.rans_encode(np.array(sy, np.uint8), f, c0, lanes=32)
+    assert words.size == 0
+    assert states[:4].tolist() == [262144, 263168, 264192, 265216]
+    assert np.all(states[4:] == 65536)
+
+
+def test_rans_single_symbol_is_identity_on_state():
+    # f = 4096: x -> (x/4096)*4096 + x mod 4096 = x, never renormalises
+    f = np.zeros(256, np.uint32)
+    f[77] = 4096
+    c0 = orc.cumulative(f)
+    states, words = orc.rans_encode(np.full(5000, 77, np.uint8), f, c0)
+    assert words.size == 0 and np.all(states == 65536)
+
+
+def _roundtrip_seq(seq, lanes):
+    sym = np.array(seq, np.uint8)
+    f, _ = orc.normalize(np.bincount(sym, minlength=256).astype(np.uint32))
+    c0 = orc.cumulative(f)
+    states, words = orc.rans_encode(sym, f, c0, lanes=lanes)
+    st, back = orc.rans_decode(states, words, sym.size, f, c0, lanes=lanes)
+    assert st == orc.OK, seq
+    assert np.array_equal(back, sym), seq
+    assert np.all(states >= 65536)
+
+
+def test_rans_bruteforce_all_short_sequences_over_four_symbols():
+    alphabet = [3, 100, 101, 250]
+    for length in range(1, 7):
+        for seq in itertools.product(alphabet, repeat=length):
+            _roundtrip_seq(seq, 1)
+            _roundtrip_seq(seq, 32)
+
+
+def test_rans_bruteforce_all_pairs_over_256_symbols():
+    for a in range(256):
+        for b in range(0, 256, 3 if a % 2 else 1):
+            _roundtrip_seq((a, b), 1)
+
+
+def test_every_single_exponent_chunk_roundtrips_with_zero_words():
+    for s in range(256):
+        v = np.full(1000, (s << 7) | 0x15, np.uint16)
+        buf = orc.compress(orc.BF16, v)
+        _, _, recs = parse_buffer(buf)
+        assert recs[0]["mode"] == 0 and recs[0]["n_words"] == 0 and recs[0]["f"] == {s: 4096}
+        assert recs[0]["states"] == [65536] * 32
+        st, back = orc.decompress(buf, orc.BF16, v.size)
+        assert st == orc.OK and np.array_equal(back, v)
+
+
+# --------------------------------------------------------------------------
+# P5: coded size against the entropy
+# --------------------------------------------------------------------------
+def _check_entropy_invariants(dtype, bits, gaussian):
+    buf = orc.compress(dtype, bits)
+    hdr, idx, recs = parse_buffer(buf)
+    e, _ = orc.split(dtype, bits)
+    ce = hdr["chunk_elems"]
+    for i, rec in enumerate(recs):
+        chunk = e[i * ce:(i + 1) * ce]
+        cnt = np.bincount(chunk, minlength=256)
+        if rec["mode"] != 0 or chunk.size < 4096:
+            continue
+        f = rec["f"]
+        cross = -sum(cnt[s] * math.log2(f[s] / 4096.0) for s in f)
+        assert 16 * rec["n_words"] <= cross + 0.01 * chunk.size, (i, rec["n_words"], cross)
+        if gaussian:
+            # words + final states within 2048 bits of N_i * H(empirical)
+            assert 16 * rec["n_words"] + 32 * 32 <= entropy_bits(cnt) + 2048, i
+
+
+def test_entropy_invariant_pr1():
+    _check_entropy_invariants(orc.BF16, workloads.bits_numpy(workloads.pr1()), True)
+
+
+def test_entropy_invariant_gradient_bucket_small():
+    t = workloads.gradient_bucket(1 << 21, device="cpu", seed=1, special_frac=1e-3)
+    _check_entropy_invariants(orc.BF16, workloads.bits_numpy(t), True)
+
+
+def test_entropy_invariant_fp32_small():
+    t = workloads.fp32_gradients(65536 * 6 + 1000, device="cpu", seed=3)
+    _check_entropy_invariants(orc.FP32, workloads.bits_numpy(t), True)
+
+
+def entropy_bound_bytes(dtype, bits, chunk_elems):
+    e, _ = orc.split(dtype, bits)
+    r = orc.raw_bytes_per_value(dtype)
+    total = 0.0
+    for i in range(0, e.size, chunk_elems):
+        c = e[i:i + chunk_elems]
+        total += r * c.size + entropy_bits(np.bincount(c, minlength=256)) / 8.0
+    return total
+
+
+def test_pr1_ratio_within_one_percent_of_entropy_bound():
+    bits = workloads.bits_numpy(workloads.pr1())
+    buf = orc.compress(orc.BF16, bits)
+    bound = entropy_bound_bytes(orc.BF16, bits, 32768)
+    orig = bits.size * 2
+    assert 0.655 < bound / orig < 0.663  # H ~ 2.54 bits per exponent
+    assert buf.size <= 1.01 * bound
+
+
+def test_page_anchor_uniform_bf16_ratio_near_64_percent():
+    # UCCL-Zip P2P evaluation (text after Fig. 8): bf16 uniform in [-1, 1)
+    # reaches about a 64% compressed/original size; loose band, the coder,
+    # chunking and headers there differ.
+    x = np.random.default_rng(9).uniform(-1, 1, 1 << 20).astype(np.float32)
+    bits = workloads.bits_numpy(__import__("torch").from_numpy(x).to(__import__("torch").bfloat16))
+    buf = orc.compress(orc.BF16, bits)
+    assert 0.60 < buf.size / (2 * bits.size) < 0.66
+
+
+# --------------------------------------------------------------------------
+# P6: layout
+# --------------------------------------------------------------------------
+def test_format_worked_example_w1():
+    g = _gold("format_w1.json")
+    buf = orc.compress(g["dtype"], np.array(g["values"], np.uint16))
+    assert buf.tobytes().hex() == "".join(g["hex_lines"])
+    st, back = orc.decompress(buf, g["dtype"], 4)
+    assert st == orc.OK and back.tolist() == g["values"]
+
+
+@pytest.mark.parametrize("dtype", [orc.BF16, orc.FP32])
+def test_empty_input_is_header_and_one_index_entry(dtype):
+    buf = orc.compress(dtype, np.zeros(0, np.uint16 if dtype == orc.BF16 else np.uint32))
+    assert buf.size == 80
+    hdr, idx, recs = parse_buffer(buf)
+    assert hdr["n"] == 0 and hdr["C"] == 0 and hdr["sm_off"] == 80 and hdr["exp_off"] == 80 and hdr["total"] == 80
+    assert idx == [0] and recs == []
+    assert orc.max_compressed_size(dtype, 0) == 80
+    st, back = orc.decompress(buf, dtype, 0)
+    assert st == orc.OK and back.size == 0
+
+
+@pytest.mark.parametrize("dtype", [orc.BF16, orc.FP32])
+def test_random_bits_go_raw_and_hit_the_exact_bound(dtype):
+    n = 3 * (32768 if dtype == orc.BF16 else 65536) + 777
+    rng = np.random.default_rng(3)
+    bits = rng.integers(0, 1 << (16 if dtype == orc.BF16 else 32), n, dtype=np.uint64)
+    bits = bits.astype(np.uint16 if dtype == orc.BF16 else np.uint32)
+    buf = orc.compress(dtype, bits)
+    _, _, recs = parse_buffer(buf)
+    assert all(r["mode"] == 1 for r in recs)
+    assert buf.size == orc.max_compressed_size(dtype, n)
+    st, back = orc.decompress(buf, dtype, n)
+    assert st == orc.OK and np.array_equal(back, bits)
+
+
+def test_layout_offsets_and_zero_padding():
+    bits = workloads.bits_numpy(workloads.gradient_bucket(100_003, seed=7, special_frac=1e-3))
+    buf = orc.compress(orc.BF16, bits, chunk_bytes=2048)
+    hdr, idx, recs = parse_buffer(buf)
+    ce = 1024
+    C = (bits.size + ce - 1) // ce
+    assert hdr["C"] == C and hdr["chunk_elems"] == ce
+    sm_off = (64 + 8 * (C + 1) + 15) // 16 * 16
+    exp_off = (sm_off + bits.size + 15) // 16 * 16
+    assert hdr["sm_off"] == sm_off and hdr["exp_off"] == exp_off and hdr["total"] == buf.size
+    assert idx[0] == 0 and idx[-1] == buf.size - exp_off
+    assert all(b - a == r["bytes"] and (a % 16 == 0) for a, b, r in zip(idx, idx[1:], recs))
+    assert not buf[64 + 8 * (C + 1):sm_off].any() and not buf[sm_off + bits.size:exp_off].any()
+    e, sm = orc.split(orc.BF16, bits)
+    assert np.array_equal(buf[sm_off:sm_off + bits.size], sm)
+    for i, r in enumerate(recs):
+        raw = r["raw"]
+        if r["mode"] == 1:
+            n_i = r["n_values"]
+            assert np.array_equal(np.frombuffer(raw[16:16 + n_i], np.uint8), e[i * ce:i * ce + n_i])
+            assert not any(raw[16 + n_i:])
+        else:
+            end = (48 + 2 * r["nsym"] + 3) // 4 * 4 + 128 + 2 * r["n_words"]
+            assert not any(raw[end:]) and not any(raw[48 + 2 * r["nsym"]:(48 + 2 * r["nsym"] + 3) // 4 * 4])
+
+
+@pytest.mark.parametrize("n,mode", [(160, 1), (161, 1), (170, 1), (176, 1), (177, 0), (1000, 0)])
+def test_mode_choice_tie_goes_raw(n, mode):
+    # one exponent: the RANS record is align16(16 + 32 + 2*1 -> 52, + 128) =
+    # 192 bytes; RAW is align16(16 + n).  n in 161..176 ties at 192 -> RAW.
+    bits = np.full(n, (130 << 7) | 3, np.uint16)
+    _, _, recs = parse_buffer(orc.compress(orc.BF16, bits))
+    assert recs[0]["mode"] == mode
+    assert recs[0]["bytes"] == (192 if mode == 0 else (16 + n + 15) // 16 * 16)
+
+
+def test_mode_choice_small_chunks_go_raw():
+    # a 64-value chunk cannot pay for 176+ bytes of table and states
+    bits = workloads.bits_numpy(workloads.pr1())[:64]
+    _, _, recs = parse_buffer(orc.compress(orc.BF16, bits))
+    assert recs[0]["mode"] == 1 and recs[0]["bytes"] == 80
+
+
+# --------------------------------------------------------------------------
+# round trips over the edge cases the method has
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", [orc.BF16, orc.FP32])
+@pytest.mark.parametrize("n", [1, 31, 32, 33, 1000, 32768 + 5, 65536 * 2 + 31])
+def test_roundtrip_ragged_sizes(dtype, n):
+    if dtype == orc.BF16:
+        bits = workloads.bits_numpy(workloads.gradient_bucket(n, seed=n, special_frac=0.01))
+    else:
+        bits = workloads.bits_numpy(workloads.fp32_gradients(n, seed=n))
+    buf = orc.compress(dtype, bits)
+    assert buf.size <= orc.max_compressed_size(dtype, n)
+    st, back = orc.decompress(buf, dtype, n)
+    assert st == orc.OK and np.array_equal(back, bits)
+
+
+def test_roundtrip_all_256_exponents_in_one_chunk():
+    rng = np.random.default_rng(1)
+    e = np.concatenate([np.arange(256), rng.integers(0, 256, 30000)]).astype(np.uint16)
+    bits = ((rng.integers(0, 2, e.size) << 15) | (e << 7) | rng.integers(0, 128, e.size)).astype(np.uint16)
+    buf = orc.compress(orc.BF16, bits)
+    _, _, recs = parse_buffer(buf)
+    st, back = orc.decompress(buf, orc.BF16, bits.size)
+    assert st == orc.OK and np.array_equal(back, bits)
+
+
+def test_invalid_chunk_sizes_rejected():
+    assert orc.chunk_elems(orc.BF16, 65536) == 32768
+    assert orc.chunk_elems(orc.FP32, 0) == 65536
+    assert orc.chunk_elems(orc.BF16, 100) == 0  # not a multiple of 32 values
+    assert orc.chunk_elems(orc.BF16, (1 << 21) + 64) == 0  # more than 2^20 values
+
+
+# --------------------------------------------------------------------------
+# P7: corruption is reported, never decoded into garbage
+# --------------------------------------------------------------------------
+def _corruptions(buf):
+    hdr, idx, recs = parse_buffer(buf)
+    exp_off = hdr["exp_off"]
+    ri = next(i for i, r in enumerate(recs) if r["mode"] == 0)
+    base = exp_off + idx[ri]
+    rec = recs[ri]
+    tab_end = (48 + 2 * rec["nsym"] + 3) // 4 * 4
+
+    def patch(off, val, width):
+        b = buf.copy()
+        b[off:off + width] = np.frombuffer(int(val).to_bytes(width, "little"), np.uint8)
+        return b
+
+    yield "truncated", buf[:-16]
+    yield "magic", patch(0, 0x31505A56, 4)
+    yield "version", patch(4, 2, 2)
+    yield "dtype", patch(6, 2, 1)
+    yield "prob_bits", patch(7, 11, 1)
+    yield "count", patch(16, hdr["n"] + 1, 8)
+    yield "chunk_elems", patch(12, 1000, 4)
+    yield "sm_off", patch(32, hdr["sm_off"] + 16, 8)
+    yield "total", patch(48, buf.size + 16, 8)
+    yield "index_first", patch(64, 16, 8)
+    yield "index_unaligned", patch(64 + 8 * (ri + 1), idx[ri + 1] + 2, 8)
+    yield "index_decreasing", patch(64 + 8 * (ri + 1), idx[ri] - 16 if idx[ri] >= 16 else 0, 8)
+    yield "rec_mode", patch(base, 2, 1)
+    yield "rec_n_values", patch(base + 8, rec["n_values"] - 1, 4)
+    yield "rec_bytes", patch(base + 12, rec["bytes"] + 16, 4)
+    yield "rec_n_words_up", patch(base + 4, rec["n_words"] + 1, 4)
+    yield "rec_n_words_down", patch(base + 4, rec["n_words"] - 8, 4)
+    yield "nsym", patch(base + 2, rec["nsym"] + 1, 2)
+    yield "freq_sum", patch(base + 48, rec["f"][min(rec["f"])] + 1, 2)
+    yield "freq_zero", patch(base + 48, 0, 2)
+    yield "state_low", patch(base + tab_end, 65535, 4)
+    yield "state_value", patch(base + tab_end + 4, rec["states"][1] ^ 0x40, 4)
+    yield "word", patch(base + tab_end + 128 + 2 * (rec["n_words"] // 2), 0x1234, 2)
+
+
+def test_corruption_detected():
+    bits = workloads.bits_numpy(workloads.pr1())[:100_000]
+    buf = orc.compress(orc.BF16, bits)
+    seen = 0
+    for name, bad in _corruptions(buf):
+        st, _ = orc.decompress(bad, orc.BF16, bits.size)
+        assert st == orc.CORRUPT, name
+        seen += 1
+    assert seen == 23
+    st, _ = orc.decompress(buf, orc.FP32, bits.size // 2)
+    assert st == orc.CORRUPT
+    st, _ = orc.decompress(buf[:40], orc.BF16, bits.size)
+    assert st == orc.CORRUPT
