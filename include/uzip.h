@@ -1,0 +1,136 @@
+/*
+ * uzip.h -- C ABI of the MI355X (gfx950) lossless bf16/fp32 tensor codec.
+ *
+ * What it computes.  A tensor is shrunk losslessly before a send and restored
+ * bit for bit after the receive, with the communication API left unchanged
+ * (UCCL-Zip: Lossless Compression Supercharged GPU Communication, abstract).
+ * Each value's exponent field is split from its sign and mantissa bits and
+ * only the exponents are entropy-coded (same page, Figure 2 and its text);
+ * every chunk of the tensor builds its own frequency table, so chunks need no
+ * global coordination (Figure 5(b)).  The exponent coder is 32-lane
+ * interleaved rANS with a 2^12 table; sign+mantissa bytes are stored raw.
+ * The output is one self-describing buffer, header + payload, in the manner of
+ * NCCLZ's batch framing (NCCLZ: Compression-Enabled GPU Collectives with
+ * Decoupled Quantization and Entropy Coding, Sec. IV-D2), a chunk is stored
+ * RAW whenever coding it would not make it smaller (Sec. IV-C, Algorithm 1),
+ * and the receiver validates the header before decoding (Algorithm 2).
+ *
+ * Buffer layout (bitstream v1, little-endian, 16-byte aligned sections):
+ *   [0, 64)            header: magic "UZP1", version 1, dtype, prob_bits 12,
+ *                      lanes 32, raw bytes per value r, chunk_elems, N, C,
+ *                      sm_off, exp_off, total_bytes
+ *   [64, 64+8(C+1))    u64 record offsets (exclusive prefix sum of sizes)
+ *   [sm_off, +r*N)     sign+mantissa bytes of every value, in value order
+ *                      (bf16: 1 byte; fp32: 3 bytes little-endian)
+ *   [exp_off, total)   one record per chunk: a 16-byte record header, then
+ *                      either the rANS table, 32 final states and 16-bit words
+ *                      (mode RANS) or the chunk's raw exponent bytes (RAW).
+ *
+ * Memory and ownership.  Every pointer named d_* is device memory of the
+ * current HIP device; every h_* pointer is host memory.  The caller owns all
+ * buffers.  Device input/output/workspace pointers must be 16-byte aligned
+ * (a null input is allowed when its element count is 0).  The library
+ * allocates nothing: work memory comes from the caller's workspace, whose
+ * size the *_workspace_size functions give.  Host arrays need only live for
+ * the duration of the call.  Calls enqueue work on `stream` and return without
+ * synchronising it; results (d_out_size, d_status, output bytes) are valid
+ * once the stream's work has completed.  Calls on different streams are
+ * independent when their workspaces differ.
+ *
+ * Errors.  Argument errors are found on the host and returned at once, with
+ * nothing launched: UZIP_ERR_INVALID_ARGUMENT (bad dtype, null or misaligned
+ * pointer, chunk_bytes not a multiple of 32 values or above 2^20 values,
+ * workspace too small), UZIP_ERR_CAPACITY (output capacity below
+ * uzip_max_compressed_size).  Corrupt compressed input is found on the device
+ * and reported per buffer in d_status (0 = valid, else
+ * UZIP_ERR_CORRUPT_INPUT); the library never falls back to copying bytes it
+ * could not validate, and never writes outside [d_out, d_out + N*sizeof(T)).
+ * UZIP_ERR_DEVICE reports a failed HIP launch or copy.
+ */
+#ifndef UZIP_H
+#define UZIP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { UZIP_BF16 = 1, UZIP_FP32 = 2 } uzip_dtype;
+
+typedef enum {
+    UZIP_OK = 0,
+    UZIP_ERR_INVALID_ARGUMENT = 1,
+    UZIP_ERR_CAPACITY = 2,
+    UZIP_ERR_CORRUPT_INPUT = 3,
+    UZIP_ERR_DEVICE = 4,
+    UZIP_ERR_UNSUPPORTED = 5
+} uzip_status;
+
+/* Exact upper bound of the compressed size of num_elements values: the size
+ * the buffer has when every chunk is stored RAW (a chunk is coded only when
+ * that is strictly smaller).  chunk_bytes is the uncompressed chunk size
+ * (0 = default: 64 KiB for bf16, 256 KiB for fp32).  Pure host function;
+ * returns 0 for an invalid dtype or chunk size. */
+size_t uzip_max_compressed_size(uzip_dtype dtype, size_t num_elements, size_t chunk_bytes);
+
+/* Workspace bytes that uzip_compress or uzip_decompress needs for one buffer
+ * of num_elements values (the larger of the two).  0 for invalid arguments. */
+size_t uzip_workspace_size(uzip_dtype dtype, size_t num_elements, size_t chunk_bytes);
+
+/* Compress num_elements bf16/fp32 values at d_in (bit patterns, any values
+ * including NaN/Inf/denormals) into d_out (out_capacity bytes, at least
+ * uzip_max_compressed_size).  The exact compressed size is written to the
+ * device word *d_out_size.  Passages: UCCL-Zip Fig. 2 (exponent split),
+ * Fig. 5(b) (per-chunk local tables); NCCLZ Sec. IV-D2 (self-describing
+ * frame), Sec. IV-C (RAW when coding does not pay). */
+uzip_status uzip_compress(uzip_dtype dtype, const void *d_in, size_t num_elements, size_t chunk_bytes,
+                          void *d_out, size_t out_capacity, uint64_t *d_out_size,
+                          void *d_workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Decompress the buffer at d_in (in_bytes bytes available) holding
+ * num_elements values of `dtype`, as the receiver expects them, into d_out
+ * (num_elements * sizeof(T) bytes).  The buffer is validated on the device
+ * (header, record index, every record, and the rANS end state of every lane)
+ * and *d_status receives 0 or UZIP_ERR_CORRUPT_INPUT.  Passage: NCCLZ
+ * Algorithm 2 (parse and validate the header, then decode). */
+uzip_status uzip_decompress(const void *d_in, size_t in_bytes, uzip_dtype dtype, size_t num_elements,
+                            void *d_out, uint32_t *d_status,
+                            void *d_workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace for one batched call over num_buffers buffers whose element
+ * counts are h_num_elements[0..num_buffers) (the larger of the compress and
+ * decompress needs). */
+size_t uzip_workspace_size_batched(uzip_dtype dtype, size_t num_buffers, const size_t *h_num_elements,
+                                   size_t chunk_bytes);
+
+/* Compress num_buffers independent buffers in one set of launches.  Buffer b
+ * reads h_in[b] (h_num_elements[b] values) and writes its own self-describing
+ * buffer to h_out[b] (capacity h_out_capacity[b]); its size goes to
+ * d_out_sizes[b].  The result for each buffer is byte-identical to a
+ * uzip_compress call on that buffer alone.  Same passages as uzip_compress;
+ * the batching serves many small messages (UCCL-Zip Fig. 11, KV transfer)
+ * and whole weight sets (Fig. 10, RL weight sync). */
+uzip_status uzip_compress_batched(uzip_dtype dtype, size_t num_buffers,
+                                  const void *const *h_in, const size_t *h_num_elements, size_t chunk_bytes,
+                                  void *const *h_out, const size_t *h_out_capacity, uint64_t *d_out_sizes,
+                                  void *d_workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Decompress num_buffers buffers in one set of launches; d_status[b] receives
+ * buffer b's validation result.  Same passage as uzip_decompress. */
+uzip_status uzip_decompress_batched(uzip_dtype dtype, size_t num_buffers,
+                                    const void *const *h_in, const size_t *h_in_bytes,
+                                    const size_t *h_num_elements, void *const *h_out, uint32_t *d_status,
+                                    void *d_workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Static English name of a status code. */
+const char *uzip_status_string(uzip_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* UZIP_H */

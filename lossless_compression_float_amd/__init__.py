@@ -1,0 +1,244 @@
+"""Python binding of the uzip C ABI (include/uzip.h): lossless bf16/fp32
+tensor compression on MI355X (gfx950).
+
+The functions named ``uzip_*`` are the C entry points with the same names and
+arguments (plain integers and device pointers), marshalled through ctypes.
+Every step of the codec runs in the HIP kernels of ``libuzip.so``; this module
+only allocates outputs and workspaces through torch (device memory and the
+current stream are all torch is used for) and passes pointers.
+
+``compress(t)`` / ``decompress(buf, dtype, n)`` and their batched forms are
+convenience wrappers over those calls.  There is no CPU fallback: loading
+fails loudly when the library is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # loads the HIP runtime the library links against
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libuzip.so")
+
+UZIP_BF16 = 1
+UZIP_FP32 = 2
+UZIP_OK = 0
+UZIP_ERR_INVALID_ARGUMENT = 1
+UZIP_ERR_CAPACITY = 2
+UZIP_ERR_CORRUPT_INPUT = 3
+UZIP_ERR_DEVICE = 4
+UZIP_ERR_UNSUPPORTED = 5
+
+EXPORTED = (
+    "uzip_max_compressed_size",
+    "uzip_workspace_size",
+    "uzip_compress",
+    "uzip_decompress",
+    "uzip_workspace_size_batched",
+    "uzip_compress_batched",
+    "uzip_decompress_batched",
+    "uzip_status_string",
+)
+
+_lib = None
+
+
+class UzipError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__("%s failed: %s (status %d)" % (what, uzip_status_string(status), status))
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libuzip.so (built in-tree by __graft_entry__.build())."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError("libuzip.so is not built (%s); run __graft_entry__.build()" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        sz, i32, u64p, vp = ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p
+        L.uzip_max_compressed_size.restype = sz
+        L.uzip_max_compressed_size.argtypes = [i32, sz, sz]
+        L.uzip_workspace_size.restype = sz
+        L.uzip_workspace_size.argtypes = [i32, sz, sz]
+        L.uzip_compress.restype = i32
+        L.uzip_compress.argtypes = [i32, vp, sz, sz, vp, sz, u64p, vp, sz, vp]
+        L.uzip_decompress.restype = i32
+        L.uzip_decompress.argtypes = [vp, sz, i32, sz, vp, vp, vp, sz, vp]
+        L.uzip_workspace_size_batched.restype = sz
+        L.uzip_workspace_size_batched.argtypes = [i32, sz, vp, sz]
+        L.uzip_compress_batched.restype = i32
+        L.uzip_compress_batched.argtypes = [i32, sz, vp, vp, sz, vp, vp, u64p, vp, sz, vp]
+        L.uzip_decompress_batched.restype = i32
+        L.uzip_decompress_batched.argtypes = [i32, sz, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.uzip_status_string.restype = ctypes.c_char_p
+        L.uzip_status_string.argtypes = [i32]
+        _lib = L
+    return _lib
+
+
+# ---- the C entry points, same names and arguments --------------------------
+def uzip_max_compressed_size(dtype: int, num_elements: int, chunk_bytes: int = 0) -> int:
+    return int(lib().uzip_max_compressed_size(dtype, num_elements, chunk_bytes))
+
+
+def uzip_workspace_size(dtype: int, num_elements: int, chunk_bytes: int = 0) -> int:
+    return int(lib().uzip_workspace_size(dtype, num_elements, chunk_bytes))
+
+
+def uzip_compress(dtype, d_in, num_elements, chunk_bytes, d_out, out_capacity, d_out_size, d_workspace,
+                  workspace_bytes, stream) -> int:
+    return int(lib().uzip_compress(dtype, d_in, num_elements, chunk_bytes, d_out, out_capacity, d_out_size,
+                                   d_workspace, workspace_bytes, stream))
+
+
+def uzip_decompress(d_in, in_bytes, dtype, num_elements, d_out, d_status, d_workspace, workspace_bytes,
+                    stream) -> int:
+    return int(lib().uzip_decompress(d_in, in_bytes, dtype, num_elements, d_out, d_status, d_workspace,
+                                     workspace_bytes, stream))
+
+
+def _sizes(vals):
+    return (ctypes.c_size_t * len(vals))(*vals)
+
+
+def _ptrs(vals):
+    return (ctypes.c_void_p * len(vals))(*vals)
+
+
+def uzip_workspace_size_batched(dtype: int, num_elements, chunk_bytes: int = 0) -> int:
+    arr = _sizes(num_elements)
+    return int(lib().uzip_workspace_size_batched(dtype, len(num_elements), ctypes.cast(arr, ctypes.c_void_p),
+                                                 chunk_bytes))
+
+
+def uzip_compress_batched(dtype, h_in, h_num_elements, chunk_bytes, h_out, h_out_capacity, d_out_sizes, d_workspace,
+                          workspace_bytes, stream) -> int:
+    a_in, a_n, a_out, a_cap = _ptrs(h_in), _sizes(h_num_elements), _ptrs(h_out), _sizes(h_out_capacity)
+    v = ctypes.c_void_p
+    return int(lib().uzip_compress_batched(dtype, len(h_in), ctypes.cast(a_in, v), ctypes.cast(a_n, v), chunk_bytes,
+                                           ctypes.cast(a_out, v), ctypes.cast(a_cap, v), d_out_sizes, d_workspace,
+                                           workspace_bytes, stream))
+
+
+def uzip_decompress_batched(dtype, h_in, h_in_bytes, h_num_elements, h_out, d_status, d_workspace, workspace_bytes,
+                            stream) -> int:
+    a_in, a_b, a_n, a_out = _ptrs(h_in), _sizes(h_in_bytes), _sizes(h_num_elements), _ptrs(h_out)
+    v = ctypes.c_void_p
+    return int(lib().uzip_decompress_batched(dtype, len(h_in), ctypes.cast(a_in, v), ctypes.cast(a_b, v),
+                                             ctypes.cast(a_n, v), ctypes.cast(a_out, v), d_status, d_workspace,
+                                             workspace_bytes, stream))
+
+
+def uzip_status_string(status: int) -> str:
+    return lib().uzip_status_string(status).decode()
+
+
+# ---- torch-level convenience wrappers ---------------------------------------
+def dtype_code(t: torch.dtype) -> int:
+    if t == torch.bfloat16:
+        return UZIP_BF16
+    if t == torch.float32:
+        return UZIP_FP32
+    raise TypeError("uzip compresses bfloat16 or float32 tensors, not %s" % t)
+
+
+def torch_dtype(code: int) -> torch.dtype:
+    return {UZIP_BF16: torch.bfloat16, UZIP_FP32: torch.float32}[code]
+
+
+def _stream(stream=None) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return int(s.cuda_stream)
+
+
+def _check(st: int, what: str):
+    if st != UZIP_OK:
+        raise UzipError(st, what)
+
+
+def workspace(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+
+def compress(t: torch.Tensor, chunk_bytes: int = 0, out: torch.Tensor | None = None,
+             ws: torch.Tensor | None = None, out_size: torch.Tensor | None = None, stream=None):
+    """Compress a contiguous bf16/fp32 CUDA tensor.  Returns (buffer, size)
+    where `buffer` has capacity uzip_max_compressed_size and `size` is a
+    one-element int64 device tensor holding the exact compressed size."""
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError("compress needs a contiguous device tensor")
+    code = dtype_code(t.dtype)
+    n = t.numel()
+    cap = uzip_max_compressed_size(code, n, chunk_bytes)
+    if cap == 0:
+        raise ValueError("invalid chunk_bytes %d" % chunk_bytes)
+    if out is None:
+        out = torch.empty(cap, dtype=torch.uint8, device=t.device)
+    if out_size is None:
+        out_size = torch.empty(1, dtype=torch.int64, device=t.device)
+    wsz = uzip_workspace_size(code, n, chunk_bytes)
+    if ws is None:
+        ws = workspace(wsz, t.device)
+    st = uzip_compress(code, t.data_ptr() if n else None, n, chunk_bytes, out.data_ptr(), out.numel(),
+                       out_size.data_ptr(), ws.data_ptr(), ws.numel(), _stream(stream))
+    _check(st, "uzip_compress")
+    return out, out_size
+
+
+def decompress(buf: torch.Tensor, dtype: torch.dtype, n: int, in_bytes: int | None = None,
+               out: torch.Tensor | None = None, status: torch.Tensor | None = None,
+               ws: torch.Tensor | None = None, stream=None):
+    """Decompress into a new (or given) tensor of n values.  Returns
+    (values, status) where status is a one-element int32 device tensor
+    (0 = valid, 3 = corrupt input)."""
+    code = dtype_code(dtype)
+    if out is None:
+        out = torch.empty(n, dtype=dtype, device=buf.device)
+    if status is None:
+        status = torch.empty(1, dtype=torch.int32, device=buf.device)
+    if ws is None:
+        ws = workspace(uzip_workspace_size(code, 0, 0), buf.device)
+    nb = buf.numel() if in_bytes is None else in_bytes
+    st = uzip_decompress(buf.data_ptr() if nb else None, nb, code, n, out.data_ptr() if n else None,
+                         status.data_ptr(), ws.data_ptr(), ws.numel(), _stream(stream))
+    _check(st, "uzip_decompress")
+    return out, status
+
+
+def compress_batched(tensors, chunk_bytes: int = 0, outs=None, ws=None, out_sizes=None, stream=None):
+    """Compress a list of same-dtype contiguous device tensors in one call.
+    Returns (buffers, sizes[int64 tensor of len(tensors)])."""
+    code = dtype_code(tensors[0].dtype)
+    dev = tensors[0].device
+    ns = [t.numel() for t in tensors]
+    caps = [uzip_max_compressed_size(code, n, chunk_bytes) for n in ns]
+    if outs is None:
+        outs = [torch.empty(c, dtype=torch.uint8, device=dev) for c in caps]
+    if out_sizes is None:
+        out_sizes = torch.empty(len(tensors), dtype=torch.int64, device=dev)
+    if ws is None:
+        ws = workspace(uzip_workspace_size_batched(code, ns, chunk_bytes), dev)
+    st = uzip_compress_batched(code, [t.data_ptr() if t.numel() else 0 for t in tensors], ns, chunk_bytes,
+                               [o.data_ptr() for o in outs], [o.numel() for o in outs], out_sizes.data_ptr(),
+                               ws.data_ptr(), ws.numel(), _stream(stream))
+    _check(st, "uzip_compress_batched")
+    return outs, out_sizes
+
+
+def decompress_batched(bufs, dtype: torch.dtype, ns, in_bytes=None, outs=None, status=None, ws=None, stream=None):
+    code = dtype_code(dtype)
+    dev = bufs[0].device
+    if outs is None:
+        outs = [torch.empty(n, dtype=dtype, device=dev) for n in ns]
+    if status is None:
+        status = torch.empty(len(bufs), dtype=torch.int32, device=dev)
+    if ws is None:
+        ws = workspace(uzip_workspace_size_batched(code, list(ns), 0), dev)
+    nbs = [b.numel() for b in bufs] if in_bytes is None else list(in_bytes)
+    st = uzip_decompress_batched(code, [b.data_ptr() for b in bufs], nbs, list(ns),
+                                 [o.data_ptr() if o.numel() else 0 for o in outs], status.data_ptr(), ws.data_ptr(),
+                                 ws.numel(), _stream(stream))
+    _check(st, "uzip_decompress_batched")
+    return outs, status

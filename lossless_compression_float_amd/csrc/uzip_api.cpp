@@ -1,0 +1,279 @@
+// uzip_api.cpp -- the C ABI declared in include/uzip.h: argument checks,
+// layout and workspace carving, descriptor upload, and launches on the
+// caller's stream.  Nothing here synchronises the stream or allocates memory.
+#include <stdint.h>
+#include <string.h>
+
+#include <algorithm>
+#include <vector>
+
+#include <hip/hip_runtime.h>
+
+#include "uzip.h"
+#include "uzip_common.hpp"
+#include "uzip_kernels.hpp"
+
+using namespace uzip;
+
+namespace {
+
+constexpr uint64_t kWsAlign = 256;
+
+uint64_t al(uint64_t v) { return (v + kWsAlign - 1) / kWsAlign * kWsAlign; }
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool dtype_ok(uzip_dtype d) { return d == UZIP_BF16 || d == UZIP_FP32; }
+
+// chunk_elems of a call, or 0 when the chunk size is invalid: the chunk must
+// hold a multiple of 32 values (whole rANS steps) and at most 2^20 values
+// (so that count * (4096 - nsym) fits 32 bits in the normalisation).
+uint64_t chunk_elems_of(uzip_dtype dtype, size_t chunk_bytes) {
+    if (!dtype_ok(dtype)) return 0;
+    const uint64_t eb = elem_bytes(dtype);
+    if (chunk_bytes == 0) chunk_bytes = dtype == UZIP_BF16 ? 65536 : 262144;
+    if (chunk_bytes % (32 * eb) != 0) return 0;
+    const uint64_t ce = chunk_bytes / eb;
+    return (ce == 0 || ce > kMaxChunkElems) ? 0 : ce;
+}
+
+struct EncWs {
+    uint64_t descs, sizes, tile_sums, tile_offs, slots, slot_stride, ntiles, bytes;
+};
+
+EncWs enc_ws(uint64_t nbuf, uint64_t chunks, uint64_t ce) {
+    EncWs w{};
+    uint64_t o = 0;
+    w.descs = o;
+    o += al(nbuf > 1 ? nbuf * sizeof(EncDesc) : 0);
+    w.sizes = o;
+    o += al(chunks * 4);
+    w.ntiles = (chunks + kTile - 1) / kTile;
+    w.tile_sums = o;
+    o += al(w.ntiles * 8);
+    w.tile_offs = o;
+    o += al((w.ntiles + 1) * 8);
+    // A slot holds the chunk's RAW record, and at least the largest RANS
+    // prefix (header, bitmap, 256 frequencies, states), which the encoder
+    // writes before it knows whether the chunk will be stored RAW.
+    w.slot_stride = std::max<uint64_t>(align16(kRecHeaderBytes + ce), align16(words_offset(256)));
+    w.slots = o;
+    o += chunks * w.slot_stride;
+    w.bytes = o + kWsAlign;  // slack: the caller's pointer need only be 16-byte aligned
+    return w;
+}
+
+struct DecWs {
+    uint64_t descs, info, chunk_first, bytes;
+};
+
+DecWs dec_ws(uint64_t nbuf) {
+    DecWs w{};
+    uint64_t o = 0;
+    w.descs = o;
+    o += al(nbuf > 1 ? nbuf * sizeof(DecDesc) : 0);
+    w.info = o;
+    o += al(nbuf * sizeof(DecInfo));
+    w.chunk_first = o;
+    o += al((nbuf + 1) * 8);
+    w.bytes = o + kWsAlign;
+    return w;
+}
+
+uint8_t *ws_base(void *ws) {
+    const uintptr_t p = reinterpret_cast<uintptr_t>(ws);
+    return reinterpret_cast<uint8_t *>((p + kWsAlign - 1) & ~uintptr_t(kWsAlign - 1));
+}
+
+uint64_t max_size(uzip_dtype dtype, uint64_t n, uint64_t ce) {
+    const Layout l = layout_of(dtype, n, ce);
+    if (l.chunks == 0) return l.exp_off;
+    const uint64_t last = n - (l.chunks - 1) * ce;
+    return l.exp_off + (l.chunks - 1) * raw_record_bytes(ce) + raw_record_bytes(last);
+}
+
+// Shared body of the single and batched compress calls.
+uzip_status compress_impl(uzip_dtype dtype, uint64_t ce, std::vector<EncDesc> &descs, uint64_t chunks,
+                          void *d_workspace, size_t workspace_bytes, hipStream_t stream) {
+    const uint32_t nbuf = (uint32_t)descs.size();
+    const EncWs w = enc_ws(nbuf, chunks, ce);
+    if (d_workspace == nullptr || workspace_bytes < w.bytes || !aligned(d_workspace, 16))
+        return UZIP_ERR_INVALID_ARGUMENT;
+    uint8_t *base = ws_base(d_workspace);
+    EncParams ep{};
+    ep.nbuf = nbuf;
+    ep.chunk_elems = (uint32_t)ce;
+    ep.total_chunks = chunks;
+    ep.slots = base + w.slots;
+    ep.slot_stride = w.slot_stride;
+    ep.rec_sizes = reinterpret_cast<uint32_t *>(base + w.sizes);
+    ep.dtype = dtype;
+    bool any_empty = false;
+    for (const EncDesc &d : descs) any_empty |= d.n == 0;
+    if (nbuf == 1) {
+        ep.single = descs[0];
+        ep.descs = nullptr;
+    } else {
+        EncDesc *dd = reinterpret_cast<EncDesc *>(base + w.descs);
+        // Pageable host -> device copy: the runtime stages the bytes before
+        // returning, so `descs` may be released once this call returns.
+        if (hipMemcpyAsync(dd, descs.data(), nbuf * sizeof(EncDesc), hipMemcpyHostToDevice, stream) != hipSuccess)
+            return UZIP_ERR_DEVICE;
+        ep.descs = dd;
+    }
+    CompactParams cp{};
+    cp.descs = ep.descs;
+    cp.single = ep.single;
+    cp.nbuf = nbuf;
+    cp.chunk_elems = ep.chunk_elems;
+    cp.total_chunks = chunks;
+    cp.slots = ep.slots;
+    cp.slot_stride = ep.slot_stride;
+    cp.rec_sizes = ep.rec_sizes;
+    cp.tile_offs = reinterpret_cast<const uint64_t *>(base + w.tile_offs);
+    cp.dtype = dtype;
+    const hipError_t e = launch_compress(ep, cp, reinterpret_cast<uint64_t *>(base + w.tile_sums),
+                                         reinterpret_cast<uint64_t *>(base + w.tile_offs), w.ntiles, any_empty, stream);
+    return e == hipSuccess ? UZIP_OK : UZIP_ERR_DEVICE;
+}
+
+uzip_status decompress_impl(uzip_dtype dtype, std::vector<DecDesc> &descs, uint32_t *d_status, void *d_workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+    const uint32_t nbuf = (uint32_t)descs.size();
+    const DecWs w = dec_ws(nbuf);
+    if (d_workspace == nullptr || workspace_bytes < w.bytes || !aligned(d_workspace, 16))
+        return UZIP_ERR_INVALID_ARGUMENT;
+    uint8_t *base = ws_base(d_workspace);
+    uint64_t max_chunks = 0;
+    for (const DecDesc &d : descs) max_chunks += (d.n + 31) / 32;  // chunks hold >= 32 values
+    DecParams vp{};
+    vp.nbuf = nbuf;
+    vp.dtype = dtype;
+    vp.info = reinterpret_cast<DecInfo *>(base + w.info);
+    vp.chunk_first = reinterpret_cast<uint64_t *>(base + w.chunk_first);
+    vp.status = d_status;
+    if (nbuf == 1) {
+        vp.single = descs[0];
+    } else {
+        DecDesc *dd = reinterpret_cast<DecDesc *>(base + w.descs);
+        if (hipMemcpyAsync(dd, descs.data(), nbuf * sizeof(DecDesc), hipMemcpyHostToDevice, stream) != hipSuccess)
+            return UZIP_ERR_DEVICE;
+        vp.descs = dd;
+    }
+    DecodeParams dp{};
+    dp.descs = vp.descs;
+    dp.single = vp.single;
+    dp.nbuf = nbuf;
+    dp.info = vp.info;
+    dp.chunk_first = vp.chunk_first;
+    dp.status = d_status;
+    const hipError_t e = launch_decompress(vp, dp, dtype, max_chunks, stream);
+    return e == hipSuccess ? UZIP_OK : UZIP_ERR_DEVICE;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t uzip_max_compressed_size(uzip_dtype dtype, size_t num_elements, size_t chunk_bytes) {
+    const uint64_t ce = chunk_elems_of(dtype, chunk_bytes);
+    return ce ? (size_t)max_size(dtype, num_elements, ce) : 0;
+}
+
+size_t uzip_workspace_size(uzip_dtype dtype, size_t num_elements, size_t chunk_bytes) {
+    const uint64_t ce = chunk_elems_of(dtype, chunk_bytes);
+    if (!ce) return 0;
+    const uint64_t chunks = (num_elements + ce - 1) / ce;
+    return (size_t)std::max(enc_ws(1, chunks, ce).bytes, dec_ws(1).bytes);
+}
+
+size_t uzip_workspace_size_batched(uzip_dtype dtype, size_t num_buffers, const size_t *h_num_elements,
+                                   size_t chunk_bytes) {
+    const uint64_t ce = chunk_elems_of(dtype, chunk_bytes);
+    if (!ce || num_buffers == 0 || num_buffers > 0xFFFFFFFFull || h_num_elements == nullptr) return 0;
+    uint64_t chunks = 0;
+    for (size_t b = 0; b < num_buffers; ++b) chunks += (h_num_elements[b] + ce - 1) / ce;
+    return (size_t)std::max(enc_ws(num_buffers, chunks, ce).bytes, dec_ws(num_buffers).bytes);
+}
+
+uzip_status uzip_compress(uzip_dtype dtype, const void *d_in, size_t num_elements, size_t chunk_bytes, void *d_out,
+                          size_t out_capacity, uint64_t *d_out_size, void *d_workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
+    const uint64_t ce = chunk_elems_of(dtype, chunk_bytes);
+    if (!ce) return UZIP_ERR_INVALID_ARGUMENT;
+    if (num_elements > 0 && (d_in == nullptr || !aligned(d_in, 16))) return UZIP_ERR_INVALID_ARGUMENT;
+    if (d_out == nullptr || !aligned(d_out, 16) || d_out_size == nullptr || !aligned(d_out_size, 8))
+        return UZIP_ERR_INVALID_ARGUMENT;
+    if (out_capacity < max_size(dtype, num_elements, ce)) return UZIP_ERR_CAPACITY;
+    const Layout l = layout_of(dtype, num_elements, ce);
+    std::vector<EncDesc> descs(1);
+    descs[0] = EncDesc{static_cast<const uint8_t *>(d_in), static_cast<uint8_t *>(d_out), d_out_size, num_elements,
+                       0, l.sm_off, l.exp_off, l.chunks};
+    return compress_impl(dtype, ce, descs, l.chunks, d_workspace, workspace_bytes, stream);
+}
+
+uzip_status uzip_decompress(const void *d_in, size_t in_bytes, uzip_dtype dtype, size_t num_elements, void *d_out,
+                            uint32_t *d_status, void *d_workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (!dtype_ok(dtype)) return UZIP_ERR_INVALID_ARGUMENT;
+    if (in_bytes > 0 && (d_in == nullptr || !aligned(d_in, 16))) return UZIP_ERR_INVALID_ARGUMENT;
+    if (num_elements > 0 && (d_out == nullptr || !aligned(d_out, 16))) return UZIP_ERR_INVALID_ARGUMENT;
+    if (d_status == nullptr || !aligned(d_status, 4)) return UZIP_ERR_INVALID_ARGUMENT;
+    std::vector<DecDesc> descs(1);
+    descs[0] = DecDesc{static_cast<const uint8_t *>(d_in), static_cast<uint8_t *>(d_out), in_bytes, num_elements};
+    return decompress_impl(dtype, descs, d_status, d_workspace, workspace_bytes, stream);
+}
+
+uzip_status uzip_compress_batched(uzip_dtype dtype, size_t num_buffers, const void *const *h_in,
+                                  const size_t *h_num_elements, size_t chunk_bytes, void *const *h_out,
+                                  const size_t *h_out_capacity, uint64_t *d_out_sizes, void *d_workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
+    const uint64_t ce = chunk_elems_of(dtype, chunk_bytes);
+    if (!ce || num_buffers == 0 || num_buffers > 0xFFFFFFFFull) return UZIP_ERR_INVALID_ARGUMENT;
+    if (!h_in || !h_num_elements || !h_out || !h_out_capacity || !d_out_sizes || !aligned(d_out_sizes, 8))
+        return UZIP_ERR_INVALID_ARGUMENT;
+    std::vector<EncDesc> descs(num_buffers);
+    uint64_t chunks = 0;
+    for (size_t b = 0; b < num_buffers; ++b) {
+        const uint64_t n = h_num_elements[b];
+        if (n > 0 && (h_in[b] == nullptr || !aligned(h_in[b], 16))) return UZIP_ERR_INVALID_ARGUMENT;
+        if (h_out[b] == nullptr || !aligned(h_out[b], 16)) return UZIP_ERR_INVALID_ARGUMENT;
+        if (h_out_capacity[b] < max_size(dtype, n, ce)) return UZIP_ERR_CAPACITY;
+        const Layout l = layout_of(dtype, n, ce);
+        descs[b] = EncDesc{static_cast<const uint8_t *>(h_in[b]), static_cast<uint8_t *>(h_out[b]), d_out_sizes + b, n,
+                           chunks, l.sm_off, l.exp_off, l.chunks};
+        chunks += l.chunks;
+    }
+    return compress_impl(dtype, ce, descs, chunks, d_workspace, workspace_bytes, stream);
+}
+
+uzip_status uzip_decompress_batched(uzip_dtype dtype, size_t num_buffers, const void *const *h_in,
+                                    const size_t *h_in_bytes, const size_t *h_num_elements, void *const *h_out,
+                                    uint32_t *d_status, void *d_workspace, size_t workspace_bytes,
+                                    hipStream_t stream) {
+    if (!dtype_ok(dtype) || num_buffers == 0 || num_buffers > 0xFFFFFFFFull) return UZIP_ERR_INVALID_ARGUMENT;
+    if (!h_in || !h_in_bytes || !h_num_elements || !h_out || !d_status || !aligned(d_status, 4))
+        return UZIP_ERR_INVALID_ARGUMENT;
+    std::vector<DecDesc> descs(num_buffers);
+    for (size_t b = 0; b < num_buffers; ++b) {
+        if (h_in_bytes[b] > 0 && (h_in[b] == nullptr || !aligned(h_in[b], 16))) return UZIP_ERR_INVALID_ARGUMENT;
+        if (h_num_elements[b] > 0 && (h_out[b] == nullptr || !aligned(h_out[b], 16)))
+            return UZIP_ERR_INVALID_ARGUMENT;
+        descs[b] = DecDesc{static_cast<const uint8_t *>(h_in[b]), static_cast<uint8_t *>(h_out[b]), h_in_bytes[b],
+                           h_num_elements[b]};
+    }
+    return decompress_impl(dtype, descs, d_status, d_workspace, workspace_bytes, stream);
+}
+
+const char *uzip_status_string(uzip_status s) {
+    switch (s) {
+        case UZIP_OK: return "ok";
+        case UZIP_ERR_INVALID_ARGUMENT: return "invalid argument";
+        case UZIP_ERR_CAPACITY: return "output capacity below uzip_max_compressed_size";
+        case UZIP_ERR_CORRUPT_INPUT: return "corrupt compressed input";
+        case UZIP_ERR_DEVICE: return "HIP launch or copy failed";
+        case UZIP_ERR_UNSUPPORTED: return "unsupported";
+    }
+    return "unknown status";
+}
+
+}  // extern "C"

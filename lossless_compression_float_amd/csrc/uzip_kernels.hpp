@@ -1,0 +1,61 @@
+// uzip_kernels.hpp -- kernel parameter blocks and launchers (internal).
+#pragma once
+
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+#include "uzip_common.hpp"
+
+namespace uzip {
+
+struct EncParams {
+    const EncDesc *descs;  // device array, used when nbuf > 1
+    EncDesc single;        // used when nbuf == 1
+    uint32_t nbuf;
+    uint32_t chunk_elems;
+    uint64_t total_chunks;  // chunks over all buffers
+    uint8_t *slots;         // one slot of slot_stride bytes per chunk
+    uint64_t slot_stride;
+    uint32_t *rec_sizes;    // record bytes per chunk
+    int dtype;
+};
+
+struct CompactParams {
+    const EncDesc *descs;
+    EncDesc single;
+    uint32_t nbuf;
+    uint32_t chunk_elems;
+    uint64_t total_chunks;
+    const uint8_t *slots;
+    uint64_t slot_stride;
+    const uint32_t *rec_sizes;
+    const uint64_t *tile_offs;  // exclusive prefix of the tile sums
+    int dtype;
+};
+
+struct DecParams {
+    const DecDesc *descs;
+    DecDesc single;
+    uint32_t nbuf;
+    int dtype;
+    DecInfo *info;
+    uint64_t *chunk_first;  // nbuf + 1 entries
+    uint32_t *status;
+};
+
+struct DecodeParams {
+    const DecDesc *descs;
+    DecDesc single;
+    uint32_t nbuf;
+    const DecInfo *info;
+    const uint64_t *chunk_first;
+    uint32_t *status;
+};
+
+hipError_t launch_compress(const EncParams &ep, const CompactParams &cp, uint64_t *tile_sums, uint64_t *tile_offs,
+                           uint64_t ntiles, bool any_empty, hipStream_t stream);
+hipError_t launch_decompress(const DecParams &vp, const DecodeParams &dp, int dtype, uint64_t max_chunks,
+                             hipStream_t stream);
+
+}  // namespace uzip

@@ -1,0 +1,123 @@
+"""The C ABI without a GPU: the library loads, exports every entry point that
+include/uzip.h declares, its host-only size functions agree with the layout
+the oracle writes, and argument errors are returned before anything is
+launched (no call here reaches the device)."""
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import lossless_compression_float_amd as uz
+import oracle as orc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "uzip.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(uzip_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_names():
+    assert declared_functions() == sorted(uz.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.check_output(["nm", "-D", "--defined-only", uz.LIB_PATH], text=True)
+    syms = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for name in declared_functions():
+        assert name in syms, name
+        assert hasattr(uz.lib(), name)
+
+
+def test_library_has_gfx950_code_object():
+    # the offload bundle of our own build names its target triple
+    assert b"amdgcn-amd-amdhsa--gfx950" in open(uz.LIB_PATH, "rb").read()
+
+
+@pytest.mark.parametrize("dtype", [uz.UZIP_BF16, uz.UZIP_FP32])
+@pytest.mark.parametrize("chunk_bytes", [0, 4096, 65536, 262144])
+def test_max_compressed_size_matches_oracle(dtype, chunk_bytes):
+    for n in [0, 1, 31, 32, 33, 1000, 32767, 32768, 32769, 65536 * 3 + 17, 268_435_456, 8_030_257_152]:
+        assert uz.uzip_max_compressed_size(dtype, n, chunk_bytes) == orc.max_compressed_size(dtype, n, chunk_bytes)
+
+
+def test_size_functions_reject_invalid_arguments():
+    assert uz.uzip_max_compressed_size(3, 100, 0) == 0
+    assert uz.uzip_max_compressed_size(uz.UZIP_BF16, 100, 100) == 0
+    assert uz.uzip_max_compressed_size(uz.UZIP_BF16, 100, (1 << 21) + 64) == 0
+    assert uz.uzip_workspace_size(uz.UZIP_FP32, 100, 8) == 0
+    assert uz.uzip_workspace_size(uz.UZIP_BF16, 0, 0) > 0
+    assert uz.uzip_workspace_size_batched(uz.UZIP_BF16, [], 0) == 0
+
+
+def test_workspace_grows_with_chunks():
+    a = uz.uzip_workspace_size(uz.UZIP_BF16, 1 << 20, 0)
+    b = uz.uzip_workspace_size(uz.UZIP_BF16, 1 << 22, 0)
+    assert b > a >= 32 * (32768 + 16)
+    assert uz.uzip_workspace_size_batched(uz.UZIP_BF16, [1 << 20, 1 << 22], 0) >= a + b - 4096
+
+
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: every call below fails its checks first
+
+
+def test_compress_argument_errors_return_synchronously():
+    n = 1000
+    cap = uz.uzip_max_compressed_size(uz.UZIP_BF16, n)
+    ws = uz.uzip_workspace_size(uz.UZIP_BF16, n)
+    call = lambda **kw: uz.uzip_compress(**{**dict(dtype=uz.UZIP_BF16, d_in=FAKE, num_elements=n, chunk_bytes=0,
+                                                     d_out=FAKE, out_capacity=cap, d_out_size=FAKE,
+                                                     d_workspace=FAKE, workspace_bytes=ws - 1, stream=None), **kw})
+    assert call(dtype=7) == uz.UZIP_ERR_INVALID_ARGUMENT
+    assert call(chunk_bytes=100) == uz.UZIP_ERR_INVALID_ARGUMENT
+    assert call(d_in=None) == uz.UZIP_ERR_INVALID_ARGUMENT
+    assert call(d_in=FAKE + 8) == uz.UZIP_ERR_INVALID_ARGUMENT
+    assert call(d_out=None) == uz.UZIP_ERR_INVALID_ARGUMENT
+    assert call(d_out_size=None) == uz.UZIP_ERR_INVALID_ARGUMENT
+    assert call(out_capacity=cap - 1) == uz.UZIP_ERR_CAPACITY
+    assert call() == uz.UZIP_ERR_INVALID_ARGUMENT  # workspace one byte short
+    assert call(d_workspace=None, workspace_bytes=ws) == uz.UZIP_ERR_INVALID_ARGUMENT
+
+
+def test_decompress_argument_errors_return_synchronously():
+    ws = uz.uzip_workspace_size(uz.UZIP_BF16, 0)
+    call = lambda **kw: uz.uzip_decompress(**{**dict(d_in=FAKE, in_bytes=1000, dtype=uz.UZIP_BF16, num_elements=10,
+                                                       d_out=FAKE, d_status=FAKE, d_workspace=FAKE,
+                                                       workspace_bytes=ws - 1, stream=None), **kw})
+    assert call(dtype=0) == uz.UZIP_ERR_INVALID_ARGUMENT
+    assert call(d_in=None) == uz.UZIP_ERR_INVALID_ARGUMENT
+    assert call(d_out=FAKE + 4) == uz.UZIP_ERR_INVALID_ARGUMENT
+    assert call(d_status=None) == uz.UZIP_ERR_INVALID_ARGUMENT
+    assert call() == uz.UZIP_ERR_INVALID_ARGUMENT
+
+
+def test_batched_argument_errors_return_synchronously():
+    ns = [100, 0, 5000]
+    caps = [uz.uzip_max_compressed_size(uz.UZIP_BF16, n) for n in ns]
+    ws = uz.uzip_workspace_size_batched(uz.UZIP_BF16, ns)
+    base = dict(dtype=uz.UZIP_BF16, h_in=[FAKE, 0, FAKE], h_num_elements=ns, chunk_bytes=0, h_out=[FAKE] * 3,
+                h_out_capacity=caps, d_out_sizes=FAKE, d_workspace=FAKE, workspace_bytes=ws - 1, stream=None)
+    call = lambda **kw: uz.uzip_compress_batched(**{**base, **kw})
+    assert call(h_in=[0, 0, FAKE]) == uz.UZIP_ERR_INVALID_ARGUMENT
+    assert call(h_out_capacity=[caps[0], caps[1], caps[2] - 16]) == uz.UZIP_ERR_CAPACITY
+    assert call() == uz.UZIP_ERR_INVALID_ARGUMENT
+    assert call(d_out_sizes=FAKE + 4) == uz.UZIP_ERR_INVALID_ARGUMENT
+
+
+def test_status_strings():
+    for s in range(6):
+        assert uz.uzip_status_string(s)
+    assert "corrupt" in uz.uzip_status_string(uz.UZIP_ERR_CORRUPT_INPUT)
+
+
+def test_product_path_does_not_touch_the_oracle():
+    pkg = os.path.join(ROOT, "lossless_compression_float_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".hpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in text.lower(), f

@@ -1,0 +1,199 @@
+"""GPU parity: the HIP path, called through the C ABI, against the oracle.
+
+Tolerance 0 everywhere: the compressed bytes must equal the oracle's byte for
+byte, and decompression must restore every bit pattern (NaN payloads,
+infinities, denormals, signed zeros included).  Small cases compare whole
+buffers; the full-size workloads compare sampled chunks record by record
+(a record depends only on its chunk's values) plus properties that hold at
+any size (bit-exact round trip, sizes, ratio against the entropy bound).
+"""
+import numpy as np
+import pytest
+import torch
+
+import lossless_compression_float_amd as uz
+import oracle as orc
+import workloads
+from uzip_testlib import corruptions, parse_buffer
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _bits_tensor(bits: np.ndarray) -> torch.Tensor:
+    if bits.dtype == np.uint16:
+        return torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).to(DEV)
+    return torch.from_numpy(bits.view(np.int32).copy()).view(torch.float32).to(DEV)
+
+
+def _code(bits):
+    return orc.BF16 if bits.dtype == np.uint16 else orc.FP32
+
+
+def gpu_compress(t: torch.Tensor, chunk_bytes: int = 0) -> np.ndarray:
+    buf, size = uz.compress(t, chunk_bytes)
+    torch.cuda.synchronize()
+    n = int(size.item())
+    assert n <= buf.numel()
+    return buf[:n].cpu().numpy()
+
+
+def gpu_decompress(buf: np.ndarray, dtype: torch.dtype, n: int, in_bytes=None):
+    b = torch.from_numpy(buf.copy()).to(DEV) if buf.size else torch.empty(16, dtype=torch.uint8, device=DEV)
+    out, st = uz.decompress(b, dtype, n, in_bytes=buf.size if in_bytes is None else in_bytes)
+    torch.cuda.synchronize()
+    return out, int(st.item())
+
+
+def check_parity(bits: np.ndarray, chunk_bytes: int = 0):
+    """GPU bytes == oracle bytes, and both decode to the input on the GPU."""
+    t = _bits_tensor(bits)
+    got = gpu_compress(t, chunk_bytes)
+    want = orc.compress(_code(bits), bits, chunk_bytes)
+    if not np.array_equal(got, want):
+        hint = "sizes %d vs %d" % (got.size, want.size)
+        if got.size == want.size:
+            hint += ", first difference at byte %d" % int(np.nonzero(got != want)[0][0])
+        pytest.fail("compressed bytes differ from the oracle: " + hint)
+    out, st = gpu_decompress(got, t.dtype, bits.size)
+    assert st == 0
+    assert torch.equal(out.view(torch.int16 if bits.dtype == np.uint16 else torch.int32),
+                       t.view(torch.int16 if bits.dtype == np.uint16 else torch.int32))
+    return got
+
+
+def test_pr1_bytes_identical_and_roundtrip():
+    bits = workloads.bits_numpy(workloads.pr1())
+    got = check_parity(bits)
+    hdr, idx, recs = parse_buffer(got)
+    assert hdr["C"] == 32 and all(r["mode"] == 0 for r in recs)
+
+
+@pytest.mark.parametrize("n", [1, 7, 31, 32, 33, 100, 1000, 32767, 32768, 32768 + 5, 65536 * 2 + 31, 300_001])
+def test_bf16_ragged_sizes(n):
+    bits = workloads.bits_numpy(workloads.gradient_bucket(n, seed=n, special_frac=0.01))
+    check_parity(bits)
+
+
+@pytest.mark.parametrize("n", [1, 3, 33, 1000, 65535, 65536, 65536 * 2 + 7, 400_003])
+def test_fp32_ragged_sizes(n):
+    bits = workloads.bits_numpy(workloads.fp32_gradients(n, seed=n))
+    check_parity(bits)
+
+
+@pytest.mark.parametrize("dtype", [np.uint16, np.uint32])
+def test_empty_buffer(dtype):
+    bits = np.zeros(0, dtype)
+    got = gpu_compress(_bits_tensor(np.zeros(1, dtype))[:0])
+    assert np.array_equal(got, orc.compress(_code(bits), bits))
+    out, st = gpu_decompress(got, torch.bfloat16 if dtype == np.uint16 else torch.float32, 0)
+    assert st == 0 and out.numel() == 0
+
+
+def test_every_bf16_bit_pattern():
+    check_parity(np.arange(65536, dtype=np.uint32).astype(np.uint16))
+
+
+def test_fp32_special_classes_and_all_exponents():
+    rng = np.random.default_rng(2)
+    exps = np.repeat(np.arange(256, dtype=np.uint32), 300)
+    v = (rng.integers(0, 2, exps.size, dtype=np.uint32) << 31) | (exps << 23) | rng.integers(0, 1 << 23, exps.size,
+                                                                                               dtype=np.uint32)
+    special = np.array([0, 0x80000000, 0x7F800000, 0xFF800000, 0x7FC00000, 0xFFC00001, 0x7F800001, 1, 0x807FFFFF],
+                       np.uint32)
+    check_parity(np.concatenate([special, v, special]))
+
+
+@pytest.mark.parametrize("dtype", [np.uint16, np.uint32])
+def test_random_bits_go_raw(dtype):
+    n = 3 * (32768 if dtype == np.uint16 else 65536) + 777
+    bits = np.random.default_rng(3).integers(0, np.iinfo(dtype).max, n, dtype=np.uint64).astype(dtype)
+    got = check_parity(bits)
+    assert got.size == orc.max_compressed_size(_code(bits), n)
+
+
+@pytest.mark.parametrize("n", [160, 161, 176, 177, 1000, 40000])
+def test_single_exponent_chunks(n):
+    check_parity(np.full(n, (130 << 7) | 3, np.uint16))
+
+
+def test_all_256_exponents_in_one_chunk():
+    rng = np.random.default_rng(1)
+    e = np.concatenate([np.arange(256), rng.integers(0, 256, 30000)]).astype(np.uint16)
+    check_parity(((rng.integers(0, 2, e.size) << 15) | (e << 7) | rng.integers(0, 128, e.size)).astype(np.uint16))
+
+
+def test_one_dominant_exponent_plus_rare_singletons():
+    rng = np.random.default_rng(4)
+    e = np.full(32768, 120, np.uint16)
+    e[rng.choice(32768, 255, replace=False)] = np.arange(256)[np.arange(256) != 120]
+    check_parity(((e << 7) | rng.integers(0, 256, e.size).astype(np.uint16) & 0x807F).astype(np.uint16))
+
+
+@pytest.mark.parametrize("dtype,chunk_bytes", [(np.uint16, 64), (np.uint16, 2048), (np.uint16, 131072),
+                                               (np.uint16, 1 << 21), (np.uint32, 128), (np.uint32, 65536),
+                                               (np.uint32, 1 << 22)])
+def test_chunk_sizes(dtype, chunk_bytes):
+    n = 1_200_001
+    if dtype == np.uint16:
+        bits = workloads.bits_numpy(workloads.gradient_bucket(n, seed=5, special_frac=1e-3))
+    else:
+        bits = workloads.bits_numpy(workloads.fp32_gradients(n, seed=5))
+    check_parity(bits, chunk_bytes)
+
+
+def test_decodes_oracle_buffers():
+    bits = workloads.bits_numpy(workloads.gradient_bucket(500_000, seed=8, special_frac=1e-3))
+    buf = orc.compress(orc.BF16, bits)
+    out, st = gpu_decompress(buf, torch.bfloat16, bits.size)
+    assert st == 0
+    assert np.array_equal(out.view(torch.int16).cpu().numpy().view(np.uint16), bits)
+
+
+def test_corrupt_buffers_are_reported():
+    bits = workloads.bits_numpy(workloads.pr1())[:100_000]
+    buf = orc.compress(orc.BF16, bits)
+    out, st = gpu_decompress(buf, torch.bfloat16, bits.size)
+    assert st == 0
+    for name, bad in corruptions(buf):
+        _, st = gpu_decompress(bad, torch.bfloat16, bits.size)
+        assert st == uz.UZIP_ERR_CORRUPT_INPUT, name
+    _, st = gpu_decompress(buf, torch.float32, bits.size // 2)
+    assert st == uz.UZIP_ERR_CORRUPT_INPUT
+    _, st = gpu_decompress(buf, torch.bfloat16, bits.size, in_bytes=40)
+    assert st == uz.UZIP_ERR_CORRUPT_INPUT
+
+
+def test_batched_matches_single_and_oracle():
+    sizes = [0, 1, 5000, 32768, 100_000, 0, 33, 70_000]
+    tensors = [workloads.gradient_bucket(n, seed=10 + i, special_frac=1e-3) if n else
+               torch.empty(0, dtype=torch.bfloat16) for i, n in enumerate(sizes)]
+    dev = [t.to(DEV) for t in tensors]
+    outs, out_sizes = uz.compress_batched(dev)
+    torch.cuda.synchronize()
+    got_sizes = out_sizes.cpu().tolist()
+    for t, o, s in zip(tensors, outs, got_sizes):
+        bits = workloads.bits_numpy(t)
+        assert np.array_equal(o[:s].cpu().numpy(), orc.compress(orc.BF16, bits))
+    vals, status = uz.decompress_batched([o[:s] for o, s in zip(outs, got_sizes)], torch.bfloat16, sizes)
+    torch.cuda.synchronize()
+    assert status.cpu().tolist() == [0] * len(sizes)
+    for t, v in zip(dev, vals):
+        assert torch.equal(t.view(torch.int16), v.view(torch.int16))
+
+
+def test_batched_fp32_and_corrupt_member():
+    sizes = [70_000, 131_072, 3]
+    tensors = [workloads.fp32_gradients(n, seed=20 + i).to(DEV) for i, n in enumerate(sizes)]
+    outs, out_sizes = uz.compress_batched(tensors)
+    torch.cuda.synchronize()
+    got = [o[:s] for o, s in zip(outs, out_sizes.cpu().tolist())]
+    for t, g in zip(tensors, got):
+        assert np.array_equal(g.cpu().numpy(), orc.compress(orc.FP32, workloads.bits_numpy(t)))
+    bad = got[1].clone()
+    bad[0] ^= 1  # magic
+    vals, status = uz.decompress_batched([got[0], bad, got[2]], torch.float32, sizes)
+    torch.cuda.synchronize()
+    assert status.cpu().tolist() == [0, uz.UZIP_ERR_CORRUPT_INPUT, 0]
+    assert torch.equal(vals[0].view(torch.int32), tensors[0].view(torch.int32))
+    assert torch.equal(vals[2].view(torch.int32), tensors[2].view(torch.int32))

@@ -18,6 +18,7 @@ import pytest
 
 import oracle as orc
 import workloads
+from uzip_testlib import corruptions as _corruptions, parse_buffer
 
 GOLD = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
@@ -34,37 +35,6 @@ def _table(d):
         f[int(k)] = fs
         c0[int(k)] = cs
     return f, c0
-
-
-# --------------------------------------------------------------------------
-# Record parsing helper (the v1 record layout read back byte by byte)
-# --------------------------------------------------------------------------
-def parse_buffer(buf):
-    b = bytes(buf)
-    hdr = dict(
-        magic=int.from_bytes(b[0:4], "little"), version=int.from_bytes(b[4:6], "little"), dtype=b[6],
-        prob_bits=b[7], lanes=b[8], r=b[9], chunk_elems=int.from_bytes(b[12:16], "little"),
-        n=int.from_bytes(b[16:24], "little"), C=int.from_bytes(b[24:32], "little"),
-        sm_off=int.from_bytes(b[32:40], "little"), exp_off=int.from_bytes(b[40:48], "little"),
-        total=int.from_bytes(b[48:56], "little"))
-    C = hdr["C"]
-    idx = [int.from_bytes(b[64 + 8 * i:72 + 8 * i], "little") for i in range(C + 1)]
-    recs = []
-    for i in range(C):
-        r = b[hdr["exp_off"] + idx[i]:hdr["exp_off"] + idx[i + 1]]
-        mode, nsym = r[0], int.from_bytes(r[2:4], "little")
-        n_words = int.from_bytes(r[4:8], "little")
-        n_values = int.from_bytes(r[8:12], "little")
-        rec = dict(mode=mode, nsym=nsym, n_words=n_words, n_values=n_values, bytes=len(r), raw=r)
-        if mode == 0:
-            bitmap = r[16:48]
-            syms = [s for s in range(256) if (bitmap[s >> 3] >> (s & 7)) & 1]
-            f = {s: int.from_bytes(r[48 + 2 * k:50 + 2 * k], "little") for k, s in enumerate(syms)}
-            tab_end = (48 + 2 * nsym + 3) // 4 * 4
-            states = [int.from_bytes(r[tab_end + 4 * j:tab_end + 4 * j + 4], "little") for j in range(32)]
-            rec.update(f=f, states=states)
-        recs.append(rec)
-    return hdr, idx, recs
 
 
 def entropy_bits(counts):
@@ -506,44 +476,6 @@ def test_invalid_chunk_sizes_rejected():
 # --------------------------------------------------------------------------
 # P7: corruption is reported, never decoded into garbage
 # --------------------------------------------------------------------------
-def _corruptions(buf):
-    hdr, idx, recs = parse_buffer(buf)
-    exp_off = hdr["exp_off"]
-    ri = next(i for i, r in enumerate(recs) if r["mode"] == 0)
-    base = exp_off + idx[ri]
-    rec = recs[ri]
-    tab_end = (48 + 2 * rec["nsym"] + 3) // 4 * 4
-
-    def patch(off, val, width):
-        b = buf.copy()
-        b[off:off + width] = np.frombuffer(int(val).to_bytes(width, "little"), np.uint8)
-        return b
-
-    yield "truncated", buf[:-16]
-    yield "magic", patch(0, 0x31505A56, 4)
-    yield "version", patch(4, 2, 2)
-    yield "dtype", patch(6, 2, 1)
-    yield "prob_bits", patch(7, 11, 1)
-    yield "count", patch(16, hdr["n"] + 1, 8)
-    yield "chunk_elems", patch(12, 1000, 4)
-    yield "sm_off", patch(32, hdr["sm_off"] + 16, 8)
-    yield "total", patch(48, buf.size + 16, 8)
-    yield "index_first", patch(64, 16, 8)
-    yield "index_unaligned", patch(64 + 8 * (ri + 1), idx[ri + 1] + 2, 8)
-    yield "index_decreasing", patch(64 + 8 * (ri + 1), idx[ri] - 16 if idx[ri] >= 16 else 0, 8)
-    yield "rec_mode", patch(base, 2, 1)
-    yield "rec_n_values", patch(base + 8, rec["n_values"] - 1, 4)
-    yield "rec_bytes", patch(base + 12, rec["bytes"] + 16, 4)
-    yield "rec_n_words_up", patch(base + 4, rec["n_words"] + 1, 4)
-    yield "rec_n_words_down", patch(base + 4, rec["n_words"] - 8, 4)
-    yield "nsym", patch(base + 2, rec["nsym"] + 1, 2)
-    yield "freq_sum", patch(base + 48, rec["f"][min(rec["f"])] + 1, 2)
-    yield "freq_zero", patch(base + 48, 0, 2)
-    yield "state_low", patch(base + tab_end, 65535, 4)
-    yield "state_value", patch(base + tab_end + 4, rec["states"][1] ^ 0x40, 4)
-    yield "word", patch(base + tab_end + 128 + 2 * (rec["n_words"] // 2), 0x1234, 2)
-
-
 def test_corruption_detected():
     bits = workloads.bits_numpy(workloads.pr1())[:100_000]
     buf = orc.compress(orc.BF16, bits)
