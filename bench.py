@@ -1,0 +1,350 @@
+#!/usr/bin/env python
+"""Throughput of the lossless bf16/fp32 codec on one MI355X.
+
+One step = compress + decompress of the whole workload (every stage of the
+path: split, histogram, table, rANS encode, size scan, compaction, validation,
+rANS decode and re-interleave), inputs already resident in HBM.  Prints one
+JSON line:
+
+  value          uncompressed GB/s of the round trip (input bytes / step time)
+  compress_gbps / decompress_gbps   per direction (HIP events on the stream)
+  ratio          compressed / original, and its entropy bound
+  roofline       dominant kernel: algorithmic bytes per launch / its average
+                 duration (HIP events around the kernel, recorded by the
+                 library on the launch stream) against the 8 TB/s HBM peak
+  cpu_baseline   the CPU oracle (single thread) on a bounded sample of the
+                 same bytes; its output also serves as a byte-for-byte check
+
+Workloads (--workload): grad_bucket (default: 268,435,456 bf16 values,
+512 MiB, 64 KiB chunks), pr1, fp32_grad, llama8b (290 buffers, batched),
+small_batch (4,096 buffers, batched).
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+# traffic measured with rocprofv3 FETCH_SIZE / WRITE_SIZE for the dominant
+# kernel of the default workload (filled in from the committed profiles; None
+# until counters for the current kernel exist)
+MEASURED_TRAFFIC = {}
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="grad_bucket",
+                    choices=["grad_bucket", "pr1", "fp32_grad", "llama8b", "small_batch"])
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum CPU-oracle time to accumulate")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+class Hip:
+    """hipEvent helpers through the HIP runtime torch has already loaded."""
+
+    def __init__(self):
+        self.rt = ctypes.CDLL("libamdhip64.so.7")
+        self.rt.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.rt.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.rt.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.rt.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self):
+        e = ctypes.c_void_p()
+        assert self.rt.hipEventCreate(ctypes.byref(e)) == 0
+        return e
+
+    def elapsed_ms(self, a, b) -> float:
+        assert self.rt.hipEventSynchronize(b) == 0
+        ms = ctypes.c_float()
+        assert self.rt.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
+        return ms.value
+
+    def destroy(self, e):
+        self.rt.hipEventDestroy(e)
+
+
+def make_workload(name, dev):
+    import torch
+
+    import workloads as W
+    if name == "grad_bucket":
+        ts = [W.gradient_bucket(W.GRAD_BUCKET_N, device=dev, seed=1)]
+        desc = ("gradient bucket: 268,435,456 bf16 values (512 MiB) N(0, s^2), s log-uniform in [1e-5, 1e-2] per "
+                "1M-value block, 0.01% Inf/NaN/denormal/zero, 64 KiB chunks")
+        batched = False
+    elif name == "pr1":
+        ts = [W.pr1(dev)]
+        desc = "PR1: 1,048,576 bf16 values N(0, 0.02^2) from seed 0 (2 MiB), 64 KiB chunks"
+        batched = False
+    elif name == "fp32_grad":
+        ts = [W.fp32_gradients(W.FP32_GRAD_N, device=dev, seed=3)]
+        desc = "fp32 gradients: 100,000,000 values N(0, 1e-6) + 10% Laplace(0, 1e-4) (400 MB), 256 KiB chunks"
+        batched = False
+    elif name == "llama8b":
+        ts = [t.reshape(-1) for t in W.llama3_8b_weights(device=dev, seed=2)]
+        desc = ("RL weight sync: Llama-3-8B-shaped bf16 weight set, 290 buffers, 8,030,257,152 values (16.06 GB), "
+                "N(0, 0.02^2), RMSNorm vectors 1.0, one batched call, 64 KiB chunks")
+        batched = True
+    else:
+        ts = W.small_message_batch(device=dev, seed=4)
+        desc = ("small-message batch: 4,096 bf16 activation buffers, 1-64 tokens x 8192 hidden, N(0,1) x "
+                "log-normal(0, 0.5) per-token RMS, one batched launch, 64 KiB chunks")
+        batched = True
+    torch.cuda.synchronize()
+    return ts, desc, batched
+
+
+def entropy_bound(ts, chunk_elems):
+    """Sum over chunks of (raw sign+mantissa bytes + n_i * H_i / 8): the size
+    an ideal per-chunk exponent coder would reach (computed with torch)."""
+    import torch
+    total = 0.0
+    for t in ts:
+        n = t.numel()
+        if n == 0:
+            continue
+        if t.dtype == torch.bfloat16:
+            e = (t.view(torch.int16).to(torch.int32) >> 7) & 0xFF
+            r = 1
+        else:
+            e = (t.view(torch.int32) >> 23) & 0xFF
+            r = 3
+        C = (n + chunk_elems - 1) // chunk_elems
+        for c0 in range(0, C, 4096):  # slices of chunks keep the index tensor small
+            c1 = min(C, c0 + 4096)
+            seg = e[c0 * chunk_elems:min(n, c1 * chunk_elems)].to(torch.int64)
+            cid = torch.arange(seg.numel(), device=seg.device) // chunk_elems
+            cnt = torch.bincount(cid * 256 + seg, minlength=(c1 - c0) * 256).view(c1 - c0, 256).double()
+            tot = cnt.sum(1, keepdim=True)
+            p = torch.where(cnt > 0, cnt / tot, torch.ones_like(cnt))
+            bits = -(cnt * torch.log2(p)).sum()
+            total += float(bits) / 8.0
+        total += r * n
+    return total
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one MI355X: this codec runs on a single GPU (no collectives, no sharding); "
+              "--gpus %d is not supported" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import lossless_compression_float_amd as uz
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    hip = Hip()
+    print("# workload %s: generating inputs" % args.workload, file=sys.stderr, flush=True)
+    ts, desc, batched = make_workload(args.workload, dev)
+    dtype = ts[0].dtype
+    code = uz.dtype_code(dtype)
+    eb = 2 if code == uz.UZIP_BF16 else 4
+    rb = 1 if code == uz.UZIP_BF16 else 3
+    chunk_elems = 32768 if code == uz.UZIP_BF16 else 65536
+    ns = [t.numel() for t in ts]
+    n_total = sum(ns)
+    in_bytes = n_total * eb
+
+    # preallocated outputs and workspaces
+    caps = [uz.uzip_max_compressed_size(code, n) for n in ns]
+    outs = [torch.empty(c, dtype=torch.uint8, device=dev) for c in caps]
+    backs = [torch.empty(n, dtype=dtype, device=dev) for n in ns]
+    if batched:
+        ws = uz.workspace(uz.uzip_workspace_size_batched(code, ns), dev)
+        sizes = torch.empty(len(ts), dtype=torch.int64, device=dev)
+        status = torch.empty(len(ts), dtype=torch.int32, device=dev)
+    else:
+        ws = uz.workspace(uz.uzip_workspace_size(code, ns[0]), dev)
+        sizes = torch.empty(1, dtype=torch.int64, device=dev)
+        status = torch.empty(1, dtype=torch.int32, device=dev)
+
+    def compress():
+        if batched:
+            uz.compress_batched(ts, outs=outs, ws=ws, out_sizes=sizes)
+        else:
+            uz.compress(ts[0], out=outs[0], ws=ws, out_size=sizes)
+
+    def decompress():
+        # in_bytes = capacity: the decoder validates the header's total against it
+        if batched:
+            uz.decompress_batched(outs, dtype, ns, outs=backs, status=status, ws=ws)
+        else:
+            uz.decompress(outs[0], dtype, ns[0], out=backs[0], status=status, ws=ws)
+
+    print("# %d buffers, %d values, %.1f MB; warmup %d, steps %d" % (len(ts), n_total, in_bytes / 1e6, args.warmup,
+                                                                      args.steps), file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        compress()
+        decompress()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    enc_ev = [(hip.event(), hip.event()) for _ in range(K)]
+    dec_ev = [(hip.event(), hip.event()) for _ in range(K)]
+    c_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    d_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(K):
+        uz.uzip_profile_set_events(enc_ev[k][0], enc_ev[k][1])
+        c_ev[k][0].record()
+        compress()
+        c_ev[k][1].record()
+        uz.uzip_profile_set_events(dec_ev[k][0], dec_ev[k][1])
+        d_ev[k][0].record()
+        decompress()
+        d_ev[k][1].record()
+    uz.uzip_profile_set_events(None, None)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / K
+    comp_ms = sorted(a.elapsed_time(b) for a, b in c_ev)
+    dec_ms = sorted(a.elapsed_time(b) for a, b in d_ev)
+    enc_kernel_ms = sum(hip.elapsed_ms(a, b) for a, b in enc_ev) / K
+    dec_kernel_ms = sum(hip.elapsed_ms(a, b) for a, b in dec_ev) / K
+    for a, b in enc_ev + dec_ev:
+        hip.destroy(a)
+        hip.destroy(b)
+
+    # correctness of what was timed: bit-exact round trip, valid status
+    st = status.cpu().tolist()
+    roundtrip_ok = all(s == 0 for s in st) and all(
+        torch.equal(a.view(torch.int16 if eb == 2 else torch.int32), b.view(torch.int16 if eb == 2 else torch.int32))
+        for a, b in zip(ts, backs))
+    comp_sizes = sizes.cpu().tolist()
+    comp_bytes = sum(comp_sizes)
+    bound = entropy_bound(ts, chunk_elems)
+
+    # algorithmic bytes per launch of the two coding kernels
+    chunks = sum((n + chunk_elems - 1) // chunk_elems for n in ns)
+    exp_offs = [((((64 + 8 * ((n + chunk_elems - 1) // chunk_elems + 1)) + 15) // 16 * 16 + rb * n) + 15) // 16 * 16
+                for n in ns]
+    rec_bytes = sum(s - e for s, e in zip(comp_sizes, exp_offs))
+    enc_bytes = n_total * eb + n_total * rb + rec_bytes
+    dec_bytes = n_total * rb + rec_bytes + sum(64 + 8 * ((n + chunk_elems - 1) // chunk_elems + 1) for n in ns) + \
+        n_total * eb
+    if enc_kernel_ms >= dec_kernel_ms:
+        kname, kbytes, kms = "k_encode", enc_bytes, enc_kernel_ms
+    else:
+        kname, kbytes, kms = "k_decode", dec_bytes, dec_kernel_ms
+    achieved = kbytes / (kms * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                "traffic": MEASURED_TRAFFIC.get((args.workload, kname)),
+                "algorithmic_bytes": kbytes, "avg_ms": round(kms, 4),
+                "k_encode_ms": round(enc_kernel_ms, 4), "k_decode_ms": round(dec_kernel_ms, 4),
+                "k_encode_frac": round(enc_bytes / (enc_kernel_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                "k_decode_frac": round(dec_bytes / (dec_kernel_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+
+    cpu = None
+    oracle_match = None
+    if not args.no_cpu_baseline:
+        cpu, oracle_match = cpu_baseline(ts, outs, comp_sizes, code, args.cpu_seconds)
+
+    med_c = comp_ms[len(comp_ms) // 2]
+    med_d = dec_ms[len(dec_ms) // 2]
+    line = {
+        "metric": "compress/decompress GB/s (uncompressed) + ratio + % HBM roofline, 1 MI355X",
+        "value": round(in_bytes / (ms_step * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u32",
+        "data": "synthetic",
+        "config": {"workload": desc, "values": n_total, "buffers": len(ts), "input_bytes": in_bytes,
+                   "value_dtype": "bf16" if eb == 2 else "fp32", "chunk_bytes": chunk_elems * eb,
+                   "step": "compress + decompress"},
+        "compress_gbps": round(in_bytes / (med_c * 1e-3) / 1e9, 2),
+        "decompress_gbps": round(in_bytes / (med_d * 1e-3) / 1e9, 2),
+        "compress_ms": {"median": round(med_c, 4), "min": round(comp_ms[0], 4)},
+        "decompress_ms": {"median": round(med_d, 4), "min": round(dec_ms[0], 4)},
+        "ratio": round(comp_bytes / in_bytes, 5),
+        "entropy_bound_ratio": round(bound / in_bytes, 5),
+        "ratio_over_bound": round(comp_bytes / bound, 5),
+        "compressed_bytes": comp_bytes,
+        "roundtrip_bit_exact": roundtrip_ok,
+        "oracle_bytes_match": oracle_match,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    if not roundtrip_ok or oracle_match is False:
+        sys.exit(1)
+
+
+def cpu_baseline(ts, outs, comp_sizes, code, min_seconds):
+    """The oracle (plain single-threaded C) on a bounded sample of the same
+    workload: whole buffers, in order, up to 512 MiB of input; passes repeat
+    until min_seconds of CPU time have been spent.  Also compares the oracle's
+    compressed bytes with the GPU's for every sampled buffer."""
+    import numpy as np
+
+    import oracle
+    import workloads as W
+    budget = 512 << 20
+    picked, acc = [], 0
+    for i, t in enumerate(ts):
+        nb = t.numel() * t.element_size()
+        if picked and acc + nb > budget:
+            break
+        picked.append(i)
+        acc += nb
+    host = [W.bits_numpy(ts[i]) for i in picked]
+    match = True
+    for i, h in zip(picked, host):
+        want = oracle.compress(code, h)
+        got = outs[i][:comp_sizes[i]].cpu().numpy()
+        match = match and np.array_equal(want, got)
+    sample_bytes = sum(h.size * h.itemsize for h in host)
+    spent, passes = 0.0, 0
+    while passes == 0 or spent < min_seconds:
+        t0 = time.perf_counter()
+        for h in host:
+            buf = oracle.compress(code, h)
+            st, back = oracle.decompress(buf, code, h.size)
+            assert st == 0
+        spent += time.perf_counter() - t0
+        passes += 1
+        if spent > 60:
+            break
+    gbps = sample_bytes * passes / spent / 1e9
+    return ({"value": round(gbps, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+             "sample": "%d of %d buffers, %d values (%.1f MB), compress + decompress, %d passes, %.1f s; host %s"
+                       % (len(picked), len(ts), sum(h.size for h in host), sample_bytes / 1e6, passes, spent,
+                          _cpu_model())},
+            bool(match))
+
+
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip() + ", %d logical cores" % os.cpu_count()
+    except OSError:
+        pass
+    return "unknown"
+
+
+if __name__ == "__main__":
+    main()

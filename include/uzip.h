@@ -126,6 +126,14 @@ uzip_status uzip_decompress_batched(uzip_dtype dtype, size_t num_buffers,
                                     const size_t *h_num_elements, void *const *h_out, uint32_t *d_status,
                                     void *d_workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Benchmark instrumentation.  While set (non-null), every compress call on
+ * the calling host thread records `main_start` on its stream right before
+ * its main coding kernel (split + histogram + table + rANS encode) and
+ * `main_stop` right after it; every decompress call does the same around
+ * its rANS decode kernel.  Pass nulls to stop.  The events belong to the
+ * caller (hipEventCreate).  Thread-local; costs nothing while unset. */
+uzip_status uzip_profile_set_events(hipEvent_t main_start, hipEvent_t main_stop);
+
 /* Static English name of a status code. */
 const char *uzip_status_string(uzip_status s);
 

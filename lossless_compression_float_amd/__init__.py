@@ -38,6 +38,7 @@ EXPORTED = (
     "uzip_workspace_size_batched",
     "uzip_compress_batched",
     "uzip_decompress_batched",
+    "uzip_profile_set_events",
     "uzip_status_string",
 )
 
@@ -72,6 +73,8 @@ def lib() -> ctypes.CDLL:
         L.uzip_compress_batched.argtypes = [i32, sz, vp, vp, sz, vp, vp, u64p, vp, sz, vp]
         L.uzip_decompress_batched.restype = i32
         L.uzip_decompress_batched.argtypes = [i32, sz, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.uzip_profile_set_events.restype = i32
+        L.uzip_profile_set_events.argtypes = [vp, vp]
         L.uzip_status_string.restype = ctypes.c_char_p
         L.uzip_status_string.argtypes = [i32]
         _lib = L
@@ -129,6 +132,10 @@ def uzip_decompress_batched(dtype, h_in, h_in_bytes, h_num_elements, h_out, d_st
     return int(lib().uzip_decompress_batched(dtype, len(h_in), ctypes.cast(a_in, v), ctypes.cast(a_b, v),
                                              ctypes.cast(a_n, v), ctypes.cast(a_out, v), d_status, d_workspace,
                                              workspace_bytes, stream))
+
+
+def uzip_profile_set_events(main_start, main_stop) -> int:
+    return int(lib().uzip_profile_set_events(main_start, main_stop))
 
 
 def uzip_status_string(status: int) -> str:

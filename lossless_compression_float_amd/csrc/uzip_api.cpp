@@ -264,6 +264,12 @@ uzip_status uzip_decompress_batched(uzip_dtype dtype, size_t num_buffers, const 
     return decompress_impl(dtype, descs, d_status, d_workspace, workspace_bytes, stream);
 }
 
+uzip_status uzip_profile_set_events(hipEvent_t main_start, hipEvent_t main_stop) {
+    g_profile.start = main_start;
+    g_profile.stop = main_stop;
+    return UZIP_OK;
+}
+
 const char *uzip_status_string(uzip_status s) {
     switch (s) {
         case UZIP_OK: return "ok";

@@ -658,6 +658,8 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
+thread_local ProfileEvents g_profile;
+
 hipError_t launch_compress(const EncParams &ep, const CompactParams &cp, uint64_t *tile_sums, uint64_t *tile_offs,
                            uint64_t ntiles, bool any_empty, hipStream_t stream) {
     if (any_empty) {
@@ -666,8 +668,10 @@ hipError_t launch_compress(const EncParams &ep, const CompactParams &cp, uint64_
     }
     if (ep.total_chunks > 0) {
         const uint64_t grid = (ep.total_chunks + 1) / 2;
+        if (g_profile.start) (void)hipEventRecord(g_profile.start, stream);
         if (ep.dtype == 1) k_encode<1><<<dim3((uint32_t)grid), dim3(64), 0, stream>>>(ep);
         else k_encode<2><<<dim3((uint32_t)grid), dim3(64), 0, stream>>>(ep);
+        if (g_profile.stop) (void)hipEventRecord(g_profile.stop, stream);
         k_tile_reduce<<<dim3((uint32_t)ntiles), dim3(256), 0, stream>>>(ep.rec_sizes, ep.total_chunks, tile_sums);
         k_scan_u64<<<1, 1024, 0, stream>>>(tile_sums, tile_offs, ntiles);
         k_compact<<<dim3((uint32_t)ep.total_chunks), dim3(64), 0, stream>>>(cp);
@@ -682,8 +686,10 @@ hipError_t launch_decompress(const DecParams &vp, const DecodeParams &dp, int dt
     if (max_chunks > 0) {
         const uint64_t half = (max_chunks + 1) / 2;
         const uint64_t grid = half < 8192 ? half : 8192;
+        if (g_profile.start) (void)hipEventRecord(g_profile.start, stream);
         if (dtype == 1) k_decode<1><<<dim3((uint32_t)grid), dim3(64), 0, stream>>>(dp);
         else k_decode<2><<<dim3((uint32_t)grid), dim3(64), 0, stream>>>(dp);
+        if (g_profile.stop) (void)hipEventRecord(g_profile.stop, stream);
     }
     return hipGetLastError();
 }

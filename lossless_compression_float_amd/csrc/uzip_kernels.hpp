@@ -53,6 +53,13 @@ struct DecodeParams {
     uint32_t *status;
 };
 
+// events recorded around the main coding kernel (benchmark instrumentation)
+struct ProfileEvents {
+    hipEvent_t start = nullptr;
+    hipEvent_t stop = nullptr;
+};
+extern thread_local ProfileEvents g_profile;
+
 hipError_t launch_compress(const EncParams &ep, const CompactParams &cp, uint64_t *tile_sums, uint64_t *tile_offs,
                            uint64_t ntiles, bool any_empty, hipStream_t stream);
 hipError_t launch_decompress(const DecParams &vp, const DecodeParams &dp, int dtype, uint64_t max_chunks,
