@@ -252,6 +252,10 @@ def main():
                 "k_encode_frac": round(enc_bytes / (enc_kernel_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
                 "k_decode_frac": round(dec_bytes / (dec_kernel_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
 
+    copy_gbps = copy_reference(ts, K)
+    roofline["hbm_copy_gbps"] = round(copy_gbps, 1)
+    roofline["frac_of_copy"] = round(achieved / copy_gbps, 4)
+
     cpu = None
     oracle_match = None
     if not args.no_cpu_baseline:
@@ -291,6 +295,30 @@ def main():
     print(json.dumps(line), flush=True)
     if not roundtrip_ok or oracle_match is False:
         sys.exit(1)
+
+
+def copy_reference(ts, steps):
+    """Measured HBM bandwidth of a plain device-to-device copy of the
+    workload's input size (read + write bytes / time), a second reference
+    beside the 8 TB/s peak.  The same copy kernel calibrates the rocprofv3
+    FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    nbytes = sum(t.numel() * t.element_size() for t in ts)
+    src = torch.empty(nbytes, dtype=torch.uint8, device=ts[0].device)
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    for _ in range(2):
+        dst.copy_(src)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(steps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    del src, dst
+    return 2 * nbytes / (ms * 1e-3) / 1e9
 
 
 def cpu_baseline(ts, outs, comp_sizes, code, min_seconds):

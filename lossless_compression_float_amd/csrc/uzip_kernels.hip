@@ -7,11 +7,12 @@
 //   k_encode     one half-wave (32 lanes) per chunk, two chunks per wave:
 //                pass 1 streams the chunk forward with 128-bit loads, writes
 //                the sign+mantissa bytes straight to their final place in the
-//                output and counts the exponents in an LDS histogram; the
+//                output and counts the exponents in LDS sub-histograms; the
 //                half-wave then normalises the counts to a 2^12 table and runs
 //                the 32-lane rANS encoder backward over the chunk (re-reading
-//                the input), placing each step's renormalisation words by wave
-//                ballot + popcount rank.  The record goes to a workspace slot.
+//                the input, which the cache still holds), placing each step's
+//                renormalisation words by wave ballot + lane rank.  The record
+//                goes to a workspace slot.
 //   k_tile_reduce, k_scan_u64
 //                exclusive scan of the record sizes (two levels: tiles of
 //                1024 chunks, then one workgroup over the tile sums).
@@ -25,8 +26,9 @@
 //                   and merges each exponent with its sign+mantissa bytes.
 //
 // Nothing here is a dense contraction: all arithmetic is 32-bit integer and
-// bit manipulation on the vector ALU, and the kernels are bounded by HBM
-// bandwidth and VALU issue, not by the matrix cores.
+// bit manipulation on the vector ALU (plus one exact binary64 multiply per
+// encoded symbol), and the kernels are bounded by HBM bandwidth, VALU issue
+// and the serial per-lane rANS chain, not by the matrix cores.
 #include <stdint.h>
 
 #include <hip/hip_runtime.h>
@@ -35,6 +37,45 @@
 #include "uzip_kernels.hpp"
 
 namespace uzip {
+
+// ---------------------------------------------------------------------------
+// Global memory is accessed through address-space-1 pointers.  The buffers
+// arrive as generic pointers inside descriptors, and generic (flat) accesses
+// also count against the LDS wait counter, so every LDS wait in a step loop
+// would also wait for the prefetched global loads.
+// ---------------------------------------------------------------------------
+#define UZ_GLOBAL __attribute__((address_space(1)))
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+template <typename T>
+struct GAccess {
+    __device__ static T load(const void *p) { return *(const UZ_GLOBAL T *)p; }
+    __device__ static void store(void *p, T v) { *(UZ_GLOBAL T *)p = v; }
+};
+template <>
+struct GAccess<uint4> {
+    __device__ static uint4 load(const void *p) {
+        const u32x4 v = *(const UZ_GLOBAL u32x4 *)p;
+        return make_uint4(v.x, v.y, v.z, v.w);
+    }
+    __device__ static void store(void *p, uint4 v) { *(UZ_GLOBAL u32x4 *)p = u32x4{v.x, v.y, v.z, v.w}; }
+};
+template <>
+struct GAccess<uint2> {
+    __device__ static uint2 load(const void *p) {
+        const u32x2 v = *(const UZ_GLOBAL u32x2 *)p;
+        return make_uint2(v.x, v.y);
+    }
+    __device__ static void store(void *p, uint2 v) { *(UZ_GLOBAL u32x2 *)p = u32x2{v.x, v.y}; }
+};
+template <typename T>
+__device__ inline T gload(const void *p) {
+    return GAccess<T>::load(p);
+}
+template <typename T>
+__device__ inline void gstore(void *p, T v) {
+    GAccess<T>::store(p, v);
+}
 
 // ---------------------------------------------------------------------------
 // half-wave (32-lane segment of a wave64) collectives
@@ -64,13 +105,27 @@ __device__ inline uint64_t wave_sum_u64(uint64_t v) {
 // bits of the 32-lane mask of this lane's half
 __device__ inline uint32_t half_mask(uint64_t m, uint32_t h) { return h ? uint32_t(m >> 32) : uint32_t(m); }
 
+// Ballot of `pred` split per half-wave: number of set lanes in this lane's
+// half, and how many of them sit below this lane.  lo_bits is all-ones in the
+// upper half (whose lanes discount the lower half's bits) and zero below.
+struct HalfBallot {
+    uint32_t cnt, rank;
+};
+__device__ inline HalfBallot half_ballot(bool pred, uint32_t h, uint32_t lo_bits) {
+    const uint64_t m = __ballot(pred);
+    const uint32_t mlo = (uint32_t)m, mhi = (uint32_t)(m >> 32);
+    const uint32_t below = __builtin_amdgcn_mbcnt_hi(mhi, __builtin_amdgcn_mbcnt_lo(mlo, 0u));
+    const uint32_t plo = __popc(mlo);
+    return HalfBallot{h ? (uint32_t)__popc(mhi) : plo, below - (plo & lo_bits)};
+}
+
 // the buffer holding global chunk g: the largest b with chunk_first[b] <= g
 // (buffers without chunks share their successor's chunk_first and are skipped)
 __device__ inline uint32_t find_enc_buffer(const EncDesc *d, uint32_t nbuf, uint64_t g) {
     uint32_t lo = 0, hi = nbuf - 1;
     while (lo < hi) {
         uint32_t mid = (lo + hi + 1) >> 1;
-        if (d[mid].chunk_first <= g) lo = mid;
+        if (gload<uint64_t>(&d[mid].chunk_first) <= g) lo = mid;
         else hi = mid - 1;
     }
     return lo;
@@ -80,16 +135,34 @@ __device__ inline uint32_t find_dec_buffer(const uint64_t *chunk_first, uint32_t
     uint32_t lo = 0, hi = nbuf - 1;
     while (lo < hi) {
         uint32_t mid = (lo + hi + 1) >> 1;
-        if (chunk_first[mid] <= g) lo = mid;
+        if (gload<uint64_t>(chunk_first + mid) <= g) lo = mid;
         else hi = mid - 1;
     }
     return lo;
 }
 
+__device__ inline EncDesc load_enc_desc(const EncDesc *d) {
+    const uint4 *q = reinterpret_cast<const uint4 *>(d);
+    EncDesc r;
+    uint4 *o = reinterpret_cast<uint4 *>(&r);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) o[k] = gload<uint4>(q + k);
+    return r;
+}
+
+__device__ inline DecDesc load_dec_desc(const DecDesc *d) {
+    const uint4 *q = reinterpret_cast<const uint4 *>(d);
+    DecDesc r;
+    uint4 *o = reinterpret_cast<uint4 *>(&r);
+    o[0] = gload<uint4>(q);
+    o[1] = gload<uint4>(q + 1);
+    return r;
+}
+
 template <int DT>
 __device__ inline uint32_t load_value(const uint8_t *in, uint32_t i) {
-    if (DT == 1) return *(const uint16_t *)(in + 2ull * i);
-    return *(const uint32_t *)(in + 4ull * i);
+    if (DT == 1) return gload<uint16_t>(in + 2ull * i);
+    return gload<uint32_t>(in + 4ull * i);
 }
 
 template <int DT>
@@ -100,6 +173,25 @@ __device__ inline uint32_t exponent_of(uint32_t v) {
 // ---------------------------------------------------------------------------
 // k_encode: split + histogram + normalise + interleaved rANS, per chunk
 // ---------------------------------------------------------------------------
+// LDS of one workgroup (two chunks), 10 KiB, reused between phases:
+//   pass 1       4 sub-histograms per chunk (lane j counts into sub j mod 4),
+//                rows padded to 264 words so the four copies of a bin sit in
+//                four different banks: hot bins no longer serialise a wave
+//   normalise    keys of the present symbols          words [0, 512)
+//   pass 2       per-symbol coder table, 16 B/entry   words [512, 2560)
+constexpr uint32_t kSubHist = 4;
+constexpr uint32_t kSubRow = 264;
+constexpr uint32_t kEncLdsWords = 2560;
+
+// Exact floor(x / f) for the encoder, where x < f * 2^20 (so the quotient is
+// below 2^20) and 1 <= f <= 4096: one binary64 multiply by
+// r_f = (1 + 2^-44) / f.  The bias keeps the product at or above x / f
+// despite both roundings, and the product exceeds x / f by less than 2^-23,
+// while x / f lies at least 1/f >= 2^-12 below the next integer; truncation
+// therefore gives the exact quotient.
+__device__ inline double enc_reciprocal(uint32_t f) { return (1.0 + 0x1p-44) / (double)f; }
+__device__ inline uint32_t enc_quotient(uint32_t x, double r) { return (uint32_t)((double)x * r); }
+
 template <int DT>
 __global__ __launch_bounds__(64) void k_encode(EncParams p) {
     constexpr uint32_t EB = DT == 1 ? 2 : 4;  // bytes per value
@@ -107,17 +199,16 @@ __global__ __launch_bounds__(64) void k_encode(EncParams p) {
     constexpr uint32_t VPL = 16 / EB;         // values per lane per 128-bit load
     constexpr uint32_t VPI = 32 * VPL;        // values per half-wave per pass-1 step
 
-    __shared__ uint32_t s_hist[2][256];
-    __shared__ uint32_t s_tab[2][256];   // f | c0 << 16
-    __shared__ uint32_t s_keys[2][256];  // remainder << 8 | (255 - symbol), present symbols
+    __shared__ __align__(16) uint32_t lds[kEncLdsWords];
 
     const uint32_t lane = threadIdx.x;
     const uint32_t h = lane >> 5, lj = lane & 31;
+    const uint32_t lo_bits = h ? 0xFFFFFFFFu : 0u;
     const uint64_t g = uint64_t(blockIdx.x) * 2 + h;
     const bool valid = g < p.total_chunks;
     const uint64_t gq = valid ? g : p.total_chunks - 1;
 
-    const EncDesc d = p.nbuf == 1 ? p.single : p.descs[find_enc_buffer(p.descs, p.nbuf, gq)];
+    const EncDesc d = p.nbuf == 1 ? p.single : load_enc_desc(p.descs + find_enc_buffer(p.descs, p.nbuf, gq));
     const uint64_t ci = gq - d.chunk_first;
     const uint64_t v0 = ci * p.chunk_elems;
     const uint32_t ni = valid ? (uint32_t)min<uint64_t>(p.chunk_elems, d.n - v0) : 0u;
@@ -125,7 +216,8 @@ __global__ __launch_bounds__(64) void k_encode(EncParams p) {
     uint8_t *sm_out = d.out + d.sm_off + v0 * R;
     uint8_t *slot = p.slots + gq * p.slot_stride;
 
-    for (uint32_t k = lj; k < 256; k += 32) s_hist[h][k] = 0;
+    uint32_t *hist = lds + h * (kSubHist * kSubRow) + (lj & (kSubHist - 1)) * kSubRow;
+    for (uint32_t k = lane; k < 2 * kSubHist * kSubRow; k += 64) lds[k] = 0;
     __syncthreads();
 
     // ---- pass 1: split, sign+mantissa bytes to the output, LDS histogram ----
@@ -137,7 +229,7 @@ __global__ __launch_bounds__(64) void k_encode(EncParams p) {
         uint32_t w[4];
         const bool full = i0 + VPL <= ni;
         if (full) {
-            const uint4 q = *(const uint4 *)(in + uint64_t(i0) * EB);
+            const uint4 q = gload<uint4>(in + uint64_t(i0) * EB);
             w[0] = q.x; w[1] = q.y; w[2] = q.z; w[3] = q.w;
         } else {
             for (int k = 0; k < 4; ++k) w[k] = 0;
@@ -156,13 +248,13 @@ __global__ __launch_bounds__(64) void k_encode(EncParams p) {
                 const uint32_t v = (w[k >> 1] >> (16 * (k & 1))) & 0xFFFFu;
                 const uint32_t sm = ((v >> 8) & 0x80u) | (v & 0x7Fu);
                 smw[k >> 2] |= sm << (8 * (k & 3));
-                if (full || i0 + k < ni) atomicAdd(&s_hist[h][(v >> 7) & 0xFFu], 1u);
+                if (full || i0 + k < ni) atomicAdd(&hist[(v >> 7) & 0xFFu], 1u);
             }
             if (full) {
-                *(uint2 *)(sm_out + i0) = make_uint2(smw[0], smw[1]);
+                gstore<uint2>(sm_out + i0, make_uint2(smw[0], smw[1]));
             } else {
                 for (uint32_t k = 0; k < 8; ++k)
-                    if (i0 + k < ni) sm_out[i0 + k] = (uint8_t)(smw[k >> 2] >> (8 * (k & 3)));
+                    if (i0 + k < ni) gstore<uint8_t>(sm_out + i0 + k, (uint8_t)(smw[k >> 2] >> (8 * (k & 3))));
             }
         } else {
             uint32_t sm[4];
@@ -170,20 +262,20 @@ __global__ __launch_bounds__(64) void k_encode(EncParams p) {
             for (uint32_t k = 0; k < 4; ++k) {
                 const uint32_t v = w[k];
                 sm[k] = ((v >> 8) & 0x800000u) | (v & 0x7FFFFFu);
-                if (full || i0 + k < ni) atomicAdd(&s_hist[h][(v >> 23) & 0xFFu], 1u);
+                if (full || i0 + k < ni) atomicAdd(&hist[(v >> 23) & 0xFFu], 1u);
             }
             if (full) {
-                uint32_t *o = (uint32_t *)(sm_out + 3ull * i0);
-                o[0] = sm[0] | (sm[1] << 24);
-                o[1] = (sm[1] >> 8) | (sm[2] << 16);
-                o[2] = (sm[2] >> 16) | (sm[3] << 8);
+                uint8_t *o = sm_out + 3ull * i0;
+                gstore<uint32_t>(o, sm[0] | (sm[1] << 24));
+                gstore<uint32_t>(o + 4, (sm[1] >> 8) | (sm[2] << 16));
+                gstore<uint32_t>(o + 8, (sm[2] >> 16) | (sm[3] << 8));
             } else {
                 for (uint32_t k = 0; k < 4; ++k) {
                     if (i0 + k < ni) {
                         uint8_t *o = sm_out + 3ull * (i0 + k);
-                        o[0] = (uint8_t)sm[k];
-                        o[1] = (uint8_t)(sm[k] >> 8);
-                        o[2] = (uint8_t)(sm[k] >> 16);
+                        gstore<uint8_t>(o, (uint8_t)sm[k]);
+                        gstore<uint8_t>(o + 1, (uint8_t)(sm[k] >> 8));
+                        gstore<uint8_t>(o + 2, (uint8_t)(sm[k] >> 16));
                     }
                 }
             }
@@ -196,11 +288,18 @@ __global__ __launch_bounds__(64) void k_encode(EncParams p) {
     // floor of each quota, give the leftover slots to the largest remainders
     // (lower symbol first on equal remainders).
     uint32_t c[8], pm = 0;
+    {
+        const uint32_t *hh = lds + h * (kSubHist * kSubRow);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        c[k] = s_hist[h][lj * 8 + k];
-        if (c[k]) pm |= 1u << k;
+        for (int k = 0; k < 8; ++k) {
+            const uint32_t s = lj * 8 + k;
+            c[k] = hh[s] + hh[kSubRow + s] + hh[2 * kSubRow + s] + hh[3 * kSubRow + s];
+            if (c[k]) pm |= 1u << k;
+        }
     }
+    __syncthreads();  // the histogram area is reused below
+    uint32_t *keys = lds + h * 256;
+    uint4 *tab = reinterpret_cast<uint4 *>(lds + 512) + h * 256;
     const uint32_t np = __popc(pm);
     const uint32_t nsym = half_sum(np);
     const uint32_t pre = half_excl_scan(np, lj);
@@ -223,7 +322,7 @@ __global__ __launch_bounds__(64) void k_encode(EncParams p) {
         uint32_t k2 = pre;
 #pragma unroll
         for (int k = 0; k < 8; ++k)
-            if (c[k]) s_keys[h][k2++] = key[k];
+            if (c[k]) keys[k2++] = key[k];
     }
     __syncthreads();
     uint32_t above[8] = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -231,7 +330,7 @@ __global__ __launch_bounds__(64) void k_encode(EncParams p) {
     const uint32_t left_w = max(left * (ni > 0), (uint32_t)__shfl_xor(left * (ni > 0), 32, 64));
     if (left_w > 0) {
         for (uint32_t m = 0; m < nsym_w; ++m) {
-            const uint32_t km = s_keys[h][m & 255];
+            const uint32_t km = keys[m & 255];
             const bool in_list = m < nsym;
 #pragma unroll
             for (int k = 0; k < 8; ++k) above[k] += (in_list && km > key[k]) ? 1u : 0u;
@@ -246,16 +345,20 @@ __global__ __launch_bounds__(64) void k_encode(EncParams p) {
     }
     const uint32_t cbase = half_excl_scan(lsum, lj);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) s_tab[h][lj * 8 + k] = f[k] | ((cbase + cpre[k]) << 16);
+    for (int k = 0; k < 8; ++k) {
+        const double r = f[k] ? enc_reciprocal(f[k]) : 0.0;
+        const uint64_t rb = (uint64_t)__double_as_longlong(r);
+        tab[lj * 8 + k] = make_uint4(f[k], cbase + cpre[k], (uint32_t)rb, (uint32_t)(rb >> 32));
+    }
 
     // record prefix: presence bitmap, frequencies (ascending symbols), pad
     if (valid) {
-        slot[kRecHeaderBytes + lj] = (uint8_t)pm;
+        gstore<uint8_t>(slot + kRecHeaderBytes + lj, (uint8_t)pm);
         uint32_t k2 = pre;
 #pragma unroll
         for (int k = 0; k < 8; ++k)
-            if (c[k]) *(uint16_t *)(slot + 48 + 2 * (k2++)) = (uint16_t)f[k];
-        if (lj == 0 && (nsym & 1)) *(uint16_t *)(slot + 48 + 2 * nsym) = 0;
+            if (c[k]) gstore<uint16_t>(slot + 48 + 2 * (k2++), (uint16_t)f[k]);
+        if (lj == 0 && (nsym & 1)) gstore<uint16_t>(slot + 48 + 2 * nsym, 0);
     }
     __syncthreads();
 
@@ -286,22 +389,18 @@ __global__ __launch_bounds__(64) void k_encode(EncParams p) {
         for (int k = 7; k >= 0; --k) {
             const uint32_t i = ((uint32_t)b * 8 + k) * 32 + lj;
             const bool act = !dead && i < ni;
-            const uint32_t ft = s_tab[h][exponent_of<DT>(cur[k])];
-            const uint32_t fs = ft & 0xFFFFu, c0 = ft >> 16;
+            const uint4 te = tab[exponent_of<DT>(cur[k])];
+            const uint32_t fs = te.x;
             const bool need = act && (x >> 20) >= fs;  // x >= f * 2^20
-            const uint32_t hm = half_mask(__ballot(need), h);
-            const uint32_t cnt = __popc(hm);
-            const uint32_t rank = __popc(hm & ((1u << lj) - 1u));
-            if (!dead && wofs + 2ull * (nw + cnt) > raw_i) dead = true;
-            if (need && !dead) {
-                *(uint16_t *)(slot + raw_i - 2ull * (nw + cnt) + 2ull * rank) = (uint16_t)(x & 0xFFFFu);
-                x >>= 16;
-            }
-            nw += cnt;
-            if (act && !dead) {
-                const uint32_t q = x / fs;
-                x = q * kTableSize + (x - q * fs) + c0;
-            }
+            const HalfBallot hb = half_ballot(need, h, lo_bits);
+            if (!dead && wofs + 2ull * (nw + hb.cnt) > raw_i) dead = true;
+            if (need && !dead)
+                gstore<uint16_t>(slot + raw_i - 2ull * (nw + hb.cnt) + 2ull * hb.rank, (uint16_t)(x & 0xFFFFu));
+            const uint32_t xs = (need && !dead) ? x >> 16 : x;
+            nw += hb.cnt;
+            const uint32_t q = enc_quotient(xs, __hiloint2double((int)te.w, (int)te.z));
+            const uint32_t xe = __umul24(q, kTableSize - fs) + (xs + te.y);  // = q * M + (xs - q * f) + c0
+            x = (act && !dead) ? xe : x;
         }
 #pragma unroll
         for (int k = 0; k < 8; ++k) cur[k] = nxt[k];
@@ -311,18 +410,19 @@ __global__ __launch_bounds__(64) void k_encode(EncParams p) {
     const bool rans = valid && !dead && rans_bytes < raw_i;
     if (valid) {
         if (rans) {
-            *(uint32_t *)(slot + states_offset(nsym) + 4 * lj) = x;
+            gstore<uint32_t>(slot + states_offset(nsym) + 4 * lj, x);
             if (lj == 0) {
-                *(uint4 *)slot = make_uint4(nsym << 16, nw, ni, (uint32_t)rans_bytes);
-                p.rec_sizes[g] = (uint32_t)rans_bytes;
+                gstore<uint4>(slot, make_uint4(nsym << 16, nw, ni, (uint32_t)rans_bytes));
+                gstore<uint32_t>(p.rec_sizes + g, (uint32_t)rans_bytes);
             }
         } else {
             if (lj == 0) {
-                *(uint4 *)slot = make_uint4(1u, 0u, ni, (uint32_t)raw_i);
-                p.rec_sizes[g] = (uint32_t)raw_i;
+                gstore<uint4>(slot, make_uint4(1u, 0u, ni, (uint32_t)raw_i));
+                gstore<uint32_t>(p.rec_sizes + g, (uint32_t)raw_i);
             }
             for (uint32_t k = lj; k + kRecHeaderBytes < raw_i; k += 32)
-                slot[kRecHeaderBytes + k] = k < ni ? (uint8_t)exponent_of<DT>(load_value<DT>(in, k)) : 0;
+                gstore<uint8_t>(slot + kRecHeaderBytes + k,
+                                k < ni ? (uint8_t)exponent_of<DT>(load_value<DT>(in, k)) : (uint8_t)0);
         }
     }
 }
@@ -334,14 +434,14 @@ __global__ __launch_bounds__(256) void k_tile_reduce(const uint32_t *sizes, uint
     __shared__ uint64_t s[256];
     const uint64_t t0 = uint64_t(blockIdx.x) * kTile;
     uint64_t acc = 0;
-    for (uint64_t k = t0 + threadIdx.x; k < t0 + kTile && k < total_chunks; k += 256) acc += sizes[k];
+    for (uint64_t k = t0 + threadIdx.x; k < t0 + kTile && k < total_chunks; k += 256) acc += gload<uint32_t>(sizes + k);
     s[threadIdx.x] = acc;
     __syncthreads();
     for (int o = 128; o > 0; o >>= 1) {
         if ((int)threadIdx.x < o) s[threadIdx.x] += s[threadIdx.x + o];
         __syncthreads();
     }
-    if (threadIdx.x == 0) tile_sums[blockIdx.x] = s[0];
+    if (threadIdx.x == 0) gstore<uint64_t>(tile_sums + blockIdx.x, s[0]);
 }
 
 // exclusive scan of n values into out[0..n] (out[n] = total); in may equal out
@@ -350,7 +450,7 @@ __global__ __launch_bounds__(1024) void k_scan_u64(const uint64_t *in, uint64_t 
     uint64_t carry = 0;
     for (uint64_t base = 0; base < n; base += 1024) {
         const uint64_t i = base + threadIdx.x;
-        const uint64_t v = i < n ? in[i] : 0;
+        const uint64_t v = i < n ? gload<uint64_t>(in + i) : 0;
         s[threadIdx.x] = v;
         __syncthreads();
         for (int o = 1; o < 1024; o <<= 1) {
@@ -359,19 +459,19 @@ __global__ __launch_bounds__(1024) void k_scan_u64(const uint64_t *in, uint64_t 
             s[threadIdx.x] += t;
             __syncthreads();
         }
-        if (i < n) out[i] = carry + s[threadIdx.x] - v;
+        if (i < n) gstore<uint64_t>(out + i, carry + s[threadIdx.x] - v);
         carry += s[1023];
         __syncthreads();
     }
-    if (threadIdx.x == 0) out[n] = carry;
+    if (threadIdx.x == 0) gstore<uint64_t>(out + n, carry);
 }
 
 // global exclusive offset of chunk g (whole wave of 64 lanes participates)
 __device__ inline uint64_t chunk_offset(const uint32_t *sizes, const uint64_t *tile_offs, uint64_t g, uint32_t lane) {
     const uint64_t t0 = (g / kTile) * kTile;
     uint64_t s = 0;
-    for (uint64_t k = t0 + lane; k < g; k += 64) s += sizes[k];
-    return tile_offs[g / kTile] + wave_sum_u64(s);
+    for (uint64_t k = t0 + lane; k < g; k += 64) s += gload<uint32_t>(sizes + k);
+    return gload<uint64_t>(tile_offs + g / kTile) + wave_sum_u64(s);
 }
 
 // ---------------------------------------------------------------------------
@@ -380,19 +480,19 @@ __device__ inline uint64_t chunk_offset(const uint32_t *sizes, const uint64_t *t
 __global__ __launch_bounds__(64) void k_compact(CompactParams p) {
     const uint64_t g = blockIdx.x;
     const uint32_t lane = threadIdx.x;
-    const EncDesc d = p.nbuf == 1 ? p.single : p.descs[find_enc_buffer(p.descs, p.nbuf, g)];
+    const EncDesc d = p.nbuf == 1 ? p.single : load_enc_desc(p.descs + find_enc_buffer(p.descs, p.nbuf, g));
     const uint64_t ci = g - d.chunk_first;
-    const uint32_t size = p.rec_sizes[g];
+    const uint32_t size = gload<uint32_t>(p.rec_sizes + g);
     const uint64_t off_g = chunk_offset(p.rec_sizes, p.tile_offs, g, lane);
     const uint64_t off_first = ci == 0 ? off_g : chunk_offset(p.rec_sizes, p.tile_offs, d.chunk_first, lane);
     const uint64_t rec_off = off_g - off_first;
     uint8_t *out = d.out;
-    if (lane == 0) *(uint64_t *)(out + kHeaderBytes + 8 * ci) = rec_off;
+    if (lane == 0) gstore<uint64_t>(out + kHeaderBytes + 8 * ci, rec_off);
     if (ci + 1 == d.chunks) {
         const uint64_t total = d.exp_off + rec_off + size;
         if (lane == 0) {
-            *(uint64_t *)(out + kHeaderBytes + 8 * d.chunks) = rec_off + size;
-            *d.out_size = total;
+            gstore<uint64_t>(out + kHeaderBytes + 8 * d.chunks, rec_off + size);
+            gstore<uint64_t>(d.out_size, total);
         }
         if (lane < 16) {
             uint32_t wv = 0;
@@ -413,30 +513,27 @@ __global__ __launch_bounds__(64) void k_compact(CompactParams p) {
                 case 13: wv = (uint32_t)(total >> 32); break;
                 default: wv = 0; break;
             }
-            ((uint32_t *)out)[lane] = wv;
+            gstore<uint32_t>(out + 4 * lane, wv);
         }
         // zero the gaps after the index and after the sign+mantissa region
         const uint64_t gap0 = kHeaderBytes + 8 * (d.chunks + 1);
-        for (uint64_t k = gap0 + lane; k < d.sm_off; k += 64) out[k] = 0;
+        for (uint64_t k = gap0 + lane; k < d.sm_off; k += 64) gstore<uint8_t>(out + k, 0);
         const uint64_t gap1 = d.sm_off + uint64_t(raw_bytes_per_value(p.dtype)) * d.n;
-        for (uint64_t k = gap1 + lane; k < d.exp_off; k += 64) out[k] = 0;
+        for (uint64_t k = gap1 + lane; k < d.exp_off; k += 64) gstore<uint8_t>(out + k, 0);
     }
     // copy the record
     const uint8_t *src = p.slots + g * p.slot_stride;
     uint8_t *dst = out + d.exp_off + rec_off;
-    const uint32_t mode = src[0];
-    if (mode == 0) {
-        const uint32_t nsym = *(const uint16_t *)(src + 2);
-        const uint32_t nw = *(const uint32_t *)(src + 4);
-        const uint32_t ni = *(const uint32_t *)(src + 8);
+    const uint4 rh = gload<uint4>(src);
+    if ((rh.x & 0xFFu) == 0) {
+        const uint32_t nsym = rh.x >> 16, nw = rh.y, ni = rh.z;
         const uint32_t wofs = (uint32_t)words_offset(nsym);
-        for (uint32_t k = lane; k < wofs / 4; k += 64) ((uint32_t *)dst)[k] = ((const uint32_t *)src)[k];
-        const uint16_t *wsrc = (const uint16_t *)(src + raw_record_bytes(ni) - 2ull * nw);
-        uint16_t *wdst = (uint16_t *)(dst + wofs);
-        for (uint32_t k = lane; k < nw; k += 64) wdst[k] = wsrc[k];
-        for (uint32_t k = wofs + 2 * nw + lane; k < size; k += 64) dst[k] = 0;
+        for (uint32_t k = lane; k < wofs / 4; k += 64) gstore<uint32_t>(dst + 4 * k, gload<uint32_t>(src + 4 * k));
+        const uint8_t *wsrc = src + raw_record_bytes(ni) - 2ull * nw;
+        for (uint32_t k = lane; k < nw; k += 64) gstore<uint16_t>(dst + wofs + 2 * k, gload<uint16_t>(wsrc + 2 * k));
+        for (uint32_t k = wofs + 2 * nw + lane; k < size; k += 64) gstore<uint8_t>(dst + k, 0);
     } else {
-        for (uint32_t k = lane; k < size / 16; k += 64) ((uint4 *)dst)[k] = ((const uint4 *)src)[k];
+        for (uint32_t k = lane; k < size / 16; k += 64) gstore<uint4>(dst + 16 * k, gload<uint4>(src + 16 * k));
     }
 }
 
@@ -444,14 +541,13 @@ __global__ __launch_bounds__(64) void k_compact(CompactParams p) {
 __global__ void k_empty_headers(const EncDesc *descs, EncDesc single, uint32_t nbuf, int dtype, uint32_t chunk_elems) {
     const uint32_t b = blockIdx.x * blockDim.x + threadIdx.x;
     if (b >= nbuf) return;
-    const EncDesc d = nbuf == 1 ? single : descs[b];
+    const EncDesc d = nbuf == 1 ? single : load_enc_desc(descs + b);
     if (d.n != 0) return;
-    uint32_t *o = (uint32_t *)d.out;
     const uint32_t hdr[20] = {kMagic, kVersion | (uint32_t(dtype) << 16) | (kProbBits << 24),
                               kLanes | (raw_bytes_per_value(dtype) << 8), chunk_elems, 0, 0, 0, 0, 80, 0, 80, 0,
                               80, 0, 0, 0, 0, 0, 0, 0};
-    for (int k = 0; k < 20; ++k) o[k] = hdr[k];
-    *d.out_size = 80;
+    for (int k = 0; k < 20; ++k) gstore<uint32_t>(d.out + 4 * k, hdr[k]);
+    gstore<uint64_t>(d.out_size, 80);
 }
 
 // ---------------------------------------------------------------------------
@@ -460,12 +556,12 @@ __global__ void k_empty_headers(const EncDesc *descs, EncDesc single, uint32_t n
 __global__ void k_dec_validate(DecParams p) {
     const uint32_t b = blockIdx.x * blockDim.x + threadIdx.x;
     if (b >= p.nbuf) return;
-    const DecDesc d = p.nbuf == 1 ? p.single : p.descs[b];
+    const DecDesc d = p.nbuf == 1 ? p.single : load_dec_desc(p.descs + b);
     bool ok = d.in_bytes >= kHeaderBytes;
     DecInfo inf = {};
     if (ok) {
-        const uint4 h0 = ((const uint4 *)d.in)[0], h1 = ((const uint4 *)d.in)[1];
-        const uint4 h2 = ((const uint4 *)d.in)[2], h3 = ((const uint4 *)d.in)[3];
+        const uint4 h0 = gload<uint4>(d.in), h1 = gload<uint4>(d.in + 16);
+        const uint4 h2 = gload<uint4>(d.in + 32), h3 = gload<uint4>(d.in + 48);
         const uint32_t r = raw_bytes_per_value(p.dtype);
         // V1 magic, version, fixed coder parameters; V2 dtype and count
         ok = h0.x == kMagic && (h0.y & 0xFFFFu) == kVersion && ((h0.y >> 16) & 0xFFu) == (uint32_t)p.dtype &&
@@ -485,8 +581,8 @@ __global__ void k_dec_validate(DecParams p) {
                  total >= exp_off;
             if (ok) {
                 // V5 ends of the index
-                const uint64_t first = *(const uint64_t *)(d.in + kHeaderBytes);
-                const uint64_t last = *(const uint64_t *)(d.in + kHeaderBytes + 8 * C);
+                const uint64_t first = gload<uint64_t>(d.in + kHeaderBytes);
+                const uint64_t last = gload<uint64_t>(d.in + kHeaderBytes + 8 * C);
                 ok = first == 0 && last == total - exp_off;
             }
             inf.chunks = ok ? C : 0;
@@ -497,54 +593,82 @@ __global__ void k_dec_validate(DecParams p) {
         }
     }
     if (!ok) inf.chunks = 0;
-    p.info[b] = inf;
-    p.status[b] = ok ? 0u : 3u;
+    const uint4 *iv = reinterpret_cast<const uint4 *>(&inf);
+    for (int k = 0; k < 4; ++k) gstore<uint4>(reinterpret_cast<uint4 *>(p.info + b) + k, iv[k]);
+    gstore<uint32_t>(p.status + b, ok ? 0u : 3u);
     if (p.nbuf == 1) {
-        p.chunk_first[0] = 0;
-        p.chunk_first[1] = inf.chunks;
+        gstore<uint64_t>(p.chunk_first, 0);
+        gstore<uint64_t>(p.chunk_first + 1, inf.chunks);
     } else {
-        p.chunk_first[b] = inf.chunks;  // counts; scanned in place afterwards
+        gstore<uint64_t>(p.chunk_first + b, inf.chunks);  // counts; scanned in place afterwards
     }
+}
+
+// LDS of one decode workgroup (two chunks), 10 KiB:
+//   s_sym [2][4096] u8   slot -> rank of its symbol among the present symbols
+//   s_rk  [2][256]  u32  rank -> (f - 1) | c0 << 12 | symbol << 24
+// so one step costs two dependent LDS reads.  Renormalisation words come from
+// a register window (two 16-bit words per lane: 64 words per half-wave) with
+// two further 32-word blocks in flight, fetched with ds_bpermute after the
+// ballot; the global loads are issued about 64 words before they are needed,
+// off the state's dependency chain.  Sign+mantissa bytes are loaded 4 steps
+// ahead.  Chunks stored RAW are copied in a separate loop.
+template <int DT>
+__device__ inline uint32_t load_sm(const uint8_t *sm, uint32_t i) {
+    if (DT == 1) return gload<uint8_t>(sm + i);
+    const uint8_t *q = sm + 3ull * i;
+    return uint32_t(gload<uint8_t>(q)) | (uint32_t(gload<uint8_t>(q + 1)) << 8) |
+           (uint32_t(gload<uint8_t>(q + 2)) << 16);
+}
+
+template <int DT>
+__device__ inline void store_value(uint8_t *outp, uint32_t i, uint32_t ex, uint32_t smv) {
+    if (DT == 1)
+        gstore<uint16_t>(outp + 2ull * i, (uint16_t)(((smv & 0x80u) << 8) | (ex << 7) | (smv & 0x7Fu)));
+    else
+        gstore<uint32_t>(outp + 4ull * i, ((smv & 0x800000u) << 8) | (ex << 23) | (smv & 0x7FFFFFu));
 }
 
 template <int DT>
 __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
     constexpr uint32_t EB = DT == 1 ? 2 : 4;
     constexpr uint32_t R = DT == 1 ? 1 : 3;
-    __shared__ uint8_t s_sym[2][kTableSize];
-    __shared__ uint32_t s_ft[2][256];  // f | c0 << 16
-    __shared__ uint8_t s_plist[2][256];
+    __shared__ __align__(16) uint8_t s_sym[2][kTableSize];
+    __shared__ __align__(16) uint32_t s_rk[2][256];
 
     const uint32_t lane = threadIdx.x;
     const uint32_t h = lane >> 5, lj = lane & 31;
-    const uint64_t G = p.chunk_first[p.nbuf];
+    const uint32_t lo_bits = h ? 0xFFFFFFFFu : 0u;
+    const uint64_t G = gload<uint64_t>(p.chunk_first + p.nbuf);
 
     for (uint64_t pair = blockIdx.x; pair * 2 < G; pair += gridDim.x) {
         const uint64_t g = pair * 2 + h;
         bool ok = g < G;
         const uint64_t gq = ok ? g : G - 1;
         const uint32_t b = p.nbuf == 1 ? 0u : find_dec_buffer(p.chunk_first, p.nbuf, gq);
-        const DecDesc d = p.nbuf == 1 ? p.single : p.descs[b];
-        const DecInfo inf = p.info[b];
-        ok = ok && p.status[b] == 0;
+        const DecDesc d = p.nbuf == 1 ? p.single : load_dec_desc(p.descs + b);
+        const uint64_t ce = gload<uint64_t>(&p.info[b].chunk_elems);
+        const uint64_t sm_off = gload<uint64_t>(&p.info[b].sm_off);
+        const uint64_t exp_off = gload<uint64_t>(&p.info[b].exp_off);
+        const uint64_t total = gload<uint64_t>(&p.info[b].total);
+        ok = ok && gload<uint32_t>(p.status + b) == 0;
         const bool real = ok;
-        const uint64_t ci = gq - p.chunk_first[b];
-        const uint64_t ce = inf.chunk_elems;
+        const uint64_t ci = gq - gload<uint64_t>(p.chunk_first + b);
         const uint64_t v0 = ci * ce;
         const uint32_t ni = ok ? (uint32_t)min<uint64_t>(ce, d.n - v0) : 0u;
 
         // record bounds from the index (V5) and record header (V6)
         uint64_t a = 0, e = 0;
         if (ok) {
-            a = *(const uint64_t *)(d.in + kHeaderBytes + 8 * ci);
-            e = *(const uint64_t *)(d.in + kHeaderBytes + 8 * (ci + 1));
-            ok = (a & 15u) == 0 && (e & 15u) == 0 && a <= e && e <= inf.total - inf.exp_off && e - a >= 16;
+            a = gload<uint64_t>(d.in + kHeaderBytes + 8 * ci);
+            e = gload<uint64_t>(d.in + kHeaderBytes + 8 * (ci + 1));
+            ok = (a & 15u) == 0 && (e & 15u) == 0 && a <= e && e <= total - exp_off && e - a >= 16;
         }
-        const uint8_t *rec = d.in + inf.exp_off + a;
+        const uint8_t *rec = d.in + exp_off + a;
         const uint64_t len = e - a;
         uint32_t mode = 1, nsym = 0, nw = 0;
         if (ok) {
-            const uint4 rh = *(const uint4 *)rec;
+            const uint4 rh = gload<uint4>(rec);
             mode = rh.x & 0xFFu;
             nsym = rh.x >> 16;
             nw = rh.y;
@@ -555,7 +679,7 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
         const bool coded = ok && mode == 0;
 
         // table: presence bitmap byte lj covers symbols 8lj..8lj+7 (V7)
-        uint32_t pb = coded ? rec[kRecHeaderBytes + lj] : 0u;
+        const uint32_t pb = coded ? gload<uint8_t>(rec + kRecHeaderBytes + lj) : 0u;
         const uint32_t np = __popc(pb);
         const uint32_t pre = half_excl_scan(np, lj);
         uint32_t fk[8], lsum = 0, cpre[8];
@@ -566,7 +690,7 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
             for (int k = 0; k < 8; ++k) {
                 fk[k] = 0;
                 if ((pb >> k) & 1u) {
-                    fk[k] = (k2 < nsym) ? *(const uint16_t *)(rec + 48 + 2 * k2) : 0u;
+                    fk[k] = (k2 < nsym) ? gload<uint16_t>(rec + 48 + 2 * k2) : 0u;
                     if (fk[k] == 0 || fk[k] > kTableSize) fok = false;
                     ++k2;
                 }
@@ -584,73 +708,90 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
             uint32_t k2 = pre;
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
-                s_ft[h][lj * 8 + k] = fk[k] | ((cbase + cpre[k]) << 16);
-                if (fk[k]) s_plist[h][k2++] = (uint8_t)(lj * 8 + k);
+                if (fk[k]) s_rk[h][k2++] = (fk[k] - 1) | ((cbase + cpre[k]) << 12) | ((lj * 8 + k) << 24);
             }
         }
         __syncthreads();
         if (coded_ok) {
             for (uint32_t m = 0; m < nsym; ++m) {
-                const uint32_t s = s_plist[h][m];
-                const uint32_t ft = s_ft[h][s];
-                const uint32_t fs = ft & 0xFFFFu, c0 = ft >> 16;
-                for (uint32_t k = lj; k < fs; k += 32) s_sym[h][c0 + k] = (uint8_t)s;
+                const uint32_t em = s_rk[h][m];
+                const uint32_t fs = (em & 0xFFFu) + 1, c0 = (em >> 12) & 0xFFFu;
+                for (uint32_t k = lj; k < fs; k += 32) s_sym[h][c0 + k] = (uint8_t)m;
             }
         }
         __syncthreads();
 
         // states (V8)
         uint32_t x = kStateLow;
-        const uint8_t *words = rec + words_offset(nsym);
-        if (coded_ok) x = *(const uint32_t *)(rec + states_offset(nsym) + 4 * lj);
+        if (coded_ok) x = gload<uint32_t>(rec + states_offset(nsym) + 4 * lj);
         const bool sbad = half_mask(__ballot(coded_ok && x < kStateLow), h) != 0;
         ok = ok && !sbad;
+        const bool rans_run = ok && mode == 0;
+        const bool raw_run = ok && mode == 1;
 
-        // decode (V9: never read past n_words; end state L on every lane)
-        const uint8_t *sm = d.in + inf.sm_off + v0 * R;
+        // word window: words [base, base+64) in P (low half: base + lj, high
+        // half: base + 32 + lj); C and D hold the next two 32-word blocks
+        const uint8_t *wp = rec + words_offset(nsym);
+        uint32_t base = 0;
+        uint32_t P = 0, C = 0, Dw = 0;
+        if (rans_run) {
+            P = (lj < nw ? (uint32_t)gload<uint16_t>(wp + 2 * lj) : 0u) |
+                ((32 + lj < nw ? (uint32_t)gload<uint16_t>(wp + 2 * (32 + lj)) : 0u) << 16);
+            C = 64 + lj < nw ? gload<uint16_t>(wp + 2 * (64 + lj)) : 0u;
+            Dw = 96 + lj < nw ? gload<uint16_t>(wp + 2 * (96 + lj)) : 0u;
+        }
+
+        // rANS decode (V9: never read past n_words; end state L on every lane)
+        const uint8_t *sm = d.in + sm_off + v0 * R;
         uint8_t *outp = d.out + v0 * EB;
-        const uint32_t T = ok ? (ni + 31) / 32 : 0u;
+        const uint32_t T = rans_run ? (ni + 31) / 32 : 0u;
         const uint32_t Tw = max(T, (uint32_t)__shfl_xor(T, 32, 64));
+        bool run = rans_run;
         uint32_t pos = 0;
-        for (uint32_t t = 0; t < Tw; ++t) {
-            const uint32_t i = t * 32 + lj;
-            const bool act = ok && i < ni;
-            const uint32_t wpre = (ok && mode == 0 && pos + lj < nw) ? *(const uint16_t *)(words + 2ull * (pos + lj)) : 0u;
-            uint32_t ex = 0;
-            bool need = false;
-            if (act) {
-                if (mode == 0) {
-                    const uint32_t slot = x & (kTableSize - 1);
-                    const uint32_t s = s_sym[h][slot];
-                    const uint32_t ft = s_ft[h][s];
-                    x = (ft & 0xFFFFu) * (x >> kProbBits) + slot - (ft >> 16);
-                    need = x < kStateLow;
-                    ex = s;
-                } else {
-                    ex = rec[kRecHeaderBytes + i];
+        uint32_t smq[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const uint32_t i = u * 32 + lj;
+            smq[u] = (rans_run && i < ni) ? load_sm<DT>(sm, i) : 0u;
+        }
+        for (uint32_t tb = 0; tb < Tw; tb += 4) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const uint32_t i = (tb + u) * 32 + lj;
+                const bool act = run && i < ni;
+                const uint32_t slot = x & (kTableSize - 1);
+                const uint32_t em = s_rk[h][s_sym[h][slot]];
+                const uint32_t xd = __umul24((em & 0xFFFu) + 1, x >> kProbBits) + slot - ((em >> 12) & 0xFFFu);
+                const bool need = act && xd < kStateLow;
+                const HalfBallot hb = half_ballot(need, h, lo_bits);
+                const uint32_t k = pos - base + hb.rank;  // < 64
+                const uint32_t wv = (uint32_t)__shfl((int)P, (int)(k & 31u), 32);
+                const uint32_t w = k < 32 ? (wv & 0xFFFFu) : (wv >> 16);
+                run = run && pos + hb.cnt <= nw;
+                const uint32_t xn = need ? (xd << 16) | w : xd;
+                x = act ? xn : x;
+                pos += hb.cnt;
+                if (pos - base >= 32) {
+                    base += 32;
+                    P = (P >> 16) | (C << 16);
+                    C = Dw;
+                    const uint32_t wi = base + 96 + lj;
+                    Dw = (rans_run && wi < nw) ? gload<uint16_t>(wp + 2ull * wi) : 0u;
                 }
-            }
-            const uint32_t hm = half_mask(__ballot(need), h);
-            const uint32_t cnt = __popc(hm);
-            const uint32_t rank = __popc(hm & ((1u << lj) - 1u));
-            const uint32_t w = (uint32_t)__shfl((int)wpre, (int)rank, 32);
-            if (ok && pos + cnt > nw) ok = false;
-            if (need && ok) x = (x << 16) | w;
-            pos += cnt;
-            if (act && ok) {
-                if (DT == 1) {
-                    const uint32_t smb = sm[i];
-                    ((uint16_t *)outp)[i] = (uint16_t)(((smb & 0x80u) << 8) | (ex << 7) | (smb & 0x7Fu));
-                } else {
-                    const uint8_t *q = sm + 3ull * i;
-                    const uint32_t s24 = uint32_t(q[0]) | (uint32_t(q[1]) << 8) | (uint32_t(q[2]) << 16);
-                    ((uint32_t *)outp)[i] = ((s24 & 0x800000u) << 8) | (ex << 23) | (s24 & 0x7FFFFFu);
-                }
+                const uint32_t smv = smq[u];
+                const uint32_t inext = i + 4 * 32;
+                smq[u] = (rans_run && inext < ni) ? load_sm<DT>(sm, inext) : 0u;
+                if (act && run) store_value<DT>(outp, i, em >> 24, smv);
             }
         }
-        const bool endbad = half_mask(__ballot(ok && mode == 0 && (x != kStateLow || pos != nw)), h) != 0;
+        const bool endbad = half_mask(__ballot(rans_run && (!run || x != kStateLow || pos != nw)), h) != 0;
         ok = ok && !endbad;
-        if (real && !ok && lj == 0) p.status[b] = 3u;
+        // chunks stored RAW: exponent bytes straight from the record
+        if (raw_run) {
+            for (uint32_t i = lj; i < ni; i += 32)
+                store_value<DT>(outp, i, gload<uint8_t>(rec + kRecHeaderBytes + i), load_sm<DT>(sm, i));
+        }
+        if (real && !ok && lj == 0) gstore<uint32_t>(p.status + b, 3u);
         __syncthreads();
     }
 }
