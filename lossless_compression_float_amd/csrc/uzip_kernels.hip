@@ -112,7 +112,7 @@ struct HalfBallot {
     uint32_t cnt, rank;
 };
 __device__ inline HalfBallot half_ballot(bool pred, uint32_t h, uint32_t lo_bits) {
-    const uint64_t m = __ballot(pred);
+    const uint64_t m = __builtin_amdgcn_ballot_w64(pred);
     const uint32_t mlo = (uint32_t)m, mhi = (uint32_t)(m >> 32);
     const uint32_t below = __builtin_amdgcn_mbcnt_hi(mhi, __builtin_amdgcn_mbcnt_lo(mlo, 0u));
     const uint32_t plo = __popc(mlo);
@@ -364,9 +364,14 @@ __global__ __launch_bounds__(64) void k_encode(EncParams p) {
 
     // ---- pass 2: 32-lane interleaved rANS, steps from the last down to 0 ----
     // Words of one step are placed, lanes ascending, right before the words of
-    // the following step, filling the slot from its end.
+    // the following step, filling the slot from its end.  Input values are
+    // prefetched one 8-step block ahead with loads that are always issued
+    // (clamped to the chunk), so the compiler's wait counts stay exact.
     const uint64_t raw_i = raw_record_bytes(ni);
     const uint64_t wofs = words_offset(nsym);
+    const uint32_t wcap = valid ? (uint32_t)((raw_i - wofs) / 2) : 0u;  // words that fit before the chunk goes RAW
+    const uint32_t last = ni ? ni - 1 : 0u;
+    uint8_t *wend = slot + raw_i;  // words fill [wend - 2 nw, wend)
     uint32_t x = kStateLow;
     uint32_t nw = 0;
     bool dead = !valid;  // set when the words outgrow the RAW size: the chunk goes RAW
@@ -375,16 +380,12 @@ __global__ __launch_bounds__(64) void k_encode(EncParams p) {
     const uint32_t nblk = (Tw + 7) / 8;
     uint32_t cur[8], nxt[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        const uint32_t i = ((nblk - 1) * 8 + k) * 32 + lj;
-        cur[k] = (nblk > 0 && i < ni) ? load_value<DT>(in, i) : 0u;
-    }
+    for (int k = 0; k < 8; ++k) cur[k] = load_value<DT>(in, min(((nblk - 1) * 8 + k) * 32 + lj, last));
     for (int32_t b = (int32_t)nblk - 1; b >= 0; --b) {
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const uint32_t i = ((uint32_t)(b - 1) * 8 + k) * 32 + lj;
-            nxt[k] = (b > 0 && i < ni) ? load_value<DT>(in, i) : 0u;
-        }
+        for (int k = 0; k < 8; ++k) nxt[k] = load_value<DT>(in, min(((uint32_t)(b - 1) * 8 + k) * 32 + lj, last));
+        // a block emits at most 256 words: check the room once per block
+        const bool roomy = nw + 256 <= wcap;
 #pragma unroll
         for (int k = 7; k >= 0; --k) {
             const uint32_t i = ((uint32_t)b * 8 + k) * 32 + lj;
@@ -393,10 +394,10 @@ __global__ __launch_bounds__(64) void k_encode(EncParams p) {
             const uint32_t fs = te.x;
             const bool need = act && (x >> 20) >= fs;  // x >= f * 2^20
             const HalfBallot hb = half_ballot(need, h, lo_bits);
-            if (!dead && wofs + 2ull * (nw + hb.cnt) > raw_i) dead = true;
-            if (need && !dead)
-                gstore<uint16_t>(slot + raw_i - 2ull * (nw + hb.cnt) + 2ull * hb.rank, (uint16_t)(x & 0xFFFFu));
-            const uint32_t xs = (need && !dead) ? x >> 16 : x;
+            if (!roomy && !dead && nw + hb.cnt > wcap) dead = true;
+            const bool emit = need && !dead;
+            if (emit) gstore<uint16_t>(wend - 2ull * (nw + hb.cnt) + 2ull * hb.rank, (uint16_t)(x & 0xFFFFu));
+            const uint32_t xs = emit ? x >> 16 : x;
             nw += hb.cnt;
             const uint32_t q = enc_quotient(xs, __hiloint2double((int)te.w, (int)te.z));
             const uint32_t xe = __umul24(q, kTableSize - fs) + (xs + te.y);  // = q * M + (xs - q * f) + c0
@@ -729,62 +730,57 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
         const bool rans_run = ok && mode == 0;
         const bool raw_run = ok && mode == 1;
 
-        // word window: words [base, base+64) in P (low half: base + lj, high
-        // half: base + 32 + lj); C and D hold the next two 32-word blocks
-        const uint8_t *wp = rec + words_offset(nsym);
-        uint32_t base = 0;
-        uint32_t P = 0, C = 0, Dw = 0;
-        if (rans_run) {
-            P = (lj < nw ? (uint32_t)gload<uint16_t>(wp + 2 * lj) : 0u) |
-                ((32 + lj < nw ? (uint32_t)gload<uint16_t>(wp + 2 * (32 + lj)) : 0u) << 16);
-            C = 64 + lj < nw ? gload<uint16_t>(wp + 2 * (64 + lj)) : 0u;
-            Dw = 96 + lj < nw ? gload<uint16_t>(wp + 2 * (96 + lj)) : 0u;
-        }
-
-        // rANS decode (V9: never read past n_words; end state L on every lane)
-        const uint8_t *sm = d.in + sm_off + v0 * R;
+        // Word window: words [base, base+64) in P (low 16 bits: word base + lj,
+        // high: base + 32 + lj).  NW holds word base + 64 + lj, loaded one step
+        // before it can be needed.  Every load is issued unconditionally at an
+        // address clamped into the record, so the compiler's wait counts stay
+        // exact and no wait lands on a just-issued load.  Words past n_words
+        // are never consumed by a valid stream; a stream that tries is caught
+        // by the end check (pos != n_words).
+        // A half that is not decoding a validated coded chunk points its loads
+        // at the workspace (always readable) instead of at offsets taken from
+        // an unvalidated header.
+        const uint8_t *safe = reinterpret_cast<const uint8_t *>(p.chunk_first);
+        const uint8_t *wbase = (rans_run && nw) ? rec + words_offset(nsym) : safe;
+        const uint32_t wmax = (rans_run && nw) ? nw - 1 : 0u;
+        const uint8_t *sm = raw_run || rans_run ? d.in + sm_off + v0 * R : safe;
+        const uint32_t last = (rans_run && ni) ? ni - 1 : 0u;
         uint8_t *outp = d.out + v0 * EB;
+        uint32_t base = 0, pos = 0;
+        uint32_t P = uint32_t(gload<uint16_t>(wbase + 2 * min(lj, wmax))) |
+                     (uint32_t(gload<uint16_t>(wbase + 2 * min(32 + lj, wmax))) << 16);
+        uint32_t NW = gload<uint16_t>(wbase + 2 * min(64 + lj, wmax));
         const uint32_t T = rans_run ? (ni + 31) / 32 : 0u;
         const uint32_t Tw = max(T, (uint32_t)__shfl_xor(T, 32, 64));
-        bool run = rans_run;
-        uint32_t pos = 0;
         uint32_t smq[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const uint32_t i = u * 32 + lj;
-            smq[u] = (rans_run && i < ni) ? load_sm<DT>(sm, i) : 0u;
-        }
+        for (int u = 0; u < 4; ++u) smq[u] = load_sm<DT>(sm, min(u * 32 + lj, last));
         for (uint32_t tb = 0; tb < Tw; tb += 4) {
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const uint32_t i = (tb + u) * 32 + lj;
-                const bool act = run && i < ni;
                 const uint32_t slot = x & (kTableSize - 1);
                 const uint32_t em = s_rk[h][s_sym[h][slot]];
                 const uint32_t xd = __umul24((em & 0xFFFu) + 1, x >> kProbBits) + slot - ((em >> 12) & 0xFFFu);
+                const bool act = i < ni;
                 const bool need = act && xd < kStateLow;
                 const HalfBallot hb = half_ballot(need, h, lo_bits);
                 const uint32_t k = pos - base + hb.rank;  // < 64
                 const uint32_t wv = (uint32_t)__shfl((int)P, (int)(k & 31u), 32);
                 const uint32_t w = k < 32 ? (wv & 0xFFFFu) : (wv >> 16);
-                run = run && pos + hb.cnt <= nw;
                 const uint32_t xn = need ? (xd << 16) | w : xd;
                 x = act ? xn : x;
                 pos += hb.cnt;
-                if (pos - base >= 32) {
-                    base += 32;
-                    P = (P >> 16) | (C << 16);
-                    C = Dw;
-                    const uint32_t wi = base + 96 + lj;
-                    Dw = (rans_run && wi < nw) ? gload<uint16_t>(wp + 2ull * wi) : 0u;
-                }
+                const bool shift = pos - base >= 32;
+                P = shift ? (P >> 16) | (NW << 16) : P;
+                base += shift ? 32u : 0u;
+                NW = gload<uint16_t>(wbase + 2 * min(base + 64 + lj, wmax));
                 const uint32_t smv = smq[u];
-                const uint32_t inext = i + 4 * 32;
-                smq[u] = (rans_run && inext < ni) ? load_sm<DT>(sm, inext) : 0u;
-                if (act && run) store_value<DT>(outp, i, em >> 24, smv);
+                smq[u] = load_sm<DT>(sm, min(i + 4 * 32, last));
+                if (rans_run && act) store_value<DT>(outp, i, em >> 24, smv);
             }
         }
-        const bool endbad = half_mask(__ballot(rans_run && (!run || x != kStateLow || pos != nw)), h) != 0;
+        const bool endbad = half_mask(__ballot(rans_run && (x != kStateLow || pos != nw)), h) != 0;
         ok = ok && !endbad;
         // chunks stored RAW: exponent bytes straight from the record
         if (raw_run) {
