@@ -64,7 +64,7 @@ EncWs enc_ws(uint64_t nbuf, uint64_t chunks, uint64_t ce) {
 }
 
 struct DecWs {
-    uint64_t descs, info, chunk_first, bytes;
+    uint64_t descs, info, pair_first, bytes;
 };
 
 DecWs dec_ws(uint64_t nbuf) {
@@ -74,7 +74,7 @@ DecWs dec_ws(uint64_t nbuf) {
     o += al(nbuf > 1 ? nbuf * sizeof(DecDesc) : 0);
     w.info = o;
     o += al(nbuf * sizeof(DecInfo));
-    w.chunk_first = o;
+    w.pair_first = o;
     o += al((nbuf + 1) * 8);
     w.bytes = o + kWsAlign;
     return w;
@@ -150,7 +150,7 @@ uzip_status decompress_impl(uzip_dtype dtype, std::vector<DecDesc> &descs, uint3
     vp.nbuf = nbuf;
     vp.dtype = dtype;
     vp.info = reinterpret_cast<DecInfo *>(base + w.info);
-    vp.chunk_first = reinterpret_cast<uint64_t *>(base + w.chunk_first);
+    vp.pair_first = reinterpret_cast<uint64_t *>(base + w.pair_first);
     vp.status = d_status;
     if (nbuf == 1) {
         vp.single = descs[0];
@@ -165,7 +165,7 @@ uzip_status decompress_impl(uzip_dtype dtype, std::vector<DecDesc> &descs, uint3
     dp.single = vp.single;
     dp.nbuf = nbuf;
     dp.info = vp.info;
-    dp.chunk_first = vp.chunk_first;
+    dp.pair_first = vp.pair_first;
     dp.status = d_status;
     const hipError_t e = launch_decompress(vp, dp, dtype, max_chunks, stream);
     return e == hipSuccess ? UZIP_OK : UZIP_ERR_DEVICE;

@@ -77,6 +77,58 @@ __device__ inline void gstore(void *p, T v) {
     GAccess<T>::store(p, v);
 }
 
+// Raw buffer resources.  A resource carries a wave-uniform base address and
+// a byte size; lanes pass 32-bit offsets, and the hardware range check turns
+// loads at or past the size into zeros and drops such stores.  The coding
+// kernels give each wave a resource per region of its chunk pair, so ragged
+// tails, idle half-waves and corrupt offsets never touch memory outside that
+// region, without per-step clamping or branches.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw 32-bit buffer access on the gfx9 family
+constexpr uint32_t kOutOfRange = 0x80000000u;  // an offset past every resource's size
+
+__device__ inline uint64_t uniform_u64(uint64_t v) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return (uint64_t(hi) << 32) | lo;
+}
+__device__ inline uint32_t uniform_u32(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ inline rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    const uint64_t b = uniform_u64(reinterpret_cast<uint64_t>(base));
+    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(b), (short)0, (int)uniform_u32(bytes),
+                                            (int)kRsrcWord3);
+}
+__device__ inline uint32_t bld8(rsrc_t r, uint32_t off) { return __builtin_amdgcn_raw_buffer_load_b8(r, (int)off, 0, 0); }
+__device__ inline uint32_t bld16(rsrc_t r, uint32_t off) { return __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0); }
+__device__ inline uint32_t bld32(rsrc_t r, uint32_t off) { return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0); }
+__device__ inline uint4 bld128(rsrc_t r, uint32_t off) {
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ inline void bst16(rsrc_t r, uint32_t off, uint32_t v) {
+    __builtin_amdgcn_raw_buffer_store_b16((unsigned short)v, r, (int)off, 0, 0);
+}
+__device__ inline void bst32(rsrc_t r, uint32_t off, uint32_t v) {
+    __builtin_amdgcn_raw_buffer_store_b32(v, r, (int)off, 0, 0);
+}
+
+// Lane masks.  lanes_lt(a, b) is the 64-bit mask of lanes with a < b (one
+// compare, no 0/1 materialisation).  vsel(mask, a, b) picks b in the lanes
+// set in a wave-uniform mask and a elsewhere: a single v_cndmask_b32 reading
+// the mask from scalar registers.
+__device__ inline uint64_t lanes_lt(uint32_t a, uint32_t b) { return __builtin_amdgcn_uicmp(a, b, 36 /* ULT */); }
+__device__ inline uint32_t vsel(uint64_t mask, uint32_t if0, uint32_t if1) {
+    uint32_t r;
+    asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(r) : "v"(if0), "v"(if1), "s"(mask));
+    return r;
+}
+// mask of the first min(k, 32) lanes of half-wave h, computed on the scalar unit
+__device__ inline uint64_t half_prefix_mask(uint32_t k, uint32_t h) {
+    const uint32_t m = k >= 32 ? 0xFFFFFFFFu : ((1u << k) - 1u);
+    return h ? uint64_t(m) << 32 : uint64_t(m);
+}
+constexpr uint64_t kHighHalf = 0xFFFFFFFF00000000ull;
+
 // ---------------------------------------------------------------------------
 // half-wave (32-lane segment of a wave64) collectives
 // ---------------------------------------------------------------------------
@@ -597,37 +649,36 @@ __global__ void k_dec_validate(DecParams p) {
     const uint4 *iv = reinterpret_cast<const uint4 *>(&inf);
     for (int k = 0; k < 4; ++k) gstore<uint4>(reinterpret_cast<uint4 *>(p.info + b) + k, iv[k]);
     gstore<uint32_t>(p.status + b, ok ? 0u : 3u);
+    const uint64_t pairs = (inf.chunks + 1) / 2;
     if (p.nbuf == 1) {
-        gstore<uint64_t>(p.chunk_first, 0);
-        gstore<uint64_t>(p.chunk_first + 1, inf.chunks);
+        gstore<uint64_t>(p.pair_first, 0);
+        gstore<uint64_t>(p.pair_first + 1, pairs);
     } else {
-        gstore<uint64_t>(p.chunk_first + b, inf.chunks);  // counts; scanned in place afterwards
+        gstore<uint64_t>(p.pair_first + b, pairs);  // counts; scanned in place afterwards
     }
 }
 
 // LDS of one decode workgroup (two chunks), 10 KiB:
 //   s_sym [2][4096] u8   slot -> rank of its symbol among the present symbols
 //   s_rk  [2][256]  u32  rank -> (f - 1) | c0 << 12 | symbol << 24
-// so one step costs two dependent LDS reads.  Renormalisation words come from
-// a register window (two 16-bit words per lane: 64 words per half-wave) with
-// two further 32-word blocks in flight, fetched with ds_bpermute after the
-// ballot; the global loads are issued about 64 words before they are needed,
-// off the state's dependency chain.  Sign+mantissa bytes are loaded 4 steps
-// ahead.  Chunks stored RAW are copied in a separate loop.
+// so one step costs two dependent LDS reads.  A workgroup decodes a pair of
+// consecutive chunks of one buffer (half-wave h decodes chunk 2p + h), so the
+// record, sign+mantissa and output regions of the pair each get one buffer
+// resource.  Renormalisation words come from a register window (two 16-bit
+// words per lane: 64 words per half-wave) refilled from a load issued one step
+// earlier, off the state's dependency chain, and are fetched with ds_bpermute
+// after the ballot.  Sign+mantissa bytes are loaded 4 steps ahead.  Chunks
+// stored RAW are copied in a separate loop.
 template <int DT>
-__device__ inline uint32_t load_sm(const uint8_t *sm, uint32_t i) {
-    if (DT == 1) return gload<uint8_t>(sm + i);
-    const uint8_t *q = sm + 3ull * i;
-    return uint32_t(gload<uint8_t>(q)) | (uint32_t(gload<uint8_t>(q + 1)) << 8) |
-           (uint32_t(gload<uint8_t>(q + 2)) << 16);
+__device__ inline uint32_t bload_sm(rsrc_t r, uint32_t off) {
+    if (DT == 1) return bld8(r, off);
+    return bld8(r, off) | (bld8(r, off + 1) << 8) | (bld8(r, off + 2) << 16);
 }
 
 template <int DT>
-__device__ inline void store_value(uint8_t *outp, uint32_t i, uint32_t ex, uint32_t smv) {
-    if (DT == 1)
-        gstore<uint16_t>(outp + 2ull * i, (uint16_t)(((smv & 0x80u) << 8) | (ex << 7) | (smv & 0x7Fu)));
-    else
-        gstore<uint32_t>(outp + 4ull * i, ((smv & 0x800000u) << 8) | (ex << 23) | (smv & 0x7FFFFFu));
+__device__ inline uint32_t merge_value(uint32_t ex, uint32_t smv) {
+    if (DT == 1) return ((smv & 0x80u) << 8) | (ex << 7) | (smv & 0x7Fu);
+    return ((smv & 0x800000u) << 8) | (ex << 23) | (smv & 0x7FFFFFu);
 }
 
 template <int DT>
@@ -639,48 +690,58 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
 
     const uint32_t lane = threadIdx.x;
     const uint32_t h = lane >> 5, lj = lane & 31;
-    const uint32_t lo_bits = h ? 0xFFFFFFFFu : 0u;
-    const uint64_t G = gload<uint64_t>(p.chunk_first + p.nbuf);
+    const uint64_t PT = uniform_u64(gload<uint64_t>(p.pair_first + p.nbuf));
 
-    for (uint64_t pair = blockIdx.x; pair * 2 < G; pair += gridDim.x) {
-        const uint64_t g = pair * 2 + h;
-        bool ok = g < G;
-        const uint64_t gq = ok ? g : G - 1;
-        const uint32_t b = p.nbuf == 1 ? 0u : find_dec_buffer(p.chunk_first, p.nbuf, gq);
+    for (uint64_t q = blockIdx.x; q < PT; q += gridDim.x) {
+        // ---- the pair: buffer, chunks, index entries (wave-uniform) ----
+        const uint32_t b = p.nbuf == 1 ? 0u : uniform_u32(find_dec_buffer(p.pair_first, p.nbuf, q));
         const DecDesc d = p.nbuf == 1 ? p.single : load_dec_desc(p.descs + b);
-        const uint64_t ce = gload<uint64_t>(&p.info[b].chunk_elems);
-        const uint64_t sm_off = gload<uint64_t>(&p.info[b].sm_off);
-        const uint64_t exp_off = gload<uint64_t>(&p.info[b].exp_off);
-        const uint64_t total = gload<uint64_t>(&p.info[b].total);
-        ok = ok && gload<uint32_t>(p.status + b) == 0;
-        const bool real = ok;
-        const uint64_t ci = gq - gload<uint64_t>(p.chunk_first + b);
-        const uint64_t v0 = ci * ce;
-        const uint32_t ni = ok ? (uint32_t)min<uint64_t>(ce, d.n - v0) : 0u;
-
-        // record bounds from the index (V5) and record header (V6)
-        uint64_t a = 0, e = 0;
-        if (ok) {
-            a = gload<uint64_t>(d.in + kHeaderBytes + 8 * ci);
-            e = gload<uint64_t>(d.in + kHeaderBytes + 8 * (ci + 1));
-            ok = (a & 15u) == 0 && (e & 15u) == 0 && a <= e && e <= total - exp_off && e - a >= 16;
+        if (uniform_u32(gload<uint32_t>(p.status + b)) != 0) continue;
+        const uint64_t ce = uniform_u64(gload<uint64_t>(&p.info[b].chunk_elems));
+        const uint64_t C = uniform_u64(gload<uint64_t>(&p.info[b].chunks));
+        const uint64_t sm_off = uniform_u64(gload<uint64_t>(&p.info[b].sm_off));
+        const uint64_t exp_off = uniform_u64(gload<uint64_t>(&p.info[b].exp_off));
+        const uint64_t total = uniform_u64(gload<uint64_t>(&p.info[b].total));
+        const uint64_t n = uniform_u64(d.n);
+        const uint64_t c0 = 2 * (q - uniform_u64(gload<uint64_t>(p.pair_first + b)));
+        const uint32_t nch = C - c0 >= 2 ? 2u : 1u;
+        const uint32_t vals0 = (uint32_t)min<uint64_t>(ce, n - c0 * ce);
+        const uint32_t vals1 = nch == 2 ? (uint32_t)min<uint64_t>(ce, n - (c0 + 1) * ce) : 0u;
+        const uint8_t *ix = d.in + kHeaderBytes + 8 * c0;
+        const uint64_t a0 = uniform_u64(gload<uint64_t>(ix));
+        const uint64_t a1 = uniform_u64(gload<uint64_t>(ix + 8));
+        const uint64_t a2 = nch == 2 ? uniform_u64(gload<uint64_t>(ix + 16)) : a1;
+        const uint64_t rawmax = raw_record_bytes(ce);
+        // V5 for the pair's index entries: aligned, ordered, inside the records,
+        // and no record longer than the RAW one (which bounds every record)
+        const bool pair_ok = ((a0 | a1 | a2) & 15u) == 0 && a0 <= a1 && a1 <= a2 && a2 <= total - exp_off &&
+                             a1 - a0 <= rawmax && a2 - a1 <= rawmax;
+        if (!pair_ok) {
+            if (lane == 0) gstore<uint32_t>(p.status + b, 3u);
+            continue;
         }
-        const uint8_t *rec = d.in + exp_off + a;
-        const uint64_t len = e - a;
+        const rsrc_t rrec = make_rsrc(d.in + exp_off + a0, (uint32_t)(a2 - a0));
+
+        // ---- this half's record (V6) ----
+        bool ok = h < nch;
+        const uint32_t ni = h ? vals1 : vals0;
+        const uint32_t rel = h ? (uint32_t)(a1 - a0) : 0u;  // record start inside rrec
+        const uint32_t len = h ? (uint32_t)(a2 - a1) : (uint32_t)(a1 - a0);
         uint32_t mode = 1, nsym = 0, nw = 0;
-        if (ok) {
-            const uint4 rh = gload<uint4>(rec);
+        ok = ok && len >= 16;
+        {
+            const uint4 rh = bld128(rrec, ok ? rel : kOutOfRange);
             mode = rh.x & 0xFFu;
             nsym = rh.x >> 16;
             nw = rh.y;
-            ok = mode <= 1 && rh.z == ni && rh.w == len;
+            ok = ok && mode <= 1 && rh.z == ni && rh.w == len;
             if (ok && mode == 1) ok = nsym == 0 && nw == 0 && len == raw_record_bytes(ni);
             if (ok && mode == 0) ok = nsym >= 1 && nsym <= 256 && len == align16(words_offset(nsym) + 2ull * nw);
         }
         const bool coded = ok && mode == 0;
 
-        // table: presence bitmap byte lj covers symbols 8lj..8lj+7 (V7)
-        const uint32_t pb = coded ? gload<uint8_t>(rec + kRecHeaderBytes + lj) : 0u;
+        // ---- table: presence bitmap byte lj covers symbols 8lj..8lj+7 (V7) ----
+        const uint32_t pb = bld8(rrec, coded ? rel + kRecHeaderBytes + lj : kOutOfRange);
         const uint32_t np = __popc(pb);
         const uint32_t pre = half_excl_scan(np, lj);
         uint32_t fk[8], lsum = 0, cpre[8];
@@ -691,7 +752,7 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
             for (int k = 0; k < 8; ++k) {
                 fk[k] = 0;
                 if ((pb >> k) & 1u) {
-                    fk[k] = (k2 < nsym) ? gload<uint16_t>(rec + 48 + 2 * k2) : 0u;
+                    fk[k] = bld16(rrec, k2 < nsym ? rel + 48 + 2 * k2 : kOutOfRange);
                     if (fk[k] == 0 || fk[k] > kTableSize) fok = false;
                     ++k2;
                 }
@@ -716,78 +777,107 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
         if (coded_ok) {
             for (uint32_t m = 0; m < nsym; ++m) {
                 const uint32_t em = s_rk[h][m];
-                const uint32_t fs = (em & 0xFFFu) + 1, c0 = (em >> 12) & 0xFFFu;
-                for (uint32_t k = lj; k < fs; k += 32) s_sym[h][c0 + k] = (uint8_t)m;
+                const uint32_t fs = (em & 0xFFFu) + 1, c0s = (em >> 12) & 0xFFFu;
+                for (uint32_t k = lj; k < fs; k += 32) s_sym[h][c0s + k] = (uint8_t)m;
             }
         }
         __syncthreads();
 
-        // states (V8)
-        uint32_t x = kStateLow;
-        if (coded_ok) x = gload<uint32_t>(rec + states_offset(nsym) + 4 * lj);
+        // ---- states (V8) ----
+        uint32_t x = bld32(rrec, coded_ok ? rel + (uint32_t)states_offset(nsym) + 4 * lj : kOutOfRange);
+        if (!coded_ok) x = kStateLow;
         const bool sbad = half_mask(__ballot(coded_ok && x < kStateLow), h) != 0;
         ok = ok && !sbad;
         const bool rans_run = ok && mode == 0;
         const bool raw_run = ok && mode == 1;
 
+        // ---- rANS decode (V9: end state L on every lane, every word consumed) ----
         // Word window: words [base, base+64) in P (low 16 bits: word base + lj,
-        // high: base + 32 + lj).  NW holds word base + 64 + lj, loaded one step
-        // before it can be needed.  Every load is issued unconditionally at an
-        // address clamped into the record, so the compiler's wait counts stay
-        // exact and no wait lands on a just-issued load.  Words past n_words
-        // are never consumed by a valid stream; a stream that tries is caught
-        // by the end check (pos != n_words).
-        // A half that is not decoding a validated coded chunk points its loads
-        // at the workspace (always readable) instead of at offsets taken from
-        // an unvalidated header.
-        const uint8_t *safe = reinterpret_cast<const uint8_t *>(p.chunk_first);
-        const uint8_t *wbase = (rans_run && nw) ? rec + words_offset(nsym) : safe;
-        const uint32_t wmax = (rans_run && nw) ? nw - 1 : 0u;
-        const uint8_t *sm = raw_run || rans_run ? d.in + sm_off + v0 * R : safe;
-        const uint32_t last = (rans_run && ni) ? ni - 1 : 0u;
-        uint8_t *outp = d.out + v0 * EB;
-        uint32_t base = 0, pos = 0;
-        uint32_t P = uint32_t(gload<uint16_t>(wbase + 2 * min(lj, wmax))) |
-                     (uint32_t(gload<uint16_t>(wbase + 2 * min(32 + lj, wmax))) << 16);
-        uint32_t NW = gload<uint16_t>(wbase + 2 * min(64 + lj, wmax));
-        const uint32_t T = rans_run ? (ni + 31) / 32 : 0u;
-        const uint32_t Tw = max(T, (uint32_t)__shfl_xor(T, 32, 64));
+        // high: base + 32 + lj); NW holds word base + 64 + lj, loaded one step
+        // before it can be needed.  The per-half stream position and window
+        // base are wave-uniform scalars (pos0/base0, pos1/base1); lanes see
+        // them through scalar lane masks.  Loads past the pair's records read
+        // zero, and words past n_words are never consumed by a valid stream (a
+        // stream that tries fails the end check pos == n_words).
+        const uint32_t pair_vals = vals0 + vals1;
+        const rsrc_t rsm = make_rsrc(d.in + sm_off + c0 * ce * R, pair_vals * R);
+        const rsrc_t rout = make_rsrc(d.out + c0 * ce * EB, pair_vals * EB);
+        const uint32_t woff = rel + (uint32_t)words_offset(nsym) + 2 * lj;  // byte offset of word lj
+        const uint32_t sm_lane = (h ? vals0 : 0u) * R + lj * R;
+        const uint32_t out_lane = rans_run ? (h ? vals0 : 0u) * EB + lj * EB : kOutOfRange;
+        // wave-uniform view of the two halves
+        const uint64_t runm = __builtin_amdgcn_ballot_w64(rans_run);
+        const bool run0 = (uint32_t)runm != 0, run1 = (runm >> 32) != 0;
+        const uint32_t ni0 = uniform_u32(__shfl((int)ni, 0, 64)), ni1 = uniform_u32(__shfl((int)ni, 32, 64));
+        const uint32_t T0 = run0 ? (ni0 + 31) / 32 : 0u, T1 = run1 ? (ni1 + 31) / 32 : 0u;
+        const uint32_t Tw = max(T0, T1);
+        // steps in which every lane of each running half holds a value
+        const uint32_t F0 = run0 ? ni0 / 32 : 0xFFFFFFFFu, F1 = run1 ? ni1 / 32 : 0xFFFFFFFFu;
+        const uint32_t Tmain = min(min(F0, F1), Tw) & ~3u;
+        uint32_t pos0 = 0, pos1 = 0, base0 = 0, base1 = 0;
+        uint32_t nwo = woff + 128;
+        uint32_t P = bld16(rrec, woff) | (bld16(rrec, woff + 64) << 16);
+        uint32_t NW = bld16(rrec, nwo);
+        const uint32_t lanebits = (h << 5) << 2;
         uint32_t smq[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) smq[u] = load_sm<DT>(sm, min(u * 32 + lj, last));
-        for (uint32_t tb = 0; tb < Tw; tb += 4) {
+        for (int u = 0; u < 4; ++u) smq[u] = bload_sm<DT>(rsm, sm_lane + u * 32 * R);
+
+        // one step of both half-waves; act = lanes holding a value this step
+        auto step = [&](uint32_t t, uint64_t act, uint32_t &smslot) __attribute__((always_inline)) {
+            const uint32_t slot = x & (kTableSize - 1);
+            const uint32_t em = s_rk[h][s_sym[h][slot]];
+            const uint32_t xd = __umul24((em & 0xFFFu) + 1, x >> kProbBits) + slot - ((em >> 12) & 0xFFFu);
+            const uint64_t m = lanes_lt(xd, kStateLow) & act;
+            const uint32_t lo = (uint32_t)m, hi = (uint32_t)(m >> 32);
+            const uint32_t clo = __builtin_popcount(lo), chi = __builtin_popcount(hi);
+            // word index relative to the window: rank inside the half + (pos - base)
+            const uint32_t bias = (pos0 - base0) + (((pos1 - base1 - clo) - (pos0 - base0)) & (h ? 0xFFFFFFFFu : 0u));
+            const uint32_t kk = __builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, bias));  // < 64
+            const uint32_t wv = (uint32_t)__builtin_amdgcn_ds_bpermute((int)(((kk << 2) & 124u) | lanebits), (int)P);
+            const uint32_t w = (wv >> ((kk >> 1) & 16u)) & 0xFFFFu;  // high word when kk >= 32
+            x = vsel(act, x, vsel(m, xd, (xd << 16) | w));
+            pos0 += clo;
+            pos1 += chi;
+            const bool sh0 = pos0 - base0 >= 32, sh1 = pos1 - base1 >= 32;
+            base0 += sh0 ? 32u : 0u;
+            base1 += sh1 ? 32u : 0u;
+            const uint64_t shm = (sh0 ? 0xFFFFFFFFull : 0ull) | (sh1 ? kHighHalf : 0ull);
+            P = vsel(shm, P, (P >> 16) | (NW << 16));
+            nwo += vsel(shm, 0u, 64u);
+            NW = bld16(rrec, nwo);
+            const uint32_t smv = smslot;
+            smslot = bload_sm<DT>(rsm, sm_lane + (t + 4) * 32 * R);
+            if (DT == 1) bst16(rout, out_lane + t * 32 * EB, merge_value<DT>(em >> 24, smv));
+            else bst32(rout, out_lane + t * 32 * EB, merge_value<DT>(em >> 24, smv));
+        };
+        uint32_t t = 0;
+        for (; t < Tmain; t += 4) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) step(t + u, runm, smq[u]);
+        }
+        for (; t < Tw; t += 4) {
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                const uint32_t i = (tb + u) * 32 + lj;
-                const uint32_t slot = x & (kTableSize - 1);
-                const uint32_t em = s_rk[h][s_sym[h][slot]];
-                const uint32_t xd = __umul24((em & 0xFFFu) + 1, x >> kProbBits) + slot - ((em >> 12) & 0xFFFu);
-                const bool act = i < ni;
-                const bool need = act && xd < kStateLow;
-                const HalfBallot hb = half_ballot(need, h, lo_bits);
-                const uint32_t k = pos - base + hb.rank;  // < 64
-                const uint32_t wv = (uint32_t)__shfl((int)P, (int)(k & 31u), 32);
-                const uint32_t w = k < 32 ? (wv & 0xFFFFu) : (wv >> 16);
-                const uint32_t xn = need ? (xd << 16) | w : xd;
-                x = act ? xn : x;
-                pos += hb.cnt;
-                const bool shift = pos - base >= 32;
-                P = shift ? (P >> 16) | (NW << 16) : P;
-                base += shift ? 32u : 0u;
-                NW = gload<uint16_t>(wbase + 2 * min(base + 64 + lj, wmax));
-                const uint32_t smv = smq[u];
-                smq[u] = load_sm<DT>(sm, min(i + 4 * 32, last));
-                if (rans_run && act) store_value<DT>(outp, i, em >> 24, smv);
+                const uint32_t tt = t + u;
+                const uint64_t act = (run0 && ni0 > 32 * tt ? half_prefix_mask(ni0 - 32 * tt, 0) : 0ull) |
+                                     (run1 && ni1 > 32 * tt ? half_prefix_mask(ni1 - 32 * tt, 1) : 0ull);
+                step(tt, act, smq[u]);
             }
         }
+        const uint32_t pos = h ? pos1 : pos0;
         const bool endbad = half_mask(__ballot(rans_run && (x != kStateLow || pos != nw)), h) != 0;
         ok = ok && !endbad;
-        // chunks stored RAW: exponent bytes straight from the record
+        // ---- chunks stored RAW: exponent bytes straight from the record ----
         if (raw_run) {
-            for (uint32_t i = lj; i < ni; i += 32)
-                store_value<DT>(outp, i, gload<uint8_t>(rec + kRecHeaderBytes + i), load_sm<DT>(sm, i));
+            const uint32_t ob = (h ? vals0 : 0u) * EB, sb = (h ? vals0 : 0u) * R;
+            for (uint32_t i = lj; i < ni; i += 32) {
+                const uint32_t v = merge_value<DT>(bld8(rrec, rel + kRecHeaderBytes + i), bload_sm<DT>(rsm, sb + i * R));
+                if (DT == 1) bst16(rout, ob + i * EB, v);
+                else bst32(rout, ob + i * EB, v);
+            }
         }
-        if (real && !ok && lj == 0) gstore<uint32_t>(p.status + b, 3u);
+        if (h < nch && !ok && lj == 0) gstore<uint32_t>(p.status + b, 3u);
         __syncthreads();
     }
 }
@@ -819,10 +909,10 @@ hipError_t launch_compress(const EncParams &ep, const CompactParams &cp, uint64_
 hipError_t launch_decompress(const DecParams &vp, const DecodeParams &dp, int dtype, uint64_t max_chunks,
                              hipStream_t stream) {
     k_dec_validate<<<(vp.nbuf + 255) / 256, 256, 0, stream>>>(vp);
-    if (vp.nbuf > 1) k_scan_u64<<<1, 1024, 0, stream>>>(vp.chunk_first, vp.chunk_first, vp.nbuf);
+    if (vp.nbuf > 1) k_scan_u64<<<1, 1024, 0, stream>>>(vp.pair_first, vp.pair_first, vp.nbuf);
     if (max_chunks > 0) {
-        const uint64_t half = (max_chunks + 1) / 2;
-        const uint64_t grid = half < 8192 ? half : 8192;
+        const uint64_t pairs = (max_chunks + 1) / 2 + vp.nbuf;  // upper bound of the chunk pairs
+        const uint64_t grid = pairs < 8192 ? pairs : 8192;
         if (g_profile.start) (void)hipEventRecord(g_profile.start, stream);
         if (dtype == 1) k_decode<1><<<dim3((uint32_t)grid), dim3(64), 0, stream>>>(dp);
         else k_decode<2><<<dim3((uint32_t)grid), dim3(64), 0, stream>>>(dp);

@@ -40,7 +40,7 @@ struct DecParams {
     uint32_t nbuf;
     int dtype;
     DecInfo *info;
-    uint64_t *chunk_first;  // nbuf + 1 entries
+    uint64_t *pair_first;  // nbuf + 1 entries: exclusive prefix of the chunk-pair counts
     uint32_t *status;
 };
 
@@ -49,7 +49,7 @@ struct DecodeParams {
     DecDesc single;
     uint32_t nbuf;
     const DecInfo *info;
-    const uint64_t *chunk_first;
+    const uint64_t *pair_first;
     uint32_t *status;
 };
 
