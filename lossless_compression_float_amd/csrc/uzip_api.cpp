@@ -104,6 +104,11 @@ uzip_status compress_impl(uzip_dtype dtype, uint64_t ce, std::vector<EncDesc> &d
     ep.nbuf = nbuf;
     ep.chunk_elems = (uint32_t)ce;
     ep.total_chunks = chunks;
+    ep.total_pairs = 0;
+    for (EncDesc &d : descs) {
+        d.pair_first = ep.total_pairs;
+        ep.total_pairs += (d.chunks + 1) / 2;
+    }
     ep.slots = base + w.slots;
     ep.slot_stride = w.slot_stride;
     ep.rec_sizes = reinterpret_cast<uint32_t *>(base + w.sizes);
@@ -208,7 +213,7 @@ uzip_status uzip_compress(uzip_dtype dtype, const void *d_in, size_t num_element
     const Layout l = layout_of(dtype, num_elements, ce);
     std::vector<EncDesc> descs(1);
     descs[0] = EncDesc{static_cast<const uint8_t *>(d_in), static_cast<uint8_t *>(d_out), d_out_size, num_elements,
-                       0, l.sm_off, l.exp_off, l.chunks};
+                       0, l.sm_off, l.exp_off, l.chunks, 0, 0};
     return compress_impl(dtype, ce, descs, l.chunks, d_workspace, workspace_bytes, stream);
 }
 
@@ -240,7 +245,7 @@ uzip_status uzip_compress_batched(uzip_dtype dtype, size_t num_buffers, const vo
         if (h_out_capacity[b] < max_size(dtype, n, ce)) return UZIP_ERR_CAPACITY;
         const Layout l = layout_of(dtype, n, ce);
         descs[b] = EncDesc{static_cast<const uint8_t *>(h_in[b]), static_cast<uint8_t *>(h_out[b]), d_out_sizes + b, n,
-                           chunks, l.sm_off, l.exp_off, l.chunks};
+                           chunks, l.sm_off, l.exp_off, l.chunks, 0, 0};
         chunks += l.chunks;
     }
     return compress_impl(dtype, ce, descs, chunks, d_workspace, workspace_bytes, stream);

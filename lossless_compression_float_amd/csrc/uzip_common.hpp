@@ -67,6 +67,8 @@ struct alignas(16) EncDesc {
     uint64_t sm_off;
     uint64_t exp_off;
     uint64_t chunks;
+    uint64_t pair_first;    // global index of the buffer's first chunk pair
+    uint64_t pad;
 };
 
 // One buffer of a decompress call as the caller states it.

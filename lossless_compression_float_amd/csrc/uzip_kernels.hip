@@ -194,12 +194,24 @@ __device__ inline uint32_t find_dec_buffer(const uint64_t *chunk_first, uint32_t
 }
 
 __device__ inline EncDesc load_enc_desc(const EncDesc *d) {
+    static_assert(sizeof(EncDesc) == 80, "descriptor layout");
     const uint4 *q = reinterpret_cast<const uint4 *>(d);
     EncDesc r;
     uint4 *o = reinterpret_cast<uint4 *>(&r);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) o[k] = gload<uint4>(q + k);
+    for (int k = 0; k < 5; ++k) o[k] = gload<uint4>(q + k);
     return r;
+}
+
+// the buffer holding global chunk pair q: the largest b with pair_first[b] <= q
+__device__ inline uint32_t find_enc_pair_buffer(const EncDesc *d, uint32_t nbuf, uint64_t q) {
+    uint32_t lo = 0, hi = nbuf - 1;
+    while (lo < hi) {
+        uint32_t mid = (lo + hi + 1) >> 1;
+        if (gload<uint64_t>(&d[mid].pair_first) <= q) lo = mid;
+        else hi = mid - 1;
+    }
+    return lo;
 }
 
 __device__ inline DecDesc load_dec_desc(const DecDesc *d) {
@@ -255,18 +267,28 @@ __global__ __launch_bounds__(64) void k_encode(EncParams p) {
 
     const uint32_t lane = threadIdx.x;
     const uint32_t h = lane >> 5, lj = lane & 31;
-    const uint32_t lo_bits = h ? 0xFFFFFFFFu : 0u;
-    const uint64_t g = uint64_t(blockIdx.x) * 2 + h;
-    const bool valid = g < p.total_chunks;
-    const uint64_t gq = valid ? g : p.total_chunks - 1;
 
-    const EncDesc d = p.nbuf == 1 ? p.single : load_enc_desc(p.descs + find_enc_buffer(p.descs, p.nbuf, gq));
-    const uint64_t ci = gq - d.chunk_first;
-    const uint64_t v0 = ci * p.chunk_elems;
-    const uint32_t ni = valid ? (uint32_t)min<uint64_t>(p.chunk_elems, d.n - v0) : 0u;
-    const uint8_t *in = d.in + v0 * EB;
-    uint8_t *sm_out = d.out + d.sm_off + v0 * R;
-    uint8_t *slot = p.slots + gq * p.slot_stride;
+    // ---- the pair: buffer and chunks (wave-uniform); half-wave h codes chunk c0 + h ----
+    const uint64_t q = blockIdx.x;
+    const EncDesc d = p.nbuf == 1 ? p.single
+                                  : load_enc_desc(p.descs + uniform_u32(find_enc_pair_buffer(p.descs, p.nbuf, q)));
+    const uint64_t ce = p.chunk_elems;
+    const uint64_t n = uniform_u64(d.n);
+    const uint64_t c0 = 2 * (q - uniform_u64(d.pair_first));
+    const uint64_t chunks = uniform_u64(d.chunks);
+    const uint32_t nch = chunks - c0 >= 2 ? 2u : 1u;
+    const uint32_t vals0 = (uint32_t)min<uint64_t>(ce, n - c0 * ce);
+    const uint32_t vals1 = nch == 2 ? (uint32_t)min<uint64_t>(ce, n - (c0 + 1) * ce) : 0u;
+    const uint64_t g0 = uniform_u64(d.chunk_first) + c0;  // global index of the pair's first chunk
+    const bool valid = h < nch;
+    const uint64_t g = g0 + (valid ? h : 0u);
+    const uint32_t ni = h ? vals1 : vals0;
+    const uint32_t pair_vals = vals0 + vals1;
+    const rsrc_t rin = make_rsrc(d.in + c0 * ce * EB, pair_vals * EB);
+    const rsrc_t rslot = make_rsrc(p.slots + g0 * p.slot_stride, (uint32_t)(nch * p.slot_stride));
+    const uint32_t in0 = (h ? vals0 : 0u) * EB;  // this half's chunk inside rin
+    uint8_t *sm_out = d.out + d.sm_off + (c0 * ce + (h ? vals0 : 0u)) * R;
+    uint8_t *slot = p.slots + g * p.slot_stride;
 
     uint32_t *hist = lds + h * (kSubHist * kSubRow) + (lj & (kSubHist - 1)) * kSubRow;
     for (uint32_t k = lane; k < 2 * kSubHist * kSubRow; k += 64) lds[k] = 0;
@@ -278,19 +300,17 @@ __global__ __launch_bounds__(64) void k_encode(EncParams p) {
     for (uint32_t it = 0; it < iters_w; ++it) {
         const uint32_t i0 = it * VPI + lj * VPL;
         if (i0 >= ni) continue;
-        uint32_t w[4];
         const bool full = i0 + VPL <= ni;
+        uint32_t w[4];
         if (full) {
-            const uint4 q = gload<uint4>(in + uint64_t(i0) * EB);
-            w[0] = q.x; w[1] = q.y; w[2] = q.z; w[3] = q.w;
-        } else {
+            const uint4 qv = bld128(rin, in0 + i0 * EB);
+            w[0] = qv.x; w[1] = qv.y; w[2] = qv.z; w[3] = qv.w;
+        } else {  // the chunk's ragged end: value by value, nothing read past the pair
             for (int k = 0; k < 4; ++k) w[k] = 0;
             for (uint32_t k = 0; k < VPL; ++k) {
-                if (i0 + k < ni) {
-                    const uint32_t v = load_value<DT>(in, i0 + k);
-                    if (DT == 1) w[k >> 1] |= v << (16 * (k & 1));
-                    else w[k] = v;
-                }
+                const uint32_t o = i0 + k < ni ? in0 + (i0 + k) * EB : kOutOfRange;
+                if (DT == 1) w[k >> 1] |= bld16(rin, o) << (16 * (k & 1));
+                else w[k] = bld32(rin, o);
             }
         }
         if (DT == 1) {
@@ -362,9 +382,9 @@ __global__ __launch_bounds__(64) void k_encode(EncParams p) {
         fl[k] = 0;
         key[k] = 0;
         if (c[k]) {
-            const uint32_t q = c[k] * Rr;  // < 2^32: c <= 2^20, R < 2^12
-            fl[k] = q / ni;
-            key[k] = ((q - fl[k] * ni) << 8) | (255u - (lj * 8 + k));
+            const uint32_t qq = c[k] * Rr;  // < 2^32: c <= 2^20, R < 2^12
+            fl[k] = qq / ni;
+            key[k] = ((qq - fl[k] * ni) << 8) | (255u - (lj * 8 + k));
             given += fl[k];
         }
     }
@@ -416,51 +436,92 @@ __global__ __launch_bounds__(64) void k_encode(EncParams p) {
 
     // ---- pass 2: 32-lane interleaved rANS, steps from the last down to 0 ----
     // Words of one step are placed, lanes ascending, right before the words of
-    // the following step, filling the slot from its end.  Input values are
-    // prefetched one 8-step block ahead with loads that are always issued
-    // (clamped to the chunk), so the compiler's wait counts stay exact.
-    const uint64_t raw_i = raw_record_bytes(ni);
-    const uint64_t wofs = words_offset(nsym);
-    const uint32_t wcap = valid ? (uint32_t)((raw_i - wofs) / 2) : 0u;  // words that fit before the chunk goes RAW
-    const uint32_t last = ni ? ni - 1 : 0u;
-    uint8_t *wend = slot + raw_i;  // words fill [wend - 2 nw, wend)
+    // the following step, filling the slot from its end.  The word counts of
+    // the two halves are wave-uniform scalars; a lane's store offset comes from
+    // one mbcnt pair, and lanes without a word store out of range (dropped).
+    // Input values are prefetched one 8-step block ahead through the pair's
+    // input resource (past the pair: zeros, never coded).
+    const uint32_t nsym0 = uniform_u32(__shfl((int)nsym, 0, 64)), nsym1 = uniform_u32(__shfl((int)nsym, 32, 64));
+    const uint32_t raw0 = (uint32_t)raw_record_bytes(vals0), raw1 = (uint32_t)raw_record_bytes(vals1);
+    const uint32_t wcap0 = (raw0 - (uint32_t)words_offset(nsym0)) / 2;
+    const uint32_t wcap1 = nch == 2 ? (raw1 - (uint32_t)words_offset(nsym1)) / 2 : 0u;
+    const uint32_t end0 = raw0 / 2, end1 = ((uint32_t)p.slot_stride + raw1) / 2;  // word index just past each slot's words
+    uint32_t nw0 = 0, nw1 = 0;
+    bool alive0 = true, alive1 = nch == 2;  // a half stops coding once its words outgrow the RAW size
     uint32_t x = kStateLow;
-    uint32_t nw = 0;
-    bool dead = !valid;  // set when the words outgrow the RAW size: the chunk goes RAW
-    const uint32_t T = (ni + 31) / 32;
-    const uint32_t Tw = max(T, (uint32_t)__shfl_xor(T, 32, 64));
-    const uint32_t nblk = (Tw + 7) / 8;
+    const uint32_t T0 = (vals0 + 31) / 32, T1 = (vals1 + 31) / 32;
+    const uint32_t nblk = (max(T0, T1) + 7) / 8;
+    const uint32_t hsel = h ? 0xFFFFFFFFu : 0u;
     uint32_t cur[8], nxt[8];
+    {
+        const uint32_t o = in0 + ((nblk - 1) * 8 * 32 + lj) * EB;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) cur[k] = load_value<DT>(in, min(((nblk - 1) * 8 + k) * 32 + lj, last));
+        for (int k = 0; k < 8; ++k) cur[k] = DT == 1 ? bld16(rin, o + k * 32 * EB) : bld32(rin, o + k * 32 * EB);
+    }
     for (int32_t b = (int32_t)nblk - 1; b >= 0; --b) {
+        {
+            const uint32_t o = b > 0 ? in0 + ((uint32_t)(b - 1) * 8 * 32 + lj) * EB : kOutOfRange;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) nxt[k] = load_value<DT>(in, min(((uint32_t)(b - 1) * 8 + k) * 32 + lj, last));
-        // a block emits at most 256 words: check the room once per block
-        const bool roomy = nw + 256 <= wcap;
-#pragma unroll
-        for (int k = 7; k >= 0; --k) {
-            const uint32_t i = ((uint32_t)b * 8 + k) * 32 + lj;
-            const bool act = !dead && i < ni;
+            for (int k = 0; k < 8; ++k) nxt[k] = DT == 1 ? bld16(rin, o + k * 32 * EB) : bld32(rin, o + k * 32 * EB);
+        }
+        // One step; CAREFUL steps rebuild the lane masks and check the room
+        // (a ragged chunk end, or words close to the RAW size), the others use
+        // the block's loop-invariant mask.
+        auto step = [&](int k, bool careful, uint64_t act) __attribute__((always_inline)) {
+            const uint32_t t = (uint32_t)b * 8 + k;
+            if (careful)
+                act = (alive0 && vals0 > 32 * t ? half_prefix_mask(vals0 - 32 * t, 0) : 0ull) |
+                      (alive1 && vals1 > 32 * t ? half_prefix_mask(vals1 - 32 * t, 1) : 0ull);
             const uint4 te = tab[exponent_of<DT>(cur[k])];
             const uint32_t fs = te.x;
-            const bool need = act && (x >> 20) >= fs;  // x >= f * 2^20
-            const HalfBallot hb = half_ballot(need, h, lo_bits);
-            if (!roomy && !dead && nw + hb.cnt > wcap) dead = true;
-            const bool emit = need && !dead;
-            if (emit) gstore<uint16_t>(wend - 2ull * (nw + hb.cnt) + 2ull * hb.rank, (uint16_t)(x & 0xFFFFu));
-            const uint32_t xs = emit ? x >> 16 : x;
-            nw += hb.cnt;
-            const uint32_t q = enc_quotient(xs, __hiloint2double((int)te.w, (int)te.z));
-            const uint32_t xe = __umul24(q, kTableSize - fs) + (xs + te.y);  // = q * M + (xs - q * f) + c0
-            x = (act && !dead) ? xe : x;
+            uint64_t m = lanes_lt(fs - 1, x >> 20) & act;  // x >= f * 2^20
+            uint32_t lo = (uint32_t)m, hi = (uint32_t)(m >> 32);
+            uint32_t clo = __builtin_popcount(lo), chi = __builtin_popcount(hi);
+            if (careful) {
+                if (alive0 && nw0 + clo > wcap0) alive0 = false;
+                if (alive1 && nw1 + chi > wcap1) alive1 = false;
+                const uint64_t am = (alive0 ? 0xFFFFFFFFull : 0ull) | (alive1 ? kHighHalf : 0ull);
+                m &= am;
+                act &= am;
+                lo = (uint32_t)m;
+                hi = (uint32_t)(m >> 32);
+                clo = __builtin_popcount(lo);
+                chi = __builtin_popcount(hi);
+            }
+            // word index: end of the slot's words - (words so far + this step's) + rank in the half
+            const uint32_t e0 = end0 - nw0 - clo, e1 = end1 - nw1 - chi - clo;
+            const uint32_t bias = e0 + ((e1 - e0) & hsel);
+            const uint32_t kk = __builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, bias));
+            bst16(rslot, vsel(m, kOutOfRange, kk << 1), x);
+            const uint32_t xs = vsel(m, x, x >> 16);
+            nw0 += clo;
+            nw1 += chi;
+            const uint32_t qd = enc_quotient(xs, __hiloint2double((int)te.w, (int)te.z));
+            const uint32_t xe = __umul24(qd, kTableSize - fs) + (xs + te.y);  // = q * M + (xs - q * f) + c0
+            x = vsel(act, x, xe);
+        };
+        // a block codes at most 256 values, so at most 256 words, per half
+        const uint32_t tend = ((uint32_t)b + 1) * 256;
+        const bool fast = (!alive0 || (vals0 >= tend && nw0 + 256 <= wcap0)) &&
+                          (!alive1 || (vals1 >= tend && nw1 + 256 <= wcap1));
+        if (fast) {
+            const uint64_t act = (alive0 ? 0xFFFFFFFFull : 0ull) | (alive1 ? kHighHalf : 0ull);
+#pragma unroll
+            for (int k = 7; k >= 0; --k) step(k, false, act);
+        } else {
+#pragma unroll
+            for (int k = 7; k >= 0; --k) step(k, true, 0ull);
         }
 #pragma unroll
         for (int k = 0; k < 8; ++k) cur[k] = nxt[k];
     }
 
+    const uint32_t nw = h ? nw1 : nw0;
+    const bool alive = h ? alive1 : alive0;
+    const uint64_t wofs = words_offset(nsym);
+    const uint64_t raw_i = raw_record_bytes(ni);
     const uint64_t rans_bytes = align16(wofs + 2ull * nw);
-    const bool rans = valid && !dead && rans_bytes < raw_i;
+    const bool rans = valid && alive && rans_bytes < raw_i;
     if (valid) {
         if (rans) {
             gstore<uint32_t>(slot + states_offset(nsym) + 4 * lj, x);
@@ -473,9 +534,10 @@ __global__ __launch_bounds__(64) void k_encode(EncParams p) {
                 gstore<uint4>(slot, make_uint4(1u, 0u, ni, (uint32_t)raw_i));
                 gstore<uint32_t>(p.rec_sizes + g, (uint32_t)raw_i);
             }
-            for (uint32_t k = lj; k + kRecHeaderBytes < raw_i; k += 32)
-                gstore<uint8_t>(slot + kRecHeaderBytes + k,
-                                k < ni ? (uint8_t)exponent_of<DT>(load_value<DT>(in, k)) : (uint8_t)0);
+            for (uint32_t k = lj; k + kRecHeaderBytes < raw_i; k += 32) {
+                const uint32_t v = DT == 1 ? bld16(rin, in0 + k * EB) : bld32(rin, in0 + k * EB);
+                gstore<uint8_t>(slot + kRecHeaderBytes + k, k < ni ? (uint8_t)exponent_of<DT>(v) : (uint8_t)0);
+            }
         }
     }
 }
@@ -813,56 +875,73 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
         const uint32_t Tw = max(T0, T1);
         // steps in which every lane of each running half holds a value
         const uint32_t F0 = run0 ? ni0 / 32 : 0xFFFFFFFFu, F1 = run1 ? ni1 / 32 : 0xFFFFFFFFu;
-        const uint32_t Tmain = min(min(F0, F1), Tw) & ~3u;
-        uint32_t pos0 = 0, pos1 = 0, base0 = 0, base1 = 0;
-        uint32_t nwo = woff + 128;
-        uint32_t P = bld16(rrec, woff) | (bld16(rrec, woff + 64) << 16);
-        uint32_t NW = bld16(rrec, nwo);
+        const uint32_t Tmain = min(min(F0, F1), Tw) & ~7u;
+        // per half: pos = words consumed, off = pos - window base (< 32 between steps)
+        uint32_t pos0 = 0, pos1 = 0, off0 = 0, off1 = 0;
+        uint64_t shprev = 0;  // lanes whose half shifted its window in the previous step
+        // Refill words: at every step, after the shift decision, load the two
+        // 32-word blocks that start 64 and 96 words past the (new) window base;
+        // two steps later a shift needs the block 64 words past the then base,
+        // which is the first of them if the step in between did not shift and
+        // the second if it did.  So every refill load is consumed two steps
+        // after it is issued, off the dependency chain.
+        uint32_t wrow = woff;  // byte offset of word (window base + lj)
+        uint32_t P = bld16(rrec, wrow) | (bld16(rrec, wrow + 64) << 16);
+        uint32_t RA[2], RB[2];
+        RA[0] = RA[1] = bld16(rrec, wrow + 128);
+        RB[0] = RB[1] = bld16(rrec, wrow + 192);
         const uint32_t lanebits = (h << 5) << 2;
-        uint32_t smq[4];
+        constexpr int kSmAhead = 8;  // sign+mantissa bytes are loaded this many steps ahead
+        uint32_t smq[kSmAhead];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) smq[u] = bload_sm<DT>(rsm, sm_lane + u * 32 * R);
+        for (int u = 0; u < kSmAhead; ++u) smq[u] = bload_sm<DT>(rsm, sm_lane + u * 32 * R);
 
-        // one step of both half-waves; act = lanes holding a value this step
-        auto step = [&](uint32_t t, uint64_t act, uint32_t &smslot) __attribute__((always_inline)) {
+        // one step of both half-waves; act = lanes holding a value this step;
+        // par = step parity (selects the refill registers)
+        auto step = [&](uint32_t t, uint64_t act, uint32_t &smslot, int par) __attribute__((always_inline)) {
             const uint32_t slot = x & (kTableSize - 1);
             const uint32_t em = s_rk[h][s_sym[h][slot]];
             const uint32_t xd = __umul24((em & 0xFFFu) + 1, x >> kProbBits) + slot - ((em >> 12) & 0xFFFu);
             const uint64_t m = lanes_lt(xd, kStateLow) & act;
             const uint32_t lo = (uint32_t)m, hi = (uint32_t)(m >> 32);
             const uint32_t clo = __builtin_popcount(lo), chi = __builtin_popcount(hi);
-            // word index relative to the window: rank inside the half + (pos - base)
-            const uint32_t bias = (pos0 - base0) + (((pos1 - base1 - clo) - (pos0 - base0)) & (h ? 0xFFFFFFFFu : 0u));
+            // word index relative to the window: (pos - base) + rank inside the half
+            const uint32_t bias = off0 + (((off1 - clo) - off0) & (h ? 0xFFFFFFFFu : 0u));
             const uint32_t kk = __builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, bias));  // < 64
             const uint32_t wv = (uint32_t)__builtin_amdgcn_ds_bpermute((int)(((kk << 2) & 124u) | lanebits), (int)P);
             const uint32_t w = (wv >> ((kk >> 1) & 16u)) & 0xFFFFu;  // high word when kk >= 32
             x = vsel(act, x, vsel(m, xd, (xd << 16) | w));
             pos0 += clo;
             pos1 += chi;
-            const bool sh0 = pos0 - base0 >= 32, sh1 = pos1 - base1 >= 32;
-            base0 += sh0 ? 32u : 0u;
-            base1 += sh1 ? 32u : 0u;
+            off0 += clo;
+            off1 += chi;
+            const bool sh0 = off0 >= 32, sh1 = off1 >= 32;
+            off0 -= sh0 ? 32u : 0u;
+            off1 -= sh1 ? 32u : 0u;
             const uint64_t shm = (sh0 ? 0xFFFFFFFFull : 0ull) | (sh1 ? kHighHalf : 0ull);
-            P = vsel(shm, P, (P >> 16) | (NW << 16));
-            nwo += vsel(shm, 0u, 64u);
-            NW = bld16(rrec, nwo);
+            const uint32_t up = vsel(shprev, RA[par], RB[par]);  // loaded two steps ago
+            P = vsel(shm, P, (P >> 16) | (up << 16));
+            wrow += vsel(shm, 0u, 64u);
+            shprev = shm;
+            RA[par] = bld16(rrec, wrow + 128);
+            RB[par] = bld16(rrec, wrow + 192);
             const uint32_t smv = smslot;
-            smslot = bload_sm<DT>(rsm, sm_lane + (t + 4) * 32 * R);
+            smslot = bload_sm<DT>(rsm, sm_lane + (t + kSmAhead) * 32 * R);
             if (DT == 1) bst16(rout, out_lane + t * 32 * EB, merge_value<DT>(em >> 24, smv));
             else bst32(rout, out_lane + t * 32 * EB, merge_value<DT>(em >> 24, smv));
         };
         uint32_t t = 0;
-        for (; t < Tmain; t += 4) {
+        for (; t < Tmain; t += kSmAhead) {
 #pragma unroll
-            for (int u = 0; u < 4; ++u) step(t + u, runm, smq[u]);
+            for (int u = 0; u < kSmAhead; ++u) step(t + u, runm, smq[u], u & 1);
         }
-        for (; t < Tw; t += 4) {
+        for (; t < Tw; t += kSmAhead) {
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
+            for (int u = 0; u < kSmAhead; ++u) {
                 const uint32_t tt = t + u;
                 const uint64_t act = (run0 && ni0 > 32 * tt ? half_prefix_mask(ni0 - 32 * tt, 0) : 0ull) |
                                      (run1 && ni1 > 32 * tt ? half_prefix_mask(ni1 - 32 * tt, 1) : 0ull);
-                step(tt, act, smq[u]);
+                step(tt, act, smq[u], u & 1);
             }
         }
         const uint32_t pos = h ? pos1 : pos0;
@@ -894,7 +973,7 @@ hipError_t launch_compress(const EncParams &ep, const CompactParams &cp, uint64_
         k_empty_headers<<<(nb + 255) / 256, 256, 0, stream>>>(ep.descs, ep.single, nb, ep.dtype, ep.chunk_elems);
     }
     if (ep.total_chunks > 0) {
-        const uint64_t grid = (ep.total_chunks + 1) / 2;
+        const uint64_t grid = ep.total_pairs;
         if (g_profile.start) (void)hipEventRecord(g_profile.start, stream);
         if (ep.dtype == 1) k_encode<1><<<dim3((uint32_t)grid), dim3(64), 0, stream>>>(ep);
         else k_encode<2><<<dim3((uint32_t)grid), dim3(64), 0, stream>>>(ep);

@@ -15,6 +15,7 @@ struct EncParams {
     uint32_t nbuf;
     uint32_t chunk_elems;
     uint64_t total_chunks;  // chunks over all buffers
+    uint64_t total_pairs;   // chunk pairs (two consecutive chunks of one buffer) over all buffers
     uint8_t *slots;         // one slot of slot_stride bytes per chunk
     uint64_t slot_stride;
     uint32_t *rec_sizes;    // record bytes per chunk
