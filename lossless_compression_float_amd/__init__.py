@@ -13,6 +13,7 @@ fails loudly when the library is missing.
 """
 from __future__ import annotations
 
+import array
 import ctypes
 import os
 
@@ -102,36 +103,40 @@ def uzip_decompress(d_in, in_bytes, dtype, num_elements, d_out, d_status, d_work
                                      workspace_bytes, stream))
 
 
+class _HostArray:
+    """A contiguous host array of 64-bit unsigned values (size_t or pointer)
+    for the C ABI's h_* arguments; `ptr` stays valid while the object lives."""
+
+    def __init__(self, vals):
+        self.buf = array.array("Q", vals)
+        self.ptr = self.buf.buffer_info()[0] if len(self.buf) else None
+
+
 def _sizes(vals):
-    return (ctypes.c_size_t * len(vals))(*vals)
+    return _HostArray(vals)
 
 
 def _ptrs(vals):
-    return (ctypes.c_void_p * len(vals))(*vals)
+    return _HostArray(vals)
 
 
 def uzip_workspace_size_batched(dtype: int, num_elements, chunk_bytes: int = 0) -> int:
     arr = _sizes(num_elements)
-    return int(lib().uzip_workspace_size_batched(dtype, len(num_elements), ctypes.cast(arr, ctypes.c_void_p),
-                                                 chunk_bytes))
+    return int(lib().uzip_workspace_size_batched(dtype, len(num_elements), arr.ptr, chunk_bytes))
 
 
 def uzip_compress_batched(dtype, h_in, h_num_elements, chunk_bytes, h_out, h_out_capacity, d_out_sizes, d_workspace,
                           workspace_bytes, stream) -> int:
     a_in, a_n, a_out, a_cap = _ptrs(h_in), _sizes(h_num_elements), _ptrs(h_out), _sizes(h_out_capacity)
-    v = ctypes.c_void_p
-    return int(lib().uzip_compress_batched(dtype, len(h_in), ctypes.cast(a_in, v), ctypes.cast(a_n, v), chunk_bytes,
-                                           ctypes.cast(a_out, v), ctypes.cast(a_cap, v), d_out_sizes, d_workspace,
-                                           workspace_bytes, stream))
+    return int(lib().uzip_compress_batched(dtype, len(h_in), a_in.ptr, a_n.ptr, chunk_bytes, a_out.ptr, a_cap.ptr,
+                                           d_out_sizes, d_workspace, workspace_bytes, stream))
 
 
 def uzip_decompress_batched(dtype, h_in, h_in_bytes, h_num_elements, h_out, d_status, d_workspace, workspace_bytes,
                             stream) -> int:
     a_in, a_b, a_n, a_out = _ptrs(h_in), _sizes(h_in_bytes), _sizes(h_num_elements), _ptrs(h_out)
-    v = ctypes.c_void_p
-    return int(lib().uzip_decompress_batched(dtype, len(h_in), ctypes.cast(a_in, v), ctypes.cast(a_b, v),
-                                             ctypes.cast(a_n, v), ctypes.cast(a_out, v), d_status, d_workspace,
-                                             workspace_bytes, stream))
+    return int(lib().uzip_decompress_batched(dtype, len(h_in), a_in.ptr, a_b.ptr, a_n.ptr, a_out.ptr, d_status,
+                                             d_workspace, workspace_bytes, stream))
 
 
 def uzip_profile_set_events(main_start, main_stop) -> int:
@@ -220,9 +225,8 @@ def compress_batched(tensors, chunk_bytes: int = 0, outs=None, ws=None, out_size
     code = dtype_code(tensors[0].dtype)
     dev = tensors[0].device
     ns = [t.numel() for t in tensors]
-    caps = [uzip_max_compressed_size(code, n, chunk_bytes) for n in ns]
     if outs is None:
-        outs = [torch.empty(c, dtype=torch.uint8, device=dev) for c in caps]
+        outs = [torch.empty(uzip_max_compressed_size(code, n, chunk_bytes), dtype=torch.uint8, device=dev) for n in ns]
     if out_sizes is None:
         out_sizes = torch.empty(len(tensors), dtype=torch.int64, device=dev)
     if ws is None:

@@ -38,9 +38,16 @@ uint64_t chunk_elems_of(uzip_dtype dtype, size_t chunk_bytes) {
 }
 
 struct EncWs {
-    uint64_t descs, sizes, tile_sums, tile_offs, slots, slot_stride, ntiles, bytes;
+    uint64_t descs, sizes, flags, ticket, slots, slot_stride, bytes;
 };
 
+// Compress workspace: descriptors (batched calls), record size per chunk,
+// one look-back word per chunk pair (at most one pair per chunk), the
+// compaction's ticket counter, and one slot per chunk, where the encoder
+// builds the record before its offset is known.  A slot holds the chunk's RAW
+// record, and at least the largest RANS prefix (header, bitmap, 256
+// frequencies, states), which the encoder writes before it knows whether the
+// chunk will be stored RAW.
 EncWs enc_ws(uint64_t nbuf, uint64_t chunks, uint64_t ce) {
     EncWs w{};
     uint64_t o = 0;
@@ -48,15 +55,11 @@ EncWs enc_ws(uint64_t nbuf, uint64_t chunks, uint64_t ce) {
     o += al(nbuf > 1 ? nbuf * sizeof(EncDesc) : 0);
     w.sizes = o;
     o += al(chunks * 4);
-    w.ntiles = (chunks + kTile - 1) / kTile;
-    w.tile_sums = o;
-    o += al(w.ntiles * 8);
-    w.tile_offs = o;
-    o += al((w.ntiles + 1) * 8);
-    // A slot holds the chunk's RAW record, and at least the largest RANS
-    // prefix (header, bitmap, 256 frequencies, states), which the encoder
-    // writes before it knows whether the chunk will be stored RAW.
-    w.slot_stride = std::max<uint64_t>(align16(kRecHeaderBytes + ce), align16(words_offset(256)));
+    w.flags = o;
+    o += al(chunks * 8);
+    w.ticket = o;
+    o += al(8);
+    w.slot_stride = std::max<uint64_t>(raw_record_bytes(ce), align16(words_offset(256)));
     w.slots = o;
     o += chunks * w.slot_stride;
     w.bytes = o + kWsAlign;  // slack: the caller's pointer need only be 16-byte aligned
@@ -105,16 +108,20 @@ uzip_status compress_impl(uzip_dtype dtype, uint64_t ce, std::vector<EncDesc> &d
     ep.chunk_elems = (uint32_t)ce;
     ep.total_chunks = chunks;
     ep.total_pairs = 0;
+    uint64_t tiles = 0;
     for (EncDesc &d : descs) {
+        const uint64_t pairs = (d.chunks + 1) / 2;
         d.pair_first = ep.total_pairs;
-        ep.total_pairs += (d.chunks + 1) / 2;
+        d.tile_first = tiles;
+        ep.total_pairs += pairs;
+        tiles += (pairs + kPairTile - 1) / kPairTile;
     }
     ep.slots = base + w.slots;
     ep.slot_stride = w.slot_stride;
     ep.rec_sizes = reinterpret_cast<uint32_t *>(base + w.sizes);
+    ep.flags = reinterpret_cast<uint64_t *>(base + w.flags);
+    ep.ticket = reinterpret_cast<uint32_t *>(base + w.ticket);
     ep.dtype = dtype;
-    bool any_empty = false;
-    for (const EncDesc &d : descs) any_empty |= d.n == 0;
     if (nbuf == 1) {
         ep.single = descs[0];
         ep.descs = nullptr;
@@ -126,19 +133,7 @@ uzip_status compress_impl(uzip_dtype dtype, uint64_t ce, std::vector<EncDesc> &d
             return UZIP_ERR_DEVICE;
         ep.descs = dd;
     }
-    CompactParams cp{};
-    cp.descs = ep.descs;
-    cp.single = ep.single;
-    cp.nbuf = nbuf;
-    cp.chunk_elems = ep.chunk_elems;
-    cp.total_chunks = chunks;
-    cp.slots = ep.slots;
-    cp.slot_stride = ep.slot_stride;
-    cp.rec_sizes = ep.rec_sizes;
-    cp.tile_offs = reinterpret_cast<const uint64_t *>(base + w.tile_offs);
-    cp.dtype = dtype;
-    const hipError_t e = launch_compress(ep, cp, reinterpret_cast<uint64_t *>(base + w.tile_sums),
-                                         reinterpret_cast<uint64_t *>(base + w.tile_offs), w.ntiles, any_empty, stream);
+    const hipError_t e = launch_compress(ep, stream);
     return e == hipSuccess ? UZIP_OK : UZIP_ERR_DEVICE;
 }
 

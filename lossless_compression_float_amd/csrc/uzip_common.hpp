@@ -25,7 +25,7 @@ constexpr uint32_t kVersion = 1;
 constexpr uint32_t kHeaderBytes = 64;
 constexpr uint32_t kRecHeaderBytes = 16;
 constexpr uint32_t kMaxChunkElems = 1u << 20;
-constexpr uint32_t kTile = 1024;  // chunks per scan tile
+constexpr uint32_t kPairTile = 64;  // chunk pairs per tile of the record-offset scan
 
 __host__ __device__ inline uint64_t align16(uint64_t v) { return (v + 15u) & ~uint64_t(15); }
 __host__ __device__ inline uint64_t align4(uint64_t v) { return (v + 3u) & ~uint64_t(3); }
@@ -68,7 +68,7 @@ struct alignas(16) EncDesc {
     uint64_t exp_off;
     uint64_t chunks;
     uint64_t pair_first;    // global index of the buffer's first chunk pair
-    uint64_t pad;
+    uint64_t tile_first;    // global index of the buffer's first tile of kPairTile chunk pairs
 };
 
 // One buffer of a decompress call as the caller states it.

@@ -12,13 +12,14 @@
 //                the 32-lane rANS encoder backward over the chunk (re-reading
 //                the input, which the cache still holds), placing each step's
 //                renormalisation words by wave ballot + lane rank.  The record
-//                goes to a workspace slot.
-//   k_tile_reduce, k_scan_u64
-//                exclusive scan of the record sizes (two levels: tiles of
-//                1024 chunks, then one workgroup over the tile sums).
-//   k_compact    moves every record to its final offset, writes the record
-//                index and, for the last chunk of a buffer, the header and the
-//                compressed size (NCCLZ Sec. IV-D2: self-describing frames).
+//                is built in a workspace slot (words filled from its end).
+//   k_compact    one wave per record, workgroups in ticket order: the record
+//                offsets (an exclusive scan of the record sizes: tile sums
+//                plus a decoupled look-back over tiles), the records copied
+//                to their final place, the index entries, and for a buffer's
+//                last record the header and the compressed size (NCCLZ
+//                Sec. IV-D2: self-describing frames).
+//   k_prepare    zeroes the look-back words; writes the buffers of empty inputs.
 // Decompression (NCCLZ Algorithm 2: validate the header, then decode):
 //   k_dec_validate  one thread per buffer checks the buffer header.
 //   k_decode        one half-wave per chunk: validates the record, builds the
@@ -171,18 +172,6 @@ __device__ inline HalfBallot half_ballot(bool pred, uint32_t h, uint32_t lo_bits
     return HalfBallot{h ? (uint32_t)__popc(mhi) : plo, below - (plo & lo_bits)};
 }
 
-// the buffer holding global chunk g: the largest b with chunk_first[b] <= g
-// (buffers without chunks share their successor's chunk_first and are skipped)
-__device__ inline uint32_t find_enc_buffer(const EncDesc *d, uint32_t nbuf, uint64_t g) {
-    uint32_t lo = 0, hi = nbuf - 1;
-    while (lo < hi) {
-        uint32_t mid = (lo + hi + 1) >> 1;
-        if (gload<uint64_t>(&d[mid].chunk_first) <= g) lo = mid;
-        else hi = mid - 1;
-    }
-    return lo;
-}
-
 __device__ inline uint32_t find_dec_buffer(const uint64_t *chunk_first, uint32_t nbuf, uint64_t g) {
     uint32_t lo = 0, hi = nbuf - 1;
     while (lo < hi) {
@@ -232,6 +221,175 @@ __device__ inline uint32_t load_value(const uint8_t *in, uint32_t i) {
 template <int DT>
 __device__ inline uint32_t exponent_of(uint32_t v) {
     return DT == 1 ? (v >> 7) & 0xFFu : (v >> 23) & 0xFFu;
+}
+
+// 32-bit word k (0..15) of a buffer header (bitstream v1; NCCLZ Sec. IV-D2
+// self-describing frame: magic, version, codec parameters, sizes)
+__device__ inline uint32_t header_word(uint32_t k, int dtype, uint32_t chunk_elems, uint64_t n, uint64_t chunks,
+                                       uint64_t sm_off, uint64_t exp_off, uint64_t total) {
+    switch (k) {
+        case 0: return kMagic;
+        case 1: return kVersion | (uint32_t(dtype) << 16) | (kProbBits << 24);
+        case 2: return kLanes | (raw_bytes_per_value(dtype) << 8);
+        case 3: return chunk_elems;
+        case 4: return (uint32_t)n;
+        case 5: return (uint32_t)(n >> 32);
+        case 6: return (uint32_t)chunks;
+        case 7: return (uint32_t)(chunks >> 32);
+        case 8: return (uint32_t)sm_off;
+        case 9: return (uint32_t)(sm_off >> 32);
+        case 10: return (uint32_t)exp_off;
+        case 11: return (uint32_t)(exp_off >> 32);
+        case 12: return (uint32_t)total;
+        case 13: return (uint32_t)(total >> 32);
+        default: return 0;
+    }
+}
+
+// Exclusive prefix of the record bytes of the tiles before tile t of a buffer
+// (first tile tfirst), by decoupled look-back (Merrill & Garland, single-pass
+// prefix scan).  A tile's leader publishes the tile's total at once, then sums
+// the published totals of the tiles before it back to the nearest one whose
+// inclusive prefix is already known, and publishes its own inclusive prefix;
+// the other waves of the tile read the same words without publishing.  A
+// look-back word holds a 2-bit state (0 nothing yet, 1 total, 2 inclusive
+// prefix) over a 62-bit byte count, so one 64-bit access carries both.  The
+// buffer's first tile publishes its inclusive prefix without waiting, so a
+// walk never leaves its buffer, and a wave only waits for tiles whose leaders
+// hold lower tickets and already run.  Lane l reads the tile at distance
+// back + l; a wave waiting for a tile re-reads its window after a short pause.
+// The whole wave calls this; the result is wave-uniform.
+__device__ inline uint64_t tile_lookback(uint64_t *flags, uint64_t t, uint64_t tfirst, uint64_t agg, bool leader,
+                                         uint32_t lane) {
+    constexpr uint64_t kAggregate = 1ull << 62, kInclusive = 2ull << 62, kCount = kAggregate - 1;
+    if (t == tfirst) {
+        if (leader && lane == 0) __hip_atomic_store(flags + t, kInclusive | agg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return 0;
+    }
+    if (leader && lane == 0) __hip_atomic_store(flags + t, kAggregate | agg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint64_t excl = 0;
+    for (uint64_t back = 1;;) {
+        const uint64_t b = back + lane;
+        const uint64_t v =
+            b <= t - tfirst ? __hip_atomic_load(flags + (t - b), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : kInclusive;
+        const uint64_t incl = __builtin_amdgcn_ballot_w64((v >> 62) == 2);
+        const uint64_t none = __builtin_amdgcn_ballot_w64((v >> 62) == 0);
+        const uint64_t upto = incl ? ((incl & (0 - incl)) << 1) - 1 : ~0ull;  // lanes up to the nearest inclusive one
+        if (none & upto) {  // a needed tile has not published yet
+            __builtin_amdgcn_s_sleep(1);
+            continue;
+        }
+        excl += wave_sum_u64(((upto >> lane) & 1) ? (v & kCount) : 0);
+        if (incl) break;
+        back += 64;
+    }
+    if (leader && lane == 0)
+        __hip_atomic_store(flags + t, kInclusive | (excl + agg), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return excl;
+}
+
+// Bytes [sh, sh + 16) of the 32 bytes L:H (sh = 4 DS + bs, bs in {0, 2}).
+template <int DS>
+__device__ inline uint4 funnel16(const uint4 &L, const uint4 &H, uint32_t bs) {
+    const uint32_t w[8] = {L.x, L.y, L.z, L.w, H.x, H.y, H.z, H.w};
+    return make_uint4(__builtin_amdgcn_alignbyte(w[DS + 1], w[DS], bs), __builtin_amdgcn_alignbyte(w[DS + 2], w[DS + 1], bs),
+                      __builtin_amdgcn_alignbyte(w[DS + 3], w[DS + 2], bs), __builtin_amdgcn_alignbyte(w[DS + 4], w[DS + 3], bs));
+}
+
+// mask of the bytes of dword j (bytes [4j, 4j + 4) of a unit) below n, n even
+__device__ inline uint32_t low_bytes_mask(uint32_t n, uint32_t j) {
+    const uint32_t vb = n > 4 * j ? min(n - 4 * j, 4u) : 0u;
+    return vb >= 4 ? 0xFFFFFFFFu : (1u << (8 * vb)) - 1u;
+}
+
+// Word area of a coded record: record bytes [wofs, size) get the W bytes of
+// words found at byte src of the slot resource, then zeros.  The whole wave
+// calls this with wave-uniform arguments; wofs is a multiple of 4, size of
+// 16, W and src are even.  Up to three head dwords bring the destination to a
+// 16-byte boundary; each later 16-byte unit is funnelled out of two aligned
+// 16-byte loads, four units per lane in flight.
+__device__ inline void copy_words(rsrc_t rslot, uint8_t *rec, uint32_t wofs, uint32_t size, uint32_t W, uint32_t src,
+                                  uint32_t lane) {
+    const uint32_t a = (wofs + 15u) & ~15u;
+    if (lane < (a - wofs) / 4) {
+        const uint32_t rel = 4 * lane, sb = src + rel;
+        uint32_t v = (sb & 2u) ? __builtin_amdgcn_alignbit(bld32(rslot, sb + 2), bld32(rslot, sb - 2), 16)
+                               : bld32(rslot, sb);
+        v &= low_bytes_mask(W > rel ? min(W - rel, 4u) : 0u, 0);
+        gstore<uint32_t>(rec + wofs + rel, v);
+    }
+    const uint32_t s0 = src + (a - wofs), sh = s0 & 15u, base = s0 - sh, bs = sh & 3u, ds = sh >> 2;
+    const uint32_t nu = (size - a) / 16;
+    for (uint32_t u0 = 0; u0 < nu; u0 += 256) {
+        uint4 L[4], H[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint32_t u = u0 + 64 * k + lane;
+            const uint32_t o = u < nu ? base + 16 * u : kOutOfRange;
+            L[k] = bld128(rslot, o);
+            H[k] = bld128(rslot, o + 16);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint32_t u = u0 + 64 * k + lane;
+            if (u < nu) {
+                uint4 v;
+                switch (ds) {
+                    case 0: v = funnel16<0>(L[k], H[k], bs); break;
+                    case 1: v = funnel16<1>(L[k], H[k], bs); break;
+                    case 2: v = funnel16<2>(L[k], H[k], bs); break;
+                    default: v = funnel16<3>(L[k], H[k], bs); break;
+                }
+                const uint32_t rel = (a - wofs) + 16 * u;
+                const uint32_t n = W > rel ? min(W - rel, 16u) : 0u;
+                v.x &= low_bytes_mask(n, 0);
+                v.y &= low_bytes_mask(n, 1);
+                v.z &= low_bytes_mask(n, 2);
+                v.w &= low_bytes_mask(n, 3);
+                gstore<uint4>(rec + a + 16 * u, v);
+            }
+        }
+    }
+}
+
+// Body of a RAW record: bytes [16, size) get the exponents of the chunk's ni
+// values (at byte in0 of the input resource), then zeros.  Whole wave,
+// wave-uniform arguments; one 16-byte unit (16 exponents) per lane.
+template <int DT>
+__device__ inline void raw_exponents(rsrc_t rin, uint8_t *rec, uint32_t size, uint32_t ni, uint32_t in0, uint32_t lane) {
+    constexpr uint32_t EB = DT == 1 ? 2 : 4;
+    const uint32_t nu = (size - kRecHeaderBytes) / 16;
+    for (uint32_t u = lane; u < nu; u += 64) {
+        uint32_t w[16];
+        if (16 * u + 16 <= ni) {
+#pragma unroll
+            for (uint32_t k = 0; k < 16 * EB / 16; ++k) {
+                const uint4 q = bld128(rin, in0 + (16 * u) * EB + 16 * k);
+                const uint32_t qq[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+                for (uint32_t t = 0; t < 4; ++t) {
+                    if (DT == 1) {
+                        w[8 * k + 2 * t] = qq[t] & 0xFFFFu;
+                        w[8 * k + 2 * t + 1] = qq[t] >> 16;
+                    } else {
+                        w[4 * k + t] = qq[t];
+                    }
+                }
+            }
+        } else {  // the chunk's end: value by value, nothing read past it
+#pragma unroll
+            for (uint32_t k = 0; k < 16; ++k) {
+                const uint32_t e = 16 * u + k;
+                const uint32_t o = e < ni ? in0 + e * EB : kOutOfRange;
+                w[k] = DT == 1 ? bld16(rin, o) : bld32(rin, o);
+            }
+        }
+        uint32_t v[4] = {0, 0, 0, 0};
+#pragma unroll
+        for (uint32_t k = 0; k < 16; ++k)
+            if (16 * u + k < ni) v[k >> 2] |= exponent_of<DT>(w[k]) << (8 * (k & 3));
+        gstore<uint4>(rec + kRecHeaderBytes + 16 * u, make_uint4(v[0], v[1], v[2], v[3]));
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -423,7 +581,7 @@ __global__ __launch_bounds__(64) void k_encode(EncParams p) {
         tab[lj * 8 + k] = make_uint4(f[k], cbase + cpre[k], (uint32_t)rb, (uint32_t)(rb >> 32));
     }
 
-    // record prefix: presence bitmap, frequencies (ascending symbols), pad
+    // record prefix in the slot: presence bitmap, frequencies (ascending symbols), pad
     if (valid) {
         gstore<uint8_t>(slot + kRecHeaderBytes + lj, (uint8_t)pm);
         uint32_t k2 = pre;
@@ -443,13 +601,16 @@ __global__ __launch_bounds__(64) void k_encode(EncParams p) {
     // input resource (past the pair: zeros, never coded).
     const uint32_t nsym0 = uniform_u32(__shfl((int)nsym, 0, 64)), nsym1 = uniform_u32(__shfl((int)nsym, 32, 64));
     const uint32_t raw0 = (uint32_t)raw_record_bytes(vals0), raw1 = (uint32_t)raw_record_bytes(vals1);
-    const uint32_t wcap0 = (raw0 - (uint32_t)words_offset(nsym0)) / 2;
-    const uint32_t wcap1 = nch == 2 ? (raw1 - (uint32_t)words_offset(nsym1)) / 2 : 0u;
+    const uint32_t wofs0 = (uint32_t)words_offset(nsym0), wofs1 = (uint32_t)words_offset(nsym1);
+    // words that fit before a record reaches its RAW size; a chunk whose table
+    // alone reaches it is RAW without coding
+    const uint32_t wcap0 = raw0 > wofs0 ? (raw0 - wofs0) / 2 : 0u;
+    const uint32_t wcap1 = nch == 2 && raw1 > wofs1 ? (raw1 - wofs1) / 2 : 0u;
     const uint32_t end0 = raw0 / 2, end1 = ((uint32_t)p.slot_stride + raw1) / 2;  // word index just past each slot's words
     uint32_t nw0 = 0, nw1 = 0;
-    bool alive0 = true, alive1 = nch == 2;  // a half stops coding once its words outgrow the RAW size
+    bool alive0 = wcap0 > 0, alive1 = wcap1 > 0;  // a half stops coding once its words outgrow the RAW size
     uint32_t x = kStateLow;
-    const uint32_t T0 = (vals0 + 31) / 32, T1 = (vals1 + 31) / 32;
+    const uint32_t T0 = alive0 ? (vals0 + 31) / 32 : 0u, T1 = alive1 ? (vals1 + 31) / 32 : 0u;
     const uint32_t nblk = (max(T0, T1) + 7) / 8;
     const uint32_t hsel = h ? 0xFFFFFFFFu : 0u;
     uint32_t cur[8], nxt[8];
@@ -516,49 +677,122 @@ __global__ __launch_bounds__(64) void k_encode(EncParams p) {
         for (int k = 0; k < 8; ++k) cur[k] = nxt[k];
     }
 
+    // ---- the record's fixed part into the slot (the words are already at its
+    // end); a RAW record gets its header only: k_compact takes its exponents
+    // from the input ----
     const uint32_t nw = h ? nw1 : nw0;
     const bool alive = h ? alive1 : alive0;
-    const uint64_t wofs = words_offset(nsym);
-    const uint64_t raw_i = raw_record_bytes(ni);
-    const uint64_t rans_bytes = align16(wofs + 2ull * nw);
-    const bool rans = valid && alive && rans_bytes < raw_i;
+    const uint32_t raw_i = h ? raw1 : raw0;
+    const uint32_t rans_bytes = (uint32_t)align16(words_offset(nsym) + 2ull * nw);
     if (valid) {
-        if (rans) {
-            gstore<uint32_t>(slot + states_offset(nsym) + 4 * lj, x);
-            if (lj == 0) {
-                gstore<uint4>(slot, make_uint4(nsym << 16, nw, ni, (uint32_t)rans_bytes));
-                gstore<uint32_t>(p.rec_sizes + g, (uint32_t)rans_bytes);
-            }
-        } else {
-            if (lj == 0) {
-                gstore<uint4>(slot, make_uint4(1u, 0u, ni, (uint32_t)raw_i));
-                gstore<uint32_t>(p.rec_sizes + g, (uint32_t)raw_i);
-            }
-            for (uint32_t k = lj; k + kRecHeaderBytes < raw_i; k += 32) {
-                const uint32_t v = DT == 1 ? bld16(rin, in0 + k * EB) : bld32(rin, in0 + k * EB);
-                gstore<uint8_t>(slot + kRecHeaderBytes + k, k < ni ? (uint8_t)exponent_of<DT>(v) : (uint8_t)0);
-            }
+        const bool rans = alive && rans_bytes < raw_i;  // ties go RAW
+        if (rans) gstore<uint32_t>(slot + states_offset(nsym) + 4 * lj, x);
+        if (lj == 0) {
+            gstore<uint4>(slot, rans ? make_uint4(nsym << 16, nw, ni, rans_bytes) : make_uint4(1u, 0u, ni, raw_i));
+            gstore<uint32_t>(p.rec_sizes + g, rans ? rans_bytes : raw_i);
         }
     }
 }
 
 // ---------------------------------------------------------------------------
-// scan of the record sizes
+// k_compact: record offsets (exclusive scan of the record sizes) and the
+// records at their final place
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_tile_reduce(const uint32_t *sizes, uint64_t total_chunks, uint64_t *tile_sums) {
-    __shared__ uint64_t s[256];
-    const uint64_t t0 = uint64_t(blockIdx.x) * kTile;
-    uint64_t acc = 0;
-    for (uint64_t k = t0 + threadIdx.x; k < t0 + kTile && k < total_chunks; k += 256) acc += gload<uint32_t>(sizes + k);
-    s[threadIdx.x] = acc;
+// A workgroup of 2 * kCompactPairs waves takes the next kCompactPairs chunk
+// pairs in ticket order; wave w works on record w & 1 of pair w >> 1.  Both
+// waves of a pair find the offset of the pair's records (the sizes of the
+// pair's tile summed directly, plus the tile's prefix by look-back over the
+// buffer's tiles, whose totals the tile's first pair publishes); then each
+// wave writes its index entry and copies its record from the slot (RAW
+// records are rebuilt from the input), and the buffer's last record writes
+// the final index entry, the header, the zero gaps and the compressed size
+// (NCCLZ Sec. IV-D2: self-describing frames).  A wave only waits for tile
+// leaders in workgroups with lower tickets, or in its own workgroup, all of
+// which already run.
+constexpr uint32_t kCompactPairs = 4;
+
+template <int DT>
+__global__ __launch_bounds__(128 * kCompactPairs) void k_compact(EncParams p) {
+    constexpr uint32_t EB = DT == 1 ? 2 : 4;
+    constexpr uint32_t R = DT == 1 ? 1 : 3;
+    __shared__ uint32_t s_ticket;
+    const uint32_t lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    if (threadIdx.x == 0) s_ticket = __hip_atomic_fetch_add(p.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
-    for (int o = 128; o > 0; o >>= 1) {
-        if ((int)threadIdx.x < o) s[threadIdx.x] += s[threadIdx.x + o];
-        __syncthreads();
+    const uint64_t q = uint64_t(uniform_u32(s_ticket)) * kCompactPairs + (w >> 1);
+    const uint32_t r = w & 1;
+    if (q >= p.total_pairs) return;
+    const EncDesc d = p.nbuf == 1 ? p.single
+                                  : load_enc_desc(p.descs + uniform_u32(find_enc_pair_buffer(p.descs, p.nbuf, q)));
+    const uint64_t ce = p.chunk_elems;
+    const uint64_t n = uniform_u64(d.n);
+    const uint64_t c0 = 2 * (q - uniform_u64(d.pair_first));
+    const uint64_t chunks = uniform_u64(d.chunks);
+    const uint32_t nch = chunks - c0 >= 2 ? 2u : 1u;
+    const uint64_t g0 = uniform_u64(d.chunk_first) + c0;
+    const uint32_t size0 = uniform_u32(gload<uint32_t>(p.rec_sizes + g0));
+    const uint32_t size1 = nch == 2 ? uniform_u32(gload<uint32_t>(p.rec_sizes + g0 + 1)) : 0u;
+    // Offset of the pair's records in two levels: the sizes of the pairs of
+    // its tile (lane l: pair l of the tile), summed directly, plus the tile's
+    // exclusive prefix by look-back over the buffer's tiles.
+    const uint64_t lp = q - uniform_u64(d.pair_first);  // pair index in the buffer
+    const uint64_t lt = lp / kPairTile;
+    const uint32_t pos = (uint32_t)(lp % kPairTile);
+    const uint64_t pl = lt * kPairTile + lane, cf = uniform_u64(d.chunk_first);
+    uint64_t ps = 0;
+    if (lane < kPairTile && 2 * pl < chunks) {
+        ps = gload<uint32_t>(p.rec_sizes + cf + 2 * pl);
+        if (2 * pl + 1 < chunks) ps += gload<uint32_t>(p.rec_sizes + cf + 2 * pl + 1);
     }
-    if (threadIdx.x == 0) gstore<uint64_t>(tile_sums + blockIdx.x, s[0]);
+    const uint64_t tile_total = wave_sum_u64(ps);
+    const uint64_t in_tile = wave_sum_u64(lane < pos ? ps : 0);
+    const uint64_t tfirst = uniform_u64(d.tile_first);
+    const uint64_t rec0 = in_tile + tile_lookback(p.flags, tfirst + lt, tfirst, tile_total, pos == 0 && r == 0, lane);
+    if (r >= nch) return;
+
+    // this wave's record
+    const uint32_t stride = (uint32_t)p.slot_stride;
+    const uint32_t vals0 = (uint32_t)min<uint64_t>(ce, n - c0 * ce);
+    const uint32_t ni = r ? (uint32_t)min<uint64_t>(ce, n - (c0 + 1) * ce) : vals0;
+    const uint32_t size = r ? size1 : size0;
+    const uint64_t off = r ? rec0 + size0 : rec0;
+    uint8_t *out = d.out;
+    const uint64_t exp_off = uniform_u64(d.exp_off);
+    uint8_t *rec = out + exp_off + off;
+    if (lane == 0) gstore<uint64_t>(out + kHeaderBytes + 8 * (c0 + r), off);
+    const rsrc_t rslot = make_rsrc(p.slots + (g0 + r) * p.slot_stride, stride);
+    const uint4 hd = bld128(rslot, 0);
+    const uint32_t mode = uniform_u32(hd.x) & 0xFFu, nsym = uniform_u32(hd.x) >> 16, nw = uniform_u32(hd.y);
+    if (mode == 0) {
+        // header, bitmap, frequencies, pad, states, then the words
+        const uint32_t wofs = (uint32_t)words_offset(nsym);
+        for (uint32_t k = lane; k < wofs / 4; k += 64) gstore<uint32_t>(rec + 4 * k, bld32(rslot, 4 * k));
+        copy_words(rslot, rec, wofs, size, 2 * nw, (uint32_t)raw_record_bytes(ni) - 2 * nw, lane);
+    } else {
+        const rsrc_t rin = make_rsrc(d.in + (c0 + r) * ce * EB, ni * EB);
+        if (lane < 4) gstore<uint32_t>(rec + 4 * lane, bld32(rslot, 4 * lane));
+        raw_exponents<DT>(rin, rec, size, ni, 0u, lane);
+    }
+
+    if (c0 + r + 1 == chunks) {  // the buffer's last record
+        const uint64_t recs = off + size;
+        const uint64_t total = exp_off + recs;
+        if (lane == 0) {
+            gstore<uint64_t>(out + kHeaderBytes + 8 * chunks, recs);
+            gstore<uint64_t>(d.out_size, total);
+        }
+        if (lane < 16)
+            gstore<uint32_t>(out + 4 * lane, header_word(lane, p.dtype, p.chunk_elems, n, chunks, d.sm_off, exp_off, total));
+        const uint64_t gap0 = kHeaderBytes + 8 * (chunks + 1);
+        for (uint64_t k = gap0 + lane; k < d.sm_off; k += 64) gstore<uint8_t>(out + k, 0);
+        const uint64_t gap1 = d.sm_off + uint64_t(R) * n;
+        for (uint64_t k = gap1 + lane; k < exp_off; k += 64) gstore<uint8_t>(out + k, 0);
+    }
 }
 
+// ---------------------------------------------------------------------------
+// scans
+// ---------------------------------------------------------------------------
 // exclusive scan of n values into out[0..n] (out[n] = total); in may equal out
 __global__ __launch_bounds__(1024) void k_scan_u64(const uint64_t *in, uint64_t *out, uint64_t n) {
     __shared__ uint64_t s[1024];
@@ -581,88 +815,23 @@ __global__ __launch_bounds__(1024) void k_scan_u64(const uint64_t *in, uint64_t 
     if (threadIdx.x == 0) gstore<uint64_t>(out + n, carry);
 }
 
-// global exclusive offset of chunk g (whole wave of 64 lanes participates)
-__device__ inline uint64_t chunk_offset(const uint32_t *sizes, const uint64_t *tile_offs, uint64_t g, uint32_t lane) {
-    const uint64_t t0 = (g / kTile) * kTile;
-    uint64_t s = 0;
-    for (uint64_t k = t0 + lane; k < g; k += 64) s += gload<uint32_t>(sizes + k);
-    return gload<uint64_t>(tile_offs + g / kTile) + wave_sum_u64(s);
-}
-
-// ---------------------------------------------------------------------------
-// k_compact: records to their final offsets, index, header, size
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(64) void k_compact(CompactParams p) {
-    const uint64_t g = blockIdx.x;
-    const uint32_t lane = threadIdx.x;
-    const EncDesc d = p.nbuf == 1 ? p.single : load_enc_desc(p.descs + find_enc_buffer(p.descs, p.nbuf, g));
-    const uint64_t ci = g - d.chunk_first;
-    const uint32_t size = gload<uint32_t>(p.rec_sizes + g);
-    const uint64_t off_g = chunk_offset(p.rec_sizes, p.tile_offs, g, lane);
-    const uint64_t off_first = ci == 0 ? off_g : chunk_offset(p.rec_sizes, p.tile_offs, d.chunk_first, lane);
-    const uint64_t rec_off = off_g - off_first;
-    uint8_t *out = d.out;
-    if (lane == 0) gstore<uint64_t>(out + kHeaderBytes + 8 * ci, rec_off);
-    if (ci + 1 == d.chunks) {
-        const uint64_t total = d.exp_off + rec_off + size;
-        if (lane == 0) {
-            gstore<uint64_t>(out + kHeaderBytes + 8 * d.chunks, rec_off + size);
-            gstore<uint64_t>(d.out_size, total);
+// Before the encoder: zero the look-back words and the ticket counter (a fill
+// kernel rather than a memset, so the call stays valid inside a captured
+// graph), and write the 80-byte buffer of every empty input (N = 0).
+__global__ __launch_bounds__(256) void k_prepare(EncParams p) {
+    const uint64_t i = uint64_t(blockIdx.x) * 256 + threadIdx.x;
+    if (i < p.total_pairs) gstore<uint64_t>(p.flags + i, 0);
+    if (i == 0) gstore<uint32_t>(p.ticket, 0);
+    if (i < p.nbuf) {
+        const EncDesc d = p.nbuf == 1 ? p.single : load_enc_desc(p.descs + i);
+        if (d.n == 0) {
+            for (uint32_t k = 0; k < 16; ++k)
+                gstore<uint32_t>(d.out + 4 * k, header_word(k, p.dtype, p.chunk_elems, 0, 0, 80, 80, 80));
+            gstore<uint64_t>(d.out + kHeaderBytes, 0);
+            gstore<uint64_t>(d.out + kHeaderBytes + 8, 0);
+            gstore<uint64_t>(d.out_size, 80);
         }
-        if (lane < 16) {
-            uint32_t wv = 0;
-            switch (lane) {
-                case 0: wv = kMagic; break;
-                case 1: wv = kVersion | (uint32_t(p.dtype) << 16) | (kProbBits << 24); break;
-                case 2: wv = kLanes | (raw_bytes_per_value(p.dtype) << 8); break;
-                case 3: wv = p.chunk_elems; break;
-                case 4: wv = (uint32_t)d.n; break;
-                case 5: wv = (uint32_t)(d.n >> 32); break;
-                case 6: wv = (uint32_t)d.chunks; break;
-                case 7: wv = (uint32_t)(d.chunks >> 32); break;
-                case 8: wv = (uint32_t)d.sm_off; break;
-                case 9: wv = (uint32_t)(d.sm_off >> 32); break;
-                case 10: wv = (uint32_t)d.exp_off; break;
-                case 11: wv = (uint32_t)(d.exp_off >> 32); break;
-                case 12: wv = (uint32_t)total; break;
-                case 13: wv = (uint32_t)(total >> 32); break;
-                default: wv = 0; break;
-            }
-            gstore<uint32_t>(out + 4 * lane, wv);
-        }
-        // zero the gaps after the index and after the sign+mantissa region
-        const uint64_t gap0 = kHeaderBytes + 8 * (d.chunks + 1);
-        for (uint64_t k = gap0 + lane; k < d.sm_off; k += 64) gstore<uint8_t>(out + k, 0);
-        const uint64_t gap1 = d.sm_off + uint64_t(raw_bytes_per_value(p.dtype)) * d.n;
-        for (uint64_t k = gap1 + lane; k < d.exp_off; k += 64) gstore<uint8_t>(out + k, 0);
     }
-    // copy the record
-    const uint8_t *src = p.slots + g * p.slot_stride;
-    uint8_t *dst = out + d.exp_off + rec_off;
-    const uint4 rh = gload<uint4>(src);
-    if ((rh.x & 0xFFu) == 0) {
-        const uint32_t nsym = rh.x >> 16, nw = rh.y, ni = rh.z;
-        const uint32_t wofs = (uint32_t)words_offset(nsym);
-        for (uint32_t k = lane; k < wofs / 4; k += 64) gstore<uint32_t>(dst + 4 * k, gload<uint32_t>(src + 4 * k));
-        const uint8_t *wsrc = src + raw_record_bytes(ni) - 2ull * nw;
-        for (uint32_t k = lane; k < nw; k += 64) gstore<uint16_t>(dst + wofs + 2 * k, gload<uint16_t>(wsrc + 2 * k));
-        for (uint32_t k = wofs + 2 * nw + lane; k < size; k += 64) gstore<uint8_t>(dst + k, 0);
-    } else {
-        for (uint32_t k = lane; k < size / 16; k += 64) gstore<uint4>(dst + 16 * k, gload<uint4>(src + 16 * k));
-    }
-}
-
-// header of an empty buffer (N = 0): 64-byte header, one index entry, pad
-__global__ void k_empty_headers(const EncDesc *descs, EncDesc single, uint32_t nbuf, int dtype, uint32_t chunk_elems) {
-    const uint32_t b = blockIdx.x * blockDim.x + threadIdx.x;
-    if (b >= nbuf) return;
-    const EncDesc d = nbuf == 1 ? single : load_enc_desc(descs + b);
-    if (d.n != 0) return;
-    const uint32_t hdr[20] = {kMagic, kVersion | (uint32_t(dtype) << 16) | (kProbBits << 24),
-                              kLanes | (raw_bytes_per_value(dtype) << 8), chunk_elems, 0, 0, 0, 0, 80, 0, 80, 0,
-                              80, 0, 0, 0, 0, 0, 0, 0};
-    for (int k = 0; k < 20; ++k) gstore<uint32_t>(d.out + 4 * k, hdr[k]);
-    gstore<uint64_t>(d.out_size, 80);
 }
 
 // ---------------------------------------------------------------------------
@@ -966,21 +1135,18 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
 // ---------------------------------------------------------------------------
 thread_local ProfileEvents g_profile;
 
-hipError_t launch_compress(const EncParams &ep, const CompactParams &cp, uint64_t *tile_sums, uint64_t *tile_offs,
-                           uint64_t ntiles, bool any_empty, hipStream_t stream) {
-    if (any_empty) {
-        const uint32_t nb = ep.nbuf;
-        k_empty_headers<<<(nb + 255) / 256, 256, 0, stream>>>(ep.descs, ep.single, nb, ep.dtype, ep.chunk_elems);
-    }
-    if (ep.total_chunks > 0) {
-        const uint64_t grid = ep.total_pairs;
+hipError_t launch_compress(const EncParams &ep, hipStream_t stream) {
+    uint64_t threads = ep.total_pairs > ep.nbuf ? ep.total_pairs : ep.nbuf;
+    k_prepare<<<dim3((uint32_t)((threads + 255) / 256)), dim3(256), 0, stream>>>(ep);
+    if (ep.total_pairs > 0) {
+        const dim3 grid((uint32_t)ep.total_pairs);
         if (g_profile.start) (void)hipEventRecord(g_profile.start, stream);
-        if (ep.dtype == 1) k_encode<1><<<dim3((uint32_t)grid), dim3(64), 0, stream>>>(ep);
-        else k_encode<2><<<dim3((uint32_t)grid), dim3(64), 0, stream>>>(ep);
+        if (ep.dtype == 1) k_encode<1><<<grid, dim3(64), 0, stream>>>(ep);
+        else k_encode<2><<<grid, dim3(64), 0, stream>>>(ep);
         if (g_profile.stop) (void)hipEventRecord(g_profile.stop, stream);
-        k_tile_reduce<<<dim3((uint32_t)ntiles), dim3(256), 0, stream>>>(ep.rec_sizes, ep.total_chunks, tile_sums);
-        k_scan_u64<<<1, 1024, 0, stream>>>(tile_sums, tile_offs, ntiles);
-        k_compact<<<dim3((uint32_t)ep.total_chunks), dim3(64), 0, stream>>>(cp);
+        const dim3 cgrid((uint32_t)((ep.total_pairs + kCompactPairs - 1) / kCompactPairs));
+        if (ep.dtype == 1) k_compact<1><<<cgrid, dim3(128 * kCompactPairs), 0, stream>>>(ep);
+        else k_compact<2><<<cgrid, dim3(128 * kCompactPairs), 0, stream>>>(ep);
     }
     return hipGetLastError();
 }

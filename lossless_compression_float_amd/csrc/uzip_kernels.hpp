@@ -16,22 +16,11 @@ struct EncParams {
     uint32_t chunk_elems;
     uint64_t total_chunks;  // chunks over all buffers
     uint64_t total_pairs;   // chunk pairs (two consecutive chunks of one buffer) over all buffers
-    uint8_t *slots;         // one slot of slot_stride bytes per chunk
+    uint8_t *slots;         // one slot of slot_stride bytes per chunk: record prefix, words filled from the end
     uint64_t slot_stride;
     uint32_t *rec_sizes;    // record bytes per chunk
-    int dtype;
-};
-
-struct CompactParams {
-    const EncDesc *descs;
-    EncDesc single;
-    uint32_t nbuf;
-    uint32_t chunk_elems;
-    uint64_t total_chunks;
-    const uint8_t *slots;
-    uint64_t slot_stride;
-    const uint32_t *rec_sizes;
-    const uint64_t *tile_offs;  // exclusive prefix of the tile sums
+    uint64_t *flags;        // one look-back word per chunk pair (zeroed before compaction)
+    uint32_t *ticket;       // chunk-pair ticket counter of the compaction (zeroed before it)
     int dtype;
 };
 
@@ -61,8 +50,7 @@ struct ProfileEvents {
 };
 extern thread_local ProfileEvents g_profile;
 
-hipError_t launch_compress(const EncParams &ep, const CompactParams &cp, uint64_t *tile_sums, uint64_t *tile_offs,
-                           uint64_t ntiles, bool any_empty, hipStream_t stream);
+hipError_t launch_compress(const EncParams &ep, hipStream_t stream);
 hipError_t launch_decompress(const DecParams &vp, const DecodeParams &dp, int dtype, uint64_t max_chunks,
                              hipStream_t stream);
 

@@ -197,3 +197,23 @@ def test_batched_fp32_and_corrupt_member():
     assert status.cpu().tolist() == [0, uz.UZIP_ERR_CORRUPT_INPUT, 0]
     assert torch.equal(vals[0].view(torch.int32), tensors[0].view(torch.int32))
     assert torch.equal(vals[2].view(torch.int32), tensors[2].view(torch.int32))
+
+
+@pytest.mark.parametrize("chunk_bytes", [64, 256])
+def test_batched_buffers_spanning_many_offset_tiles(chunk_bytes):
+    # small chunks give buffers of hundreds to thousands of records, so the
+    # record offsets of each buffer span many 64-pair tiles of the scan
+    sizes = [10_000, 0, 50_001, 8_192, 300_000, 65]
+    tensors = [workloads.gradient_bucket(n, seed=30 + i, special_frac=1e-3).to(DEV) if n else
+               torch.empty(0, dtype=torch.bfloat16, device=DEV) for i, n in enumerate(sizes)]
+    outs, out_sizes = uz.compress_batched(tensors, chunk_bytes=chunk_bytes)
+    torch.cuda.synchronize()
+    got = [o[:s] for o, s in zip(outs, out_sizes.cpu().tolist())]
+    for t, g in zip(tensors, got):
+        want = orc.compress(orc.BF16, workloads.bits_numpy(t), chunk_bytes)
+        assert np.array_equal(g.cpu().numpy(), want)
+    vals, status = uz.decompress_batched(got, torch.bfloat16, sizes)
+    torch.cuda.synchronize()
+    assert status.cpu().tolist() == [0] * len(sizes)
+    for t, v in zip(tensors, vals):
+        assert torch.equal(t.view(torch.int16), v.view(torch.int16))
