@@ -578,7 +578,9 @@ __global__ __launch_bounds__(64) void k_encode(EncParams p) {
     for (int k = 0; k < 8; ++k) {
         const double r = f[k] ? enc_reciprocal(f[k]) : 0.0;
         const uint64_t rb = (uint64_t)__double_as_longlong(r);
-        tab[lj * 8 + k] = make_uint4(f[k], cbase + cpre[k], (uint32_t)rb, (uint32_t)(rb >> 32));
+        // (f - 1) | (4096 - f) << 16: the emission threshold and the multiplier of the coding step
+        tab[lj * 8 + k] = make_uint4(((f[k] - 1) & 0xFFFFu) | ((kTableSize - f[k]) << 16), cbase + cpre[k], (uint32_t)rb,
+                                     (uint32_t)(rb >> 32));
     }
 
     // record prefix in the slot: presence bitmap, frequencies (ascending symbols), pad
@@ -607,7 +609,7 @@ __global__ __launch_bounds__(64) void k_encode(EncParams p) {
     const uint32_t wcap0 = raw0 > wofs0 ? (raw0 - wofs0) / 2 : 0u;
     const uint32_t wcap1 = nch == 2 && raw1 > wofs1 ? (raw1 - wofs1) / 2 : 0u;
     const uint32_t end0 = raw0 / 2, end1 = ((uint32_t)p.slot_stride + raw1) / 2;  // word index just past each slot's words
-    uint32_t nw0 = 0, nw1 = 0;
+    uint32_t r0 = end0, r1 = end1;  // word index just past the words still to come, per half
     bool alive0 = wcap0 > 0, alive1 = wcap1 > 0;  // a half stops coding once its words outgrow the RAW size
     uint32_t x = kStateLow;
     const uint32_t T0 = alive0 ? (vals0 + 31) / 32 : 0u, T1 = alive1 ? (vals1 + 31) / 32 : 0u;
@@ -633,14 +635,15 @@ __global__ __launch_bounds__(64) void k_encode(EncParams p) {
             if (careful)
                 act = (alive0 && vals0 > 32 * t ? half_prefix_mask(vals0 - 32 * t, 0) : 0ull) |
                       (alive1 && vals1 > 32 * t ? half_prefix_mask(vals1 - 32 * t, 1) : 0ull);
-            const uint4 te = tab[exponent_of<DT>(cur[k])];
-            const uint32_t fs = te.x;
-            uint64_t m = lanes_lt(fs - 1, x >> 20) & act;  // x >= f * 2^20
+            uint32_t ex;  // the value's exponent
+            asm("v_bfe_u32 %0, %1, %2, 8" : "=v"(ex) : "v"(cur[k]), "i"(DT == 1 ? 7 : 23));
+            const uint4 te = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint8_t *>(tab) + (ex << 4));
+            uint64_t m = lanes_lt(te.x & 0xFFFFu, x >> 20) & act;  // x >= f * 2^20
             uint32_t lo = (uint32_t)m, hi = (uint32_t)(m >> 32);
             uint32_t clo = __builtin_popcount(lo), chi = __builtin_popcount(hi);
             if (careful) {
-                if (alive0 && nw0 + clo > wcap0) alive0 = false;
-                if (alive1 && nw1 + chi > wcap1) alive1 = false;
+                if (alive0 && (end0 - r0) + clo > wcap0) alive0 = false;
+                if (alive1 && (end1 - r1) + chi > wcap1) alive1 = false;
                 const uint64_t am = (alive0 ? 0xFFFFFFFFull : 0ull) | (alive1 ? kHighHalf : 0ull);
                 m &= am;
                 act &= am;
@@ -650,21 +653,27 @@ __global__ __launch_bounds__(64) void k_encode(EncParams p) {
                 chi = __builtin_popcount(hi);
             }
             // word index: end of the slot's words - (words so far + this step's) + rank in the half
-            const uint32_t e0 = end0 - nw0 - clo, e1 = end1 - nw1 - chi - clo;
-            const uint32_t bias = e0 + ((e1 - e0) & hsel);
-            const uint32_t kk = __builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, bias));
+            // (r0, r1: word index just past the words still to come)
+            const uint32_t e0 = r0 - clo;
+            r1 -= chi;
+            const uint32_t e1 = r1 - clo;
+            r0 = e0;
+            uint32_t hb;  // e1 - e0 in the upper half, 0 in the lower
+            asm("v_and_b32 %0, %1, %2" : "=v"(hb) : "s"(e1 - e0), "v"(hsel));
+            const uint32_t kk = __builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, e0 + hb));
             bst16(rslot, vsel(m, kOutOfRange, kk << 1), x);
             const uint32_t xs = vsel(m, x, x >> 16);
-            nw0 += clo;
-            nw1 += chi;
             const uint32_t qd = enc_quotient(xs, __hiloint2double((int)te.w, (int)te.z));
-            const uint32_t xe = __umul24(qd, kTableSize - fs) + (xs + te.y);  // = q * M + (xs - q * f) + c0
-            x = vsel(act, x, xe);
+            const uint32_t xe = __umul24(qd, te.x >> 16) + (xs + te.y);  // = q * M + (xs - q * f) + c0
+            // Lanes past a ragged chunk end keep their state.  Outside CAREFUL
+            // steps every lane of a live half codes a value, and a stopped
+            // half's state is never used (its chunk is stored RAW).
+            x = careful ? vsel(act, x, xe) : xe;
         };
         // a block codes at most 256 values, so at most 256 words, per half
         const uint32_t tend = ((uint32_t)b + 1) * 256;
-        const bool fast = (!alive0 || (vals0 >= tend && nw0 + 256 <= wcap0)) &&
-                          (!alive1 || (vals1 >= tend && nw1 + 256 <= wcap1));
+        const bool fast = (!alive0 || (vals0 >= tend && (end0 - r0) + 256 <= wcap0)) &&
+                          (!alive1 || (vals1 >= tend && (end1 - r1) + 256 <= wcap1));
         if (fast) {
             const uint64_t act = (alive0 ? 0xFFFFFFFFull : 0ull) | (alive1 ? kHighHalf : 0ull);
 #pragma unroll
@@ -680,7 +689,7 @@ __global__ __launch_bounds__(64) void k_encode(EncParams p) {
     // ---- the record's fixed part into the slot (the words are already at its
     // end); a RAW record gets its header only: k_compact takes its exponents
     // from the input ----
-    const uint32_t nw = h ? nw1 : nw0;
+    const uint32_t nw = h ? end1 - r1 : end0 - r0;  // words emitted
     const bool alive = h ? alive1 : alive0;
     const uint32_t raw_i = h ? raw1 : raw0;
     const uint32_t rans_bytes = (uint32_t)align16(words_offset(nsym) + 2ull * nw);
@@ -891,7 +900,7 @@ __global__ void k_dec_validate(DecParams p) {
 
 // LDS of one decode workgroup (two chunks), 10 KiB:
 //   s_sym [2][4096] u8   slot -> rank of its symbol among the present symbols
-//   s_rk  [2][256]  u32  rank -> (f - 1) | c0 << 12 | symbol << 24
+//   s_rk  [2][256]  u32  rank -> (4096 - f) | symbol << 12 | c0 << 20
 // so one step costs two dependent LDS reads.  A workgroup decodes a pair of
 // consecutive chunks of one buffer (half-wave h decodes chunk 2p + h), so the
 // record, sign+mantissa and output regions of the pair each get one buffer
@@ -916,8 +925,11 @@ template <int DT>
 __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
     constexpr uint32_t EB = DT == 1 ? 2 : 4;
     constexpr uint32_t R = DT == 1 ? 1 : 3;
-    __shared__ __align__(16) uint8_t s_sym[2][kTableSize];
-    __shared__ __align__(16) uint32_t s_rk[2][256];
+    // one LDS array, so that the slot table sits at address 0 and a slot's
+    // address is a single and-or of the state
+    __shared__ __align__(16) uint32_t s_dec[2 * kTableSize / 4 + 2 * 256];
+    uint8_t(*s_sym)[kTableSize] = reinterpret_cast<uint8_t(*)[kTableSize]>(s_dec);
+    uint32_t(*s_rk)[256] = reinterpret_cast<uint32_t(*)[256]>(s_dec + 2 * kTableSize / 4);
 
     const uint32_t lane = threadIdx.x;
     const uint32_t h = lane >> 5, lj = lane & 31;
@@ -1001,14 +1013,14 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
             uint32_t k2 = pre;
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
-                if (fk[k]) s_rk[h][k2++] = (fk[k] - 1) | ((cbase + cpre[k]) << 12) | ((lj * 8 + k) << 24);
+                if (fk[k]) s_rk[h][k2++] = (kTableSize - fk[k]) | ((lj * 8 + k) << 12) | ((cbase + cpre[k]) << 20);
             }
         }
         __syncthreads();
         if (coded_ok) {
             for (uint32_t m = 0; m < nsym; ++m) {
                 const uint32_t em = s_rk[h][m];
-                const uint32_t fs = (em & 0xFFFu) + 1, c0s = (em >> 12) & 0xFFFu;
+                const uint32_t fs = kTableSize - (em & 0xFFFu), c0s = em >> 20;
                 for (uint32_t k = lj; k < fs; k += 32) s_sym[h][c0s + k] = (uint8_t)m;
             }
         }
@@ -1024,12 +1036,12 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
 
         // ---- rANS decode (V9: end state L on every lane, every word consumed) ----
         // Word window: words [base, base+64) in P (low 16 bits: word base + lj,
-        // high: base + 32 + lj); NW holds word base + 64 + lj, loaded one step
-        // before it can be needed.  The per-half stream position and window
-        // base are wave-uniform scalars (pos0/base0, pos1/base1); lanes see
-        // them through scalar lane masks.  Loads past the pair's records read
-        // zero, and words past n_words are never consumed by a valid stream (a
-        // stream that tries fails the end check pos == n_words).
+        // high: base + 32 + lj).  The per-half offset of the stream position
+        // past the window base is a wave-uniform scalar (off0, off1); lanes
+        // see it through scalar lane masks, and the window base lives in wrow.
+        // Loads past the pair's records read zero, and words past n_words are
+        // never consumed by a valid stream (a stream that tries fails the end
+        // check pos == n_words).
         const uint32_t pair_vals = vals0 + vals1;
         const rsrc_t rsm = make_rsrc(d.in + sm_off + c0 * ce * R, pair_vals * R);
         const rsrc_t rout = make_rsrc(d.out + c0 * ce * EB, pair_vals * EB);
@@ -1045,8 +1057,8 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
         // steps in which every lane of each running half holds a value
         const uint32_t F0 = run0 ? ni0 / 32 : 0xFFFFFFFFu, F1 = run1 ? ni1 / 32 : 0xFFFFFFFFu;
         const uint32_t Tmain = min(min(F0, F1), Tw) & ~7u;
-        // per half: pos = words consumed, off = pos - window base (< 32 between steps)
-        uint32_t pos0 = 0, pos1 = 0, off0 = 0, off1 = 0;
+        // per half: off = words consumed - window base (< 32 between steps)
+        uint32_t off0 = 0, off1 = 0;
         uint64_t shprev = 0;  // lanes whose half shifted its window in the previous step
         // Refill words: at every step, after the shift decision, load the two
         // 32-word blocks that start 64 and 96 words past the (new) window base;
@@ -1060,28 +1072,42 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
         RA[0] = RA[1] = bld16(rrec, wrow + 128);
         RB[0] = RB[1] = bld16(rrec, wrow + 192);
         const uint32_t lanebits = (h << 5) << 2;
+        const uint32_t hsel = h ? 0xFFFFFFFFu : 0u;
+        const uint32_t hsym = h << kProbBits, hrk = h << 8;  // this half's table rows
+        const uint32_t selbase = 0x05040100u;
+        const uint8_t *s_symf = &s_sym[0][0];
+        const uint32_t *s_rkf = &s_rk[0][0];
         constexpr int kSmAhead = 8;  // sign+mantissa bytes are loaded this many steps ahead
         uint32_t smq[kSmAhead];
 #pragma unroll
         for (int u = 0; u < kSmAhead; ++u) smq[u] = bload_sm<DT>(rsm, sm_lane + u * 32 * R);
 
-        // one step of both half-waves; act = lanes holding a value this step;
-        // par = step parity (selects the refill registers)
-        auto step = [&](uint32_t t, uint64_t act, uint32_t &smslot, int par) __attribute__((always_inline)) {
-            const uint32_t slot = x & (kTableSize - 1);
-            const uint32_t em = s_rk[h][s_sym[h][slot]];
-            const uint32_t xd = __umul24((em & 0xFFFu) + 1, x >> kProbBits) + slot - ((em >> 12) & 0xFFFu);
+        // One step of both half-waves.  act = lanes holding a value this step
+        // (TAIL steps only: in the main loop every lane of a running half
+        // holds one, and lanes of a half that is not running never reach the
+        // output or the checks); par = step parity (selects the refill
+        // registers).  With the table entry em = g | sym << 12 | c0 << 20,
+        // g = 4096 - f, the decode step f * (x >> 12) + (x & 4095) - c0 is
+        // x - (g * (x >> 12) + c0).
+        auto step = [&](uint32_t t, uint64_t act, bool tail, uint32_t &smslot, int par) __attribute__((always_inline)) {
+            uint32_t slot_addr;  // (x & 4095) | this half's row: the byte address in s_sym
+            asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(slot_addr) : "v"(x), "s"(kTableSize - 1), "v"(hsym));
+            const uint32_t em = s_rkf[s_symf[slot_addr] | hrk];
+            const uint32_t xd = x - (__umul24(em & 0xFFFu, x >> kProbBits) + (em >> 20));
             const uint64_t m = lanes_lt(xd, kStateLow) & act;
             const uint32_t lo = (uint32_t)m, hi = (uint32_t)(m >> 32);
             const uint32_t clo = __builtin_popcount(lo), chi = __builtin_popcount(hi);
             // word index relative to the window: (pos - base) + rank inside the half
-            const uint32_t bias = off0 + (((off1 - clo) - off0) & (h ? 0xFFFFFFFFu : 0u));
+            uint32_t hb;  // ((off1 - clo) - off0) in the upper half, 0 in the lower
+            asm("v_and_b32 %0, %1, %2" : "=v"(hb) : "s"((off1 - clo) - off0), "v"(hsel));
+            const uint32_t bias = off0 + hb;
             const uint32_t kk = __builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, bias));  // < 64
             const uint32_t wv = (uint32_t)__builtin_amdgcn_ds_bpermute((int)(((kk << 2) & 124u) | lanebits), (int)P);
-            const uint32_t w = (wv >> ((kk >> 1) & 16u)) & 0xFFFFu;  // high word when kk >= 32
-            x = vsel(act, x, vsel(m, xd, (xd << 16) | w));
-            pos0 += clo;
-            pos1 += chi;
+            // (xd << 16) | word: bytes 0-1 (kk < 32) or 2-3 of wv below bytes 0-1 of xd
+            uint32_t sel;  // 0x05040100, or 0x05040302 for kk >= 32
+            asm("v_mad_u32_u24 %0, %1, %2, %3" : "=v"(sel) : "v"(__builtin_amdgcn_ubfe(kk, 5, 1)), "s"(0x0202u), "v"(selbase));
+            const uint32_t xn = __builtin_amdgcn_perm(xd, wv, sel);
+            x = tail ? vsel(act, x, vsel(m, xd, xn)) : vsel(m, xd, xn);
             off0 += clo;
             off1 += chi;
             const bool sh0 = off0 >= 32, sh1 = off1 >= 32;
@@ -1089,20 +1115,29 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
             off1 -= sh1 ? 32u : 0u;
             const uint64_t shm = (sh0 ? 0xFFFFFFFFull : 0ull) | (sh1 ? kHighHalf : 0ull);
             const uint32_t up = vsel(shprev, RA[par], RB[par]);  // loaded two steps ago
-            P = vsel(shm, P, (P >> 16) | (up << 16));
+            P = vsel(shm, P, __builtin_amdgcn_alignbit(up, P, 16));
             wrow += vsel(shm, 0u, 64u);
             shprev = shm;
             RA[par] = bld16(rrec, wrow + 128);
             RB[par] = bld16(rrec, wrow + 192);
             const uint32_t smv = smslot;
             smslot = bload_sm<DT>(rsm, sm_lane + (t + kSmAhead) * 32 * R);
-            if (DT == 1) bst16(rout, out_lane + t * 32 * EB, merge_value<DT>(em >> 24, smv));
-            else bst32(rout, out_lane + t * 32 * EB, merge_value<DT>(em >> 24, smv));
+            if (DT == 1) {
+                // sign (bit 7 of sm) to bit 15, mantissa bits 0-6, exponent
+                // (em bits 12-19) to bits 7-14; the store keeps the low 16 bits
+                uint32_t v;
+                asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(v) : "s"(0x807Fu), "v"(__umul24(smv, 0x101u)), "v"(em >> 5));
+                bst16(rout, out_lane + t * 32 * EB, v);
+            } else {
+                // sign (bit 23 of sm) to bit 31, mantissa bits 0-22, exponent to bits 23-30
+                const uint32_t sp = smv | ((smv & 0x800000u) << 8), ex = em << 11;
+                bst32(rout, out_lane + t * 32 * EB, (sp & 0x807FFFFFu) | (ex & ~0x807FFFFFu));
+            }
         };
         uint32_t t = 0;
         for (; t < Tmain; t += kSmAhead) {
 #pragma unroll
-            for (int u = 0; u < kSmAhead; ++u) step(t + u, runm, smq[u], u & 1);
+            for (int u = 0; u < kSmAhead; ++u) step(t + u, runm, false, smq[u], u & 1);
         }
         for (; t < Tw; t += kSmAhead) {
 #pragma unroll
@@ -1110,10 +1145,10 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
                 const uint32_t tt = t + u;
                 const uint64_t act = (run0 && ni0 > 32 * tt ? half_prefix_mask(ni0 - 32 * tt, 0) : 0ull) |
                                      (run1 && ni1 > 32 * tt ? half_prefix_mask(ni1 - 32 * tt, 1) : 0ull);
-                step(tt, act, smq[u], u & 1);
+                step(tt, act, true, smq[u], u & 1);
             }
         }
-        const uint32_t pos = h ? pos1 : pos0;
+        const uint32_t pos = (wrow - woff) / 2 + (h ? off1 : off0);  // words consumed
         const bool endbad = half_mask(__ballot(rans_run && (x != kStateLow || pos != nw)), h) != 0;
         ok = ok && !endbad;
         // ---- chunks stored RAW: exponent bytes straight from the record ----
