@@ -449,13 +449,71 @@ __global__ __launch_bounds__(64) void k_encode(EncParams p) {
     uint8_t *slot = p.slots + g * p.slot_stride;
 
     uint32_t *hist = lds + h * (kSubHist * kSubRow) + (lj & (kSubHist - 1)) * kSubRow;
+    uint32_t first_it = 0;
     for (uint32_t k = lane; k < 2 * kSubHist * kSubRow; k += 64) lds[k] = 0;
     __syncthreads();
 
     // ---- pass 1: split, sign+mantissa bytes to the output, LDS histogram ----
+    // Main loop: iterations in which every lane of each coding half holds a
+    // full 128-bit vector, with four to eight loads in flight per lane.  A half without
+    // a chunk (the buffer's odd last chunk) reads zeros past the pair, counts
+    // them into the padding words of its histogram rows (a word per lane, so
+    // without conflicts) and stores nothing: its sign+mantissa offsets lie
+    // past the pair's output range.
+    {
+        // (a multiple of 4 iterations, so that no step of the loop is conditional)
+        const uint32_t fullmin = min(vals0 / VPI, nch == 2 ? vals1 / VPI : 0xFFFFFFFFu) & ~3u;
+        uint32_t *hm = valid ? hist : hist + 256 + (lj >> 2);
+        const rsrc_t rsmo = make_rsrc(d.out + d.sm_off + c0 * ce * R, pair_vals * R);
+        const uint32_t smo = (h ? vals0 : 0u) * R + lj * VPL * R;  // this lane's first sign+mantissa byte
+        auto vec = [&](uint32_t it) __attribute__((always_inline)) {
+            return bld128(rin, it < fullmin ? in0 + (it * VPI + lj * VPL) * EB : kOutOfRange);
+        };
+        auto split = [&](const uint4 &qv, uint32_t it) __attribute__((always_inline)) {
+            const uint32_t w[4] = {qv.x, qv.y, qv.z, qv.w};
+            const uint32_t o = smo + it * VPI * R;
+            if (DT == 1) {
+                uint32_t smw[2] = {0, 0};
+#pragma unroll
+                for (uint32_t k = 0; k < 8; ++k) {
+                    const uint32_t v = (w[k >> 1] >> (16 * (k & 1))) & 0xFFFFu;
+                    smw[k >> 2] |= (((v >> 8) & 0x80u) | (v & 0x7Fu)) << (8 * (k & 3));
+                    atomicAdd(&hm[(v >> 7) & 0xFFu], 1u);
+                }
+                bst32(rsmo, o, smw[0]);
+                bst32(rsmo, o + 4, smw[1]);
+            } else {
+                uint32_t sm[4];
+#pragma unroll
+                for (uint32_t k = 0; k < 4; ++k) {
+                    sm[k] = ((w[k] >> 8) & 0x800000u) | (w[k] & 0x7FFFFFu);
+                    atomicAdd(&hm[(w[k] >> 23) & 0xFFu], 1u);
+                }
+                bst32(rsmo, o, sm[0] | (sm[1] << 24));
+                bst32(rsmo, o + 4, (sm[1] >> 8) | (sm[2] << 16));
+                bst32(rsmo, o + 8, (sm[2] >> 16) | (sm[3] << 8));
+            }
+        };
+        // double buffer: the next four vectors are requested before the
+        // current four are split
+        uint4 qa = vec(0), qb = vec(1), qc = vec(2), qd = vec(3);
+        for (uint32_t it = 0; it < fullmin; it += 4) {
+            const uint4 na = vec(it + 4), nb = vec(it + 5), nc = vec(it + 6), nd = vec(it + 7);
+            split(qa, it);
+            split(qb, it + 1);
+            split(qc, it + 2);
+            split(qd, it + 3);
+            qa = na;
+            qb = nb;
+            qc = nc;
+            qd = nd;
+        }
+        first_it = fullmin;
+    }
+    // the rest: the longer half's remaining vectors and the ragged ends
     const uint32_t iters = (ni + VPI - 1) / VPI;
     const uint32_t iters_w = max(iters, (uint32_t)__shfl_xor(iters, 32, 64));
-    for (uint32_t it = 0; it < iters_w; ++it) {
+    for (uint32_t it = first_it; it < iters_w; ++it) {
         const uint32_t i0 = it * VPI + lj * VPL;
         if (i0 >= ni) continue;
         const bool full = i0 + VPL <= ni;
