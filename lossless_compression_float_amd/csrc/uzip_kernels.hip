@@ -1115,6 +1115,7 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
         // steps in which every lane of each running half holds a value
         const uint32_t F0 = run0 ? ni0 / 32 : 0xFFFFFFFFu, F1 = run1 ? ni1 / 32 : 0xFFFFFFFFu;
         const uint32_t Tmain = min(min(F0, F1), Tw) & ~7u;
+        const uint32_t Tmain16 = Tmain & ~15u;  // bf16 main loop: 16 steps per iteration
         // per half: off = words consumed - window base (< 32 between steps)
         uint32_t off0 = 0, off1 = 0;
         uint64_t shprev = 0;  // lanes whose half shifted its window in the previous step
@@ -1124,6 +1125,11 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
         // which is the first of them if the step in between did not shift and
         // the second if it did.  So every refill load is consumed two steps
         // after it is issued, off the dependency chain.
+        // bf16: this lane's sign+mantissa dword of group 0 (see the main loop),
+        // loaded before the word window so that many memory operations lie
+        // between these loads and their first use
+        const uint32_t smd0 = (h ? vals0 : 0u) + 4 * lj;
+        const uint32_t D0first = DT == 1 ? bld32(rsm, smd0) : 0u, D1first = DT == 1 ? bld32(rsm, smd0 + 128) : 0u;
         uint32_t wrow = woff;  // byte offset of word (window base + lj)
         uint32_t P = bld16(rrec, wrow) | (bld16(rrec, wrow + 64) << 16);
         uint32_t RA[2], RB[2];
@@ -1132,14 +1138,10 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
         const uint32_t lanebits = (h << 5) << 2;
         const uint32_t hsel = h ? 0xFFFFFFFFu : 0u;
         const uint32_t hsym = h << kProbBits, hrk = h << 8;  // this half's table rows
-        const uint32_t selbase = 0x05040100u;
+        const uint32_t selbase = 0x05040100u, selkeep = 0x07060504u;
+        uint32_t offv = 0;  // this half's offset (off0 or off1) as a lane register
         const uint8_t *s_symf = &s_sym[0][0];
         const uint32_t *s_rkf = &s_rk[0][0];
-        constexpr int kSmAhead = 8;  // sign+mantissa bytes are loaded this many steps ahead
-        uint32_t smq[kSmAhead];
-#pragma unroll
-        for (int u = 0; u < kSmAhead; ++u) smq[u] = bload_sm<DT>(rsm, sm_lane + u * 32 * R);
-
         // One step of both half-waves.  act = lanes holding a value this step
         // (TAIL steps only: in the main loop every lane of a running half
         // holds one, and lanes of a half that is not running never reach the
@@ -1147,7 +1149,8 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
         // registers).  With the table entry em = g | sym << 12 | c0 << 20,
         // g = 4096 - f, the decode step f * (x >> 12) + (x & 4095) - c0 is
         // x - (g * (x >> 12) + c0).
-        auto step = [&](uint32_t t, uint64_t act, bool tail, uint32_t &smslot, int par) __attribute__((always_inline)) {
+        // sp: the value's sign+mantissa, for bf16 as the byte in bytes 0 and 1
+        auto step = [&](uint32_t t, uint64_t act, bool tail, uint32_t sp, int par) __attribute__((always_inline)) {
             uint32_t slot_addr;  // (x & 4095) | this half's row: the byte address in s_sym
             asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(slot_addr) : "v"(x), "s"(kTableSize - 1), "v"(hsym));
             const uint32_t em = s_rkf[s_symf[slot_addr] | hrk];
@@ -1155,22 +1158,25 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
             const uint64_t m = lanes_lt(xd, kStateLow) & act;
             const uint32_t lo = (uint32_t)m, hi = (uint32_t)(m >> 32);
             const uint32_t clo = __builtin_popcount(lo), chi = __builtin_popcount(hi);
-            // word index relative to the window: (pos - base) + rank inside the half
-            uint32_t hb;  // ((off1 - clo) - off0) in the upper half, 0 in the lower
-            asm("v_and_b32 %0, %1, %2" : "=v"(hb) : "s"((off1 - clo) - off0), "v"(hsel));
-            const uint32_t bias = off0 + hb;
-            const uint32_t kk = __builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, bias));  // < 64
+            // word index relative to the window: (pos - base) + rank inside the
+            // half, from the offset register and one mbcnt per half (no scalar
+            // arithmetic between the compare and the word fetch)
+            const uint32_t kk = vsel(kHighHalf, __builtin_amdgcn_mbcnt_lo(lo, offv), __builtin_amdgcn_mbcnt_hi(hi, offv));
             const uint32_t wv = (uint32_t)__builtin_amdgcn_ds_bpermute((int)(((kk << 2) & 124u) | lanebits), (int)P);
-            // (xd << 16) | word: bytes 0-1 (kk < 32) or 2-3 of wv below bytes 0-1 of xd
-            uint32_t sel;  // 0x05040100, or 0x05040302 for kk >= 32
-            asm("v_mad_u32_u24 %0, %1, %2, %3" : "=v"(sel) : "v"(__builtin_amdgcn_ubfe(kk, 5, 1)), "s"(0x0202u), "v"(selbase));
-            const uint32_t xn = __builtin_amdgcn_perm(xd, wv, sel);
-            x = tail ? vsel(act, x, vsel(m, xd, xn)) : vsel(m, xd, xn);
+            // x' = (xd << 16) | word: bytes 0-1 (kk < 32) or 2-3 of wv below bytes
+            // 0-1 of xd; lanes without a word keep xd (bytes 4-7)
+            uint32_t selw;
+            asm("v_mad_u32_u24 %0, %1, %2, %3" : "=v"(selw) : "v"(__builtin_amdgcn_ubfe(kk, 5, 1)), "s"(0x0202u), "v"(selbase));
+            const uint32_t xn = __builtin_amdgcn_perm(xd, wv, vsel(m, selkeep, selw));
+            x = tail ? vsel(act, x, xn) : xn;
             off0 += clo;
             off1 += chi;
             const bool sh0 = off0 >= 32, sh1 = off1 >= 32;
             off0 -= sh0 ? 32u : 0u;
             off1 -= sh1 ? 32u : 0u;
+            uint32_t ho;  // off1 - off0 in the upper half, 0 in the lower
+            asm("v_and_b32 %0, %1, %2" : "=v"(ho) : "s"(off1 - off0), "v"(hsel));
+            offv = off0 + ho;
             const uint64_t shm = (sh0 ? 0xFFFFFFFFull : 0ull) | (sh1 ? kHighHalf : 0ull);
             const uint32_t up = vsel(shprev, RA[par], RB[par]);  // loaded two steps ago
             P = vsel(shm, P, __builtin_amdgcn_alignbit(up, P, 16));
@@ -1178,32 +1184,70 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
             shprev = shm;
             RA[par] = bld16(rrec, wrow + 128);
             RB[par] = bld16(rrec, wrow + 192);
-            const uint32_t smv = smslot;
-            smslot = bload_sm<DT>(rsm, sm_lane + (t + kSmAhead) * 32 * R);
             if (DT == 1) {
-                // sign (bit 7 of sm) to bit 15, mantissa bits 0-6, exponent
-                // (em bits 12-19) to bits 7-14; the store keeps the low 16 bits
+                // sign (bit 7 of sm, copied to bit 15) and mantissa bits 0-6
+                // from sp, exponent (em bits 12-19) to bits 7-14; the store
+                // keeps the low 16 bits
                 uint32_t v;
-                asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(v) : "s"(0x807Fu), "v"(__umul24(smv, 0x101u)), "v"(em >> 5));
+                asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(v) : "s"(0x807Fu), "v"(sp), "v"(em >> 5));
                 bst16(rout, out_lane + t * 32 * EB, v);
             } else {
                 // sign (bit 23 of sm) to bit 31, mantissa bits 0-22, exponent to bits 23-30
-                const uint32_t sp = smv | ((smv & 0x800000u) << 8), ex = em << 11;
-                bst32(rout, out_lane + t * 32 * EB, (sp & 0x807FFFFFu) | (ex & ~0x807FFFFFu));
+                const uint32_t sx = sp | ((sp & 0x800000u) << 8), ex = em << 11;
+                bst32(rout, out_lane + t * 32 * EB, (sx & 0x807FFFFFu) | (ex & ~0x807FFFFFu));
             }
         };
         uint32_t t = 0;
-        for (; t < Tmain; t += kSmAhead) {
+        if (DT == 1) {
+            // bf16 sign+mantissa bytes: one dword per lane per group of 4
+            // steps (the 128 bytes of the group), two groups ahead; step s of
+            // a group takes byte lj & 3 of lane 8s + lj / 4 of its half with
+            // one bpermute, and one perm copies it into bytes 0 and 1.  Every
+            // byte of a main-loop group lies inside both chunks.
+            const uint32_t smsrc = ((lj >> 2) + 32 * h) << 2;       // bpermute address of step 0 of a group
+            const uint32_t smsel = 0x0C0C0000u | ((lj & 3) * 0x0101u);
+            // two register sets alternate (16 steps per loop iteration), so no
+            // loaded register is copied
+            auto group8 = [&](uint32_t t0, uint32_t Da, uint32_t Db) __attribute__((always_inline)) {
 #pragma unroll
-            for (int u = 0; u < kSmAhead; ++u) step(t + u, runm, false, smq[u], u & 1);
+                for (int u = 0; u < 8; ++u) {
+                    const uint32_t w = (uint32_t)__builtin_amdgcn_ds_bpermute((int)(smsrc + 32 * (u & 3)), (int)(u < 4 ? Da : Db));
+                    step(t0 + u, runm, false, __builtin_amdgcn_perm(0u, w, smsel), u & 1);
+                }
+            };
+            uint32_t D0 = D0first, D1 = D1first;
+            for (; t < Tmain16; t += 16) {
+                const uint32_t N0 = bld32(rsm, smd0 + (t + 8) * 32), N1 = bld32(rsm, smd0 + (t + 12) * 32);
+                group8(t, D0, D1);
+                D0 = bld32(rsm, smd0 + (t + 16) * 32);
+                D1 = bld32(rsm, smd0 + (t + 20) * 32);
+                group8(t + 8, N0, N1);
+            }
+        } else {
+            constexpr int kSmAhead = 8;  // sign+mantissa bytes are loaded this many steps ahead
+            uint32_t smq[kSmAhead];
+#pragma unroll
+            for (int u = 0; u < kSmAhead; ++u) smq[u] = bload_sm<DT>(rsm, sm_lane + u * 32 * R);
+            for (; t < Tmain; t += kSmAhead) {
+#pragma unroll
+                for (int u = 0; u < kSmAhead; ++u) {
+                    const uint32_t sp = smq[u];
+                    smq[u] = bload_sm<DT>(rsm, sm_lane + (t + u + kSmAhead) * 32 * R);
+                    step(t + u, runm, false, sp, u & 1);
+                }
+            }
         }
-        for (; t < Tw; t += kSmAhead) {
+        // tail: the last steps of the shorter chunk and the ragged end, value by value
+        for (; t < Tw; t += 8) {
+            uint32_t smt[8];
 #pragma unroll
-            for (int u = 0; u < kSmAhead; ++u) {
+            for (int u = 0; u < 8; ++u) smt[u] = bload_sm<DT>(rsm, sm_lane + (t + u) * 32 * R);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
                 const uint32_t tt = t + u;
                 const uint64_t act = (run0 && ni0 > 32 * tt ? half_prefix_mask(ni0 - 32 * tt, 0) : 0ull) |
                                      (run1 && ni1 > 32 * tt ? half_prefix_mask(ni1 - 32 * tt, 1) : 0ull);
-                step(tt, act, true, smq[u], u & 1);
+                step(tt, act, true, DT == 1 ? __umul24(smt[u], 0x101u) : smt[u], u & 1);
             }
         }
         const uint32_t pos = (wrow - woff) / 2 + (h ? off1 : off0);  // words consumed
