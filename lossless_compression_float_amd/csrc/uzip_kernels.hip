@@ -1093,17 +1093,20 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
         const bool raw_run = ok && mode == 1;
 
         // ---- rANS decode (V9: end state L on every lane, every word consumed) ----
-        // Word window: words [base, base+64) in P (low 16 bits: word base + lj,
-        // high: base + 32 + lj).  The per-half offset of the stream position
-        // past the window base is a wave-uniform scalar (off0, off1); lanes
-        // see it through scalar lane masks, and the window base lives in wrow.
-        // Loads past the pair's records read zero, and words past n_words are
-        // never consumed by a valid stream (a stream that tries fails the end
-        // check pos == n_words).
+        // Word window of a half: words [base, base + 64), two blocks of 32
+        // words, each held by 16 lanes of the half as adjacent word pairs (lane
+        // i of a group: words 2i and 2i + 1 of its block, one dword in P).  The
+        // group holding the front block [base, base + 32) is given by a parity
+        // bit (par0, par1).  Word kk of the window (kk < 64) lives in lane
+        // ((kk >> 1) + 16 * parity) mod 32 of the half, half-word kk & 1.  The
+        // offset of the stream position past the base is a wave-uniform scalar
+        // (off0, off1), also held per lane in offv.  Loads past the pair's
+        // records read zero, and words past n_words are never consumed by a
+        // valid stream (a stream that tries fails the end check pos ==
+        // n_words).
         const uint32_t pair_vals = vals0 + vals1;
         const rsrc_t rsm = make_rsrc(d.in + sm_off + c0 * ce * R, pair_vals * R);
         const rsrc_t rout = make_rsrc(d.out + c0 * ce * EB, pair_vals * EB);
-        const uint32_t woff = rel + (uint32_t)words_offset(nsym) + 2 * lj;  // byte offset of word lj
         const uint32_t sm_lane = (h ? vals0 : 0u) * R + lj * R;
         const uint32_t out_lane = rans_run ? (h ? vals0 : 0u) * EB + lj * EB : kOutOfRange;
         // wave-uniform view of the two halves
@@ -1118,28 +1121,32 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
         const uint32_t Tmain16 = Tmain & ~15u;  // bf16 main loop: 16 steps per iteration
         // per half: off = words consumed - window base (< 32 between steps)
         uint32_t off0 = 0, off1 = 0;
-        uint64_t shprev = 0;  // lanes whose half shifted its window in the previous step
-        // Refill words: at every step, after the shift decision, load the two
-        // 32-word blocks that start 64 and 96 words past the (new) window base;
-        // two steps later a shift needs the block 64 words past the then base,
-        // which is the first of them if the step in between did not shift and
-        // the second if it did.  So every refill load is consumed two steps
-        // after it is issued, off the dependency chain.
+        uint32_t par0 = 0, par1 = 0;  // the group (0: lanes 0-15 of the half, 1: 16-31) holding the front block
         // bf16: this lane's sign+mantissa dword of group 0 (see the main loop),
         // loaded before the word window so that many memory operations lie
         // between these loads and their first use
         const uint32_t smd0 = (h ? vals0 : 0u) + 4 * lj;
         const uint32_t D0first = DT == 1 ? bld32(rsm, smd0) : 0u, D1first = DT == 1 ? bld32(rsm, smd0 + 128) : 0u;
-        uint32_t wrow = woff;  // byte offset of word (window base + lj)
-        uint32_t P = bld16(rrec, wrow) | (bld16(rrec, wrow + 64) << 16);
-        uint32_t RA[2], RB[2];
-        RA[0] = RA[1] = bld16(rrec, wrow + 128);
-        RB[0] = RB[1] = bld16(rrec, wrow + 192);
+        // Refill: at every step, after the shift decision, each lane loads the
+        // word pair it would take at the next shift if no shift came in between:
+        // front-group lanes from the block 64 words past the base, back-group
+        // lanes from the block 96 words past it (ra, a byte offset).  Two steps
+        // later the front group is either the same (no shift in between: it
+        // needs the block 64 past the then base, loaded) or the former back
+        // group (one shift: the then base is 32 further, so it needs the block
+        // 96 past the old one, loaded).  Every refill load is consumed two
+        // steps after it is issued (NX[par]), off the dependency chain.
+        const uint32_t wstart = rel + (uint32_t)words_offset(nsym);  // byte offset of word 0
+        uint32_t P = bld32(rrec, wstart + 4 * lj);                    // words 2lj, 2lj + 1
+        uint32_t ra = wstart + 128 + 4 * lj;                          // words 64 + 2lj, 65 + 2lj
+        uint32_t NX[2];
+        NX[0] = NX[1] = bld32(rrec, ra);
         const uint32_t lanebits = (h << 5) << 2;
         const uint32_t hsel = h ? 0xFFFFFFFFu : 0u;
         const uint32_t hsym = h << kProbBits, hrk = h << 8;  // this half's table rows
         const uint32_t selbase = 0x05040100u, selkeep = 0x07060504u;
         uint32_t offv = 0;  // this half's offset (off0 or off1) as a lane register
+        uint32_t parv = 0;  // 64 * this half's parity (the bpermute address term)
         const uint8_t *s_symf = &s_sym[0][0];
         const uint32_t *s_rkf = &s_rk[0][0];
         // One step of both half-waves.  act = lanes holding a value this step
@@ -1162,28 +1169,37 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
             // half, from the offset register and one mbcnt per half (no scalar
             // arithmetic between the compare and the word fetch)
             const uint32_t kk = vsel(kHighHalf, __builtin_amdgcn_mbcnt_lo(lo, offv), __builtin_amdgcn_mbcnt_hi(hi, offv));
-            const uint32_t wv = (uint32_t)__builtin_amdgcn_ds_bpermute((int)(((kk << 2) & 124u) | lanebits), (int)P);
-            // x' = (xd << 16) | word: bytes 0-1 (kk < 32) or 2-3 of wv below bytes
+            uint32_t wa;  // lane ((kk >> 1) + 16 * parity) mod 32 of this half
+            asm("v_lshl_add_u32 %0, %1, 1, %2" : "=v"(wa) : "v"(kk), "v"(parv));
+            const uint32_t wv = (uint32_t)__builtin_amdgcn_ds_bpermute((int)((wa & 124u) | lanebits), (int)P);
+            // x' = (xd << 16) | word: bytes 0-1 (kk even) or 2-3 of wv below bytes
             // 0-1 of xd; lanes without a word keep xd (bytes 4-7)
             uint32_t selw;
-            asm("v_mad_u32_u24 %0, %1, %2, %3" : "=v"(selw) : "v"(__builtin_amdgcn_ubfe(kk, 5, 1)), "s"(0x0202u), "v"(selbase));
+            asm("v_mad_u32_u24 %0, %1, %2, %3" : "=v"(selw) : "v"(kk & 1u), "s"(0x0202u), "v"(selbase));
             const uint32_t xn = __builtin_amdgcn_perm(xd, wv, vsel(m, selkeep, selw));
             x = tail ? vsel(act, x, xn) : xn;
+            // window shifts (integer arithmetic only, so that it stays scalar):
+            // s = 1 when the half's offset reaches the back block
             off0 += clo;
             off1 += chi;
-            const bool sh0 = off0 >= 32, sh1 = off1 >= 32;
-            off0 -= sh0 ? 32u : 0u;
-            off1 -= sh1 ? 32u : 0u;
+            const uint32_t s0 = off0 >> 5, s1 = off1 >> 5;
+            off0 &= 31u;
+            off1 &= 31u;
             uint32_t ho;  // off1 - off0 in the upper half, 0 in the lower
             asm("v_and_b32 %0, %1, %2" : "=v"(ho) : "s"(off1 - off0), "v"(hsel));
             offv = off0 + ho;
-            const uint64_t shm = (sh0 ? 0xFFFFFFFFull : 0ull) | (sh1 ? kHighHalf : 0ull);
-            const uint32_t up = vsel(shprev, RA[par], RB[par]);  // loaded two steps ago
-            P = vsel(shm, P, __builtin_amdgcn_alignbit(up, P, 16));
-            wrow += vsel(shm, 0u, 64u);
-            shprev = shm;
-            RA[par] = bld16(rrec, wrow + 128);
-            RB[par] = bld16(rrec, wrow + 192);
+            // a shifting half: its front group takes the pairs loaded two steps
+            // ago, then the groups swap roles
+            const uint32_t m0 = (0xFFFFu << (16 * par0)) & (0u - s0), m1 = (0xFFFFu << (16 * par1)) & (0u - s1);
+            const uint64_t rm = (uint64_t(m1) << 32) | m0;
+            P = vsel(rm, P, NX[par]);
+            ra += vsel(rm, 0u, 128u);
+            par0 ^= s0;
+            par1 ^= s1;
+            uint32_t hp;  // 64 * (par1 - par0) in the upper half, 0 in the lower
+            asm("v_and_b32 %0, %1, %2" : "=v"(hp) : "s"(64 * (par1 - par0)), "v"(hsel));
+            parv = 64 * par0 + hp;
+            NX[par] = bld32(rrec, ra);
             if (DT == 1) {
                 // sign (bit 7 of sm, copied to bit 15) and mantissa bits 0-6
                 // from sp, exponent (em bits 12-19) to bits 7-14; the store
@@ -1250,7 +1266,10 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
                 step(tt, act, true, DT == 1 ? __umul24(smt[u], 0x101u) : smt[u], u & 1);
             }
         }
-        const uint32_t pos = (wrow - woff) / 2 + (h ? off1 : off0);  // words consumed
+        // words consumed: the window base is 32 words per shift, and every
+        // shift refilled one group (its lanes' ra advanced by 128 bytes)
+        const uint32_t refills = (ra - (wstart + 128 + 4 * lj)) / 128;
+        const uint32_t pos = 32 * (refills + (uint32_t)__shfl_xor((int)refills, 16, 64)) + (h ? off1 : off0);
         const bool endbad = half_mask(__ballot(rans_run && (x != kStateLow || pos != nw)), h) != 0;
         ok = ok && !endbad;
         // ---- chunks stored RAW: exponent bytes straight from the record ----
