@@ -33,10 +33,22 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
-# traffic measured with rocprofv3 FETCH_SIZE / WRITE_SIZE for the dominant
-# kernel of the default workload (filled in from the committed profiles; None
-# until counters for the current kernel exist)
-MEASURED_TRAFFIC = {}
+# HBM bytes per launch from two rocprofv3 passes (FETCH_SIZE, then WRITE_SIZE)
+# on the gradient bucket, reads scaled by 2.000 and writes by 1.000 (what the
+# same counters read for the benchmark's plain 512 MiB device copy); the
+# kernel source they were taken on is identified by its digest, and the
+# figure is reported only while the source is unchanged.
+MEASURED_TRAFFIC_SOURCE = "e1cadc2684bf"
+MEASURED_TRAFFIC = {("grad_bucket", "k_encode"): 1435545600, ("grad_bucket", "k_decode"): 897427456}
+
+
+def kernel_source_digest() -> str:
+    import hashlib
+    path = os.path.join(ROOT, "lossless_compression_float_amd", "csrc", "uzip_kernels.hip")
+    try:
+        return hashlib.sha256(open(path, "rb").read()).hexdigest()[:12]
+    except OSError:
+        return ""
 
 
 def parse():
@@ -244,9 +256,11 @@ def main():
     else:
         kname, kbytes, kms = "k_decode", dec_bytes, dec_kernel_ms
     achieved = kbytes / (kms * 1e-3) / 1e9
+    traffic = MEASURED_TRAFFIC.get((args.workload, kname)) if kernel_source_digest() == MEASURED_TRAFFIC_SOURCE else None
     roofline = {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                "traffic": MEASURED_TRAFFIC.get((args.workload, kname)),
+                "traffic": traffic,
+                "traffic_over_algorithmic": round(traffic / kbytes, 4) if traffic else None,
                 "algorithmic_bytes": kbytes, "avg_ms": round(kms, 4),
                 "k_encode_ms": round(enc_kernel_ms, 4), "k_decode_ms": round(dec_kernel_ms, 4),
                 "k_encode_frac": round(enc_bytes / (enc_kernel_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
