@@ -1,0 +1,118 @@
+"""GPU parity at the benchmark's full sizes, in the launch configuration the
+benchmark times (one call per workload, default chunk sizes, batched calls
+for the buffer sets).
+
+Tolerance 0: compressed bytes equal the oracle's, byte for byte, wherever the
+oracle is run (whole buffers up to a few GB; a stated sample of the 16 GB
+weight set), and the properties that hold at any size are checked on every
+buffer: header fields, index monotone and consistent with the record headers,
+total size, and a bit-exact round trip on the GPU.
+"""
+import numpy as np
+import pytest
+import torch
+
+import lossless_compression_float_amd as uz
+import oracle as orc
+import workloads
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _host(buf: torch.Tensor, size: int) -> np.ndarray:
+    return buf[:size].cpu().numpy()
+
+
+def _check_frame(b: np.ndarray, code: int, n: int, chunk_elems: int):
+    """Header, index and record headers of one compressed buffer (any size)."""
+    C = (n + chunk_elems - 1) // chunk_elems
+    r = 1 if code == orc.BF16 else 3
+    hdr = np.frombuffer(b[:64].tobytes(), dtype=np.uint64)
+    assert int.from_bytes(b[0:4].tobytes(), "little") == 0x31505A55
+    assert int(b[6]) == code and int(b[7]) == 12 and int(b[8]) == 32 and int(b[9]) == r
+    assert int.from_bytes(b[12:16].tobytes(), "little") == chunk_elems
+    assert int(hdr[2]) == n and int(hdr[3]) == C
+    sm_off, exp_off, total = int(hdr[4]), int(hdr[5]), int(hdr[6])
+    assert sm_off == (64 + 8 * (C + 1) + 15) // 16 * 16
+    assert exp_off == (sm_off + r * n + 15) // 16 * 16
+    assert total == b.size
+    idx = np.frombuffer(b[64:64 + 8 * (C + 1)].tobytes(), dtype=np.uint64).astype(np.int64)
+    assert idx[0] == 0 and idx[-1] == total - exp_off
+    sizes = np.diff(idx)
+    assert np.all(sizes > 0) and np.all(sizes % 16 == 0)
+    # every record header states its own size, its chunk's value count and a valid mode
+    heads = np.stack([b[exp_off + idx[:-1] + k] for k in range(16)], axis=1).astype(np.uint32)
+    rec_bytes = heads[:, 12] | (heads[:, 13] << 8) | (heads[:, 14] << 16) | (heads[:, 15] << 24)
+    n_values = heads[:, 8] | (heads[:, 9] << 8) | (heads[:, 10] << 16) | (heads[:, 11] << 24)
+    want_vals = np.full(C, chunk_elems, dtype=np.int64)
+    want_vals[-1] = n - (C - 1) * chunk_elems
+    assert np.array_equal(rec_bytes.astype(np.int64), sizes)
+    assert np.array_equal(n_values.astype(np.int64), want_vals)
+    assert np.all(heads[:, 0] <= 1)
+
+
+def _same_bits(a: torch.Tensor, b: torch.Tensor) -> bool:
+    v = torch.int16 if a.dtype == torch.bfloat16 else torch.int32
+    return torch.equal(a.view(v), b.view(v))
+
+
+def test_gradient_bucket_512mib_equals_oracle():
+    t = workloads.gradient_bucket(workloads.GRAD_BUCKET_N, device=DEV, seed=1)
+    buf, size = uz.compress(t)
+    torch.cuda.synchronize()
+    got = _host(buf, int(size.item()))
+    _check_frame(got, orc.BF16, t.numel(), 32768)
+    assert np.array_equal(got, orc.compress(orc.BF16, workloads.bits_numpy(t)))
+    back, st = uz.decompress(buf, torch.bfloat16, t.numel(), in_bytes=got.size)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0 and _same_bits(back, t)
+
+
+def test_fp32_gradients_100m_equals_oracle():
+    t = workloads.fp32_gradients(workloads.FP32_GRAD_N, device=DEV, seed=3)
+    buf, size = uz.compress(t)
+    torch.cuda.synchronize()
+    got = _host(buf, int(size.item()))
+    _check_frame(got, orc.FP32, t.numel(), 65536)
+    assert np.array_equal(got, orc.compress(orc.FP32, workloads.bits_numpy(t)))
+    back, st = uz.decompress(buf, torch.float32, t.numel(), in_bytes=got.size)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0 and _same_bits(back, t)
+
+
+def test_small_message_batch_4096_buffers_equal_oracle():
+    ts = workloads.small_message_batch(device=DEV, seed=4)
+    outs, sizes = uz.compress_batched(ts)
+    torch.cuda.synchronize()
+    sizes = sizes.cpu().tolist()
+    for t, o, s in zip(ts, outs, sizes):
+        got = _host(o, s)
+        _check_frame(got, orc.BF16, t.numel(), 32768)
+        assert np.array_equal(got, orc.compress(orc.BF16, workloads.bits_numpy(t)))
+    backs, st = uz.decompress_batched([o[:s] for o, s in zip(outs, sizes)], torch.bfloat16, [t.numel() for t in ts])
+    torch.cuda.synchronize()
+    assert st.cpu().tolist() == [0] * len(ts)
+    assert all(_same_bits(a, b) for a, b in zip(ts, backs))
+
+
+def test_llama3_8b_weight_set_16gb_one_batched_call():
+    ts = [t.reshape(-1) for t in workloads.llama3_8b_weights(device=DEV, seed=2)]
+    assert len(ts) == 290
+    outs, sizes = uz.compress_batched(ts)
+    torch.cuda.synchronize()
+    sizes = sizes.cpu().tolist()
+    # the oracle on a sample: embedding, every tensor of the first and the last
+    # layer, lm_head, and every RMSNorm vector (single-symbol chunks)
+    sample = {0, len(ts) - 1} | set(range(1, 10)) | set(range(len(ts) - 10, len(ts) - 1))
+    sample |= {1 + 9 * L for L in range(32)} | {6 + 9 * L for L in range(32)}
+    for i, (t, o, s) in enumerate(zip(ts, outs, sizes)):
+        got = _host(o, s)
+        _check_frame(got, orc.BF16, t.numel(), 32768)
+        if i in sample:
+            assert np.array_equal(got, orc.compress(orc.BF16, workloads.bits_numpy(t))), "buffer %d" % i
+        del got
+    backs, st = uz.decompress_batched([o[:s] for o, s in zip(outs, sizes)], torch.bfloat16, [t.numel() for t in ts])
+    torch.cuda.synchronize()
+    assert st.cpu().tolist() == [0] * len(ts)
+    assert all(_same_bits(a, b) for a, b in zip(ts, backs))

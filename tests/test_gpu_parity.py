@@ -2,10 +2,9 @@
 
 Tolerance 0 everywhere: the compressed bytes must equal the oracle's byte for
 byte, and decompression must restore every bit pattern (NaN payloads,
-infinities, denormals, signed zeros included).  Small cases compare whole
-buffers; the full-size workloads compare sampled chunks record by record
-(a record depends only on its chunk's values) plus properties that hold at
-any size (bit-exact round trip, sizes, ratio against the entropy bound).
+infinities, denormals, signed zeros included).  These cases are small enough
+to compare whole buffers; the benchmark's full-size workloads are in
+test_gpu_full_size.py.
 """
 import numpy as np
 import pytest
