@@ -1096,11 +1096,12 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
         // Word window of a half: words [base, base + 64), two blocks of 32
         // words, each held by 16 lanes of the half as adjacent word pairs (lane
         // i of a group: words 2i and 2i + 1 of its block, one dword in P).  The
-        // group holding the front block [base, base + 32) is given by a parity
-        // bit (par0, par1).  Word kk of the window (kk < 64) lives in lane
-        // ((kk >> 1) + 16 * parity) mod 32 of the half, half-word kk & 1.  The
-        // offset of the stream position past the base is a wave-uniform scalar
-        // (off0, off1), also held per lane in offv.  Loads past the pair's
+        // state of a half is one scalar, o = (words consumed) mod 64 (o0, o1;
+        // per lane in offv): the group holding the front block [base, base +
+        // 32) is o >> 5, the position past the base is o & 31, and word o + k
+        // of the stream (k < 32) lives in lane ((o + k) >> 1) mod 32 of the
+        // half, half-word (o + k) & 1.  A half shifts when o crosses a
+        // multiple of 32.  Loads past the pair's
         // records read zero, and words past n_words are never consumed by a
         // valid stream (a stream that tries fails the end check pos ==
         // n_words).
@@ -1120,8 +1121,7 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
         const uint32_t Tmain = min(min(F0, F1), Tw) & ~7u;
         const uint32_t Tmain16 = Tmain & ~15u;  // bf16 main loop: 16 steps per iteration
         // per half: off = words consumed - window base (< 32 between steps)
-        uint32_t off0 = 0, off1 = 0;
-        uint32_t par0 = 0, par1 = 0;  // the group (0: lanes 0-15 of the half, 1: 16-31) holding the front block
+        uint32_t o0 = 0, o1 = 0;  // words consumed mod 64, per half
         // bf16: this lane's sign+mantissa dword of group 0 (see the main loop),
         // loaded before the word window so that many memory operations lie
         // between these loads and their first use
@@ -1145,8 +1145,7 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
         const uint32_t hsel = h ? 0xFFFFFFFFu : 0u;
         const uint32_t hsym = h << kProbBits, hrk = h << 8;  // this half's table rows
         const uint32_t selbase = 0x05040100u, selkeep = 0x07060504u;
-        uint32_t offv = 0;  // this half's offset (off0 or off1) as a lane register
-        uint32_t parv = 0;  // 64 * this half's parity (the bpermute address term)
+        uint32_t offv = 0;  // this half's o (o0 or o1) as a lane register
         const uint8_t *s_symf = &s_sym[0][0];
         const uint32_t *s_rkf = &s_rk[0][0];
         // One step of both half-waves.  act = lanes holding a value this step
@@ -1165,13 +1164,12 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
             const uint64_t m = lanes_lt(xd, kStateLow) & act;
             const uint32_t lo = (uint32_t)m, hi = (uint32_t)(m >> 32);
             const uint32_t clo = __builtin_popcount(lo), chi = __builtin_popcount(hi);
-            // word index relative to the window: (pos - base) + rank inside the
-            // half, from the offset register and one mbcnt per half (no scalar
-            // arithmetic between the compare and the word fetch)
+            // the lane's word: stream position o + rank inside the half, from the
+            // offset register and one mbcnt per half (no scalar arithmetic
+            // between the compare and the word fetch)
             const uint32_t kk = vsel(kHighHalf, __builtin_amdgcn_mbcnt_lo(lo, offv), __builtin_amdgcn_mbcnt_hi(hi, offv));
-            uint32_t wa;  // lane ((kk >> 1) + 16 * parity) mod 32 of this half
-            asm("v_lshl_add_u32 %0, %1, 1, %2" : "=v"(wa) : "v"(kk), "v"(parv));
-            const uint32_t wv = (uint32_t)__builtin_amdgcn_ds_bpermute((int)((wa & 124u) | lanebits), (int)P);
+            // lane (kk >> 1) mod 32 of this half
+            const uint32_t wv = (uint32_t)__builtin_amdgcn_ds_bpermute((int)(((kk << 1) & 124u) | lanebits), (int)P);
             // x' = (xd << 16) | word: bytes 0-1 (kk even) or 2-3 of wv below bytes
             // 0-1 of xd; lanes without a word keep xd (bytes 4-7)
             uint32_t selw;
@@ -1180,25 +1178,19 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
             x = tail ? vsel(act, x, xn) : xn;
             // window shifts (integer arithmetic only, so that it stays scalar):
             // s = 1 when the half's offset reaches the back block
-            off0 += clo;
-            off1 += chi;
-            const uint32_t s0 = off0 >> 5, s1 = off1 >> 5;
-            off0 &= 31u;
-            off1 &= 31u;
-            uint32_t ho;  // off1 - off0 in the upper half, 0 in the lower
-            asm("v_and_b32 %0, %1, %2" : "=v"(ho) : "s"(off1 - off0), "v"(hsel));
-            offv = off0 + ho;
-            // a shifting half: its front group takes the pairs loaded two steps
-            // ago, then the groups swap roles
-            const uint32_t m0 = (0xFFFFu << (16 * par0)) & (0u - s0), m1 = (0xFFFFu << (16 * par1)) & (0u - s1);
+            const uint32_t n0 = (o0 + clo) & 63u, n1 = (o1 + chi) & 63u;
+            const uint32_t s0 = (n0 ^ o0) >> 5, s1 = (n1 ^ o1) >> 5;  // 1: the half crossed into its back block
+            // a shifting half: its front group (o >> 5 before the step) takes the
+            // pairs loaded two steps ago, then the groups swap roles
+            const uint32_t m0 = (0xFFFFu << (16 * (o0 >> 5))) & (0u - s0), m1 = (0xFFFFu << (16 * (o1 >> 5))) & (0u - s1);
             const uint64_t rm = (uint64_t(m1) << 32) | m0;
+            o0 = n0;
+            o1 = n1;
+            uint32_t ho;  // o1 - o0 in the upper half, 0 in the lower
+            asm("v_and_b32 %0, %1, %2" : "=v"(ho) : "s"(o1 - o0), "v"(hsel));
+            offv = o0 + ho;
             P = vsel(rm, P, NX[par]);
             ra += vsel(rm, 0u, 128u);
-            par0 ^= s0;
-            par1 ^= s1;
-            uint32_t hp;  // 64 * (par1 - par0) in the upper half, 0 in the lower
-            asm("v_and_b32 %0, %1, %2" : "=v"(hp) : "s"(64 * (par1 - par0)), "v"(hsel));
-            parv = 64 * par0 + hp;
             NX[par] = bld32(rrec, ra);
             if (DT == 1) {
                 // sign (bit 7 of sm, copied to bit 15) and mantissa bits 0-6
@@ -1269,7 +1261,7 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
         // words consumed: the window base is 32 words per shift, and every
         // shift refilled one group (its lanes' ra advanced by 128 bytes)
         const uint32_t refills = (ra - (wstart + 128 + 4 * lj)) / 128;
-        const uint32_t pos = 32 * (refills + (uint32_t)__shfl_xor((int)refills, 16, 64)) + (h ? off1 : off0);
+        const uint32_t pos = 32 * (refills + (uint32_t)__shfl_xor((int)refills, 16, 64)) + ((h ? o1 : o0) & 31u);
         const bool endbad = half_mask(__ballot(rans_run && (x != kStateLow || pos != nw)), h) != 0;
         ok = ok && !endbad;
         // ---- chunks stored RAW: exponent bytes straight from the record ----
