@@ -116,7 +116,10 @@ __device__ inline void bst32(rsrc_t r, uint32_t off, uint32_t v) {
 // Lane masks.  lanes_lt(a, b) is the 64-bit mask of lanes with a < b (one
 // compare, no 0/1 materialisation).  vsel(mask, a, b) picks b in the lanes
 // set in a wave-uniform mask and a elsewhere: a single v_cndmask_b32 reading
-// the mask from scalar registers.
+// the mask from scalar registers.  The mask must be written by the scalar
+// unit (e.g. a compare result and-ed with another mask), not straight by a
+// vector compare: a vector read of scalar registers that a vector instruction
+// just wrote needs wait states, which the compiler does not insert for asm.
 __device__ inline uint64_t lanes_lt(uint32_t a, uint32_t b) { return __builtin_amdgcn_uicmp(a, b, 36 /* ULT */); }
 __device__ inline uint32_t vsel(uint64_t mask, uint32_t if0, uint32_t if1) {
     uint32_t r;
@@ -1095,16 +1098,15 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
         // ---- rANS decode (V9: end state L on every lane, every word consumed) ----
         // Word window of a half: words [base, base + 64), two blocks of 32
         // words, each held by 16 lanes of the half as adjacent word pairs (lane
-        // i of a group: words 2i and 2i + 1 of its block, one dword in P).  The
-        // state of a half is one scalar, o = (words consumed) mod 64 (o0, o1;
-        // per lane in offv): the group holding the front block [base, base +
-        // 32) is o >> 5, the position past the base is o & 31, and word o + k
-        // of the stream (k < 32) lives in lane ((o + k) >> 1) mod 32 of the
-        // half, half-word (o + k) & 1.  A half shifts when o crosses a
-        // multiple of 32.  Loads past the pair's
-        // records read zero, and words past n_words are never consumed by a
-        // valid stream (a stream that tries fails the end check pos ==
-        // n_words).
+        // i of a group: words 2i and 2i + 1 of its block, one dword in P); base
+        // is a multiple of 32.  Word k of the stream lives in lane (k >> 1) mod
+        // 32 of the half, half-word k & 1.  The bookkeeping is per lane, in
+        // vector registers: offv = words consumed by the lane's half, lim = the
+        // count at which the lane's block is used up (the end of its block);
+        // the lane then takes the pair 64 words further, loaded ahead into NX.
+        // Loads past the pair's records read zero, and words past n_words are
+        // never consumed by a valid stream (a stream that tries fails the end
+        // check offv == n_words).
         const uint32_t pair_vals = vals0 + vals1;
         const rsrc_t rsm = make_rsrc(d.in + sm_off + c0 * ce * R, pair_vals * R);
         const rsrc_t rout = make_rsrc(d.out + c0 * ce * EB, pair_vals * EB);
@@ -1120,39 +1122,44 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
         const uint32_t F0 = run0 ? ni0 / 32 : 0xFFFFFFFFu, F1 = run1 ? ni1 / 32 : 0xFFFFFFFFu;
         const uint32_t Tmain = min(min(F0, F1), Tw) & ~7u;
         const uint32_t Tmain16 = Tmain & ~15u;  // bf16 main loop: 16 steps per iteration
-        // per half: off = words consumed - window base (< 32 between steps)
-        uint32_t o0 = 0, o1 = 0;  // words consumed mod 64, per half
         // bf16: this lane's sign+mantissa dword of group 0 (see the main loop),
         // loaded before the word window so that many memory operations lie
         // between these loads and their first use
         const uint32_t smd0 = (h ? vals0 : 0u) + 4 * lj;
         const uint32_t D0first = DT == 1 ? bld32(rsm, smd0) : 0u, D1first = DT == 1 ? bld32(rsm, smd0 + 128) : 0u;
-        // Refill: at every step, after the shift decision, each lane loads the
-        // word pair it would take at the next shift if no shift came in between:
-        // front-group lanes from the block 64 words past the base, back-group
-        // lanes from the block 96 words past it (ra, a byte offset).  Two steps
-        // later the front group is either the same (no shift in between: it
-        // needs the block 64 past the then base, loaded) or the former back
-        // group (one shift: the then base is 32 further, so it needs the block
-        // 96 past the old one, loaded).  Every refill load is consumed two
-        // steps after it is issued (NX[par]), off the dependency chain.
+        // Refill: at every step, after its own refill decision, each lane loads
+        // the pair it takes at its next refill (block end lim, 32 words past
+        // it, pair position 2i) into NX[t mod 4]; the load is consumed four
+        // steps later.  Waiting for a load also waits for every older store
+        // (one counter covers both), so the distance keeps the output stores
+        // off the critical path.  A lane refills at most once every two steps
+        // (a refill takes 64 words, a step at most 32); one that refills again
+        // two or three steps after its last refill (more than 16 words per
+        // step: near-uniform exponents only) finds in NX a pair loaded before
+        // that refill.  bf16 detects this from the refill masks of the last
+        // three steps (scalar) and then reloads synchronously; fp32, whose
+        // waves are too few to hide a branch, also loads the pair 64 words
+        // further (NB), which is the right one exactly in that case.
         const uint32_t wstart = rel + (uint32_t)words_offset(nsym);  // byte offset of word 0
         uint32_t P = bld32(rrec, wstart + 4 * lj);                    // words 2lj, 2lj + 1
-        uint32_t ra = wstart + 128 + 4 * lj;                          // words 64 + 2lj, 65 + 2lj
-        uint32_t NX[2];
-        NX[0] = NX[1] = bld32(rrec, ra);
+        uint32_t lim = 32 + 32 * (lj >> 4);                           // end of the lane's block
+        const uint32_t rbase = wstart + 64 + 4 * (lj & 15u);          // byte offset of its next pair = 2 lim + rbase
+        uint32_t NX[4], NB[4];
+        NX[0] = NX[1] = NX[2] = NX[3] = bld32(rrec, 2 * lim + rbase); // words 64 + 2lj, 65 + 2lj
+        NB[0] = NB[1] = NB[2] = NB[3] = DT == 1 ? 0u : bld32(rrec, 2 * lim + rbase + 128);
+        uint64_t R1 = 0, R2 = 0, R3 = 0;  // bf16: refill masks of the last three steps
+        uint32_t age = 4;                  // fp32: steps since the lane's last refill
         const uint32_t lanebits = (h << 5) << 2;
-        const uint32_t hsel = h ? 0xFFFFFFFFu : 0u;
         const uint32_t hsym = h << kProbBits, hrk = h << 8;  // this half's table rows
         const uint32_t selbase = 0x05040100u, selkeep = 0x07060504u;
-        uint32_t offv = 0;  // this half's o (o0 or o1) as a lane register
+        uint32_t offv = 0;  // words consumed by this half
         const uint8_t *s_symf = &s_sym[0][0];
         const uint32_t *s_rkf = &s_rk[0][0];
         // One step of both half-waves.  act = lanes holding a value this step
         // (TAIL steps only: in the main loop every lane of a running half
         // holds one, and lanes of a half that is not running never reach the
-        // output or the checks); par = step parity (selects the refill
-        // registers).  With the table entry em = g | sym << 12 | c0 << 20,
+        // output or the checks); par = step mod 4 (selects the refill
+        // register).  With the table entry em = g | sym << 12 | c0 << 20,
         // g = 4096 - f, the decode step f * (x >> 12) + (x & 4095) - c0 is
         // x - (g * (x >> 12) + c0).
         // sp: the value's sign+mantissa, for bf16 as the byte in bytes 0 and 1
@@ -1161,12 +1168,13 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
             asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(slot_addr) : "v"(x), "s"(kTableSize - 1), "v"(hsym));
             const uint32_t em = s_rkf[s_symf[slot_addr] | hrk];
             const uint32_t xd = x - (__umul24(em & 0xFFFu, x >> kProbBits) + (em >> 20));
+            // (the and with act also puts the mask in registers written by the
+            // scalar unit: inline asm below reads it, and the hardware needs
+            // spacing between a vector compare writing scalar registers and a
+            // vector read of them, which the compiler cannot see through asm)
             const uint64_t m = lanes_lt(xd, kStateLow) & act;
             const uint32_t lo = (uint32_t)m, hi = (uint32_t)(m >> 32);
-            const uint32_t clo = __builtin_popcount(lo), chi = __builtin_popcount(hi);
-            // the lane's word: stream position o + rank inside the half, from the
-            // offset register and one mbcnt per half (no scalar arithmetic
-            // between the compare and the word fetch)
+            // the lane's word: stream position offv + rank inside the half (one mbcnt per half)
             const uint32_t kk = vsel(kHighHalf, __builtin_amdgcn_mbcnt_lo(lo, offv), __builtin_amdgcn_mbcnt_hi(hi, offv));
             // lane (kk >> 1) mod 32 of this half
             const uint32_t wv = (uint32_t)__builtin_amdgcn_ds_bpermute((int)(((kk << 1) & 124u) | lanebits), (int)P);
@@ -1176,22 +1184,37 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
             asm("v_mad_u32_u24 %0, %1, %2, %3" : "=v"(selw) : "v"(kk & 1u), "s"(0x0202u), "v"(selbase));
             const uint32_t xn = __builtin_amdgcn_perm(xd, wv, vsel(m, selkeep, selw));
             x = tail ? vsel(act, x, xn) : xn;
-            // window shifts (integer arithmetic only, so that it stays scalar):
-            // s = 1 when the half's offset reaches the back block
-            const uint32_t n0 = (o0 + clo) & 63u, n1 = (o1 + chi) & 63u;
-            const uint32_t s0 = (n0 ^ o0) >> 5, s1 = (n1 ^ o1) >> 5;  // 1: the half crossed into its back block
-            // a shifting half: its front group (o >> 5 before the step) takes the
-            // pairs loaded two steps ago, then the groups swap roles
-            const uint32_t m0 = (0xFFFFu << (16 * (o0 >> 5))) & (0u - s0), m1 = (0xFFFFu << (16 * (o1 >> 5))) & (0u - s1);
-            const uint64_t rm = (uint64_t(m1) << 32) | m0;
-            o0 = n0;
-            o1 = n1;
-            uint32_t ho;  // o1 - o0 in the upper half, 0 in the lower
-            asm("v_and_b32 %0, %1, %2" : "=v"(ho) : "s"(o1 - o0), "v"(hsel));
-            offv = o0 + ho;
-            P = vsel(rm, P, NX[par]);
-            ra += vsel(rm, 0u, 128u);
-            NX[par] = bld32(rrec, ra);
+            // bookkeeping in vector registers: the half's consumed count, then
+            // the lanes whose block is used up take the pairs loaded two steps ago
+            uint32_t olo, ohi;
+            asm("v_bcnt_u32_b32 %0, %1, %2" : "=v"(olo) : "s"(lo), "v"(offv));
+            asm("v_bcnt_u32_b32 %0, %1, %2" : "=v"(ohi) : "s"(hi), "v"(offv));
+            offv = vsel(kHighHalf, olo, ohi);
+            // (plain selects: the mask comes from a vector compare, and the
+            // compiler spaces its reads as the hardware requires)
+            const bool used_up = offv >= lim;
+            if (DT == 1) {
+                const uint64_t um = __builtin_amdgcn_ballot_w64(used_up);
+                const uint64_t stale = um & (R2 | R3);
+                R3 = R2;
+                R2 = R1;
+                R1 = um;
+                if (stale) {
+                    // (the asm copy makes the wait for the fresh pair happen
+                    // inside the branch, so no load is pending where the paths meet)
+                    uint32_t fresh;
+                    asm volatile("v_mov_b32 %0, %1" : "=v"(fresh) : "v"(bld32(rrec, 2 * lim + rbase)));
+                    P = used_up ? fresh : P;
+                } else {
+                    P = used_up ? NX[par] : P;
+                }
+            } else {
+                P = used_up ? (age < 4u ? NB[par] : NX[par]) : P;
+                age = used_up ? 1u : age + 1u;
+            }
+            lim += used_up ? 64u : 0u;
+            NX[par] = bld32(rrec, 2 * lim + rbase);
+            if (DT != 1) NB[par] = bld32(rrec, 2 * lim + rbase + 128);
             if (DT == 1) {
                 // sign (bit 7 of sm, copied to bit 15) and mantissa bits 0-6
                 // from sp, exponent (em bits 12-19) to bits 7-14; the store
@@ -1220,7 +1243,7 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
 #pragma unroll
                 for (int u = 0; u < 8; ++u) {
                     const uint32_t w = (uint32_t)__builtin_amdgcn_ds_bpermute((int)(smsrc + 32 * (u & 3)), (int)(u < 4 ? Da : Db));
-                    step(t0 + u, runm, false, __builtin_amdgcn_perm(0u, w, smsel), u & 1);
+                    step(t0 + u, runm, false, __builtin_amdgcn_perm(0u, w, smsel), u & 3);
                 }
             };
             uint32_t D0 = D0first, D1 = D1first;
@@ -1241,7 +1264,7 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
                 for (int u = 0; u < kSmAhead; ++u) {
                     const uint32_t sp = smq[u];
                     smq[u] = bload_sm<DT>(rsm, sm_lane + (t + u + kSmAhead) * 32 * R);
-                    step(t + u, runm, false, sp, u & 1);
+                    step(t + u, runm, false, sp, u & 3);
                 }
             }
         }
@@ -1255,14 +1278,10 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
                 const uint32_t tt = t + u;
                 const uint64_t act = (run0 && ni0 > 32 * tt ? half_prefix_mask(ni0 - 32 * tt, 0) : 0ull) |
                                      (run1 && ni1 > 32 * tt ? half_prefix_mask(ni1 - 32 * tt, 1) : 0ull);
-                step(tt, act, true, DT == 1 ? __umul24(smt[u], 0x101u) : smt[u], u & 1);
+                step(tt, act, true, DT == 1 ? __umul24(smt[u], 0x101u) : smt[u], u & 3);
             }
         }
-        // words consumed: the window base is 32 words per shift, and every
-        // shift refilled one group (its lanes' ra advanced by 128 bytes)
-        const uint32_t refills = (ra - (wstart + 128 + 4 * lj)) / 128;
-        const uint32_t pos = 32 * (refills + (uint32_t)__shfl_xor((int)refills, 16, 64)) + ((h ? o1 : o0) & 31u);
-        const bool endbad = half_mask(__ballot(rans_run && (x != kStateLow || pos != nw)), h) != 0;
+        const bool endbad = half_mask(__ballot(rans_run && (x != kStateLow || offv != nw)), h) != 0;
         ok = ok && !endbad;
         // ---- chunks stored RAW: exponent bytes straight from the record ----
         if (raw_run) {

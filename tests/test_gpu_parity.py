@@ -129,6 +129,34 @@ def test_one_dominant_exponent_plus_rare_singletons():
     check_parity(((e << 7) | rng.integers(0, 256, e.size).astype(np.uint16) & 0x807F).astype(np.uint16))
 
 
+@pytest.mark.parametrize("dtype", [np.uint16, np.uint32])
+@pytest.mark.parametrize("tail", [8, 16])
+def test_burst_of_rare_exponents(dtype, tail):
+    """One exponent for most of each chunk, then a run of the 255 others drawn
+    uniformly: the others get f = 1 or 2, so that run costs 11-12 bits per
+    value, more than 21 renormalisation words per step for a half-wave.  A
+    lane of the decoder then takes new words twice within three steps, which
+    the steady data of the other tests never does (the decoder's refill path
+    for that case)."""
+    rng = np.random.default_rng(11 + tail)
+    ce = 32768 if dtype == np.uint16 else 65536
+    n = 3 * ce + 1000
+    e = np.full(n, 127, dtype=np.uint32)
+    others = np.array([s for s in range(256) if s != 127], dtype=np.uint32)
+    for c0 in range(0, n, ce):
+        m = min(ce, n - c0)
+        k = m // tail
+        e[c0 + m - k: c0 + m] = rng.choice(others, k)
+    if dtype == np.uint16:
+        bits = (e << 7) | (rng.integers(0, 2, n, dtype=np.uint32) << 15) | rng.integers(0, 128, n, dtype=np.uint32)
+    else:
+        bits = (e << 23) | (rng.integers(0, 2, n, dtype=np.uint32) << 31) | rng.integers(0, 1 << 23, n, dtype=np.uint32)
+    bits = bits.astype(dtype)
+    _, _, recs = parse_buffer(orc.compress(_code(bits), bits))
+    assert all(r["mode"] == 0 for r in recs)  # every chunk is coded
+    check_parity(bits)
+
+
 @pytest.mark.parametrize("dtype,chunk_bytes", [(np.uint16, 64), (np.uint16, 2048), (np.uint16, 131072),
                                                (np.uint16, 1 << 21), (np.uint32, 128), (np.uint32, 65536),
                                                (np.uint32, 1 << 22)])
