@@ -112,6 +112,11 @@ __device__ inline void bst16(rsrc_t r, uint32_t off, uint32_t v) {
 __device__ inline void bst32(rsrc_t r, uint32_t off, uint32_t v) {
     __builtin_amdgcn_raw_buffer_store_b32(v, r, (int)off, 0, 0);
 }
+// Loops that issue loads in asm and wait for them explicitly start with this:
+// scalar registers of a buffer resource written by a vector instruction need
+// five wait states before a memory instruction reads them, which the compiler
+// does not insert before asm.
+__device__ inline void asm_vmem_fence() { asm volatile("s_nop 4"); }
 
 // Lane masks.  lanes_lt(a, b) is the 64-bit mask of lanes with a < b (one
 // compare, no 0/1 materialisation).  vsel(mask, a, b) picks b in the lanes
@@ -676,76 +681,112 @@ __global__ __launch_bounds__(64) void k_encode(EncParams p) {
     const uint32_t T0 = alive0 ? (vals0 + 31) / 32 : 0u, T1 = alive1 ? (vals1 + 31) / 32 : 0u;
     const uint32_t nblk = (max(T0, T1) + 7) / 8;
     const uint32_t hsel = h ? 0xFFFFFFFFu : 0u;
-    uint32_t cur[8], nxt[8];
-    {
-        const uint32_t o = in0 + ((nblk - 1) * 8 * 32 + lj) * EB;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) cur[k] = DT == 1 ? bld16(rin, o + k * 32 * EB) : bld32(rin, o + k * 32 * EB);
-    }
-    for (int32_t b = (int32_t)nblk - 1; b >= 0; --b) {
-        {
-            const uint32_t o = b > 0 ? in0 + ((uint32_t)(b - 1) * 8 * 32 + lj) * EB : kOutOfRange;
-#pragma unroll
-            for (int k = 0; k < 8; ++k) nxt[k] = DT == 1 ? bld16(rin, o + k * 32 * EB) : bld32(rin, o + k * 32 * EB);
+    // One step; CAREFUL steps rebuild the lane masks and check the room
+    // (a ragged chunk end, or words close to the RAW size), the others use
+    // the block's loop-invariant mask.
+    auto step = [&](int32_t b, int k, uint32_t v, bool careful, uint64_t act) __attribute__((always_inline)) {
+        const uint32_t t = (uint32_t)b * 8 + k;
+        if (careful)
+            act = (alive0 && vals0 > 32 * t ? half_prefix_mask(vals0 - 32 * t, 0) : 0ull) |
+                  (alive1 && vals1 > 32 * t ? half_prefix_mask(vals1 - 32 * t, 1) : 0ull);
+        uint32_t ex;  // the value's exponent
+        asm("v_bfe_u32 %0, %1, %2, 8" : "=v"(ex) : "v"(v), "i"(DT == 1 ? 7 : 23));
+        const uint4 te = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint8_t *>(tab) + (ex << 4));
+        uint64_t m = lanes_lt(te.x & 0xFFFFu, x >> 20) & act;  // x >= f * 2^20
+        uint32_t lo = (uint32_t)m, hi = (uint32_t)(m >> 32);
+        uint32_t clo = __builtin_popcount(lo), chi = __builtin_popcount(hi);
+        if (careful) {
+            if (alive0 && (end0 - r0) + clo > wcap0) alive0 = false;
+            if (alive1 && (end1 - r1) + chi > wcap1) alive1 = false;
+            const uint64_t am = (alive0 ? 0xFFFFFFFFull : 0ull) | (alive1 ? kHighHalf : 0ull);
+            m &= am;
+            act &= am;
+            lo = (uint32_t)m;
+            hi = (uint32_t)(m >> 32);
+            clo = __builtin_popcount(lo);
+            chi = __builtin_popcount(hi);
         }
-        // One step; CAREFUL steps rebuild the lane masks and check the room
-        // (a ragged chunk end, or words close to the RAW size), the others use
-        // the block's loop-invariant mask.
-        auto step = [&](int k, bool careful, uint64_t act) __attribute__((always_inline)) {
-            const uint32_t t = (uint32_t)b * 8 + k;
-            if (careful)
-                act = (alive0 && vals0 > 32 * t ? half_prefix_mask(vals0 - 32 * t, 0) : 0ull) |
-                      (alive1 && vals1 > 32 * t ? half_prefix_mask(vals1 - 32 * t, 1) : 0ull);
-            uint32_t ex;  // the value's exponent
-            asm("v_bfe_u32 %0, %1, %2, 8" : "=v"(ex) : "v"(cur[k]), "i"(DT == 1 ? 7 : 23));
-            const uint4 te = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint8_t *>(tab) + (ex << 4));
-            uint64_t m = lanes_lt(te.x & 0xFFFFu, x >> 20) & act;  // x >= f * 2^20
-            uint32_t lo = (uint32_t)m, hi = (uint32_t)(m >> 32);
-            uint32_t clo = __builtin_popcount(lo), chi = __builtin_popcount(hi);
-            if (careful) {
-                if (alive0 && (end0 - r0) + clo > wcap0) alive0 = false;
-                if (alive1 && (end1 - r1) + chi > wcap1) alive1 = false;
-                const uint64_t am = (alive0 ? 0xFFFFFFFFull : 0ull) | (alive1 ? kHighHalf : 0ull);
-                m &= am;
-                act &= am;
-                lo = (uint32_t)m;
-                hi = (uint32_t)(m >> 32);
-                clo = __builtin_popcount(lo);
-                chi = __builtin_popcount(hi);
-            }
-            // word index: end of the slot's words - (words so far + this step's) + rank in the half
-            // (r0, r1: word index just past the words still to come)
-            const uint32_t e0 = r0 - clo;
-            r1 -= chi;
-            const uint32_t e1 = r1 - clo;
-            r0 = e0;
-            uint32_t hb;  // e1 - e0 in the upper half, 0 in the lower
-            asm("v_and_b32 %0, %1, %2" : "=v"(hb) : "s"(e1 - e0), "v"(hsel));
-            const uint32_t kk = __builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, e0 + hb));
-            bst16(rslot, vsel(m, kOutOfRange, kk << 1), x);
-            const uint32_t xs = vsel(m, x, x >> 16);
-            const uint32_t qd = enc_quotient(xs, __hiloint2double((int)te.w, (int)te.z));
-            const uint32_t xe = __umul24(qd, te.x >> 16) + (xs + te.y);  // = q * M + (xs - q * f) + c0
-            // Lanes past a ragged chunk end keep their state.  Outside CAREFUL
-            // steps every lane of a live half codes a value, and a stopped
-            // half's state is never used (its chunk is stored RAW).
-            x = careful ? vsel(act, x, xe) : xe;
-        };
-        // a block codes at most 256 values, so at most 256 words, per half
+        // word index: end of the slot's words - (words so far + this step's) + rank in the half
+        // (r0, r1: word index just past the words still to come)
+        const uint32_t e0 = r0 - clo;
+        r1 -= chi;
+        const uint32_t e1 = r1 - clo;
+        r0 = e0;
+        uint32_t hb;  // e1 - e0 in the upper half, 0 in the lower
+        asm("v_and_b32 %0, %1, %2" : "=v"(hb) : "s"(e1 - e0), "v"(hsel));
+        const uint32_t kk = __builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, e0 + hb));
+        bst16(rslot, vsel(m, kOutOfRange, kk << 1), x);
+        const uint32_t xs = vsel(m, x, x >> 16);
+        const uint32_t qd = enc_quotient(xs, __hiloint2double((int)te.w, (int)te.z));
+        const uint32_t xe = __umul24(qd, te.x >> 16) + (xs + te.y);  // = q * M + (xs - q * f) + c0
+        // Lanes past a ragged chunk end keep their state.  Outside CAREFUL
+        // steps every lane of a live half codes a value, and a stopped
+        // half's state is never used (its chunk is stored RAW).
+        x = careful ? vsel(act, x, xe) : xe;
+    };
+    // a block codes at most 256 values, so at most 256 words, per half: a
+    // FAST block needs no per-step checks
+    auto block_fast = [&](int32_t b) __attribute__((always_inline)) {
         const uint32_t tend = ((uint32_t)b + 1) * 256;
-        const bool fast = (!alive0 || (vals0 >= tend && (end0 - r0) + 256 <= wcap0)) &&
-                          (!alive1 || (vals1 >= tend && (end1 - r1) + 256 <= wcap1));
-        if (fast) {
-            const uint64_t act = (alive0 ? 0xFFFFFFFFull : 0ull) | (alive1 ? kHighHalf : 0ull);
+        return (!alive0 || (vals0 >= tend && (end0 - r0) + 256 <= wcap0)) &&
+               (!alive1 || (vals1 >= tend && (end1 - r1) + 256 <= wcap1));
+    };
+    auto fast_block = [&](int32_t b, const uint32_t(&V)[8]) __attribute__((always_inline)) {
+        const uint64_t act = (alive0 ? 0xFFFFFFFFull : 0ull) | (alive1 ? kHighHalf : 0ull);
 #pragma unroll
-            for (int k = 7; k >= 0; --k) step(k, false, act);
-        } else {
+        for (int k = 7; k >= 0; --k) step(b, k, V[k], false, act);
+    };
+    // Block values: lane lj's values of steps 8b .. 8b + 7 (past the pair: zeros).
+    // Runs of FAST blocks are software-pipelined: the next block's values are
+    // loaded while a block is coded.  One counter tracks loads and stores in
+    // issue order, so the compiler's wait for those values, placed after the
+    // block's word stores, would also wait for the stores.  The loads are
+    // therefore issued in asm and waited for explicitly: between the loads
+    // and their wait lies only the coding of one FAST block, straight-line
+    // code with exactly eight word stores, so at most eight operations may
+    // remain outstanding.  Every branch and loop edge comes after a wait, so
+    // no register with a load in flight is ever copied (a test checks the
+    // generated code for this).  Other blocks use ordinary loads.
+    auto asm_load_block = [&](int32_t bb, uint32_t(&V)[8]) __attribute__((always_inline)) {
+        const uint32_t o = bb >= 0 ? in0 + ((uint32_t)bb * 8 * 32 + lj) * EB : kOutOfRange;
 #pragma unroll
-            for (int k = 7; k >= 0; --k) step(k, true, 0ull);
+        for (int k = 0; k < 8; ++k) {
+            if (DT == 1)
+                asm volatile("buffer_load_ushort %0, %1, %2, 0 offen offset:%3" : "=v"(V[k]) : "v"(o), "s"(rin), "i"(k * 32 * EB));
+            else
+                asm volatile("buffer_load_dword %0, %1, %2, 0 offen offset:%3" : "=v"(V[k]) : "v"(o), "s"(rin), "i"(k * 32 * EB));
         }
+    };
+#define UZIP_WAIT_BLOCK(N, V)                                                                                     \
+    asm volatile("s_waitcnt vmcnt(" #N ")" : "+v"(V[0]), "+v"(V[1]), "+v"(V[2]), "+v"(V[3]), "+v"(V[4]), "+v"(V[5]), \
+                 "+v"(V[6]), "+v"(V[7]))
+    for (int32_t b = (int32_t)nblk - 1; b >= 0;) {
+        if (!block_fast(b)) {
+            const uint32_t o = in0 + ((uint32_t)b * 8 * 32 + lj) * EB;
+            uint32_t V[8];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) cur[k] = nxt[k];
+            for (int k = 0; k < 8; ++k) V[k] = DT == 1 ? bld16(rin, o + k * 32 * EB) : bld32(rin, o + k * 32 * EB);
+#pragma unroll
+            for (int k = 7; k >= 0; --k) step(b, k, V[k], true, 0ull);
+            --b;
+            continue;
+        }
+        uint32_t VA[8], VB[8];
+        asm_vmem_fence();
+        asm_load_block(b, VA);
+        UZIP_WAIT_BLOCK(0, VA);
+        for (;;) {
+            asm_load_block(b - 1, VB);
+            fast_block(b, VA);
+            UZIP_WAIT_BLOCK(8, VB);
+            if (--b < 0 || !block_fast(b)) break;
+            asm_load_block(b - 1, VA);
+            fast_block(b, VB);
+            UZIP_WAIT_BLOCK(8, VA);
+            if (--b < 0 || !block_fast(b)) break;
+        }
     }
+#undef UZIP_WAIT_BLOCK
 
     // ---- the record's fixed part into the slot (the words are already at its
     // end); a RAW record gets its header only: k_compact takes its exponents
