@@ -47,6 +47,7 @@ namespace uzip {
 // ---------------------------------------------------------------------------
 #define UZ_GLOBAL __attribute__((address_space(1)))
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 template <typename T>
 struct GAccess {
@@ -474,9 +475,6 @@ __global__ __launch_bounds__(64) void k_encode(EncParams p) {
         uint32_t *hm = valid ? hist : hist + 256 + (lj >> 2);
         const rsrc_t rsmo = make_rsrc(d.out + d.sm_off + c0 * ce * R, pair_vals * R);
         const uint32_t smo = (h ? vals0 : 0u) * R + lj * VPL * R;  // this lane's first sign+mantissa byte
-        auto vec = [&](uint32_t it) __attribute__((always_inline)) {
-            return bld128(rin, it < fullmin ? in0 + (it * VPI + lj * VPL) * EB : kOutOfRange);
-        };
         auto split = [&](const uint4 &qv, uint32_t it) __attribute__((always_inline)) {
             const uint32_t w[4] = {qv.x, qv.y, qv.z, qv.w};
             const uint32_t o = smo + it * VPI * R;
@@ -488,8 +486,7 @@ __global__ __launch_bounds__(64) void k_encode(EncParams p) {
                     smw[k >> 2] |= (((v >> 8) & 0x80u) | (v & 0x7Fu)) << (8 * (k & 3));
                     atomicAdd(&hm[(v >> 7) & 0xFFu], 1u);
                 }
-                bst32(rsmo, o, smw[0]);
-                bst32(rsmo, o + 4, smw[1]);
+                __builtin_amdgcn_raw_buffer_store_b64(u32x2{smw[0], smw[1]}, rsmo, (int)o, 0, 0);
             } else {
                 uint32_t sm[4];
 #pragma unroll
@@ -497,25 +494,48 @@ __global__ __launch_bounds__(64) void k_encode(EncParams p) {
                     sm[k] = ((w[k] >> 8) & 0x800000u) | (w[k] & 0x7FFFFFu);
                     atomicAdd(&hm[(w[k] >> 23) & 0xFFu], 1u);
                 }
-                bst32(rsmo, o, sm[0] | (sm[1] << 24));
-                bst32(rsmo, o + 4, (sm[1] >> 8) | (sm[2] << 16));
-                bst32(rsmo, o + 8, (sm[2] >> 16) | (sm[3] << 8));
+                __builtin_amdgcn_raw_buffer_store_b96(
+                    u32x3{sm[0] | (sm[1] << 24), (sm[1] >> 8) | (sm[2] << 16), (sm[2] >> 16) | (sm[3] << 8)}, rsmo, (int)o,
+                    0, 0);
             }
         };
-        // double buffer: the next four vectors are requested before the
-        // current four are split
-        uint4 qa = vec(0), qb = vec(1), qc = vec(2), qd = vec(3);
-        for (uint32_t it = 0; it < fullmin; it += 4) {
-            const uint4 na = vec(it + 4), nb = vec(it + 5), nc = vec(it + 6), nd = vec(it + 7);
-            split(qa, it);
-            split(qb, it + 1);
-            split(qc, it + 2);
-            split(qd, it + 3);
-            qa = na;
-            qb = nb;
-            qc = nc;
-            qd = nd;
+        // Sets of four vectors (iterations 4s .. 4s + 3), software-pipelined:
+        // the next set is loaded while a set is split.  As in the coding pass,
+        // the loads are issued in asm and waited for explicitly, so that the
+        // wait does not also cover the sign+mantissa stores: between a set's
+        // loads and its wait lies only the straight-line split of the set
+        // before, with exactly one store per vector.
+        auto asm_load_set = [&](uint32_t st, u32x4(&V)[4]) __attribute__((always_inline)) {
+#pragma unroll
+            for (uint32_t k = 0; k < 4; ++k) {
+                const uint32_t it = 4 * st + k;
+                const uint32_t o = it < fullmin ? in0 + (it * VPI + lj * VPL) * EB : kOutOfRange;
+                asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen" : "=v"(V[k]) : "v"(o), "s"(rin));
+            }
+        };
+        auto split_set = [&](uint32_t st, const u32x4(&V)[4]) __attribute__((always_inline)) {
+#pragma unroll
+            for (uint32_t k = 0; k < 4; ++k) split(make_uint4(V[k].x, V[k].y, V[k].z, V[k].w), 4 * st + k);
+        };
+#define UZIP_WAIT_SET(N, V) asm volatile("s_waitcnt vmcnt(" #N ")" : "+v"(V[0]), "+v"(V[1]), "+v"(V[2]), "+v"(V[3]))
+        const uint32_t nsets = fullmin / 4;
+        if (nsets > 0) {
+            u32x4 A[4], B[4];
+            asm_vmem_fence();
+            asm_load_set(0, A);
+            UZIP_WAIT_SET(0, A);
+            for (uint32_t st = 0;;) {
+                asm_load_set(st + 1, B);
+                split_set(st, A);
+                UZIP_WAIT_SET(4, B);
+                if (++st >= nsets) break;
+                asm_load_set(st + 1, A);
+                split_set(st, B);
+                UZIP_WAIT_SET(4, A);
+                if (++st >= nsets) break;
+            }
         }
+#undef UZIP_WAIT_SET
         first_it = fullmin;
     }
     // the rest: the longer half's remaining vectors and the ragged ends
