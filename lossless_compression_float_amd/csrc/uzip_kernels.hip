@@ -1224,7 +1224,7 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
         // g = 4096 - f, the decode step f * (x >> 12) + (x & 4095) - c0 is
         // x - (g * (x >> 12) + c0).
         // sp: the value's sign+mantissa, for bf16 as the byte in bytes 0 and 1
-        auto step = [&](uint32_t t, uint64_t act, bool tail, uint32_t sp, int par) __attribute__((always_inline)) {
+        auto step = [&](uint32_t t, uint64_t act, bool tail, uint32_t sp, int par, bool store) __attribute__((always_inline)) {
             uint32_t slot_addr;  // (x & 4095) | this half's row: the byte address in s_sym
             asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(slot_addr) : "v"(x), "s"(kTableSize - 1), "v"(hsym));
             const uint32_t em = s_rkf[s_symf[slot_addr] | hrk];
@@ -1282,11 +1282,13 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
                 // keeps the low 16 bits
                 uint32_t v;
                 asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(v) : "s"(0x807Fu), "v"(sp), "v"(em >> 5));
-                bst16(rout, out_lane + t * 32 * EB, v);
+                if (store) bst16(rout, out_lane + t * 32 * EB, v);
+                return v;
             } else {
                 // sign (bit 23 of sm) to bit 31, mantissa bits 0-22, exponent to bits 23-30
                 const uint32_t sx = sp | ((sp & 0x800000u) << 8), ex = em << 11;
                 bst32(rout, out_lane + t * 32 * EB, (sx & 0x807FFFFFu) | (ex & ~0x807FFFFFu));
+                return 0u;
             }
         };
         uint32_t t = 0;
@@ -1298,13 +1300,31 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
             // byte of a main-loop group lies inside both chunks.
             const uint32_t smsrc = ((lj >> 2) + 32 * h) << 2;       // bpermute address of step 0 of a group
             const uint32_t smsel = 0x0C0C0000u | ((lj & 3) * 0x0101u);
+            // Output: the values of two steps (128 bytes of the half's chunk)
+            // leave as one dword per lane: each lane packs its two values,
+            // then lane j takes the pairs of lanes 2j' and 2j' + 1 (j' = j mod
+            // 16) and keeps their first step's values (j < 16) or their
+            // second's: the dword at byte 64t + 4j.  One dword store replaces
+            // two 16-bit stores.
+            const uint32_t pk_src = ((2 * (lj & 15u)) + 32 * h) << 2;
+            const uint32_t pk_sel = lj < 16 ? 0x05040100u : 0x07060302u;
+            const uint32_t out_pair = rans_run ? (h ? vals0 : 0u) * EB + 4 * lj : kOutOfRange;
             // two register sets alternate (16 steps per loop iteration), so no
             // loaded register is copied
             auto group8 = [&](uint32_t t0, uint32_t Da, uint32_t Db) __attribute__((always_inline)) {
+                uint32_t vprev = 0;
 #pragma unroll
                 for (int u = 0; u < 8; ++u) {
                     const uint32_t w = (uint32_t)__builtin_amdgcn_ds_bpermute((int)(smsrc + 32 * (u & 3)), (int)(u < 4 ? Da : Db));
-                    step(t0 + u, runm, false, __builtin_amdgcn_perm(0u, w, smsel), u & 3);
+                    const uint32_t v = step(t0 + u, runm, false, __builtin_amdgcn_perm(0u, w, smsel), u & 3, false);
+                    if (u & 1) {
+                        const uint32_t q = __builtin_amdgcn_perm(v, vprev, 0x05040100u);
+                        const uint32_t qa = (uint32_t)__builtin_amdgcn_ds_bpermute((int)pk_src, (int)q);
+                        const uint32_t qb = (uint32_t)__builtin_amdgcn_ds_bpermute((int)(pk_src + 4), (int)q);
+                        bst32(rout, out_pair + (t0 + u - 1) * 64, __builtin_amdgcn_perm(qb, qa, pk_sel));
+                    } else {
+                        vprev = v;
+                    }
                 }
             };
             uint32_t D0 = D0first, D1 = D1first;
@@ -1325,7 +1345,7 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
                 for (int u = 0; u < kSmAhead; ++u) {
                     const uint32_t sp = smq[u];
                     smq[u] = bload_sm<DT>(rsm, sm_lane + (t + u + kSmAhead) * 32 * R);
-                    step(t + u, runm, false, sp, u & 3);
+                    step(t + u, runm, false, sp, u & 3, true);
                 }
             }
         }
@@ -1339,7 +1359,7 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
                 const uint32_t tt = t + u;
                 const uint64_t act = (run0 && ni0 > 32 * tt ? half_prefix_mask(ni0 - 32 * tt, 0) : 0ull) |
                                      (run1 && ni1 > 32 * tt ? half_prefix_mask(ni1 - 32 * tt, 1) : 0ull);
-                step(tt, act, true, DT == 1 ? __umul24(smt[u], 0x101u) : smt[u], u & 3);
+                step(tt, act, true, DT == 1 ? __umul24(smt[u], 0x101u) : smt[u], u & 3, true);
             }
         }
         const bool endbad = half_mask(__ballot(rans_run && (x != kStateLow || offv != nw)), h) != 0;
