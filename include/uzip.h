@@ -59,7 +59,14 @@
 extern "C" {
 #endif
 
-typedef enum { UZIP_BF16 = 1, UZIP_FP32 = 2 } uzip_dtype;
+/* Value types (UCCL-Zip, Fig. 13: bfloat16, float16, float32, float8_e4m3fn
+ * and float8_e5m2 payloads).  The coded symbol of a value is the byte of its
+ * exponent field: bf16 bits 14..7 and fp32 bits 30..23 (the exponent; the
+ * sign and mantissa are stored raw, 1 and 3 bytes per value); fp16 bits 15..8
+ * (sign, the 5 exponent bits and the top 2 mantissa bits; the low mantissa
+ * byte is raw); fp8 the whole byte (nothing raw).  Neither fp16 nor fp8 has a
+ * byte-aligned field of exponent bits alone. */
+typedef enum { UZIP_BF16 = 1, UZIP_FP32 = 2, UZIP_FP16 = 3, UZIP_FP8_E4M3 = 4, UZIP_FP8_E5M2 = 5 } uzip_dtype;
 
 typedef enum {
     UZIP_OK = 0,
@@ -73,7 +80,7 @@ typedef enum {
 /* Exact upper bound of the compressed size of num_elements values: the size
  * the buffer has when every chunk is stored RAW (a chunk is coded only when
  * that is strictly smaller).  chunk_bytes is the uncompressed chunk size
- * (0 = default: 64 KiB for bf16, 256 KiB for fp32).  Pure host function;
+ * (0 = default: 256 KiB for fp32, 64 KiB for the others).  Pure host function;
  * returns 0 for an invalid dtype or chunk size. */
 size_t uzip_max_compressed_size(uzip_dtype dtype, size_t num_elements, size_t chunk_bytes);
 

@@ -24,6 +24,9 @@ LIB_PATH = os.path.join(_PKG, "libuzip.so")
 
 UZIP_BF16 = 1
 UZIP_FP32 = 2
+UZIP_FP16 = 3
+UZIP_FP8_E4M3 = 4
+UZIP_FP8_E5M2 = 5
 UZIP_OK = 0
 UZIP_ERR_INVALID_ARGUMENT = 1
 UZIP_ERR_CAPACITY = 2
@@ -148,16 +151,18 @@ def uzip_status_string(status: int) -> str:
 
 
 # ---- torch-level convenience wrappers ---------------------------------------
+_CODES = {torch.bfloat16: UZIP_BF16, torch.float32: UZIP_FP32, torch.float16: UZIP_FP16,
+          torch.float8_e4m3fn: UZIP_FP8_E4M3, torch.float8_e5m2: UZIP_FP8_E5M2}
+
+
 def dtype_code(t: torch.dtype) -> int:
-    if t == torch.bfloat16:
-        return UZIP_BF16
-    if t == torch.float32:
-        return UZIP_FP32
-    raise TypeError("uzip compresses bfloat16 or float32 tensors, not %s" % t)
+    if t in _CODES:
+        return _CODES[t]
+    raise TypeError("uzip compresses bfloat16, float16, float32, float8_e4m3fn or float8_e5m2 tensors, not %s" % t)
 
 
 def torch_dtype(code: int) -> torch.dtype:
-    return {UZIP_BF16: torch.bfloat16, UZIP_FP32: torch.float32}[code]
+    return {v: k for k, v in _CODES.items()}[code]
 
 
 def _stream(stream=None) -> int:

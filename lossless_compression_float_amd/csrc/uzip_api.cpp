@@ -23,7 +23,7 @@ uint64_t al(uint64_t v) { return (v + kWsAlign - 1) / kWsAlign * kWsAlign; }
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
-bool dtype_ok(uzip_dtype d) { return d == UZIP_BF16 || d == UZIP_FP32; }
+bool dtype_ok(uzip_dtype d) { return d >= UZIP_BF16 && d <= UZIP_FP8_E5M2; }
 
 // chunk_elems of a call, or 0 when the chunk size is invalid: the chunk must
 // hold a multiple of 32 values (whole rANS steps) and at most 2^20 values
@@ -31,7 +31,7 @@ bool dtype_ok(uzip_dtype d) { return d == UZIP_BF16 || d == UZIP_FP32; }
 uint64_t chunk_elems_of(uzip_dtype dtype, size_t chunk_bytes) {
     if (!dtype_ok(dtype)) return 0;
     const uint64_t eb = elem_bytes(dtype);
-    if (chunk_bytes == 0) chunk_bytes = dtype == UZIP_BF16 ? 65536 : 262144;
+    if (chunk_bytes == 0) chunk_bytes = dtype == UZIP_FP32 ? 262144 : 65536;
     if (chunk_bytes % (32 * eb) != 0) return 0;
     const uint64_t ce = chunk_bytes / eb;
     return (ce == 0 || ce > kMaxChunkElems) ? 0 : ce;

@@ -30,9 +30,11 @@ constexpr uint32_t kPairTile = 64;  // chunk pairs per tile of the record-offset
 __host__ __device__ inline uint64_t align16(uint64_t v) { return (v + 15u) & ~uint64_t(15); }
 __host__ __device__ inline uint64_t align4(uint64_t v) { return (v + 3u) & ~uint64_t(3); }
 
-// sign+mantissa bytes per value (bf16 = 1, fp32 = 3) and bytes per value
-__host__ __device__ inline uint32_t raw_bytes_per_value(int dtype) { return dtype == 1 ? 1u : 3u; }
-__host__ __device__ inline uint32_t elem_bytes(int dtype) { return dtype == 1 ? 2u : 4u; }
+// bytes stored raw per value (bf16 1, fp32 3, fp16 1, fp8 0) and bytes per value
+__host__ __device__ inline uint32_t raw_bytes_per_value(int dtype) {
+    return dtype == 2 ? 3u : (dtype == 1 || dtype == 3) ? 1u : 0u;
+}
+__host__ __device__ inline uint32_t elem_bytes(int dtype) { return dtype == 2 ? 4u : (dtype == 1 || dtype == 3) ? 2u : 1u; }
 
 // record bytes of a chunk stored RAW: 16-byte record header + exponents, padded
 __host__ __device__ inline uint64_t raw_record_bytes(uint64_t n_values) { return align16(kRecHeaderBytes + n_values); }

@@ -221,15 +221,42 @@ __device__ inline DecDesc load_dec_desc(const DecDesc *d) {
     return r;
 }
 
-template <int DT>
-__device__ inline uint32_t load_value(const uint8_t *in, uint32_t i) {
-    if (DT == 1) return gload<uint16_t>(in + 2ull * i);
-    return gload<uint32_t>(in + 4ull * i);
-}
+// Value formats (kernel template parameter DT): 1 bf16, 2 fp32, 3 fp16, 4 fp8
+// (e4m3 and e5m2 alike; the header's dtype byte tells them apart).  EB bytes
+// per value, R bytes stored raw per value; the coded symbol is the 8-bit
+// field at bit SYM: the exponent of bf16 and fp32, the high byte of fp16
+// (sign, exponent, top 2 mantissa bits), the whole byte of fp8.
+template <int DT> struct Fmt;
+template <> struct Fmt<1> { static constexpr uint32_t EB = 2, R = 1, SYM = 7; };
+template <> struct Fmt<2> { static constexpr uint32_t EB = 4, R = 3, SYM = 23; };
+template <> struct Fmt<3> { static constexpr uint32_t EB = 2, R = 1, SYM = 8; };
+template <> struct Fmt<4> { static constexpr uint32_t EB = 1, R = 0, SYM = 0; };
 
 template <int DT>
 __device__ inline uint32_t exponent_of(uint32_t v) {
-    return DT == 1 ? (v >> 7) & 0xFFu : (v >> 23) & 0xFFu;
+    return (v >> Fmt<DT>::SYM) & 0xFFu;
+}
+// the raw field of a value (R bytes, little-endian): bf16 sign at bit 7 and 7
+// mantissa bits, fp32 sign at bit 23 and 23 mantissa bits, fp16 the low byte
+template <int DT>
+__device__ inline uint32_t raw_of(uint32_t v) {
+    if (DT == 1) return ((v >> 8) & 0x80u) | (v & 0x7Fu);
+    if (DT == 2) return ((v >> 8) & 0x800000u) | (v & 0x7FFFFFu);
+    if (DT == 3) return v & 0xFFu;
+    return 0u;
+}
+// one value through a buffer resource (zero-extended)
+template <int DT>
+__device__ inline uint32_t bld_value(rsrc_t r, uint32_t off) {
+    if (Fmt<DT>::EB == 1) return __builtin_amdgcn_raw_buffer_load_b8(r, (int)off, 0, 0);
+    if (Fmt<DT>::EB == 2) return __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
+    return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+}
+template <int DT>
+__device__ inline void bst_value(rsrc_t r, uint32_t off, uint32_t v) {
+    if (Fmt<DT>::EB == 1) __builtin_amdgcn_raw_buffer_store_b8((unsigned char)v, r, (int)off, 0, 0);
+    else if (Fmt<DT>::EB == 2) __builtin_amdgcn_raw_buffer_store_b16((unsigned short)v, r, (int)off, 0, 0);
+    else __builtin_amdgcn_raw_buffer_store_b32(v, r, (int)off, 0, 0);
 }
 
 // 32-bit word k (0..15) of a buffer header (bitstream v1; NCCLZ Sec. IV-D2
@@ -366,7 +393,7 @@ __device__ inline void copy_words(rsrc_t rslot, uint8_t *rec, uint32_t wofs, uin
 // wave-uniform arguments; one 16-byte unit (16 exponents) per lane.
 template <int DT>
 __device__ inline void raw_exponents(rsrc_t rin, uint8_t *rec, uint32_t size, uint32_t ni, uint32_t in0, uint32_t lane) {
-    constexpr uint32_t EB = DT == 1 ? 2 : 4;
+    constexpr uint32_t EB = Fmt<DT>::EB;
     const uint32_t nu = (size - kRecHeaderBytes) / 16;
     for (uint32_t u = lane; u < nu; u += 64) {
         uint32_t w[16];
@@ -377,12 +404,9 @@ __device__ inline void raw_exponents(rsrc_t rin, uint8_t *rec, uint32_t size, ui
                 const uint32_t qq[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
                 for (uint32_t t = 0; t < 4; ++t) {
-                    if (DT == 1) {
-                        w[8 * k + 2 * t] = qq[t] & 0xFFFFu;
-                        w[8 * k + 2 * t + 1] = qq[t] >> 16;
-                    } else {
-                        w[4 * k + t] = qq[t];
-                    }
+#pragma unroll
+                    for (uint32_t b = 0; b < 4 / EB; ++b)  // values per dword
+                        w[(16 / EB) * k + (4 / EB) * t + b] = EB == 4 ? qq[t] : (qq[t] >> (8 * EB * b)) & ((1u << (8 * EB)) - 1u);
                 }
             }
         } else {  // the chunk's end: value by value, nothing read past it
@@ -390,7 +414,7 @@ __device__ inline void raw_exponents(rsrc_t rin, uint8_t *rec, uint32_t size, ui
             for (uint32_t k = 0; k < 16; ++k) {
                 const uint32_t e = 16 * u + k;
                 const uint32_t o = e < ni ? in0 + e * EB : kOutOfRange;
-                w[k] = DT == 1 ? bld16(rin, o) : bld32(rin, o);
+                w[k] = bld_value<DT>(rin, o);
             }
         }
         uint32_t v[4] = {0, 0, 0, 0};
@@ -425,8 +449,8 @@ __device__ inline uint32_t enc_quotient(uint32_t x, double r) { return (uint32_t
 
 template <int DT>
 __global__ __launch_bounds__(64) void k_encode(EncParams p) {
-    constexpr uint32_t EB = DT == 1 ? 2 : 4;  // bytes per value
-    constexpr uint32_t R = DT == 1 ? 1 : 3;   // raw sign+mantissa bytes per value
+    constexpr uint32_t EB = Fmt<DT>::EB;      // bytes per value
+    constexpr uint32_t R = Fmt<DT>::R;        // raw bytes per value
     constexpr uint32_t VPL = 16 / EB;         // values per lane per 128-bit load
     constexpr uint32_t VPI = 32 * VPL;        // values per half-wave per pass-1 step
 
@@ -478,15 +502,18 @@ __global__ __launch_bounds__(64) void k_encode(EncParams p) {
         auto split = [&](const uint4 &qv, uint32_t it) __attribute__((always_inline)) {
             const uint32_t w[4] = {qv.x, qv.y, qv.z, qv.w};
             const uint32_t o = smo + it * VPI * R;
-            if (DT == 1) {
+            if (DT == 1 || DT == 3) {
                 uint32_t smw[2] = {0, 0};
 #pragma unroll
                 for (uint32_t k = 0; k < 8; ++k) {
                     const uint32_t v = (w[k >> 1] >> (16 * (k & 1))) & 0xFFFFu;
-                    smw[k >> 2] |= (((v >> 8) & 0x80u) | (v & 0x7Fu)) << (8 * (k & 3));
-                    atomicAdd(&hm[(v >> 7) & 0xFFu], 1u);
+                    smw[k >> 2] |= raw_of<DT>(v) << (8 * (k & 3));
+                    atomicAdd(&hm[exponent_of<DT>(v)], 1u);
                 }
                 __builtin_amdgcn_raw_buffer_store_b64(u32x2{smw[0], smw[1]}, rsmo, (int)o, 0, 0);
+            } else if (DT == 4) {  // the whole byte is the symbol; nothing raw
+#pragma unroll
+                for (uint32_t k = 0; k < 16; ++k) atomicAdd(&hm[(w[k >> 2] >> (8 * (k & 3))) & 0xFFu], 1u);
             } else {
                 uint32_t sm[4];
 #pragma unroll
@@ -502,9 +529,10 @@ __global__ __launch_bounds__(64) void k_encode(EncParams p) {
         // Sets of four vectors (iterations 4s .. 4s + 3), software-pipelined:
         // the next set is loaded while a set is split.  As in the coding pass,
         // the loads are issued in asm and waited for explicitly, so that the
-        // wait does not also cover the sign+mantissa stores: between a set's
-        // loads and its wait lies only the straight-line split of the set
-        // before, with exactly one store per vector.
+        // wait does not also cover the raw-byte stores: between a set's loads
+        // and its wait lies only the straight-line split of the set before,
+        // with exactly one store per vector (none for fp8).
+        constexpr uint32_t kSetStores = R > 0 ? 4 : 0;
         auto asm_load_set = [&](uint32_t st, u32x4(&V)[4]) __attribute__((always_inline)) {
 #pragma unroll
             for (uint32_t k = 0; k < 4; ++k) {
@@ -517,7 +545,8 @@ __global__ __launch_bounds__(64) void k_encode(EncParams p) {
 #pragma unroll
             for (uint32_t k = 0; k < 4; ++k) split(make_uint4(V[k].x, V[k].y, V[k].z, V[k].w), 4 * st + k);
         };
-#define UZIP_WAIT_SET(N, V) asm volatile("s_waitcnt vmcnt(" #N ")" : "+v"(V[0]), "+v"(V[1]), "+v"(V[2]), "+v"(V[3]))
+#define UZIP_WAIT_SET(N, V) \
+    asm volatile("s_waitcnt vmcnt(%4)" : "+v"(V[0]), "+v"(V[1]), "+v"(V[2]), "+v"(V[3]) : "i"(N))
         const uint32_t nsets = fullmin / 4;
         if (nsets > 0) {
             u32x4 A[4], B[4];
@@ -527,11 +556,11 @@ __global__ __launch_bounds__(64) void k_encode(EncParams p) {
             for (uint32_t st = 0;;) {
                 asm_load_set(st + 1, B);
                 split_set(st, A);
-                UZIP_WAIT_SET(4, B);
+                UZIP_WAIT_SET(kSetStores, B);
                 if (++st >= nsets) break;
                 asm_load_set(st + 1, A);
                 split_set(st, B);
-                UZIP_WAIT_SET(4, A);
+                UZIP_WAIT_SET(kSetStores, A);
                 if (++st >= nsets) break;
             }
         }
@@ -553,18 +582,20 @@ __global__ __launch_bounds__(64) void k_encode(EncParams p) {
             for (int k = 0; k < 4; ++k) w[k] = 0;
             for (uint32_t k = 0; k < VPL; ++k) {
                 const uint32_t o = i0 + k < ni ? in0 + (i0 + k) * EB : kOutOfRange;
-                if (DT == 1) w[k >> 1] |= bld16(rin, o) << (16 * (k & 1));
-                else w[k] = bld32(rin, o);
+                w[k / (4 / EB)] |= bld_value<DT>(rin, o) << (8 * EB * (k % (4 / EB)));
             }
         }
-        if (DT == 1) {
+        if (DT == 4) {
+#pragma unroll
+            for (uint32_t k = 0; k < 16; ++k)
+                if (full || i0 + k < ni) atomicAdd(&hist[(w[k >> 2] >> (8 * (k & 3))) & 0xFFu], 1u);
+        } else if (DT == 1 || DT == 3) {
             uint32_t smw[2] = {0, 0};
 #pragma unroll
             for (uint32_t k = 0; k < 8; ++k) {
                 const uint32_t v = (w[k >> 1] >> (16 * (k & 1))) & 0xFFFFu;
-                const uint32_t sm = ((v >> 8) & 0x80u) | (v & 0x7Fu);
-                smw[k >> 2] |= sm << (8 * (k & 3));
-                if (full || i0 + k < ni) atomicAdd(&hist[(v >> 7) & 0xFFu], 1u);
+                smw[k >> 2] |= raw_of<DT>(v) << (8 * (k & 3));
+                if (full || i0 + k < ni) atomicAdd(&hist[exponent_of<DT>(v)], 1u);
             }
             if (full) {
                 gstore<uint2>(sm_out + i0, make_uint2(smw[0], smw[1]));
@@ -710,7 +741,7 @@ __global__ __launch_bounds__(64) void k_encode(EncParams p) {
             act = (alive0 && vals0 > 32 * t ? half_prefix_mask(vals0 - 32 * t, 0) : 0ull) |
                   (alive1 && vals1 > 32 * t ? half_prefix_mask(vals1 - 32 * t, 1) : 0ull);
         uint32_t ex;  // the value's exponent
-        asm("v_bfe_u32 %0, %1, %2, 8" : "=v"(ex) : "v"(v), "i"(DT == 1 ? 7 : 23));
+        asm("v_bfe_u32 %0, %1, %2, 8" : "=v"(ex) : "v"(v), "i"(Fmt<DT>::SYM));
         const uint4 te = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint8_t *>(tab) + (ex << 4));
         uint64_t m = lanes_lt(te.x & 0xFFFFu, x >> 20) & act;  // x >= f * 2^20
         uint32_t lo = (uint32_t)m, hi = (uint32_t)(m >> 32);
@@ -771,7 +802,9 @@ __global__ __launch_bounds__(64) void k_encode(EncParams p) {
         const uint32_t o = bb >= 0 ? in0 + ((uint32_t)bb * 8 * 32 + lj) * EB : kOutOfRange;
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-            if (DT == 1)
+            if (EB == 1)
+                asm volatile("buffer_load_ubyte %0, %1, %2, 0 offen offset:%3" : "=v"(V[k]) : "v"(o), "s"(rin), "i"(k * 32 * EB));
+            else if (EB == 2)
                 asm volatile("buffer_load_ushort %0, %1, %2, 0 offen offset:%3" : "=v"(V[k]) : "v"(o), "s"(rin), "i"(k * 32 * EB));
             else
                 asm volatile("buffer_load_dword %0, %1, %2, 0 offen offset:%3" : "=v"(V[k]) : "v"(o), "s"(rin), "i"(k * 32 * EB));
@@ -785,7 +818,7 @@ __global__ __launch_bounds__(64) void k_encode(EncParams p) {
             const uint32_t o = in0 + ((uint32_t)b * 8 * 32 + lj) * EB;
             uint32_t V[8];
 #pragma unroll
-            for (int k = 0; k < 8; ++k) V[k] = DT == 1 ? bld16(rin, o + k * 32 * EB) : bld32(rin, o + k * 32 * EB);
+            for (int k = 0; k < 8; ++k) V[k] = bld_value<DT>(rin, o + k * 32 * EB);
 #pragma unroll
             for (int k = 7; k >= 0; --k) step(b, k, V[k], true, 0ull);
             --b;
@@ -844,8 +877,8 @@ constexpr uint32_t kCompactPairs = 4;
 
 template <int DT>
 __global__ __launch_bounds__(128 * kCompactPairs) void k_compact(EncParams p) {
-    constexpr uint32_t EB = DT == 1 ? 2 : 4;
-    constexpr uint32_t R = DT == 1 ? 1 : 3;
+    constexpr uint32_t EB = Fmt<DT>::EB;
+    constexpr uint32_t R = Fmt<DT>::R;
     __shared__ uint32_t s_ticket;
     const uint32_t lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     if (threadIdx.x == 0) s_ticket = __hip_atomic_fetch_add(p.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1033,20 +1066,27 @@ __global__ void k_dec_validate(DecParams p) {
 // stored RAW are copied in a separate loop.
 template <int DT>
 __device__ inline uint32_t bload_sm(rsrc_t r, uint32_t off) {
-    if (DT == 1) return bld8(r, off);
+    if (Fmt<DT>::R == 0) return 0u;
+    if (Fmt<DT>::R == 1) return bld8(r, off);
     return bld8(r, off) | (bld8(r, off + 1) << 8) | (bld8(r, off + 2) << 16);
 }
 
+// inverse of the split: a value from its symbol and its raw field
 template <int DT>
 __device__ inline uint32_t merge_value(uint32_t ex, uint32_t smv) {
     if (DT == 1) return ((smv & 0x80u) << 8) | (ex << 7) | (smv & 0x7Fu);
-    return ((smv & 0x800000u) << 8) | (ex << 23) | (smv & 0x7FFFFFu);
+    if (DT == 2) return ((smv & 0x800000u) << 8) | (ex << 23) | (smv & 0x7FFFFFu);
+    if (DT == 3) return (ex << 8) | (smv & 0xFFu);
+    return ex;
 }
 
 template <int DT>
 __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
-    constexpr uint32_t EB = DT == 1 ? 2 : 4;
-    constexpr uint32_t R = DT == 1 ? 1 : 3;
+    constexpr uint32_t EB = Fmt<DT>::EB;
+    constexpr uint32_t R = Fmt<DT>::R;
+    // bf16 and fp16: 2-byte values with one raw byte, which share the main
+    // loop below (raw bytes by dword and bpermute, two steps per store)
+    constexpr bool kB16 = DT == 1 || DT == 3;
     // one LDS array, so that the slot table sits at address 0 and a slot's
     // address is a single and-or of the state
     __shared__ __align__(16) uint32_t s_dec[2 * kTableSize / 4 + 2 * 256];
@@ -1187,7 +1227,7 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
         // loaded before the word window so that many memory operations lie
         // between these loads and their first use
         const uint32_t smd0 = (h ? vals0 : 0u) + 4 * lj;
-        const uint32_t D0first = DT == 1 ? bld32(rsm, smd0) : 0u, D1first = DT == 1 ? bld32(rsm, smd0 + 128) : 0u;
+        const uint32_t D0first = kB16 ? bld32(rsm, smd0) : 0u, D1first = kB16 ? bld32(rsm, smd0 + 128) : 0u;
         // Refill: at every step, after its own refill decision, each lane loads
         // the pair it takes at its next refill (block end lim, 32 words past
         // it, pair position 2i) into NX[t mod 4]; the load is consumed four
@@ -1207,7 +1247,7 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
         const uint32_t rbase = wstart + 64 + 4 * (lj & 15u);          // byte offset of its next pair = 2 lim + rbase
         uint32_t NX[4], NB[4];
         NX[0] = NX[1] = NX[2] = NX[3] = bld32(rrec, 2 * lim + rbase); // words 64 + 2lj, 65 + 2lj
-        NB[0] = NB[1] = NB[2] = NB[3] = DT == 1 ? 0u : bld32(rrec, 2 * lim + rbase + 128);
+        NB[0] = NB[1] = NB[2] = NB[3] = kB16 ? 0u : bld32(rrec, 2 * lim + rbase + 128);
         uint64_t R1 = 0, R2 = 0, R3 = 0;  // bf16: refill masks of the last three steps
         uint32_t age = 4;                  // fp32: steps since the lane's last refill
         const uint32_t lanebits = (h << 5) << 2;
@@ -1254,7 +1294,7 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
             // (plain selects: the mask comes from a vector compare, and the
             // compiler spaces its reads as the hardware requires)
             const bool used_up = offv >= lim;
-            if (DT == 1) {
+            if (kB16) {
                 const uint64_t um = __builtin_amdgcn_ballot_w64(used_up);
                 const uint64_t stale = um & (R2 | R3);
                 R3 = R2;
@@ -1275,7 +1315,7 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
             }
             lim += used_up ? 64u : 0u;
             NX[par] = bld32(rrec, 2 * lim + rbase);
-            if (DT != 1) NB[par] = bld32(rrec, 2 * lim + rbase + 128);
+            if (!kB16) NB[par] = bld32(rrec, 2 * lim + rbase + 128);
             if (DT == 1) {
                 // sign (bit 7 of sm, copied to bit 15) and mantissa bits 0-6
                 // from sp, exponent (em bits 12-19) to bits 7-14; the store
@@ -1284,15 +1324,24 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
                 asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(v) : "s"(0x807Fu), "v"(sp), "v"(em >> 5));
                 if (store) bst16(rout, out_lane + t * 32 * EB, v);
                 return v;
-            } else {
+            } else if (DT == 3) {
+                // the low byte from sp, the symbol (em bits 12-19) to bits 8-15
+                uint32_t v;
+                asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(v) : "s"(0x00FFu), "v"(sp), "v"(em >> 4));
+                if (store) bst16(rout, out_lane + t * 32 * EB, v);
+                return v;
+            } else if (DT == 2) {
                 // sign (bit 23 of sm) to bit 31, mantissa bits 0-22, exponent to bits 23-30
                 const uint32_t sx = sp | ((sp & 0x800000u) << 8), ex = em << 11;
                 bst32(rout, out_lane + t * 32 * EB, (sx & 0x807FFFFFu) | (ex & ~0x807FFFFFu));
                 return 0u;
+            } else {
+                bst_value<DT>(rout, out_lane + t * 32 * EB, em >> 12);  // the symbol is the value
+                return 0u;
             }
         };
         uint32_t t = 0;
-        if (DT == 1) {
+        if (kB16) {
             // bf16 sign+mantissa bytes: one dword per lane per group of 4
             // steps (the 128 bytes of the group), two groups ahead; step s of
             // a group takes byte lj & 3 of lane 8s + lj / 4 of its half with
@@ -1335,6 +1384,12 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
                 D1 = bld32(rsm, smd0 + (t + 20) * 32);
                 group8(t + 8, N0, N1);
             }
+        } else if (DT == 4) {
+            // fp8: no raw bytes
+            for (; t < Tmain; t += 8) {
+#pragma unroll
+                for (int u = 0; u < 8; ++u) step(t + u, runm, false, 0u, u & 3, true);
+            }
         } else {
             constexpr int kSmAhead = 8;  // sign+mantissa bytes are loaded this many steps ahead
             uint32_t smq[kSmAhead];
@@ -1359,7 +1414,7 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
                 const uint32_t tt = t + u;
                 const uint64_t act = (run0 && ni0 > 32 * tt ? half_prefix_mask(ni0 - 32 * tt, 0) : 0ull) |
                                      (run1 && ni1 > 32 * tt ? half_prefix_mask(ni1 - 32 * tt, 1) : 0ull);
-                step(tt, act, true, DT == 1 ? __umul24(smt[u], 0x101u) : smt[u], u & 3, true);
+                step(tt, act, true, DT == 1 ? __umul24(smt[u], 0x101u) : smt[u], u & 3, true);  // (bf16: sign byte in bits 8-15 too)
             }
         }
         const bool endbad = half_mask(__ballot(rans_run && (x != kStateLow || offv != nw)), h) != 0;
@@ -1369,8 +1424,7 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
             const uint32_t ob = (h ? vals0 : 0u) * EB, sb = (h ? vals0 : 0u) * R;
             for (uint32_t i = lj; i < ni; i += 32) {
                 const uint32_t v = merge_value<DT>(bld8(rrec, rel + kRecHeaderBytes + i), bload_sm<DT>(rsm, sb + i * R));
-                if (DT == 1) bst16(rout, ob + i * EB, v);
-                else bst32(rout, ob + i * EB, v);
+                bst_value<DT>(rout, ob + i * EB, v);
             }
         }
         if (h < nch && !ok && lj == 0) gstore<uint32_t>(p.status + b, 3u);
@@ -1383,18 +1437,29 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
 // ---------------------------------------------------------------------------
 thread_local ProfileEvents g_profile;
 
+// kernel template for a dtype code: bf16 1, fp32 2, fp16 3, both fp8 codes 4
+static int kernel_format(int dtype) { return dtype <= 3 ? dtype : 4; }
+
 hipError_t launch_compress(const EncParams &ep, hipStream_t stream) {
     uint64_t threads = ep.total_pairs > ep.nbuf ? ep.total_pairs : ep.nbuf;
     k_prepare<<<dim3((uint32_t)((threads + 255) / 256)), dim3(256), 0, stream>>>(ep);
     if (ep.total_pairs > 0) {
         const dim3 grid((uint32_t)ep.total_pairs);
         if (g_profile.start) (void)hipEventRecord(g_profile.start, stream);
-        if (ep.dtype == 1) k_encode<1><<<grid, dim3(64), 0, stream>>>(ep);
-        else k_encode<2><<<grid, dim3(64), 0, stream>>>(ep);
+        switch (kernel_format(ep.dtype)) {
+        case 1: k_encode<1><<<grid, dim3(64), 0, stream>>>(ep); break;
+        case 2: k_encode<2><<<grid, dim3(64), 0, stream>>>(ep); break;
+        case 3: k_encode<3><<<grid, dim3(64), 0, stream>>>(ep); break;
+        default: k_encode<4><<<grid, dim3(64), 0, stream>>>(ep); break;
+        }
         if (g_profile.stop) (void)hipEventRecord(g_profile.stop, stream);
         const dim3 cgrid((uint32_t)((ep.total_pairs + kCompactPairs - 1) / kCompactPairs));
-        if (ep.dtype == 1) k_compact<1><<<cgrid, dim3(128 * kCompactPairs), 0, stream>>>(ep);
-        else k_compact<2><<<cgrid, dim3(128 * kCompactPairs), 0, stream>>>(ep);
+        switch (kernel_format(ep.dtype)) {
+        case 1: k_compact<1><<<cgrid, dim3(128 * kCompactPairs), 0, stream>>>(ep); break;
+        case 2: k_compact<2><<<cgrid, dim3(128 * kCompactPairs), 0, stream>>>(ep); break;
+        case 3: k_compact<3><<<cgrid, dim3(128 * kCompactPairs), 0, stream>>>(ep); break;
+        default: k_compact<4><<<cgrid, dim3(128 * kCompactPairs), 0, stream>>>(ep); break;
+        }
     }
     return hipGetLastError();
 }
@@ -1407,8 +1472,12 @@ hipError_t launch_decompress(const DecParams &vp, const DecodeParams &dp, int dt
         const uint64_t pairs = (max_chunks + 1) / 2 + vp.nbuf;  // upper bound of the chunk pairs
         const uint64_t grid = pairs < 8192 ? pairs : 8192;
         if (g_profile.start) (void)hipEventRecord(g_profile.start, stream);
-        if (dtype == 1) k_decode<1><<<dim3((uint32_t)grid), dim3(64), 0, stream>>>(dp);
-        else k_decode<2><<<dim3((uint32_t)grid), dim3(64), 0, stream>>>(dp);
+        switch (kernel_format(dtype)) {
+        case 1: k_decode<1><<<dim3((uint32_t)grid), dim3(64), 0, stream>>>(dp); break;
+        case 2: k_decode<2><<<dim3((uint32_t)grid), dim3(64), 0, stream>>>(dp); break;
+        case 3: k_decode<3><<<dim3((uint32_t)grid), dim3(64), 0, stream>>>(dp); break;
+        default: k_decode<4><<<dim3((uint32_t)grid), dim3(64), 0, stream>>>(dp); break;
+        }
         if (g_profile.stop) (void)hipEventRecord(g_profile.stop, stream);
     }
     return hipGetLastError();

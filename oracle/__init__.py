@@ -24,6 +24,12 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 
 BF16 = 1
 FP32 = 2
+FP16 = 3
+FP8_E4M3 = 4
+FP8_E5M2 = 5
+DTYPES = (BF16, FP32, FP16, FP8_E4M3, FP8_E5M2)
+_ELEM = {BF16: np.uint16, FP32: np.uint32, FP16: np.uint16, FP8_E4M3: np.uint8, FP8_E5M2: np.uint8}
+_RAW = {BF16: 1, FP32: 3, FP16: 1, FP8_E4M3: 0, FP8_E5M2: 0}
 OK, INVALID, CAPACITY, CORRUPT = 0, 1, 2, 3
 
 LANES = 32
@@ -83,16 +89,16 @@ def _p(a: np.ndarray):
 
 
 def _bits(dtype: int, values) -> np.ndarray:
-    """Bit patterns as a contiguous uint16 (bf16) or uint32 (fp32) array."""
+    """Bit patterns as a contiguous uint8/16/32 array (the dtype's width)."""
     a = np.ascontiguousarray(values)
-    want = np.uint16 if dtype == BF16 else np.uint32
+    want = _ELEM[dtype]
     if a.dtype.itemsize != np.dtype(want).itemsize:
         raise ValueError("expected %d-byte elements, got %s" % (np.dtype(want).itemsize, a.dtype))
     return a.view(want).reshape(-1)
 
 
 def raw_bytes_per_value(dtype: int) -> int:
-    return 1 if dtype == BF16 else 3
+    return _RAW[dtype]
 
 
 def chunk_elems(dtype: int, chunk_bytes: int = 0) -> int:
@@ -100,20 +106,23 @@ def chunk_elems(dtype: int, chunk_bytes: int = 0) -> int:
 
 
 def split(dtype: int, values):
-    """Exponent bytes (n,) and sign+mantissa bytes (r*n,) of each value."""
+    """Coded bytes (n,) and raw bytes (r*n,) of each value (the exponent and the
+    sign+mantissa for bf16 and fp32)."""
     v = _bits(dtype, values)
     n = v.size
     e = np.empty(n, np.uint8)
-    sm = np.empty(n * raw_bytes_per_value(dtype), np.uint8)
+    sm = np.empty(max(n * raw_bytes_per_value(dtype), 1), np.uint8)
     lib().orc_split(dtype, _p(v), n, _p(e), _p(sm))
-    return e, sm
+    return e, sm[: n * raw_bytes_per_value(dtype)]
 
 
 def merge(dtype: int, e, sm) -> np.ndarray:
     e = np.ascontiguousarray(e, np.uint8)
     sm = np.ascontiguousarray(sm, np.uint8)
     n = e.size
-    out = np.empty(n, np.uint16 if dtype == BF16 else np.uint32)
+    out = np.empty(n, _ELEM[dtype])
+    if sm.size == 0:
+        sm = np.zeros(1, np.uint8)
     lib().orc_merge(dtype, _p(e), _p(sm), n, _p(out))
     return out
 
@@ -189,13 +198,13 @@ def compress(dtype: int, values, chunk_bytes: int = 0) -> np.ndarray:
 
 
 def decompress(buf, dtype: int, n: int):
-    """Returns (status, bit patterns uint16/uint32 of length n)."""
+    """Returns (status, bit patterns of the dtype's width, length n)."""
     b = np.ascontiguousarray(buf, np.uint8)
     if b.size == 0:
         b = np.zeros(1, np.uint8)
         nbytes = 0
     else:
         nbytes = b.size
-    out = np.zeros(max(n, 1), np.uint16 if dtype == BF16 else np.uint32)
+    out = np.zeros(max(n, 1), _ELEM[dtype])
     st = lib().orc_decompress(_p(b), nbytes, dtype, n, _p(out))
     return int(st), out[:n]

@@ -55,6 +55,9 @@
 
 #define ORC_DT_BF16 1
 #define ORC_DT_FP32 2
+#define ORC_DT_FP16 3
+#define ORC_DT_FP8_E4M3 4
+#define ORC_DT_FP8_E5M2 5
 
 enum { ORC_OK = 0, ORC_INVALID = 1, ORC_CAPACITY = 2, ORC_CORRUPT = 3 };
 
@@ -81,16 +84,30 @@ static uint64_t get64(const uint8_t *p) {
     return v;
 }
 
-/* bytes of sign+mantissa stored raw per value, and bytes per value */
-static int orc_raw_bytes(int dtype) { return dtype == ORC_DT_BF16 ? 1 : (dtype == ORC_DT_FP32 ? 3 : 0); }
-static int orc_elem_bytes(int dtype) { return dtype == ORC_DT_BF16 ? 2 : (dtype == ORC_DT_FP32 ? 4 : 0); }
+/* bytes stored raw per value, and bytes per value (0: not a dtype) */
+static int orc_raw_bytes(int dtype) {
+    switch (dtype) {
+    case ORC_DT_BF16: return 1;
+    case ORC_DT_FP32: return 3;
+    case ORC_DT_FP16: return 1;
+    default: return 0; /* fp8: the whole byte is coded */
+    }
+}
+static int orc_elem_bytes(int dtype) {
+    switch (dtype) {
+    case ORC_DT_BF16: case ORC_DT_FP16: return 2;
+    case ORC_DT_FP32: return 4;
+    case ORC_DT_FP8_E4M3: case ORC_DT_FP8_E5M2: return 1;
+    default: return 0;
+    }
+}
 
-/* chunk_bytes 0 selects the per-dtype default (64 KiB bf16, 256 KiB fp32).
+/* chunk_bytes 0 selects the per-dtype default (256 KiB fp32, 64 KiB others).
  * Returns chunk_elems, or 0 when the chunk size is invalid. */
 uint64_t orc_chunk_elems(int dtype, uint64_t chunk_bytes) {
     int eb = orc_elem_bytes(dtype);
     if (eb == 0) return 0;
-    if (chunk_bytes == 0) chunk_bytes = dtype == ORC_DT_BF16 ? 65536u : 262144u;
+    if (chunk_bytes == 0) chunk_bytes = dtype == ORC_DT_FP32 ? 262144u : 65536u;
     if (chunk_bytes % (uint64_t)(32 * eb) != 0) return 0;
     uint64_t ce = chunk_bytes / (uint64_t)eb;
     if (ce == 0 || ce > ORC_MAX_CHUNK_ELEMS) return 0;
@@ -101,9 +118,26 @@ uint64_t orc_chunk_elems(int dtype, uint64_t chunk_bytes) {
  * bf16 word v: exponent e = bits 14..7; sign+mantissa byte sm keeps the sign
  * as its top bit and the 7 mantissa bits below it.
  * fp32 word v: exponent e = bits 30..23; sm is 24 bits: sign at bit 23 and
- * the 23 mantissa bits below, stored as 3 bytes little-endian. */
+ * the 23 mantissa bits below, stored as 3 bytes little-endian.
+ * fp16 and fp8 (the other types of UCCL-Zip Fig. 13; the pages give no
+ * layout for them): the coded symbol is the byte that holds the exponent and
+ * the remaining bytes are stored raw.  fp16 word v: e = bits 15..8 (sign, the
+ * 5 exponent bits, the top 2 mantissa bits), sm = bits 7..0.  fp8 byte v:
+ * e = v, nothing raw.  (Neither has a byte-aligned field of exponent bits
+ * alone; the sign and mantissa bits coded along are near-uniform and cost
+ * about what they would raw.) */
 void orc_split(int dtype, const void *in, uint64_t n, uint8_t *e_out, uint8_t *sm_out) {
-    if (dtype == ORC_DT_BF16) {
+    if (dtype == ORC_DT_FP16) {
+        const uint16_t *v = (const uint16_t *)in;
+        for (uint64_t i = 0; i < n; ++i) {
+            e_out[i] = (uint8_t)(v[i] >> 8);
+            sm_out[i] = (uint8_t)(v[i] & 0xFFu);
+        }
+    } else if (dtype == ORC_DT_FP8_E4M3 || dtype == ORC_DT_FP8_E5M2) {
+        const uint8_t *v = (const uint8_t *)in;
+        for (uint64_t i = 0; i < n; ++i) e_out[i] = v[i];
+        (void)sm_out;
+    } else if (dtype == ORC_DT_BF16) {
         const uint16_t *v = (const uint16_t *)in;
         for (uint64_t i = 0; i < n; ++i) {
             uint32_t x = v[i];
@@ -125,7 +159,14 @@ void orc_split(int dtype, const void *in, uint64_t n, uint8_t *e_out, uint8_t *s
 
 /* inverse of orc_split */
 void orc_merge(int dtype, const uint8_t *e, const uint8_t *sm, uint64_t n, void *out) {
-    if (dtype == ORC_DT_BF16) {
+    if (dtype == ORC_DT_FP16) {
+        uint16_t *v = (uint16_t *)out;
+        for (uint64_t i = 0; i < n; ++i) v[i] = (uint16_t)(((uint32_t)e[i] << 8) | sm[i]);
+    } else if (dtype == ORC_DT_FP8_E4M3 || dtype == ORC_DT_FP8_E5M2) {
+        uint8_t *v = (uint8_t *)out;
+        for (uint64_t i = 0; i < n; ++i) v[i] = e[i];
+        (void)sm;
+    } else if (dtype == ORC_DT_BF16) {
         uint16_t *v = (uint16_t *)out;
         for (uint64_t i = 0; i < n; ++i) {
             uint32_t s = sm[i];
@@ -358,10 +399,11 @@ int orc_compress(int dtype, const void *in, uint64_t n, uint64_t chunk_bytes, ui
     uint64_t C, sm_off, exp_off;
     orc_layout(dtype, n, ce, &C, &sm_off, &exp_off);
     uint8_t *e = (uint8_t *)malloc((size_t)(n ? n : 1));
-    uint8_t *sm = (uint8_t *)malloc((size_t)(n ? n * (uint64_t)r : 1));
+    const uint64_t sm_bytes = n * (uint64_t)r;
+    uint8_t *sm = (uint8_t *)malloc((size_t)(sm_bytes > 0 ? sm_bytes : 1));
     orc_split(dtype, in, n, e, sm);
     memset(out, 0, (size_t)exp_off);
-    memcpy(out + sm_off, sm, (size_t)(n * (uint64_t)r));
+    memcpy(out + sm_off, sm, (size_t)sm_bytes);
     uint64_t off = 0;
     put64(out + ORC_HDR_BYTES, 0);
     for (uint64_t i = 0; i < C; ++i) {
@@ -443,7 +485,7 @@ static int orc_decode_record(const uint8_t *rec, uint64_t rec_len, uint64_t ni, 
  * ORC_CORRUPT for any inconsistency; never reads outside in[0, in_bytes). */
 int orc_decompress(const uint8_t *in, uint64_t in_bytes, int dtype, uint64_t n, void *out) {
     int r = orc_raw_bytes(dtype);
-    if (r == 0) return ORC_INVALID;
+    if (orc_elem_bytes(dtype) == 0) return ORC_INVALID;
     if (in_bytes < ORC_HDR_BYTES) return ORC_CORRUPT;
     /* V1: magic, version and the fixed coder parameters */
     if (get32(in) != ORC_MAGIC || get16(in + 4) != ORC_VERSION) return ORC_CORRUPT;

@@ -39,7 +39,7 @@ def test_library_has_gfx950_code_object():
     assert b"amdgcn-amd-amdhsa--gfx950" in open(uz.LIB_PATH, "rb").read()
 
 
-@pytest.mark.parametrize("dtype", [uz.UZIP_BF16, uz.UZIP_FP32])
+@pytest.mark.parametrize("dtype", [uz.UZIP_BF16, uz.UZIP_FP32, uz.UZIP_FP16, uz.UZIP_FP8_E4M3, uz.UZIP_FP8_E5M2])
 @pytest.mark.parametrize("chunk_bytes", [0, 4096, 65536, 262144])
 def test_max_compressed_size_matches_oracle(dtype, chunk_bytes):
     for n in [0, 1, 31, 32, 33, 1000, 32767, 32768, 32769, 65536 * 3 + 17, 268_435_456, 8_030_257_152]:
@@ -47,9 +47,11 @@ def test_max_compressed_size_matches_oracle(dtype, chunk_bytes):
 
 
 def test_size_functions_reject_invalid_arguments():
-    assert uz.uzip_max_compressed_size(3, 100, 0) == 0
+    assert uz.uzip_max_compressed_size(0, 100, 0) == 0 and uz.uzip_max_compressed_size(6, 100, 0) == 0
     assert uz.uzip_max_compressed_size(uz.UZIP_BF16, 100, 100) == 0
     assert uz.uzip_max_compressed_size(uz.UZIP_BF16, 100, (1 << 21) + 64) == 0
+    assert uz.uzip_max_compressed_size(uz.UZIP_FP8_E4M3, 100, 1 << 20) > 0  # 2^20 values per chunk at most
+    assert uz.uzip_max_compressed_size(uz.UZIP_FP8_E4M3, 100, (1 << 20) + 32) == 0
     assert uz.uzip_workspace_size(uz.UZIP_FP32, 100, 8) == 0
     assert uz.uzip_workspace_size(uz.UZIP_BF16, 0, 0) > 0
     assert uz.uzip_workspace_size_batched(uz.UZIP_BF16, [], 0) == 0

@@ -19,14 +19,28 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
 
-def _bits_tensor(bits: np.ndarray) -> torch.Tensor:
-    if bits.dtype == np.uint16:
-        return torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).to(DEV)
-    return torch.from_numpy(bits.view(np.int32).copy()).view(torch.float32).to(DEV)
+_VIEW = {np.uint8: torch.uint8, np.uint16: torch.int16, np.uint32: torch.int32}
+_ORC = {torch.bfloat16: orc.BF16, torch.float32: orc.FP32, torch.float16: orc.FP16,
+        torch.float8_e4m3fn: orc.FP8_E4M3, torch.float8_e5m2: orc.FP8_E5M2}
 
 
-def _code(bits):
-    return orc.BF16 if bits.dtype == np.uint16 else orc.FP32
+def _default_dtype(bits: np.ndarray) -> torch.dtype:
+    return {np.uint16: torch.bfloat16, np.uint32: torch.float32}[bits.dtype.type]
+
+
+def _bits_tensor(bits: np.ndarray, tdtype: torch.dtype = None) -> torch.Tensor:
+    tdtype = tdtype or _default_dtype(bits)
+    raw = torch.from_numpy(bits.view(np.int16 if bits.dtype == np.uint16 else
+                                     np.int32 if bits.dtype == np.uint32 else np.uint8).copy())
+    return raw.view(tdtype).to(DEV)
+
+
+def _code(bits, tdtype: torch.dtype = None):
+    return _ORC[tdtype or _default_dtype(bits)]
+
+
+def _int_view(t: torch.Tensor) -> torch.Tensor:
+    return t.view({1: torch.uint8, 2: torch.int16, 4: torch.int32}[t.element_size()])
 
 
 def gpu_compress(t: torch.Tensor, chunk_bytes: int = 0) -> np.ndarray:
@@ -44,11 +58,13 @@ def gpu_decompress(buf: np.ndarray, dtype: torch.dtype, n: int, in_bytes=None):
     return out, int(st.item())
 
 
-def check_parity(bits: np.ndarray, chunk_bytes: int = 0):
-    """GPU bytes == oracle bytes, and both decode to the input on the GPU."""
-    t = _bits_tensor(bits)
+def check_parity(bits: np.ndarray, chunk_bytes: int = 0, tdtype: torch.dtype = None):
+    """GPU bytes == oracle bytes, and both decode to the input on the GPU.
+    `bits` is uint16 (bf16 unless `tdtype` says float16), uint32 (fp32) or
+    uint8 (one of the float8 formats, named by `tdtype`)."""
+    t = _bits_tensor(bits, tdtype)
     got = gpu_compress(t, chunk_bytes)
-    want = orc.compress(_code(bits), bits, chunk_bytes)
+    want = orc.compress(_code(bits, tdtype), bits, chunk_bytes)
     if not np.array_equal(got, want):
         hint = "sizes %d vs %d" % (got.size, want.size)
         if got.size == want.size:
@@ -56,8 +72,7 @@ def check_parity(bits: np.ndarray, chunk_bytes: int = 0):
         pytest.fail("compressed bytes differ from the oracle: " + hint)
     out, st = gpu_decompress(got, t.dtype, bits.size)
     assert st == 0
-    assert torch.equal(out.view(torch.int16 if bits.dtype == np.uint16 else torch.int32),
-                       t.view(torch.int16 if bits.dtype == np.uint16 else torch.int32))
+    assert torch.equal(_int_view(out), _int_view(t))
     return got
 
 

@@ -8,8 +8,8 @@ sync (UCCL-Zip Fig. 10, Fig. 12), gradients (NCCLZ Sec. V), inference
 activations / KV blocks (UCCL-Zip Fig. 11).  None of the pages' datasets or
 checkpoints is used; these generators stand in for them.
 
-All generators return torch tensors of dtype bfloat16 or float32 on the
-requested device.  Large inputs are generated on the GPU with torch's
+All generators return torch tensors of dtype bfloat16, float16, float32 or
+one of the two float8 formats on the requested device.  Large inputs are generated on the GPU with torch's
 device generator (seeded); the same call on a CPU device gives a different
 (but equally seeded) stream, so parity tests always compare both codecs on
 the very bytes one generator produced.  Special values (Inf, NaN payloads,
@@ -153,10 +153,42 @@ def small_message_batch(num_buffers: int = SMALL_BATCH_BUFFERS, hidden: int = SM
     return out
 
 
+FP16_ACT_N = 268_435_456
+FP8_WEIGHT_N = 268_435_456
+FP8_BLOCK = 8192
+
+
+def fp16_activations(n: int = FP16_ACT_N, device="cpu", seed: int = 5, row: int = 8192) -> torch.Tensor:
+    """fp16 activation / KV-block tensor (the UCCL-Zip inference payloads move
+    fp16 and bf16 tensors; Fig. 13 lists float16): rows of `row` values,
+    x = N(0, 1) * r with r = exp(N(0, 0.5^2)) per row."""
+    g = _gen(device, seed)
+    nrow = max(1, math.ceil(n / row))
+    r = torch.exp(0.5 * torch.randn(nrow, generator=g, device=device, dtype=torch.float32))
+    x = torch.randn(nrow * row, generator=g, device=device, dtype=torch.float32).view(nrow, row)
+    x.mul_(r.unsqueeze(1))
+    return x.view(-1)[:n].to(torch.float16)
+
+
+def fp8_weights(n: int = FP8_WEIGHT_N, device="cpu", seed: int = 6, fmt: torch.dtype = torch.float8_e4m3fn) -> torch.Tensor:
+    """fp8 weight tensor (Fig. 13 lists float8_e4m3fn and float8_e5m2): N(0, 1)
+    values scaled per block of 8,192 so that the block's largest magnitude
+    maps to the format's largest finite value (block-scaled quantization),
+    then rounded to the format."""
+    g = _gen(device, seed)
+    fmax = torch.finfo(fmt).max
+    nblk = max(1, math.ceil(n / FP8_BLOCK))
+    x = torch.randn(nblk * FP8_BLOCK, generator=g, device=device, dtype=torch.float32).view(nblk, FP8_BLOCK)
+    x.mul_(fmax / x.abs().amax(dim=1, keepdim=True))
+    return x.view(-1)[:n].to(fmt)
+
+
 def bits_numpy(t: torch.Tensor) -> np.ndarray:
-    """Bit patterns of a bf16/fp32 tensor as a CPU uint16/uint32 numpy array."""
-    if t.dtype == torch.bfloat16:
+    """Bit patterns of a bf16/fp16/fp32/fp8 tensor as a CPU uint16/uint32/uint8 numpy array."""
+    if t.dtype in (torch.bfloat16, torch.float16):
         return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16).reshape(-1)
     if t.dtype == torch.float32:
         return t.contiguous().view(torch.int32).cpu().numpy().view(np.uint32).reshape(-1)
-    raise TypeError("expected bfloat16 or float32, got %s" % t.dtype)
+    if t.dtype in (torch.float8_e4m3fn, torch.float8_e5m2):
+        return t.contiguous().view(torch.uint8).cpu().numpy().reshape(-1)
+    raise TypeError("expected a bf16, fp16, fp32 or fp8 tensor, got %s" % t.dtype)
