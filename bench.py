@@ -17,7 +17,8 @@ JSON line:
 
 Workloads (--workload): grad_bucket (default: 268,435,456 bf16 values,
 512 MiB, 64 KiB chunks), pr1, fp32_grad, llama8b (290 buffers, batched),
-small_batch (4,096 buffers, batched).
+small_batch (4,096 buffers, batched), fp16_act (268,435,456 fp16 values),
+fp8_e4m3 and fp8_e5m2 (268,435,456 block-scaled fp8 weights each).
 """
 from __future__ import annotations
 
@@ -33,6 +34,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+VALUE_DTYPE = {1: "bf16", 2: "fp32", 3: "fp16", 4: "fp8_e4m3fn", 5: "fp8_e5m2"}
 # HBM bytes per launch from two rocprofv3 passes (FETCH_SIZE, then WRITE_SIZE)
 # on the gradient bucket, reads scaled by 2.000 and writes by 1.000 (what the
 # same counters read for the benchmark's plain 512 MiB device copy); the
@@ -57,7 +59,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="grad_bucket",
-                    choices=["grad_bucket", "pr1", "fp32_grad", "llama8b", "small_batch"])
+                    choices=["grad_bucket", "pr1", "fp32_grad", "llama8b", "small_batch", "fp16_act", "fp8_e4m3",
+                             "fp8_e5m2"])
+    ap.add_argument("--chunk-bytes", type=int, default=0, help="uncompressed chunk size (0: the dtype's default)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum CPU-oracle time to accumulate")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     return ap.parse_args()
@@ -110,6 +114,17 @@ def make_workload(name, dev):
         desc = ("RL weight sync: Llama-3-8B-shaped bf16 weight set, 290 buffers, 8,030,257,152 values (16.06 GB), "
                 "N(0, 0.02^2), RMSNorm vectors 1.0, one batched call, 64 KiB chunks")
         batched = True
+    elif name == "fp16_act":
+        ts = [W.fp16_activations(W.FP16_ACT_N, device=dev, seed=5)]
+        desc = ("fp16 activations: 268,435,456 values (512 MiB), rows of 8192 N(0,1) x log-normal(0, 0.5) per-row "
+                "scale")
+        batched = False
+    elif name in ("fp8_e4m3", "fp8_e5m2"):
+        fmt = torch.float8_e4m3fn if name == "fp8_e4m3" else torch.float8_e5m2
+        ts = [W.fp8_weights(W.FP8_WEIGHT_N, device=dev, seed=6, fmt=fmt)]
+        desc = ("fp8 %s weights: 268,435,456 values (256 MiB), N(0,1) scaled per 8192-value block so the block "
+                "absmax is the format's largest finite value" % ("e4m3fn" if name == "fp8_e4m3" else "e5m2"))
+        batched = False
     else:
         ts = W.small_message_batch(device=dev, seed=4)
         desc = ("small-message batch: 4,096 bf16 activation buffers, 1-64 tokens x 8192 hidden, N(0,1) x "
@@ -131,9 +146,15 @@ def entropy_bound(ts, chunk_elems):
         if t.dtype == torch.bfloat16:
             e = (t.view(torch.int16).to(torch.int32) >> 7) & 0xFF
             r = 1
-        else:
+        elif t.dtype == torch.float16:
+            e = (t.view(torch.int16).to(torch.int32) >> 8) & 0xFF
+            r = 1
+        elif t.dtype == torch.float32:
             e = (t.view(torch.int32) >> 23) & 0xFF
             r = 3
+        else:
+            e = t.view(torch.uint8)
+            r = 0
         C = (n + chunk_elems - 1) // chunk_elems
         for c0 in range(0, C, 4096):  # slices of chunks keep the index tensor small
             c1 = min(C, c0 + 4096)
@@ -166,31 +187,34 @@ def main():
     ts, desc, batched = make_workload(args.workload, dev)
     dtype = ts[0].dtype
     code = uz.dtype_code(dtype)
-    eb = 2 if code == uz.UZIP_BF16 else 4
-    rb = 1 if code == uz.UZIP_BF16 else 3
-    chunk_elems = 32768 if code == uz.UZIP_BF16 else 65536
+    eb = dtype.itemsize
+    rb = {uz.UZIP_BF16: 1, uz.UZIP_FP16: 1, uz.UZIP_FP32: 3}.get(code, 0)
+    cb = args.chunk_bytes or (262144 if code == uz.UZIP_FP32 else 65536)
+    chunk_elems = cb // eb
     ns = [t.numel() for t in ts]
     n_total = sum(ns)
     in_bytes = n_total * eb
 
     # preallocated outputs and workspaces
-    caps = [uz.uzip_max_compressed_size(code, n) for n in ns]
+    caps = [uz.uzip_max_compressed_size(code, n, cb) for n in ns]
+    if 0 in caps:
+        sys.exit("invalid --chunk-bytes %d" % args.chunk_bytes)
     outs = [torch.empty(c, dtype=torch.uint8, device=dev) for c in caps]
     backs = [torch.empty(n, dtype=dtype, device=dev) for n in ns]
     if batched:
-        ws = uz.workspace(uz.uzip_workspace_size_batched(code, ns), dev)
+        ws = uz.workspace(uz.uzip_workspace_size_batched(code, ns, cb), dev)
         sizes = torch.empty(len(ts), dtype=torch.int64, device=dev)
         status = torch.empty(len(ts), dtype=torch.int32, device=dev)
     else:
-        ws = uz.workspace(uz.uzip_workspace_size(code, ns[0]), dev)
+        ws = uz.workspace(uz.uzip_workspace_size(code, ns[0], cb), dev)
         sizes = torch.empty(1, dtype=torch.int64, device=dev)
         status = torch.empty(1, dtype=torch.int32, device=dev)
 
     def compress():
         if batched:
-            uz.compress_batched(ts, outs=outs, ws=ws, out_sizes=sizes)
+            uz.compress_batched(ts, cb, outs=outs, ws=ws, out_sizes=sizes)
         else:
-            uz.compress(ts[0], out=outs[0], ws=ws, out_size=sizes)
+            uz.compress(ts[0], cb, out=outs[0], ws=ws, out_size=sizes)
 
     def decompress():
         # in_bytes = capacity: the decoder validates the header's total against it
@@ -235,10 +259,10 @@ def main():
         hip.destroy(b)
 
     # correctness of what was timed: bit-exact round trip, valid status
+    iv = {1: torch.uint8, 2: torch.int16, 4: torch.int32}[eb]
     st = status.cpu().tolist()
     roundtrip_ok = all(s == 0 for s in st) and all(
-        torch.equal(a.view(torch.int16 if eb == 2 else torch.int32), b.view(torch.int16 if eb == 2 else torch.int32))
-        for a, b in zip(ts, backs))
+        torch.equal(a.view(iv), b.view(iv)) for a, b in zip(ts, backs))
     comp_sizes = sizes.cpu().tolist()
     comp_bytes = sum(comp_sizes)
     bound = entropy_bound(ts, chunk_elems)
@@ -273,7 +297,7 @@ def main():
     cpu = None
     oracle_match = None
     if not args.no_cpu_baseline:
-        cpu, oracle_match = cpu_baseline(ts, outs, comp_sizes, code, args.cpu_seconds)
+        cpu, oracle_match = cpu_baseline(ts, outs, comp_sizes, code, args.cpu_seconds, cb)
 
     med_c = comp_ms[len(comp_ms) // 2]
     med_d = dec_ms[len(dec_ms) // 2]
@@ -291,7 +315,7 @@ def main():
         "dtype": "u32",
         "data": "synthetic",
         "config": {"workload": desc, "values": n_total, "buffers": len(ts), "input_bytes": in_bytes,
-                   "value_dtype": "bf16" if eb == 2 else "fp32", "chunk_bytes": chunk_elems * eb,
+                   "value_dtype": VALUE_DTYPE[code], "chunk_bytes": chunk_elems * eb,
                    "step": "compress + decompress"},
         "compress_gbps": round(in_bytes / (med_c * 1e-3) / 1e9, 2),
         "decompress_gbps": round(in_bytes / (med_d * 1e-3) / 1e9, 2),
@@ -335,7 +359,7 @@ def copy_reference(ts, steps):
     return 2 * nbytes / (ms * 1e-3) / 1e9
 
 
-def cpu_baseline(ts, outs, comp_sizes, code, min_seconds):
+def cpu_baseline(ts, outs, comp_sizes, code, min_seconds, chunk_bytes):
     """The oracle (plain single-threaded C) on a bounded sample of the same
     workload: whole buffers, in order, up to 512 MiB of input; passes repeat
     until min_seconds of CPU time have been spent.  Also compares the oracle's
@@ -355,7 +379,7 @@ def cpu_baseline(ts, outs, comp_sizes, code, min_seconds):
     host = [W.bits_numpy(ts[i]) for i in picked]
     match = True
     for i, h in zip(picked, host):
-        want = oracle.compress(code, h)
+        want = oracle.compress(code, h, chunk_bytes)
         got = outs[i][:comp_sizes[i]].cpu().numpy()
         match = match and np.array_equal(want, got)
     sample_bytes = sum(h.size * h.itemsize for h in host)
@@ -363,7 +387,7 @@ def cpu_baseline(ts, outs, comp_sizes, code, min_seconds):
     while passes == 0 or spent < min_seconds:
         t0 = time.perf_counter()
         for h in host:
-            buf = oracle.compress(code, h)
+            buf = oracle.compress(code, h, chunk_bytes)
             st, back = oracle.decompress(buf, code, h.size)
             assert st == 0
         spent += time.perf_counter() - t0
