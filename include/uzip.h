@@ -133,6 +133,72 @@ uzip_status uzip_decompress_batched(uzip_dtype dtype, size_t num_buffers,
                                     const size_t *h_num_elements, void *const *h_out, uint32_t *d_status,
                                     void *d_workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* ---- per-call arbitration: code the call, or send it RAW ----------------
+ * NCCLZ Sec. IV-C (runtime entropy-coding arbitration, Eq. (1) and (2),
+ * Algorithm 1).  A call whose payload B = num_elements * sizeof(T) is at most
+ * small_bytes is stored RAW without looking at it.  Otherwise the first
+ * min(num_elements, 65536 / sizeof(T)) values (at most 64 KiB) are sampled:
+ * their coded-symbol histogram gives the empirical entropy h (bits per value,
+ * in units of 2^-16, logarithms as integers by the squaring method), and the
+ * coded frame is predicted as
+ *   P = exp_off + ceil(N h / 2^19) + C (align4(48 + 2 nsym) + 136)
+ * (the layout's fixed part, the symbols at the sample's entropy, and each
+ * record's fixed part plus half a padding unit; nsym = symbols present in the
+ * sample).  With P_raw = uzip_max_compressed_size (the all-RAW frame), the
+ * times of Eq. (1) in nanoseconds are
+ *   raw_ns   = ceil(P_raw * 1000 / link_bytes_per_us)
+ *   coded_ns = fixed_ns + ceil(P * 1000 / link_bytes_per_us)
+ *              + ceil(exposed_encode_permil * B / encode_bytes_per_us)
+ *              + ceil(exposed_decode_permil * B / decode_bytes_per_us).
+ * Coding is admitted when P < P_raw and (P_raw - P) * 1000 >=
+ * min_gain_permil * B; it is chosen when admitted and coded_ns < raw_ns
+ * (Eq. (2); ties go RAW).  A RAW plan writes the all-RAW frame (every record
+ * RAW, size P_raw); a coded plan writes exactly what uzip_compress writes.
+ * Either frame decodes with uzip_decompress.  Every step is integer
+ * arithmetic, so the plan is one fixed function of the input and the policy.
+ * Rates are bytes per microsecond (= MB/s); all must be > 0; the per-mille
+ * fields are at most 1000; reserved must be 0; num_elements < 2^44. */
+typedef struct uzip_policy {
+    uint64_t link_bytes_per_us;   /* effective link bandwidth (beta_eff) */
+    uint64_t encode_bytes_per_us; /* compress rate of uncompressed bytes */
+    uint64_t decode_bytes_per_us; /* decompress rate of uncompressed bytes */
+    uint64_t fixed_ns;            /* fixed cost a coded transfer adds (alpha) */
+    uint64_t small_bytes;         /* payloads of at most this size go RAW unsampled */
+    uint32_t exposed_encode_permil; /* share of the encode time not hidden by overlap */
+    uint32_t exposed_decode_permil; /* share of the decode time not hidden by overlap */
+    uint32_t min_gain_permil;     /* least predicted saving, per mille of B */
+    uint32_t reserved;
+} uzip_policy;
+
+/* What a call decided (device-written, 32 bytes per buffer). */
+typedef enum { UZIP_PLAN_CODED = 0, UZIP_PLAN_RAW = 1, UZIP_PLAN_RAW_SMALL = 2 } uzip_plan_decision;
+typedef struct uzip_plan {
+    uint32_t decision;        /* uzip_plan_decision */
+    uint32_t sample_values;   /* values sampled (0 on the small path) */
+    uint64_t predicted_bytes; /* P (0 on the small path) */
+    uint64_t raw_ns;          /* 0 on the small path */
+    uint64_t coded_ns;        /* 0 on the small path */
+} uzip_plan;
+
+/* uzip_compress with the arbitration above.  *policy is read on the host
+ * before the call returns; d_plan (device, 8-byte aligned, caller-owned)
+ * receives the plan, which the encoder reads on the device, so the call stays
+ * asynchronous.  Same workspace as uzip_compress.  Errors as uzip_compress,
+ * plus UZIP_ERR_INVALID_ARGUMENT for a null d_plan or an invalid policy. */
+uzip_status uzip_compress_arbitrated(uzip_dtype dtype, const void *d_in, size_t num_elements, size_t chunk_bytes,
+                                     const uzip_policy *policy, void *d_out, size_t out_capacity,
+                                     uint64_t *d_out_size, uzip_plan *d_plan,
+                                     void *d_workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* The batched form: one plan per buffer (d_plans[b]), each buffer's frame
+ * byte-identical to uzip_compress_arbitrated on that buffer alone. */
+uzip_status uzip_compress_batched_arbitrated(uzip_dtype dtype, size_t num_buffers,
+                                             const void *const *h_in, const size_t *h_num_elements,
+                                             size_t chunk_bytes, const uzip_policy *policy,
+                                             void *const *h_out, const size_t *h_out_capacity,
+                                             uint64_t *d_out_sizes, uzip_plan *d_plans,
+                                             void *d_workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Benchmark instrumentation.  While set (non-null), every compress call on
  * the calling host thread records `main_start` on its stream right before
  * its main coding kernel (split + histogram + table + rANS encode) and

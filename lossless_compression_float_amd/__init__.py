@@ -34,6 +34,23 @@ UZIP_ERR_CORRUPT_INPUT = 3
 UZIP_ERR_DEVICE = 4
 UZIP_ERR_UNSUPPORTED = 5
 
+UZIP_PLAN_CODED = 0
+UZIP_PLAN_RAW = 1
+UZIP_PLAN_RAW_SMALL = 2
+
+
+class uzip_policy(ctypes.Structure):
+    """The per-call arbitration's cost-model inputs (uzip.h: uzip_policy)."""
+    _fields_ = [("link_bytes_per_us", ctypes.c_uint64), ("encode_bytes_per_us", ctypes.c_uint64),
+                ("decode_bytes_per_us", ctypes.c_uint64), ("fixed_ns", ctypes.c_uint64),
+                ("small_bytes", ctypes.c_uint64), ("exposed_encode_permil", ctypes.c_uint32),
+                ("exposed_decode_permil", ctypes.c_uint32), ("min_gain_permil", ctypes.c_uint32),
+                ("reserved", ctypes.c_uint32)]
+
+
+PLAN_FIELDS = ("decision", "sample_values", "predicted_bytes", "raw_ns", "coded_ns")
+PLAN_BYTES = 32
+
 EXPORTED = (
     "uzip_max_compressed_size",
     "uzip_workspace_size",
@@ -42,6 +59,8 @@ EXPORTED = (
     "uzip_workspace_size_batched",
     "uzip_compress_batched",
     "uzip_decompress_batched",
+    "uzip_compress_arbitrated",
+    "uzip_compress_batched_arbitrated",
     "uzip_profile_set_events",
     "uzip_status_string",
 )
@@ -77,6 +96,12 @@ def lib() -> ctypes.CDLL:
         L.uzip_compress_batched.argtypes = [i32, sz, vp, vp, sz, vp, vp, u64p, vp, sz, vp]
         L.uzip_decompress_batched.restype = i32
         L.uzip_decompress_batched.argtypes = [i32, sz, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.uzip_compress_arbitrated.restype = i32
+        L.uzip_compress_arbitrated.argtypes = [i32, vp, sz, sz, ctypes.POINTER(uzip_policy), vp, sz, u64p, vp, vp,
+                                               sz, vp]
+        L.uzip_compress_batched_arbitrated.restype = i32
+        L.uzip_compress_batched_arbitrated.argtypes = [i32, sz, vp, vp, sz, ctypes.POINTER(uzip_policy), vp, vp,
+                                                       u64p, vp, vp, sz, vp]
         L.uzip_profile_set_events.restype = i32
         L.uzip_profile_set_events.argtypes = [vp, vp]
         L.uzip_status_string.restype = ctypes.c_char_p
@@ -140,6 +165,22 @@ def uzip_decompress_batched(dtype, h_in, h_in_bytes, h_num_elements, h_out, d_st
     a_in, a_b, a_n, a_out = _ptrs(h_in), _sizes(h_in_bytes), _sizes(h_num_elements), _ptrs(h_out)
     return int(lib().uzip_decompress_batched(dtype, len(h_in), a_in.ptr, a_b.ptr, a_n.ptr, a_out.ptr, d_status,
                                              d_workspace, workspace_bytes, stream))
+
+
+def uzip_compress_arbitrated(dtype, d_in, num_elements, chunk_bytes, policy, d_out, out_capacity, d_out_size,
+                             d_plan, d_workspace, workspace_bytes, stream) -> int:
+    pol = ctypes.byref(policy) if policy is not None else None
+    return int(lib().uzip_compress_arbitrated(dtype, d_in, num_elements, chunk_bytes, pol, d_out, out_capacity,
+                                              d_out_size, d_plan, d_workspace, workspace_bytes, stream))
+
+
+def uzip_compress_batched_arbitrated(dtype, h_in, h_num_elements, chunk_bytes, policy, h_out, h_out_capacity,
+                                     d_out_sizes, d_plans, d_workspace, workspace_bytes, stream) -> int:
+    a_in, a_n, a_out, a_cap = _ptrs(h_in), _sizes(h_num_elements), _ptrs(h_out), _sizes(h_out_capacity)
+    pol = ctypes.byref(policy) if policy is not None else None
+    return int(lib().uzip_compress_batched_arbitrated(dtype, len(h_in), a_in.ptr, a_n.ptr, chunk_bytes, pol,
+                                                      a_out.ptr, a_cap.ptr, d_out_sizes, d_plans, d_workspace,
+                                                      workspace_bytes, stream))
 
 
 def uzip_profile_set_events(main_start, main_stop) -> int:
@@ -258,3 +299,62 @@ def decompress_batched(bufs, dtype: torch.dtype, ns, in_bytes=None, outs=None, s
                                  ws.numel(), _stream(stream))
     _check(st, "uzip_decompress_batched")
     return outs, status
+
+
+def policy(**fields) -> uzip_policy:
+    """A uzip_policy from keyword fields (unset fields are 0)."""
+    return uzip_policy(**fields)
+
+
+def plans_as_dicts(plans: torch.Tensor) -> list:
+    """Device plan records (int64 tensor of 4 words per buffer) as dicts."""
+    w = plans.view(-1, 4).cpu().tolist()
+    return [{"decision": r[0] & 0xFFFFFFFF, "sample_values": (r[0] >> 32) & 0xFFFFFFFF, "predicted_bytes": r[1],
+             "raw_ns": r[2], "coded_ns": r[3]} for r in w]
+
+
+def compress_arbitrated(t: torch.Tensor, pol: uzip_policy, chunk_bytes: int = 0, out=None, ws=None, out_size=None,
+                        plan=None, stream=None):
+    """Arbitrated compress of one tensor.  Returns (buffer, size, plan) where
+    plan is an int64 device tensor of 4 words (see plans_as_dicts)."""
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError("compress needs a contiguous device tensor")
+    code = dtype_code(t.dtype)
+    n = t.numel()
+    cap = uzip_max_compressed_size(code, n, chunk_bytes)
+    if cap == 0:
+        raise ValueError("invalid chunk_bytes %d" % chunk_bytes)
+    if out is None:
+        out = torch.empty(cap, dtype=torch.uint8, device=t.device)
+    if out_size is None:
+        out_size = torch.empty(1, dtype=torch.int64, device=t.device)
+    if plan is None:
+        plan = torch.empty(4, dtype=torch.int64, device=t.device)
+    if ws is None:
+        ws = workspace(uzip_workspace_size(code, n, chunk_bytes), t.device)
+    st = uzip_compress_arbitrated(code, t.data_ptr() if n else None, n, chunk_bytes, pol, out.data_ptr(), out.numel(),
+                                  out_size.data_ptr(), plan.data_ptr(), ws.data_ptr(), ws.numel(), _stream(stream))
+    _check(st, "uzip_compress_arbitrated")
+    return out, out_size, plan
+
+
+def compress_batched_arbitrated(tensors, pol: uzip_policy, chunk_bytes: int = 0, outs=None, ws=None, out_sizes=None,
+                                plans=None, stream=None):
+    """Arbitrated compress of a list of tensors.  Returns (buffers, sizes, plans[int64, 4 words per buffer])."""
+    code = dtype_code(tensors[0].dtype)
+    dev = tensors[0].device
+    ns = [t.numel() for t in tensors]
+    if outs is None:
+        outs = [torch.empty(uzip_max_compressed_size(code, n, chunk_bytes), dtype=torch.uint8, device=dev) for n in ns]
+    if out_sizes is None:
+        out_sizes = torch.empty(len(tensors), dtype=torch.int64, device=dev)
+    if plans is None:
+        plans = torch.empty(4 * len(tensors), dtype=torch.int64, device=dev)
+    if ws is None:
+        ws = workspace(uzip_workspace_size_batched(code, ns, chunk_bytes), dev)
+    st = uzip_compress_batched_arbitrated(code, [t.data_ptr() if t.numel() else 0 for t in tensors], ns, chunk_bytes,
+                                          pol, [o.data_ptr() for o in outs], [o.numel() for o in outs],
+                                          out_sizes.data_ptr(), plans.data_ptr(), ws.data_ptr(), ws.numel(),
+                                          _stream(stream))
+    _check(st, "uzip_compress_batched_arbitrated")
+    return outs, out_sizes, plans

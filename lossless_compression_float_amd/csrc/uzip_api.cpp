@@ -95,9 +95,21 @@ uint64_t max_size(uzip_dtype dtype, uint64_t n, uint64_t ce) {
     return l.exp_off + (l.chunks - 1) * raw_record_bytes(ce) + raw_record_bytes(last);
 }
 
-// Shared body of the single and batched compress calls.
+static_assert(sizeof(uzip_policy) == 56 && sizeof(uzip_plan) == 32, "arbitration structs as uzip.h lays them out");
+
+// The cost model's inputs must be usable as the header states: positive
+// rates, per-mille fields at most 1000, reserved zero.
+bool policy_ok(const uzip_policy *p) {
+    return p != nullptr && p->link_bytes_per_us > 0 && p->encode_bytes_per_us > 0 && p->decode_bytes_per_us > 0 &&
+           p->exposed_encode_permil <= 1000 && p->exposed_decode_permil <= 1000 && p->min_gain_permil <= 1000 &&
+           p->reserved == 0;
+}
+
+// Shared body of the single and batched compress calls (plans non-null: the
+// arbitrated forms).
 uzip_status compress_impl(uzip_dtype dtype, uint64_t ce, std::vector<EncDesc> &descs, uint64_t chunks,
-                          void *d_workspace, size_t workspace_bytes, hipStream_t stream) {
+                          void *d_workspace, size_t workspace_bytes, hipStream_t stream,
+                          uzip_plan *plans = nullptr, const uzip_policy *policy = nullptr) {
     const uint32_t nbuf = (uint32_t)descs.size();
     const EncWs w = enc_ws(nbuf, chunks, ce);
     if (d_workspace == nullptr || workspace_bytes < w.bytes || !aligned(d_workspace, 16))
@@ -122,6 +134,8 @@ uzip_status compress_impl(uzip_dtype dtype, uint64_t ce, std::vector<EncDesc> &d
     ep.flags = reinterpret_cast<uint64_t *>(base + w.flags);
     ep.ticket = reinterpret_cast<uint32_t *>(base + w.ticket);
     ep.dtype = dtype;
+    ep.plans = plans;
+    if (policy) ep.policy = *policy;
     if (nbuf == 1) {
         ep.single = descs[0];
         ep.descs = nullptr;
@@ -135,6 +149,50 @@ uzip_status compress_impl(uzip_dtype dtype, uint64_t ce, std::vector<EncDesc> &d
     }
     const hipError_t e = launch_compress(ep, stream);
     return e == hipSuccess ? UZIP_OK : UZIP_ERR_DEVICE;
+}
+
+// Body of uzip_compress and uzip_compress_arbitrated (policy null: no arbitration).
+uzip_status compress_single(uzip_dtype dtype, const void *d_in, size_t num_elements, size_t chunk_bytes,
+                            const uzip_policy *policy, void *d_out, size_t out_capacity, uint64_t *d_out_size,
+                            uzip_plan *d_plan, void *d_workspace, size_t workspace_bytes, hipStream_t stream) {
+    const uint64_t ce = chunk_elems_of(dtype, chunk_bytes);
+    if (!ce) return UZIP_ERR_INVALID_ARGUMENT;
+    if (num_elements > 0 && (d_in == nullptr || !aligned(d_in, 16))) return UZIP_ERR_INVALID_ARGUMENT;
+    if (d_out == nullptr || !aligned(d_out, 16) || d_out_size == nullptr || !aligned(d_out_size, 8))
+        return UZIP_ERR_INVALID_ARGUMENT;
+    if (out_capacity < max_size(dtype, num_elements, ce)) return UZIP_ERR_CAPACITY;
+    const Layout l = layout_of(dtype, num_elements, ce);
+    std::vector<EncDesc> descs(1);
+    descs[0] = EncDesc{static_cast<const uint8_t *>(d_in), static_cast<uint8_t *>(d_out), d_out_size, num_elements,
+                       0, l.sm_off, l.exp_off, l.chunks, 0, 0};
+    return compress_impl(dtype, ce, descs, l.chunks, d_workspace, workspace_bytes, stream,
+                         policy ? d_plan : nullptr, policy);
+}
+
+// Body of uzip_compress_batched and its arbitrated form (policy null: no arbitration).
+uzip_status compress_batched(uzip_dtype dtype, size_t num_buffers, const void *const *h_in,
+                             const size_t *h_num_elements, size_t chunk_bytes, const uzip_policy *policy,
+                             void *const *h_out, const size_t *h_out_capacity, uint64_t *d_out_sizes,
+                             uzip_plan *d_plans, void *d_workspace, size_t workspace_bytes, hipStream_t stream) {
+    const uint64_t ce = chunk_elems_of(dtype, chunk_bytes);
+    if (!ce || num_buffers == 0 || num_buffers > 0xFFFFFFFFull) return UZIP_ERR_INVALID_ARGUMENT;
+    if (!h_in || !h_num_elements || !h_out || !h_out_capacity || !d_out_sizes || !aligned(d_out_sizes, 8))
+        return UZIP_ERR_INVALID_ARGUMENT;
+    std::vector<EncDesc> descs(num_buffers);
+    uint64_t chunks = 0;
+    for (size_t b = 0; b < num_buffers; ++b) {
+        const uint64_t n = h_num_elements[b];
+        if (policy != nullptr && n >= (1ull << 44)) return UZIP_ERR_INVALID_ARGUMENT;
+        if (n > 0 && (h_in[b] == nullptr || !aligned(h_in[b], 16))) return UZIP_ERR_INVALID_ARGUMENT;
+        if (h_out[b] == nullptr || !aligned(h_out[b], 16)) return UZIP_ERR_INVALID_ARGUMENT;
+        if (h_out_capacity[b] < max_size(dtype, n, ce)) return UZIP_ERR_CAPACITY;
+        const Layout l = layout_of(dtype, n, ce);
+        descs[b] = EncDesc{static_cast<const uint8_t *>(h_in[b]), static_cast<uint8_t *>(h_out[b]), d_out_sizes + b, n,
+                           chunks, l.sm_off, l.exp_off, l.chunks, 0, 0};
+        chunks += l.chunks;
+    }
+    return compress_impl(dtype, ce, descs, chunks, d_workspace, workspace_bytes, stream,
+                         policy ? d_plans : nullptr, policy);
 }
 
 uzip_status decompress_impl(uzip_dtype dtype, std::vector<DecDesc> &descs, uint32_t *d_status, void *d_workspace,
@@ -199,17 +257,18 @@ size_t uzip_workspace_size_batched(uzip_dtype dtype, size_t num_buffers, const s
 uzip_status uzip_compress(uzip_dtype dtype, const void *d_in, size_t num_elements, size_t chunk_bytes, void *d_out,
                           size_t out_capacity, uint64_t *d_out_size, void *d_workspace, size_t workspace_bytes,
                           hipStream_t stream) {
-    const uint64_t ce = chunk_elems_of(dtype, chunk_bytes);
-    if (!ce) return UZIP_ERR_INVALID_ARGUMENT;
-    if (num_elements > 0 && (d_in == nullptr || !aligned(d_in, 16))) return UZIP_ERR_INVALID_ARGUMENT;
-    if (d_out == nullptr || !aligned(d_out, 16) || d_out_size == nullptr || !aligned(d_out_size, 8))
+    return compress_single(dtype, d_in, num_elements, chunk_bytes, nullptr, d_out, out_capacity, d_out_size, nullptr,
+                           d_workspace, workspace_bytes, stream);
+}
+
+uzip_status uzip_compress_arbitrated(uzip_dtype dtype, const void *d_in, size_t num_elements, size_t chunk_bytes,
+                                     const uzip_policy *policy, void *d_out, size_t out_capacity,
+                                     uint64_t *d_out_size, uzip_plan *d_plan, void *d_workspace,
+                                     size_t workspace_bytes, hipStream_t stream) {
+    if (!policy_ok(policy) || d_plan == nullptr || !aligned(d_plan, 8) || num_elements >= (1ull << 44))
         return UZIP_ERR_INVALID_ARGUMENT;
-    if (out_capacity < max_size(dtype, num_elements, ce)) return UZIP_ERR_CAPACITY;
-    const Layout l = layout_of(dtype, num_elements, ce);
-    std::vector<EncDesc> descs(1);
-    descs[0] = EncDesc{static_cast<const uint8_t *>(d_in), static_cast<uint8_t *>(d_out), d_out_size, num_elements,
-                       0, l.sm_off, l.exp_off, l.chunks, 0, 0};
-    return compress_impl(dtype, ce, descs, l.chunks, d_workspace, workspace_bytes, stream);
+    return compress_single(dtype, d_in, num_elements, chunk_bytes, policy, d_out, out_capacity, d_out_size, d_plan,
+                           d_workspace, workspace_bytes, stream);
 }
 
 uzip_status uzip_decompress(const void *d_in, size_t in_bytes, uzip_dtype dtype, size_t num_elements, void *d_out,
@@ -227,23 +286,19 @@ uzip_status uzip_compress_batched(uzip_dtype dtype, size_t num_buffers, const vo
                                   const size_t *h_num_elements, size_t chunk_bytes, void *const *h_out,
                                   const size_t *h_out_capacity, uint64_t *d_out_sizes, void *d_workspace,
                                   size_t workspace_bytes, hipStream_t stream) {
-    const uint64_t ce = chunk_elems_of(dtype, chunk_bytes);
-    if (!ce || num_buffers == 0 || num_buffers > 0xFFFFFFFFull) return UZIP_ERR_INVALID_ARGUMENT;
-    if (!h_in || !h_num_elements || !h_out || !h_out_capacity || !d_out_sizes || !aligned(d_out_sizes, 8))
-        return UZIP_ERR_INVALID_ARGUMENT;
-    std::vector<EncDesc> descs(num_buffers);
-    uint64_t chunks = 0;
-    for (size_t b = 0; b < num_buffers; ++b) {
-        const uint64_t n = h_num_elements[b];
-        if (n > 0 && (h_in[b] == nullptr || !aligned(h_in[b], 16))) return UZIP_ERR_INVALID_ARGUMENT;
-        if (h_out[b] == nullptr || !aligned(h_out[b], 16)) return UZIP_ERR_INVALID_ARGUMENT;
-        if (h_out_capacity[b] < max_size(dtype, n, ce)) return UZIP_ERR_CAPACITY;
-        const Layout l = layout_of(dtype, n, ce);
-        descs[b] = EncDesc{static_cast<const uint8_t *>(h_in[b]), static_cast<uint8_t *>(h_out[b]), d_out_sizes + b, n,
-                           chunks, l.sm_off, l.exp_off, l.chunks, 0, 0};
-        chunks += l.chunks;
-    }
-    return compress_impl(dtype, ce, descs, chunks, d_workspace, workspace_bytes, stream);
+    return compress_batched(dtype, num_buffers, h_in, h_num_elements, chunk_bytes, nullptr, h_out, h_out_capacity,
+                            d_out_sizes, nullptr, d_workspace, workspace_bytes, stream);
+}
+
+uzip_status uzip_compress_batched_arbitrated(uzip_dtype dtype, size_t num_buffers, const void *const *h_in,
+                                             const size_t *h_num_elements, size_t chunk_bytes,
+                                             const uzip_policy *policy, void *const *h_out,
+                                             const size_t *h_out_capacity, uint64_t *d_out_sizes,
+                                             uzip_plan *d_plans, void *d_workspace, size_t workspace_bytes,
+                                             hipStream_t stream) {
+    if (!policy_ok(policy) || d_plans == nullptr || !aligned(d_plans, 8)) return UZIP_ERR_INVALID_ARGUMENT;
+    return compress_batched(dtype, num_buffers, h_in, h_num_elements, chunk_bytes, policy, h_out, h_out_capacity,
+                            d_out_sizes, d_plans, d_workspace, workspace_bytes, stream);
 }
 
 uzip_status uzip_decompress_batched(uzip_dtype dtype, size_t num_buffers, const void *const *h_in,

@@ -461,8 +461,8 @@ __global__ __launch_bounds__(64) void k_encode(EncParams p) {
 
     // ---- the pair: buffer and chunks (wave-uniform); half-wave h codes chunk c0 + h ----
     const uint64_t q = blockIdx.x;
-    const EncDesc d = p.nbuf == 1 ? p.single
-                                  : load_enc_desc(p.descs + uniform_u32(find_enc_pair_buffer(p.descs, p.nbuf, q)));
+    const uint32_t bi = p.nbuf == 1 ? 0u : uniform_u32(find_enc_pair_buffer(p.descs, p.nbuf, q));
+    const EncDesc d = p.nbuf == 1 ? p.single : load_enc_desc(p.descs + bi);
     const uint64_t ce = p.chunk_elems;
     const uint64_t n = uniform_u64(d.n);
     const uint64_t c0 = 2 * (q - uniform_u64(d.pair_first));
@@ -629,6 +629,17 @@ __global__ __launch_bounds__(64) void k_encode(EncParams p) {
         }
     }
     __syncthreads();
+
+    // ---- a RAW plan of the per-call arbitration: the sign+mantissa bytes are
+    // in place; every record is RAW (k_compact copies the exponents) ----
+    if (p.plans != nullptr && uniform_u32(gload<uint32_t>(&p.plans[bi].decision)) != UZIP_PLAN_CODED) {
+        if (valid && lj == 0) {
+            const uint32_t raw_i = (uint32_t)raw_record_bytes(ni);
+            gstore<uint4>(slot, make_uint4(1u, 0u, ni, raw_i));
+            gstore<uint32_t>(p.rec_sizes + g, raw_i);
+        }
+        return;
+    }
 
     // ---- normalise the counts to a table of 4096 (lane lj owns symbols 8lj..8lj+7) ----
     // Reserve one slot per present symbol, share R = 4096 - nsym slots by the
@@ -856,6 +867,90 @@ __global__ __launch_bounds__(64) void k_encode(EncParams p) {
             gstore<uint32_t>(p.rec_sizes + g, rans ? rans_bytes : raw_i);
         }
     }
+}
+
+// ---------------------------------------------------------------------------
+// k_plan: per-call arbitration (NCCLZ Sec. IV-C, Eq. (1) and (2), Algorithm 1)
+// ---------------------------------------------------------------------------
+// 2^16 log2(x) for x >= 1, rounded down, digit by digit (the squaring method):
+// with x = 2^y z, z in [1, 2), squaring z doubles log2 z, and the integer part
+// of the square is the next binary digit.  z has 31 fraction bits and is
+// truncated after every squaring, so the result is exact at powers of two
+// and at most one unit below 2^16 log2 x elsewhere.
+__device__ inline uint32_t log2_q16(uint32_t x) {
+    const uint32_t y = 31u - (uint32_t)__builtin_clz(x);
+    uint64_t z = uint64_t(x) << (31u - y);
+    uint32_t frac = 0;
+    for (int i = 0; i < 16; ++i) {
+        z = (z * z) >> 31;
+        frac <<= 1;
+        if (z >> 32) {
+            z >>= 1;
+            frac |= 1u;
+        }
+    }
+    return (y << 16) | frac;
+}
+
+__device__ inline uint64_t ceil_div_u64(uint64_t a, uint64_t b) { return a / b + (a % b != 0); }
+
+// One workgroup of 256 threads per buffer.  A buffer of at most small_bytes
+// goes RAW unsampled.  Otherwise the workgroup counts the coded symbols of the
+// buffer's first min(N, 64 KiB / value size) values in LDS, sums
+// c (log2 S - log2 c) over the 256 counts (one count per thread) for the
+// sample's entropy, predicts the coded frame from it, and evaluates the two
+// transfer times of the cost model in integer nanoseconds: coded when the
+// predicted gain is admitted and coding is strictly faster, RAW otherwise.
+// k_encode reads the decision on the device.
+template <int DT>
+__global__ __launch_bounds__(256) void k_plan(EncParams p) {
+    constexpr uint32_t EB = Fmt<DT>::EB;
+    __shared__ uint32_t hist[256];
+    __shared__ uint64_t part[4];
+    __shared__ uint32_t present[4];
+    const uint32_t t = threadIdx.x;
+    const EncDesc d = p.nbuf == 1 ? p.single : load_enc_desc(p.descs + blockIdx.x);
+    uint8_t *out = reinterpret_cast<uint8_t *>(p.plans + blockIdx.x);
+    const uzip_policy &pol = p.policy;
+    const uint64_t n = d.n, B = n * EB;
+    if (B <= pol.small_bytes) {  // the small-call fast path
+        if (t < 4) gstore<uint2>(out + 8 * t, make_uint2(t == 0 ? UZIP_PLAN_RAW_SMALL : 0u, 0u));
+        return;
+    }
+    const uint32_t S = (uint32_t)min<uint64_t>(n, 65536u / EB);
+    hist[t] = 0;
+    __syncthreads();
+    const rsrc_t rin = make_rsrc(d.in, S * EB);
+    for (uint32_t i = t; i < S; i += 256) atomicAdd(&hist[exponent_of<DT>(bld_value<DT>(rin, i * EB))], 1u);
+    __syncthreads();
+    const uint32_t c = hist[t];
+    const uint64_t term = c ? uint64_t(c) * (log2_q16(S) - log2_q16(c)) : 0ull;
+    const uint64_t wsum = wave_sum_u64(term);
+    const uint32_t wpresent = (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(c != 0));
+    if ((t & 63) == 0) {
+        part[t >> 6] = wsum;
+        present[t >> 6] = wpresent;
+    }
+    __syncthreads();
+    if (t != 0) return;
+    const uint64_t hs = part[0] + part[1] + part[2] + part[3];
+    const uint32_t nsym = present[0] + present[1] + present[2] + present[3];
+    const uint64_t h = hs / S;  // bits per value in units of 2^-16
+    const uint64_t ce = p.chunk_elems;
+    const Layout l = layout_of(p.dtype, n, ce);
+    const uint64_t pred = l.exp_off + ceil_div_u64(n * h, 1ull << 19) + l.chunks * (words_offset(nsym) + 8);
+    const uint64_t praw = l.exp_off + (l.chunks - 1) * raw_record_bytes(ce) + raw_record_bytes(n - (l.chunks - 1) * ce);
+    const uint64_t t_raw = ceil_div_u64(praw * 1000, pol.link_bytes_per_us);
+    const uint64_t t_code = pol.fixed_ns + ceil_div_u64(pred * 1000, pol.link_bytes_per_us) +
+                            ceil_div_u64(uint64_t(pol.exposed_encode_permil) * B, pol.encode_bytes_per_us) +
+                            ceil_div_u64(uint64_t(pol.exposed_decode_permil) * B, pol.decode_bytes_per_us);
+    const bool admitted = pred < praw && (praw - pred) * 1000 >= uint64_t(pol.min_gain_permil) * B;
+    const uint32_t decision = admitted && t_code < t_raw ? UZIP_PLAN_CODED : UZIP_PLAN_RAW;
+    // the plan as uzip_plan lays it out (8-byte aligned: four 8-byte stores)
+    gstore<uint2>(out, make_uint2(decision, S));
+    gstore<uint2>(out + 8, make_uint2((uint32_t)pred, (uint32_t)(pred >> 32)));
+    gstore<uint2>(out + 16, make_uint2((uint32_t)t_raw, (uint32_t)(t_raw >> 32)));
+    gstore<uint2>(out + 24, make_uint2((uint32_t)t_code, (uint32_t)(t_code >> 32)));
 }
 
 // ---------------------------------------------------------------------------
@@ -1442,6 +1537,14 @@ static int kernel_format(int dtype) { return dtype <= 3 ? dtype : 4; }
 
 hipError_t launch_compress(const EncParams &ep, hipStream_t stream) {
     uint64_t threads = ep.total_pairs > ep.nbuf ? ep.total_pairs : ep.nbuf;
+    if (ep.plans != nullptr) {
+        switch (kernel_format(ep.dtype)) {
+        case 1: k_plan<1><<<dim3(ep.nbuf), dim3(256), 0, stream>>>(ep); break;
+        case 2: k_plan<2><<<dim3(ep.nbuf), dim3(256), 0, stream>>>(ep); break;
+        case 3: k_plan<3><<<dim3(ep.nbuf), dim3(256), 0, stream>>>(ep); break;
+        default: k_plan<4><<<dim3(ep.nbuf), dim3(256), 0, stream>>>(ep); break;
+        }
+    }
     k_prepare<<<dim3((uint32_t)((threads + 255) / 256)), dim3(256), 0, stream>>>(ep);
     if (ep.total_pairs > 0) {
         const dim3 grid((uint32_t)ep.total_pairs);

@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include "uzip.h"
 #include "uzip_common.hpp"
 
 namespace uzip {
@@ -22,6 +23,8 @@ struct EncParams {
     uint64_t *flags;        // one look-back word per chunk pair (zeroed before compaction)
     uint32_t *ticket;       // chunk-pair ticket counter of the compaction (zeroed before it)
     int dtype;
+    uzip_plan *plans;       // per-call arbitration: one plan per buffer (null: every buffer is coded)
+    uzip_policy policy;     // the cost model's inputs when plans is set
 };
 
 struct DecParams {

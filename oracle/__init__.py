@@ -81,6 +81,12 @@ def lib():
         _lib.orc_compress.argtypes = [i32, vp, u64, u64, vp, u64, vp]
         _lib.orc_decompress.restype = i32
         _lib.orc_decompress.argtypes = [vp, u64, i32, u64, vp]
+        _lib.orc_log2_q16.restype = ctypes.c_uint32
+        _lib.orc_log2_q16.argtypes = [ctypes.c_uint32]
+        _lib.orc_plan_call.restype = i32
+        _lib.orc_plan_call.argtypes = [i32, vp, u64, u64, vp, vp]
+        _lib.orc_compress_arbitrated.restype = i32
+        _lib.orc_compress_arbitrated.argtypes = [i32, vp, u64, u64, vp, vp, vp, u64, vp]
     return _lib
 
 
@@ -208,3 +214,56 @@ def decompress(buf, dtype: int, n: int):
     out = np.zeros(max(n, 1), _ELEM[dtype])
     st = lib().orc_decompress(_p(b), nbytes, dtype, n, _p(out))
     return int(st), out[:n]
+
+
+# ---- per-call arbitration (NCCLZ Sec. IV-C, Eq. (1)-(2), Algorithm 1) -------
+class Policy(ctypes.Structure):
+    """Cost-model inputs: effective link bandwidth, encode and decode rates
+    (bytes per microsecond), the exposed fractions of the codec time (per
+    mille), the fixed cost of a coded transfer (ns), the small-call threshold
+    (bytes) and the minimum predicted gain (per mille of the payload)."""
+    _fields_ = [("link_bytes_per_us", ctypes.c_uint64), ("encode_bytes_per_us", ctypes.c_uint64),
+                ("decode_bytes_per_us", ctypes.c_uint64), ("fixed_ns", ctypes.c_uint64),
+                ("small_bytes", ctypes.c_uint64), ("exposed_encode_permil", ctypes.c_uint32),
+                ("exposed_decode_permil", ctypes.c_uint32), ("min_gain_permil", ctypes.c_uint32),
+                ("reserved", ctypes.c_uint32)]
+
+
+class Plan(ctypes.Structure):
+    """decision 0 coded, 1 RAW by the cost model, 2 RAW as a small call."""
+    _fields_ = [("decision", ctypes.c_uint32), ("sample_values", ctypes.c_uint32),
+                ("predicted_bytes", ctypes.c_uint64), ("raw_ns", ctypes.c_uint64), ("coded_ns", ctypes.c_uint64)]
+
+    def as_dict(self):
+        return {f: int(getattr(self, f)) for f, _ in self._fields_}
+
+
+def log2_q16(x: int) -> int:
+    """floor(2^16 log2 x) by the squaring method (x >= 1)."""
+    return int(lib().orc_log2_q16(x))
+
+
+def plan_call(dtype: int, values, policy: Policy, chunk_bytes: int = 0) -> dict:
+    v = _bits(dtype, values)
+    plan = Plan()
+    st = lib().orc_plan_call(dtype, _p(v) if v.size else None, v.size, chunk_bytes, ctypes.byref(policy),
+                             ctypes.byref(plan))
+    if st != OK:
+        raise ValueError("oracle plan failed with status %d" % st)
+    return plan.as_dict()
+
+
+def compress_arbitrated(dtype: int, values, policy: Policy, chunk_bytes: int = 0):
+    """(compressed buffer, plan) of an arbitrated call."""
+    v = _bits(dtype, values)
+    cap = max_compressed_size(dtype, v.size, chunk_bytes)
+    if cap == 0:
+        raise ValueError("invalid chunk_bytes")
+    out = np.empty(cap, np.uint8)
+    size = ctypes.c_uint64(0)
+    plan = Plan()
+    st = lib().orc_compress_arbitrated(dtype, _p(v) if v.size else None, v.size, chunk_bytes, ctypes.byref(policy),
+                                       ctypes.byref(plan), _p(out), cap, ctypes.byref(size))
+    if st != OK:
+        raise ValueError("oracle arbitrated compress failed with status %d" % st)
+    return out[: size.value].copy(), plan.as_dict()

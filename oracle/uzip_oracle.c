@@ -347,7 +347,7 @@ uint64_t orc_max_compressed_size(int dtype, uint64_t n, uint64_t chunk_bytes) {
 
 /* Encode one chunk's record (steps 2-4 plus the RANS/RAW choice) into rec,
  * which must hold align16(16 + ni) bytes.  Returns the record size. */
-static uint64_t orc_encode_record(const uint8_t *e, uint64_t ni, uint8_t *rec) {
+static uint64_t orc_encode_record(const uint8_t *e, uint64_t ni, uint8_t *rec, int force_raw) {
     uint32_t counts[256], f[256], c0[256], states[ORC_LANES];
     orc_histogram(e, ni, counts);
     int nsym = orc_normalize(counts, (uint32_t)ni, f);
@@ -359,7 +359,7 @@ static uint64_t orc_encode_record(const uint8_t *e, uint64_t ni, uint8_t *rec) {
     uint64_t rans_bytes = orc_align16(words_at + 2 * n_words);
     uint64_t raw_bytes = orc_align16(ORC_REC_HDR + ni);
     uint64_t rec_bytes;
-    if (rans_bytes < raw_bytes) {
+    if (!force_raw && rans_bytes < raw_bytes) {
         rec_bytes = rans_bytes;
         memset(rec, 0, (size_t)rec_bytes);
         rec[0] = 0; /* mode RANS */
@@ -389,9 +389,10 @@ static uint64_t orc_encode_record(const uint8_t *e, uint64_t ni, uint8_t *rec) {
 }
 
 /* Whole-buffer compression.  out must hold cap >= orc_max_compressed_size
- * bytes.  *out_size receives the exact compressed size. */
-int orc_compress(int dtype, const void *in, uint64_t n, uint64_t chunk_bytes, uint8_t *out, uint64_t cap,
-                 uint64_t *out_size) {
+ * bytes.  *out_size receives the exact compressed size.  force_raw stores
+ * every record RAW (the frame a RAW plan commits). */
+static int orc_compress_frame(int dtype, const void *in, uint64_t n, uint64_t chunk_bytes, uint8_t *out, uint64_t cap,
+                              uint64_t *out_size, int force_raw) {
     uint64_t ce = orc_chunk_elems(dtype, chunk_bytes);
     if (ce == 0) return ORC_INVALID;
     if (cap < orc_max_compressed_size(dtype, n, chunk_bytes)) return ORC_CAPACITY;
@@ -408,7 +409,7 @@ int orc_compress(int dtype, const void *in, uint64_t n, uint64_t chunk_bytes, ui
     put64(out + ORC_HDR_BYTES, 0);
     for (uint64_t i = 0; i < C; ++i) {
         uint64_t ni = (i + 1 < C) ? ce : n - i * ce;
-        off += orc_encode_record(e + i * ce, ni, out + exp_off + off);
+        off += orc_encode_record(e + i * ce, ni, out + exp_off + off, force_raw);
         put64(out + ORC_HDR_BYTES + 8 * (i + 1), off);
     }
     uint64_t total = exp_off + off;
@@ -430,6 +431,136 @@ int orc_compress(int dtype, const void *in, uint64_t n, uint64_t chunk_bytes, ui
     free(sm);
     *out_size = total;
     return ORC_OK;
+}
+
+int orc_compress(int dtype, const void *in, uint64_t n, uint64_t chunk_bytes, uint8_t *out, uint64_t cap,
+                 uint64_t *out_size) {
+    return orc_compress_frame(dtype, in, n, chunk_bytes, out, cap, out_size, 0);
+}
+
+/* ---- per-call arbitration: code the call, or send it RAW ------------------
+ * NCCLZ Sec. IV-C ("runtime entropy-coding arbitration", Eq. (1) and (2),
+ * Algorithm 1): a call that is small goes RAW at once; otherwise a bounded
+ * sample taken from the start of the payload predicts the coded size P, and
+ * the time of each choice is modelled as
+ *     T = alpha + P / beta_eff + lambda_enc * E + lambda_dec * D
+ * (RAW: P = its frame size, no codec cost, no alpha).  Coding is admitted
+ * only if the predicted frame is smaller than the RAW frame by at least the
+ * minimum gain; the smaller T wins, RAW on ties.  Every quantity is an
+ * integer, so that the decision is one fixed function of the input.
+ * Readings where the pages leave the step open: the sample is the first
+ * min(N, 65536 / bytes-per-value) values (at most 64 KiB, the pages' sample
+ * bound); the coded-size prediction is the sample's empirical entropy per
+ * value times N, plus each chunk's fixed record part and half a padding unit;
+ * logarithms are 2^16 log2 x in integers, by the squaring method.  The post-check
+ * of the realised frame is not needed: a chunk is stored RAW whenever coding
+ * would not make it strictly smaller, so a coded frame is never larger than
+ * the RAW frame. */
+typedef struct {
+    uint64_t link_bytes_per_us;   /* beta_eff, > 0 */
+    uint64_t encode_bytes_per_us; /* E = B / encode rate, rate > 0 */
+    uint64_t decode_bytes_per_us; /* D = B / decode rate, rate > 0 */
+    uint64_t fixed_ns;            /* alpha of a coded transfer */
+    uint64_t small_bytes;         /* calls with B <= this go RAW unsampled */
+    uint32_t exposed_encode_permil;
+    uint32_t exposed_decode_permil;
+    uint32_t min_gain_permil;
+    uint32_t reserved;
+} orc_policy;
+
+typedef struct {
+    uint32_t decision; /* 0 coded, 1 RAW by the cost model, 2 RAW as a small call */
+    uint32_t sample_values;
+    uint64_t predicted_bytes;
+    uint64_t raw_ns;
+    uint64_t coded_ns;
+} orc_plan;
+
+#define ORC_SAMPLE_BYTES 65536u
+
+/* 2^16 * log2(x) for x >= 1, rounded down, digit by digit: with
+ * x = 2^y * z, z in [1, 2), each squaring of z doubles log2(z), and its
+ * integer part is the next binary digit.  z is kept in fixed point with 31
+ * fraction bits, truncated after every squaring, so the result is exact at
+ * powers of two and at most one unit (plus the truncation, < 1e-5 unit)
+ * below 2^16 log2(x) elsewhere. */
+uint32_t orc_log2_q16(uint32_t x) {
+    uint32_t y = 0;
+    while ((x >> y) > 1u) y += 1;
+    uint64_t z = (uint64_t)x << (31 - y);
+    uint32_t frac = 0;
+    for (int i = 0; i < 16; ++i) {
+        z = (z * z) >> 31;
+        frac <<= 1;
+        if (z >= ((uint64_t)1 << 32)) {
+            z >>= 1;
+            frac |= 1u;
+        }
+    }
+    return (y << 16) | frac;
+}
+
+static uint64_t orc_ceil_div(uint64_t a, uint64_t b) { return a / b + (a % b != 0); }
+
+int orc_plan_call(int dtype, const void *in, uint64_t n, uint64_t chunk_bytes, const orc_policy *pol, orc_plan *plan) {
+    uint64_t ce = orc_chunk_elems(dtype, chunk_bytes);
+    if (ce == 0 || pol->link_bytes_per_us == 0 || pol->encode_bytes_per_us == 0 || pol->decode_bytes_per_us == 0 ||
+        pol->exposed_encode_permil > 1000 || pol->exposed_decode_permil > 1000 || pol->min_gain_permil > 1000 ||
+        pol->reserved != 0)
+        return ORC_INVALID;
+    memset(plan, 0, sizeof(*plan));
+    uint64_t eb = (uint64_t)orc_elem_bytes(dtype);
+    uint64_t B = n * eb;
+    /* Algorithm 1's fast path: a small call is committed RAW at once */
+    if (B <= pol->small_bytes) {
+        plan->decision = 2;
+        return ORC_OK;
+    }
+    /* the bounded sample and its statistics */
+    uint64_t S = n < ORC_SAMPLE_BYTES / eb ? n : ORC_SAMPLE_BYTES / eb;
+    uint8_t *e = (uint8_t *)malloc((size_t)S);
+    uint8_t *sm = (uint8_t *)malloc((size_t)(S * 3 + 1));
+    orc_split(dtype, in, S, e, sm);
+    uint32_t counts[256];
+    orc_histogram(e, S, counts);
+    free(e);
+    free(sm);
+    uint64_t hs = 0; /* sample entropy in bits, times 2^16 */
+    uint32_t nsym = 0;
+    for (int s = 0; s < 256; ++s) {
+        if (counts[s] == 0) continue;
+        nsym += 1;
+        hs += (uint64_t)counts[s] * (orc_log2_q16((uint32_t)S) - orc_log2_q16(counts[s]));
+    }
+    uint64_t h = hs / S; /* bits per value, times 2^16 */
+    /* the predicted coded frame: header, index and raw bytes as laid out,
+     * the coded symbols at the sample's entropy, each record's fixed part */
+    uint64_t C, sm_off, exp_off;
+    orc_layout(dtype, n, ce, &C, &sm_off, &exp_off);
+    uint64_t rec_fixed = orc_align4(ORC_REC_HDR + 32 + 2 * (uint64_t)nsym) + 4 * ORC_LANES + 8;
+    uint64_t P = exp_off + orc_ceil_div(n * h, (uint64_t)1 << 19) + C * rec_fixed;
+    uint64_t P_raw = orc_max_compressed_size(dtype, n, chunk_bytes);
+    /* Eq. (1) for RAW and for coding, in nanoseconds */
+    uint64_t t_raw = orc_ceil_div(P_raw * 1000, pol->link_bytes_per_us);
+    uint64_t t_code = pol->fixed_ns + orc_ceil_div(P * 1000, pol->link_bytes_per_us) +
+                      orc_ceil_div((uint64_t)pol->exposed_encode_permil * B, pol->encode_bytes_per_us) +
+                      orc_ceil_div((uint64_t)pol->exposed_decode_permil * B, pol->decode_bytes_per_us);
+    /* admission (predicted gain at least the minimum), then Eq. (2) */
+    int admitted = P < P_raw && (P_raw - P) * 1000 >= (uint64_t)pol->min_gain_permil * B;
+    plan->decision = (admitted && t_code < t_raw) ? 0u : 1u;
+    plan->sample_values = (uint32_t)S;
+    plan->predicted_bytes = P;
+    plan->raw_ns = t_raw;
+    plan->coded_ns = t_code;
+    return ORC_OK;
+}
+
+/* Plan the call, then write the frame the plan chose. */
+int orc_compress_arbitrated(int dtype, const void *in, uint64_t n, uint64_t chunk_bytes, const orc_policy *pol,
+                            orc_plan *plan, uint8_t *out, uint64_t cap, uint64_t *out_size) {
+    int st = orc_plan_call(dtype, in, n, chunk_bytes, pol, plan);
+    if (st != ORC_OK) return st;
+    return orc_compress_frame(dtype, in, n, chunk_bytes, out, cap, out_size, plan->decision != 0);
 }
 
 /* Decode one record into the chunk's exponents.  rec holds rec_len bytes

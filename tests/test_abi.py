@@ -123,3 +123,46 @@ def test_product_path_does_not_touch_the_oracle():
             if f.endswith((".py", ".hip", ".cpp", ".hpp", ".h")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in text.lower(), f
+
+
+def _policy(**kw):
+    base = dict(link_bytes_per_us=25000, encode_bytes_per_us=10**6, decode_bytes_per_us=10**6)
+    base.update(kw)
+    return uz.policy(**base)
+
+
+def test_arbitration_structs_match_the_header():
+    import ctypes
+    assert ctypes.sizeof(uz.uzip_policy) == 56 and uz.PLAN_BYTES == 32
+    assert ctypes.sizeof(uz.uzip_policy) == ctypes.sizeof(orc.Policy)
+    assert ctypes.sizeof(orc.Plan) == uz.PLAN_BYTES
+
+
+def test_arbitrated_argument_errors_return_synchronously():
+    n = 1000
+    cap = uz.uzip_max_compressed_size(uz.UZIP_BF16, n)
+    ws = uz.uzip_workspace_size(uz.UZIP_BF16, n)
+    call = lambda **kw: uz.uzip_compress_arbitrated(**{**dict(dtype=uz.UZIP_BF16, d_in=FAKE, num_elements=n,
+                                                              chunk_bytes=0, policy=_policy(), d_out=FAKE,
+                                                              out_capacity=cap, d_out_size=FAKE, d_plan=FAKE,
+                                                              d_workspace=FAKE, workspace_bytes=ws - 1,
+                                                              stream=None), **kw})
+    assert call(policy=None) == uz.UZIP_ERR_INVALID_ARGUMENT
+    for bad in [dict(link_bytes_per_us=0), dict(encode_bytes_per_us=0), dict(decode_bytes_per_us=0),
+                dict(exposed_encode_permil=1001), dict(exposed_decode_permil=1001), dict(min_gain_permil=1001),
+                dict(reserved=7)]:
+        assert call(policy=_policy(**bad)) == uz.UZIP_ERR_INVALID_ARGUMENT, bad
+    assert call(d_plan=None) == uz.UZIP_ERR_INVALID_ARGUMENT
+    assert call(d_plan=FAKE + 4) == uz.UZIP_ERR_INVALID_ARGUMENT
+    assert call(num_elements=1 << 44, out_capacity=1 << 62) == uz.UZIP_ERR_INVALID_ARGUMENT
+    assert call(out_capacity=cap - 1, workspace_bytes=ws) == uz.UZIP_ERR_CAPACITY
+    assert call() == uz.UZIP_ERR_INVALID_ARGUMENT  # workspace one byte short
+    ns = [100, 0]
+    bcall = lambda **kw: uz.uzip_compress_batched_arbitrated(**{**dict(
+        dtype=uz.UZIP_BF16, h_in=[FAKE, 0], h_num_elements=ns, chunk_bytes=0, policy=_policy(), h_out=[FAKE, FAKE],
+        h_out_capacity=[uz.uzip_max_compressed_size(uz.UZIP_BF16, k) for k in ns], d_out_sizes=FAKE, d_plans=FAKE,
+        d_workspace=FAKE, workspace_bytes=0, stream=None), **kw})
+    assert bcall(policy=None) == uz.UZIP_ERR_INVALID_ARGUMENT
+    assert bcall(policy=_policy(min_gain_permil=2000)) == uz.UZIP_ERR_INVALID_ARGUMENT
+    assert bcall(d_plans=None) == uz.UZIP_ERR_INVALID_ARGUMENT
+    assert bcall() == uz.UZIP_ERR_INVALID_ARGUMENT  # no workspace
