@@ -62,6 +62,8 @@ def parse():
                     choices=["grad_bucket", "pr1", "fp32_grad", "llama8b", "small_batch", "fp16_act", "fp8_e4m3",
                              "fp8_e5m2"])
     ap.add_argument("--chunk-bytes", type=int, default=0, help="uncompressed chunk size (0: the dtype's default)")
+    ap.add_argument("--link-gbps", type=float, default=0.0,
+                    help="compress with the per-call arbitration for a link of this many GB/s (0: plain compress)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum CPU-oracle time to accumulate")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     return ap.parse_args()
@@ -210,8 +212,21 @@ def main():
         sizes = torch.empty(1, dtype=torch.int64, device=dev)
         status = torch.empty(1, dtype=torch.int32, device=dev)
 
+    pol = None
+    if args.link_gbps > 0:
+        # codec rates near this codec's own measured bf16 throughput; nothing
+        # of the codec time hidden by overlap; a 10 us fixed cost per coded call
+        pol = uz.policy(link_bytes_per_us=int(args.link_gbps * 1000), encode_bytes_per_us=1_250_000,
+                        decode_bytes_per_us=1_600_000, fixed_ns=10_000, small_bytes=0,
+                        exposed_encode_permil=1000, exposed_decode_permil=1000, min_gain_permil=20)
+        plans = torch.empty(4 * len(ts), dtype=torch.int64, device=dev)
+
     def compress():
-        if batched:
+        if pol is not None and batched:
+            uz.compress_batched_arbitrated(ts, pol, cb, outs=outs, ws=ws, out_sizes=sizes, plans=plans)
+        elif pol is not None:
+            uz.compress_arbitrated(ts[0], pol, cb, out=outs[0], ws=ws, out_size=sizes, plan=plans)
+        elif batched:
             uz.compress_batched(ts, cb, outs=outs, ws=ws, out_sizes=sizes)
         else:
             uz.compress(ts[0], cb, out=outs[0], ws=ws, out_size=sizes)
@@ -272,7 +287,11 @@ def main():
     exp_offs = [((((64 + 8 * ((n + chunk_elems - 1) // chunk_elems + 1)) + 15) // 16 * 16 + rb * n) + 15) // 16 * 16
                 for n in ns]
     rec_bytes = sum(s - e for s, e in zip(comp_sizes, exp_offs))
-    enc_bytes = n_total * eb + n_total * rb + rec_bytes
+    decisions = [p["decision"] for p in uz.plans_as_dicts(plans)] if pol is not None else []
+    # a RAW plan's k_encode only splits (k_compact writes the RAW records)
+    raw_planned = sum(n for n, dcs in zip(ns, decisions) if dcs != uz.UZIP_PLAN_CODED)
+    enc_bytes = n_total * eb + n_total * rb + rec_bytes - sum(
+        s - e for s, e, dcs in zip(comp_sizes, exp_offs, decisions) if dcs != uz.UZIP_PLAN_CODED)
     dec_bytes = n_total * rb + rec_bytes + sum(64 + 8 * ((n + chunk_elems - 1) // chunk_elems + 1) for n in ns) + \
         n_total * eb
     if enc_kernel_ms >= dec_kernel_ms:
@@ -297,7 +316,7 @@ def main():
     cpu = None
     oracle_match = None
     if not args.no_cpu_baseline:
-        cpu, oracle_match = cpu_baseline(ts, outs, comp_sizes, code, args.cpu_seconds, cb)
+        cpu, oracle_match = cpu_baseline(ts, outs, comp_sizes, code, args.cpu_seconds, cb, pol)
 
     med_c = comp_ms[len(comp_ms) // 2]
     med_d = dec_ms[len(dec_ms) // 2]
@@ -330,6 +349,12 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
+    if pol is not None:
+        line["config"]["arbitration"] = {f: getattr(pol, f) for f, _ in pol._fields_}
+        line["plans"] = {"coded": decisions.count(0), "raw": decisions.count(1), "raw_small": decisions.count(2),
+                         "raw_planned_values": raw_planned}
+        if len(ts) == 1:
+            line["plans"]["plan"] = uz.plans_as_dicts(plans)[0]
     print(json.dumps(line), flush=True)
     if not roundtrip_ok or oracle_match is False:
         sys.exit(1)
@@ -359,7 +384,7 @@ def copy_reference(ts, steps):
     return 2 * nbytes / (ms * 1e-3) / 1e9
 
 
-def cpu_baseline(ts, outs, comp_sizes, code, min_seconds, chunk_bytes):
+def cpu_baseline(ts, outs, comp_sizes, code, min_seconds, chunk_bytes, pol=None):
     """The oracle (plain single-threaded C) on a bounded sample of the same
     workload: whole buffers, in order, up to 512 MiB of input; passes repeat
     until min_seconds of CPU time have been spent.  Also compares the oracle's
@@ -379,7 +404,11 @@ def cpu_baseline(ts, outs, comp_sizes, code, min_seconds, chunk_bytes):
     host = [W.bits_numpy(ts[i]) for i in picked]
     match = True
     for i, h in zip(picked, host):
-        want = oracle.compress(code, h, chunk_bytes)
+        if pol is None:
+            want = oracle.compress(code, h, chunk_bytes)
+        else:  # the arbitrated frame (the plan may have chosen RAW)
+            opol = oracle.Policy(**{f: getattr(pol, f) for f, _ in pol._fields_})
+            want = oracle.compress_arbitrated(code, h, opol, chunk_bytes)[0]
         got = outs[i][:comp_sizes[i]].cpu().numpy()
         match = match and np.array_equal(want, got)
     sample_bytes = sum(h.size * h.itemsize for h in host)

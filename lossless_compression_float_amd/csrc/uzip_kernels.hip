@@ -462,6 +462,8 @@ __global__ __launch_bounds__(64) void k_encode(EncParams p) {
     // ---- the pair: buffer and chunks (wave-uniform); half-wave h codes chunk c0 + h ----
     const uint64_t q = blockIdx.x;
     const uint32_t bi = p.nbuf == 1 ? 0u : uniform_u32(find_enc_pair_buffer(p.descs, p.nbuf, q));
+    // a buffer that the per-call arbitration sends RAW is written by k_raw_frame
+    if (p.plans != nullptr && uniform_u32(gload<uint32_t>(&p.plans[bi].decision)) != UZIP_PLAN_CODED) return;
     const EncDesc d = p.nbuf == 1 ? p.single : load_enc_desc(p.descs + bi);
     const uint64_t ce = p.chunk_elems;
     const uint64_t n = uniform_u64(d.n);
@@ -629,17 +631,6 @@ __global__ __launch_bounds__(64) void k_encode(EncParams p) {
         }
     }
     __syncthreads();
-
-    // ---- a RAW plan of the per-call arbitration: the sign+mantissa bytes are
-    // in place; every record is RAW (k_compact copies the exponents) ----
-    if (p.plans != nullptr && uniform_u32(gload<uint32_t>(&p.plans[bi].decision)) != UZIP_PLAN_CODED) {
-        if (valid && lj == 0) {
-            const uint32_t raw_i = (uint32_t)raw_record_bytes(ni);
-            gstore<uint4>(slot, make_uint4(1u, 0u, ni, raw_i));
-            gstore<uint32_t>(p.rec_sizes + g, raw_i);
-        }
-        return;
-    }
 
     // ---- normalise the counts to a table of 4096 (lane lj owns symbols 8lj..8lj+7) ----
     // Reserve one slot per present symbol, share R = 4096 - nsym slots by the
@@ -905,7 +896,7 @@ __device__ inline uint64_t ceil_div_u64(uint64_t a, uint64_t b) { return a / b +
 template <int DT>
 __global__ __launch_bounds__(256) void k_plan(EncParams p) {
     constexpr uint32_t EB = Fmt<DT>::EB;
-    __shared__ uint32_t hist[256];
+    __shared__ uint32_t hist[8][257];  // 8 sub-histograms (thread t counts into t & 7), padded rows
     __shared__ uint64_t part[4];
     __shared__ uint32_t present[4];
     const uint32_t t = threadIdx.x;
@@ -918,12 +909,36 @@ __global__ __launch_bounds__(256) void k_plan(EncParams p) {
         return;
     }
     const uint32_t S = (uint32_t)min<uint64_t>(n, 65536u / EB);
-    hist[t] = 0;
+    for (uint32_t k = 0; k < 8; ++k) hist[k][t] = 0;
+    if (t < 8) hist[t][256] = 0;
     __syncthreads();
+    uint32_t *sub = hist[t & 7];
+    // the sample in one round of loads: thread t takes the whole 16-byte
+    // units t + 256 k (k < 16) of the at most 64 KiB; a partial last unit is
+    // read value by value (a 128-bit load that crosses the end of the range
+    // would read its last dword as zero)
     const rsrc_t rin = make_rsrc(d.in, S * EB);
-    for (uint32_t i = t; i < S; i += 256) atomicAdd(&hist[exponent_of<DT>(bld_value<DT>(rin, i * EB))], 1u);
+    constexpr uint32_t VPU = 16 / EB;
+    const uint32_t units = S / VPU;
+    uint4 q[16];
+#pragma unroll
+    for (uint32_t k = 0; k < 16; ++k) q[k] = bld128(rin, t + 256 * k < units ? 16 * (t + 256 * k) : kOutOfRange);
+#pragma unroll
+    for (uint32_t k = 0; k < 16; ++k) {
+        if (t + 256 * k >= units) continue;
+        const uint32_t w[4] = {q[k].x, q[k].y, q[k].z, q[k].w};
+#pragma unroll
+        for (uint32_t j = 0; j < VPU; ++j) {
+            const uint32_t v = EB == 4 ? w[j] : (w[j / (4 / EB)] >> (8 * EB * (j % (4 / EB)))) & ((1u << (8 * EB)) - 1u);
+            atomicAdd(&sub[exponent_of<DT>(v)], 1u);
+        }
+    }
+    if (t == 0)
+        for (uint32_t i = units * VPU; i < S; ++i) atomicAdd(&sub[exponent_of<DT>(bld_value<DT>(rin, i * EB))], 1u);
     __syncthreads();
-    const uint32_t c = hist[t];
+    uint32_t c = 0;
+#pragma unroll
+    for (uint32_t k = 0; k < 8; ++k) c += hist[k][t];
     const uint64_t term = c ? uint64_t(c) * (log2_q16(S) - log2_q16(c)) : 0ull;
     const uint64_t wsum = wave_sum_u64(term);
     const uint32_t wpresent = (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(c != 0));
@@ -951,6 +966,112 @@ __global__ __launch_bounds__(256) void k_plan(EncParams p) {
     gstore<uint2>(out + 8, make_uint2((uint32_t)pred, (uint32_t)(pred >> 32)));
     gstore<uint2>(out + 16, make_uint2((uint32_t)t_raw, (uint32_t)(t_raw >> 32)));
     gstore<uint2>(out + 24, make_uint2((uint32_t)t_code, (uint32_t)(t_code >> 32)));
+}
+
+// The frame of a buffer that its plan sends RAW, in one pass over the input:
+// every record is RAW, so record c starts at c * align16(16 + chunk_elems)
+// with no scan.  A workgroup (256 threads) takes a chunk at a time: each
+// thread reads units of 16 values (EB 128-bit loads) and writes their raw
+// bytes to the sign+mantissa region and their symbol bytes to the record
+// (128-bit stores); the chunk's ragged end goes value by value, with the
+// record's zero padding.  Thread 0 writes the record header and the chunk's
+// index entry; the buffer's last chunk also writes the final index entry,
+// the header, the zero gaps and the compressed size.  Coded buffers are left
+// to k_encode and k_compact.
+__device__ inline uint32_t find_enc_chunk_buffer(const EncDesc *d, uint32_t nbuf, uint64_t g) {
+    uint32_t lo = 0, hi = nbuf - 1;  // the last buffer whose first chunk is <= g (empty ones own none)
+    while (lo < hi) {
+        const uint32_t mid = (lo + hi + 1) >> 1;
+        if (gload<uint64_t>(&d[mid].chunk_first) <= g) lo = mid;
+        else hi = mid - 1;
+    }
+    return lo;
+}
+
+template <int DT>
+__global__ __launch_bounds__(256) void k_raw_frame(EncParams p) {
+    constexpr uint32_t EB = Fmt<DT>::EB, R = Fmt<DT>::R;
+    const uint32_t t = threadIdx.x;
+    for (uint64_t g = blockIdx.x; g < p.total_chunks; g += gridDim.x) {
+        const uint32_t bi = p.nbuf == 1 ? 0u : uniform_u32(find_enc_chunk_buffer(p.descs, p.nbuf, g));
+        if (uniform_u32(gload<uint32_t>(&p.plans[bi].decision)) == UZIP_PLAN_CODED) continue;
+        const EncDesc d = p.nbuf == 1 ? p.single : load_enc_desc(p.descs + bi);
+        const uint64_t ce = p.chunk_elems, n = uniform_u64(d.n), chunks = uniform_u64(d.chunks);
+        const uint64_t c = g - uniform_u64(d.chunk_first);
+        const uint32_t ni = (uint32_t)min<uint64_t>(ce, n - c * ce);
+        const uint64_t rrb = raw_record_bytes(ce), off = c * rrb;
+        uint8_t *out = d.out;
+        const uint64_t exp_off = uniform_u64(d.exp_off), sm_off = uniform_u64(d.sm_off);
+        const rsrc_t rin = make_rsrc(d.in + c * ce * EB, ni * EB);
+        const rsrc_t rsm = make_rsrc(out + sm_off + c * ce * R, ni * R);
+        const uint32_t rbytes = (uint32_t)raw_record_bytes(ni);
+        const rsrc_t rrec = make_rsrc(out + exp_off + off, rbytes);
+        const uint32_t nu = ni / 16;
+        constexpr uint32_t U = 4;  // units per thread in flight
+        for (uint32_t u0 = t; u0 < nu; u0 += 256 * U) {
+            uint4 qs[U][EB];
+#pragma unroll
+            for (uint32_t j = 0; j < U; ++j) {
+                const uint32_t u = u0 + 256 * j;
+#pragma unroll
+                for (uint32_t k = 0; k < EB; ++k) qs[j][k] = bld128(rin, u < nu ? 16 * EB * u + 16 * k : kOutOfRange);
+            }
+#pragma unroll
+            for (uint32_t j = 0; j < U; ++j) {
+                const uint32_t u = u0 + 256 * j;
+                const uint32_t so = u < nu ? 16 * R * u : kOutOfRange, eo = u < nu ? kRecHeaderBytes + 16 * u : kOutOfRange;
+                uint32_t w[4 * EB];
+#pragma unroll
+                for (uint32_t k = 0; k < EB; ++k) {
+                    w[4 * k] = qs[j][k].x; w[4 * k + 1] = qs[j][k].y; w[4 * k + 2] = qs[j][k].z; w[4 * k + 3] = qs[j][k].w;
+                }
+                uint32_t ex[4] = {0, 0, 0, 0}, rw[12] = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+                for (uint32_t k = 0; k < 16; ++k) {
+                    const uint32_t v = EB == 4 ? w[k] : (w[k / (4 / EB)] >> (8 * EB * (k % (4 / EB)))) & ((1u << (8 * EB)) - 1u);
+                    ex[k >> 2] |= exponent_of<DT>(v) << (8 * (k & 3));
+                    if (R == 1) rw[k >> 2] |= raw_of<DT>(v) << (8 * (k & 3));
+                    if (R == 3) {  // 3 bytes at byte 3k of rw
+                        const uint32_t b = 3 * k, sm = raw_of<DT>(v);
+                        rw[b >> 2] |= sm << (8 * (b & 3));
+                        if ((b & 3) > 1) rw[(b >> 2) + 1] |= sm >> (32 - 8 * (b & 3));
+                    }
+                }
+                __builtin_amdgcn_raw_buffer_store_b128(u32x4{ex[0], ex[1], ex[2], ex[3]}, rrec, (int)eo, 0, 0);
+#pragma unroll
+                for (uint32_t k = 0; k < R; ++k)
+                    __builtin_amdgcn_raw_buffer_store_b128(u32x4{rw[4 * k], rw[4 * k + 1], rw[4 * k + 2], rw[4 * k + 3]}, rsm,
+                                                           (int)(so + 16 * k), 0, 0);
+            }
+        }
+        // the chunk's ragged end: the last unit of symbol bytes with its zero
+        // padding, and the raw bytes value by value
+        if (nu * 16 < ni && t == 0) {
+            uint32_t ex[4] = {0, 0, 0, 0};
+            for (uint32_t k = 0; 16 * nu + k < ni; ++k) {
+                const uint32_t v = bld_value<DT>(rin, (16 * nu + k) * EB);
+                ex[k >> 2] |= exponent_of<DT>(v) << (8 * (k & 3));
+                const uint32_t sm = raw_of<DT>(v);
+                for (uint32_t r = 0; r < R; ++r)
+                    __builtin_amdgcn_raw_buffer_store_b8((unsigned char)(sm >> (8 * r)), rsm, (int)((16 * nu + k) * R + r), 0, 0);
+            }
+            __builtin_amdgcn_raw_buffer_store_b128(u32x4{ex[0], ex[1], ex[2], ex[3]}, rrec, (int)(kRecHeaderBytes + 16 * nu), 0, 0);
+        }
+        if (t == 0) {
+            gstore<uint4>(out + exp_off + off, make_uint4(1u, 0u, ni, rbytes));
+            gstore<uint64_t>(out + kHeaderBytes + 8 * c, off);
+        }
+        if (c + 1 == chunks) {  // the buffer's last record
+            const uint64_t total = exp_off + off + rbytes;
+            if (t == 0) {
+                gstore<uint64_t>(out + kHeaderBytes + 8 * chunks, off + rbytes);
+                gstore<uint64_t>(d.out_size, total);
+            }
+            if (t < 16) gstore<uint32_t>(out + 4 * t, header_word(t, p.dtype, p.chunk_elems, n, chunks, sm_off, exp_off, total));
+            for (uint64_t k = kHeaderBytes + 8 * (chunks + 1) + t; k < sm_off; k += 256) gstore<uint8_t>(out + k, 0);
+            for (uint64_t k = sm_off + uint64_t(R) * n + t; k < exp_off; k += 256) gstore<uint8_t>(out + k, 0);
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -981,8 +1102,11 @@ __global__ __launch_bounds__(128 * kCompactPairs) void k_compact(EncParams p) {
     const uint64_t q = uint64_t(uniform_u32(s_ticket)) * kCompactPairs + (w >> 1);
     const uint32_t r = w & 1;
     if (q >= p.total_pairs) return;
-    const EncDesc d = p.nbuf == 1 ? p.single
-                                  : load_enc_desc(p.descs + uniform_u32(find_enc_pair_buffer(p.descs, p.nbuf, q)));
+    const uint32_t bi = p.nbuf == 1 ? 0u : uniform_u32(find_enc_pair_buffer(p.descs, p.nbuf, q));
+    // RAW-planned buffers are complete (k_raw_frame); their tiles take no part
+    // in any other buffer's look-back
+    if (p.plans != nullptr && uniform_u32(gload<uint32_t>(&p.plans[bi].decision)) != UZIP_PLAN_CODED) return;
+    const EncDesc d = p.nbuf == 1 ? p.single : load_enc_desc(p.descs + bi);
     const uint64_t ce = p.chunk_elems;
     const uint64_t n = uniform_u64(d.n);
     const uint64_t c0 = 2 * (q - uniform_u64(d.pair_first));
@@ -1173,6 +1297,47 @@ __device__ inline uint32_t merge_value(uint32_t ex, uint32_t smv) {
     if (DT == 2) return ((smv & 0x800000u) << 8) | (ex << 23) | (smv & 0x7FFFFFu);
     if (DT == 3) return (ex << 8) | (smv & 0xFFu);
     return ex;
+}
+
+// 16 values rebuilt from 16 symbol bytes E and their 16 R raw bytes S, stored
+// as 16 EB bytes at `off` of r (an out-of-range offset drops the stores)
+template <int DT>
+__device__ inline void store_unit(rsrc_t r, uint32_t off, const uint4 &E, const uint4 *S) {
+    const uint32_t e[4] = {E.x, E.y, E.z, E.w};
+    if (DT == 4) {
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4{E.x, E.y, E.z, E.w}, r, (int)off, 0, 0);
+    } else if (DT == 1 || DT == 3) {
+        const uint32_t sv[4] = {S[0].x, S[0].y, S[0].z, S[0].w};
+        uint32_t o[8];
+#pragma unroll
+        for (uint32_t d = 0; d < 4; ++d) {
+            // low and high byte of four values at once, then interleaved
+            uint32_t lo = sv[d], hi = e[d];
+            if (DT == 1) {
+                lo = (sv[d] & 0x7F7F7F7Fu) | ((e[d] & 0x01010101u) << 7);
+                hi = (sv[d] & 0x80808080u) | ((e[d] >> 1) & 0x7F7F7F7Fu);
+            }
+            o[2 * d] = __builtin_amdgcn_perm(hi, lo, 0x05010400u);
+            o[2 * d + 1] = __builtin_amdgcn_perm(hi, lo, 0x07030602u);
+        }
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4{o[0], o[1], o[2], o[3]}, r, (int)off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4{o[4], o[5], o[6], o[7]}, r, (int)(off + 16), 0, 0);
+    } else {
+        const uint32_t w[12] = {S[0].x, S[0].y, S[0].z, S[0].w, S[1].x, S[1].y,
+                                S[1].z, S[1].w, S[2].x, S[2].y, S[2].z, S[2].w};
+        uint32_t o[16];
+#pragma unroll
+        for (uint32_t k = 0; k < 16; ++k) {
+            // raw field k: bytes 3k .. 3k + 2 of w
+            const uint32_t b = 3 * k, d = b >> 2;
+            const uint32_t sm = __builtin_amdgcn_alignbyte(w[d + 1 < 12 ? d + 1 : 11], w[d], b & 3) & 0xFFFFFFu;
+            o[k] = merge_value<2>((e[k >> 2] >> (8 * (k & 3))) & 0xFFu, sm);
+        }
+#pragma unroll
+        for (uint32_t q = 0; q < 4; ++q)
+            __builtin_amdgcn_raw_buffer_store_b128(u32x4{o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]}, r,
+                                                   (int)(off + 16 * q), 0, 0);
+    }
 }
 
 template <int DT>
@@ -1516,9 +1681,28 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
         ok = ok && !endbad;
         // ---- chunks stored RAW: exponent bytes straight from the record ----
         if (raw_run) {
-            const uint32_t ob = (h ? vals0 : 0u) * EB, sb = (h ? vals0 : 0u) * R;
-            for (uint32_t i = lj; i < ni; i += 32) {
-                const uint32_t v = merge_value<DT>(bld8(rrec, rel + kRecHeaderBytes + i), bload_sm<DT>(rsm, sb + i * R));
+            // units of 16 values: 16 exponent bytes and 16 R raw bytes in,
+            // 16 EB bytes out, all 128-bit; four units per lane in flight
+            const uint32_t ob = (h ? vals0 : 0u) * EB, sb = (h ? vals0 : 0u) * R, eo = rel + kRecHeaderBytes;
+            const uint32_t nu = ni / 16;
+            constexpr uint32_t U = 4, RS = R > 0 ? R : 1;
+            for (uint32_t u0 = lj; u0 < nu; u0 += 32 * U) {
+                uint4 E[U], S[U][RS];
+#pragma unroll
+                for (uint32_t k = 0; k < U; ++k) {
+                    const uint32_t u = u0 + 32 * k;
+                    E[k] = bld128(rrec, u < nu ? eo + 16 * u : kOutOfRange);
+#pragma unroll
+                    for (uint32_t r = 0; r < R; ++r) S[k][r] = bld128(rsm, u < nu ? sb + 16 * R * u + 16 * r : kOutOfRange);
+                }
+#pragma unroll
+                for (uint32_t k = 0; k < U; ++k) {
+                    const uint32_t u = u0 + 32 * k;
+                    store_unit<DT>(rout, u < nu ? ob + 16 * EB * u : kOutOfRange, E[k], S[k]);
+                }
+            }
+            for (uint32_t i = 16 * nu + lj; i < ni; i += 32) {  // the chunk's last values
+                const uint32_t v = merge_value<DT>(bld8(rrec, eo + i), bload_sm<DT>(rsm, sb + i * R));
                 bst_value<DT>(rout, ob + i * EB, v);
             }
         }
@@ -1556,6 +1740,15 @@ hipError_t launch_compress(const EncParams &ep, hipStream_t stream) {
         default: k_encode<4><<<grid, dim3(64), 0, stream>>>(ep); break;
         }
         if (g_profile.stop) (void)hipEventRecord(g_profile.stop, stream);
+        if (ep.plans != nullptr) {
+            const dim3 rgrid((uint32_t)(ep.total_chunks < 2048 ? ep.total_chunks : 2048));
+            switch (kernel_format(ep.dtype)) {
+            case 1: k_raw_frame<1><<<rgrid, dim3(256), 0, stream>>>(ep); break;
+            case 2: k_raw_frame<2><<<rgrid, dim3(256), 0, stream>>>(ep); break;
+            case 3: k_raw_frame<3><<<rgrid, dim3(256), 0, stream>>>(ep); break;
+            default: k_raw_frame<4><<<rgrid, dim3(256), 0, stream>>>(ep); break;
+            }
+        }
         const dim3 cgrid((uint32_t)((ep.total_pairs + kCompactPairs - 1) / kCompactPairs));
         switch (kernel_format(ep.dtype)) {
         case 1: k_compact<1><<<cgrid, dim3(128 * kCompactPairs), 0, stream>>>(ep); break;
