@@ -27,7 +27,7 @@ def _host(buf: torch.Tensor, size: int) -> np.ndarray:
 def _check_frame(b: np.ndarray, code: int, n: int, chunk_elems: int):
     """Header, index and record headers of one compressed buffer (any size)."""
     C = (n + chunk_elems - 1) // chunk_elems
-    r = 1 if code == orc.BF16 else 3
+    r = {orc.BF16: 1, orc.FP32: 3, orc.FP16: 1, orc.FP8_E4M3: 0, orc.FP8_E5M2: 0}[code]
     hdr = np.frombuffer(b[:64].tobytes(), dtype=np.uint64)
     assert int.from_bytes(b[0:4].tobytes(), "little") == 0x31505A55
     assert int(b[6]) == code and int(b[7]) == 12 and int(b[8]) == 32 and int(b[9]) == r
@@ -53,7 +53,7 @@ def _check_frame(b: np.ndarray, code: int, n: int, chunk_elems: int):
 
 
 def _same_bits(a: torch.Tensor, b: torch.Tensor) -> bool:
-    v = torch.int16 if a.dtype == torch.bfloat16 else torch.int32
+    v = {1: torch.uint8, 2: torch.int16, 4: torch.int32}[a.element_size()]
     return torch.equal(a.view(v), b.view(v))
 
 
@@ -116,3 +116,41 @@ def test_llama3_8b_weight_set_16gb_one_batched_call():
     torch.cuda.synchronize()
     assert st.cpu().tolist() == [0] * len(ts)
     assert all(_same_bits(a, b) for a, b in zip(ts, backs))
+
+
+@pytest.mark.parametrize("name", ["fp16_act", "fp8_e4m3", "fp8_e5m2"])
+def test_fp16_and_fp8_workloads_equal_oracle(name):
+    if name == "fp16_act":
+        t, code, ce = workloads.fp16_activations(workloads.FP16_ACT_N, device=DEV, seed=5), orc.FP16, 32768
+    else:
+        fmt = torch.float8_e4m3fn if name == "fp8_e4m3" else torch.float8_e5m2
+        code = orc.FP8_E4M3 if name == "fp8_e4m3" else orc.FP8_E5M2
+        t, ce = workloads.fp8_weights(workloads.FP8_WEIGHT_N, device=DEV, seed=6, fmt=fmt), 65536
+    buf, size = uz.compress(t)
+    torch.cuda.synchronize()
+    got = _host(buf, int(size.item()))
+    _check_frame(got, code, t.numel(), ce)
+    assert np.array_equal(got, orc.compress(code, workloads.bits_numpy(t)))
+    back, st = uz.decompress(buf, t.dtype, t.numel(), in_bytes=got.size)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0 and _same_bits(back, t)
+
+
+@pytest.mark.parametrize("link", [50_000, 4_000_000])
+def test_gradient_bucket_arbitrated_equals_oracle(link):
+    """The benchmark's arbitration policy at 50 GB/s (coded) and 4 TB/s (RAW)."""
+    fields = dict(link_bytes_per_us=link, encode_bytes_per_us=1_250_000, decode_bytes_per_us=1_600_000,
+                  fixed_ns=10_000, small_bytes=0, exposed_encode_permil=1000, exposed_decode_permil=1000,
+                  min_gain_permil=20, reserved=0)
+    t = workloads.gradient_bucket(workloads.GRAD_BUCKET_N, device=DEV, seed=1)
+    buf, size, plan = uz.compress_arbitrated(t, uz.policy(**fields))
+    torch.cuda.synchronize()
+    got = _host(buf, int(size.item()))
+    _check_frame(got, orc.BF16, t.numel(), 32768)
+    want, want_plan = orc.compress_arbitrated(orc.BF16, workloads.bits_numpy(t), orc.Policy(**fields))
+    assert uz.plans_as_dicts(plan)[0] == want_plan
+    assert want_plan["decision"] == (uz.UZIP_PLAN_CODED if link == 50_000 else uz.UZIP_PLAN_RAW)
+    assert np.array_equal(got, want)
+    back, st = uz.decompress(buf, torch.bfloat16, t.numel(), in_bytes=got.size)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0 and _same_bits(back, t)
