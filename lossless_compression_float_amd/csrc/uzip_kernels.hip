@@ -1275,7 +1275,8 @@ __global__ void k_dec_validate(DecParams p) {
 // LDS of one decode workgroup (two chunks), 10 KiB:
 //   s_sym [2][4096] u8   slot -> rank of its symbol among the present symbols
 //   s_rk  [2][256]  u32  rank -> (4096 - f) | symbol << 12 | c0 << 20
-// so one step costs two dependent LDS reads.  A workgroup decodes a pair of
+// so one step costs two dependent LDS reads; fp32 adds s_slot [2][4096] u32
+// (slot -> its rank's entry, 34 KiB in all) and reads once per step.  A workgroup decodes a pair of
 // consecutive chunks of one buffer (half-wave h decodes chunk 2p + h), so the
 // record, sign+mantissa and output regions of the pair each get one buffer
 // resource.  Renormalisation words come from a register window (two 16-bit
@@ -1347,11 +1348,21 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
     // bf16 and fp16: 2-byte values with one raw byte, which share the main
     // loop below (raw bytes by dword and bpermute, two steps per store)
     constexpr bool kB16 = DT == 1 || DT == 3;
+    // refills found stale by the scalar refill masks and reloaded in a rare
+    // branch (bf16, fp16, fp8); fp32 also loads the pair 64 words further
+    constexpr bool kScalarStale = DT != 2;
     // one LDS array, so that the slot table sits at address 0 and a slot's
     // address is a single and-or of the state
-    __shared__ __align__(16) uint32_t s_dec[2 * kTableSize / 4 + 2 * 256];
+    // fp32 (about one wave per SIMD, so each step's latency is exposed) looks
+    // up its entry in one read of a direct slot table, kTableSize u32 per
+    // chunk (32 KiB per workgroup); the others read the slot's rank byte,
+    // then the rank's entry (10 KiB per workgroup, more waves per CU)
+    constexpr bool kDirect = DT == 2;
+    constexpr uint32_t kSlotWords = kDirect ? 2 * kTableSize : 2 * kTableSize / 4;
+    __shared__ __align__(16) uint32_t s_dec[kSlotWords + 2 * 256];
     uint8_t(*s_sym)[kTableSize] = reinterpret_cast<uint8_t(*)[kTableSize]>(s_dec);
-    uint32_t(*s_rk)[256] = reinterpret_cast<uint32_t(*)[256]>(s_dec + 2 * kTableSize / 4);
+    uint32_t(*s_slot)[kTableSize] = reinterpret_cast<uint32_t(*)[kTableSize]>(s_dec);
+    uint32_t(*s_rk)[256] = reinterpret_cast<uint32_t(*)[256]>(s_dec + kSlotWords);
 
     const uint32_t lane = threadIdx.x;
     const uint32_t h = lane >> 5, lj = lane & 31;
@@ -1443,7 +1454,11 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
             for (uint32_t m = 0; m < nsym; ++m) {
                 const uint32_t em = s_rk[h][m];
                 const uint32_t fs = kTableSize - (em & 0xFFFu), c0s = em >> 20;
-                for (uint32_t k = lj; k < fs; k += 32) s_sym[h][c0s + k] = (uint8_t)m;
+                if (kDirect) {
+                    for (uint32_t k = lj; k < fs; k += 32) s_slot[h][c0s + k] = em;
+                } else {
+                    for (uint32_t k = lj; k < fs; k += 32) s_sym[h][c0s + k] = (uint8_t)m;
+                }
             }
         }
         __syncthreads();
@@ -1497,18 +1512,18 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
         // (a refill takes 64 words, a step at most 32); one that refills again
         // two or three steps after its last refill (more than 16 words per
         // step: near-uniform exponents only) finds in NX a pair loaded before
-        // that refill.  bf16 detects this from the refill masks of the last
-        // three steps (scalar) and then reloads synchronously; fp32, whose
-        // waves are too few to hide a branch, also loads the pair 64 words
-        // further (NB), which is the right one exactly in that case.
+        // that refill.  bf16, fp16 and fp8 detect this from the refill masks
+        // of the last three steps (scalar) and then reload synchronously;
+        // fp32, whose waves are too few to hide a branch, also loads the pair
+        // 64 words further (NB), which is the right one exactly in that case.
         const uint32_t wstart = rel + (uint32_t)words_offset(nsym);  // byte offset of word 0
         uint32_t P = bld32(rrec, wstart + 4 * lj);                    // words 2lj, 2lj + 1
         uint32_t lim = 32 + 32 * (lj >> 4);                           // end of the lane's block
         const uint32_t rbase = wstart + 64 + 4 * (lj & 15u);          // byte offset of its next pair = 2 lim + rbase
         uint32_t NX[4], NB[4];
         NX[0] = NX[1] = NX[2] = NX[3] = bld32(rrec, 2 * lim + rbase); // words 64 + 2lj, 65 + 2lj
-        NB[0] = NB[1] = NB[2] = NB[3] = kB16 ? 0u : bld32(rrec, 2 * lim + rbase + 128);
-        uint64_t R1 = 0, R2 = 0, R3 = 0;  // bf16: refill masks of the last three steps
+        NB[0] = NB[1] = NB[2] = NB[3] = kScalarStale ? 0u : bld32(rrec, 2 * lim + rbase + 128);
+        uint64_t R1 = 0, R2 = 0, R3 = 0;  // refill masks of the last three steps (kScalarStale)
         uint32_t age = 4;                  // fp32: steps since the lane's last refill
         const uint32_t lanebits = (h << 5) << 2;
         const uint32_t hsym = h << kProbBits, hrk = h << 8;  // this half's table rows
@@ -1516,6 +1531,7 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
         uint32_t offv = 0;  // words consumed by this half
         const uint8_t *s_symf = &s_sym[0][0];
         const uint32_t *s_rkf = &s_rk[0][0];
+        const uint32_t *s_slotf = &s_slot[0][0];
         // One step of both half-waves.  act = lanes holding a value this step
         // (TAIL steps only: in the main loop every lane of a running half
         // holds one, and lanes of a half that is not running never reach the
@@ -1525,9 +1541,9 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
         // x - (g * (x >> 12) + c0).
         // sp: the value's sign+mantissa, for bf16 as the byte in bytes 0 and 1
         auto step = [&](uint32_t t, uint64_t act, bool tail, uint32_t sp, int par, bool store) __attribute__((always_inline)) {
-            uint32_t slot_addr;  // (x & 4095) | this half's row: the byte address in s_sym
+            uint32_t slot_addr;  // (x & 4095) | this half's row: the index in s_sym / s_slot
             asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(slot_addr) : "v"(x), "s"(kTableSize - 1), "v"(hsym));
-            const uint32_t em = s_rkf[s_symf[slot_addr] | hrk];
+            const uint32_t em = kDirect ? s_slotf[slot_addr] : s_rkf[s_symf[slot_addr] | hrk];
             const uint32_t xd = x - (__umul24(em & 0xFFFu, x >> kProbBits) + (em >> 20));
             // (the and with act also puts the mask in registers written by the
             // scalar unit: inline asm below reads it, and the hardware needs
@@ -1554,7 +1570,7 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
             // (plain selects: the mask comes from a vector compare, and the
             // compiler spaces its reads as the hardware requires)
             const bool used_up = offv >= lim;
-            if (kB16) {
+            if (kScalarStale) {
                 const uint64_t um = __builtin_amdgcn_ballot_w64(used_up);
                 const uint64_t stale = um & (R2 | R3);
                 R3 = R2;
@@ -1575,7 +1591,7 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
             }
             lim += used_up ? 64u : 0u;
             NX[par] = bld32(rrec, 2 * lim + rbase);
-            if (!kB16) NB[par] = bld32(rrec, 2 * lim + rbase + 128);
+            if (!kScalarStale) NB[par] = bld32(rrec, 2 * lim + rbase + 128);
             if (DT == 1) {
                 // sign (bit 7 of sm, copied to bit 15) and mantissa bits 0-6
                 // from sp, exponent (em bits 12-19) to bits 7-14; the store
@@ -1596,8 +1612,9 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
                 bst32(rout, out_lane + t * 32 * EB, (sx & 0x807FFFFFu) | (ex & ~0x807FFFFFu));
                 return 0u;
             } else {
-                bst_value<DT>(rout, out_lane + t * 32 * EB, em >> 12);  // the symbol is the value
-                return 0u;
+                const uint32_t v = (em >> 12) & 0xFFu;  // the symbol is the value
+                if (store) bst_value<DT>(rout, out_lane + t * 32 * EB, v);
+                return v;
             }
         };
         uint32_t t = 0;
@@ -1645,7 +1662,8 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
                 group8(t + 8, N0, N1);
             }
         } else if (DT == 4) {
-            // fp8: no raw bytes
+            // fp8: no raw bytes, one byte store per step (packing four steps
+            // into a dword through two bpermute rounds measured slower)
             for (; t < Tmain; t += 8) {
 #pragma unroll
                 for (int u = 0; u < 8; ++u) step(t + u, runm, false, 0u, u & 3, true);
