@@ -136,3 +136,15 @@ def test_prediction_other_dtypes(dtype):
     plan = orc.plan_call(dtype, bits, policy())
     actual = orc.compress(dtype, bits).size
     assert abs(plan["predicted_bytes"] / actual - 1) < 0.02
+
+
+@pytest.mark.parametrize("dtype", [orc.BF16, orc.FP32, orc.FP16, orc.FP8_E4M3])
+def test_oracle_reports_every_raw_record_corruption(dtype):
+    from uzip_testlib import raw_corruptions
+    eb = np.dtype(orc._ELEM[dtype]).itemsize
+    bits = np.random.default_rng(dtype).integers(0, 1 << (8 * eb), 100_000, dtype=np.uint64).astype(orc._ELEM[dtype])
+    buf, plan = orc.compress_arbitrated(dtype, bits, policy(link_bytes_per_us=10**9))
+    assert plan["decision"] == 1
+    assert orc.decompress(buf, dtype, bits.size)[0] == orc.OK
+    for name, bad in raw_corruptions(buf):
+        assert orc.decompress(bad, dtype, bits.size)[0] == orc.CORRUPT, name

@@ -113,29 +113,31 @@ def test_random_bits_are_never_coded():
     assert plan["decision"] == uz.UZIP_PLAN_RAW  # no predicted gain: not admitted
 
 
-@pytest.mark.parametrize("chunk_bytes", [0, 4096])
-def test_batched_mixed_decisions(chunk_bytes):
+@pytest.mark.parametrize("tdtype,chunk_bytes", [(torch.bfloat16, 0), (torch.bfloat16, 4096), (torch.float32, 0),
+                                                (torch.float16, 0), (torch.float8_e4m3fn, 0), (torch.float8_e5m2, 8192)])
+def test_batched_mixed_decisions(tdtype, chunk_bytes):
     """Small buffers take the fast path, random bits go RAW by the model, the
     rest is coded; every buffer equals its own oracle call."""
     rng = np.random.default_rng(7)
-    bits = [_workload(torch.bfloat16, 100_000, seed=1), np.zeros(0, np.uint16), _workload(torch.bfloat16, 300, seed=2),
-            rng.integers(0, 1 << 16, 80_000).astype(np.uint16), _workload(torch.bfloat16, 65_537, seed=3),
-            _workload(torch.bfloat16, 2_000, seed=4)]
+    elem = NP_ELEM[tdtype]
+    eb = np.dtype(elem).itemsize
+    rand = rng.integers(0, 1 << (8 * eb), 160_000 // eb, dtype=np.uint64).astype(elem)
+    bits = [_workload(tdtype, 200_000 // eb, seed=1), np.zeros(0, elem), _workload(tdtype, 600 // eb, seed=2),
+            rand, _workload(tdtype, 131_074 // eb, seed=3), _workload(tdtype, 4_000 // eb, seed=4)]
     kw = dict(link_bytes_per_us=5_000, small_bytes=4_096)
     gp, op = both_policies(**kw)
-    ts = [_bits_tensor(b, torch.bfloat16) if b.size else torch.empty(0, dtype=torch.bfloat16, device=DEV)
-          for b in bits]
+    ts = [_bits_tensor(b, tdtype) if b.size else torch.empty(0, dtype=tdtype, device=DEV) for b in bits]
     outs, sizes, plans = uz.compress_batched_arbitrated(ts, gp, chunk_bytes)
     torch.cuda.synchronize()
     got_plans = uz.plans_as_dicts(plans)
     decisions = []
     for b, o, s, p in zip(bits, outs, sizes.cpu().tolist(), got_plans):
-        want, want_plan = orc.compress_arbitrated(orc.BF16, b, op, chunk_bytes)
+        want, want_plan = orc.compress_arbitrated(ORC_CODE[tdtype], b, op, chunk_bytes)
         assert p == want_plan
         assert np.array_equal(o[:s].cpu().numpy(), want)
         decisions.append(p["decision"])
     assert decisions == [0, 2, 2, 1, 0, 2]
-    vals, status = uz.decompress_batched([o[:s] for o, s in zip(outs, sizes.cpu().tolist())], torch.bfloat16,
+    vals, status = uz.decompress_batched([o[:s] for o, s in zip(outs, sizes.cpu().tolist())], tdtype,
                                          [b.size for b in bits])
     torch.cuda.synchronize()
     assert status.cpu().tolist() == [0] * len(bits)
@@ -153,3 +155,23 @@ def test_plain_compress_is_unchanged_by_a_previous_raw_plan():
     buf, size = uz.compress(t, ws=ws)
     torch.cuda.synchronize()
     assert np.array_equal(buf[:int(size.item())].cpu().numpy(), orc.compress(orc.BF16, bits))
+
+
+@pytest.mark.parametrize("tdtype", [torch.bfloat16, torch.float32, torch.float8_e5m2])
+def test_corrupt_raw_frames_are_reported(tdtype):
+    """The decoder's RAW-record path validates as the coded one does: every
+    corruption of an all-RAW frame is reported, and the clean frame decodes."""
+    from uzip_testlib import raw_corruptions
+    bits = _workload(tdtype, 150_000, seed=9)
+    _, op = both_policies(link_bytes_per_us=10**9)
+    buf, plan = orc.compress_arbitrated(ORC_CODE[tdtype], bits, op)
+    assert plan["decision"] == uz.UZIP_PLAN_RAW
+    out, st = gpu_decompress(buf, tdtype, bits.size)
+    assert st == 0 and np.array_equal(_int_view(out).cpu().numpy().view(bits.dtype), bits)
+    n_bad = 0
+    for name, bad in raw_corruptions(buf):
+        want = orc.decompress(bad, ORC_CODE[tdtype], bits.size)[0]
+        _, st = gpu_decompress(bad, tdtype, bits.size)
+        assert st == (uz.UZIP_ERR_CORRUPT_INPUT if want == orc.CORRUPT else 0), name
+        n_bad += want == orc.CORRUPT
+    assert n_bad == 12  # every one of them is a corruption the oracle reports

@@ -70,3 +70,31 @@ def corruptions(buf):
     yield "word", patch(base + tab_end + 128 + 2 * (rec["n_words"] // 2), 0x1234, 2)
 
 
+
+
+def raw_corruptions(buf):
+    """Corruptions of a buffer whose records are RAW: the header ones, and the
+    record fields a RAW record must hold exactly (mode, nsym 0, n_words 0,
+    n_values, rec_bytes = align16(16 + n_values))."""
+    hdr, idx, recs = parse_buffer(buf)
+    ri = next(i for i, r in enumerate(recs) if r["mode"] == 1)
+    base = hdr["exp_off"] + idx[ri]
+    rec = recs[ri]
+
+    def patch(off, val, width):
+        b = buf.copy()
+        b[off:off + width] = np.frombuffer(int(val).to_bytes(width, "little"), np.uint8)
+        return b
+
+    yield "truncated", buf[:-16]
+    yield "magic", patch(0, 0x31505A56, 4)
+    yield "dtype", patch(6, 6, 1)
+    yield "count", patch(16, hdr["n"] + 1, 8)
+    yield "total", patch(48, buf.size + 16, 8)
+    yield "index_unaligned", patch(64 + 8 * (ri + 1), idx[ri + 1] + 2, 8)
+    yield "raw_mode", patch(base, 2, 1)
+    yield "raw_nsym", patch(base + 2, 1, 2)
+    yield "raw_n_words", patch(base + 4, 1, 4)
+    yield "raw_n_values", patch(base + 8, rec["n_values"] - 1, 4)
+    yield "raw_bytes", patch(base + 12, rec["bytes"] - 16, 4)
+    yield "raw_as_rans", patch(base, 0, 1)
