@@ -1,7 +1,8 @@
 /*
  * uzip_oracle.c -- plain, slow, single-threaded CPU oracle of the uzip v1
- * bitstream (lossless bf16/fp32 compression by exponent/sign+mantissa split
- * and 32-lane interleaved rANS of the exponent stream).
+ * bitstream (lossless bf16/fp32, and fp16/fp8, compression by exponent /
+ * sign+mantissa split and 32-lane interleaved rANS of the exponent stream),
+ * and of the per-call RAW arbitration.
  *
  * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may link, load or
  * call this file.  Only the test-suite, the smoke check and the CPU-baseline
@@ -24,6 +25,12 @@
  *    size, payload size, codec parameters); Sec. IV-C / Algorithm 1: a RAW
  *    frame is committed when coding does not pay; Algorithm 2: the receiver
  *    validates the header before decoding.
+ *  - UCCL-Zip review page, Figure 13: the payload types bfloat16, float16,
+ *    float32, float8_e4m3fn and float8_e5m2.  For fp16 and fp8 the coded
+ *    symbol is the byte that holds the exponent (orc_split).
+ *  - NCCLZ Sec. IV-C, Eq. (1) and (2), Algorithm 1: the runtime arbitration
+ *    between coding and RAW from a bounded sample and a link/codec time
+ *    model (orc_plan_call, orc_compress_arbitrated).
  *  - The pages give no formulas for the coder.  The textbook methods used
  *    where they are silent: J. Duda, "Asymmetric numeral systems" (arXiv
  *    1311.2540) for rANS with a 2^12 table, 32-bit state and 16-bit
