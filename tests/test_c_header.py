@@ -1,0 +1,62 @@
+"""include/uzip.h as a C11 header: a C translation unit that calls every
+declared entry point with typed arguments compiles warning-free under
+-pedantic and links against libuzip.so; the host-only size functions then
+run from C and agree with the Python binding (no call reaches a device)."""
+import os
+import subprocess
+import tempfile
+
+import lossless_compression_float_amd as uz
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+C_SRC = r"""
+#include <stdio.h>
+#include "uzip.h"
+
+int main(int argc, char **argv) {
+    (void)argv;
+    if (argc > 100) {  /* never taken: type-checks every call without running a device call */
+        const void *in[1] = {0};
+        void *out[1] = {0};
+        size_t n[1] = {0}, cap[1] = {0}, inb[1] = {0};
+        uzip_policy pol = {0};
+        uzip_plan *plan = 0;
+        uint64_t *sz = 0;
+        uint32_t *st = 0;
+        hipStream_t s = 0;
+        int r = 0;
+        r |= uzip_compress(UZIP_BF16, in[0], 0, 0, out[0], 0, sz, out[0], 0, s);
+        r |= uzip_decompress(in[0], 0, UZIP_FP32, 0, out[0], st, out[0], 0, s);
+        r |= uzip_compress_batched(UZIP_FP16, 1, in, n, 0, out, cap, sz, out[0], 0, s);
+        r |= uzip_decompress_batched(UZIP_FP8_E4M3, 1, in, inb, n, out, st, out[0], 0, s);
+        r |= uzip_compress_arbitrated(UZIP_FP8_E5M2, in[0], 0, 0, &pol, out[0], 0, sz, plan, out[0], 0, s);
+        r |= uzip_compress_batched_arbitrated(UZIP_BF16, 1, in, n, 0, &pol, out, cap, sz, plan, out[0], 0, s);
+        r |= uzip_profile_set_events(0, 0);
+        return r;
+    }
+    size_t nb[2] = {1000, 70000};
+    printf("%zu %zu %zu %zu %d %d %s\n", uzip_max_compressed_size(UZIP_BF16, 1000, 0),
+           uzip_max_compressed_size(UZIP_FP8_E4M3, 70000, 4096), uzip_workspace_size(UZIP_FP32, 100000, 0),
+           uzip_workspace_size_batched(UZIP_FP16, 2, nb, 0), (int)sizeof(uzip_policy), (int)sizeof(uzip_plan),
+           uzip_status_string(UZIP_ERR_CORRUPT_INPUT));
+    return 0;
+}
+"""
+
+
+def test_header_is_c11_and_links():
+    with tempfile.TemporaryDirectory() as d:
+        src, exe = os.path.join(d, "t.c"), os.path.join(d, "t")
+        open(src, "w").write(C_SRC)
+        libdir = os.path.dirname(uz.LIB_PATH)
+        subprocess.check_call(["gcc", "-std=c11", "-Wall", "-Wextra", "-pedantic", "-Werror", "-D__HIP_PLATFORM_AMD__",
+                               "-I" + os.path.join(ROOT, "include"), "-isystem", "/opt/rocm/include", "-o", exe, src,
+                               "-L" + libdir, "-luzip", "-Wl,-rpath," + libdir])
+        out = subprocess.check_output([exe], text=True).split()
+    assert int(out[0]) == uz.uzip_max_compressed_size(uz.UZIP_BF16, 1000)
+    assert int(out[1]) == uz.uzip_max_compressed_size(uz.UZIP_FP8_E4M3, 70000, 4096)
+    assert int(out[2]) == uz.uzip_workspace_size(uz.UZIP_FP32, 100000)
+    assert int(out[3]) == uz.uzip_workspace_size_batched(uz.UZIP_FP16, [1000, 70000])
+    assert out[4:6] == ["56", "32"]
+    assert " ".join(out[6:]) == uz.uzip_status_string(uz.UZIP_ERR_CORRUPT_INPUT)
