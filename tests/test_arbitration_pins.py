@@ -47,6 +47,8 @@ def test_worked_example_w3():
     g = json.load(open(os.path.join(GOLDEN, "arbitration_w3.json")))
     for i, case in enumerate(g["cases"]):
         bits = bf16_with_exponents(case["exponents"], seed=i)
+        if "fill" in case:  # values past the sample, which the plan sees only through N
+            bits = np.concatenate([bits, np.full(case["n"] - bits.size, case["fill"], np.uint16)])
         assert bits.size == case["n"]
         plan = orc.plan_call(orc.BF16, bits, orc.Policy(**case["policy"]))
         assert plan == case["plan"], case["what"]

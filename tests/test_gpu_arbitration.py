@@ -63,6 +63,8 @@ def test_worked_example_w3_on_the_gpu():
         e = np.concatenate([np.full(c, int(s), np.uint16) for s, c in case["exponents"].items()])
         e = rng.permutation(e)
         bits = ((e << 7) | rng.integers(0, 256, e.size).astype(np.uint16) & 0x807F).astype(np.uint16)
+        if "fill" in case:  # values past the sample, which the plan sees only through N
+            bits = np.concatenate([bits, np.full(case["n"] - bits.size, case["fill"], np.uint16)])
         pol = uz.policy(**case["policy"])
         _, _, plan = uz.compress_arbitrated(_bits_tensor(bits, torch.bfloat16), pol)
         torch.cuda.synchronize()
