@@ -1,5 +1,6 @@
 /*
- * uzip.h -- C ABI of the MI355X (gfx950) lossless bf16/fp32 tensor codec.
+ * uzip.h -- C ABI of the MI355X (gfx950) lossless bf16/fp32 (and fp16/fp8)
+ * tensor codec.
  *
  * What it computes.  A tensor is shrunk losslessly before a send and restored
  * bit for bit after the receive, with the communication API left unchanged
@@ -21,7 +22,8 @@
  *                      sm_off, exp_off, total_bytes
  *   [64, 64+8(C+1))    u64 record offsets (exclusive prefix sum of sizes)
  *   [sm_off, +r*N)     sign+mantissa bytes of every value, in value order
- *                      (bf16: 1 byte; fp32: 3 bytes little-endian)
+ *                      (bf16: 1 byte; fp32: 3 bytes little-endian; fp16: the
+ *                      low byte; fp8: none)
  *   [exp_off, total)   one record per chunk: a 16-byte record header, then
  *                      either the rANS table, 32 final states and 16-bit words
  *                      (mode RANS) or the chunk's raw exponent bytes (RAW).
@@ -88,7 +90,7 @@ size_t uzip_max_compressed_size(uzip_dtype dtype, size_t num_elements, size_t ch
  * of num_elements values (the larger of the two).  0 for invalid arguments. */
 size_t uzip_workspace_size(uzip_dtype dtype, size_t num_elements, size_t chunk_bytes);
 
-/* Compress num_elements bf16/fp32 values at d_in (bit patterns, any values
+/* Compress num_elements values of `dtype` at d_in (bit patterns, any values
  * including NaN/Inf/denormals) into d_out (out_capacity bytes, at least
  * uzip_max_compressed_size).  The exact compressed size is written to the
  * device word *d_out_size.  Passages: UCCL-Zip Fig. 2 (exponent split),

@@ -1,5 +1,5 @@
-"""Python binding of the uzip C ABI (include/uzip.h): lossless bf16/fp32
-tensor compression on MI355X (gfx950).
+"""Python binding of the uzip C ABI (include/uzip.h): lossless bf16/fp32 (and
+fp16/fp8) tensor compression on MI355X (gfx950).
 
 The functions named ``uzip_*`` are the C entry points with the same names and
 arguments (plain integers and device pointers), marshalled through ctypes.
@@ -222,7 +222,7 @@ def workspace(nbytes: int, device) -> torch.Tensor:
 
 def compress(t: torch.Tensor, chunk_bytes: int = 0, out: torch.Tensor | None = None,
              ws: torch.Tensor | None = None, out_size: torch.Tensor | None = None, stream=None):
-    """Compress a contiguous bf16/fp32 CUDA tensor.  Returns (buffer, size)
+    """Compress a contiguous bf16/fp32/fp16/fp8 device tensor.  Returns (buffer, size)
     where `buffer` has capacity uzip_max_compressed_size and `size` is a
     one-element int64 device tensor holding the exact compressed size."""
     if not t.is_cuda or not t.is_contiguous():
