@@ -434,9 +434,15 @@ __device__ inline void raw_exponents(rsrc_t rin, uint8_t *rec, uint32_t size, ui
 //                four different banks: hot bins no longer serialise a wave
 //   normalise    keys of the present symbols          words [0, 512)
 //   pass 2       per-symbol coder table, 16 B/entry   words [512, 2560)
-constexpr uint32_t kSubHist = 4;
-constexpr uint32_t kSubRow = 264;
-constexpr uint32_t kEncLdsWords = 2560;
+// fp8 counts a whole byte per value, 16 per 128-bit load, with eight waves per
+// CU (a chunk holds 64 Ki values): it takes 8 sub-histograms in rows of 260
+// words (eight copies of a bin in eight banks, 16.25 KiB in all), which its
+// occupancy affords; the 2-byte types keep 10 KiB for 16 waves per CU.
+template <int DT> struct EncLds {
+    static constexpr uint32_t kSubHist = DT == 4 ? 8 : 4;
+    static constexpr uint32_t kSubRow = DT == 4 ? 260 : 264;
+    static constexpr uint32_t kWords = 2 * kSubHist * kSubRow > 2560 ? 2 * kSubHist * kSubRow : 2560;
+};
 
 // Exact floor(x / f) for the encoder, where x < f * 2^20 (so the quotient is
 // below 2^20) and 1 <= f <= 4096: one binary64 multiply by
@@ -454,7 +460,8 @@ __global__ __launch_bounds__(64) void k_encode(EncParams p) {
     constexpr uint32_t VPL = 16 / EB;         // values per lane per 128-bit load
     constexpr uint32_t VPI = 32 * VPL;        // values per half-wave per pass-1 step
 
-    __shared__ __align__(16) uint32_t lds[kEncLdsWords];
+    constexpr uint32_t kSubHist = EncLds<DT>::kSubHist, kSubRow = EncLds<DT>::kSubRow;
+    __shared__ __align__(16) uint32_t lds[EncLds<DT>::kWords];
 
     const uint32_t lane = threadIdx.x;
     const uint32_t h = lane >> 5, lj = lane & 31;
@@ -498,7 +505,7 @@ __global__ __launch_bounds__(64) void k_encode(EncParams p) {
     {
         // (a multiple of 4 iterations, so that no step of the loop is conditional)
         const uint32_t fullmin = min(vals0 / VPI, nch == 2 ? vals1 / VPI : 0xFFFFFFFFu) & ~3u;
-        uint32_t *hm = valid ? hist : hist + 256 + (lj >> 2);
+        uint32_t *hm = valid ? hist : hist + 256 + lj / kSubHist;
         const rsrc_t rsmo = make_rsrc(d.out + d.sm_off + c0 * ce * R, pair_vals * R);
         const uint32_t smo = (h ? vals0 : 0u) * R + lj * VPL * R;  // this lane's first sign+mantissa byte
         auto split = [&](const uint4 &qv, uint32_t it) __attribute__((always_inline)) {
@@ -642,7 +649,9 @@ __global__ __launch_bounds__(64) void k_encode(EncParams p) {
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
             const uint32_t s = lj * 8 + k;
-            c[k] = hh[s] + hh[kSubRow + s] + hh[2 * kSubRow + s] + hh[3 * kSubRow + s];
+            c[k] = 0;
+#pragma unroll
+            for (uint32_t r = 0; r < kSubHist; ++r) c[k] += hh[r * kSubRow + s];
             if (c[k]) pm |= 1u << k;
         }
     }
