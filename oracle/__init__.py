@@ -81,6 +81,10 @@ def lib():
         _lib.orc_compress.argtypes = [i32, vp, u64, u64, vp, u64, vp]
         _lib.orc_decompress.restype = i32
         _lib.orc_decompress.argtypes = [vp, u64, i32, u64, vp]
+        _lib.orc_compress_sampled.restype = i32
+        _lib.orc_compress_sampled.argtypes = [i32, vp, u64, u64, vp, u64, vp]
+        _lib.orc_normalize_sampled.restype = i32
+        _lib.orc_normalize_sampled.argtypes = [vp, ctypes.c_uint32, vp]
         _lib.orc_log2_q16.restype = ctypes.c_uint32
         _lib.orc_log2_q16.argtypes = [ctypes.c_uint32]
         _lib.orc_plan_call.restype = i32
@@ -267,3 +271,27 @@ def compress_arbitrated(dtype: int, values, policy: Policy, chunk_bytes: int = 0
     if st != OK:
         raise ValueError("oracle arbitrated compress failed with status %d" % st)
     return out[: size.value].copy(), plan.as_dict()
+
+
+# ---- sampled tables (UCCL-Zip: each block's table from a sample) ------------
+def normalize_sampled(counts, S: int):
+    """(nsym, f[256]): the sampled symbols' frequencies summing to 4095 (ESC holds slot 4095)."""
+    c = np.ascontiguousarray(counts, np.uint32)
+    f = np.zeros(256, np.uint32)
+    nsym = lib().orc_normalize_sampled(_p(c), S, _p(f))
+    return int(nsym), f
+
+
+def compress_sampled(dtype: int, values, chunk_bytes: int = 0) -> np.ndarray:
+    """A frame with sampled tables (header flag bit 0), exact size."""
+    v = _bits(dtype, values)
+    cap = max_compressed_size(dtype, v.size, chunk_bytes)
+    if cap == 0:
+        raise ValueError("invalid chunk_bytes")
+    out = np.empty(cap, np.uint8)
+    size = ctypes.c_uint64(0)
+    st = lib().orc_compress_sampled(dtype, _p(v) if v.size else None, v.size, chunk_bytes, _p(out), cap,
+                                    ctypes.byref(size))
+    if st != OK:
+        raise ValueError("oracle sampled compress failed with status %d" % st)
+    return out[: size.value].copy()

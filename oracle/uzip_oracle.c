@@ -244,6 +244,54 @@ void orc_cumulative(const uint32_t f[256], uint32_t c0[256]) {
     }
 }
 
+/* ---- sampled tables (UCCL-Zip Sec. 3, Figure 5 text: each block builds its
+ * table from a sample of its data) ------------------------------------------
+ * The table of a chunk is normalised from the counts of a sample spread over
+ * the chunk: value i belongs to it when i mod (chunk_elems / 8) is below
+ * max(1, chunk_elems / 64), i.e. eight evenly spaced runs of contiguous values,
+ * an eighth of a full chunk (so a chunk whose scale drifts, row by row, is
+ * sampled throughout).  A symbol the sample did not see has
+ * no slot of its own; it is coded as the escape symbol ESC, which always holds
+ * exactly one slot, the last one (c0 = 4095), and its byte goes to the
+ * record's escape list in value order.  The sampled symbols share the other
+ * 4095 slots by the rule of orc_normalize: one reserved slot each, the rest
+ * by the floor of each quota of R = 4096 - nsym - 1, and the leftover slots to
+ * the largest remainders, lower symbol first.  (The same rule over nsym + 1
+ * symbols with ESC last and counted 0 gives ESC exactly its reserved slot: the
+ * leftover count is the sum of the fractional quotas, below the number of
+ * symbols whose quota has one.)  Returns nsym, the sampled symbols. */
+int orc_normalize_sampled(const uint32_t counts[256], uint32_t S, uint32_t f[256]) {
+    int nsym = 0;
+    for (int s = 0; s < 256; ++s) {
+        f[s] = 0;
+        if (counts[s] > 0) nsym += 1;
+    }
+    if (nsym == 0) return 0;
+    uint64_t R = ORC_M - (uint64_t)nsym - 1;
+    uint64_t rem[256];
+    uint64_t given = 0;
+    for (int s = 0; s < 256; ++s) {
+        if (counts[s] == 0) continue;
+        uint64_t q = (uint64_t)counts[s] * R;
+        f[s] = 1u + (uint32_t)(q / S);
+        rem[s] = q % S;
+        given += q / S;
+    }
+    uint64_t d = R - given;
+    int served[256];
+    for (int s = 0; s < 256; ++s) served[s] = 0;
+    for (uint64_t k = 0; k < d; ++k) {
+        int best = -1;
+        for (int s = 0; s < 256; ++s) {
+            if (counts[s] == 0 || served[s]) continue;
+            if (best < 0 || rem[s] > rem[best]) best = s;
+        }
+        served[best] = 1;
+        f[best] += 1;
+    }
+    return nsym;
+}
+
 /* ---- step 4: interleaved rANS encode (Duda; Giesen) ----------------------
  * Value i belongs to lane i mod K and step i / K.  Every lane starts at
  * x = L.  Steps run from the last one down to 0.  For each lane with a value
@@ -395,11 +443,106 @@ static uint64_t orc_encode_record(const uint8_t *e, uint64_t ni, uint8_t *rec, i
     return rec_bytes;
 }
 
+/* One chunk's record in a sampled-table frame: mode 2 (coded with a table
+ * from the chunk's sample and an escape list) when strictly smaller than the
+ * RAW record, else RAW.  Layout of mode 2: the 16-byte header (mode 2, nsym,
+ * n_words, n_values, rec_bytes), the bitmap of the sampled symbols, their
+ * frequencies (ascending symbol), zero padding to 4 bytes, u32 n_esc, the 32
+ * final states, the words, the n_esc escaped bytes in value order, zero
+ * padding to 16 bytes.  The coder works on ranks: rank r < nsym is the r-th
+ * sampled symbol, rank nsym is ESC (f = 1, c0 = 4095). */
+/* counts of the chunk's sample (see above); returns its size S >= 1 for ni >= 1 */
+uint64_t orc_sample_counts(const uint8_t *e, uint64_t ni, uint64_t ce, uint32_t counts[256]) {
+    uint64_t period = ce / 8, run = ce / 64 > 0 ? ce / 64 : 1, S = 0;
+    for (int s = 0; s < 256; ++s) counts[s] = 0;
+    for (uint64_t i = 0; i < ni; ++i) {
+        if (i % period < run) {
+            counts[e[i]] += 1;
+            S += 1;
+        }
+    }
+    return S;
+}
+
+static uint64_t orc_encode_record_sampled(const uint8_t *e, uint64_t ni, uint64_t ce, uint8_t *rec) {
+    uint32_t counts[256], f[256], c0[256], states[ORC_LANES];
+    uint64_t S = orc_sample_counts(e, ni, ce, counts);
+    int nsym = orc_normalize_sampled(counts, (uint32_t)S, f);
+    orc_cumulative(f, c0);
+    /* rank tables: the sampled symbols in ascending order, then ESC */
+    uint32_t fr[256], cr[256];
+    int rank[256];
+    int r = 0;
+    for (int s = 0; s < 256; ++s) {
+        rank[s] = -1;
+        if (f[s] == 0) continue;
+        rank[s] = r;
+        fr[r] = f[s];
+        cr[r] = c0[s];
+        r += 1;
+    }
+    for (int k = r; k < 256; ++k) fr[k] = cr[k] = 0;
+    if (nsym < 256) {
+        fr[nsym] = 1;
+        cr[nsym] = ORC_M - 1;
+    }
+    uint8_t *m = (uint8_t *)malloc((size_t)(ni ? ni : 1));
+    uint8_t *esc = (uint8_t *)malloc((size_t)(ni ? ni : 1));
+    uint64_t n_esc = 0;
+    for (uint64_t i = 0; i < ni; ++i) {
+        if (rank[e[i]] >= 0) {
+            m[i] = (uint8_t)rank[e[i]];
+        } else {  /* unseen by the sample (so nsym < 256) */
+            m[i] = (uint8_t)nsym;
+            esc[n_esc++] = e[i];
+        }
+    }
+    uint16_t *words = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)(ni ? ni : 1));
+    uint64_t n_words = orc_rans_encode(m, ni, ORC_LANES, fr, cr, states, words);
+    uint64_t tab_end = orc_align4(ORC_REC_HDR + 32 + 2 * (uint64_t)nsym);
+    uint64_t states_at = tab_end + 4, words_at = states_at + 4 * ORC_LANES;
+    uint64_t esc_at = words_at + 2 * n_words;
+    uint64_t coded_bytes = orc_align16(esc_at + n_esc);
+    uint64_t raw_bytes = orc_align16(ORC_REC_HDR + ni);
+    uint64_t rec_bytes;
+    if (coded_bytes < raw_bytes) {
+        rec_bytes = coded_bytes;
+        memset(rec, 0, (size_t)rec_bytes);
+        rec[0] = 2; /* mode: coded with a sampled table */
+        put16(rec + 2, (uint32_t)nsym);
+        put32(rec + 4, (uint32_t)n_words);
+        put32(rec + 8, (uint32_t)ni);
+        put32(rec + 12, (uint32_t)rec_bytes);
+        int k = 0;
+        for (int s = 0; s < 256; ++s) {
+            if (f[s] == 0) continue;
+            rec[16 + (s >> 3)] |= (uint8_t)(1u << (s & 7));
+            put16(rec + 48 + 2 * k, f[s]);
+            k += 1;
+        }
+        put32(rec + tab_end, (uint32_t)n_esc);
+        for (int j = 0; j < ORC_LANES; ++j) put32(rec + states_at + 4 * (uint64_t)j, states[j]);
+        for (uint64_t w = 0; w < n_words; ++w) put16(rec + words_at + 2 * w, words[w]);
+        memcpy(rec + esc_at, esc, (size_t)n_esc);
+    } else {
+        rec_bytes = raw_bytes;
+        memset(rec, 0, (size_t)rec_bytes);
+        rec[0] = 1;
+        put32(rec + 8, (uint32_t)ni);
+        put32(rec + 12, (uint32_t)rec_bytes);
+        memcpy(rec + ORC_REC_HDR, e, (size_t)ni);
+    }
+    free(m);
+    free(esc);
+    free(words);
+    return rec_bytes;
+}
+
 /* Whole-buffer compression.  out must hold cap >= orc_max_compressed_size
  * bytes.  *out_size receives the exact compressed size.  force_raw stores
  * every record RAW (the frame a RAW plan commits). */
 static int orc_compress_frame(int dtype, const void *in, uint64_t n, uint64_t chunk_bytes, uint8_t *out, uint64_t cap,
-                              uint64_t *out_size, int force_raw) {
+                              uint64_t *out_size, int force_raw, int sampled) {
     uint64_t ce = orc_chunk_elems(dtype, chunk_bytes);
     if (ce == 0) return ORC_INVALID;
     if (cap < orc_max_compressed_size(dtype, n, chunk_bytes)) return ORC_CAPACITY;
@@ -416,7 +559,8 @@ static int orc_compress_frame(int dtype, const void *in, uint64_t n, uint64_t ch
     put64(out + ORC_HDR_BYTES, 0);
     for (uint64_t i = 0; i < C; ++i) {
         uint64_t ni = (i + 1 < C) ? ce : n - i * ce;
-        off += orc_encode_record(e + i * ce, ni, out + exp_off + off, force_raw);
+        off += sampled && !force_raw ? orc_encode_record_sampled(e + i * ce, ni, ce, out + exp_off + off)
+                                     : orc_encode_record(e + i * ce, ni, out + exp_off + off, force_raw);
         put64(out + ORC_HDR_BYTES + 8 * (i + 1), off);
     }
     uint64_t total = exp_off + off;
@@ -426,7 +570,7 @@ static int orc_compress_frame(int dtype, const void *in, uint64_t n, uint64_t ch
     out[7] = ORC_PROB_BITS;
     out[8] = ORC_LANES;
     out[9] = (uint8_t)r;
-    put16(out + 10, 0);
+    put16(out + 10, sampled ? 1u : 0u); /* flags: bit 0 = sampled tables */
     put32(out + 12, (uint32_t)ce);
     put64(out + 16, n);
     put64(out + 24, C);
@@ -442,7 +586,13 @@ static int orc_compress_frame(int dtype, const void *in, uint64_t n, uint64_t ch
 
 int orc_compress(int dtype, const void *in, uint64_t n, uint64_t chunk_bytes, uint8_t *out, uint64_t cap,
                  uint64_t *out_size) {
-    return orc_compress_frame(dtype, in, n, chunk_bytes, out, cap, out_size, 0);
+    return orc_compress_frame(dtype, in, n, chunk_bytes, out, cap, out_size, 0, 0);
+}
+
+/* Whole-buffer compression with sampled tables (header flag bit 0). */
+int orc_compress_sampled(int dtype, const void *in, uint64_t n, uint64_t chunk_bytes, uint8_t *out, uint64_t cap,
+                         uint64_t *out_size) {
+    return orc_compress_frame(dtype, in, n, chunk_bytes, out, cap, out_size, 0, 1);
 }
 
 /* ---- per-call arbitration: code the call, or send it RAW ------------------
@@ -567,24 +717,30 @@ int orc_compress_arbitrated(int dtype, const void *in, uint64_t n, uint64_t chun
                             orc_plan *plan, uint8_t *out, uint64_t cap, uint64_t *out_size) {
     int st = orc_plan_call(dtype, in, n, chunk_bytes, pol, plan);
     if (st != ORC_OK) return st;
-    return orc_compress_frame(dtype, in, n, chunk_bytes, out, cap, out_size, plan->decision != 0);
+    return orc_compress_frame(dtype, in, n, chunk_bytes, out, cap, out_size, plan->decision != 0, 0);
 }
 
 /* Decode one record into the chunk's exponents.  rec holds rec_len bytes
  * (already known to lie inside the buffer).  Checks V6-V9. */
-static int orc_decode_record(const uint8_t *rec, uint64_t rec_len, uint64_t ni, uint8_t *e) {
+static int orc_decode_record_sampled(const uint8_t *rec, uint64_t rec_len, uint64_t ni, uint32_t nsym,
+                                     uint64_t n_words, uint8_t *e);
+
+static int orc_decode_record(const uint8_t *rec, uint64_t rec_len, uint64_t ni, uint8_t *e, int sampled) {
     if (rec_len < ORC_REC_HDR) return ORC_CORRUPT;
     uint32_t mode = rec[0];
     uint32_t nsym = get16(rec + 2);
     uint64_t n_words = get32(rec + 4);
     uint64_t n_values = get32(rec + 8);
     uint64_t rec_bytes = get32(rec + 12);
-    if (mode > 1 || n_values != ni || rec_bytes != rec_len) return ORC_CORRUPT;
+    if (mode > 2 || n_values != ni || rec_bytes != rec_len) return ORC_CORRUPT;
     if (mode == 1) {
         if (nsym != 0 || n_words != 0 || rec_len != orc_align16(ORC_REC_HDR + ni)) return ORC_CORRUPT;
         memcpy(e, rec + ORC_REC_HDR, (size_t)ni);
         return ORC_OK;
     }
+    /* a frame uses one kind of coded record: mode 0 (full histograms) or mode 2 (sampled) */
+    if ((mode == 2) != (sampled != 0)) return ORC_CORRUPT;
+    if (mode == 2) return orc_decode_record_sampled(rec, rec_len, ni, nsym, n_words, e);
     /* RANS: bitmap, frequencies, states, words */
     if (rec_len < ORC_REC_HDR + 32) return ORC_CORRUPT;
     uint32_t pop = 0;
@@ -621,6 +777,69 @@ static int orc_decode_record(const uint8_t *rec, uint64_t rec_len, uint64_t ni, 
 /* Whole-buffer decompression with validation V1-V9.  The caller states the
  * dtype and element count, as a receiver does.  Returns ORC_OK, or
  * ORC_CORRUPT for any inconsistency; never reads outside in[0, in_bytes). */
+/* Mode 2: the sampled table, ESC in the last slot, the escape list in value
+ * order.  Checks: bitmap and nsym agree (1..256), every frequency >= 1 and
+ * they sum to 4095, n_esc and the words fit the record exactly, the rANS
+ * stream ends as in orc_rans_decode, every escape of the list is used, and
+ * no escaped byte is a sampled symbol (such a value would have been coded
+ * directly). */
+static int orc_decode_record_sampled(const uint8_t *rec, uint64_t rec_len, uint64_t ni, uint32_t nsym,
+                                     uint64_t n_words, uint8_t *e) {
+    if (rec_len < ORC_REC_HDR + 32) return ORC_CORRUPT;
+    uint32_t pop = 0;
+    for (int s = 0; s < 256; ++s) pop += (rec[16 + (s >> 3)] >> (s & 7)) & 1u;
+    if (pop != nsym || nsym < 1 || nsym > 256) return ORC_CORRUPT;
+    uint64_t tab_end = orc_align4(ORC_REC_HDR + 32 + 2 * (uint64_t)nsym);
+    uint64_t states_at = tab_end + 4, words_at = states_at + 4 * ORC_LANES;
+    if (rec_len < words_at) return ORC_CORRUPT;
+    uint64_t n_esc = get32(rec + tab_end);
+    if (n_esc > ni || rec_len != orc_align16(words_at + 2 * n_words + n_esc)) return ORC_CORRUPT;
+    uint32_t fr[256], cr[256], states[ORC_LANES];
+    uint8_t sym_of_rank[256];
+    int present[256];
+    uint32_t acc = 0;
+    int k = 0;
+    for (int s = 0; s < 256; ++s) {
+        present[s] = (rec[16 + (s >> 3)] >> (s & 7)) & 1u;
+        if (!present[s]) continue;
+        uint32_t fs = get16(rec + 48 + 2 * k);
+        if (fs == 0) return ORC_CORRUPT;
+        fr[k] = fs;
+        cr[k] = acc;
+        sym_of_rank[k] = (uint8_t)s;
+        acc += fs;
+        k += 1;
+    }
+    if (acc != ORC_M - 1) return ORC_CORRUPT;
+    for (int j = k; j < 256; ++j) fr[j] = cr[j] = 0;
+    if (nsym < 256) {
+        fr[nsym] = 1;
+        cr[nsym] = ORC_M - 1;
+    }
+    for (int j = 0; j < ORC_LANES; ++j) {
+        states[j] = get32(rec + states_at + 4 * (uint64_t)j);
+        if (states[j] < ORC_L) return ORC_CORRUPT;
+    }
+    uint16_t *words = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)(n_words ? n_words : 1));
+    for (uint64_t w = 0; w < n_words; ++w) words[w] = (uint16_t)get16(rec + words_at + 2 * w);
+    uint8_t *ranks = (uint8_t *)malloc((size_t)(ni ? ni : 1));
+    int st = orc_rans_decode(states, words, n_words, ni, ORC_LANES, fr, cr, ranks);
+    free(words);
+    const uint8_t *esc = rec + words_at + 2 * n_words;
+    uint64_t used = 0;
+    for (uint64_t i = 0; i < ni && st == ORC_OK; ++i) {
+        if (ranks[i] < nsym) {
+            e[i] = sym_of_rank[ranks[i]];
+        } else {  /* ESC (only reachable when nsym < 256) */
+            if (used >= n_esc || present[esc[used]]) st = ORC_CORRUPT;
+            else e[i] = esc[used++];
+        }
+    }
+    if (st == ORC_OK && used != n_esc) st = ORC_CORRUPT;
+    free(ranks);
+    return st;
+}
+
 int orc_decompress(const uint8_t *in, uint64_t in_bytes, int dtype, uint64_t n, void *out) {
     int r = orc_raw_bytes(dtype);
     if (orc_elem_bytes(dtype) == 0) return ORC_INVALID;
@@ -628,6 +847,9 @@ int orc_decompress(const uint8_t *in, uint64_t in_bytes, int dtype, uint64_t n, 
     /* V1: magic, version and the fixed coder parameters */
     if (get32(in) != ORC_MAGIC || get16(in + 4) != ORC_VERSION) return ORC_CORRUPT;
     if (in[7] != ORC_PROB_BITS || in[8] != ORC_LANES || in[9] != (uint8_t)r) return ORC_CORRUPT;
+    /* flags: bit 0 = sampled tables; no other bit is defined */
+    uint32_t flags = get16(in + 10);
+    if (flags > 1) return ORC_CORRUPT;
     /* V2: dtype and element count as the caller states them */
     if (in[6] != (uint8_t)dtype || get64(in + 16) != n) return ORC_CORRUPT;
     /* V3: chunk size and chunk count */
@@ -652,7 +874,7 @@ int orc_decompress(const uint8_t *in, uint64_t in_bytes, int dtype, uint64_t n, 
     for (uint64_t i = 0; i < C && st == ORC_OK; ++i) {
         uint64_t ni = (i + 1 < C) ? ce : n - i * ce;
         uint64_t a = get64(in + ORC_HDR_BYTES + 8 * i), b = get64(in + ORC_HDR_BYTES + 8 * (i + 1));
-        st = orc_decode_record(in + exp_off + a, b - a, ni, e + i * ce);
+        st = orc_decode_record(in + exp_off + a, b - a, ni, e + i * ce, (int)(flags & 1u));
     }
     if (st == ORC_OK) orc_merge(dtype, e, in + sm_off, n, out);
     free(e);
