@@ -18,8 +18,11 @@
  *
  * Buffer layout (bitstream v1, little-endian, 16-byte aligned sections):
  *   [0, 64)            header: magic "UZP1", version 1, dtype, prob_bits 12,
- *                      lanes 32, raw bytes per value r, chunk_elems, N, C,
- *                      sm_off, exp_off, total_bytes
+ *                      lanes 32, raw bytes per value r, u16 flags,
+ *                      chunk_elems, N, C, sm_off, exp_off, total_bytes
+ *                      (flags: 0, or bit 0 = chunk tables taken from samples
+ *                      with an escape list, record mode 2; this library
+ *                      writes flags 0 and reports bit 0 as unsupported)
  *   [64, 64+8(C+1))    u64 record offsets (exclusive prefix sum of sizes)
  *   [sm_off, +r*N)     sign+mantissa bytes of every value, in value order
  *                      (bf16: 1 byte; fp32: 3 bytes little-endian; fp16: the
@@ -104,7 +107,8 @@ uzip_status uzip_compress(uzip_dtype dtype, const void *d_in, size_t num_element
  * num_elements values of `dtype`, as the receiver expects them, into d_out
  * (num_elements * sizeof(T) bytes).  The buffer is validated on the device
  * (header, record index, every record, and the rANS end state of every lane)
- * and *d_status receives 0 or UZIP_ERR_CORRUPT_INPUT.  Passage: NCCLZ
+ * and *d_status receives 0, UZIP_ERR_CORRUPT_INPUT, or UZIP_ERR_UNSUPPORTED
+ * for a frame with sampled tables (flag bit 0).  Passage: NCCLZ
  * Algorithm 2 (parse and validate the header, then decode). */
 uzip_status uzip_decompress(const void *d_in, size_t in_bytes, uzip_dtype dtype, size_t num_elements,
                             void *d_out, uint32_t *d_status,

@@ -1234,14 +1234,19 @@ __global__ void k_dec_validate(DecParams p) {
     if (b >= p.nbuf) return;
     const DecDesc d = p.nbuf == 1 ? p.single : load_dec_desc(p.descs + b);
     bool ok = d.in_bytes >= kHeaderBytes;
+    bool sampled = false;  // flag bit 0: tables from samples (record mode 2), not decoded here
     DecInfo inf = {};
     if (ok) {
         const uint4 h0 = gload<uint4>(d.in), h1 = gload<uint4>(d.in + 16);
         const uint4 h2 = gload<uint4>(d.in + 32), h3 = gload<uint4>(d.in + 48);
         const uint32_t r = raw_bytes_per_value(p.dtype);
-        // V1 magic, version, fixed coder parameters; V2 dtype and count
+        // V1 magic, version, fixed coder parameters, flags (bit 0 the only
+        // one defined); V2 dtype and count
+        const uint32_t flags = h0.z >> 16;
         ok = h0.x == kMagic && (h0.y & 0xFFFFu) == kVersion && ((h0.y >> 16) & 0xFFu) == (uint32_t)p.dtype &&
-             (h0.y >> 24) == kProbBits && (h0.z & 0xFFu) == kLanes && ((h0.z >> 8) & 0xFFu) == r;
+             (h0.y >> 24) == kProbBits && (h0.z & 0xFFu) == kLanes && ((h0.z >> 8) & 0xFFu) == r && flags <= 1;
+        sampled = ok && flags == 1;
+        ok = ok && !sampled;
         const uint64_t n = uint64_t(h1.x) | (uint64_t(h1.y) << 32);
         const uint64_t C = uint64_t(h1.z) | (uint64_t(h1.w) << 32);
         const uint64_t ce = h0.w;
@@ -1271,7 +1276,7 @@ __global__ void k_dec_validate(DecParams p) {
     if (!ok) inf.chunks = 0;
     const uint4 *iv = reinterpret_cast<const uint4 *>(&inf);
     for (int k = 0; k < 4; ++k) gstore<uint4>(reinterpret_cast<uint4 *>(p.info + b) + k, iv[k]);
-    gstore<uint32_t>(p.status + b, ok ? 0u : 3u);
+    gstore<uint32_t>(p.status + b, ok ? 0u : sampled ? (uint32_t)UZIP_ERR_UNSUPPORTED : 3u);
     const uint64_t pairs = (inf.chunks + 1) / 2;
     if (p.nbuf == 1) {
         gstore<uint64_t>(p.pair_first, 0);

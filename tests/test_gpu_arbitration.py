@@ -176,4 +176,4 @@ def test_corrupt_raw_frames_are_reported(tdtype):
         _, st = gpu_decompress(bad, tdtype, bits.size)
         assert st == (uz.UZIP_ERR_CORRUPT_INPUT if want == orc.CORRUPT else 0), name
         n_bad += want == orc.CORRUPT
-    assert n_bad == 12  # every one of them is a corruption the oracle reports
+    assert n_bad == 13  # every one of them is a corruption the oracle reports

@@ -485,7 +485,7 @@ def test_corruption_detected():
         st, _ = orc.decompress(bad, orc.BF16, bits.size)
         assert st == orc.CORRUPT, name
         seen += 1
-    assert seen == 23
+    assert seen == 24
     st, _ = orc.decompress(buf, orc.FP32, bits.size // 2)
     assert st == orc.CORRUPT
     st, _ = orc.decompress(buf[:40], orc.BF16, bits.size)

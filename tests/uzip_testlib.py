@@ -50,6 +50,7 @@ def corruptions(buf):
     yield "version", patch(4, 2, 2)
     yield "dtype", patch(6, 2, 1)
     yield "prob_bits", patch(7, 11, 1)
+    yield "flags", patch(10, 2, 2)
     yield "count", patch(16, hdr["n"] + 1, 8)
     yield "chunk_elems", patch(12, 1000, 4)
     yield "sm_off", patch(32, hdr["sm_off"] + 16, 8)
@@ -89,6 +90,7 @@ def raw_corruptions(buf):
     yield "truncated", buf[:-16]
     yield "magic", patch(0, 0x31505A56, 4)
     yield "dtype", patch(6, 6, 1)
+    yield "flags", patch(10, 2, 2)
     yield "count", patch(16, hdr["n"] + 1, 8)
     yield "total", patch(48, buf.size + 16, 8)
     yield "index_unaligned", patch(64 + 8 * (ri + 1), idx[ri + 1] + 2, 8)
