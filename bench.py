@@ -64,6 +64,8 @@ def parse():
     ap.add_argument("--chunk-bytes", type=int, default=0, help="uncompressed chunk size (0: the dtype's default)")
     ap.add_argument("--link-gbps", type=float, default=0.0,
                     help="compress with the per-call arbitration for a link of this many GB/s (0: plain compress)")
+    ap.add_argument("--sampled", action="store_true",
+                    help="tables from each chunk's sample (uzip_compress_sampled): one read of the input")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum CPU-oracle time to accumulate")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     return ap.parse_args()
@@ -227,9 +229,9 @@ def main():
         elif pol is not None:
             uz.compress_arbitrated(ts[0], pol, cb, out=outs[0], ws=ws, out_size=sizes, plan=plans)
         elif batched:
-            uz.compress_batched(ts, cb, outs=outs, ws=ws, out_sizes=sizes)
+            uz.compress_batched(ts, cb, outs=outs, ws=ws, out_sizes=sizes, sampled=args.sampled)
         else:
-            uz.compress(ts[0], cb, out=outs[0], ws=ws, out_size=sizes)
+            uz.compress(ts[0], cb, out=outs[0], ws=ws, out_size=sizes, sampled=args.sampled)
 
     def decompress():
         # in_bytes = capacity: the decoder validates the header's total against it
@@ -300,7 +302,8 @@ def main():
     else:
         kname, kbytes, kms = "k_decode", dec_bytes, dec_kernel_ms
     achieved = kbytes / (kms * 1e-3) / 1e9
-    traffic = MEASURED_TRAFFIC.get((args.workload, kname)) if kernel_source_digest() == MEASURED_TRAFFIC_SOURCE else None
+    tkey = (args.workload + (":sampled" if args.sampled else ""), kname)
+    traffic = MEASURED_TRAFFIC.get(tkey) if kernel_source_digest() == MEASURED_TRAFFIC_SOURCE else None
     roofline = {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                 "traffic": traffic,
@@ -319,7 +322,7 @@ def main():
     cpu = None
     oracle_match = None
     if not args.no_cpu_baseline:
-        cpu, oracle_match = cpu_baseline(ts, outs, comp_sizes, code, args.cpu_seconds, cb, pol)
+        cpu, oracle_match = cpu_baseline(ts, outs, comp_sizes, code, args.cpu_seconds, cb, pol, args.sampled)
 
     med_c = comp_ms[len(comp_ms) // 2]
     med_d = dec_ms[len(dec_ms) // 2]
@@ -338,7 +341,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": desc, "values": n_total, "buffers": len(ts), "input_bytes": in_bytes,
                    "value_dtype": VALUE_DTYPE[code], "chunk_bytes": chunk_elems * eb,
-                   "step": "compress + decompress"},
+                   "tables": "sampled" if args.sampled else "full", "step": "compress + decompress"},
         "compress_gbps": round(in_bytes / (med_c * 1e-3) / 1e9, 2),
         "decompress_gbps": round(in_bytes / (med_d * 1e-3) / 1e9, 2),
         "compress_ms": {"median": round(med_c, 4), "min": round(comp_ms[0], 4)},
@@ -387,7 +390,7 @@ def copy_reference(ts, steps):
     return 2 * nbytes / (ms * 1e-3) / 1e9
 
 
-def cpu_baseline(ts, outs, comp_sizes, code, min_seconds, chunk_bytes, pol=None):
+def cpu_baseline(ts, outs, comp_sizes, code, min_seconds, chunk_bytes, pol=None, sampled=False):
     """The oracle (plain single-threaded C) on a bounded sample of the same
     workload: whole buffers, in order, up to 512 MiB of input; passes repeat
     until min_seconds of CPU time have been spent.  Also compares the oracle's
@@ -408,7 +411,7 @@ def cpu_baseline(ts, outs, comp_sizes, code, min_seconds, chunk_bytes, pol=None)
     match = True
     for i, h in zip(picked, host):
         if pol is None:
-            want = oracle.compress(code, h, chunk_bytes)
+            want = (oracle.compress_sampled if sampled else oracle.compress)(code, h, chunk_bytes)
         else:  # the arbitrated frame (the plan may have chosen RAW)
             opol = oracle.Policy(**{f: getattr(pol, f) for f, _ in pol._fields_})
             want = oracle.compress_arbitrated(code, h, opol, chunk_bytes)[0]
@@ -419,7 +422,7 @@ def cpu_baseline(ts, outs, comp_sizes, code, min_seconds, chunk_bytes, pol=None)
     while passes == 0 or spent < min_seconds:
         t0 = time.perf_counter()
         for h in host:
-            buf = oracle.compress(code, h, chunk_bytes)
+            buf = (oracle.compress_sampled if sampled else oracle.compress)(code, h, chunk_bytes)
             st, back = oracle.decompress(buf, code, h.size)
             assert st == 0
         spent += time.perf_counter() - t0

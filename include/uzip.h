@@ -21,15 +21,17 @@
  *                      lanes 32, raw bytes per value r, u16 flags,
  *                      chunk_elems, N, C, sm_off, exp_off, total_bytes
  *                      (flags: 0, or bit 0 = chunk tables taken from samples
- *                      with an escape list, record mode 2; this library
- *                      writes flags 0 and reports bit 0 as unsupported)
+ *                      with an escape list, record mode 2, written by the
+ *                      *_sampled calls; the decoder reads both kinds)
  *   [64, 64+8(C+1))    u64 record offsets (exclusive prefix sum of sizes)
  *   [sm_off, +r*N)     sign+mantissa bytes of every value, in value order
  *                      (bf16: 1 byte; fp32: 3 bytes little-endian; fp16: the
  *                      low byte; fp8: none)
  *   [exp_off, total)   one record per chunk: a 16-byte record header, then
  *                      either the rANS table, 32 final states and 16-bit words
- *                      (mode RANS) or the chunk's raw exponent bytes (RAW).
+ *                      (mode RANS; mode 2 adds the escape count before the
+ *                      states and the escaped exponent bytes after the words)
+ *                      or the chunk's raw exponent bytes (RAW).
  *
  * Memory and ownership.  Every pointer named d_* is device memory of the
  * current HIP device; every h_* pointer is host memory.  The caller owns all
@@ -79,7 +81,7 @@ typedef enum {
     UZIP_ERR_CAPACITY = 2,
     UZIP_ERR_CORRUPT_INPUT = 3,
     UZIP_ERR_DEVICE = 4,
-    UZIP_ERR_UNSUPPORTED = 5
+    UZIP_ERR_UNSUPPORTED = 5 /* reserved: no call of this version returns it */
 } uzip_status;
 
 /* Exact upper bound of the compressed size of num_elements values: the size
@@ -107,9 +109,10 @@ uzip_status uzip_compress(uzip_dtype dtype, const void *d_in, size_t num_element
  * num_elements values of `dtype`, as the receiver expects them, into d_out
  * (num_elements * sizeof(T) bytes).  The buffer is validated on the device
  * (header, record index, every record, and the rANS end state of every lane)
- * and *d_status receives 0, UZIP_ERR_CORRUPT_INPUT, or UZIP_ERR_UNSUPPORTED
- * for a frame with sampled tables (flag bit 0).  Passage: NCCLZ
- * Algorithm 2 (parse and validate the header, then decode). */
+ * and *d_status receives 0 or UZIP_ERR_CORRUPT_INPUT.  Frames of both kinds
+ * (full tables, or sampled tables: header flag bit 0) are read; the kind
+ * comes from the frame.  Passage: NCCLZ Algorithm 2 (parse and validate the
+ * header, then decode). */
 uzip_status uzip_decompress(const void *d_in, size_t in_bytes, uzip_dtype dtype, size_t num_elements,
                             void *d_out, uint32_t *d_status,
                             void *d_workspace, size_t workspace_bytes, hipStream_t stream);
@@ -131,6 +134,30 @@ uzip_status uzip_compress_batched(uzip_dtype dtype, size_t num_buffers,
                                   const void *const *h_in, const size_t *h_num_elements, size_t chunk_bytes,
                                   void *const *h_out, const size_t *h_out_capacity, uint64_t *d_out_sizes,
                                   void *d_workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ---- sampled tables: one read of the input --------------------------------
+ * UCCL-Zip (Sec. 3, the text on Figure 5) lets each block build its table
+ * from a sample of its own data.  These calls take each chunk's table from
+ * eight evenly spaced runs of max(1, chunk_elems / 64) values, one every
+ * chunk_elems / 8 (an eighth of a full chunk).  The sampled symbols share
+ * 4095 table slots (one each, the rest by largest remainder of the sample's
+ * counts); the table's last slot is an escape symbol, and a value whose
+ * exponent the sample missed is coded as the escape, its exponent byte
+ * appended to the record's escape list in value order (record mode 2, header
+ * flag bit 0).  The encoder then splits, stores the sign+mantissa bytes and
+ * codes in one backward pass over the input, instead of a counting pass and
+ * a coding pass.  Arguments, sizes (uzip_max_compressed_size,
+ * uzip_workspace_size*), ownership and errors are those of uzip_compress and
+ * uzip_compress_batched; a chunk is still stored RAW when coding does not
+ * make it smaller.  uzip_decompress and uzip_decompress_batched read these
+ * frames (and batches mixing both kinds). */
+uzip_status uzip_compress_sampled(uzip_dtype dtype, const void *d_in, size_t num_elements, size_t chunk_bytes,
+                                  void *d_out, size_t out_capacity, uint64_t *d_out_size,
+                                  void *d_workspace, size_t workspace_bytes, hipStream_t stream);
+uzip_status uzip_compress_batched_sampled(uzip_dtype dtype, size_t num_buffers,
+                                          const void *const *h_in, const size_t *h_num_elements, size_t chunk_bytes,
+                                          void *const *h_out, const size_t *h_out_capacity, uint64_t *d_out_sizes,
+                                          void *d_workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Decompress num_buffers buffers in one set of launches; d_status[b] receives
  * buffer b's validation result.  Same passage as uzip_decompress. */

@@ -61,6 +61,8 @@ EXPORTED = (
     "uzip_decompress_batched",
     "uzip_compress_arbitrated",
     "uzip_compress_batched_arbitrated",
+    "uzip_compress_sampled",
+    "uzip_compress_batched_sampled",
     "uzip_profile_set_events",
     "uzip_status_string",
 )
@@ -88,12 +90,16 @@ def lib() -> ctypes.CDLL:
         L.uzip_workspace_size.argtypes = [i32, sz, sz]
         L.uzip_compress.restype = i32
         L.uzip_compress.argtypes = [i32, vp, sz, sz, vp, sz, u64p, vp, sz, vp]
+        L.uzip_compress_sampled.restype = i32
+        L.uzip_compress_sampled.argtypes = [i32, vp, sz, sz, vp, sz, u64p, vp, sz, vp]
         L.uzip_decompress.restype = i32
         L.uzip_decompress.argtypes = [vp, sz, i32, sz, vp, vp, vp, sz, vp]
         L.uzip_workspace_size_batched.restype = sz
         L.uzip_workspace_size_batched.argtypes = [i32, sz, vp, sz]
         L.uzip_compress_batched.restype = i32
         L.uzip_compress_batched.argtypes = [i32, sz, vp, vp, sz, vp, vp, u64p, vp, sz, vp]
+        L.uzip_compress_batched_sampled.restype = i32
+        L.uzip_compress_batched_sampled.argtypes = [i32, sz, vp, vp, sz, vp, vp, u64p, vp, sz, vp]
         L.uzip_decompress_batched.restype = i32
         L.uzip_decompress_batched.argtypes = [i32, sz, vp, vp, vp, vp, vp, vp, sz, vp]
         L.uzip_compress_arbitrated.restype = i32
@@ -123,6 +129,12 @@ def uzip_compress(dtype, d_in, num_elements, chunk_bytes, d_out, out_capacity, d
                   workspace_bytes, stream) -> int:
     return int(lib().uzip_compress(dtype, d_in, num_elements, chunk_bytes, d_out, out_capacity, d_out_size,
                                    d_workspace, workspace_bytes, stream))
+
+
+def uzip_compress_sampled(dtype, d_in, num_elements, chunk_bytes, d_out, out_capacity, d_out_size, d_workspace,
+                          workspace_bytes, stream) -> int:
+    return int(lib().uzip_compress_sampled(dtype, d_in, num_elements, chunk_bytes, d_out, out_capacity, d_out_size,
+                                           d_workspace, workspace_bytes, stream))
 
 
 def uzip_decompress(d_in, in_bytes, dtype, num_elements, d_out, d_status, d_workspace, workspace_bytes,
@@ -158,6 +170,13 @@ def uzip_compress_batched(dtype, h_in, h_num_elements, chunk_bytes, h_out, h_out
     a_in, a_n, a_out, a_cap = _ptrs(h_in), _sizes(h_num_elements), _ptrs(h_out), _sizes(h_out_capacity)
     return int(lib().uzip_compress_batched(dtype, len(h_in), a_in.ptr, a_n.ptr, chunk_bytes, a_out.ptr, a_cap.ptr,
                                            d_out_sizes, d_workspace, workspace_bytes, stream))
+
+
+def uzip_compress_batched_sampled(dtype, h_in, h_num_elements, chunk_bytes, h_out, h_out_capacity, d_out_sizes,
+                                  d_workspace, workspace_bytes, stream) -> int:
+    a_in, a_n, a_out, a_cap = _ptrs(h_in), _sizes(h_num_elements), _ptrs(h_out), _sizes(h_out_capacity)
+    return int(lib().uzip_compress_batched_sampled(dtype, len(h_in), a_in.ptr, a_n.ptr, chunk_bytes, a_out.ptr,
+                                                   a_cap.ptr, d_out_sizes, d_workspace, workspace_bytes, stream))
 
 
 def uzip_decompress_batched(dtype, h_in, h_in_bytes, h_num_elements, h_out, d_status, d_workspace, workspace_bytes,
@@ -221,10 +240,12 @@ def workspace(nbytes: int, device) -> torch.Tensor:
 
 
 def compress(t: torch.Tensor, chunk_bytes: int = 0, out: torch.Tensor | None = None,
-             ws: torch.Tensor | None = None, out_size: torch.Tensor | None = None, stream=None):
+             ws: torch.Tensor | None = None, out_size: torch.Tensor | None = None, stream=None,
+             sampled: bool = False):
     """Compress a contiguous bf16/fp32/fp16/fp8 device tensor.  Returns (buffer, size)
     where `buffer` has capacity uzip_max_compressed_size and `size` is a
-    one-element int64 device tensor holding the exact compressed size."""
+    one-element int64 device tensor holding the exact compressed size.
+    sampled=True builds each chunk's table from a sample (uzip_compress_sampled)."""
     if not t.is_cuda or not t.is_contiguous():
         raise ValueError("compress needs a contiguous device tensor")
     code = dtype_code(t.dtype)
@@ -239,9 +260,10 @@ def compress(t: torch.Tensor, chunk_bytes: int = 0, out: torch.Tensor | None = N
     wsz = uzip_workspace_size(code, n, chunk_bytes)
     if ws is None:
         ws = workspace(wsz, t.device)
-    st = uzip_compress(code, t.data_ptr() if n else None, n, chunk_bytes, out.data_ptr(), out.numel(),
-                       out_size.data_ptr(), ws.data_ptr(), ws.numel(), _stream(stream))
-    _check(st, "uzip_compress")
+    fn = uzip_compress_sampled if sampled else uzip_compress
+    st = fn(code, t.data_ptr() if n else None, n, chunk_bytes, out.data_ptr(), out.numel(),
+            out_size.data_ptr(), ws.data_ptr(), ws.numel(), _stream(stream))
+    _check(st, fn.__name__)
     return out, out_size
 
 
@@ -265,9 +287,11 @@ def decompress(buf: torch.Tensor, dtype: torch.dtype, n: int, in_bytes: int | No
     return out, status
 
 
-def compress_batched(tensors, chunk_bytes: int = 0, outs=None, ws=None, out_sizes=None, stream=None):
+def compress_batched(tensors, chunk_bytes: int = 0, outs=None, ws=None, out_sizes=None, stream=None,
+                     sampled: bool = False):
     """Compress a list of same-dtype contiguous device tensors in one call.
-    Returns (buffers, sizes[int64 tensor of len(tensors)])."""
+    Returns (buffers, sizes[int64 tensor of len(tensors)]).  sampled=True:
+    uzip_compress_batched_sampled."""
     code = dtype_code(tensors[0].dtype)
     dev = tensors[0].device
     ns = [t.numel() for t in tensors]
@@ -277,10 +301,11 @@ def compress_batched(tensors, chunk_bytes: int = 0, outs=None, ws=None, out_size
         out_sizes = torch.empty(len(tensors), dtype=torch.int64, device=dev)
     if ws is None:
         ws = workspace(uzip_workspace_size_batched(code, ns, chunk_bytes), dev)
-    st = uzip_compress_batched(code, [t.data_ptr() if t.numel() else 0 for t in tensors], ns, chunk_bytes,
-                               [o.data_ptr() for o in outs], [o.numel() for o in outs], out_sizes.data_ptr(),
-                               ws.data_ptr(), ws.numel(), _stream(stream))
-    _check(st, "uzip_compress_batched")
+    fn = uzip_compress_batched_sampled if sampled else uzip_compress_batched
+    st = fn(code, [t.data_ptr() if t.numel() else 0 for t in tensors], ns, chunk_bytes,
+            [o.data_ptr() for o in outs], [o.numel() for o in outs], out_sizes.data_ptr(),
+            ws.data_ptr(), ws.numel(), _stream(stream))
+    _check(st, fn.__name__)
     return outs, out_sizes
 
 

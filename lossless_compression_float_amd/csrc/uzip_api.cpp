@@ -59,7 +59,7 @@ EncWs enc_ws(uint64_t nbuf, uint64_t chunks, uint64_t ce) {
     o += al(chunks * 8);
     w.ticket = o;
     o += al(8);
-    w.slot_stride = std::max<uint64_t>(raw_record_bytes(ce), align16(words_offset(256)));
+    w.slot_stride = std::max<uint64_t>(raw_record_bytes(ce), align16(words_offset_sampled(256)));
     w.slots = o;
     o += chunks * w.slot_stride;
     w.bytes = o + kWsAlign;  // slack: the caller's pointer need only be 16-byte aligned
@@ -67,7 +67,7 @@ EncWs enc_ws(uint64_t nbuf, uint64_t chunks, uint64_t ce) {
 }
 
 struct DecWs {
-    uint64_t descs, info, pair_first, bytes;
+    uint64_t descs, info, pair_first, kinds, bytes;
 };
 
 DecWs dec_ws(uint64_t nbuf) {
@@ -79,6 +79,8 @@ DecWs dec_ws(uint64_t nbuf) {
     o += al(nbuf * sizeof(DecInfo));
     w.pair_first = o;
     o += al((nbuf + 1) * 8);
+    w.kinds = o;
+    o += al(4);
     w.bytes = o + kWsAlign;
     return w;
 }
@@ -109,7 +111,7 @@ bool policy_ok(const uzip_policy *p) {
 // arbitrated forms).
 uzip_status compress_impl(uzip_dtype dtype, uint64_t ce, std::vector<EncDesc> &descs, uint64_t chunks,
                           void *d_workspace, size_t workspace_bytes, hipStream_t stream,
-                          uzip_plan *plans = nullptr, const uzip_policy *policy = nullptr) {
+                          uzip_plan *plans = nullptr, const uzip_policy *policy = nullptr, bool sampled = false) {
     const uint32_t nbuf = (uint32_t)descs.size();
     const EncWs w = enc_ws(nbuf, chunks, ce);
     if (d_workspace == nullptr || workspace_bytes < w.bytes || !aligned(d_workspace, 16))
@@ -134,6 +136,7 @@ uzip_status compress_impl(uzip_dtype dtype, uint64_t ce, std::vector<EncDesc> &d
     ep.flags = reinterpret_cast<uint64_t *>(base + w.flags);
     ep.ticket = reinterpret_cast<uint32_t *>(base + w.ticket);
     ep.dtype = dtype;
+    ep.sampled = sampled ? 1u : 0u;
     ep.plans = plans;
     if (policy) ep.policy = *policy;
     if (nbuf == 1) {
@@ -154,7 +157,8 @@ uzip_status compress_impl(uzip_dtype dtype, uint64_t ce, std::vector<EncDesc> &d
 // Body of uzip_compress and uzip_compress_arbitrated (policy null: no arbitration).
 uzip_status compress_single(uzip_dtype dtype, const void *d_in, size_t num_elements, size_t chunk_bytes,
                             const uzip_policy *policy, void *d_out, size_t out_capacity, uint64_t *d_out_size,
-                            uzip_plan *d_plan, void *d_workspace, size_t workspace_bytes, hipStream_t stream) {
+                            uzip_plan *d_plan, void *d_workspace, size_t workspace_bytes, hipStream_t stream,
+                            bool sampled = false) {
     const uint64_t ce = chunk_elems_of(dtype, chunk_bytes);
     if (!ce) return UZIP_ERR_INVALID_ARGUMENT;
     if (num_elements > 0 && (d_in == nullptr || !aligned(d_in, 16))) return UZIP_ERR_INVALID_ARGUMENT;
@@ -166,14 +170,15 @@ uzip_status compress_single(uzip_dtype dtype, const void *d_in, size_t num_eleme
     descs[0] = EncDesc{static_cast<const uint8_t *>(d_in), static_cast<uint8_t *>(d_out), d_out_size, num_elements,
                        0, l.sm_off, l.exp_off, l.chunks, 0, 0};
     return compress_impl(dtype, ce, descs, l.chunks, d_workspace, workspace_bytes, stream,
-                         policy ? d_plan : nullptr, policy);
+                         policy ? d_plan : nullptr, policy, sampled);
 }
 
 // Body of uzip_compress_batched and its arbitrated form (policy null: no arbitration).
 uzip_status compress_batched(uzip_dtype dtype, size_t num_buffers, const void *const *h_in,
                              const size_t *h_num_elements, size_t chunk_bytes, const uzip_policy *policy,
                              void *const *h_out, const size_t *h_out_capacity, uint64_t *d_out_sizes,
-                             uzip_plan *d_plans, void *d_workspace, size_t workspace_bytes, hipStream_t stream) {
+                             uzip_plan *d_plans, void *d_workspace, size_t workspace_bytes, hipStream_t stream,
+                             bool sampled = false) {
     const uint64_t ce = chunk_elems_of(dtype, chunk_bytes);
     if (!ce || num_buffers == 0 || num_buffers > 0xFFFFFFFFull) return UZIP_ERR_INVALID_ARGUMENT;
     if (!h_in || !h_num_elements || !h_out || !h_out_capacity || !d_out_sizes || !aligned(d_out_sizes, 8))
@@ -192,7 +197,7 @@ uzip_status compress_batched(uzip_dtype dtype, size_t num_buffers, const void *c
         chunks += l.chunks;
     }
     return compress_impl(dtype, ce, descs, chunks, d_workspace, workspace_bytes, stream,
-                         policy ? d_plans : nullptr, policy);
+                         policy ? d_plans : nullptr, policy, sampled);
 }
 
 uzip_status decompress_impl(uzip_dtype dtype, std::vector<DecDesc> &descs, uint32_t *d_status, void *d_workspace,
@@ -210,6 +215,7 @@ uzip_status decompress_impl(uzip_dtype dtype, std::vector<DecDesc> &descs, uint3
     vp.info = reinterpret_cast<DecInfo *>(base + w.info);
     vp.pair_first = reinterpret_cast<uint64_t *>(base + w.pair_first);
     vp.status = d_status;
+    vp.kinds = reinterpret_cast<uint32_t *>(base + w.kinds);
     if (nbuf == 1) {
         vp.single = descs[0];
     } else {
@@ -225,6 +231,7 @@ uzip_status decompress_impl(uzip_dtype dtype, std::vector<DecDesc> &descs, uint3
     dp.info = vp.info;
     dp.pair_first = vp.pair_first;
     dp.status = d_status;
+    dp.kinds = vp.kinds;
     const hipError_t e = launch_decompress(vp, dp, dtype, max_chunks, stream);
     return e == hipSuccess ? UZIP_OK : UZIP_ERR_DEVICE;
 }
@@ -261,6 +268,13 @@ uzip_status uzip_compress(uzip_dtype dtype, const void *d_in, size_t num_element
                            d_workspace, workspace_bytes, stream);
 }
 
+uzip_status uzip_compress_sampled(uzip_dtype dtype, const void *d_in, size_t num_elements, size_t chunk_bytes,
+                                  void *d_out, size_t out_capacity, uint64_t *d_out_size, void *d_workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
+    return compress_single(dtype, d_in, num_elements, chunk_bytes, nullptr, d_out, out_capacity, d_out_size, nullptr,
+                           d_workspace, workspace_bytes, stream, true);
+}
+
 uzip_status uzip_compress_arbitrated(uzip_dtype dtype, const void *d_in, size_t num_elements, size_t chunk_bytes,
                                      const uzip_policy *policy, void *d_out, size_t out_capacity,
                                      uint64_t *d_out_size, uzip_plan *d_plan, void *d_workspace,
@@ -288,6 +302,14 @@ uzip_status uzip_compress_batched(uzip_dtype dtype, size_t num_buffers, const vo
                                   size_t workspace_bytes, hipStream_t stream) {
     return compress_batched(dtype, num_buffers, h_in, h_num_elements, chunk_bytes, nullptr, h_out, h_out_capacity,
                             d_out_sizes, nullptr, d_workspace, workspace_bytes, stream);
+}
+
+uzip_status uzip_compress_batched_sampled(uzip_dtype dtype, size_t num_buffers, const void *const *h_in,
+                                          const size_t *h_num_elements, size_t chunk_bytes, void *const *h_out,
+                                          const size_t *h_out_capacity, uint64_t *d_out_sizes, void *d_workspace,
+                                          size_t workspace_bytes, hipStream_t stream) {
+    return compress_batched(dtype, num_buffers, h_in, h_num_elements, chunk_bytes, nullptr, h_out, h_out_capacity,
+                            d_out_sizes, nullptr, d_workspace, workspace_bytes, stream, true);
 }
 
 uzip_status uzip_compress_batched_arbitrated(uzip_dtype dtype, size_t num_buffers, const void *const *h_in,

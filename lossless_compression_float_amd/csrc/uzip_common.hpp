@@ -44,6 +44,16 @@ __host__ __device__ inline uint64_t raw_record_bytes(uint64_t n_values) { return
 __host__ __device__ inline uint64_t states_offset(uint32_t nsym) { return align4(kRecHeaderBytes + 32 + 2ull * nsym); }
 __host__ __device__ inline uint64_t words_offset(uint32_t nsym) { return states_offset(nsym) + 4ull * kLanes; }
 
+// A record coded with a table from the chunk's sample (record mode 2, frames
+// with header flag bit 0): after the frequencies and their padding comes the
+// u32 count of escaped values, then the 32 states, the words, and the escaped
+// exponent bytes in value order.  The escape symbol holds the table's last
+// slot (f = 1, c0 = 4095); the sampled symbols share the other 4095.
+constexpr uint32_t kEscSlot = kTableSize - 1;
+__host__ __device__ inline uint64_t esc_count_offset(uint32_t nsym) { return align4(kRecHeaderBytes + 32 + 2ull * nsym); }
+__host__ __device__ inline uint64_t states_offset_sampled(uint32_t nsym) { return esc_count_offset(nsym) + 4; }
+__host__ __device__ inline uint64_t words_offset_sampled(uint32_t nsym) { return states_offset_sampled(nsym) + 4ull * kLanes; }
+
 struct Layout {
     uint64_t chunks;   // C
     uint64_t sm_off;   // start of the sign+mantissa region
@@ -88,7 +98,8 @@ struct alignas(16) DecInfo {
     uint64_t sm_off;
     uint64_t exp_off;
     uint64_t total;
-    uint64_t pad[3];
+    uint64_t flags;        // header flags (bit 0: sampled tables, record mode 2)
+    uint64_t pad[2];
 };
 
 }  // namespace uzip

@@ -110,6 +110,9 @@ __device__ inline uint4 bld128(rsrc_t r, uint32_t off) {
 __device__ inline void bst16(rsrc_t r, uint32_t off, uint32_t v) {
     __builtin_amdgcn_raw_buffer_store_b16((unsigned short)v, r, (int)off, 0, 0);
 }
+__device__ inline void bst8(rsrc_t r, uint32_t off, uint32_t v) {
+    __builtin_amdgcn_raw_buffer_store_b8((unsigned char)v, r, (int)off, 0, 0);
+}
 __device__ inline void bst32(rsrc_t r, uint32_t off, uint32_t v) {
     __builtin_amdgcn_raw_buffer_store_b32(v, r, (int)off, 0, 0);
 }
@@ -127,6 +130,7 @@ __device__ inline void asm_vmem_fence() { asm volatile("s_nop 4"); }
 // vector compare: a vector read of scalar registers that a vector instruction
 // just wrote needs wait states, which the compiler does not insert for asm.
 __device__ inline uint64_t lanes_lt(uint32_t a, uint32_t b) { return __builtin_amdgcn_uicmp(a, b, 36 /* ULT */); }
+__device__ inline uint64_t lanes_eq(uint32_t a, uint32_t b) { return __builtin_amdgcn_uicmp(a, b, 32 /* EQ */); }
 __device__ inline uint32_t vsel(uint64_t mask, uint32_t if0, uint32_t if1) {
     uint32_t r;
     asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(r) : "v"(if0), "v"(if1), "s"(mask));
@@ -262,11 +266,11 @@ __device__ inline void bst_value(rsrc_t r, uint32_t off, uint32_t v) {
 // 32-bit word k (0..15) of a buffer header (bitstream v1; NCCLZ Sec. IV-D2
 // self-describing frame: magic, version, codec parameters, sizes)
 __device__ inline uint32_t header_word(uint32_t k, int dtype, uint32_t chunk_elems, uint64_t n, uint64_t chunks,
-                                       uint64_t sm_off, uint64_t exp_off, uint64_t total) {
+                                       uint64_t sm_off, uint64_t exp_off, uint64_t total, uint32_t flags = 0) {
     switch (k) {
         case 0: return kMagic;
         case 1: return kVersion | (uint32_t(dtype) << 16) | (kProbBits << 24);
-        case 2: return kLanes | (raw_bytes_per_value(dtype) << 8);
+        case 2: return kLanes | (raw_bytes_per_value(dtype) << 8) | (flags << 16);
         case 3: return chunk_elems;
         case 4: return (uint32_t)n;
         case 5: return (uint32_t)(n >> 32);
@@ -453,7 +457,7 @@ template <int DT> struct EncLds {
 __device__ inline double enc_reciprocal(uint32_t f) { return (1.0 + 0x1p-44) / (double)f; }
 __device__ inline uint32_t enc_quotient(uint32_t x, double r) { return (uint32_t)((double)x * r); }
 
-template <int DT>
+template <int DT, bool S>
 __global__ __launch_bounds__(64) void k_encode(EncParams p) {
     constexpr uint32_t EB = Fmt<DT>::EB;      // bytes per value
     constexpr uint32_t R = Fmt<DT>::R;        // raw bytes per value
@@ -495,6 +499,43 @@ __global__ __launch_bounds__(64) void k_encode(EncParams p) {
     for (uint32_t k = lane; k < 2 * kSubHist * kSubRow; k += 64) lds[k] = 0;
     __syncthreads();
 
+    uint32_t scnt = 0;  // sampled values of this half's chunk (S)
+    if constexpr (S) {
+        // ---- the chunk's sample: eight evenly spaced runs of max(1, ce/64)
+        // contiguous values, one every ce/8 (an eighth of a full chunk), counted
+        // into the LDS histogram; the sign+mantissa split happens in the coding
+        // pass, which reads every value once ----
+        const uint32_t period = (uint32_t)ce / 8, runlen = max(1u, (uint32_t)ce / 64);
+        for (uint32_t r = 0; r < 8; ++r) scnt += r * period < ni ? min(runlen, ni - r * period) : 0u;
+        if (runlen % VPL == 0) {
+            const uint32_t rv = runlen / VPL, nvec = 8 * rv;  // 128-bit vectors per run and per sample
+            for (uint32_t k0 = 0; k0 < nvec; k0 += 4 * 32) {
+                uint4 qv[4];
+                uint32_t i0[4];
+#pragma unroll
+                for (uint32_t u = 0; u < 4; ++u) {
+                    const uint32_t k = k0 + 32 * u + lj;
+                    i0[u] = k < nvec ? (k / rv) * period + (k % rv) * VPL : 0xFFFFFFFFu;
+                    qv[u] = bld128(rin, i0[u] < ni ? in0 + i0[u] * EB : kOutOfRange);  // past the pair: zeros
+                }
+#pragma unroll
+                for (uint32_t u = 0; u < 4; ++u) {
+                    if (i0[u] >= ni) continue;
+                    const uint32_t w[4] = {qv[u].x, qv[u].y, qv[u].z, qv[u].w};
+#pragma unroll
+                    for (uint32_t k = 0; k < VPL; ++k) {
+                        const uint32_t v = EB == 4 ? w[k] : (w[k / (4 / EB)] >> (8 * EB * (k % (4 / EB)))) & ((1u << (8 * EB)) - 1u);
+                        if (i0[u] + k < ni) atomicAdd(&hist[exponent_of<DT>(v)], 1u);
+                    }
+                }
+            }
+        } else {  // runs shorter than a vector (small chunks): value by value
+            for (uint32_t j = lj; j < 8 * runlen; j += 32) {
+                const uint32_t i = (j / runlen) * period + j % runlen;
+                if (i < ni) atomicAdd(&hist[exponent_of<DT>(bld_value<DT>(rin, in0 + i * EB))], 1u);
+            }
+        }
+    } else {
     // ---- pass 1: split, sign+mantissa bytes to the output, LDS histogram ----
     // Main loop: iterations in which every lane of each coding half holds a
     // full 128-bit vector, with four to eight loads in flight per lane.  A half without
@@ -637,6 +678,7 @@ __global__ __launch_bounds__(64) void k_encode(EncParams p) {
             }
         }
     }
+    }  // pass 1
     __syncthreads();
 
     // ---- normalise the counts to a table of 4096 (lane lj owns symbols 8lj..8lj+7) ----
@@ -661,7 +703,10 @@ __global__ __launch_bounds__(64) void k_encode(EncParams p) {
     const uint32_t np = __popc(pm);
     const uint32_t nsym = half_sum(np);
     const uint32_t pre = half_excl_scan(np, lj);
-    const uint32_t Rr = kTableSize - nsym;
+    // full tables share R = 4096 - nsym slots by the chunk's counts; sampled
+    // ones R = 4095 - nsym by the sample's (the escape symbol keeps slot 4095)
+    const uint32_t den = S ? scnt : ni;
+    const uint32_t Rr = kTableSize - nsym - (S ? 1u : 0u);
     uint32_t fl[8], key[8], given = 0;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
@@ -669,8 +714,8 @@ __global__ __launch_bounds__(64) void k_encode(EncParams p) {
         key[k] = 0;
         if (c[k]) {
             const uint32_t qq = c[k] * Rr;  // < 2^32: c <= 2^20, R < 2^12
-            fl[k] = qq / ni;
-            key[k] = ((qq - fl[k] * ni) << 8) | (255u - (lj * 8 + k));
+            fl[k] = qq / den;
+            key[k] = ((qq - fl[k] * den) << 8) | (255u - (lj * 8 + k));
             given += fl[k];
         }
     }
@@ -704,10 +749,13 @@ __global__ __launch_bounds__(64) void k_encode(EncParams p) {
     const uint32_t cbase = half_excl_scan(lsum, lj);
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-        const double r = f[k] ? enc_reciprocal(f[k]) : 0.0;
+        // a symbol the sample missed is coded as the escape symbol (f = 1, c0 = 4095)
+        const bool esc = S && f[k] == 0;
+        const uint32_t fe = esc ? 1u : f[k], ce0 = esc ? kEscSlot : cbase + cpre[k];
+        const double r = fe ? enc_reciprocal(fe) : 0.0;
         const uint64_t rb = (uint64_t)__double_as_longlong(r);
         // (f - 1) | (4096 - f) << 16: the emission threshold and the multiplier of the coding step
-        tab[lj * 8 + k] = make_uint4(((f[k] - 1) & 0xFFFFu) | ((kTableSize - f[k]) << 16), cbase + cpre[k], (uint32_t)rb,
+        tab[lj * 8 + k] = make_uint4(((fe - 1) & 0xFFFFu) | ((kTableSize - fe) << 16), ce0, (uint32_t)rb,
                                      (uint32_t)(rb >> 32));
     }
 
@@ -731,18 +779,41 @@ __global__ __launch_bounds__(64) void k_encode(EncParams p) {
     // input resource (past the pair: zeros, never coded).
     const uint32_t nsym0 = uniform_u32(__shfl((int)nsym, 0, 64)), nsym1 = uniform_u32(__shfl((int)nsym, 32, 64));
     const uint32_t raw0 = (uint32_t)raw_record_bytes(vals0), raw1 = (uint32_t)raw_record_bytes(vals1);
-    const uint32_t wofs0 = (uint32_t)words_offset(nsym0), wofs1 = (uint32_t)words_offset(nsym1);
+    const uint32_t wofs0 = (uint32_t)(S ? words_offset_sampled(nsym0) : words_offset(nsym0));
+    const uint32_t wofs1 = (uint32_t)(S ? words_offset_sampled(nsym1) : words_offset(nsym1));
     // words that fit before a record reaches its RAW size; a chunk whose table
     // alone reaches it is RAW without coding
     const uint32_t wcap0 = raw0 > wofs0 ? (raw0 - wofs0) / 2 : 0u;
     const uint32_t wcap1 = nch == 2 && raw1 > wofs1 ? (raw1 - wofs1) / 2 : 0u;
     const uint32_t end0 = raw0 / 2, end1 = ((uint32_t)p.slot_stride + raw1) / 2;  // word index just past each slot's words
     uint32_t r0 = end0, r1 = end1;  // word index just past the words still to come, per half
-    bool alive0 = wcap0 > 0, alive1 = wcap1 > 0;  // a half stops coding once its words outgrow the RAW size
+    // sampled tables: the bytes for words and escapes before a record reaches its RAW size
+    const uint32_t room0 = raw0 > wofs0 ? raw0 - wofs0 : 0u, room1 = nch == 2 && raw1 > wofs1 ? raw1 - wofs1 : 0u;
+    // a half stops coding once its words (and escapes) outgrow the RAW size
+    bool alive0 = S ? room0 > 0 : wcap0 > 0, alive1 = S ? room1 > 0 : wcap1 > 0;
+    uint32_t nesc0 = 0, nesc1 = 0;  // escaped values so far, per half (sampled tables)
     uint32_t x = kStateLow;
-    const uint32_t T0 = alive0 ? (vals0 + 31) / 32 : 0u, T1 = alive1 ? (vals1 + 31) / 32 : 0u;
+    // (with sampled tables every value is visited: the pass also writes the sign+mantissa bytes)
+    const uint32_t T0 = S || alive0 ? (vals0 + 31) / 32 : 0u, T1 = S || alive1 ? (vals1 + 31) / 32 : 0u;
+    // sampled tables: the pair's sign+mantissa bytes (past a chunk's end: out of range, dropped)
+    const rsrc_t rsm2 = make_rsrc(d.out + d.sm_off + c0 * ce * R, pair_vals * R);
+    const uint32_t smo2 = ((h ? vals0 : 0u) + lj) * R;
+    const uint32_t escbase = h * (uint32_t)p.slot_stride + (h ? wofs1 : wofs0);  // this half's escape area in rslot
+    // Escaped exponents go to the slot's escape area, last value first (a
+    // value's byte lands at the count of escapes after it); the compaction
+    // writes them after the words in value order.
+    auto put_escapes = [&](uint64_t escm, uint32_t ex) __attribute__((always_inline)) {
+        const uint32_t elo = __builtin_popcount((uint32_t)escm), ehi = __builtin_popcount((uint32_t)(escm >> 32));
+        const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(escm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)escm, 0u));
+        const uint32_t above = (h ? ehi : elo) - (below - (h ? elo : 0u)) - 1u;
+        const uint32_t pos = (h ? nesc1 : nesc0) + above;
+        bst8(rslot, (escm >> lane) & 1u ? escbase + pos : kOutOfRange, ex);
+        nesc0 += elo;
+        nesc1 += ehi;
+    };
     const uint32_t nblk = (max(T0, T1) + 7) / 8;
     const uint32_t hsel = h ? 0xFFFFFFFFu : 0u;
+    uint64_t escany = 0;  // FAST steps (sampled tables): lanes whose value escaped, not yet placed
     // One step; CAREFUL steps rebuild the lane masks and check the room
     // (a ragged chunk end, or words close to the RAW size), the others use
     // the block's loop-invariant mask.
@@ -757,12 +828,21 @@ __global__ __launch_bounds__(64) void k_encode(EncParams p) {
         uint64_t m = lanes_lt(te.x & 0xFFFFu, x >> 20) & act;  // x >= f * 2^20
         uint32_t lo = (uint32_t)m, hi = (uint32_t)(m >> 32);
         uint32_t clo = __builtin_popcount(lo), chi = __builtin_popcount(hi);
+        uint64_t escm = 0;
         if (careful) {
-            if (alive0 && (end0 - r0) + clo > wcap0) alive0 = false;
-            if (alive1 && (end1 - r1) + chi > wcap1) alive1 = false;
+            if (S) {
+                escm = lanes_eq(te.y, kEscSlot) & act;
+                const uint32_t elo = __builtin_popcount((uint32_t)escm), ehi = __builtin_popcount((uint32_t)(escm >> 32));
+                if (alive0 && 2 * ((end0 - r0) + clo) + nesc0 + elo > room0) alive0 = false;
+                if (alive1 && 2 * ((end1 - r1) + chi) + nesc1 + ehi > room1) alive1 = false;
+            } else {
+                if (alive0 && (end0 - r0) + clo > wcap0) alive0 = false;
+                if (alive1 && (end1 - r1) + chi > wcap1) alive1 = false;
+            }
             const uint64_t am = (alive0 ? 0xFFFFFFFFull : 0ull) | (alive1 ? kHighHalf : 0ull);
             m &= am;
             act &= am;
+            escm &= am;
             lo = (uint32_t)m;
             hi = (uint32_t)(m >> 32);
             clo = __builtin_popcount(lo);
@@ -785,13 +865,43 @@ __global__ __launch_bounds__(64) void k_encode(EncParams p) {
         // steps every lane of a live half codes a value, and a stopped
         // half's state is never used (its chunk is stored RAW).
         x = careful ? vsel(act, x, xe) : xe;
+        if (S) {
+            if (R == 1) bst8(rsm2, smo2 + t * 32 * R, raw_of<DT>(v));
+            if (R == 3) {
+                const uint32_t smv = raw_of<DT>(v);
+                bst16(rsm2, smo2 + t * 32 * R, smv);
+                bst8(rsm2, smo2 + t * 32 * R + 2, smv >> 16);
+            }
+            if (careful) {
+                if (escm) put_escapes(escm, ex);
+            } else {
+                escany |= lanes_eq(te.y, kEscSlot);
+            }
+        }
     };
     // a block codes at most 256 values, so at most 256 words, per half: a
     // FAST block needs no per-step checks
+    // (sampled tables: and at most 256 escapes)
     auto block_fast = [&](int32_t b) __attribute__((always_inline)) {
         const uint32_t tend = ((uint32_t)b + 1) * 256;
+        if (S)
+            return (!alive0 || (vals0 >= tend && 2 * ((end0 - r0) + 256) + nesc0 + 256 <= room0)) &&
+                   (!alive1 || (vals1 >= tend && 2 * ((end1 - r1) + 256) + nesc1 + 256 <= room1));
         return (!alive0 || (vals0 >= tend && (end0 - r0) + 256 <= wcap0)) &&
                (!alive1 || (vals1 >= tend && (end1 - r1) + 256 <= wcap1));
+    };
+    // Escapes of a FAST block, placed after the block (its values are still in
+    // registers and nothing is in flight): the block's steps again, last first,
+    // from the table's c0 column alone.
+    auto block_escapes = [&](const uint32_t(&V)[8]) __attribute__((always_inline)) {
+        const uint64_t act = (alive0 ? 0xFFFFFFFFull : 0ull) | (alive1 ? kHighHalf : 0ull);
+        for (int k = 7; k >= 0; --k) {
+            uint32_t ex;
+            asm("v_bfe_u32 %0, %1, %2, 8" : "=v"(ex) : "v"(V[k]), "i"(Fmt<DT>::SYM));
+            const uint32_t cy = *reinterpret_cast<const uint32_t *>(reinterpret_cast<const uint8_t *>(tab) + (ex << 4) + 4);
+            const uint64_t escm = lanes_eq(cy, kEscSlot) & act;
+            if (escm) put_escapes(escm, ex);
+        }
     };
     auto fast_block = [&](int32_t b, const uint32_t(&V)[8]) __attribute__((always_inline)) {
         const uint64_t act = (alive0 ? 0xFFFFFFFFull : 0ull) | (alive1 ? kHighHalf : 0ull);
@@ -821,9 +931,11 @@ __global__ __launch_bounds__(64) void k_encode(EncParams p) {
                 asm volatile("buffer_load_dword %0, %1, %2, 0 offen offset:%3" : "=v"(V[k]) : "v"(o), "s"(rin), "i"(k * 32 * EB));
         }
     };
-#define UZIP_WAIT_BLOCK(N, V)                                                                                     \
-    asm volatile("s_waitcnt vmcnt(" #N ")" : "+v"(V[0]), "+v"(V[1]), "+v"(V[2]), "+v"(V[3]), "+v"(V[4]), "+v"(V[5]), \
-                 "+v"(V[6]), "+v"(V[7]))
+    // stores of a FAST block: its words, and with sampled tables its sign+mantissa bytes
+    constexpr uint32_t kBlockStores = 8 + (S ? 8 * (R == 3 ? 2 : R) : 0);
+#define UZIP_WAIT_BLOCK(N, V)                                                                                         \
+    asm volatile("s_waitcnt vmcnt(%8)" : "+v"(V[0]), "+v"(V[1]), "+v"(V[2]), "+v"(V[3]), "+v"(V[4]), "+v"(V[5]), \
+                 "+v"(V[6]), "+v"(V[7]) : "i"(N))
     for (int32_t b = (int32_t)nblk - 1; b >= 0;) {
         if (!block_fast(b)) {
             const uint32_t o = in0 + ((uint32_t)b * 8 * 32 + lj) * EB;
@@ -842,11 +954,19 @@ __global__ __launch_bounds__(64) void k_encode(EncParams p) {
         for (;;) {
             asm_load_block(b - 1, VB);
             fast_block(b, VA);
-            UZIP_WAIT_BLOCK(8, VB);
+            UZIP_WAIT_BLOCK(kBlockStores, VB);
+            if (S && escany) {
+                escany = 0;
+                block_escapes(VA);
+            }
             if (--b < 0 || !block_fast(b)) break;
             asm_load_block(b - 1, VA);
             fast_block(b, VB);
-            UZIP_WAIT_BLOCK(8, VA);
+            UZIP_WAIT_BLOCK(kBlockStores, VA);
+            if (S && escany) {
+                escany = 0;
+                block_escapes(VB);
+            }
             if (--b < 0 || !block_fast(b)) break;
         }
     }
@@ -856,14 +976,19 @@ __global__ __launch_bounds__(64) void k_encode(EncParams p) {
     // end); a RAW record gets its header only: k_compact takes its exponents
     // from the input ----
     const uint32_t nw = h ? end1 - r1 : end0 - r0;  // words emitted
+    const uint32_t ne = h ? nesc1 : nesc0;          // values escaped (sampled tables)
     const bool alive = h ? alive1 : alive0;
     const uint32_t raw_i = h ? raw1 : raw0;
-    const uint32_t rans_bytes = (uint32_t)align16(words_offset(nsym) + 2ull * nw);
+    const uint32_t rans_bytes = (uint32_t)(S ? align16(words_offset_sampled(nsym) + 2ull * nw + ne)
+                                             : align16(words_offset(nsym) + 2ull * nw));
     if (valid) {
         const bool rans = alive && rans_bytes < raw_i;  // ties go RAW
-        if (rans) gstore<uint32_t>(slot + states_offset(nsym) + 4 * lj, x);
+        if (rans) gstore<uint32_t>(slot + (S ? states_offset_sampled(nsym) : states_offset(nsym)) + 4 * lj, x);
         if (lj == 0) {
-            gstore<uint4>(slot, rans ? make_uint4(nsym << 16, nw, ni, rans_bytes) : make_uint4(1u, 0u, ni, raw_i));
+            if (S && rans) gstore<uint32_t>(slot + esc_count_offset(nsym), ne);
+            // record mode 0 (full table) or 2 (sampled table), else 1 (RAW)
+            gstore<uint4>(slot, rans ? make_uint4((S ? 2u : 0u) | (nsym << 16), nw, ni, rans_bytes)
+                                     : make_uint4(1u, 0u, ni, raw_i));
             gstore<uint32_t>(p.rec_sizes + g, rans ? rans_bytes : raw_i);
         }
     }
@@ -1155,11 +1280,22 @@ __global__ __launch_bounds__(128 * kCompactPairs) void k_compact(EncParams p) {
     const rsrc_t rslot = make_rsrc(p.slots + (g0 + r) * p.slot_stride, stride);
     const uint4 hd = bld128(rslot, 0);
     const uint32_t mode = uniform_u32(hd.x) & 0xFFu, nsym = uniform_u32(hd.x) >> 16, nw = uniform_u32(hd.y);
-    if (mode == 0) {
-        // header, bitmap, frequencies, pad, states, then the words
-        const uint32_t wofs = (uint32_t)words_offset(nsym);
+    if (mode == 0 || mode == 2) {
+        // header, bitmap, frequencies, pad, (escape count,) states, then the
+        // words; a sampled-table record ends with its escaped exponents
+        const uint32_t wofs = (uint32_t)(mode == 2 ? words_offset_sampled(nsym) : words_offset(nsym));
         for (uint32_t k = lane; k < wofs / 4; k += 64) gstore<uint32_t>(rec + 4 * k, bld32(rslot, 4 * k));
         copy_words(rslot, rec, wofs, size, 2 * nw, (uint32_t)raw_record_bytes(ni) - 2 * nw, lane);
+        if (mode == 2) {
+            const uint32_t ne = uniform_u32(bld32(rslot, (uint32_t)esc_count_offset(nsym)));
+            if (ne > 0) {
+                // the escape area holds them last value first, from byte wofs of the
+                // slot; the zero padding the word copy wrote there must land first
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                for (uint32_t j = lane; j < ne; j += 64)
+                    gstore<uint8_t>(rec + wofs + 2 * nw + j, (uint8_t)bld8(rslot, wofs + ne - 1 - j));
+            }
+        }
     } else {
         const rsrc_t rin = make_rsrc(d.in + (c0 + r) * ce * EB, ni * EB);
         if (lane < 4) gstore<uint32_t>(rec + 4 * lane, bld32(rslot, 4 * lane));
@@ -1174,7 +1310,8 @@ __global__ __launch_bounds__(128 * kCompactPairs) void k_compact(EncParams p) {
             gstore<uint64_t>(d.out_size, total);
         }
         if (lane < 16)
-            gstore<uint32_t>(out + 4 * lane, header_word(lane, p.dtype, p.chunk_elems, n, chunks, d.sm_off, exp_off, total));
+            gstore<uint32_t>(out + 4 * lane,
+                             header_word(lane, p.dtype, p.chunk_elems, n, chunks, d.sm_off, exp_off, total, p.sampled));
         const uint64_t gap0 = kHeaderBytes + 8 * (chunks + 1);
         for (uint64_t k = gap0 + lane; k < d.sm_off; k += 64) gstore<uint8_t>(out + k, 0);
         const uint64_t gap1 = d.sm_off + uint64_t(R) * n;
@@ -1185,8 +1322,9 @@ __global__ __launch_bounds__(128 * kCompactPairs) void k_compact(EncParams p) {
 // ---------------------------------------------------------------------------
 // scans
 // ---------------------------------------------------------------------------
-// exclusive scan of n values into out[0..n] (out[n] = total); in may equal out
-__global__ __launch_bounds__(1024) void k_scan_u64(const uint64_t *in, uint64_t *out, uint64_t n) {
+// exclusive scan of n values into out[0..n] (out[n] = total) by one workgroup
+// of 1024 threads; in may equal out
+__device__ inline void block_scan_u64(const uint64_t *in, uint64_t *out, uint64_t n) {
     __shared__ uint64_t s[1024];
     uint64_t carry = 0;
     for (uint64_t base = 0; base < n; base += 1024) {
@@ -1207,6 +1345,22 @@ __global__ __launch_bounds__(1024) void k_scan_u64(const uint64_t *in, uint64_t 
     if (threadIdx.x == 0) gstore<uint64_t>(out + n, carry);
 }
 
+// Batched decompression, after validation (one workgroup): the exclusive scan
+// of the buffers' chunk-pair counts, in place, and which decoders have work
+// (bit 0: a valid buffer with full tables, bit 1: one with sampled tables).
+__global__ __launch_bounds__(1024) void k_dec_scan(DecParams p) {
+    __shared__ uint32_t s_kinds;
+    if (threadIdx.x == 0) s_kinds = 0;
+    __syncthreads();
+    uint32_t kinds = 0;
+    for (uint32_t b = threadIdx.x; b < p.nbuf; b += 1024)
+        if (gload<uint32_t>(p.status + b) == 0) kinds |= (gload<uint64_t>(&p.info[b].flags) & 1u) ? 2u : 1u;
+    if (kinds) atomicOr(&s_kinds, kinds);
+    __syncthreads();
+    if (threadIdx.x == 0) gstore<uint32_t>(p.kinds, s_kinds);
+    block_scan_u64(p.pair_first, p.pair_first, p.nbuf);
+}
+
 // Before the encoder: zero the look-back words and the ticket counter (a fill
 // kernel rather than a memset, so the call stays valid inside a captured
 // graph), and write the 80-byte buffer of every empty input (N = 0).
@@ -1218,7 +1372,7 @@ __global__ __launch_bounds__(256) void k_prepare(EncParams p) {
         const EncDesc d = p.nbuf == 1 ? p.single : load_enc_desc(p.descs + i);
         if (d.n == 0) {
             for (uint32_t k = 0; k < 16; ++k)
-                gstore<uint32_t>(d.out + 4 * k, header_word(k, p.dtype, p.chunk_elems, 0, 0, 80, 80, 80));
+                gstore<uint32_t>(d.out + 4 * k, header_word(k, p.dtype, p.chunk_elems, 0, 0, 80, 80, 80, p.sampled));
             gstore<uint64_t>(d.out + kHeaderBytes, 0);
             gstore<uint64_t>(d.out + kHeaderBytes + 8, 0);
             gstore<uint64_t>(d.out_size, 80);
@@ -1234,7 +1388,7 @@ __global__ void k_dec_validate(DecParams p) {
     if (b >= p.nbuf) return;
     const DecDesc d = p.nbuf == 1 ? p.single : load_dec_desc(p.descs + b);
     bool ok = d.in_bytes >= kHeaderBytes;
-    bool sampled = false;  // flag bit 0: tables from samples (record mode 2), not decoded here
+    bool sampled = false;  // flag bit 0: tables from samples (record mode 2)
     DecInfo inf = {};
     if (ok) {
         const uint4 h0 = gload<uint4>(d.in), h1 = gload<uint4>(d.in + 16);
@@ -1245,8 +1399,7 @@ __global__ void k_dec_validate(DecParams p) {
         const uint32_t flags = h0.z >> 16;
         ok = h0.x == kMagic && (h0.y & 0xFFFFu) == kVersion && ((h0.y >> 16) & 0xFFu) == (uint32_t)p.dtype &&
              (h0.y >> 24) == kProbBits && (h0.z & 0xFFu) == kLanes && ((h0.z >> 8) & 0xFFu) == r && flags <= 1;
-        sampled = ok && flags == 1;
-        ok = ok && !sampled;
+        sampled = flags == 1;
         const uint64_t n = uint64_t(h1.x) | (uint64_t(h1.y) << 32);
         const uint64_t C = uint64_t(h1.z) | (uint64_t(h1.w) << 32);
         const uint64_t ce = h0.w;
@@ -1271,16 +1424,18 @@ __global__ void k_dec_validate(DecParams p) {
             inf.sm_off = sm_off;
             inf.exp_off = exp_off;
             inf.total = total;
+            inf.flags = flags;
         }
     }
     if (!ok) inf.chunks = 0;
     const uint4 *iv = reinterpret_cast<const uint4 *>(&inf);
     for (int k = 0; k < 4; ++k) gstore<uint4>(reinterpret_cast<uint4 *>(p.info + b) + k, iv[k]);
-    gstore<uint32_t>(p.status + b, ok ? 0u : sampled ? (uint32_t)UZIP_ERR_UNSUPPORTED : 3u);
+    gstore<uint32_t>(p.status + b, ok ? 0u : 3u);
     const uint64_t pairs = (inf.chunks + 1) / 2;
     if (p.nbuf == 1) {
         gstore<uint64_t>(p.pair_first, 0);
         gstore<uint64_t>(p.pair_first + 1, pairs);
+        gstore<uint32_t>(p.kinds, ok ? (sampled ? 2u : 1u) : 0u);
     } else {
         gstore<uint64_t>(p.pair_first + b, pairs);  // counts; scanned in place afterwards
     }
@@ -1355,7 +1510,10 @@ __device__ inline void store_unit(rsrc_t r, uint32_t off, const uint4 &E, const 
     }
 }
 
-template <int DT>
+// S: the variant for frames with sampled tables (record mode 2).  Both are
+// launched for every call; each leaves at once unless a valid buffer of its
+// kind is present, and skips the buffers of the other kind.
+template <int DT, bool S>
 __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
     constexpr uint32_t EB = Fmt<DT>::EB;
     constexpr uint32_t R = Fmt<DT>::R;
@@ -1380,6 +1538,7 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
 
     const uint32_t lane = threadIdx.x;
     const uint32_t h = lane >> 5, lj = lane & 31;
+    if ((uniform_u32(gload<uint32_t>(p.kinds)) & (S ? 2u : 1u)) == 0) return;
     const uint64_t PT = uniform_u64(gload<uint64_t>(p.pair_first + p.nbuf));
 
     for (uint64_t q = blockIdx.x; q < PT; q += gridDim.x) {
@@ -1387,6 +1546,7 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
         const uint32_t b = p.nbuf == 1 ? 0u : uniform_u32(find_dec_buffer(p.pair_first, p.nbuf, q));
         const DecDesc d = p.nbuf == 1 ? p.single : load_dec_desc(p.descs + b);
         if (uniform_u32(gload<uint32_t>(p.status + b)) != 0) continue;
+        if (((uniform_u32((uint32_t)gload<uint64_t>(&p.info[b].flags)) & 1u) != 0) != S) continue;
         const uint64_t ce = uniform_u64(gload<uint64_t>(&p.info[b].chunk_elems));
         const uint64_t C = uniform_u64(gload<uint64_t>(&p.info[b].chunks));
         const uint64_t sm_off = uniform_u64(gload<uint64_t>(&p.info[b].sm_off));
@@ -1417,18 +1577,27 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
         const uint32_t ni = h ? vals1 : vals0;
         const uint32_t rel = h ? (uint32_t)(a1 - a0) : 0u;  // record start inside rrec
         const uint32_t len = h ? (uint32_t)(a2 - a1) : (uint32_t)(a1 - a0);
-        uint32_t mode = 1, nsym = 0, nw = 0;
+        uint32_t mode = 1, nsym = 0, nw = 0, nesc = 0;
+        // coded records: mode 0 in frames with full tables, mode 2 with sampled ones
+        constexpr uint32_t kCoded = S ? 2u : 0u;
         ok = ok && len >= 16;
         {
             const uint4 rh = bld128(rrec, ok ? rel : kOutOfRange);
             mode = rh.x & 0xFFu;
             nsym = rh.x >> 16;
             nw = rh.y;
-            ok = ok && mode <= 1 && rh.z == ni && rh.w == len;
+            ok = ok && (mode == 1 || mode == kCoded) && rh.z == ni && rh.w == len;
             if (ok && mode == 1) ok = nsym == 0 && nw == 0 && len == raw_record_bytes(ni);
-            if (ok && mode == 0) ok = nsym >= 1 && nsym <= 256 && len == align16(words_offset(nsym) + 2ull * nw);
+            if (ok && mode == kCoded) ok = nsym >= 1 && nsym <= 256;
+            if (S && ok && mode == kCoded) {
+                ok = len >= words_offset_sampled(nsym);
+                nesc = bld32(rrec, ok ? rel + (uint32_t)esc_count_offset(nsym) : kOutOfRange);
+                ok = ok && nesc <= ni && len == align16(words_offset_sampled(nsym) + 2ull * nw + nesc);
+            } else if (ok && mode == kCoded) {
+                ok = len == align16(words_offset(nsym) + 2ull * nw);
+            }
         }
-        const bool coded = ok && mode == 0;
+        const bool coded = ok && mode == kCoded;
 
         // ---- table: presence bitmap byte lj covers symbols 8lj..8lj+7 (V7) ----
         const uint32_t pb = bld8(rrec, coded ? rel + kRecHeaderBytes + lj : kOutOfRange);
@@ -1454,8 +1623,9 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
         const uint32_t cbase = half_excl_scan(lsum, lj);
         const uint32_t seen = half_sum(np);
         const bool fbad = half_mask(__ballot(!fok), h) != 0;
-        if (coded) ok = seen == nsym && !fbad && tot == kTableSize;
-        const bool coded_ok = ok && mode == 0;
+        // (a sampled table leaves its last slot to the escape symbol)
+        if (coded) ok = seen == nsym && !fbad && tot == kTableSize - (S ? 1u : 0u);
+        const bool coded_ok = ok && mode == kCoded;
         if (coded_ok) {
             uint32_t k2 = pre;
 #pragma unroll
@@ -1463,9 +1633,12 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
                 if (fk[k]) s_rk[h][k2++] = (kTableSize - fk[k]) | ((lj * 8 + k) << 12) | ((cbase + cpre[k]) << 20);
             }
         }
+        // the escape symbol: rank nsym, f = 1, slot 4095 (no owner when all 256
+        // symbols are sampled: a stream reaching it is corrupt, found below)
+        if (S && coded_ok && lj == 0 && nsym < 256) s_rk[h][nsym] = (kTableSize - 1u) | (kEscSlot << 20);
         __syncthreads();
         if (coded_ok) {
-            for (uint32_t m = 0; m < nsym; ++m) {
+            for (uint32_t m = 0; m < nsym + (S && nsym < 256 ? 1u : 0u); ++m) {
                 const uint32_t em = s_rk[h][m];
                 const uint32_t fs = kTableSize - (em & 0xFFFu), c0s = em >> 20;
                 if (kDirect) {
@@ -1478,11 +1651,12 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
         __syncthreads();
 
         // ---- states (V8) ----
-        uint32_t x = bld32(rrec, coded_ok ? rel + (uint32_t)states_offset(nsym) + 4 * lj : kOutOfRange);
+        uint32_t x = bld32(rrec, coded_ok ? rel + (uint32_t)(S ? states_offset_sampled(nsym) : states_offset(nsym)) + 4 * lj
+                                          : kOutOfRange);
         if (!coded_ok) x = kStateLow;
         const bool sbad = half_mask(__ballot(coded_ok && x < kStateLow), h) != 0;
         ok = ok && !sbad;
-        const bool rans_run = ok && mode == 0;
+        const bool rans_run = ok && mode == kCoded;
         const bool raw_run = ok && mode == 1;
 
         // ---- rANS decode (V9: end state L on every lane, every word consumed) ----
@@ -1530,7 +1704,7 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
         // of the last three steps (scalar) and then reload synchronously;
         // fp32, whose waves are too few to hide a branch, also loads the pair
         // 64 words further (NB), which is the right one exactly in that case.
-        const uint32_t wstart = rel + (uint32_t)words_offset(nsym);  // byte offset of word 0
+        const uint32_t wstart = rel + (uint32_t)(S ? words_offset_sampled(nsym) : words_offset(nsym));  // byte offset of word 0
         uint32_t P = bld32(rrec, wstart + 4 * lj);                    // words 2lj, 2lj + 1
         uint32_t lim = 32 + 32 * (lj >> 4);                           // end of the lane's block
         const uint32_t rbase = wstart + 64 + 4 * (lj & 15u);          // byte offset of its next pair = 2 lim + rbase
@@ -1546,6 +1720,35 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
         const uint8_t *s_symf = &s_sym[0][0];
         const uint32_t *s_rkf = &s_rk[0][0];
         const uint32_t *s_slotf = &s_slot[0][0];
+        // Escapes (sampled tables): the value whose slot is 4095 takes its
+        // exponent from the record's escape list, in value order; a half's
+        // first 128 escaped bytes are held four to a lane (fetched by
+        // bpermute), later ones are loaded.  The byte must not be a sampled
+        // symbol, and the list must be used exactly.
+        const uint32_t escat = rel + (uint32_t)words_offset_sampled(nsym) + 2 * nw;  // byte offset of the list
+        uint32_t escw = 0;
+        if (S) {
+            const uint32_t ea = (escat & ~3u) + 4 * lj;
+            escw = __builtin_amdgcn_alignbyte(bld32(rrec, rans_run ? ea + 4 : kOutOfRange),
+                                              bld32(rrec, rans_run ? ea : kOutOfRange), escat & 3u);
+        }
+        const uint32_t escaddr = kEscSlot | hsym;
+        uint32_t escv = 0;  // escapes used by this half
+        bool escbad = false;
+        auto escape_entry = [&](uint64_t escm, uint32_t em) __attribute__((always_inline)) {
+            const uint32_t elo = __builtin_popcount((uint32_t)escm), ehi = __builtin_popcount((uint32_t)(escm >> 32));
+            const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(escm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)escm, 0u));
+            const uint32_t idx = escv + below - (h ? elo : 0u);
+            const bool mine = (escm >> lane) & 1u;
+            const uint32_t ew = (uint32_t)__builtin_amdgcn_ds_bpermute((int)((((idx >> 2) & 31u) | (h << 5)) << 2), (int)escw);
+            uint32_t e = (ew >> (8 * (idx & 3u))) & 0xFFu;
+            if (idx >= 128) e = bld8(rrec, mine && idx < nesc ? escat + idx : kOutOfRange);
+            // the bitmap byte of e's symbol group is held by lane e >> 3 of the half
+            const uint32_t pbe = (uint32_t)__builtin_amdgcn_ds_bpermute((int)(((e >> 3) | (h << 5)) << 2), (int)pb);
+            escbad = escbad || (mine && (idx >= nesc || nsym == 256 || ((pbe >> (e & 7u)) & 1u)));
+            escv += h ? ehi : elo;
+            return mine ? (em & ~0xFF000u) | (e << 12) : em;
+        };
         // One step of both half-waves.  act = lanes holding a value this step
         // (TAIL steps only: in the main loop every lane of a running half
         // holds one, and lanes of a half that is not running never reach the
@@ -1557,8 +1760,12 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
         auto step = [&](uint32_t t, uint64_t act, bool tail, uint32_t sp, int par, bool store) __attribute__((always_inline)) {
             uint32_t slot_addr;  // (x & 4095) | this half's row: the index in s_sym / s_slot
             asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(slot_addr) : "v"(x), "s"(kTableSize - 1), "v"(hsym));
-            const uint32_t em = kDirect ? s_slotf[slot_addr] : s_rkf[s_symf[slot_addr] | hrk];
+            uint32_t em = kDirect ? s_slotf[slot_addr] : s_rkf[s_symf[slot_addr] | hrk];
             const uint32_t xd = x - (__umul24(em & 0xFFFu, x >> kProbBits) + (em >> 20));
+            if (S) {  // (only the symbol bits of em are used below)
+                const uint64_t escm = lanes_eq(slot_addr, escaddr) & act;
+                if (escm) em = escape_entry(escm, em);
+            }
             // (the and with act also puts the mask in registers written by the
             // scalar unit: inline asm below reads it, and the hardware needs
             // spacing between a vector compare writing scalar registers and a
@@ -1709,7 +1916,8 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
                 step(tt, act, true, DT == 1 ? __umul24(smt[u], 0x101u) : smt[u], u & 3, true);  // (bf16: sign byte in bits 8-15 too)
             }
         }
-        const bool endbad = half_mask(__ballot(rans_run && (x != kStateLow || offv != nw)), h) != 0;
+        const bool endbad =
+            half_mask(__ballot(rans_run && (x != kStateLow || offv != nw || (S && (escbad || escv != nesc)))), h) != 0;
         ok = ok && !endbad;
         // ---- chunks stored RAW: exponent bytes straight from the record ----
         if (raw_run) {
@@ -1719,18 +1927,18 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
             const uint32_t nu = ni / 16;
             constexpr uint32_t U = 4, RS = R > 0 ? R : 1;
             for (uint32_t u0 = lj; u0 < nu; u0 += 32 * U) {
-                uint4 E[U], S[U][RS];
+                uint4 E[U], SV[U][RS];
 #pragma unroll
                 for (uint32_t k = 0; k < U; ++k) {
                     const uint32_t u = u0 + 32 * k;
                     E[k] = bld128(rrec, u < nu ? eo + 16 * u : kOutOfRange);
 #pragma unroll
-                    for (uint32_t r = 0; r < R; ++r) S[k][r] = bld128(rsm, u < nu ? sb + 16 * R * u + 16 * r : kOutOfRange);
+                    for (uint32_t r = 0; r < R; ++r) SV[k][r] = bld128(rsm, u < nu ? sb + 16 * R * u + 16 * r : kOutOfRange);
                 }
 #pragma unroll
                 for (uint32_t k = 0; k < U; ++k) {
                     const uint32_t u = u0 + 32 * k;
-                    store_unit<DT>(rout, u < nu ? ob + 16 * EB * u : kOutOfRange, E[k], S[k]);
+                    store_unit<DT>(rout, u < nu ? ob + 16 * EB * u : kOutOfRange, E[k], SV[k]);
                 }
             }
             for (uint32_t i = 16 * nu + lj; i < ni; i += 32) {  // the chunk's last values
@@ -1765,11 +1973,16 @@ hipError_t launch_compress(const EncParams &ep, hipStream_t stream) {
     if (ep.total_pairs > 0) {
         const dim3 grid((uint32_t)ep.total_pairs);
         if (g_profile.start) (void)hipEventRecord(g_profile.start, stream);
-        switch (kernel_format(ep.dtype)) {
-        case 1: k_encode<1><<<grid, dim3(64), 0, stream>>>(ep); break;
-        case 2: k_encode<2><<<grid, dim3(64), 0, stream>>>(ep); break;
-        case 3: k_encode<3><<<grid, dim3(64), 0, stream>>>(ep); break;
-        default: k_encode<4><<<grid, dim3(64), 0, stream>>>(ep); break;
+        const int kf = kernel_format(ep.dtype) + (ep.sampled ? 8 : 0);
+        switch (kf) {
+        case 1: k_encode<1, false><<<grid, dim3(64), 0, stream>>>(ep); break;
+        case 2: k_encode<2, false><<<grid, dim3(64), 0, stream>>>(ep); break;
+        case 3: k_encode<3, false><<<grid, dim3(64), 0, stream>>>(ep); break;
+        case 4: k_encode<4, false><<<grid, dim3(64), 0, stream>>>(ep); break;
+        case 9: k_encode<1, true><<<grid, dim3(64), 0, stream>>>(ep); break;
+        case 10: k_encode<2, true><<<grid, dim3(64), 0, stream>>>(ep); break;
+        case 11: k_encode<3, true><<<grid, dim3(64), 0, stream>>>(ep); break;
+        default: k_encode<4, true><<<grid, dim3(64), 0, stream>>>(ep); break;
         }
         if (g_profile.stop) (void)hipEventRecord(g_profile.stop, stream);
         if (ep.plans != nullptr) {
@@ -1795,16 +2008,24 @@ hipError_t launch_compress(const EncParams &ep, hipStream_t stream) {
 hipError_t launch_decompress(const DecParams &vp, const DecodeParams &dp, int dtype, uint64_t max_chunks,
                              hipStream_t stream) {
     k_dec_validate<<<(vp.nbuf + 255) / 256, 256, 0, stream>>>(vp);
-    if (vp.nbuf > 1) k_scan_u64<<<1, 1024, 0, stream>>>(vp.pair_first, vp.pair_first, vp.nbuf);
+    if (vp.nbuf > 1) k_dec_scan<<<1, 1024, 0, stream>>>(vp);
     if (max_chunks > 0) {
         const uint64_t pairs = (max_chunks + 1) / 2 + vp.nbuf;  // upper bound of the chunk pairs
         const uint64_t grid = pairs < 8192 ? pairs : 8192;
         if (g_profile.start) (void)hipEventRecord(g_profile.start, stream);
+        // full-table frames, then sampled-table frames (each kernel leaves at
+        // once when the call holds no valid buffer of its kind)
         switch (kernel_format(dtype)) {
-        case 1: k_decode<1><<<dim3((uint32_t)grid), dim3(64), 0, stream>>>(dp); break;
-        case 2: k_decode<2><<<dim3((uint32_t)grid), dim3(64), 0, stream>>>(dp); break;
-        case 3: k_decode<3><<<dim3((uint32_t)grid), dim3(64), 0, stream>>>(dp); break;
-        default: k_decode<4><<<dim3((uint32_t)grid), dim3(64), 0, stream>>>(dp); break;
+        case 1: k_decode<1, false><<<dim3((uint32_t)grid), dim3(64), 0, stream>>>(dp); break;
+        case 2: k_decode<2, false><<<dim3((uint32_t)grid), dim3(64), 0, stream>>>(dp); break;
+        case 3: k_decode<3, false><<<dim3((uint32_t)grid), dim3(64), 0, stream>>>(dp); break;
+        default: k_decode<4, false><<<dim3((uint32_t)grid), dim3(64), 0, stream>>>(dp); break;
+        }
+        switch (kernel_format(dtype)) {
+        case 1: k_decode<1, true><<<dim3((uint32_t)grid), dim3(64), 0, stream>>>(dp); break;
+        case 2: k_decode<2, true><<<dim3((uint32_t)grid), dim3(64), 0, stream>>>(dp); break;
+        case 3: k_decode<3, true><<<dim3((uint32_t)grid), dim3(64), 0, stream>>>(dp); break;
+        default: k_decode<4, true><<<dim3((uint32_t)grid), dim3(64), 0, stream>>>(dp); break;
         }
         if (g_profile.stop) (void)hipEventRecord(g_profile.stop, stream);
     }

@@ -23,6 +23,7 @@ struct EncParams {
     uint64_t *flags;        // one look-back word per chunk pair (zeroed before compaction)
     uint32_t *ticket;       // chunk-pair ticket counter of the compaction (zeroed before it)
     int dtype;
+    uint32_t sampled;       // 1: tables from each chunk's sample (header flag bit 0, record mode 2)
     uzip_plan *plans;       // per-call arbitration: one plan per buffer (null: every buffer is coded)
     uzip_policy policy;     // the cost model's inputs when plans is set
 };
@@ -35,6 +36,7 @@ struct DecParams {
     DecInfo *info;
     uint64_t *pair_first;  // nbuf + 1 entries: exclusive prefix of the chunk-pair counts
     uint32_t *status;
+    uint32_t *kinds;       // written after validation: which decoders have work (see DecodeParams)
 };
 
 struct DecodeParams {
@@ -44,6 +46,7 @@ struct DecodeParams {
     const DecInfo *info;
     const uint64_t *pair_first;
     uint32_t *status;
+    const uint32_t *kinds;  // bit 0: some valid buffer has full tables, bit 1: some has sampled ones
 };
 
 // events recorded around the main coding kernel (benchmark instrumentation)

@@ -262,14 +262,13 @@ def test_batched_buffers_spanning_many_offset_tiles(chunk_bytes):
 
 
 def test_header_flags():
-    """Flag bit 0 (tables from samples, record mode 2) is a frame this decoder
-    reports as unsupported; any other flag is corrupt; the oracle reads both
-    kinds of valid frame."""
+    """Flag bit 0 (tables from samples, record mode 2) is a frame the decoder
+    reads like the oracle; any other flag is corrupt."""
     bits = workloads.bits_numpy(workloads.gradient_bucket(100_000, seed=13, special_frac=1e-3))
     sampled = orc.compress_sampled(orc.BF16, bits)
     assert orc.decompress(sampled, orc.BF16, bits.size)[0] == orc.OK
-    _, st = gpu_decompress(sampled, torch.bfloat16, bits.size)
-    assert st == uz.UZIP_ERR_UNSUPPORTED
+    out, st = gpu_decompress(sampled, torch.bfloat16, bits.size)
+    assert st == 0 and np.array_equal(out.view(torch.int16).cpu().numpy().view(np.uint16), bits)
     full = orc.compress(orc.BF16, bits)
     bad = full.copy()
     bad[10] = 2

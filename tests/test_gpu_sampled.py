@@ -1,0 +1,213 @@
+"""GPU parity for frames with sampled tables (header flag bit 0, record mode 2).
+
+Each chunk's table comes from a spread eighth of the chunk (UCCL-Zip Sec. 3,
+Figure 5: every block builds its own table from a sample of its data); a value
+whose exponent the sample missed is coded as the escape symbol and its exponent
+goes to the record's escape list.  uzip_compress_sampled must write the
+oracle's sampled frame byte for byte (tolerance 0), and uzip_decompress must
+restore every bit of it and report every corruption the oracle reports.
+"""
+import numpy as np
+import pytest
+import torch
+
+import lossless_compression_float_amd as uz
+import oracle as orc
+import workloads
+from uzip_testlib import parse_buffer
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+_ORC = {torch.bfloat16: orc.BF16, torch.float32: orc.FP32, torch.float16: orc.FP16,
+        torch.float8_e4m3fn: orc.FP8_E4M3, torch.float8_e5m2: orc.FP8_E5M2}
+_INT = {1: torch.uint8, 2: torch.int16, 4: torch.int32}
+
+
+def _tensor(bits: np.ndarray, tdtype: torch.dtype) -> torch.Tensor:
+    view = {np.uint16: np.int16, np.uint32: np.int32, np.uint8: np.uint8}[bits.dtype.type]
+    return torch.from_numpy(bits.view(view).copy()).view(tdtype).to(DEV)
+
+
+def _decompress(buf: np.ndarray, tdtype: torch.dtype, n: int):
+    b = torch.from_numpy(buf.copy()).to(DEV)
+    out, st = uz.decompress(b, tdtype, n, in_bytes=buf.size)
+    torch.cuda.synchronize()
+    return out, int(st.item())
+
+
+def check_sampled(bits: np.ndarray, tdtype: torch.dtype, chunk_bytes: int = 0) -> np.ndarray:
+    t = _tensor(bits, tdtype)
+    buf, size = uz.compress(t, chunk_bytes, sampled=True)
+    torch.cuda.synchronize()
+    got = buf[:int(size.item())].cpu().numpy()
+    want = orc.compress_sampled(_ORC[tdtype], bits, chunk_bytes)
+    if not np.array_equal(got, want):
+        hint = "sizes %d vs %d" % (got.size, want.size)
+        if got.size == want.size:
+            hint += ", first difference at byte %d" % int(np.nonzero(got != want)[0][0])
+        pytest.fail("sampled frame differs from the oracle's: " + hint)
+    out, st = _decompress(got, tdtype, bits.size)
+    assert st == 0
+    assert torch.equal(out.view(_INT[out.element_size()]), t.view(_INT[t.element_size()]))
+    return got
+
+
+def _modes(buf):
+    return [r["mode"] for r in parse_buffer(buf)[2]]
+
+
+def _n_esc(rec):
+    r = rec["raw"]
+    tab_end = (48 + 2 * rec["nsym"] + 3) // 4 * 4
+    return int.from_bytes(r[tab_end:tab_end + 4], "little")
+
+
+def test_pr1_sampled():
+    bits = workloads.bits_numpy(workloads.pr1())
+    buf = check_sampled(bits, torch.bfloat16)
+    assert set(_modes(buf)) == {2}
+
+
+def test_gradient_bucket_with_specials_has_escapes():
+    bits = workloads.bits_numpy(workloads.gradient_bucket(300_001, seed=5, special_frac=1e-3))
+    buf = check_sampled(bits, torch.bfloat16)
+    recs = parse_buffer(buf)[2]
+    assert sum(_n_esc(r) for r in recs if r["mode"] == 2) > 0
+
+
+@pytest.mark.parametrize("tdtype,n,chunk_bytes", [
+    (torch.bfloat16, 100_003, 0),
+    (torch.bfloat16, 5_000, 64),      # 32-value chunks: runs of one value, sampled value by value
+    (torch.bfloat16, 20_000, 2048),   # runs of 16 values: two 128-bit vectors each
+    (torch.bfloat16, 777, 192),       # 96-value chunks (runs of one value every 12)
+    (torch.float32, 300_017, 0),
+    (torch.float32, 9_000, 512),      # runs of 2 values: shorter than a vector
+    (torch.float16, 150_001, 0),
+    (torch.float8_e4m3fn, 200_003, 0),
+    (torch.float8_e5m2, 200_003, 0),
+])
+def test_dtypes_and_chunk_sizes(tdtype, n, chunk_bytes):
+    rng = np.random.default_rng(n)
+    x = rng.normal(0.0, 0.02, n)
+    if tdtype == torch.float32:
+        bits = x.astype(np.float32).view(np.uint32)
+    else:
+        bits = workloads.bits_numpy(torch.from_numpy(x).to(tdtype))
+    check_sampled(bits, tdtype, chunk_bytes)
+
+
+def test_many_escapes_in_one_chunk():
+    # 300 escapes (more than the 128 a half holds in registers), coded
+    n = 32768
+    e = np.full(n, 127, np.uint16)
+    period, run = n // 8, n // 64
+    unsampled = np.nonzero((np.arange(n) % period) >= run)[0]
+    pos = np.sort(np.random.default_rng(1).choice(unsampled, 300, replace=False))
+    e[pos] = 100
+    bits = ((e << 7) | (np.arange(n) & 0x7F)).astype(np.uint16)
+    buf = check_sampled(bits, torch.bfloat16)
+    rec = parse_buffer(buf)[2][0]
+    assert rec["mode"] == 2 and _n_esc(rec) == 300
+
+
+def test_escape_heavy_chunk_goes_raw():
+    # the sample sees one exponent, the rest are spread: the record is RAW
+    n = 2 * 32768 + 4000
+    rng = np.random.default_rng(2)
+    e = rng.integers(1, 255, n).astype(np.uint16)
+    e[(np.arange(n) % 32768) % 4096 < 512] = 127
+    bits = ((e << 7) | (np.arange(n) & 0x7F)).astype(np.uint16)
+    buf = check_sampled(bits, torch.bfloat16)
+    assert _modes(buf)[0] == 1
+
+
+def test_escapes_in_ragged_tail():
+    # the last chunk holds 1000 values; its sample is values 0..511, escapes after
+    n = 32768 + 1000
+    e = np.full(n, 120, np.uint16)
+    e[32768 + 600::7] = 90
+    bits = ((e << 7) | (np.arange(n) & 0x7F)).astype(np.uint16)
+    buf = check_sampled(bits, torch.bfloat16)
+    recs = parse_buffer(buf)[2]
+    assert recs[1]["mode"] == 2 and _n_esc(recs[1]) == len(range(32768 + 600, n, 7))
+
+
+def test_all_256_symbols_sampled():
+    # fp8: every byte value inside the sample, so no escape symbol exists
+    n = 65536
+    v = np.random.default_rng(3).integers(0, 256, n).astype(np.uint8)
+    v[:256] = np.arange(256, dtype=np.uint8)
+    check_sampled(v, torch.float8_e4m3fn, 65536)
+
+
+def test_single_symbol_and_empty():
+    check_sampled(np.full(70_000, 0x3F80, np.uint16), torch.bfloat16)
+    check_sampled(np.zeros(0, np.uint16), torch.bfloat16)
+    check_sampled(np.array([0x7FC1], np.uint16), torch.bfloat16)
+
+
+def test_batched_sampled_and_mixed_decode():
+    """One batched sampled call over ragged buffers (one empty); then one
+    batched decode over sampled and full-table frames together."""
+    rng = np.random.default_rng(4)
+    sizes = [0, 1, 31, 32768, 50_001, 3 * 32768 + 17]
+    tensors = [torch.from_numpy(rng.normal(0, 0.02, n)).to(torch.bfloat16).to(DEV) for n in sizes]
+    outs, osz = uz.compress_batched(tensors, sampled=True)
+    torch.cuda.synchronize()
+    got = [o[:int(s)].cpu().numpy() for o, s in zip(outs, osz.cpu().tolist())]
+    for t, g in zip(tensors, got):
+        assert np.array_equal(g, orc.compress_sampled(orc.BF16, workloads.bits_numpy(t)))
+    full, fsz = uz.compress_batched(tensors)
+    torch.cuda.synchronize()
+    mixed = [outs[i] if i % 2 == 0 else full[i] for i in range(len(sizes))]
+    vals, status = uz.decompress_batched(mixed, torch.bfloat16, sizes)
+    torch.cuda.synchronize()
+    assert status.cpu().tolist() == [0] * len(sizes)
+    for t, v in zip(tensors, vals):
+        assert torch.equal(t.view(torch.int16), v.view(torch.int16))
+
+
+def _patch(buf, off, val, width):
+    b = buf.copy()
+    b[off:off + width] = np.frombuffer(int(val).to_bytes(width, "little"), np.uint8)
+    return b
+
+
+def test_corruptions_reported_as_the_oracle_reports():
+    n = 32768
+    e = np.full(n, 127, np.uint16)
+    e[1000], e[2000], e[3000] = 126, 130, 126  # unsampled positions: three escapes
+    e[:64] = 128
+    bits = ((e << 7) | (np.arange(n) & 0x7F)).astype(np.uint16)
+    buf = check_sampled(bits, torch.bfloat16)
+    hdr, idx, recs = parse_buffer(buf)
+    rec = recs[0]
+    base = hdr["exp_off"] + idx[0]
+    tab_end = (48 + 2 * rec["nsym"] + 3) // 4 * 4
+    words_at = tab_end + 4 + 128
+    esc_at = words_at + 2 * rec["n_words"]
+    assert _n_esc(rec) == 3
+    bad = {
+        "flags_2": _patch(buf, 10, 2, 2),
+        "flags_0": _patch(buf, 10, 0, 2),  # a mode-2 record in a full-table frame
+        "mode_0": _patch(buf, base, 0, 1),
+        "n_esc_up": _patch(buf, base + tab_end, 4, 4),
+        "n_esc_down": _patch(buf, base + tab_end, 2, 4),
+        "escape_is_sampled": _patch(buf, base + esc_at, 127, 1),
+        "freq_sum": _patch(buf, base + 48, int.from_bytes(rec["raw"][48:50], "little") + 1, 2),
+        "state_low": _patch(buf, base + tab_end + 4, 65535, 4),
+        "state": _patch(buf, base + tab_end + 4 + 4 * 5, rec["raw"][tab_end + 24] ^ 0x40, 1),
+        "word": _patch(buf, base + words_at, 0x1234, 2),
+        "rec_bytes": _patch(buf, base + 12, rec["bytes"] + 16, 4),
+        "nsym": _patch(buf, base + 2, rec["nsym"] + 1, 2),
+    }
+    for name, b in bad.items():
+        want = orc.decompress(b, orc.BF16, n)[0]
+        _, st = _decompress(b, torch.bfloat16, n)
+        assert (st == 0) == (want == orc.OK), name
+        assert want == orc.CORRUPT, name
+    # a full-table frame that claims sampled tables
+    full = orc.compress(orc.BF16, bits)
+    _, st = _decompress(_patch(full, 10, 1, 2), torch.bfloat16, n)
+    assert st == uz.UZIP_ERR_CORRUPT_INPUT
