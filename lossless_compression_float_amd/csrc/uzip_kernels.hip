@@ -32,6 +32,8 @@
 // and the serial per-lane rANS chain, not by the matrix cores.
 #include <stdint.h>
 
+#include <type_traits>
+
 #include <hip/hip_runtime.h>
 
 #include "uzip_common.hpp"
@@ -813,17 +815,20 @@ __global__ __launch_bounds__(64) void k_encode(EncParams p) {
     };
     const uint32_t nblk = (max(T0, T1) + 7) / 8;
     const uint32_t hsel = h ? 0xFFFFFFFFu : 0u;
-    uint64_t escany = 0;  // FAST steps (sampled tables): lanes whose value escaped, not yet placed
+    uint32_t escsteps = 0;  // FAST blocks (sampled tables): bit k set when step k has an escape not yet placed
     // One step; CAREFUL steps rebuild the lane masks and check the room
     // (a ragged chunk end, or words close to the RAW size), the others use
     // the block's loop-invariant mask.
-    auto step = [&](int32_t b, int k, uint32_t v, bool careful, uint64_t act) __attribute__((always_inline)) {
+    // (FAST steps with sampled tables get the exponent from the block's staging
+    // area, have_ex; the others extract it from the value v)
+    auto step = [&](int32_t b, int k, uint32_t v, bool careful, uint64_t act, bool have_ex = false,
+                    uint32_t ex_in = 0u) __attribute__((always_inline)) {
         const uint32_t t = (uint32_t)b * 8 + k;
         if (careful)
             act = (alive0 && vals0 > 32 * t ? half_prefix_mask(vals0 - 32 * t, 0) : 0ull) |
                   (alive1 && vals1 > 32 * t ? half_prefix_mask(vals1 - 32 * t, 1) : 0ull);
-        uint32_t ex;  // the value's exponent
-        asm("v_bfe_u32 %0, %1, %2, 8" : "=v"(ex) : "v"(v), "i"(Fmt<DT>::SYM));
+        uint32_t ex = ex_in;  // the value's exponent
+        if (!have_ex) asm("v_bfe_u32 %0, %1, %2, 8" : "=v"(ex) : "v"(v), "i"(Fmt<DT>::SYM));
         const uint4 te = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint8_t *>(tab) + (ex << 4));
         uint64_t m = lanes_lt(te.x & 0xFFFFu, x >> 20) & act;  // x >= f * 2^20
         uint32_t lo = (uint32_t)m, hi = (uint32_t)(m >> 32);
@@ -865,48 +870,30 @@ __global__ __launch_bounds__(64) void k_encode(EncParams p) {
         // steps every lane of a live half codes a value, and a stopped
         // half's state is never used (its chunk is stored RAW).
         x = careful ? vsel(act, x, xe) : xe;
-        if (S) {
+        if (S && careful) {  // (FAST blocks store their sign+mantissa bytes when the block is staged)
             if (R == 1) bst8(rsm2, smo2 + t * 32 * R, raw_of<DT>(v));
             if (R == 3) {
                 const uint32_t smv = raw_of<DT>(v);
                 bst16(rsm2, smo2 + t * 32 * R, smv);
                 bst8(rsm2, smo2 + t * 32 * R + 2, smv >> 16);
             }
-            if (careful) {
-                if (escm) put_escapes(escm, ex);
-            } else {
-                escany |= lanes_eq(te.y, kEscSlot);
-            }
+            if (escm) put_escapes(escm, ex);
+        } else if (S) {
+            escsteps |= lanes_eq(te.y, kEscSlot) != 0 ? 1u << k : 0u;
         }
     };
     // a block codes at most 256 values, so at most 256 words, per half: a
     // FAST block needs no per-step checks
-    // (sampled tables: and at most 256 escapes)
+    // (sampled tables: at most 256 escapes too, and every value of the block
+    // inside its chunk: the block's sign+mantissa bytes leave in whole units)
     auto block_fast = [&](int32_t b) __attribute__((always_inline)) {
         const uint32_t tend = ((uint32_t)b + 1) * 256;
         if (S)
-            return (!alive0 || (vals0 >= tend && 2 * ((end0 - r0) + 256) + nesc0 + 256 <= room0)) &&
-                   (!alive1 || (vals1 >= tend && 2 * ((end1 - r1) + 256) + nesc1 + 256 <= room1));
+            return vals0 >= tend && (nch == 1 || vals1 >= tend) &&
+                   (!alive0 || 2 * ((end0 - r0) + 256) + nesc0 + 256 <= room0) &&
+                   (!alive1 || 2 * ((end1 - r1) + 256) + nesc1 + 256 <= room1);
         return (!alive0 || (vals0 >= tend && (end0 - r0) + 256 <= wcap0)) &&
                (!alive1 || (vals1 >= tend && (end1 - r1) + 256 <= wcap1));
-    };
-    // Escapes of a FAST block, placed after the block (its values are still in
-    // registers and nothing is in flight): the block's steps again, last first,
-    // from the table's c0 column alone.
-    auto block_escapes = [&](const uint32_t(&V)[8]) __attribute__((always_inline)) {
-        const uint64_t act = (alive0 ? 0xFFFFFFFFull : 0ull) | (alive1 ? kHighHalf : 0ull);
-        for (int k = 7; k >= 0; --k) {
-            uint32_t ex;
-            asm("v_bfe_u32 %0, %1, %2, 8" : "=v"(ex) : "v"(V[k]), "i"(Fmt<DT>::SYM));
-            const uint32_t cy = *reinterpret_cast<const uint32_t *>(reinterpret_cast<const uint8_t *>(tab) + (ex << 4) + 4);
-            const uint64_t escm = lanes_eq(cy, kEscSlot) & act;
-            if (escm) put_escapes(escm, ex);
-        }
-    };
-    auto fast_block = [&](int32_t b, const uint32_t(&V)[8]) __attribute__((always_inline)) {
-        const uint64_t act = (alive0 ? 0xFFFFFFFFull : 0ull) | (alive1 ? kHighHalf : 0ull);
-#pragma unroll
-        for (int k = 7; k >= 0; --k) step(b, k, V[k], false, act);
     };
     // Block values: lane lj's values of steps 8b .. 8b + 7 (past the pair: zeros).
     // Runs of FAST blocks are software-pipelined: the next block's values are
@@ -919,56 +906,191 @@ __global__ __launch_bounds__(64) void k_encode(EncParams p) {
     // remain outstanding.  Every branch and loop edge comes after a wait, so
     // no register with a load in flight is ever copied (a test checks the
     // generated code for this).  Other blocks use ordinary loads.
-    auto asm_load_block = [&](int32_t bb, uint32_t(&V)[8]) __attribute__((always_inline)) {
-        const uint32_t o = bb >= 0 ? in0 + ((uint32_t)bb * 8 * 32 + lj) * EB : kOutOfRange;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            if (EB == 1)
-                asm volatile("buffer_load_ubyte %0, %1, %2, 0 offen offset:%3" : "=v"(V[k]) : "v"(o), "s"(rin), "i"(k * 32 * EB));
-            else if (EB == 2)
-                asm volatile("buffer_load_ushort %0, %1, %2, 0 offen offset:%3" : "=v"(V[k]) : "v"(o), "s"(rin), "i"(k * 32 * EB));
-            else
-                asm volatile("buffer_load_dword %0, %1, %2, 0 offen offset:%3" : "=v"(V[k]) : "v"(o), "s"(rin), "i"(k * 32 * EB));
-        }
-    };
-    // stores of a FAST block: its words, and with sampled tables its sign+mantissa bytes
-    constexpr uint32_t kBlockStores = 8 + (S ? 8 * (R == 3 ? 2 : R) : 0);
 #define UZIP_WAIT_BLOCK(N, V)                                                                                         \
     asm volatile("s_waitcnt vmcnt(%8)" : "+v"(V[0]), "+v"(V[1]), "+v"(V[2]), "+v"(V[3]), "+v"(V[4]), "+v"(V[5]), \
                  "+v"(V[6]), "+v"(V[7]) : "i"(N))
-    for (int32_t b = (int32_t)nblk - 1; b >= 0;) {
-        if (!block_fast(b)) {
-            const uint32_t o = in0 + ((uint32_t)b * 8 * 32 + lj) * EB;
-            uint32_t V[8];
+    if constexpr (!S) {
+        auto fast_block = [&](int32_t b, const uint32_t(&V)[8]) __attribute__((always_inline)) {
+            const uint64_t act = (alive0 ? 0xFFFFFFFFull : 0ull) | (alive1 ? kHighHalf : 0ull);
 #pragma unroll
-            for (int k = 0; k < 8; ++k) V[k] = bld_value<DT>(rin, o + k * 32 * EB);
+            for (int k = 7; k >= 0; --k) step(b, k, V[k], false, act);
+        };
+        auto asm_load_block = [&](int32_t bb, uint32_t(&V)[8]) __attribute__((always_inline)) {
+            const uint32_t o = bb >= 0 ? in0 + ((uint32_t)bb * 8 * 32 + lj) * EB : kOutOfRange;
 #pragma unroll
-            for (int k = 7; k >= 0; --k) step(b, k, V[k], true, 0ull);
-            --b;
-            continue;
-        }
-        uint32_t VA[8], VB[8];
-        asm_vmem_fence();
-        asm_load_block(b, VA);
-        UZIP_WAIT_BLOCK(0, VA);
-        for (;;) {
-            asm_load_block(b - 1, VB);
-            fast_block(b, VA);
-            UZIP_WAIT_BLOCK(kBlockStores, VB);
-            if (S && escany) {
-                escany = 0;
-                block_escapes(VA);
+            for (int k = 0; k < 8; ++k) {
+                if (EB == 1)
+                    asm volatile("buffer_load_ubyte %0, %1, %2, 0 offen offset:%3" : "=v"(V[k]) : "v"(o), "s"(rin), "i"(k * 32 * EB));
+                else if (EB == 2)
+                    asm volatile("buffer_load_ushort %0, %1, %2, 0 offen offset:%3" : "=v"(V[k]) : "v"(o), "s"(rin), "i"(k * 32 * EB));
+                else
+                    asm volatile("buffer_load_dword %0, %1, %2, 0 offen offset:%3" : "=v"(V[k]) : "v"(o), "s"(rin), "i"(k * 32 * EB));
             }
-            if (--b < 0 || !block_fast(b)) break;
-            asm_load_block(b - 1, VA);
-            fast_block(b, VB);
-            UZIP_WAIT_BLOCK(kBlockStores, VA);
-            if (S && escany) {
-                escany = 0;
-                block_escapes(VB);
+        };
+        for (int32_t b = (int32_t)nblk - 1; b >= 0;) {
+            if (!block_fast(b)) {
+                const uint32_t o = in0 + ((uint32_t)b * 8 * 32 + lj) * EB;
+                uint32_t V[8];
+#pragma unroll
+                for (int k = 0; k < 8; ++k) V[k] = bld_value<DT>(rin, o + k * 32 * EB);
+#pragma unroll
+                for (int k = 7; k >= 0; --k) step(b, k, V[k], true, 0ull);
+                --b;
+                continue;
             }
-            if (--b < 0 || !block_fast(b)) break;
+            uint32_t VA[8], VB[8];
+            asm_vmem_fence();
+            asm_load_block(b, VA);
+            UZIP_WAIT_BLOCK(0, VA);
+            for (;;) {
+                asm_load_block(b - 1, VB);
+                fast_block(b, VA);
+                UZIP_WAIT_BLOCK(8, VB);
+                if (--b < 0 || !block_fast(b)) break;
+                asm_load_block(b - 1, VA);
+                fast_block(b, VB);
+                UZIP_WAIT_BLOCK(8, VA);
+                if (--b < 0 || !block_fast(b)) break;
+            }
         }
+    } else {
+        // Sampled tables: a FAST block is read as whole units, lane lj taking
+        // values 8lj .. 8lj + 7 of its half's 256 (one 128-bit load; fp32
+        // two, fp8 one 64-bit), and staged: the lane stores their sign+mantissa
+        // bytes as one unit and writes their eight exponents to the half's
+        // 256-byte staging area in LDS, from which step k of lane j reads byte
+        // 32k + j.  The next block's unit is loaded (asm) while a block is
+        // coded, as above, and staged after its wait.
+        uint8_t *stage = reinterpret_cast<uint8_t *>(lds) + h * 256;  // (the keys' words, free in this pass)
+        constexpr uint32_t NU = EB == 4 ? 2 : 1;  // loads per unit (fp8: one 64-bit)
+        using UnitT = typename std::conditional<EB == 1, u32x2, u32x4>::type;
+        auto asm_load_unit = [&](int32_t bb, UnitT(&U)[2]) __attribute__((always_inline)) {
+            const uint32_t o = bb >= 0 ? in0 + ((uint32_t)bb * 256 + 8 * lj) * EB : kOutOfRange;
+            if constexpr (EB == 1) {
+                asm volatile("buffer_load_dwordx2 %0, %1, %2, 0 offen" : "=v"(U[0]) : "v"(o), "s"(rin));
+            } else {
+#pragma unroll
+                for (uint32_t u = 0; u < NU; ++u)
+                    asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen offset:%3" : "=v"(U[u]) : "v"(o), "s"(rin), "i"(16 * u));
+            }
+        };
+        // the unit's sign+mantissa bytes (bf16, fp16: 8; fp32: 24), stored by store_sm
+        constexpr uint32_t kSmStores = R == 0 ? 0 : R == 1 ? 1 : 2;
+        auto stage_unit = [&](const UnitT(&U)[2], uint32_t(&SM)[6]) __attribute__((always_inline)) {
+            uint32_t e0, e1;  // the eight exponents, value order
+            if constexpr (DT == 1 || DT == 3) {
+                // low and high bytes of four values at once
+                const uint32_t lo0 = __builtin_amdgcn_perm(U[0].y, U[0].x, 0x06040200u);
+                const uint32_t hi0 = __builtin_amdgcn_perm(U[0].y, U[0].x, 0x07050301u);
+                const uint32_t lo1 = __builtin_amdgcn_perm(U[0].w, U[0].z, 0x06040200u);
+                const uint32_t hi1 = __builtin_amdgcn_perm(U[0].w, U[0].z, 0x07050301u);
+                uint32_t s0 = lo0, s1 = lo1;
+                e0 = hi0;
+                e1 = hi1;
+                if (DT == 1) {  // sign = bit 7 of the high byte, exponent = its bits 0-6 and bit 7 of the low byte
+                    s0 = (hi0 & 0x80808080u) | (lo0 & 0x7F7F7F7Fu);
+                    s1 = (hi1 & 0x80808080u) | (lo1 & 0x7F7F7F7Fu);
+                    e0 = ((hi0 << 1) & 0xFEFEFEFEu) | ((lo0 >> 7) & 0x01010101u);
+                    e1 = ((hi1 << 1) & 0xFEFEFEFEu) | ((lo1 >> 7) & 0x01010101u);
+                }
+                SM[0] = s0;
+                SM[1] = s1;
+            } else if constexpr (DT == 2) {
+                const uint32_t w[8] = {U[0].x, U[0].y, U[0].z, U[0].w, U[1].x, U[1].y, U[1].z, U[1].w};
+                uint32_t sm[8], ex[8];
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    sm[k] = ((w[k] >> 8) & 0x800000u) | (w[k] & 0x7FFFFFu);
+                    ex[k] = (w[k] >> 23) & 0xFFu;
+                }
+                e0 = ex[0] | (ex[1] << 8) | (ex[2] << 16) | (ex[3] << 24);
+                e1 = ex[4] | (ex[5] << 8) | (ex[6] << 16) | (ex[7] << 24);
+                SM[0] = sm[0] | (sm[1] << 24);
+                SM[1] = (sm[1] >> 8) | (sm[2] << 16);
+                SM[2] = (sm[2] >> 16) | (sm[3] << 8);
+                SM[3] = sm[4] | (sm[5] << 24);
+                SM[4] = (sm[5] >> 8) | (sm[6] << 16);
+                SM[5] = (sm[6] >> 16) | (sm[7] << 8);
+            } else {  // fp8: the byte is the symbol, nothing raw
+                e0 = U[0].x;
+                e1 = U[0].y;
+            }
+            asm volatile("" ::: "memory");  // (after the last block's reads of the area)
+            *reinterpret_cast<u32x2 *>(stage + 8 * lj) = u32x2{e0, e1};
+        };
+        // (issued after the next unit's loads, so that the wait for those loads
+        // does not also wait for this store)
+        auto store_sm = [&](int32_t bb, const uint32_t(&SM)[6]) __attribute__((always_inline)) {
+            const uint32_t so = ((h ? vals0 : 0u) + (uint32_t)bb * 256 + 8 * lj) * R;  // past the pair: dropped
+            if constexpr (R == 1) {
+                __builtin_amdgcn_raw_buffer_store_b64(u32x2{SM[0], SM[1]}, rsm2, (int)so, 0, 0);
+            } else if constexpr (R == 3) {
+                __builtin_amdgcn_raw_buffer_store_b96(u32x3{SM[0], SM[1], SM[2]}, rsm2, (int)so, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b96(u32x3{SM[3], SM[4], SM[5]}, rsm2, (int)(so + 12), 0, 0);
+            }
+        };
+        auto fast_block_s = [&](int32_t b) __attribute__((always_inline)) {
+            const uint64_t act = (alive0 ? 0xFFFFFFFFull : 0ull) | (alive1 ? kHighHalf : 0ull);
+            asm volatile("" ::: "memory");  // (after the staging writes)
+            uint32_t E[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) E[k] = stage[32 * k + lj];
+#pragma unroll
+            for (int k = 7; k >= 0; --k) step(b, k, 0u, false, act, true, E[k]);
+        };
+        // escapes of a FAST block, placed after the block from the staged exponents, last first
+        auto block_escapes_s = [&]() __attribute__((always_inline)) {
+            const uint64_t act = (alive0 ? 0xFFFFFFFFull : 0ull) | (alive1 ? kHighHalf : 0ull);
+            for (int k = 7; k >= 0; --k) {
+                if (((escsteps >> k) & 1u) == 0) continue;
+                const uint32_t ex = stage[32 * k + lj];
+                const uint32_t cy = *reinterpret_cast<const uint32_t *>(reinterpret_cast<const uint8_t *>(tab) + (ex << 4) + 4);
+                const uint64_t escm = lanes_eq(cy, kEscSlot) & act;
+                if (escm) put_escapes(escm, ex);
+            }
+        };
+#define UZIP_WAIT_UNIT(N, U) asm volatile("s_waitcnt vmcnt(%2)" : "+v"(U[0]), "+v"(U[1]) : "i"(N))
+        for (int32_t b = (int32_t)nblk - 1; b >= 0;) {
+            if (!block_fast(b)) {
+                const uint32_t o = in0 + ((uint32_t)b * 8 * 32 + lj) * EB;
+                uint32_t V[8];
+#pragma unroll
+                for (int k = 0; k < 8; ++k) V[k] = bld_value<DT>(rin, o + k * 32 * EB);
+#pragma unroll
+                for (int k = 7; k >= 0; --k) step(b, k, V[k], true, 0ull);
+                --b;
+                continue;
+            }
+            UnitT UA[2] = {}, UB[2] = {};
+            uint32_t SM[6] = {0, 0, 0, 0, 0, 0};
+            asm_vmem_fence();
+            asm_load_unit(b, UA);
+            UZIP_WAIT_UNIT(0, UA);
+            stage_unit(UA, SM);
+            for (;;) {
+                asm_load_unit(b - 1, UB);
+                store_sm(b, SM);
+                fast_block_s(b);
+                UZIP_WAIT_UNIT(8 + kSmStores, UB);
+                if (escsteps) {
+                    block_escapes_s();
+                    escsteps = 0;
+                }
+                if (--b < 0 || !block_fast(b)) break;
+                stage_unit(UB, SM);
+                asm_load_unit(b - 1, UA);
+                store_sm(b, SM);
+                fast_block_s(b);
+                UZIP_WAIT_UNIT(8 + kSmStores, UA);
+                if (escsteps) {
+                    block_escapes_s();
+                    escsteps = 0;
+                }
+                if (--b < 0 || !block_fast(b)) break;
+                stage_unit(UA, SM);
+            }
+        }
+#undef UZIP_WAIT_UNIT
     }
 #undef UZIP_WAIT_BLOCK
 
@@ -1684,7 +1806,10 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
         const uint32_t Tw = max(T0, T1);
         // steps in which every lane of each running half holds a value
         const uint32_t F0 = run0 ? ni0 / 32 : 0xFFFFFFFFu, F1 = run1 ? ni1 / 32 : 0xFFFFFFFFu;
-        const uint32_t Tmain = min(min(F0, F1), Tw) & ~7u;
+        // (sampled tables: a half with more escapes than its registers hold
+        // is decoded by the tail loop alone, whose escape path may load)
+        const uint32_t nesc_w = S ? max(uniform_u32(__shfl((int)nesc, 0, 64)), uniform_u32(__shfl((int)nesc, 32, 64))) : 0u;
+        const uint32_t Tmain = S && nesc_w > 128 ? 0u : min(min(F0, F1), Tw) & ~7u;
         const uint32_t Tmain16 = Tmain & ~15u;  // bf16 main loop: 16 steps per iteration
         // bf16: this lane's sign+mantissa dword of group 0 (see the main loop),
         // loaded before the word window so that many memory operations lie
@@ -1735,19 +1860,31 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
         const uint32_t escaddr = kEscSlot | hsym;
         uint32_t escv = 0;  // escapes used by this half
         bool escbad = false;
-        auto escape_entry = [&](uint64_t escm, uint32_t em) __attribute__((always_inline)) {
+        // (called once a step's value v is built; returns it with the escaped
+        // exponent in place for the escaping lanes)
+        auto escape_value = [&](uint64_t escm, uint32_t v, uint32_t sp, bool tail) __attribute__((always_inline)) {
             const uint32_t elo = __builtin_popcount((uint32_t)escm), ehi = __builtin_popcount((uint32_t)(escm >> 32));
             const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(escm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)escm, 0u));
             const uint32_t idx = escv + below - (h ? elo : 0u);
             const bool mine = (escm >> lane) & 1u;
             const uint32_t ew = (uint32_t)__builtin_amdgcn_ds_bpermute((int)((((idx >> 2) & 31u) | (h << 5)) << 2), (int)escw);
             uint32_t e = (ew >> (8 * (idx & 3u))) & 0xFFu;
-            if (idx >= 128) e = bld8(rrec, mine && idx < nesc ? escat + idx : kOutOfRange);
+            if (tail && idx >= 128) e = bld8(rrec, mine && idx < nesc ? escat + idx : kOutOfRange);
             // the bitmap byte of e's symbol group is held by lane e >> 3 of the half
             const uint32_t pbe = (uint32_t)__builtin_amdgcn_ds_bpermute((int)(((e >> 3) | (h << 5)) << 2), (int)pb);
             escbad = escbad || (mine && (idx >= nesc || nsym == 256 || ((pbe >> (e & 7u)) & 1u)));
             escv += h ? ehi : elo;
-            return mine ? (em & ~0xFF000u) | (e << 12) : em;
+            uint32_t ve;
+            if (DT == 1) {
+                asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(ve) : "s"(0x807Fu), "v"(sp), "v"(e << 7));
+            } else if (DT == 3) {
+                asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(ve) : "s"(0x00FFu), "v"(sp), "v"(e << 8));
+            } else if (DT == 2) {
+                ve = ((sp | ((sp & 0x800000u) << 8)) & 0x807FFFFFu) | (e << 23);
+            } else {
+                ve = e;
+            }
+            return mine ? ve : v;
         };
         // One step of both half-waves.  act = lanes holding a value this step
         // (TAIL steps only: in the main loop every lane of a running half
@@ -1760,12 +1897,11 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
         auto step = [&](uint32_t t, uint64_t act, bool tail, uint32_t sp, int par, bool store) __attribute__((always_inline)) {
             uint32_t slot_addr;  // (x & 4095) | this half's row: the index in s_sym / s_slot
             asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(slot_addr) : "v"(x), "s"(kTableSize - 1), "v"(hsym));
-            uint32_t em = kDirect ? s_slotf[slot_addr] : s_rkf[s_symf[slot_addr] | hrk];
+            // (sampled tables: the lanes at the escape slot; their values are
+            // patched once built, so the rare branch needs no table entry)
+            const uint64_t escm = S ? lanes_eq(slot_addr, escaddr) & act : 0ull;
+            const uint32_t em = kDirect ? s_slotf[slot_addr] : s_rkf[s_symf[slot_addr] | hrk];
             const uint32_t xd = x - (__umul24(em & 0xFFFu, x >> kProbBits) + (em >> 20));
-            if (S) {  // (only the symbol bits of em are used below)
-                const uint64_t escm = lanes_eq(slot_addr, escaddr) & act;
-                if (escm) em = escape_entry(escm, em);
-            }
             // (the and with act also puts the mask in registers written by the
             // scalar unit: inline asm below reads it, and the hardware needs
             // spacing between a vector compare writing scalar registers and a
@@ -1819,21 +1955,26 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
                 // keeps the low 16 bits
                 uint32_t v;
                 asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(v) : "s"(0x807Fu), "v"(sp), "v"(em >> 5));
+                if (S && __builtin_expect(escm != 0, 0)) v = escape_value(escm, v, sp, tail);
                 if (store) bst16(rout, out_lane + t * 32 * EB, v);
                 return v;
             } else if (DT == 3) {
                 // the low byte from sp, the symbol (em bits 12-19) to bits 8-15
                 uint32_t v;
                 asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(v) : "s"(0x00FFu), "v"(sp), "v"(em >> 4));
+                if (S && __builtin_expect(escm != 0, 0)) v = escape_value(escm, v, sp, tail);
                 if (store) bst16(rout, out_lane + t * 32 * EB, v);
                 return v;
             } else if (DT == 2) {
                 // sign (bit 23 of sm) to bit 31, mantissa bits 0-22, exponent to bits 23-30
                 const uint32_t sx = sp | ((sp & 0x800000u) << 8), ex = em << 11;
-                bst32(rout, out_lane + t * 32 * EB, (sx & 0x807FFFFFu) | (ex & ~0x807FFFFFu));
+                uint32_t v = (sx & 0x807FFFFFu) | (ex & ~0x807FFFFFu);
+                if (S && __builtin_expect(escm != 0, 0)) v = escape_value(escm, v, sp, tail);
+                bst32(rout, out_lane + t * 32 * EB, v);
                 return 0u;
             } else {
-                const uint32_t v = (em >> 12) & 0xFFu;  // the symbol is the value
+                uint32_t v = (em >> 12) & 0xFFu;  // the symbol is the value
+                if (S && __builtin_expect(escm != 0, 0)) v = escape_value(escm, v, sp, tail);
                 if (store) bst_value<DT>(rout, out_lane + t * 32 * EB, v);
                 return v;
             }

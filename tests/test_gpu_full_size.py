@@ -24,8 +24,9 @@ def _host(buf: torch.Tensor, size: int) -> np.ndarray:
     return buf[:size].cpu().numpy()
 
 
-def _check_frame(b: np.ndarray, code: int, n: int, chunk_elems: int):
-    """Header, index and record headers of one compressed buffer (any size)."""
+def _check_frame(b: np.ndarray, code: int, n: int, chunk_elems: int, modes=(0, 1)):
+    """Header, index and record headers of one compressed buffer (any size);
+    `modes`: the record modes the frame may hold (sampled tables: 1 and 2)."""
     C = (n + chunk_elems - 1) // chunk_elems
     r = {orc.BF16: 1, orc.FP32: 3, orc.FP16: 1, orc.FP8_E4M3: 0, orc.FP8_E5M2: 0}[code]
     hdr = np.frombuffer(b[:64].tobytes(), dtype=np.uint64)
@@ -49,7 +50,7 @@ def _check_frame(b: np.ndarray, code: int, n: int, chunk_elems: int):
     want_vals[-1] = n - (C - 1) * chunk_elems
     assert np.array_equal(rec_bytes.astype(np.int64), sizes)
     assert np.array_equal(n_values.astype(np.int64), want_vals)
-    assert np.all(heads[:, 0] <= 1)
+    assert np.all(np.isin(heads[:, 0], modes))
 
 
 def _same_bits(a: torch.Tensor, b: torch.Tensor) -> bool:
@@ -79,6 +80,37 @@ def test_fp32_gradients_100m_equals_oracle():
     back, st = uz.decompress(buf, torch.float32, t.numel(), in_bytes=got.size)
     torch.cuda.synchronize()
     assert int(st.item()) == 0 and _same_bits(back, t)
+
+
+@pytest.mark.parametrize("name", ["grad_bucket", "fp32_grad"])
+def test_sampled_tables_full_size_equal_oracle(name):
+    """uzip_compress_sampled at the benchmark's sizes: the oracle's sampled frame, byte for byte."""
+    if name == "grad_bucket":
+        t, code, ce = workloads.gradient_bucket(workloads.GRAD_BUCKET_N, device=DEV, seed=1), orc.BF16, 32768
+    else:
+        t, code, ce = workloads.fp32_gradients(workloads.FP32_GRAD_N, device=DEV, seed=3), orc.FP32, 65536
+    buf, size = uz.compress(t, sampled=True)
+    torch.cuda.synchronize()
+    got = _host(buf, int(size.item()))
+    _check_frame(got, code, t.numel(), ce, modes=(1, 2))
+    assert int(got[10]) == 1  # header flag bit 0
+    assert np.array_equal(got, orc.compress_sampled(code, workloads.bits_numpy(t)))
+    back, st = uz.decompress(buf, t.dtype, t.numel(), in_bytes=got.size)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0 and _same_bits(back, t)
+
+
+def test_sampled_small_message_batch_equals_oracle():
+    ts = workloads.small_message_batch(device=DEV, seed=4)
+    outs, sizes = uz.compress_batched(ts, sampled=True)
+    torch.cuda.synchronize()
+    sz = sizes.cpu().tolist()
+    for t, o, s in zip(ts, outs, sz):
+        assert np.array_equal(_host(o, s), orc.compress_sampled(orc.BF16, workloads.bits_numpy(t)))
+    vals, status = uz.decompress_batched(outs, torch.bfloat16, [t.numel() for t in ts], in_bytes=sz)
+    torch.cuda.synchronize()
+    assert status.cpu().tolist() == [0] * len(ts)
+    assert all(_same_bits(a, b) for a, b in zip(ts, vals))
 
 
 def test_small_message_batch_4096_buffers_equal_oracle():
