@@ -1809,7 +1809,7 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
         // (sampled tables: a half with more escapes than its registers hold
         // is decoded by the tail loop alone, whose escape path may load)
         const uint32_t nesc_w = S ? max(uniform_u32(__shfl((int)nesc, 0, 64)), uniform_u32(__shfl((int)nesc, 32, 64))) : 0u;
-        const uint32_t Tmain = S && nesc_w > 128 ? 0u : min(min(F0, F1), Tw) & ~7u;
+        const uint32_t Tmain = S && nesc_w > 256 ? 0u : min(min(F0, F1), Tw) & ~7u;
         const uint32_t Tmain16 = Tmain & ~15u;  // bf16 main loop: 16 steps per iteration
         // bf16: this lane's sign+mantissa dword of group 0 (see the main loop),
         // loaded before the word window so that many memory operations lie
@@ -1847,19 +1847,32 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
         const uint32_t *s_slotf = &s_slot[0][0];
         // Escapes (sampled tables): the value whose slot is 4095 takes its
         // exponent from the record's escape list, in value order; a half's
-        // first 128 escaped bytes are held four to a lane (fetched by
-        // bpermute), later ones are loaded.  The byte must not be a sampled
-        // symbol, and the list must be used exactly.
+        // first 256 escaped bytes are held four to a lane in two registers
+        // (fetched by bpermute), later ones are loaded.  The byte must not be
+        // a sampled symbol, and the list must be used exactly.
         const uint32_t escat = rel + (uint32_t)words_offset_sampled(nsym) + 2 * nw;  // byte offset of the list
-        uint32_t escw = 0;
+        uint32_t escw = 0, escw1 = 0;  // list bytes [4j, 4j + 4) and [128 + 4j, 132 + 4j) of lane j of the half
         if (S) {
             const uint32_t ea = (escat & ~3u) + 4 * lj;
             escw = __builtin_amdgcn_alignbyte(bld32(rrec, rans_run ? ea + 4 : kOutOfRange),
                                               bld32(rrec, rans_run ? ea : kOutOfRange), escat & 3u);
+            escw1 = __builtin_amdgcn_alignbyte(bld32(rrec, rans_run ? ea + 132 : kOutOfRange),
+                                               bld32(rrec, rans_run ? ea + 128 : kOutOfRange), escat & 3u);
         }
         const uint32_t escaddr = kEscSlot | hsym;
         uint32_t escv = 0;  // escapes used by this half
         bool escbad = false;
+        if (S) {
+            // the held list bytes are checked here, once: none may be a sampled
+            // symbol (lane e >> 3 of the half holds the bitmap byte of e's group)
+#pragma unroll
+            for (uint32_t k = 0; k < 8; ++k) {
+                const uint32_t e = ((k < 4 ? escw : escw1) >> (8 * (k & 3u))) & 0xFFu;
+                const uint32_t idx = (k < 4 ? 0u : 128u) + 4 * lj + (k & 3u);
+                const uint32_t pbe = (uint32_t)__builtin_amdgcn_ds_bpermute((int)(((e >> 3) | (h << 5)) << 2), (int)pb);
+                escbad = escbad || (rans_run && idx < nesc && ((pbe >> (e & 7u)) & 1u));
+            }
+        }
         // (called once a step's value v is built; returns it with the escaped
         // exponent in place for the escaping lanes)
         auto escape_value = [&](uint64_t escm, uint32_t v, uint32_t sp, bool tail) __attribute__((always_inline)) {
@@ -1867,12 +1880,19 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
             const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(escm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)escm, 0u));
             const uint32_t idx = escv + below - (h ? elo : 0u);
             const bool mine = (escm >> lane) & 1u;
-            const uint32_t ew = (uint32_t)__builtin_amdgcn_ds_bpermute((int)((((idx >> 2) & 31u) | (h << 5)) << 2), (int)escw);
-            uint32_t e = (ew >> (8 * (idx & 3u))) & 0xFFu;
-            if (tail && idx >= 128) e = bld8(rrec, mine && idx < nesc ? escat + idx : kOutOfRange);
-            // the bitmap byte of e's symbol group is held by lane e >> 3 of the half
-            const uint32_t pbe = (uint32_t)__builtin_amdgcn_ds_bpermute((int)(((e >> 3) | (h << 5)) << 2), (int)pb);
-            escbad = escbad || (mine && (idx >= nesc || nsym == 256 || ((pbe >> (e & 7u)) & 1u)));
+            const int src = (int)((((idx >> 2) & 31u) | (h << 5)) << 2);
+            const uint32_t ew0 = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)escw);
+            const uint32_t ew1 = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)escw1);
+            uint32_t e = ((idx >= 128 ? ew1 : ew0) >> (8 * (idx & 3u))) & 0xFFu;
+            bool bad = idx >= nesc || nsym == 256;
+            if (tail && idx >= 256) {
+                // past the held bytes: load it, and check here that it is no sampled
+                // symbol (the bitmap byte of e's group is held by lane e >> 3 of the half)
+                e = bld8(rrec, mine && idx < nesc ? escat + idx : kOutOfRange);
+                const uint32_t pbe = (uint32_t)__builtin_amdgcn_ds_bpermute((int)(((e >> 3) | (h << 5)) << 2), (int)pb);
+                bad = bad || ((pbe >> (e & 7u)) & 1u);
+            }
+            escbad = escbad || (mine && bad);
             escv += h ? ehi : elo;
             uint32_t ve;
             if (DT == 1) {

@@ -67,13 +67,14 @@ def test_workspace_grows_with_chunks():
 FAKE = 0x10000  # 16-byte aligned, never dereferenced: every call below fails its checks first
 
 
-def test_compress_argument_errors_return_synchronously():
+@pytest.mark.parametrize("fn", [uz.uzip_compress, uz.uzip_compress_sampled])
+def test_compress_argument_errors_return_synchronously(fn):
     n = 1000
     cap = uz.uzip_max_compressed_size(uz.UZIP_BF16, n)
     ws = uz.uzip_workspace_size(uz.UZIP_BF16, n)
-    call = lambda **kw: uz.uzip_compress(**{**dict(dtype=uz.UZIP_BF16, d_in=FAKE, num_elements=n, chunk_bytes=0,
-                                                     d_out=FAKE, out_capacity=cap, d_out_size=FAKE,
-                                                     d_workspace=FAKE, workspace_bytes=ws - 1, stream=None), **kw})
+    call = lambda **kw: fn(**{**dict(dtype=uz.UZIP_BF16, d_in=FAKE, num_elements=n, chunk_bytes=0,
+                                     d_out=FAKE, out_capacity=cap, d_out_size=FAKE,
+                                     d_workspace=FAKE, workspace_bytes=ws - 1, stream=None), **kw})
     assert call(dtype=7) == uz.UZIP_ERR_INVALID_ARGUMENT
     assert call(chunk_bytes=100) == uz.UZIP_ERR_INVALID_ARGUMENT
     assert call(d_in=None) == uz.UZIP_ERR_INVALID_ARGUMENT
@@ -97,13 +98,14 @@ def test_decompress_argument_errors_return_synchronously():
     assert call() == uz.UZIP_ERR_INVALID_ARGUMENT
 
 
-def test_batched_argument_errors_return_synchronously():
+@pytest.mark.parametrize("fn", [uz.uzip_compress_batched, uz.uzip_compress_batched_sampled])
+def test_batched_argument_errors_return_synchronously(fn):
     ns = [100, 0, 5000]
     caps = [uz.uzip_max_compressed_size(uz.UZIP_BF16, n) for n in ns]
     ws = uz.uzip_workspace_size_batched(uz.UZIP_BF16, ns)
     base = dict(dtype=uz.UZIP_BF16, h_in=[FAKE, 0, FAKE], h_num_elements=ns, chunk_bytes=0, h_out=[FAKE] * 3,
                 h_out_capacity=caps, d_out_sizes=FAKE, d_workspace=FAKE, workspace_bytes=ws - 1, stream=None)
-    call = lambda **kw: uz.uzip_compress_batched(**{**base, **kw})
+    call = lambda **kw: fn(**{**base, **kw})
     assert call(h_in=[0, 0, FAKE]) == uz.UZIP_ERR_INVALID_ARGUMENT
     assert call(h_out_capacity=[caps[0], caps[1], caps[2] - 16]) == uz.UZIP_ERR_CAPACITY
     assert call() == uz.UZIP_ERR_INVALID_ARGUMENT

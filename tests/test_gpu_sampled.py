@@ -97,18 +97,22 @@ def test_dtypes_and_chunk_sizes(tdtype, n, chunk_bytes):
     check_sampled(bits, tdtype, chunk_bytes)
 
 
-def test_many_escapes_in_one_chunk():
-    # 300 escapes (more than the 128 a half holds in registers), coded
-    n = 32768
+@pytest.mark.parametrize("count", [200, 300])
+def test_many_escapes_in_one_chunk(count):
+    # a half holds 256 escapes in registers: 200 stay in the main loop, 300
+    # send the pair to the tail loop, whose escape path loads; both coded
+    n = 2 * 32768
     e = np.full(n, 127, np.uint16)
-    period, run = n // 8, n // 64
-    unsampled = np.nonzero((np.arange(n) % period) >= run)[0]
-    pos = np.sort(np.random.default_rng(1).choice(unsampled, 300, replace=False))
+    period, run = 32768 // 8, 32768 // 64
+    unsampled = np.nonzero((np.arange(32768) % period) >= run)[0]
+    pos = np.sort(np.random.default_rng(count).choice(unsampled, count, replace=False))
     e[pos] = 100
+    e[32768 + pos[:count // 3]] = 101
     bits = ((e << 7) | (np.arange(n) & 0x7F)).astype(np.uint16)
     buf = check_sampled(bits, torch.bfloat16)
-    rec = parse_buffer(buf)[2][0]
-    assert rec["mode"] == 2 and _n_esc(rec) == 300
+    recs = parse_buffer(buf)[2]
+    assert recs[0]["mode"] == 2 and _n_esc(recs[0]) == count
+    assert recs[1]["mode"] == 2 and _n_esc(recs[1]) == count // 3
 
 
 def test_escape_heavy_chunk_goes_raw():
