@@ -960,18 +960,22 @@ __global__ __launch_bounds__(64) void k_encode(EncParams p) {
         // bytes as one unit and writes their eight exponents to the half's
         // 256-byte staging area in LDS, from which step k of lane j reads byte
         // 32k + j.  The next block's unit is loaded (asm) while a block is
-        // coded, as above, and staged after its wait.
+        // coded, as above, and staged after its wait.  The unit loads carry the
+        // non-temporal hint: each value is read once (measured: about 2% faster
+        // than the default policy on the gradient bucket; the same hint on the
+        // sign+mantissa stores, on the full-table encoder's loads or on the
+        // decoder's loads was slower).
         uint8_t *stage = reinterpret_cast<uint8_t *>(lds) + h * 256;  // (the keys' words, free in this pass)
         constexpr uint32_t NU = EB == 4 ? 2 : 1;  // loads per unit (fp8: one 64-bit)
         using UnitT = typename std::conditional<EB == 1, u32x2, u32x4>::type;
         auto asm_load_unit = [&](int32_t bb, UnitT(&U)[2]) __attribute__((always_inline)) {
             const uint32_t o = bb >= 0 ? in0 + ((uint32_t)bb * 256 + 8 * lj) * EB : kOutOfRange;
             if constexpr (EB == 1) {
-                asm volatile("buffer_load_dwordx2 %0, %1, %2, 0 offen" : "=v"(U[0]) : "v"(o), "s"(rin));
+                asm volatile("buffer_load_dwordx2 %0, %1, %2, 0 offen nt" : "=v"(U[0]) : "v"(o), "s"(rin));
             } else {
 #pragma unroll
                 for (uint32_t u = 0; u < NU; ++u)
-                    asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen offset:%3" : "=v"(U[u]) : "v"(o), "s"(rin), "i"(16 * u));
+                    asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen offset:%3 nt" : "=v"(U[u]) : "v"(o), "s"(rin), "i"(16 * u));
             }
         };
         // the unit's sign+mantissa bytes (bf16, fp16: 8; fp32: 24), stored by store_sm
