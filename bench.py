@@ -14,6 +14,8 @@ JSON line:
                  library on the launch stream) against the 8 TB/s HBM peak
   cpu_baseline   the CPU oracle (single thread) on a bounded sample of the
                  same bytes; its output also serves as a byte-for-byte check
+  sampled_tables (full-table runs) the same workload measured again with
+                 tables from each chunk's sample (uzip_compress_sampled)
 
 Workloads (--workload): grad_bucket (default: 268,435,456 bf16 values,
 512 MiB, 64 KiB chunks), pr1, fp32_grad, llama8b (290 buffers, batched),
@@ -67,6 +69,8 @@ def parse():
                     help="compress with the per-call arbitration for a link of this many GB/s (0: plain compress)")
     ap.add_argument("--sampled", action="store_true",
                     help="tables from each chunk's sample (uzip_compress_sampled): one read of the input")
+    ap.add_argument("--no-sampled-line", action="store_true",
+                    help="skip the second, shorter measurement with sampled tables that a full-table run appends")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum CPU-oracle time to accumulate")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     return ap.parse_args()
@@ -224,15 +228,15 @@ def main():
                         exposed_encode_permil=1000, exposed_decode_permil=1000, min_gain_permil=20)
         plans = torch.empty(4 * len(ts), dtype=torch.int64, device=dev)
 
-    def compress():
+    def compress(sampled=args.sampled):
         if pol is not None and batched:
             uz.compress_batched_arbitrated(ts, pol, cb, outs=outs, ws=ws, out_sizes=sizes, plans=plans)
         elif pol is not None:
             uz.compress_arbitrated(ts[0], pol, cb, out=outs[0], ws=ws, out_size=sizes, plan=plans)
         elif batched:
-            uz.compress_batched(ts, cb, outs=outs, ws=ws, out_sizes=sizes, sampled=args.sampled)
+            uz.compress_batched(ts, cb, outs=outs, ws=ws, out_sizes=sizes, sampled=sampled)
         else:
-            uz.compress(ts[0], cb, out=outs[0], ws=ws, out_size=sizes, sampled=args.sampled)
+            uz.compress(ts[0], cb, out=outs[0], ws=ws, out_size=sizes, sampled=sampled)
 
     def decompress():
         # in_bytes = capacity: the decoder validates the header's total against it
@@ -243,53 +247,61 @@ def main():
 
     print("# %d buffers, %d values, %.1f MB; warmup %d, steps %d" % (len(ts), n_total, in_bytes / 1e6, args.warmup,
                                                                       args.steps), file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
-        compress()
-        decompress()
-    torch.cuda.synchronize()
-
     K = args.steps
-    enc_ev = [(hip.event(), hip.event()) for _ in range(K)]
-    dec_ev = [(hip.event(), hip.event()) for _ in range(K)]
-    c_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
-    d_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(K):
-        uz.uzip_profile_set_events(enc_ev[k][0], enc_ev[k][1])
-        c_ev[k][0].record()
-        compress()
-        c_ev[k][1].record()
-        uz.uzip_profile_set_events(dec_ev[k][0], dec_ev[k][1])
-        d_ev[k][0].record()
-        decompress()
-        d_ev[k][1].record()
-    uz.uzip_profile_set_events(None, None)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_step = (t1 - t0) * 1e3 / K
-    comp_ms = sorted(a.elapsed_time(b) for a, b in c_ev)
-    dec_ms = sorted(a.elapsed_time(b) for a, b in d_ev)
-    enc_kernel_ms = sum(hip.elapsed_ms(a, b) for a, b in enc_ev) / K
-    dec_kernel_ms = sum(hip.elapsed_ms(a, b) for a, b in dec_ev) / K
-    for a, b in enc_ev + dec_ev:
-        hip.destroy(a)
-        hip.destroy(b)
 
-    # correctness of what was timed: bit-exact round trip, valid status
+    def timed(sampled):
+        """W warm-ups, then K timed steps: step time, whole-call times per
+        direction (torch events) and the main coding kernels' durations (HIP
+        events the library records on the launch stream)."""
+        for _ in range(args.warmup):
+            compress(sampled)
+            decompress()
+        torch.cuda.synchronize()
+        enc_ev = [(hip.event(), hip.event()) for _ in range(K)]
+        dec_ev = [(hip.event(), hip.event()) for _ in range(K)]
+        c_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+        d_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(K):
+            uz.uzip_profile_set_events(enc_ev[k][0], enc_ev[k][1])
+            c_ev[k][0].record()
+            compress(sampled)
+            c_ev[k][1].record()
+            uz.uzip_profile_set_events(dec_ev[k][0], dec_ev[k][1])
+            d_ev[k][0].record()
+            decompress()
+            d_ev[k][1].record()
+        uz.uzip_profile_set_events(None, None)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        res = ((t1 - t0) * 1e3 / K, sorted(a.elapsed_time(b) for a, b in c_ev), sorted(a.elapsed_time(b) for a, b in d_ev),
+               sum(hip.elapsed_ms(a, b) for a, b in enc_ev) / K, sum(hip.elapsed_ms(a, b) for a, b in dec_ev) / K)
+        for a, b in enc_ev + dec_ev:
+            hip.destroy(a)
+            hip.destroy(b)
+        return res
+
     iv = {1: torch.uint8, 2: torch.int16, 4: torch.int32}[eb]
-    st = status.cpu().tolist()
-    roundtrip_ok = all(s == 0 for s in st) and all(
-        torch.equal(a.view(iv), b.view(iv)) for a, b in zip(ts, backs))
+
+    def roundtrip_exact():
+        """correctness of what was timed: bit-exact round trip, valid status"""
+        return all(s == 0 for s in status.cpu().tolist()) and all(
+            torch.equal(a.view(iv), b.view(iv)) for a, b in zip(ts, backs))
+
+    def record_bytes(comp_sizes):
+        exp_offs = [((((64 + 8 * ((n + chunk_elems - 1) // chunk_elems + 1)) + 15) // 16 * 16 + rb * n) + 15) // 16 * 16
+                    for n in ns]
+        return exp_offs, sum(s - e for s, e in zip(comp_sizes, exp_offs))
+
+    ms_step, comp_ms, dec_ms, enc_kernel_ms, dec_kernel_ms = timed(args.sampled)
+    roundtrip_ok = roundtrip_exact()
     comp_sizes = sizes.cpu().tolist()
     comp_bytes = sum(comp_sizes)
     bound = entropy_bound(ts, chunk_elems)
 
     # algorithmic bytes per launch of the two coding kernels
-    chunks = sum((n + chunk_elems - 1) // chunk_elems for n in ns)
-    exp_offs = [((((64 + 8 * ((n + chunk_elems - 1) // chunk_elems + 1)) + 15) // 16 * 16 + rb * n) + 15) // 16 * 16
-                for n in ns]
-    rec_bytes = sum(s - e for s, e in zip(comp_sizes, exp_offs))
+    exp_offs, rec_bytes = record_bytes(comp_sizes)
     decisions = [p["decision"] for p in uz.plans_as_dicts(plans)] if pol is not None else []
     # a RAW plan's k_encode only splits (k_compact writes the RAW records)
     raw_planned = sum(n for n, dcs in zip(ns, decisions) if dcs != uz.UZIP_PLAN_CODED)
@@ -356,6 +368,34 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
+    if pol is None and not args.sampled and not args.no_sampled_line:
+        # the same workload with sampled tables (uzip_compress_sampled), a
+        # second and separate measurement: the headline figures above are the
+        # full-table ones
+        s_step, s_comp, s_dec, s_enc, s_decm = timed(True)
+        s_ok = roundtrip_exact()
+        s_sizes = sizes.cpu().tolist()
+        s_bytes = sum(s_sizes)
+        _, s_rec = record_bytes(s_sizes)
+        s_enc_b = n_total * eb + n_total * rb + s_rec
+        s_dec_b = n_total * rb + s_rec + sum(64 + 8 * ((n + chunk_elems - 1) // chunk_elems + 1) for n in ns) + n_total * eb
+        s_match = None
+        if not args.no_cpu_baseline:
+            import oracle
+            import workloads as W
+            s_match = bool(np.array_equal(oracle.compress_sampled(code, W.bits_numpy(ts[0]), cb),
+                                          outs[0][:s_sizes[0]].cpu().numpy()))
+        line["sampled_tables"] = {
+            "value": round(in_bytes / (s_step * 1e-3) / 1e9, 2),
+            "compress_gbps": round(in_bytes / (s_comp[len(s_comp) // 2] * 1e-3) / 1e9, 2),
+            "decompress_gbps": round(in_bytes / (s_dec[len(s_dec) // 2] * 1e-3) / 1e9, 2),
+            "ratio": round(s_bytes / in_bytes, 5), "ratio_over_bound": round(s_bytes / bound, 5),
+            "k_encode_ms": round(s_enc, 4), "k_decode_ms": round(s_decm, 4),
+            "k_encode_frac": round(s_enc_b / (s_enc * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "k_decode_frac": round(s_dec_b / (s_decm * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "roundtrip_bit_exact": s_ok, "oracle_bytes_match_first_buffer": s_match}
+        roundtrip_ok = roundtrip_ok and s_ok
+        oracle_match = oracle_match if s_match is not False else False
     if pol is not None:
         line["config"]["arbitration"] = {f: getattr(pol, f) for f, _ in pol._fields_}
         line["plans"] = {"coded": decisions.count(0), "raw": decisions.count(1), "raw_small": decisions.count(2),
