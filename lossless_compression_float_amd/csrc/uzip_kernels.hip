@@ -1348,8 +1348,10 @@ __global__ __launch_bounds__(256) void k_raw_frame(EncParams p) {
 // the final index entry, the header, the zero gaps and the compressed size
 // (NCCLZ Sec. IV-D2: self-describing frames).  A wave only waits for tile
 // leaders in workgroups with lower tickets, or in its own workgroup, all of
-// which already run.
-constexpr uint32_t kCompactPairs = 4;
+// which already run.  Eight pairs per 1024-thread workgroup: fewer tickets and
+// workgroup launches than four or two per workgroup (gradient bucket: the
+// compaction and its launch gaps ≈10 µs shorter than with four).
+constexpr uint32_t kCompactPairs = 8;
 
 template <int DT>
 __global__ __launch_bounds__(128 * kCompactPairs) void k_compact(EncParams p) {
