@@ -6,7 +6,8 @@ path: split, histogram, table, rANS encode, size scan, compaction, validation,
 rANS decode and re-interleave), inputs already resident in HBM.  Prints one
 JSON line:
 
-  value          uncompressed GB/s of the round trip (input bytes / step time)
+  value          uncompressed GB/s of the round trip (input bytes / step time),
+                 after untimed settle round trips (--settle-seconds) and W warm-ups
   compress_gbps / decompress_gbps   per direction (HIP events on the stream)
   ratio          compressed / original, and its entropy bound
   roofline       dominant kernel: algorithmic bytes per launch / its average
@@ -69,6 +70,9 @@ def parse():
                     help="compress with the per-call arbitration for a link of this many GB/s (0: plain compress)")
     ap.add_argument("--sampled", action="store_true",
                     help="tables from each chunk's sample (uzip_compress_sampled): one read of the input")
+    ap.add_argument("--settle-seconds", type=float, default=0.5,
+                    help="untimed round trips before the warm-up steps, until this much time has passed: the GPU "
+                         "reaches its steady clocks only after a fraction of a second of sustained work")
     ap.add_argument("--no-sampled-line", action="store_true",
                     help="skip the second, shorter measurement with sampled tables that a full-table run appends")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum CPU-oracle time to accumulate")
@@ -249,6 +253,18 @@ def main():
                                                                       args.steps), file=sys.stderr, flush=True)
     K = args.steps
 
+    # settle: untimed round trips until the GPU has run for --settle-seconds
+    # (measured: with 3 warm-up steps alone the gradient bucket's kernels run
+    # 5-10% slower than in steady state)
+    settle_steps, t_settle = 0, time.perf_counter()
+    while time.perf_counter() - t_settle < args.settle_seconds:
+        for _ in range(4):
+            compress()
+            decompress()
+        settle_steps += 4
+        torch.cuda.synchronize()
+    settle_s = time.perf_counter() - t_settle
+
     def timed(sampled):
         """W warm-ups, then K timed steps: step time, whole-call times per
         direction (torch events) and the main coding kernels' durations (HIP
@@ -346,6 +362,7 @@ def main():
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
+        "settle": {"steps": settle_steps, "seconds": round(settle_s, 3)},
         "ms_per_step": round(ms_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
