@@ -13,6 +13,11 @@
 //                the input, which the cache still holds), placing each step's
 //                renormalisation words by wave ballot + lane rank.  The record
 //                is built in a workspace slot (words filled from its end).
+//                With tables from each chunk's sample (k_encode<DT, true>;
+//                UCCL-Zip Sec. 3, the text on Figure 5) there is no counting
+//                pass: the sample fixes the table and one backward pass
+//                splits, stores the sign+mantissa bytes and codes, unseen
+//                exponents going to the record's escape list.
 //   k_compact    one wave per record, workgroups in ticket order: the record
 //                offsets (an exclusive scan of the record sizes: tile sums
 //                plus a decoupled look-back over tiles), the records copied
@@ -22,9 +27,13 @@
 //   k_prepare    zeroes the look-back words; writes the buffers of empty inputs.
 // Decompression (NCCLZ Algorithm 2: validate the header, then decode):
 //   k_dec_validate  one thread per buffer checks the buffer header.
+//   k_dec_scan      (batched calls) pair offsets, and which frame kinds occur.
 //   k_decode        one half-wave per chunk: validates the record, builds the
 //                   slot->symbol table in LDS, runs the rANS decoder forward
-//                   and merges each exponent with its sign+mantissa bytes.
+//                   and merges each exponent with its sign+mantissa bytes;
+//                   k_decode<DT, true> reads sampled-table frames (escapes).
+//                   Both variants are launched; each leaves at once unless
+//                   the call holds a valid frame of its kind.
 //
 // Nothing here is a dense contraction: all arithmetic is 32-bit integer and
 // bit manipulation on the vector ALU (plus one exact binary64 multiply per
