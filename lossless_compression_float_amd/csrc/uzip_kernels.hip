@@ -828,8 +828,8 @@ __global__ __launch_bounds__(64) void k_encode(EncParams p) {
     // One step; CAREFUL steps rebuild the lane masks and check the room
     // (a ragged chunk end, or words close to the RAW size), the others use
     // the block's loop-invariant mask.
-    // (FAST steps with sampled tables get the exponent from the block's staging
-    // area, have_ex; the others extract it from the value v)
+    // (FAST steps get the exponent from the block's staging area, have_ex;
+    // CAREFUL steps extract it from the value v)
     auto step = [&](int32_t b, int k, uint32_t v, bool careful, uint64_t act, bool have_ex = false,
                     uint32_t ex_in = 0u) __attribute__((always_inline)) {
         const uint32_t t = (uint32_t)b * 8 + k;
@@ -904,208 +904,168 @@ __global__ __launch_bounds__(64) void k_encode(EncParams p) {
         return (!alive0 || (vals0 >= tend && (end0 - r0) + 256 <= wcap0)) &&
                (!alive1 || (vals1 >= tend && (end1 - r1) + 256 <= wcap1));
     };
-    // Block values: lane lj's values of steps 8b .. 8b + 7 (past the pair: zeros).
-    // Runs of FAST blocks are software-pipelined: the next block's values are
-    // loaded while a block is coded.  One counter tracks loads and stores in
-    // issue order, so the compiler's wait for those values, placed after the
-    // block's word stores, would also wait for the stores.  The loads are
-    // therefore issued in asm and waited for explicitly: between the loads
-    // and their wait lies only the coding of one FAST block, straight-line
-    // code with exactly eight word stores, so at most eight operations may
-    // remain outstanding.  Every branch and loop edge comes after a wait, so
-    // no register with a load in flight is ever copied (a test checks the
+    // A FAST block is read as whole units, lane lj taking values 8lj .. 8lj + 7
+    // of its half's 256 (one 128-bit load; fp32 two, fp8 one 64-bit), and
+    // staged: the lane writes their eight exponents to the half's 256-byte
+    // staging area in LDS, from which step k of lane j reads byte 32k + j
+    // (value 256b + 32k + j, the value that step codes); with sampled tables
+    // it also stores their sign+mantissa bytes as one unit.  (Measured against
+    // one 16-bit load per value and step in the full-table encoder: 0.7% faster
+    // for bf16, 1.5% fp16, 3-4.5% fp8.)
+    // Runs of FAST blocks are software-pipelined: the next block's unit is
+    // loaded while a block is coded, and staged after its wait.  One counter
+    // tracks loads and stores in issue order, so the compiler's wait for those
+    // values, placed after the block's word stores, would also wait for the
+    // stores.  The loads are therefore issued in asm and waited for
+    // explicitly: between the loads and their wait lies only the coding of one
+    // FAST block, straight-line code with exactly eight word stores (and the
+    // unit's sign+mantissa stores), so at most that many operations may remain
+    // outstanding.  Every branch and loop edge comes after a wait, so no
+    // register with a load in flight is ever copied (a test checks the
     // generated code for this).  Other blocks use ordinary loads.
-#define UZIP_WAIT_BLOCK(N, V)                                                                                         \
-    asm volatile("s_waitcnt vmcnt(%8)" : "+v"(V[0]), "+v"(V[1]), "+v"(V[2]), "+v"(V[3]), "+v"(V[4]), "+v"(V[5]), \
-                 "+v"(V[6]), "+v"(V[7]) : "i"(N))
-    if constexpr (!S) {
-        auto fast_block = [&](int32_t b, const uint32_t(&V)[8]) __attribute__((always_inline)) {
-            const uint64_t act = (alive0 ? 0xFFFFFFFFull : 0ull) | (alive1 ? kHighHalf : 0ull);
+    // With sampled tables the unit loads carry the non-temporal hint: each
+    // value is read once (measured: about 2% faster than the default policy on
+    // the gradient bucket; the same hint on the sign+mantissa stores, on the
+    // full-table encoder's loads, which re-read what pass 1 read, or on the
+    // decoder's loads was slower).
+    uint8_t *stage = reinterpret_cast<uint8_t *>(lds) + h * 256;  // (the keys' words, free in this pass)
+    constexpr uint32_t NU = EB == 4 ? 2 : 1;  // loads per unit (fp8: one 64-bit)
+    using UnitT = typename std::conditional<EB == 1, u32x2, u32x4>::type;
+    auto asm_load_unit = [&](int32_t bb, UnitT(&U)[2]) __attribute__((always_inline)) {
+        const uint32_t o = bb >= 0 ? in0 + ((uint32_t)bb * 256 + 8 * lj) * EB : kOutOfRange;
+        if constexpr (EB == 1 && S) {
+            asm volatile("buffer_load_dwordx2 %0, %1, %2, 0 offen nt" : "=v"(U[0]) : "v"(o), "s"(rin));
+        } else if constexpr (EB == 1) {
+            asm volatile("buffer_load_dwordx2 %0, %1, %2, 0 offen" : "=v"(U[0]) : "v"(o), "s"(rin));
+        } else if constexpr (S) {
 #pragma unroll
-            for (int k = 7; k >= 0; --k) step(b, k, V[k], false, act);
-        };
-        auto asm_load_block = [&](int32_t bb, uint32_t(&V)[8]) __attribute__((always_inline)) {
-            const uint32_t o = bb >= 0 ? in0 + ((uint32_t)bb * 8 * 32 + lj) * EB : kOutOfRange;
+            for (uint32_t u = 0; u < NU; ++u)
+                asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen offset:%3 nt" : "=v"(U[u]) : "v"(o), "s"(rin), "i"(16 * u));
+        } else {
+#pragma unroll
+            for (uint32_t u = 0; u < NU; ++u)
+                asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen offset:%3" : "=v"(U[u]) : "v"(o), "s"(rin), "i"(16 * u));
+        }
+    };
+    // the unit's sign+mantissa bytes (bf16, fp16: 8; fp32: 24), stored by store_sm
+    constexpr uint32_t kSmStores = !S || R == 0 ? 0 : R == 1 ? 1 : 2;
+    auto stage_unit = [&](const UnitT(&U)[2], uint32_t(&SM)[6]) __attribute__((always_inline)) {
+        uint32_t e0, e1;  // the eight exponents, value order
+        if constexpr (DT == 1 || DT == 3) {
+            // low and high bytes of four values at once
+            const uint32_t lo0 = __builtin_amdgcn_perm(U[0].y, U[0].x, 0x06040200u);
+            const uint32_t hi0 = __builtin_amdgcn_perm(U[0].y, U[0].x, 0x07050301u);
+            const uint32_t lo1 = __builtin_amdgcn_perm(U[0].w, U[0].z, 0x06040200u);
+            const uint32_t hi1 = __builtin_amdgcn_perm(U[0].w, U[0].z, 0x07050301u);
+            uint32_t s0 = lo0, s1 = lo1;
+            e0 = hi0;
+            e1 = hi1;
+            if (DT == 1) {  // sign = bit 7 of the high byte, exponent = its bits 0-6 and bit 7 of the low byte
+                s0 = (hi0 & 0x80808080u) | (lo0 & 0x7F7F7F7Fu);
+                s1 = (hi1 & 0x80808080u) | (lo1 & 0x7F7F7F7Fu);
+                e0 = ((hi0 << 1) & 0xFEFEFEFEu) | ((lo0 >> 7) & 0x01010101u);
+                e1 = ((hi1 << 1) & 0xFEFEFEFEu) | ((lo1 >> 7) & 0x01010101u);
+            }
+            SM[0] = s0;
+            SM[1] = s1;
+        } else if constexpr (DT == 2) {
+            const uint32_t w[8] = {U[0].x, U[0].y, U[0].z, U[0].w, U[1].x, U[1].y, U[1].z, U[1].w};
+            uint32_t sm[8], ex[8];
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
-                if (EB == 1)
-                    asm volatile("buffer_load_ubyte %0, %1, %2, 0 offen offset:%3" : "=v"(V[k]) : "v"(o), "s"(rin), "i"(k * 32 * EB));
-                else if (EB == 2)
-                    asm volatile("buffer_load_ushort %0, %1, %2, 0 offen offset:%3" : "=v"(V[k]) : "v"(o), "s"(rin), "i"(k * 32 * EB));
-                else
-                    asm volatile("buffer_load_dword %0, %1, %2, 0 offen offset:%3" : "=v"(V[k]) : "v"(o), "s"(rin), "i"(k * 32 * EB));
+                sm[k] = ((w[k] >> 8) & 0x800000u) | (w[k] & 0x7FFFFFu);
+                ex[k] = (w[k] >> 23) & 0xFFu;
             }
-        };
-        for (int32_t b = (int32_t)nblk - 1; b >= 0;) {
-            if (!block_fast(b)) {
-                const uint32_t o = in0 + ((uint32_t)b * 8 * 32 + lj) * EB;
-                uint32_t V[8];
-#pragma unroll
-                for (int k = 0; k < 8; ++k) V[k] = bld_value<DT>(rin, o + k * 32 * EB);
-#pragma unroll
-                for (int k = 7; k >= 0; --k) step(b, k, V[k], true, 0ull);
-                --b;
-                continue;
-            }
-            uint32_t VA[8], VB[8];
-            asm_vmem_fence();
-            asm_load_block(b, VA);
-            UZIP_WAIT_BLOCK(0, VA);
-            for (;;) {
-                asm_load_block(b - 1, VB);
-                fast_block(b, VA);
-                UZIP_WAIT_BLOCK(8, VB);
-                if (--b < 0 || !block_fast(b)) break;
-                asm_load_block(b - 1, VA);
-                fast_block(b, VB);
-                UZIP_WAIT_BLOCK(8, VA);
-                if (--b < 0 || !block_fast(b)) break;
-            }
+            e0 = ex[0] | (ex[1] << 8) | (ex[2] << 16) | (ex[3] << 24);
+            e1 = ex[4] | (ex[5] << 8) | (ex[6] << 16) | (ex[7] << 24);
+            SM[0] = sm[0] | (sm[1] << 24);
+            SM[1] = (sm[1] >> 8) | (sm[2] << 16);
+            SM[2] = (sm[2] >> 16) | (sm[3] << 8);
+            SM[3] = sm[4] | (sm[5] << 24);
+            SM[4] = (sm[5] >> 8) | (sm[6] << 16);
+            SM[5] = (sm[6] >> 16) | (sm[7] << 8);
+        } else {  // fp8: the byte is the symbol, nothing raw
+            e0 = U[0].x;
+            e1 = U[0].y;
         }
-    } else {
-        // Sampled tables: a FAST block is read as whole units, lane lj taking
-        // values 8lj .. 8lj + 7 of its half's 256 (one 128-bit load; fp32
-        // two, fp8 one 64-bit), and staged: the lane stores their sign+mantissa
-        // bytes as one unit and writes their eight exponents to the half's
-        // 256-byte staging area in LDS, from which step k of lane j reads byte
-        // 32k + j.  The next block's unit is loaded (asm) while a block is
-        // coded, as above, and staged after its wait.  The unit loads carry the
-        // non-temporal hint: each value is read once (measured: about 2% faster
-        // than the default policy on the gradient bucket; the same hint on the
-        // sign+mantissa stores, on the full-table encoder's loads or on the
-        // decoder's loads was slower).
-        uint8_t *stage = reinterpret_cast<uint8_t *>(lds) + h * 256;  // (the keys' words, free in this pass)
-        constexpr uint32_t NU = EB == 4 ? 2 : 1;  // loads per unit (fp8: one 64-bit)
-        using UnitT = typename std::conditional<EB == 1, u32x2, u32x4>::type;
-        auto asm_load_unit = [&](int32_t bb, UnitT(&U)[2]) __attribute__((always_inline)) {
-            const uint32_t o = bb >= 0 ? in0 + ((uint32_t)bb * 256 + 8 * lj) * EB : kOutOfRange;
-            if constexpr (EB == 1) {
-                asm volatile("buffer_load_dwordx2 %0, %1, %2, 0 offen nt" : "=v"(U[0]) : "v"(o), "s"(rin));
-            } else {
+        asm volatile("" ::: "memory");  // (after the last block's reads of the area)
+        *reinterpret_cast<u32x2 *>(stage + 8 * lj) = u32x2{e0, e1};
+    };
+    // (issued after the next unit's loads, so that the wait for those loads
+    // does not also wait for this store)
+    auto store_sm = [&](int32_t bb, const uint32_t(&SM)[6]) __attribute__((always_inline)) {
+        const uint32_t so = ((h ? vals0 : 0u) + (uint32_t)bb * 256 + 8 * lj) * R;  // past the pair: dropped
+        if constexpr (!S) {
+            (void)so;
+        } else if constexpr (R == 1) {
+            __builtin_amdgcn_raw_buffer_store_b64(u32x2{SM[0], SM[1]}, rsm2, (int)so, 0, 0);
+        } else if constexpr (R == 3) {
+            __builtin_amdgcn_raw_buffer_store_b96(u32x3{SM[0], SM[1], SM[2]}, rsm2, (int)so, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b96(u32x3{SM[3], SM[4], SM[5]}, rsm2, (int)(so + 12), 0, 0);
+        }
+    };
+    auto fast_block = [&](int32_t b) __attribute__((always_inline)) {
+        const uint64_t act = (alive0 ? 0xFFFFFFFFull : 0ull) | (alive1 ? kHighHalf : 0ull);
+        asm volatile("" ::: "memory");  // (after the staging writes)
+        uint32_t E[8];
 #pragma unroll
-                for (uint32_t u = 0; u < NU; ++u)
-                    asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen offset:%3 nt" : "=v"(U[u]) : "v"(o), "s"(rin), "i"(16 * u));
-            }
-        };
-        // the unit's sign+mantissa bytes (bf16, fp16: 8; fp32: 24), stored by store_sm
-        constexpr uint32_t kSmStores = R == 0 ? 0 : R == 1 ? 1 : 2;
-        auto stage_unit = [&](const UnitT(&U)[2], uint32_t(&SM)[6]) __attribute__((always_inline)) {
-            uint32_t e0, e1;  // the eight exponents, value order
-            if constexpr (DT == 1 || DT == 3) {
-                // low and high bytes of four values at once
-                const uint32_t lo0 = __builtin_amdgcn_perm(U[0].y, U[0].x, 0x06040200u);
-                const uint32_t hi0 = __builtin_amdgcn_perm(U[0].y, U[0].x, 0x07050301u);
-                const uint32_t lo1 = __builtin_amdgcn_perm(U[0].w, U[0].z, 0x06040200u);
-                const uint32_t hi1 = __builtin_amdgcn_perm(U[0].w, U[0].z, 0x07050301u);
-                uint32_t s0 = lo0, s1 = lo1;
-                e0 = hi0;
-                e1 = hi1;
-                if (DT == 1) {  // sign = bit 7 of the high byte, exponent = its bits 0-6 and bit 7 of the low byte
-                    s0 = (hi0 & 0x80808080u) | (lo0 & 0x7F7F7F7Fu);
-                    s1 = (hi1 & 0x80808080u) | (lo1 & 0x7F7F7F7Fu);
-                    e0 = ((hi0 << 1) & 0xFEFEFEFEu) | ((lo0 >> 7) & 0x01010101u);
-                    e1 = ((hi1 << 1) & 0xFEFEFEFEu) | ((lo1 >> 7) & 0x01010101u);
-                }
-                SM[0] = s0;
-                SM[1] = s1;
-            } else if constexpr (DT == 2) {
-                const uint32_t w[8] = {U[0].x, U[0].y, U[0].z, U[0].w, U[1].x, U[1].y, U[1].z, U[1].w};
-                uint32_t sm[8], ex[8];
+        for (int k = 0; k < 8; ++k) E[k] = stage[32 * k + lj];
 #pragma unroll
-                for (int k = 0; k < 8; ++k) {
-                    sm[k] = ((w[k] >> 8) & 0x800000u) | (w[k] & 0x7FFFFFu);
-                    ex[k] = (w[k] >> 23) & 0xFFu;
-                }
-                e0 = ex[0] | (ex[1] << 8) | (ex[2] << 16) | (ex[3] << 24);
-                e1 = ex[4] | (ex[5] << 8) | (ex[6] << 16) | (ex[7] << 24);
-                SM[0] = sm[0] | (sm[1] << 24);
-                SM[1] = (sm[1] >> 8) | (sm[2] << 16);
-                SM[2] = (sm[2] >> 16) | (sm[3] << 8);
-                SM[3] = sm[4] | (sm[5] << 24);
-                SM[4] = (sm[5] >> 8) | (sm[6] << 16);
-                SM[5] = (sm[6] >> 16) | (sm[7] << 8);
-            } else {  // fp8: the byte is the symbol, nothing raw
-                e0 = U[0].x;
-                e1 = U[0].y;
-            }
-            asm volatile("" ::: "memory");  // (after the last block's reads of the area)
-            *reinterpret_cast<u32x2 *>(stage + 8 * lj) = u32x2{e0, e1};
-        };
-        // (issued after the next unit's loads, so that the wait for those loads
-        // does not also wait for this store)
-        auto store_sm = [&](int32_t bb, const uint32_t(&SM)[6]) __attribute__((always_inline)) {
-            const uint32_t so = ((h ? vals0 : 0u) + (uint32_t)bb * 256 + 8 * lj) * R;  // past the pair: dropped
-            if constexpr (R == 1) {
-                __builtin_amdgcn_raw_buffer_store_b64(u32x2{SM[0], SM[1]}, rsm2, (int)so, 0, 0);
-            } else if constexpr (R == 3) {
-                __builtin_amdgcn_raw_buffer_store_b96(u32x3{SM[0], SM[1], SM[2]}, rsm2, (int)so, 0, 0);
-                __builtin_amdgcn_raw_buffer_store_b96(u32x3{SM[3], SM[4], SM[5]}, rsm2, (int)(so + 12), 0, 0);
-            }
-        };
-        auto fast_block_s = [&](int32_t b) __attribute__((always_inline)) {
-            const uint64_t act = (alive0 ? 0xFFFFFFFFull : 0ull) | (alive1 ? kHighHalf : 0ull);
-            asm volatile("" ::: "memory");  // (after the staging writes)
-            uint32_t E[8];
-#pragma unroll
-            for (int k = 0; k < 8; ++k) E[k] = stage[32 * k + lj];
-#pragma unroll
-            for (int k = 7; k >= 0; --k) step(b, k, 0u, false, act, true, E[k]);
-        };
-        // escapes of a FAST block, placed after the block from the staged exponents, last first
-        auto block_escapes_s = [&]() __attribute__((always_inline)) {
-            const uint64_t act = (alive0 ? 0xFFFFFFFFull : 0ull) | (alive1 ? kHighHalf : 0ull);
-            for (int k = 7; k >= 0; --k) {
-                if (((escsteps >> k) & 1u) == 0) continue;
-                const uint32_t ex = stage[32 * k + lj];
-                const uint32_t cy = *reinterpret_cast<const uint32_t *>(reinterpret_cast<const uint8_t *>(tab) + (ex << 4) + 4);
-                const uint64_t escm = lanes_eq(cy, kEscSlot) & act;
-                if (escm) put_escapes(escm, ex);
-            }
-        };
+        for (int k = 7; k >= 0; --k) step(b, k, 0u, false, act, true, E[k]);
+    };
+    // escapes of a FAST block, placed after the block from the staged exponents, last first
+    auto block_escapes_s = [&]() __attribute__((always_inline)) {
+        const uint64_t act = (alive0 ? 0xFFFFFFFFull : 0ull) | (alive1 ? kHighHalf : 0ull);
+        for (int k = 7; k >= 0; --k) {
+            if (((escsteps >> k) & 1u) == 0) continue;
+            const uint32_t ex = stage[32 * k + lj];
+            const uint32_t cy = *reinterpret_cast<const uint32_t *>(reinterpret_cast<const uint8_t *>(tab) + (ex << 4) + 4);
+            const uint64_t escm = lanes_eq(cy, kEscSlot) & act;
+            if (escm) put_escapes(escm, ex);
+        }
+    };
 #define UZIP_WAIT_UNIT(N, U) asm volatile("s_waitcnt vmcnt(%2)" : "+v"(U[0]), "+v"(U[1]) : "i"(N))
-        for (int32_t b = (int32_t)nblk - 1; b >= 0;) {
-            if (!block_fast(b)) {
-                const uint32_t o = in0 + ((uint32_t)b * 8 * 32 + lj) * EB;
-                uint32_t V[8];
+    for (int32_t b = (int32_t)nblk - 1; b >= 0;) {
+        if (!block_fast(b)) {
+            const uint32_t o = in0 + ((uint32_t)b * 8 * 32 + lj) * EB;
+            uint32_t V[8];
 #pragma unroll
-                for (int k = 0; k < 8; ++k) V[k] = bld_value<DT>(rin, o + k * 32 * EB);
+            for (int k = 0; k < 8; ++k) V[k] = bld_value<DT>(rin, o + k * 32 * EB);
 #pragma unroll
-                for (int k = 7; k >= 0; --k) step(b, k, V[k], true, 0ull);
-                --b;
-                continue;
-            }
-            UnitT UA[2] = {}, UB[2] = {};
-            uint32_t SM[6] = {0, 0, 0, 0, 0, 0};
-            asm_vmem_fence();
-            asm_load_unit(b, UA);
-            UZIP_WAIT_UNIT(0, UA);
-            stage_unit(UA, SM);
-            for (;;) {
-                asm_load_unit(b - 1, UB);
-                store_sm(b, SM);
-                fast_block_s(b);
-                UZIP_WAIT_UNIT(8 + kSmStores, UB);
-                if (escsteps) {
-                    block_escapes_s();
-                    escsteps = 0;
-                }
-                if (--b < 0 || !block_fast(b)) break;
-                stage_unit(UB, SM);
-                asm_load_unit(b - 1, UA);
-                store_sm(b, SM);
-                fast_block_s(b);
-                UZIP_WAIT_UNIT(8 + kSmStores, UA);
-                if (escsteps) {
-                    block_escapes_s();
-                    escsteps = 0;
-                }
-                if (--b < 0 || !block_fast(b)) break;
-                stage_unit(UA, SM);
-            }
+            for (int k = 7; k >= 0; --k) step(b, k, V[k], true, 0ull);
+            --b;
+            continue;
         }
-#undef UZIP_WAIT_UNIT
+        UnitT UA[2] = {}, UB[2] = {};
+        uint32_t SM[6] = {0, 0, 0, 0, 0, 0};
+        asm_vmem_fence();
+        asm_load_unit(b, UA);
+        UZIP_WAIT_UNIT(0, UA);
+        stage_unit(UA, SM);
+        for (;;) {
+            asm_load_unit(b - 1, UB);
+            store_sm(b, SM);
+            fast_block(b);
+            UZIP_WAIT_UNIT(8 + kSmStores, UB);
+            if (escsteps) {
+                block_escapes_s();
+                escsteps = 0;
+            }
+            if (--b < 0 || !block_fast(b)) break;
+            stage_unit(UB, SM);
+            asm_load_unit(b - 1, UA);
+            store_sm(b, SM);
+            fast_block(b);
+            UZIP_WAIT_UNIT(8 + kSmStores, UA);
+            if (escsteps) {
+                block_escapes_s();
+                escsteps = 0;
+            }
+            if (--b < 0 || !block_fast(b)) break;
+            stage_unit(UA, SM);
+        }
     }
-#undef UZIP_WAIT_BLOCK
+#undef UZIP_WAIT_UNIT
 
     // ---- the record's fixed part into the slot (the words are already at its
     // end); a RAW record gets its header only: k_compact takes its exponents
