@@ -10,18 +10,25 @@ JSON line:
                  after untimed settle round trips (--settle-seconds) and W warm-ups
   compress_gbps / decompress_gbps   per direction (HIP events on the stream)
   ratio          compressed / original, and its entropy bound
+  latency_ms     per call (whole call, HIP events on the stream), median and
+                 minimum, per direction
   roofline       dominant kernel: algorithmic bytes per launch / its average
-                 duration (HIP events around the kernel, recorded by the
-                 library on the launch stream) against the 8 TB/s HBM peak
-  cpu_baseline   the CPU oracle (single thread) on a bounded sample of the
-                 same bytes; its output also serves as a byte-for-byte check
+                 duration (two caller events the library records on the
+                 launch stream around that kernel, uzip_*_batched_timed)
+                 against the 8 TB/s HBM peak
+  cpu_baseline   the CPU oracle (single thread, pinned to one core) on a
+                 bounded sample of the same bytes, per direction; its output
+                 also serves as a byte-for-byte check
   sampled_tables (full-table runs) the same workload measured again with
                  tables from each chunk's sample (uzip_compress_sampled)
 
-Workloads (--workload): grad_bucket (default: 268,435,456 bf16 values,
-512 MiB, 64 KiB chunks), pr1, fp32_grad, llama8b (290 buffers, batched),
-small_batch (4,096 buffers, batched), fp16_act (268,435,456 fp16 values),
-fp8_e4m3 and fp8_e5m2 (268,435,456 block-scaled fp8 weights each).
+Workloads (--workload): llama8b (default: the Llama-3-8B-shaped bf16 weight
+set, 290 buffers, 16.06 GB, one batched call per direction), grad_bucket
+(268,435,456 bf16 values, 512 MiB), pr1, fp32_grad, small_batch (4,096
+buffers, batched), fp16_act (268,435,456 fp16 values), fp8_e4m3 and fp8_e5m2
+(268,435,456 block-scaled fp8 weights each).  Every workload goes through the
+batched entry points (a one-buffer call writes what the single-buffer call
+writes).
 """
 from __future__ import annotations
 
@@ -62,7 +69,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="grad_bucket",
+    ap.add_argument("--workload", default="llama8b",
                     choices=["grad_bucket", "pr1", "fp32_grad", "llama8b", "small_batch", "fp16_act", "fp8_e4m3",
                              "fp8_e5m2"])
     ap.add_argument("--chunk-bytes", type=int, default=0, help="uncompressed chunk size (0: the dtype's default)")
@@ -75,7 +82,8 @@ def parse():
                          "reaches its steady clocks only after a fraction of a second of sustained work")
     ap.add_argument("--no-sampled-line", action="store_true",
                     help="skip the second, shorter measurement with sampled tables that a full-table run appends")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum CPU-oracle time to accumulate")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="minimum CPU-oracle time to accumulate per direction")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     return ap.parse_args()
 
@@ -147,39 +155,20 @@ def make_workload(name, dev):
     return ts, desc, batched
 
 
-def entropy_bound(ts, chunk_elems):
-    """Sum over chunks of (raw sign+mantissa bytes + n_i * H_i / 8): the size
-    an ideal per-chunk exponent coder would reach (computed with torch)."""
-    import torch
-    total = 0.0
-    for t in ts:
-        n = t.numel()
-        if n == 0:
-            continue
-        if t.dtype == torch.bfloat16:
-            e = (t.view(torch.int16).to(torch.int32) >> 7) & 0xFF
-            r = 1
-        elif t.dtype == torch.float16:
-            e = (t.view(torch.int16).to(torch.int32) >> 8) & 0xFF
-            r = 1
-        elif t.dtype == torch.float32:
-            e = (t.view(torch.int32) >> 23) & 0xFF
-            r = 3
-        else:
-            e = t.view(torch.uint8)
-            r = 0
-        C = (n + chunk_elems - 1) // chunk_elems
-        for c0 in range(0, C, 4096):  # slices of chunks keep the index tensor small
-            c1 = min(C, c0 + 4096)
-            seg = e[c0 * chunk_elems:min(n, c1 * chunk_elems)].to(torch.int64)
-            cid = torch.arange(seg.numel(), device=seg.device) // chunk_elems
-            cnt = torch.bincount(cid * 256 + seg, minlength=(c1 - c0) * 256).view(c1 - c0, 256).double()
-            tot = cnt.sum(1, keepdim=True)
-            p = torch.where(cnt > 0, cnt / tot, torch.ones_like(cnt))
-            bits = -(cnt * torch.log2(p)).sum()
-            total += float(bits) / 8.0
-        total += r * n
-    return total
+def entropy_bound(ts, code, chunk_bytes):
+    """The oracle's entropy bound (sum over chunks of the raw bytes plus
+    n_i H_i / 8), buffer by buffer on host copies, 16 buffers at a time (the
+    oracle is plain C called through ctypes, which releases the GIL)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import oracle
+    import workloads as W
+
+    def one(t):
+        return oracle.entropy_bound(code, W.bits_numpy(t), chunk_bytes) if t.numel() else 0.0
+
+    with ThreadPoolExecutor(max_workers=16) as pool:
+        return sum(pool.map(one, ts))
 
 
 def main():
@@ -214,14 +203,21 @@ def main():
         sys.exit("invalid --chunk-bytes %d" % args.chunk_bytes)
     outs = [torch.empty(c, dtype=torch.uint8, device=dev) for c in caps]
     backs = [torch.empty(n, dtype=dtype, device=dev) for n in ns]
-    if batched:
-        ws = uz.workspace(uz.uzip_workspace_size_batched(code, ns, cb), dev)
-        sizes = torch.empty(len(ts), dtype=torch.int64, device=dev)
-        status = torch.empty(len(ts), dtype=torch.int32, device=dev)
-    else:
-        ws = uz.workspace(uz.uzip_workspace_size(code, ns[0], cb), dev)
-        sizes = torch.empty(1, dtype=torch.int64, device=dev)
-        status = torch.empty(1, dtype=torch.int32, device=dev)
+    ws = uz.workspace(uz.uzip_workspace_size_batched(code, ns, cb), dev)
+    sizes = torch.empty(len(ts), dtype=torch.int64, device=dev)
+    status = torch.empty(len(ts), dtype=torch.int32, device=dev)
+
+    L = uz.lib()
+    stream = torch.cuda.current_stream().cuda_stream
+    # the calls' host arrays, built once (what a caller moving the same set of
+    # buffers every step keeps); the library builds and uploads its device
+    # descriptors on every call
+    a_in = uz._ptrs([t.data_ptr() if t.numel() else 0 for t in ts])
+    a_n = uz._sizes(ns)
+    a_out = uz._ptrs([o.data_ptr() for o in outs])
+    a_cap = uz._sizes([o.numel() for o in outs])
+    a_inb = uz._sizes(caps)  # decompress: capacity readable; the header's total is validated against it
+    a_back = uz._ptrs([b.data_ptr() if b.numel() else 0 for b in backs])
 
     pol = None
     if args.link_gbps > 0:
@@ -232,22 +228,21 @@ def main():
                         exposed_encode_permil=1000, exposed_decode_permil=1000, min_gain_permil=20)
         plans = torch.empty(4 * len(ts), dtype=torch.int64, device=dev)
 
-    def compress(sampled=args.sampled):
-        if pol is not None and batched:
-            uz.compress_batched_arbitrated(ts, pol, cb, outs=outs, ws=ws, out_sizes=sizes, plans=plans)
-        elif pol is not None:
-            uz.compress_arbitrated(ts[0], pol, cb, out=outs[0], ws=ws, out_size=sizes, plan=plans)
-        elif batched:
-            uz.compress_batched(ts, cb, outs=outs, ws=ws, out_sizes=sizes, sampled=sampled)
-        else:
-            uz.compress(ts[0], cb, out=outs[0], ws=ws, out_size=sizes, sampled=sampled)
+    pol_ref = ctypes.byref(pol) if pol is not None else None
+    plans_ptr = plans.data_ptr() if pol is not None else None
 
-    def decompress():
-        # in_bytes = capacity: the decoder validates the header's total against it
-        if batched:
-            uz.decompress_batched(outs, dtype, ns, outs=backs, status=status, ws=ws)
-        else:
-            uz.decompress(outs[0], dtype, ns[0], out=backs[0], status=status, ws=ws)
+    def compress(sampled=args.sampled, ev=(None, None)):
+        st = L.uzip_compress_batched_timed(code, len(ts), a_in.ptr, a_n.ptr, cb, 1 if sampled else 0, pol_ref,
+                                           a_out.ptr, a_cap.ptr, sizes.data_ptr(), plans_ptr, ws.data_ptr(),
+                                           ws.numel(), stream, ev[0], ev[1])
+        if st != 0:
+            raise uz.UzipError(st, "uzip_compress_batched_timed")
+
+    def decompress(ev=(None, None)):
+        st = L.uzip_decompress_batched_timed(code, len(ts), a_out.ptr, a_inb.ptr, a_n.ptr, a_back.ptr,
+                                             status.data_ptr(), ws.data_ptr(), ws.numel(), stream, ev[0], ev[1])
+        if st != 0:
+            raise uz.UzipError(st, "uzip_decompress_batched_timed")
 
     print("# %d buffers, %d values, %.1f MB; warmup %d, steps %d" % (len(ts), n_total, in_bytes / 1e6, args.warmup,
                                                                       args.steps), file=sys.stderr, flush=True)
@@ -283,15 +278,12 @@ def main():
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for k in range(K):
-            uz.uzip_profile_set_events(enc_ev[k][0], enc_ev[k][1])
             c_ev[k][0].record()
-            compress(sampled)
+            compress(sampled, enc_ev[k])
             c_ev[k][1].record()
-            uz.uzip_profile_set_events(dec_ev[k][0], dec_ev[k][1])
             d_ev[k][0].record()
-            decompress()
+            decompress(dec_ev[k])
             d_ev[k][1].record()
-        uz.uzip_profile_set_events(None, None)
         torch.cuda.synchronize()
         t1 = time.perf_counter()
         res = ((t1 - t0) * 1e3 / K, sorted(a.elapsed_time(b) for a, b in c_ev), sorted(a.elapsed_time(b) for a, b in d_ev),
@@ -317,7 +309,7 @@ def main():
     roundtrip_ok = roundtrip_exact()
     comp_sizes = sizes.cpu().tolist()
     comp_bytes = sum(comp_sizes)
-    bound = entropy_bound(ts, chunk_elems)
+    bound = entropy_bound(ts, code, cb)
 
     # algorithmic bytes per launch of the two coding kernels
     exp_offs, rec_bytes = record_bytes(comp_sizes)
@@ -351,10 +343,12 @@ def main():
     roofline["hbm_copy_gbps"] = round(copy_gbps, 1)
     roofline["frac_of_copy"] = round(achieved / copy_gbps, 4)
 
+    med_rt_ms = ms_step
     cpu = None
     oracle_match = None
     if not args.no_cpu_baseline:
-        cpu, oracle_match = cpu_baseline(ts, outs, comp_sizes, code, args.cpu_seconds, cb, pol, args.sampled)
+        cpu, oracle_match = cpu_baseline(ts, outs, comp_sizes, code, args.cpu_seconds, cb, pol, args.sampled,
+                                         in_bytes / (med_rt_ms * 1e-3) / 1e9)
 
     med_c = comp_ms[len(comp_ms) // 2]
     med_d = dec_ms[len(dec_ms) // 2]
@@ -377,8 +371,9 @@ def main():
                    "tables": "sampled" if args.sampled else "full", "step": "compress + decompress"},
         "compress_gbps": round(in_bytes / (med_c * 1e-3) / 1e9, 2),
         "decompress_gbps": round(in_bytes / (med_d * 1e-3) / 1e9, 2),
-        "compress_ms": {"median": round(med_c, 4), "min": round(comp_ms[0], 4)},
-        "decompress_ms": {"median": round(med_d, 4), "min": round(dec_ms[0], 4)},
+        "latency_ms": {"compress": {"median": round(med_c, 4), "min": round(comp_ms[0], 4)},
+                       "decompress": {"median": round(med_d, 4), "min": round(dec_ms[0], 4)},
+                       "per": "whole call over all %d buffers" % len(ts)},
         "ratio": round(comp_bytes / in_bytes, 5),
         "entropy_bound_ratio": round(bound / in_bytes, 5),
         "ratio_over_bound": round(comp_bytes / bound, 5),
@@ -421,7 +416,7 @@ def main():
     if pol is not None:
         line["config"]["arbitration"] = {f: getattr(pol, f) for f, _ in pol._fields_}
         line["plans"] = {"coded": decisions.count(0), "raw": decisions.count(1), "raw_small": decisions.count(2),
-                         "raw_planned_values": raw_planned}
+                         "raw_realized": decisions.count(3), "raw_planned_values": raw_planned}
         if len(ts) == 1:
             line["plans"]["plan"] = uz.plans_as_dicts(plans)[0]
     print(json.dumps(line), flush=True)
@@ -453,11 +448,14 @@ def copy_reference(ts, steps):
     return 2 * nbytes / (ms * 1e-3) / 1e9
 
 
-def cpu_baseline(ts, outs, comp_sizes, code, min_seconds, chunk_bytes, pol=None, sampled=False):
-    """The oracle (plain single-threaded C) on a bounded sample of the same
-    workload: whole buffers, in order, up to 512 MiB of input; passes repeat
-    until min_seconds of CPU time have been spent.  Also compares the oracle's
-    compressed bytes with the GPU's for every sampled buffer."""
+def cpu_baseline(ts, outs, comp_sizes, code, min_seconds, chunk_bytes, pol=None, sampled=False, gpu_gbps=None):
+    """The oracle (plain single-threaded C, gcc -O2) on a bounded sample of the
+    same workload: whole buffers, in order, up to 512 MiB of input (at least
+    one buffer).  Compress and decompress are timed separately, each repeated
+    until min_seconds have been spent, with the calling thread pinned to one
+    core (os.sched_setaffinity on this thread; restored afterwards).  Also
+    compares the oracle's compressed bytes with the GPU's for every sampled
+    buffer."""
     import numpy as np
 
     import oracle
@@ -471,40 +469,67 @@ def cpu_baseline(ts, outs, comp_sizes, code, min_seconds, chunk_bytes, pol=None,
         picked.append(i)
         acc += nb
     host = [W.bits_numpy(ts[i]) for i in picked]
+    comp = (oracle.compress_sampled if sampled else oracle.compress)
     match = True
+    frames = []
     for i, h in zip(picked, host):
         if pol is None:
-            want = (oracle.compress_sampled if sampled else oracle.compress)(code, h, chunk_bytes)
+            want = comp(code, h, chunk_bytes)
         else:  # the arbitrated frame (the plan may have chosen RAW)
             opol = oracle.Policy(**{f: getattr(pol, f) for f, _ in pol._fields_})
             want = oracle.compress_arbitrated(code, h, opol, chunk_bytes)[0]
         got = outs[i][:comp_sizes[i]].cpu().numpy()
         match = match and np.array_equal(want, got)
+        frames.append(want)
     sample_bytes = sum(h.size * h.itemsize for h in host)
-    spent, passes = 0.0, 0
-    while passes == 0 or spent < min_seconds:
-        t0 = time.perf_counter()
-        for h in host:
-            buf = (oracle.compress_sampled if sampled else oracle.compress)(code, h, chunk_bytes)
-            st, back = oracle.decompress(buf, code, h.size)
-            assert st == 0
-        spent += time.perf_counter() - t0
-        passes += 1
-        if spent > 60:
-            break
-    gbps = sample_bytes * passes / spent / 1e9
-    return ({"value": round(gbps, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-             "sample": "%d of %d buffers, %d values (%.1f MB), compress + decompress, %d passes, %.1f s; host %s"
-                       % (len(picked), len(ts), sum(h.size for h in host), sample_bytes / 1e6, passes, spent,
-                          _cpu_model())},
-            bool(match))
+    old_aff = os.sched_getaffinity(0)
+    core = min(old_aff)
+    os.sched_setaffinity(0, {core})
+    try:
+        def timed(fn):
+            spent, passes = 0.0, 0
+            while passes == 0 or spent < min_seconds:
+                t0 = time.perf_counter()
+                fn()
+                spent += time.perf_counter() - t0
+                passes += 1
+                if spent > 60:
+                    break
+            return spent, passes
+
+        def do_compress():
+            for h in host:
+                comp(code, h, chunk_bytes)
+
+        def do_decompress():
+            for h, f in zip(host, frames):
+                st, _ = oracle.decompress(f, code, h.size)
+                assert st == 0
+
+        c_s, c_p = timed(do_compress)
+        d_s, d_p = timed(do_decompress)
+    finally:
+        os.sched_setaffinity(0, old_aff)
+    c_gbps = sample_bytes * c_p / c_s / 1e9
+    d_gbps = sample_bytes * d_p / d_s / 1e9
+    rt_gbps = 1.0 / (1.0 / c_gbps + 1.0 / d_gbps)
+    out = {"value": round(rt_gbps, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+           "compress_gbps": round(c_gbps, 4), "decompress_gbps": round(d_gbps, 4),
+           "sample": "%d of %d buffers, %d values (%.1f MB); compress %d passes in %.1f s, decompress %d passes in "
+                     "%.1f s; value = round trip (input bytes over compress + decompress time), one thread pinned "
+                     "to core %d" % (len(picked), len(ts), sum(h.size for h in host), sample_bytes / 1e6, c_p, c_s,
+                                      d_p, d_s, core),
+           "cpu_model": _cpu_model(), "nproc": os.cpu_count()}
+    if gpu_gbps:
+        out["gpu_over_cpu"] = round(gpu_gbps / rt_gbps, 1)
+    return out, bool(match)
 
 
 def _cpu_model() -> str:
     try:
         for line in open("/proc/cpuinfo"):
             if line.startswith("model name"):
-                return line.split(":", 1)[1].strip() + ", %d logical cores" % os.cpu_count()
+                return line.split(":", 1)[1].strip()
     except OSError:
         pass
     return "unknown"

@@ -37,12 +37,18 @@
  * current HIP device; every h_* pointer is host memory.  The caller owns all
  * buffers.  Device input/output/workspace pointers must be 16-byte aligned
  * (a null input is allowed when its element count is 0).  The library
- * allocates nothing: work memory comes from the caller's workspace, whose
- * size the *_workspace_size functions give.  Host arrays need only live for
- * the duration of the call.  Calls enqueue work on `stream` and return without
- * synchronising it; results (d_out_size, d_status, output bytes) are valid
- * once the stream's work has completed.  Calls on different streams are
- * independent when their workspaces differ.
+ * allocates no device memory: work memory comes from the caller's workspace,
+ * whose size the *_workspace_size functions give.  Host arrays need only live
+ * for the duration of the call: a batched call over more than one buffer
+ * copies its per-buffer descriptors through a small pinned host staging area
+ * that the library keeps per calling thread and device (allocated on that
+ * thread's first such call, grown when a call needs more, kept until the
+ * process ends), so the call never waits for work already queued on the
+ * stream.  Calls enqueue work on `stream` and return without synchronising
+ * it; results (d_out_size, d_status, output bytes) are valid once the
+ * stream's work has completed.  Calls on different streams are independent
+ * when their workspaces differ.  The library keeps no other state between
+ * calls.
  *
  * Errors.  Argument errors are found on the host and returned at once, with
  * nothing launched: UZIP_ERR_INVALID_ARGUMENT (bad dtype, null or misaligned
@@ -85,14 +91,21 @@ typedef enum {
 } uzip_status;
 
 /* Exact upper bound of the compressed size of num_elements values: the size
- * the buffer has when every chunk is stored RAW (a chunk is coded only when
- * that is strictly smaller).  chunk_bytes is the uncompressed chunk size
- * (0 = default: 256 KiB for fp32, 64 KiB for the others).  Pure host function;
- * returns 0 for an invalid dtype or chunk size. */
+ * of the self-describing frame (NCCLZ Sec. IV-D2, batch framing: header,
+ * record index, raw region, records) when every chunk is stored RAW, the
+ * frame a RAW decision commits (Sec. IV-C, Algorithm 1).  It is exact because
+ * a chunk is coded only when that is strictly smaller, and a frame holding a
+ * longer coded record is rejected as corrupt.  chunk_bytes is the
+ * uncompressed chunk size (0 = default: 256 KiB for fp32, 64 KiB for the
+ * others).  Pure host function; returns 0 for an invalid dtype or chunk size. */
 size_t uzip_max_compressed_size(uzip_dtype dtype, size_t num_elements, size_t chunk_bytes);
 
 /* Workspace bytes that uzip_compress or uzip_decompress needs for one buffer
- * of num_elements values (the larger of the two).  0 for invalid arguments. */
+ * of num_elements values (the larger of the two): the per-chunk record slots
+ * and sizes in which each chunk's record (its local table, UCCL-Zip
+ * Figure 5(b), and its rANS words) is built before the offset scan places it
+ * in the frame (NCCLZ Sec. IV-D2), plus the scan's look-back words.  Pure
+ * host function; 0 for invalid arguments. */
 size_t uzip_workspace_size(uzip_dtype dtype, size_t num_elements, size_t chunk_bytes);
 
 /* Compress num_elements values of `dtype` at d_in (bit patterns, any values
@@ -119,7 +132,8 @@ uzip_status uzip_decompress(const void *d_in, size_t in_bytes, uzip_dtype dtype,
 
 /* Workspace for one batched call over num_buffers buffers whose element
  * counts are h_num_elements[0..num_buffers) (the larger of the compress and
- * decompress needs). */
+ * decompress needs): that of uzip_workspace_size over all the chunks, plus
+ * one descriptor per buffer.  Pure host function; 0 for invalid arguments. */
 size_t uzip_workspace_size_batched(uzip_dtype dtype, size_t num_buffers, const size_t *h_num_elements,
                                    size_t chunk_bytes);
 
@@ -186,7 +200,9 @@ uzip_status uzip_decompress_batched(uzip_dtype dtype, size_t num_buffers,
  * Coding is admitted when P < P_raw and (P_raw - P) * 1000 >=
  * min_gain_permil * B; it is chosen when admitted and coded_ns < raw_ns
  * (Eq. (2); ties go RAW).  A RAW plan writes the all-RAW frame (every record
- * RAW, size P_raw); a coded plan writes exactly what uzip_compress writes.
+ * RAW, size P_raw); a coded plan writes exactly what uzip_compress writes,
+ * unless that frame's realised size fails the same gain rule, in which case
+ * the all-RAW frame is written instead (UZIP_PLAN_RAW_REALIZED).
  * Either frame decodes with uzip_decompress.  Every step is integer
  * arithmetic, so the plan is one fixed function of the input and the policy.
  * Rates are bytes per microsecond (= MB/s); all must be > 0; the per-mille
@@ -203,8 +219,18 @@ typedef struct uzip_policy {
     uint32_t reserved;
 } uzip_policy;
 
-/* What a call decided (device-written, 32 bytes per buffer). */
-typedef enum { UZIP_PLAN_CODED = 0, UZIP_PLAN_RAW = 1, UZIP_PLAN_RAW_SMALL = 2 } uzip_plan_decision;
+/* What a call decided (device-written, 32 bytes per buffer).  A coded plan
+ * is checked once its frame is written (Algorithm 1 accepts a materialised
+ * plan only if its realised output passes the gain check): when the realised
+ * size R fails R < P_raw and (P_raw - R) * 1000 >= min_gain_permil * B, the
+ * all-RAW frame replaces it and the decision becomes UZIP_PLAN_RAW_REALIZED
+ * (the other plan fields keep the prediction). */
+typedef enum {
+    UZIP_PLAN_CODED = 0,
+    UZIP_PLAN_RAW = 1,
+    UZIP_PLAN_RAW_SMALL = 2,
+    UZIP_PLAN_RAW_REALIZED = 3
+} uzip_plan_decision;
 typedef struct uzip_plan {
     uint32_t decision;        /* uzip_plan_decision */
     uint32_t sample_values;   /* values sampled (0 on the small path) */
@@ -232,13 +258,29 @@ uzip_status uzip_compress_batched_arbitrated(uzip_dtype dtype, size_t num_buffer
                                              uint64_t *d_out_sizes, uzip_plan *d_plans,
                                              void *d_workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* Benchmark instrumentation.  While set (non-null), every compress call on
- * the calling host thread records `main_start` on its stream right before
- * its main coding kernel (split + histogram + table + rANS encode) and
- * `main_stop` right after it; every decompress call does the same around
- * its rANS decode kernel.  Pass nulls to stop.  The events belong to the
- * caller (hipEventCreate).  Thread-local; costs nothing while unset. */
-uzip_status uzip_profile_set_events(hipEvent_t main_start, hipEvent_t main_stop);
+/* ---- instrumented forms (benchmarks) --------------------------------------
+ * The batched compress and decompress with two caller events recorded on
+ * `stream` around the main coding kernel: main_start right before the kernel
+ * that splits, counts, normalises and rANS-encodes (compress) or the rANS
+ * decoders (decompress), main_stop right after it, so that the caller can
+ * time that kernel alone with hipEventElapsedTime.  Both events or neither
+ * (nulls: no events); they belong to the caller (hipEventCreate) and are
+ * used during this call only.  sampled (0 or 1) selects the
+ * uzip_compress_batched_sampled form, a non-null policy (with d_plans) the
+ * arbitrated one (not both).  Otherwise arguments, results and errors are
+ * those of uzip_compress_batched / uzip_decompress_batched; a call over one
+ * buffer writes exactly what the single-buffer call writes. */
+uzip_status uzip_compress_batched_timed(uzip_dtype dtype, size_t num_buffers, const void *const *h_in,
+                                        const size_t *h_num_elements, size_t chunk_bytes, uint32_t sampled,
+                                        const uzip_policy *policy, void *const *h_out, const size_t *h_out_capacity,
+                                        uint64_t *d_out_sizes, uzip_plan *d_plans, void *d_workspace,
+                                        size_t workspace_bytes, hipStream_t stream, hipEvent_t main_start,
+                                        hipEvent_t main_stop);
+uzip_status uzip_decompress_batched_timed(uzip_dtype dtype, size_t num_buffers, const void *const *h_in,
+                                          const size_t *h_in_bytes, const size_t *h_num_elements,
+                                          void *const *h_out, uint32_t *d_status, void *d_workspace,
+                                          size_t workspace_bytes, hipStream_t stream, hipEvent_t main_start,
+                                          hipEvent_t main_stop);
 
 /* Static English name of a status code. */
 const char *uzip_status_string(uzip_status s);

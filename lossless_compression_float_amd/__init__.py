@@ -37,6 +37,7 @@ UZIP_ERR_UNSUPPORTED = 5
 UZIP_PLAN_CODED = 0
 UZIP_PLAN_RAW = 1
 UZIP_PLAN_RAW_SMALL = 2
+UZIP_PLAN_RAW_REALIZED = 3
 
 
 class uzip_policy(ctypes.Structure):
@@ -63,7 +64,8 @@ EXPORTED = (
     "uzip_compress_batched_arbitrated",
     "uzip_compress_sampled",
     "uzip_compress_batched_sampled",
-    "uzip_profile_set_events",
+    "uzip_compress_batched_timed",
+    "uzip_decompress_batched_timed",
     "uzip_status_string",
 )
 
@@ -108,8 +110,11 @@ def lib() -> ctypes.CDLL:
         L.uzip_compress_batched_arbitrated.restype = i32
         L.uzip_compress_batched_arbitrated.argtypes = [i32, sz, vp, vp, sz, ctypes.POINTER(uzip_policy), vp, vp,
                                                        u64p, vp, vp, sz, vp]
-        L.uzip_profile_set_events.restype = i32
-        L.uzip_profile_set_events.argtypes = [vp, vp]
+        L.uzip_compress_batched_timed.restype = i32
+        L.uzip_compress_batched_timed.argtypes = [i32, sz, vp, vp, sz, ctypes.c_uint32, ctypes.POINTER(uzip_policy),
+                                                  vp, vp, u64p, vp, vp, sz, vp, vp, vp]
+        L.uzip_decompress_batched_timed.restype = i32
+        L.uzip_decompress_batched_timed.argtypes = [i32, sz, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp]
         L.uzip_status_string.restype = ctypes.c_char_p
         L.uzip_status_string.argtypes = [i32]
         _lib = L
@@ -202,8 +207,21 @@ def uzip_compress_batched_arbitrated(dtype, h_in, h_num_elements, chunk_bytes, p
                                                       workspace_bytes, stream))
 
 
-def uzip_profile_set_events(main_start, main_stop) -> int:
-    return int(lib().uzip_profile_set_events(main_start, main_stop))
+def uzip_compress_batched_timed(dtype, h_in, h_num_elements, chunk_bytes, sampled, policy, h_out, h_out_capacity,
+                                d_out_sizes, d_plans, d_workspace, workspace_bytes, stream, main_start,
+                                main_stop) -> int:
+    a_in, a_n, a_out, a_cap = _ptrs(h_in), _sizes(h_num_elements), _ptrs(h_out), _sizes(h_out_capacity)
+    pol = ctypes.byref(policy) if policy is not None else None
+    return int(lib().uzip_compress_batched_timed(dtype, len(h_in), a_in.ptr, a_n.ptr, chunk_bytes, sampled, pol,
+                                                 a_out.ptr, a_cap.ptr, d_out_sizes, d_plans, d_workspace,
+                                                 workspace_bytes, stream, main_start, main_stop))
+
+
+def uzip_decompress_batched_timed(dtype, h_in, h_in_bytes, h_num_elements, h_out, d_status, d_workspace,
+                                  workspace_bytes, stream, main_start, main_stop) -> int:
+    a_in, a_b, a_n, a_out = _ptrs(h_in), _sizes(h_in_bytes), _sizes(h_num_elements), _ptrs(h_out)
+    return int(lib().uzip_decompress_batched_timed(dtype, len(h_in), a_in.ptr, a_b.ptr, a_n.ptr, a_out.ptr, d_status,
+                                                   d_workspace, workspace_bytes, stream, main_start, main_stop))
 
 
 def uzip_status_string(status: int) -> str:
@@ -228,6 +246,24 @@ def torch_dtype(code: int) -> torch.dtype:
 def _stream(stream=None) -> int:
     s = stream if stream is not None else torch.cuda.current_stream()
     return int(s.cuda_stream)
+
+
+def _keep_for(stream, *tensors):
+    """Tensors allocated here on the current stream but used by kernels on
+    another `stream`: tell torch's caching allocator so (record_stream), or
+    it could hand their memory to new work on the current stream while those
+    kernels still read or write it.  Nothing to do when `stream` is None or
+    is the current stream."""
+    if stream is None:
+        return
+    if stream == torch.cuda.current_stream(stream.device):
+        return
+    for t in tensors:
+        if isinstance(t, torch.Tensor):
+            t.record_stream(stream)
+        else:
+            for u in t:
+                u.record_stream(stream)
 
 
 def _check(st: int, what: str):
@@ -264,6 +300,7 @@ def compress(t: torch.Tensor, chunk_bytes: int = 0, out: torch.Tensor | None = N
     st = fn(code, t.data_ptr() if n else None, n, chunk_bytes, out.data_ptr(), out.numel(),
             out_size.data_ptr(), ws.data_ptr(), ws.numel(), _stream(stream))
     _check(st, fn.__name__)
+    _keep_for(stream, out, out_size, ws)
     return out, out_size
 
 
@@ -284,6 +321,7 @@ def decompress(buf: torch.Tensor, dtype: torch.dtype, n: int, in_bytes: int | No
     st = uzip_decompress(buf.data_ptr() if nb else None, nb, code, n, out.data_ptr() if n else None,
                          status.data_ptr(), ws.data_ptr(), ws.numel(), _stream(stream))
     _check(st, "uzip_decompress")
+    _keep_for(stream, out, status, ws)
     return out, status
 
 
@@ -306,6 +344,7 @@ def compress_batched(tensors, chunk_bytes: int = 0, outs=None, ws=None, out_size
             [o.data_ptr() for o in outs], [o.numel() for o in outs], out_sizes.data_ptr(),
             ws.data_ptr(), ws.numel(), _stream(stream))
     _check(st, fn.__name__)
+    _keep_for(stream, outs, out_sizes, ws)
     return outs, out_sizes
 
 
@@ -323,6 +362,7 @@ def decompress_batched(bufs, dtype: torch.dtype, ns, in_bytes=None, outs=None, s
                                  [o.data_ptr() if o.numel() else 0 for o in outs], status.data_ptr(), ws.data_ptr(),
                                  ws.numel(), _stream(stream))
     _check(st, "uzip_decompress_batched")
+    _keep_for(stream, outs, status, ws)
     return outs, status
 
 
@@ -360,6 +400,7 @@ def compress_arbitrated(t: torch.Tensor, pol: uzip_policy, chunk_bytes: int = 0,
     st = uzip_compress_arbitrated(code, t.data_ptr() if n else None, n, chunk_bytes, pol, out.data_ptr(), out.numel(),
                                   out_size.data_ptr(), plan.data_ptr(), ws.data_ptr(), ws.numel(), _stream(stream))
     _check(st, "uzip_compress_arbitrated")
+    _keep_for(stream, out, out_size, plan, ws)
     return out, out_size, plan
 
 
@@ -382,4 +423,5 @@ def compress_batched_arbitrated(tensors, pol: uzip_policy, chunk_bytes: int = 0,
                                           out_sizes.data_ptr(), plans.data_ptr(), ws.data_ptr(), ws.numel(),
                                           _stream(stream))
     _check(st, "uzip_compress_batched_arbitrated")
+    _keep_for(stream, outs, out_sizes, plans, ws)
     return outs, out_sizes, plans

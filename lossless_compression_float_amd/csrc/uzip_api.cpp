@@ -1,6 +1,8 @@
 // uzip_api.cpp -- the C ABI declared in include/uzip.h: argument checks,
 // layout and workspace carving, descriptor upload, and launches on the
-// caller's stream.  Nothing here synchronises the stream or allocates memory.
+// caller's stream.  Nothing here synchronises the stream.  Device memory is
+// never allocated; the batched calls stage their descriptors in a small
+// pinned host area per calling thread (see DescStage).
 #include <stdint.h>
 #include <string.h>
 
@@ -99,6 +101,69 @@ uint64_t max_size(uzip_dtype dtype, uint64_t n, uint64_t ce) {
 
 static_assert(sizeof(uzip_policy) == 56 && sizeof(uzip_plan) == 32, "arbitration structs as uzip.h lays them out");
 
+// Host staging of the batched calls' descriptors.  A host-to-device copy from
+// pageable memory does not return before the stream has reached it, so it
+// would hold the caller behind every kernel already queued; the descriptors
+// are written to pinned host memory instead and copied asynchronously.  Each
+// host thread keeps, per device, a ring of kStageSlots pinned buffers, each
+// with an event recorded after its copy: a slot is reused once its event has
+// completed, so the caller waits only when it runs kStageSlots batched calls
+// ahead of the device.  The buffers are allocated on a thread's first batched
+// call on a device (and grown when a call needs more), and kept until the
+// process ends.
+constexpr int kStageSlots = 8;
+constexpr int kStageDevices = 16;
+
+struct StageSlot {
+    void *host = nullptr;
+    size_t cap = 0;
+    hipEvent_t done = nullptr;
+    bool pending = false;
+};
+
+struct DescStage {
+    StageSlot slot[kStageDevices][kStageSlots];
+    int next[kStageDevices] = {};
+};
+
+thread_local DescStage t_stage;
+
+// Copies `bytes` of `src` to the device at `dst` on `stream` without waiting
+// for the stream.  Returns false on a HIP error.
+bool stage_copy(void *dst, const void *src, size_t bytes, hipStream_t stream) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return false;
+    if (dev < 0 || dev >= kStageDevices)  // beyond the staged devices: a plain (blocking) copy
+        return hipMemcpyAsync(dst, src, bytes, hipMemcpyHostToDevice, stream) == hipSuccess;
+    int &next = t_stage.next[dev];
+    StageSlot &sl = t_stage.slot[dev][next];
+    next = (next + 1) % kStageSlots;
+    if (sl.pending) {
+        if (hipEventSynchronize(sl.done) != hipSuccess) return false;
+        sl.pending = false;
+    }
+    if (sl.done == nullptr && hipEventCreateWithFlags(&sl.done, hipEventDisableTiming) != hipSuccess) {
+        sl.done = nullptr;
+        return false;
+    }
+    if (sl.cap < bytes) {
+        if (sl.host != nullptr) (void)hipHostFree(sl.host);
+        sl.host = nullptr;
+        sl.cap = 0;
+        const size_t cap = std::max<size_t>(bytes, 64 << 10);
+        if (hipHostMalloc(&sl.host, cap, hipHostMallocDefault) != hipSuccess) {
+            sl.host = nullptr;
+            return false;
+        }
+        sl.cap = cap;
+    }
+    memcpy(sl.host, src, bytes);
+    if (hipMemcpyAsync(dst, sl.host, bytes, hipMemcpyHostToDevice, stream) != hipSuccess) return false;
+    if (hipEventRecord(sl.done, stream) != hipSuccess) return false;
+    sl.pending = true;
+    return true;
+}
+
 // The cost model's inputs must be usable as the header states: positive
 // rates, per-mille fields at most 1000, reserved zero.
 bool policy_ok(const uzip_policy *p) {
@@ -111,7 +176,8 @@ bool policy_ok(const uzip_policy *p) {
 // arbitrated forms).
 uzip_status compress_impl(uzip_dtype dtype, uint64_t ce, std::vector<EncDesc> &descs, uint64_t chunks,
                           void *d_workspace, size_t workspace_bytes, hipStream_t stream,
-                          uzip_plan *plans = nullptr, const uzip_policy *policy = nullptr, bool sampled = false) {
+                          uzip_plan *plans = nullptr, const uzip_policy *policy = nullptr, bool sampled = false,
+                          const ProfileEvents *ev = nullptr) {
     const uint32_t nbuf = (uint32_t)descs.size();
     const EncWs w = enc_ws(nbuf, chunks, ce);
     if (d_workspace == nullptr || workspace_bytes < w.bytes || !aligned(d_workspace, 16))
@@ -144,13 +210,10 @@ uzip_status compress_impl(uzip_dtype dtype, uint64_t ce, std::vector<EncDesc> &d
         ep.descs = nullptr;
     } else {
         EncDesc *dd = reinterpret_cast<EncDesc *>(base + w.descs);
-        // Pageable host -> device copy: the runtime stages the bytes before
-        // returning, so `descs` may be released once this call returns.
-        if (hipMemcpyAsync(dd, descs.data(), nbuf * sizeof(EncDesc), hipMemcpyHostToDevice, stream) != hipSuccess)
-            return UZIP_ERR_DEVICE;
+        if (!stage_copy(dd, descs.data(), nbuf * sizeof(EncDesc), stream)) return UZIP_ERR_DEVICE;
         ep.descs = dd;
     }
-    const hipError_t e = launch_compress(ep, stream);
+    const hipError_t e = launch_compress(ep, stream, ev);
     return e == hipSuccess ? UZIP_OK : UZIP_ERR_DEVICE;
 }
 
@@ -178,7 +241,7 @@ uzip_status compress_batched(uzip_dtype dtype, size_t num_buffers, const void *c
                              const size_t *h_num_elements, size_t chunk_bytes, const uzip_policy *policy,
                              void *const *h_out, const size_t *h_out_capacity, uint64_t *d_out_sizes,
                              uzip_plan *d_plans, void *d_workspace, size_t workspace_bytes, hipStream_t stream,
-                             bool sampled = false) {
+                             bool sampled = false, const ProfileEvents *ev = nullptr) {
     const uint64_t ce = chunk_elems_of(dtype, chunk_bytes);
     if (!ce || num_buffers == 0 || num_buffers > 0xFFFFFFFFull) return UZIP_ERR_INVALID_ARGUMENT;
     if (!h_in || !h_num_elements || !h_out || !h_out_capacity || !d_out_sizes || !aligned(d_out_sizes, 8))
@@ -197,11 +260,11 @@ uzip_status compress_batched(uzip_dtype dtype, size_t num_buffers, const void *c
         chunks += l.chunks;
     }
     return compress_impl(dtype, ce, descs, chunks, d_workspace, workspace_bytes, stream,
-                         policy ? d_plans : nullptr, policy, sampled);
+                         policy ? d_plans : nullptr, policy, sampled, ev);
 }
 
 uzip_status decompress_impl(uzip_dtype dtype, std::vector<DecDesc> &descs, uint32_t *d_status, void *d_workspace,
-                            size_t workspace_bytes, hipStream_t stream) {
+                            size_t workspace_bytes, hipStream_t stream, const ProfileEvents *ev = nullptr) {
     const uint32_t nbuf = (uint32_t)descs.size();
     const DecWs w = dec_ws(nbuf);
     if (d_workspace == nullptr || workspace_bytes < w.bytes || !aligned(d_workspace, 16))
@@ -220,8 +283,7 @@ uzip_status decompress_impl(uzip_dtype dtype, std::vector<DecDesc> &descs, uint3
         vp.single = descs[0];
     } else {
         DecDesc *dd = reinterpret_cast<DecDesc *>(base + w.descs);
-        if (hipMemcpyAsync(dd, descs.data(), nbuf * sizeof(DecDesc), hipMemcpyHostToDevice, stream) != hipSuccess)
-            return UZIP_ERR_DEVICE;
+        if (!stage_copy(dd, descs.data(), nbuf * sizeof(DecDesc), stream)) return UZIP_ERR_DEVICE;
         vp.descs = dd;
     }
     DecodeParams dp{};
@@ -232,7 +294,7 @@ uzip_status decompress_impl(uzip_dtype dtype, std::vector<DecDesc> &descs, uint3
     dp.pair_first = vp.pair_first;
     dp.status = d_status;
     dp.kinds = vp.kinds;
-    const hipError_t e = launch_decompress(vp, dp, dtype, max_chunks, stream);
+    const hipError_t e = launch_decompress(vp, dp, dtype, max_chunks, stream, ev);
     return e == hipSuccess ? UZIP_OK : UZIP_ERR_DEVICE;
 }
 
@@ -327,7 +389,17 @@ uzip_status uzip_decompress_batched(uzip_dtype dtype, size_t num_buffers, const 
                                     const size_t *h_in_bytes, const size_t *h_num_elements, void *const *h_out,
                                     uint32_t *d_status, void *d_workspace, size_t workspace_bytes,
                                     hipStream_t stream) {
+    return uzip_decompress_batched_timed(dtype, num_buffers, h_in, h_in_bytes, h_num_elements, h_out, d_status,
+                                         d_workspace, workspace_bytes, stream, nullptr, nullptr);
+}
+
+uzip_status uzip_decompress_batched_timed(uzip_dtype dtype, size_t num_buffers, const void *const *h_in,
+                                          const size_t *h_in_bytes, const size_t *h_num_elements,
+                                          void *const *h_out, uint32_t *d_status, void *d_workspace,
+                                          size_t workspace_bytes, hipStream_t stream, hipEvent_t main_start,
+                                          hipEvent_t main_stop) {
     if (!dtype_ok(dtype) || num_buffers == 0 || num_buffers > 0xFFFFFFFFull) return UZIP_ERR_INVALID_ARGUMENT;
+    if ((main_start == nullptr) != (main_stop == nullptr)) return UZIP_ERR_INVALID_ARGUMENT;
     if (!h_in || !h_in_bytes || !h_num_elements || !h_out || !d_status || !aligned(d_status, 4))
         return UZIP_ERR_INVALID_ARGUMENT;
     std::vector<DecDesc> descs(num_buffers);
@@ -338,13 +410,24 @@ uzip_status uzip_decompress_batched(uzip_dtype dtype, size_t num_buffers, const 
         descs[b] = DecDesc{static_cast<const uint8_t *>(h_in[b]), static_cast<uint8_t *>(h_out[b]), h_in_bytes[b],
                            h_num_elements[b]};
     }
-    return decompress_impl(dtype, descs, d_status, d_workspace, workspace_bytes, stream);
+    const ProfileEvents ev{main_start, main_stop};
+    return decompress_impl(dtype, descs, d_status, d_workspace, workspace_bytes, stream,
+                           main_start != nullptr ? &ev : nullptr);
 }
 
-uzip_status uzip_profile_set_events(hipEvent_t main_start, hipEvent_t main_stop) {
-    g_profile.start = main_start;
-    g_profile.stop = main_stop;
-    return UZIP_OK;
+uzip_status uzip_compress_batched_timed(uzip_dtype dtype, size_t num_buffers, const void *const *h_in,
+                                        const size_t *h_num_elements, size_t chunk_bytes, uint32_t sampled,
+                                        const uzip_policy *policy, void *const *h_out, const size_t *h_out_capacity,
+                                        uint64_t *d_out_sizes, uzip_plan *d_plans, void *d_workspace,
+                                        size_t workspace_bytes, hipStream_t stream, hipEvent_t main_start,
+                                        hipEvent_t main_stop) {
+    if ((main_start == nullptr) != (main_stop == nullptr) || sampled > 1) return UZIP_ERR_INVALID_ARGUMENT;
+    if (policy != nullptr && (sampled || !policy_ok(policy) || d_plans == nullptr || !aligned(d_plans, 8)))
+        return UZIP_ERR_INVALID_ARGUMENT;
+    const ProfileEvents ev{main_start, main_stop};
+    return compress_batched(dtype, num_buffers, h_in, h_num_elements, chunk_bytes, policy, h_out, h_out_capacity,
+                            d_out_sizes, d_plans, d_workspace, workspace_bytes, stream, sampled != 0,
+                            main_start != nullptr ? &ev : nullptr);
 }
 
 const char *uzip_status_string(uzip_status s) {

@@ -1223,7 +1223,10 @@ __global__ __launch_bounds__(256) void k_raw_frame(EncParams p) {
     const uint32_t t = threadIdx.x;
     for (uint64_t g = blockIdx.x; g < p.total_chunks; g += gridDim.x) {
         const uint32_t bi = p.nbuf == 1 ? 0u : uniform_u32(find_enc_chunk_buffer(p.descs, p.nbuf, g));
-        if (uniform_u32(gload<uint32_t>(&p.plans[bi].decision)) == UZIP_PLAN_CODED) continue;
+        // pass 0 (before the compaction): the buffers planned RAW; pass 1
+        // (after the realised-gain check): the buffers whose coded frame failed it
+        const uint32_t dec = uniform_u32(gload<uint32_t>(&p.plans[bi].decision));
+        if (dec == UZIP_PLAN_CODED || (dec == UZIP_PLAN_RAW_REALIZED) != (p.raw_pass != 0)) continue;
         const EncDesc d = p.nbuf == 1 ? p.single : load_enc_desc(p.descs + bi);
         const uint64_t ce = p.chunk_elems, n = uniform_u64(d.n), chunks = uniform_u64(d.chunks);
         const uint64_t c = g - uniform_u64(d.chunk_first);
@@ -1301,6 +1304,28 @@ __global__ __launch_bounds__(256) void k_raw_frame(EncParams p) {
             for (uint64_t k = sm_off + uint64_t(R) * n + t; k < exp_off; k += 256) gstore<uint8_t>(out + k, 0);
         }
     }
+}
+
+// Acceptance of the realised frame (NCCLZ Algorithm 1: a materialised coded
+// plan is kept only if its realised output passes the capacity and gain
+// checks, else the RAW frame is committed).  One thread per buffer, after the
+// compaction has written each coded buffer's size R: the coded frame stays
+// when R < P_raw and (P_raw - R) * 1000 >= min_gain * B, the admission rule
+// on the realised size; otherwise the plan becomes UZIP_PLAN_RAW_REALIZED and
+// the second k_raw_frame pass rewrites the buffer as its all-RAW frame.
+// (Capacity always holds: no record exceeds its RAW record.)
+template <int DT>
+__global__ __launch_bounds__(256) void k_accept(EncParams p) {
+    const uint32_t bi = blockIdx.x * 256 + threadIdx.x;
+    if (bi >= p.nbuf) return;
+    if (gload<uint32_t>(&p.plans[bi].decision) != UZIP_PLAN_CODED) return;
+    const EncDesc d = p.nbuf == 1 ? p.single : load_enc_desc(p.descs + bi);
+    const uint64_t ce = p.chunk_elems, n = d.n, B = n * Fmt<DT>::EB;
+    const Layout l = layout_of(p.dtype, n, ce);
+    const uint64_t praw = l.exp_off + (l.chunks - 1) * raw_record_bytes(ce) + raw_record_bytes(n - (l.chunks - 1) * ce);
+    const uint64_t R = gload<uint64_t>(d.out_size);
+    const bool accepted = R < praw && (praw - R) * 1000 >= uint64_t(p.policy.min_gain_permil) * B;
+    if (!accepted) gstore<uint32_t>(&p.plans[bi].decision, UZIP_PLAN_RAW_REALIZED);
 }
 
 // ---------------------------------------------------------------------------
@@ -1660,7 +1685,9 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
         const uint64_t a2 = nch == 2 ? uniform_u64(gload<uint64_t>(ix + 16)) : a1;
         const uint64_t rawmax = raw_record_bytes(ce);
         // V5 for the pair's index entries: aligned, ordered, inside the records,
-        // and no record longer than the RAW one (which bounds every record)
+        // and no record longer than a full chunk's RAW record (a coarse bound
+        // that keeps the 32-bit resource sizes below valid; each record is then
+        // held to its own chunk's RAW size below)
         const bool pair_ok = ((a0 | a1 | a2) & 15u) == 0 && a0 <= a1 && a1 <= a2 && a2 <= total - exp_off &&
                              a1 - a0 <= rawmax && a2 - a1 <= rawmax;
         if (!pair_ok) {
@@ -1685,7 +1712,9 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
             nw = rh.y;
             ok = ok && (mode == 1 || mode == kCoded) && rh.z == ni && rh.w == len;
             if (ok && mode == 1) ok = nsym == 0 && nw == 0 && len == raw_record_bytes(ni);
-            if (ok && mode == kCoded) ok = nsym >= 1 && nsym <= 256;
+            // a coded record is strictly smaller than the chunk's RAW record
+            // (it would have been stored RAW otherwise); a longer one is corrupt
+            if (ok && mode == kCoded) ok = nsym >= 1 && nsym <= 256 && len < raw_record_bytes(ni);
             if (S && ok && mode == kCoded) {
                 ok = len >= words_offset_sampled(nsym);
                 nesc = bld32(rrec, ok ? rel + (uint32_t)esc_count_offset(nsym) : kOutOfRange);
@@ -2090,12 +2119,10 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-thread_local ProfileEvents g_profile;
-
 // kernel template for a dtype code: bf16 1, fp32 2, fp16 3, both fp8 codes 4
 static int kernel_format(int dtype) { return dtype <= 3 ? dtype : 4; }
 
-hipError_t launch_compress(const EncParams &ep, hipStream_t stream) {
+hipError_t launch_compress(const EncParams &ep, hipStream_t stream, const ProfileEvents *ev) {
     uint64_t threads = ep.total_pairs > ep.nbuf ? ep.total_pairs : ep.nbuf;
     if (ep.plans != nullptr) {
         switch (kernel_format(ep.dtype)) {
@@ -2108,7 +2135,7 @@ hipError_t launch_compress(const EncParams &ep, hipStream_t stream) {
     k_prepare<<<dim3((uint32_t)((threads + 255) / 256)), dim3(256), 0, stream>>>(ep);
     if (ep.total_pairs > 0) {
         const dim3 grid((uint32_t)ep.total_pairs);
-        if (g_profile.start) (void)hipEventRecord(g_profile.start, stream);
+        if (ev != nullptr) (void)hipEventRecord(ev->start, stream);
         const int kf = kernel_format(ep.dtype) + (ep.sampled ? 8 : 0);
         switch (kf) {
         case 1: k_encode<1, false><<<grid, dim3(64), 0, stream>>>(ep); break;
@@ -2120,7 +2147,7 @@ hipError_t launch_compress(const EncParams &ep, hipStream_t stream) {
         case 11: k_encode<3, true><<<grid, dim3(64), 0, stream>>>(ep); break;
         default: k_encode<4, true><<<grid, dim3(64), 0, stream>>>(ep); break;
         }
-        if (g_profile.stop) (void)hipEventRecord(g_profile.stop, stream);
+        if (ev != nullptr) (void)hipEventRecord(ev->stop, stream);
         if (ep.plans != nullptr) {
             const dim3 rgrid((uint32_t)(ep.total_chunks < 2048 ? ep.total_chunks : 2048));
             switch (kernel_format(ep.dtype)) {
@@ -2137,18 +2164,31 @@ hipError_t launch_compress(const EncParams &ep, hipStream_t stream) {
         case 3: k_compact<3><<<cgrid, dim3(128 * kCompactPairs), 0, stream>>>(ep); break;
         default: k_compact<4><<<cgrid, dim3(128 * kCompactPairs), 0, stream>>>(ep); break;
         }
+        if (ep.plans != nullptr) {
+            // the realised frames' gain check, then the RAW frame of each buffer that failed it
+            const dim3 agrid((ep.nbuf + 255) / 256);
+            EncParams rp = ep;
+            rp.raw_pass = 1;
+            const dim3 rgrid((uint32_t)(ep.total_chunks < 2048 ? ep.total_chunks : 2048));
+            switch (kernel_format(ep.dtype)) {
+            case 1: k_accept<1><<<agrid, dim3(256), 0, stream>>>(ep); k_raw_frame<1><<<rgrid, dim3(256), 0, stream>>>(rp); break;
+            case 2: k_accept<2><<<agrid, dim3(256), 0, stream>>>(ep); k_raw_frame<2><<<rgrid, dim3(256), 0, stream>>>(rp); break;
+            case 3: k_accept<3><<<agrid, dim3(256), 0, stream>>>(ep); k_raw_frame<3><<<rgrid, dim3(256), 0, stream>>>(rp); break;
+            default: k_accept<4><<<agrid, dim3(256), 0, stream>>>(ep); k_raw_frame<4><<<rgrid, dim3(256), 0, stream>>>(rp); break;
+            }
+        }
     }
     return hipGetLastError();
 }
 
 hipError_t launch_decompress(const DecParams &vp, const DecodeParams &dp, int dtype, uint64_t max_chunks,
-                             hipStream_t stream) {
+                             hipStream_t stream, const ProfileEvents *ev) {
     k_dec_validate<<<(vp.nbuf + 255) / 256, 256, 0, stream>>>(vp);
     if (vp.nbuf > 1) k_dec_scan<<<1, 1024, 0, stream>>>(vp);
     if (max_chunks > 0) {
         const uint64_t pairs = (max_chunks + 1) / 2 + vp.nbuf;  // upper bound of the chunk pairs
         const uint64_t grid = pairs < 8192 ? pairs : 8192;
-        if (g_profile.start) (void)hipEventRecord(g_profile.start, stream);
+        if (ev != nullptr) (void)hipEventRecord(ev->start, stream);
         // full-table frames, then sampled-table frames (each kernel leaves at
         // once when the call holds no valid buffer of its kind)
         switch (kernel_format(dtype)) {
@@ -2163,7 +2203,7 @@ hipError_t launch_decompress(const DecParams &vp, const DecodeParams &dp, int dt
         case 3: k_decode<3, true><<<dim3((uint32_t)grid), dim3(64), 0, stream>>>(dp); break;
         default: k_decode<4, true><<<dim3((uint32_t)grid), dim3(64), 0, stream>>>(dp); break;
         }
-        if (g_profile.stop) (void)hipEventRecord(g_profile.stop, stream);
+        if (ev != nullptr) (void)hipEventRecord(ev->stop, stream);
     }
     return hipGetLastError();
 }

@@ -26,6 +26,7 @@ struct EncParams {
     uint32_t sampled;       // 1: tables from each chunk's sample (header flag bit 0, record mode 2)
     uzip_plan *plans;       // per-call arbitration: one plan per buffer (null: every buffer is coded)
     uzip_policy policy;     // the cost model's inputs when plans is set
+    uint32_t raw_pass;      // k_raw_frame: 0 writes the buffers planned RAW, 1 those whose realised frame failed
 };
 
 struct DecParams {
@@ -49,15 +50,15 @@ struct DecodeParams {
     const uint32_t *kinds;  // bit 0: some valid buffer has full tables, bit 1: some has sampled ones
 };
 
-// events recorded around the main coding kernel (benchmark instrumentation)
+// events the caller asks to have recorded around the main coding kernel
+// (benchmark instrumentation; passed per call, never kept)
 struct ProfileEvents {
     hipEvent_t start = nullptr;
     hipEvent_t stop = nullptr;
 };
-extern thread_local ProfileEvents g_profile;
 
-hipError_t launch_compress(const EncParams &ep, hipStream_t stream);
+hipError_t launch_compress(const EncParams &ep, hipStream_t stream, const ProfileEvents *ev = nullptr);
 hipError_t launch_decompress(const DecParams &vp, const DecodeParams &dp, int dtype, uint64_t max_chunks,
-                             hipStream_t stream);
+                             hipStream_t stream, const ProfileEvents *ev = nullptr);
 
 }  // namespace uzip

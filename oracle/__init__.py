@@ -46,7 +46,7 @@ def build(force: bool = False) -> str:
         return os.environ["UZIP_ORACLE_LIB"]
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
         tmp = _LIB + ".tmp%d" % os.getpid()
-        subprocess.check_call(["gcc", "-O2", "-std=c11", "-Wall", "-shared", "-fPIC", "-o", tmp, _SRC])
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-Wall", "-shared", "-fPIC", "-o", tmp, _SRC, "-lm"])
         os.replace(tmp, _LIB)
     return _LIB
 
@@ -89,6 +89,8 @@ def lib():
         _lib.orc_log2_q16.argtypes = [ctypes.c_uint32]
         _lib.orc_plan_call.restype = i32
         _lib.orc_plan_call.argtypes = [i32, vp, u64, u64, vp, vp]
+        _lib.orc_entropy_bound.restype = ctypes.c_double
+        _lib.orc_entropy_bound.argtypes = [i32, vp, u64, u64]
         _lib.orc_compress_arbitrated.restype = i32
         _lib.orc_compress_arbitrated.argtypes = [i32, vp, u64, u64, vp, vp, vp, u64, vp]
     return _lib
@@ -191,6 +193,16 @@ def rans_decode(states, words, n: int, f, c0, lanes: int = LANES):
 
 def max_compressed_size(dtype: int, n: int, chunk_bytes: int = 0) -> int:
     return int(lib().orc_max_compressed_size(dtype, n, chunk_bytes))
+
+
+def entropy_bound(dtype: int, values, chunk_bytes: int = 0) -> float:
+    """Bytes an ideal per-chunk coder of the coded symbols would reach: the raw
+    bytes plus, per chunk, n_i times the empirical entropy of its symbols / 8."""
+    v = _bits(dtype, values)
+    r = float(lib().orc_entropy_bound(dtype, _p(v) if v.size else None, v.size, chunk_bytes))
+    if r < 0:
+        raise ValueError("invalid chunk_bytes")
+    return r
 
 
 def compress(dtype: int, values, chunk_bytes: int = 0) -> np.ndarray:

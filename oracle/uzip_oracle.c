@@ -42,8 +42,9 @@
  * (hand-derived traces, closed forms, brute force, invariants, library
  * routines); none is "parity unpinned".
  *
- * Build: gcc -O2 -std=c11 -shared -fPIC -o liboracle.so uzip_oracle.c
+ * Build: gcc -O2 -std=c11 -shared -fPIC -o liboracle.so uzip_oracle.c -lm
  */
+#include <math.h>
 #include <stddef.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -400,6 +401,38 @@ uint64_t orc_max_compressed_size(int dtype, uint64_t n, uint64_t chunk_bytes) {
     return total;
 }
 
+/* The entropy bound of a buffer in bytes: for every chunk, its raw
+ * sign+mantissa bytes plus n_i H_i / 8, where H_i is the empirical entropy
+ * (bits per value) of the chunk's coded symbols, -sum_s (c_s / n_i)
+ * log2(c_s / n_i) over the chunk's histogram.  It is the size an ideal coder
+ * of each chunk's symbols with the chunk's own table would reach, with no
+ * table, state or framing bytes; the compressed size is measured against it.
+ * Computed in binary64. */
+double orc_entropy_bound(int dtype, const void *in, uint64_t n, uint64_t chunk_bytes) {
+    uint64_t ce = orc_chunk_elems(dtype, chunk_bytes);
+    if (ce == 0) return -1.0;
+    int r = orc_raw_bytes(dtype);
+    uint8_t *e = (uint8_t *)malloc((size_t)(n ? n : 1));
+    uint8_t *sm = (uint8_t *)malloc((size_t)(n * (uint64_t)r + 1));
+    orc_split(dtype, in, n, e, sm);
+    free(sm);
+    double total = (double)r * (double)n;
+    for (uint64_t c0 = 0; c0 < n; c0 += ce) {
+        uint64_t ni = n - c0 < ce ? n - c0 : ce;
+        uint32_t counts[256];
+        orc_histogram(e + c0, ni, counts);
+        double bits = 0.0;
+        for (int s = 0; s < 256; ++s) {
+            if (counts[s] == 0) continue;
+            double p = (double)counts[s] / (double)ni;
+            bits -= (double)counts[s] * log2(p);
+        }
+        total += bits / 8.0;
+    }
+    free(e);
+    return total;
+}
+
 /* Encode one chunk's record (steps 2-4 plus the RANS/RAW choice) into rec,
  * which must hold align16(16 + ni) bytes.  Returns the record size. */
 static uint64_t orc_encode_record(const uint8_t *e, uint64_t ni, uint8_t *rec, int force_raw) {
@@ -609,10 +642,14 @@ int orc_compress_sampled(int dtype, const void *in, uint64_t n, uint64_t chunk_b
  * min(N, 65536 / bytes-per-value) values (at most 64 KiB, the pages' sample
  * bound); the coded-size prediction is the sample's empirical entropy per
  * value times N, plus each chunk's fixed record part and half a padding unit;
- * logarithms are 2^16 log2 x in integers, by the squaring method.  The post-check
- * of the realised frame is not needed: a chunk is stored RAW whenever coding
- * would not make it strictly smaller, so a coded frame is never larger than
- * the RAW frame. */
+ * logarithms are 2^16 log2 x in integers, by the squaring method.
+ * Algorithm 1 accepts a materialised coded frame only if it passes the same
+ * checks on its realised size (capacity and gain); otherwise it commits the
+ * RAW frame.  Capacity always holds here (a coded frame is never larger than
+ * the RAW frame, whose size is the output's capacity); the gain check is the
+ * admission rule with the realised size R in place of P:
+ * R < P_raw and (P_raw - R) * 1000 >= min_gain * B.  A coded plan that fails
+ * it becomes decision 3 and writes the all-RAW frame. */
 typedef struct {
     uint64_t link_bytes_per_us;   /* beta_eff, > 0 */
     uint64_t encode_bytes_per_us; /* E = B / encode rate, rate > 0 */
@@ -626,7 +663,8 @@ typedef struct {
 } orc_policy;
 
 typedef struct {
-    uint32_t decision; /* 0 coded, 1 RAW by the cost model, 2 RAW as a small call */
+    uint32_t decision; /* 0 coded, 1 RAW by the cost model, 2 RAW as a small call,
+                          3 RAW because the realised coded frame failed the gain check */
     uint32_t sample_values;
     uint64_t predicted_bytes;
     uint64_t raw_ns;
@@ -712,12 +750,22 @@ int orc_plan_call(int dtype, const void *in, uint64_t n, uint64_t chunk_bytes, c
     return ORC_OK;
 }
 
-/* Plan the call, then write the frame the plan chose. */
+/* Plan the call, write the frame the plan chose, and check a coded frame's
+ * realised gain (Algorithm 1's acceptance of the materialised plan): one that
+ * fails it is replaced by the RAW frame. */
 int orc_compress_arbitrated(int dtype, const void *in, uint64_t n, uint64_t chunk_bytes, const orc_policy *pol,
                             orc_plan *plan, uint8_t *out, uint64_t cap, uint64_t *out_size) {
     int st = orc_plan_call(dtype, in, n, chunk_bytes, pol, plan);
     if (st != ORC_OK) return st;
-    return orc_compress_frame(dtype, in, n, chunk_bytes, out, cap, out_size, plan->decision != 0, 0);
+    st = orc_compress_frame(dtype, in, n, chunk_bytes, out, cap, out_size, plan->decision != 0, 0);
+    if (st != ORC_OK || plan->decision != 0) return st;
+    uint64_t B = n * (uint64_t)orc_elem_bytes(dtype);
+    uint64_t P_raw = orc_max_compressed_size(dtype, n, chunk_bytes);
+    uint64_t R = *out_size;
+    int accepted = R < P_raw && (P_raw - R) * 1000 >= (uint64_t)pol->min_gain_permil * B;
+    if (accepted) return ORC_OK;
+    plan->decision = 3;
+    return orc_compress_frame(dtype, in, n, chunk_bytes, out, cap, out_size, 1, 0);
 }
 
 /* Decode one record into the chunk's exponents.  rec holds rec_len bytes
@@ -740,6 +788,11 @@ static int orc_decode_record(const uint8_t *rec, uint64_t rec_len, uint64_t ni, 
     }
     /* a frame uses one kind of coded record: mode 0 (full histograms) or mode 2 (sampled) */
     if ((mode == 2) != (sampled != 0)) return ORC_CORRUPT;
+    /* a coded record exists only because it is strictly smaller than the
+     * chunk's RAW record (the RAW rule, NCCLZ Sec. IV-C); one that is not is
+     * rejected, so no record is ever longer than its RAW record and the
+     * all-RAW size bounds every valid frame */
+    if (rec_len >= orc_align16(ORC_REC_HDR + ni)) return ORC_CORRUPT;
     if (mode == 2) return orc_decode_record_sampled(rec, rec_len, ni, nsym, n_words, e);
     /* RANS: bitmap, frequencies, states, words */
     if (rec_len < ORC_REC_HDR + 32) return ORC_CORRUPT;

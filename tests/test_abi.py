@@ -168,3 +168,35 @@ def test_arbitrated_argument_errors_return_synchronously():
     assert bcall(policy=_policy(min_gain_permil=2000)) == uz.UZIP_ERR_INVALID_ARGUMENT
     assert bcall(d_plans=None) == uz.UZIP_ERR_INVALID_ARGUMENT
     assert bcall() == uz.UZIP_ERR_INVALID_ARGUMENT  # no workspace
+
+
+def test_outputs_allocated_for_another_stream_are_recorded_on_it(monkeypatch):
+    """Tensors the wrappers allocate on the current stream but hand to kernels
+    on another stream are recorded on that stream (record_stream), so torch's
+    caching allocator cannot reuse their memory before those kernels finish;
+    nothing is recorded when the stream is the current one or None."""
+    import torch
+
+    class FakeStream:
+        device = "cuda:0"
+
+    class FakeTensor(torch.Tensor):
+        pass
+
+    current, side = FakeStream(), FakeStream()
+    monkeypatch.setattr(torch.cuda, "current_stream", lambda device=None: current)
+    seen = []
+
+    class T:
+        def __init__(self, name):
+            self.name = name
+
+        def record_stream(self, s):
+            seen.append((self.name, s))
+
+    monkeypatch.setattr(torch, "Tensor", T)
+    uz._keep_for(None, T("a"))
+    uz._keep_for(current, T("b"))
+    assert seen == []
+    uz._keep_for(side, T("out"), [T("o1"), T("o2")], T("ws"))
+    assert seen == [("out", side), ("o1", side), ("o2", side), ("ws", side)]

@@ -150,3 +150,77 @@ def test_oracle_reports_every_raw_record_corruption(dtype):
     assert orc.decompress(buf, dtype, bits.size)[0] == orc.OK
     for name, bad in raw_corruptions(buf):
         assert orc.decompress(bad, dtype, bits.size)[0] == orc.CORRUPT, name
+
+
+def _prefix_compressible(seed=5):
+    """bf16, 8 chunks of 64 KiB: the first chunk (exactly the 64 KiB sample)
+    near-Gaussian, the other seven random bit patterns.  The sample predicts
+    a frame about two thirds of the payload; the realised frame codes one
+    chunk and stores seven RAW."""
+    rng = np.random.default_rng(seed)
+    head = workloads.bits_numpy(workloads.pr1())[:32768]
+    tail = rng.integers(0, 1 << 16, 7 * 32768, dtype=np.uint32).astype(np.uint16)
+    return np.concatenate([head, tail])
+
+
+def test_realised_gain_check_commits_raw():
+    """NCCLZ Algorithm 1 accepts a materialised coded frame only if its
+    realised size passes the gain check; otherwise the RAW frame is committed
+    (decision 3).  The rule's boundary is found from the sizes alone: the
+    realised size R of the coded frame (what uzip_compress writes), the RAW
+    frame P_raw and B = 2N; the largest minimum gain that R meets is
+    g* = floor((P_raw - R) * 1000 / B)."""
+    bits = _prefix_compressible()
+    B = 2 * bits.size
+    P_raw = orc.max_compressed_size(orc.BF16, bits.size)
+    coded = orc.compress(orc.BF16, bits)
+    R = coded.size
+    assert R < P_raw
+    g_star = (P_raw - R) * 1000 // B
+    slow = dict(link_bytes_per_us=1000)  # coding pays on a slow link
+    plan = orc.plan_call(orc.BF16, bits, policy(**slow, min_gain_permil=g_star + 1))
+    # the prefix over-predicts: coding is admitted and chosen...
+    assert plan["decision"] == 0
+    assert (P_raw - plan["predicted_bytes"]) * 1000 >= (g_star + 1) * B
+    # ...and at g* + 1 the realised frame fails the check: the RAW frame is committed
+    buf, plan = orc.compress_arbitrated(orc.BF16, bits, policy(**slow, min_gain_permil=g_star + 1))
+    assert plan["decision"] == 3
+    assert buf.size == P_raw
+    assert all(r["mode"] == 1 for r in parse_buffer(buf)[2])
+    st, back = orc.decompress(buf, orc.BF16, bits.size)
+    assert st == orc.OK and np.array_equal(back, bits)
+    raw_plan, p1 = orc.compress_arbitrated(orc.BF16, bits, policy(link_bytes_per_us=10**9))
+    assert p1["decision"] == 1 and np.array_equal(buf, raw_plan)
+    # at g* it passes: the coded frame is committed
+    buf, plan = orc.compress_arbitrated(orc.BF16, bits, policy(**slow, min_gain_permil=g_star))
+    assert plan["decision"] == 0 and np.array_equal(buf, coded)
+    # the plan's other fields are those of the prediction, unchanged by the check
+    p_pred = orc.plan_call(orc.BF16, bits, policy(**slow, min_gain_permil=g_star + 1))
+    _, p_real = orc.compress_arbitrated(orc.BF16, bits, policy(**slow, min_gain_permil=g_star + 1))
+    assert {k: v for k, v in p_real.items() if k != "decision"} == {k: v for k, v in p_pred.items() if k != "decision"}
+
+
+def test_realised_check_on_iid_data_keeps_the_coded_frame():
+    """On i.i.d. data the prediction is close (within 1%), so a coded plan
+    admitted with a margin is also accepted once realised."""
+    bits = workloads.bits_numpy(workloads.pr1())
+    buf, plan = orc.compress_arbitrated(orc.BF16, bits, policy(min_gain_permil=300))
+    assert plan["decision"] == 0 and np.array_equal(buf, orc.compress(orc.BF16, bits))
+
+
+def test_realised_gain_boundary_is_inclusive():
+    """A realised gain exactly at the minimum passes, as the admission rule
+    does (gain * 1000 >= min_gain * B).  80,000 bf16 values: the first 32,768
+    are PR1's first chunk (its coded record is 22,240 bytes below its RAW
+    record), the rest random bits stored RAW, so P_raw - R = 22,240 and
+    22,240 * 1000 = 139 * B exactly (B = 160,000)."""
+    head = workloads.bits_numpy(workloads.pr1())[:32768]
+    tail = np.random.default_rng(1).integers(0, 1 << 16, 80000 - 32768, dtype=np.uint32).astype(np.uint16)
+    bits = np.concatenate([head, tail])
+    B = 2 * bits.size
+    coded = orc.compress(orc.BF16, bits)
+    assert orc.max_compressed_size(orc.BF16, bits.size) - coded.size == 22240 and 22240 * 1000 == 139 * B
+    buf, plan = orc.compress_arbitrated(orc.BF16, bits, policy(link_bytes_per_us=1000, min_gain_permil=139))
+    assert plan["decision"] == 0 and np.array_equal(buf, coded)
+    _, plan = orc.compress_arbitrated(orc.BF16, bits, policy(link_bytes_per_us=1000, min_gain_permil=140))
+    assert plan["decision"] == 3

@@ -32,7 +32,10 @@ int main(int argc, char **argv) {
         r |= uzip_decompress_batched(UZIP_FP8_E4M3, 1, in, inb, n, out, st, out[0], 0, s);
         r |= uzip_compress_arbitrated(UZIP_FP8_E5M2, in[0], 0, 0, &pol, out[0], 0, sz, plan, out[0], 0, s);
         r |= uzip_compress_batched_arbitrated(UZIP_BF16, 1, in, n, 0, &pol, out, cap, sz, plan, out[0], 0, s);
-        r |= uzip_profile_set_events(0, 0);
+        r |= uzip_compress_sampled(UZIP_BF16, in[0], 0, 0, out[0], 0, sz, out[0], 0, s);
+        r |= uzip_compress_batched_sampled(UZIP_FP32, 1, in, n, 0, out, cap, sz, out[0], 0, s);
+        r |= uzip_compress_batched_timed(UZIP_BF16, 1, in, n, 0, 0u, &pol, out, cap, sz, plan, out[0], 0, s, 0, 0);
+        r |= uzip_decompress_batched_timed(UZIP_BF16, 1, in, inb, n, out, st, out[0], 0, s, 0, 0);
         return r;
     }
     size_t nb[2] = {1000, 70000};

@@ -177,3 +177,55 @@ def test_corrupt_raw_frames_are_reported(tdtype):
         assert st == (uz.UZIP_ERR_CORRUPT_INPUT if want == orc.CORRUPT else 0), name
         n_bad += want == orc.CORRUPT
     assert n_bad == 13  # every one of them is a corruption the oracle reports
+
+
+def _prefix_compressible(n=8 * 32768, seed=5):
+    """bf16: a near-Gaussian first 64 KiB chunk (the sample), random bits after it."""
+    head = workloads.bits_numpy(workloads.pr1())[:32768]
+    tail = np.random.default_rng(seed).integers(0, 1 << 16, n - 32768, dtype=np.uint32).astype(np.uint16)
+    return np.concatenate([head, tail])
+
+
+def test_realised_gain_check_on_the_gpu():
+    """A prefix that over-predicts: the plan codes, the realised frame fails
+    the gain check, and the device commits the all-RAW frame (decision 3),
+    as the oracle does; at the exact boundary (g* = floor((P_raw - R) 1000 / B))
+    the coded frame stays."""
+    bits = _prefix_compressible()
+    B = 2 * bits.size
+    R = orc.compress(orc.BF16, bits).size
+    g_star = (orc.max_compressed_size(orc.BF16, bits.size) - R) * 1000 // B
+    plan, got = check_arbitrated(bits, torch.bfloat16, link_bytes_per_us=1000, fixed_ns=0,
+                                 min_gain_permil=g_star + 1)
+    assert plan["decision"] == uz.UZIP_PLAN_RAW_REALIZED
+    assert all(r["mode"] == 1 for r in parse_buffer(got)[2])
+    plan, got = check_arbitrated(bits, torch.bfloat16, link_bytes_per_us=1000, fixed_ns=0, min_gain_permil=g_star)
+    assert plan["decision"] == uz.UZIP_PLAN_CODED and got.size == R
+
+
+def test_realised_check_in_a_batch():
+    """One batched call in which every decision occurs: coded and kept, coded
+    then rejected once realised, RAW by the model, and the small path; each
+    buffer equals its own oracle call."""
+    good = workloads.bits_numpy(workloads.pr1())[:5 * 32768]
+    bad = _prefix_compressible(6 * 32768, seed=6)
+    rand = np.random.default_rng(8).integers(0, 1 << 16, 70_000, dtype=np.uint32).astype(np.uint16)
+    small = good[:1000].copy()
+    bits = [good, bad, rand, small, bad[:32768 + 5000].copy()]
+    kw = dict(link_bytes_per_us=1000, fixed_ns=0, small_bytes=4096, min_gain_permil=150)
+    gp, op = both_policies(**kw)
+    ts = [_bits_tensor(b, torch.bfloat16) for b in bits]
+    outs, sizes, plans = uz.compress_batched_arbitrated(ts, gp)
+    torch.cuda.synchronize()
+    got_plans = uz.plans_as_dicts(plans)
+    for b, o, s, p in zip(bits, outs, sizes.cpu().tolist(), got_plans):
+        want, want_plan = orc.compress_arbitrated(orc.BF16, b, op)
+        assert p == want_plan
+        assert np.array_equal(o[:s].cpu().numpy(), want)
+    assert [p["decision"] for p in got_plans] == [0, 3, 1, 2, 0]
+    vals, status = uz.decompress_batched([o[:s] for o, s in zip(outs, sizes.cpu().tolist())], torch.bfloat16,
+                                         [b.size for b in bits])
+    torch.cuda.synchronize()
+    assert status.cpu().tolist() == [0] * len(bits)
+    for t, v in zip(ts, vals):
+        assert torch.equal(_int_view(t), _int_view(v))

@@ -69,3 +69,36 @@ def test_random_corruptions_match_the_oracle_verdict(which):
             assert np.array_equal(got, oval), "%s copy %d: values differ" % (name, i)
     # the sweep reaches both verdicts
     assert 0 < accepted < COPIES, name
+
+
+def test_coded_records_not_smaller_than_raw_get_the_oracle_verdict():
+    """Frames with valid rANS streams whose coded record is longer than the
+    chunk's RAW record (table {120: 4095, 121: 1}, 49,344 bytes against
+    32,784), exactly its size, or 16 bytes smaller: the GPU decoder gives each
+    the oracle's verdict (corrupt, corrupt, valid), decoded in one batched
+    call.  These are ordinary rejected decodes."""
+    from uzip_testlib import coded_frame, long_record_frame, parse_buffer
+    frames = [long_record_frame(orc.rans_encode)]
+    sized = {}
+    for k in range(21700, 21900):
+        sym = np.full(32768, 120, np.uint8)
+        sym[:k] = 121
+        fr = coded_frame(sym, {120: 4095, 121: 1}, orc.rans_encode)
+        size = parse_buffer(fr[0])[2][0]["bytes"]
+        if size in (32784, 32768) and size not in sized:
+            sized[size] = fr
+        if len(sized) == 2:
+            break
+    frames += [sized[32784], sized[32768]]
+    want = [orc.decompress(f, orc.BF16, v.size) for f, v in frames]
+    assert [w[0] for w in want] == [orc.CORRUPT, orc.CORRUPT, orc.OK]
+    bufs = [torch.from_numpy(f).to(DEV) for f, _ in frames]
+    vals, status = uz.decompress_batched(bufs, torch.bfloat16, [v.size for _, v in frames])
+    torch.cuda.synchronize()
+    assert status.cpu().tolist() == [3, 3, 0]
+    assert np.array_equal(vals[2].view(torch.int16).cpu().numpy().view(np.uint16), frames[2][1])
+    # and each alone, through the single-buffer call
+    for (f, v), (ost, _) in zip(frames, want):
+        out, st = uz.decompress(torch.from_numpy(f).to(DEV), torch.bfloat16, v.size)
+        torch.cuda.synchronize()
+        assert (int(st.item()) == 0) == (ost == orc.OK)

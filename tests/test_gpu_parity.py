@@ -276,3 +276,26 @@ def test_header_flags():
     assert st == uz.UZIP_ERR_CORRUPT_INPUT
     out, st = gpu_decompress(full, torch.bfloat16, bits.size)
     assert st == 0 and np.array_equal(out.view(torch.int16).cpu().numpy().view(np.uint16), bits)
+
+
+def test_calls_on_a_side_stream():
+    """Compress and decompress enqueued on a non-current stream, with the
+    outputs and workspaces the wrappers allocate (recorded on that stream),
+    while the current stream allocates and writes other memory meanwhile."""
+    bits = workloads.bits_numpy(workloads.gradient_bucket(300_001, seed=21, special_frac=1e-3))
+    t = _bits_tensor(bits)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    buf, size = uz.compress(t, stream=side)
+    junk = [torch.full((1 << 20,), 7, dtype=torch.uint8, device=DEV) for _ in range(8)]  # reuse pressure
+    side.synchronize()
+    got = buf[:int(size.item())].cpu().numpy()
+    assert np.array_equal(got, orc.compress(orc.BF16, bits))
+    out, st = uz.decompress(buf[:got.size], torch.bfloat16, bits.size, stream=side)
+    junk += [torch.full((1 << 20,), 9, dtype=torch.uint8, device=DEV) for _ in range(8)]
+    side.synchronize()
+    assert int(st.item()) == 0 and torch.equal(_int_view(out), _int_view(t))
+    outs, sizes = uz.compress_batched([t, t[:1000]], stream=side)
+    side.synchronize()
+    assert np.array_equal(outs[1][:int(sizes[1].item())].cpu().numpy(), orc.compress(orc.BF16, bits[:1000]))
+    del junk

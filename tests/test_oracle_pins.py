@@ -19,7 +19,7 @@ import torch
 
 import oracle as orc
 import workloads
-from uzip_testlib import corruptions as _corruptions, parse_buffer
+from uzip_testlib import coded_frame, corruptions as _corruptions, long_record_frame, parse_buffer
 
 GOLD = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
@@ -492,6 +492,65 @@ def test_corruption_detected():
     assert st == orc.CORRUPT
 
 
+def test_coded_record_longer_than_raw_is_rejected():
+    """A coded record exists only because it is strictly smaller than the
+    chunk's RAW record (the RAW rule of NCCLZ Sec. IV-C); a frame whose coded
+    record is longer (non-canonical table {120: 4095, 121: 1} over 32,768
+    values of exponent 121: 24,576 words, 49,344 bytes against 32,784 RAW) is
+    corrupt, although its rANS stream itself decodes."""
+    buf, values = long_record_frame(orc.rans_encode)
+    hdr, idx, recs = parse_buffer(buf)
+    rec = recs[0]
+    assert rec["mode"] == 0 and rec["n_words"] == 24576 and rec["bytes"] == 49344
+    assert rec["bytes"] > (16 + 32768 + 15) // 16 * 16 == 32784
+    # the stream alone is valid: it decodes to the chunk's exponents
+    f = np.zeros(256, np.uint32)
+    f[120], f[121] = 4095, 1
+    c0 = orc.cumulative(f)
+    words_at = (16 + 32 + 2 * 2 + 3) // 4 * 4 + 128
+    words = np.frombuffer(rec["raw"][words_at:words_at + 2 * 24576], "<u2")
+    st, sym = orc.rans_decode(np.array(rec["states"], np.uint32), words, 32768, f, c0)
+    assert st == orc.OK and np.all(sym == 121)
+    # ...but the frame is rejected for the record length alone
+    st, _ = orc.decompress(buf, orc.BF16, values.size)
+    assert st == orc.CORRUPT
+    # and the canonical frame of the same values is a RANS record of 0 words
+    good = orc.compress(orc.BF16, values)
+    st, back = orc.decompress(good, orc.BF16, values.size)
+    assert st == orc.OK and np.array_equal(back, values)
+    assert parse_buffer(good)[2][0]["n_words"] == 0
+
+
+def _raw_sized_records():
+    """Two valid one-chunk frames (32,768 bf16 values, table {120: 4095, 121: 1},
+    the first k values of exponent 121 and the rest 120): one whose coded
+    record is exactly the RAW record's 32,784 bytes, one 16 bytes smaller."""
+    out = {}
+    for k in range(21700, 21900):
+        sym = np.full(32768, 120, np.uint8)
+        sym[:k] = 121
+        buf, values = coded_frame(sym, {120: 4095, 121: 1}, orc.rans_encode)
+        size = parse_buffer(buf)[2][0]["bytes"]
+        if size in (32784, 32768) and size not in out:
+            out[size] = (buf, values)
+        if len(out) == 2:
+            return out
+    raise AssertionError("no k gives both record sizes")
+
+
+def test_coded_record_bound_is_strict():
+    """The bound is strict, as the mode rule is: a chunk is coded only when
+    that is strictly smaller than RAW.  A coded record of exactly the RAW size
+    (a valid stream) is rejected; one 16 bytes smaller is accepted."""
+    recs = _raw_sized_records()
+    buf, values = recs[32784]
+    st, _ = orc.decompress(buf, orc.BF16, values.size)
+    assert st == orc.CORRUPT
+    buf, values = recs[32768]
+    st, back = orc.decompress(buf, orc.BF16, values.size)
+    assert st == orc.OK and np.array_equal(back, values)
+
+
 # ---- fp16 and fp8 payloads (UCCL-Zip Fig. 13 types): the coded symbol is the
 # byte that holds the exponent, the rest is raw --------------------------------
 def test_split_fp16_exhaustive_is_the_byte_planes():
@@ -588,3 +647,36 @@ def test_new_dtypes_within_one_percent_of_entropy_bound(dtype):
         buf = orc.compress(dtype, bits, chunk_bytes)
         bound = entropy_bound_bytes(dtype, bits, orc.chunk_elems(dtype, chunk_bytes))
         assert buf.size <= tol * bound, (chunk_bytes, buf.size / bound)
+
+
+# --------------------------------------------------------------------------
+# the entropy bound the compressed sizes are measured against
+# --------------------------------------------------------------------------
+def test_entropy_bound_closed_forms():
+    """Per chunk: raw bytes + n_i H_i / 8.  A constant chunk has H = 0; a chunk
+    of 2^k equally frequent exponents has H = k bits exactly; the histogram is
+    per chunk (two constant chunks of different exponents have H = 0 each,
+    where one histogram over both would give 1 bit)."""
+    ce = 32768
+    const = np.full(ce, 0x3F80, np.uint16)  # exponent 127
+    assert orc.entropy_bound(orc.BF16, const) == ce
+    for k in (1, 2, 3, 5, 8):
+        e = np.arange(ce) % (1 << k)
+        v = ((e + (0 if k == 8 else 100)) << 7).astype(np.uint16)
+        assert orc.entropy_bound(orc.BF16, v) == pytest.approx(ce + ce * k / 8, abs=1e-6)
+    two = np.concatenate([np.full(ce, 100 << 7, np.uint16), np.full(ce, 101 << 7, np.uint16)])
+    assert orc.entropy_bound(orc.BF16, two) == 2 * ce
+    # fp32: three raw bytes per value; a 256 KiB chunk of two exponents, half each
+    f = np.where(np.arange(65536) % 2 == 0, 1.5, 3.0).astype(np.float32).view(np.uint32)
+    assert orc.entropy_bound(orc.FP32, f) == pytest.approx(3 * 65536 + 65536 / 8, abs=1e-6)
+    # a ragged last chunk is its own chunk
+    tail = np.concatenate([np.full(ce, 100 << 7, np.uint16), (np.arange(64) % 4 + 100 << 7).astype(np.uint16)])
+    assert orc.entropy_bound(orc.BF16, tail) == pytest.approx(ce + 64 + 64 * 2 / 8, abs=1e-6)
+
+
+def test_entropy_bound_pr1_matches_the_survey_figure():
+    """PR1 (1,048,576 bf16 values N(0, 0.02^2), seed 0): 0.6590 of the input,
+    the figure computed independently with numpy when the workloads were
+    specified."""
+    b = workloads.bits_numpy(workloads.pr1())
+    assert orc.entropy_bound(orc.BF16, b) / (2 * b.size) == pytest.approx(0.6590, abs=5e-5)

@@ -100,3 +100,65 @@ def raw_corruptions(buf):
     yield "raw_n_values", patch(base + 8, rec["n_values"] - 1, 4)
     yield "raw_bytes", patch(base + 12, rec["bytes"] - 16, 4)
     yield "raw_as_rans", patch(base, 0, 1)
+
+
+
+def coded_frame(sym, ftab, rans_encode):
+    """A bf16 frame of one chunk holding len(sym) <= 32,768 values whose
+    exponents are `sym` (sign+mantissa 0), its record coded (mode 0) with the
+    explicit table `ftab` ({symbol: frequency}, summing to 4096) whether or
+    not that is canonical.  The states and words come from `rans_encode` (the
+    oracle's coder), so the stream decodes.  Returns (frame, values)."""
+    sym = np.ascontiguousarray(sym, np.uint8)
+    n, ce = sym.size, 32768
+    f = np.zeros(256, np.uint32)
+    for k, v in ftab.items():
+        f[k] = v
+    c0 = np.concatenate([[0], np.cumsum(f)[:-1]]).astype(np.uint32)
+    states, words = rans_encode(sym, f, c0)
+    syms = sorted(ftab)
+    nsym = len(syms)
+    tab_end = (16 + 32 + 2 * nsym + 3) // 4 * 4
+    words_at = tab_end + 4 * 32
+    rec_bytes = (words_at + 2 * words.size + 15) // 16 * 16
+    rec = np.zeros(rec_bytes, np.uint8)
+
+    def put_to(a, off, val, width):
+        a[off:off + width] = np.frombuffer(int(val).to_bytes(width, "little"), np.uint8)
+
+    put_to(rec, 2, nsym, 2)
+    put_to(rec, 4, words.size, 4)
+    put_to(rec, 8, n, 4)
+    put_to(rec, 12, rec_bytes, 4)
+    for k, s_ in enumerate(syms):
+        rec[16 + s_ // 8] |= 1 << (s_ % 8)
+        put_to(rec, 48 + 2 * k, ftab[s_], 2)
+    rec[tab_end:words_at] = states.astype("<u4").view(np.uint8)
+    rec[words_at:words_at + 2 * words.size] = words.astype("<u2").view(np.uint8)
+    C = 1
+    sm_off = (64 + 8 * (C + 1) + 15) // 16 * 16
+    exp_off = (sm_off + n + 15) // 16 * 16
+    total = exp_off + rec_bytes
+    buf = np.zeros(total, np.uint8)
+    put_to(buf, 0, 0x31505A55, 4)
+    put_to(buf, 4, 1, 2)
+    buf[6], buf[7], buf[8], buf[9] = 1, 12, 32, 1
+    put_to(buf, 12, ce, 4)
+    put_to(buf, 16, n, 8)
+    put_to(buf, 24, C, 8)
+    put_to(buf, 32, sm_off, 8)
+    put_to(buf, 40, exp_off, 8)
+    put_to(buf, 48, total, 8)
+    put_to(buf, 72, rec_bytes, 8)
+    buf[exp_off:] = rec
+    values = (sym.astype(np.uint16) << 7).astype(np.uint16)
+    return buf, values
+
+
+def long_record_frame(rans_encode):
+    """One full 64 KiB bf16 chunk (32,768 values, all exponent 121) coded with
+    the valid but non-canonical table {120: 4095, 121: 1}: every value costs
+    ~12 bits, so the record (24,576 words, 49,344 bytes) is longer than the
+    chunk's RAW record (32,784 bytes); only the record-length rule can reject
+    the frame."""
+    return coded_frame(np.full(32768, 121, np.uint8), {120: 4095, 121: 1}, rans_encode)
