@@ -174,11 +174,10 @@ bool policy_ok(const uzip_policy *p) {
 
 // Shared body of the single and batched compress calls (plans non-null: the
 // arbitrated forms).
-uzip_status compress_impl(uzip_dtype dtype, uint64_t ce, std::vector<EncDesc> &descs, uint64_t chunks,
+uzip_status compress_impl(uzip_dtype dtype, uint64_t ce, EncDesc *descs, uint32_t nbuf, uint64_t chunks,
                           void *d_workspace, size_t workspace_bytes, hipStream_t stream,
                           uzip_plan *plans = nullptr, const uzip_policy *policy = nullptr, bool sampled = false,
                           const ProfileEvents *ev = nullptr) {
-    const uint32_t nbuf = (uint32_t)descs.size();
     const EncWs w = enc_ws(nbuf, chunks, ce);
     if (d_workspace == nullptr || workspace_bytes < w.bytes || !aligned(d_workspace, 16))
         return UZIP_ERR_INVALID_ARGUMENT;
@@ -189,7 +188,8 @@ uzip_status compress_impl(uzip_dtype dtype, uint64_t ce, std::vector<EncDesc> &d
     ep.total_chunks = chunks;
     ep.total_pairs = 0;
     uint64_t tiles = 0;
-    for (EncDesc &d : descs) {
+    for (uint32_t b = 0; b < nbuf; ++b) {
+        EncDesc &d = descs[b];
         const uint64_t pairs = (d.chunks + 1) / 2;
         d.pair_first = ep.total_pairs;
         d.tile_first = tiles;
@@ -210,7 +210,7 @@ uzip_status compress_impl(uzip_dtype dtype, uint64_t ce, std::vector<EncDesc> &d
         ep.descs = nullptr;
     } else {
         EncDesc *dd = reinterpret_cast<EncDesc *>(base + w.descs);
-        if (!stage_copy(dd, descs.data(), nbuf * sizeof(EncDesc), stream)) return UZIP_ERR_DEVICE;
+        if (!stage_copy(dd, descs, nbuf * sizeof(EncDesc), stream)) return UZIP_ERR_DEVICE;
         ep.descs = dd;
     }
     const hipError_t e = launch_compress(ep, stream, ev);
@@ -229,10 +229,9 @@ uzip_status compress_single(uzip_dtype dtype, const void *d_in, size_t num_eleme
         return UZIP_ERR_INVALID_ARGUMENT;
     if (out_capacity < max_size(dtype, num_elements, ce)) return UZIP_ERR_CAPACITY;
     const Layout l = layout_of(dtype, num_elements, ce);
-    std::vector<EncDesc> descs(1);
-    descs[0] = EncDesc{static_cast<const uint8_t *>(d_in), static_cast<uint8_t *>(d_out), d_out_size, num_elements,
-                       0, l.sm_off, l.exp_off, l.chunks, 0, 0};
-    return compress_impl(dtype, ce, descs, l.chunks, d_workspace, workspace_bytes, stream,
+    EncDesc desc{static_cast<const uint8_t *>(d_in), static_cast<uint8_t *>(d_out), d_out_size, num_elements,
+                 0, l.sm_off, l.exp_off, l.chunks, 0, 0};
+    return compress_impl(dtype, ce, &desc, 1, l.chunks, d_workspace, workspace_bytes, stream,
                          policy ? d_plan : nullptr, policy, sampled);
 }
 
@@ -246,7 +245,9 @@ uzip_status compress_batched(uzip_dtype dtype, size_t num_buffers, const void *c
     if (!ce || num_buffers == 0 || num_buffers > 0xFFFFFFFFull) return UZIP_ERR_INVALID_ARGUMENT;
     if (!h_in || !h_num_elements || !h_out || !h_out_capacity || !d_out_sizes || !aligned(d_out_sizes, 8))
         return UZIP_ERR_INVALID_ARGUMENT;
-    std::vector<EncDesc> descs(num_buffers);
+    // (kept per thread across calls: no heap allocation once it has grown)
+    thread_local std::vector<EncDesc> descs;
+    if (descs.size() < num_buffers) descs.resize(num_buffers);
     uint64_t chunks = 0;
     for (size_t b = 0; b < num_buffers; ++b) {
         const uint64_t n = h_num_elements[b];
@@ -259,19 +260,19 @@ uzip_status compress_batched(uzip_dtype dtype, size_t num_buffers, const void *c
                            chunks, l.sm_off, l.exp_off, l.chunks, 0, 0};
         chunks += l.chunks;
     }
-    return compress_impl(dtype, ce, descs, chunks, d_workspace, workspace_bytes, stream,
+    return compress_impl(dtype, ce, descs.data(), (uint32_t)num_buffers, chunks, d_workspace, workspace_bytes, stream,
                          policy ? d_plans : nullptr, policy, sampled, ev);
 }
 
-uzip_status decompress_impl(uzip_dtype dtype, std::vector<DecDesc> &descs, uint32_t *d_status, void *d_workspace,
-                            size_t workspace_bytes, hipStream_t stream, const ProfileEvents *ev = nullptr) {
-    const uint32_t nbuf = (uint32_t)descs.size();
+uzip_status decompress_impl(uzip_dtype dtype, const DecDesc *descs, uint32_t nbuf, uint32_t *d_status,
+                            void *d_workspace, size_t workspace_bytes, hipStream_t stream,
+                            const ProfileEvents *ev = nullptr) {
     const DecWs w = dec_ws(nbuf);
     if (d_workspace == nullptr || workspace_bytes < w.bytes || !aligned(d_workspace, 16))
         return UZIP_ERR_INVALID_ARGUMENT;
     uint8_t *base = ws_base(d_workspace);
     uint64_t max_chunks = 0;
-    for (const DecDesc &d : descs) max_chunks += (d.n + 31) / 32;  // chunks hold >= 32 values
+    for (uint32_t b = 0; b < nbuf; ++b) max_chunks += (descs[b].n + 31) / 32;  // chunks hold >= 32 values
     DecParams vp{};
     vp.nbuf = nbuf;
     vp.dtype = dtype;
@@ -283,7 +284,7 @@ uzip_status decompress_impl(uzip_dtype dtype, std::vector<DecDesc> &descs, uint3
         vp.single = descs[0];
     } else {
         DecDesc *dd = reinterpret_cast<DecDesc *>(base + w.descs);
-        if (!stage_copy(dd, descs.data(), nbuf * sizeof(DecDesc), stream)) return UZIP_ERR_DEVICE;
+        if (!stage_copy(dd, descs, nbuf * sizeof(DecDesc), stream)) return UZIP_ERR_DEVICE;
         vp.descs = dd;
     }
     DecodeParams dp{};
@@ -353,9 +354,8 @@ uzip_status uzip_decompress(const void *d_in, size_t in_bytes, uzip_dtype dtype,
     if (in_bytes > 0 && (d_in == nullptr || !aligned(d_in, 16))) return UZIP_ERR_INVALID_ARGUMENT;
     if (num_elements > 0 && (d_out == nullptr || !aligned(d_out, 16))) return UZIP_ERR_INVALID_ARGUMENT;
     if (d_status == nullptr || !aligned(d_status, 4)) return UZIP_ERR_INVALID_ARGUMENT;
-    std::vector<DecDesc> descs(1);
-    descs[0] = DecDesc{static_cast<const uint8_t *>(d_in), static_cast<uint8_t *>(d_out), in_bytes, num_elements};
-    return decompress_impl(dtype, descs, d_status, d_workspace, workspace_bytes, stream);
+    const DecDesc desc{static_cast<const uint8_t *>(d_in), static_cast<uint8_t *>(d_out), in_bytes, num_elements};
+    return decompress_impl(dtype, &desc, 1, d_status, d_workspace, workspace_bytes, stream);
 }
 
 uzip_status uzip_compress_batched(uzip_dtype dtype, size_t num_buffers, const void *const *h_in,
@@ -402,7 +402,8 @@ uzip_status uzip_decompress_batched_timed(uzip_dtype dtype, size_t num_buffers, 
     if ((main_start == nullptr) != (main_stop == nullptr)) return UZIP_ERR_INVALID_ARGUMENT;
     if (!h_in || !h_in_bytes || !h_num_elements || !h_out || !d_status || !aligned(d_status, 4))
         return UZIP_ERR_INVALID_ARGUMENT;
-    std::vector<DecDesc> descs(num_buffers);
+    thread_local std::vector<DecDesc> descs;  // (kept per thread across calls)
+    if (descs.size() < num_buffers) descs.resize(num_buffers);
     for (size_t b = 0; b < num_buffers; ++b) {
         if (h_in_bytes[b] > 0 && (h_in[b] == nullptr || !aligned(h_in[b], 16))) return UZIP_ERR_INVALID_ARGUMENT;
         if (h_num_elements[b] > 0 && (h_out[b] == nullptr || !aligned(h_out[b], 16)))
@@ -411,7 +412,7 @@ uzip_status uzip_decompress_batched_timed(uzip_dtype dtype, size_t num_buffers, 
                            h_num_elements[b]};
     }
     const ProfileEvents ev{main_start, main_stop};
-    return decompress_impl(dtype, descs, d_status, d_workspace, workspace_bytes, stream,
+    return decompress_impl(dtype, descs.data(), (uint32_t)num_buffers, d_status, d_workspace, workspace_bytes, stream,
                            main_start != nullptr ? &ev : nullptr);
 }
 
