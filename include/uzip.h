@@ -87,7 +87,8 @@ typedef enum {
     UZIP_ERR_CAPACITY = 2,
     UZIP_ERR_CORRUPT_INPUT = 3,
     UZIP_ERR_DEVICE = 4,
-    UZIP_ERR_UNSUPPORTED = 5 /* reserved: no call of this version returns it */
+    UZIP_ERR_UNSUPPORTED = 5, /* reserved: no call of this version returns it */
+    UZIP_ERR_SCRATCH_LIMIT = 6 /* uzip_compress_noalloc: the input needs more than its scratch */
 } uzip_status;
 
 /* Exact upper bound of the compressed size of num_elements values: the size
@@ -117,6 +118,24 @@ size_t uzip_workspace_size(uzip_dtype dtype, size_t num_elements, size_t chunk_b
 uzip_status uzip_compress(uzip_dtype dtype, const void *d_in, size_t num_elements, size_t chunk_bytes,
                           void *d_out, size_t out_capacity, uint64_t *d_out_size,
                           void *d_workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ---- compress without allocating --------------------------------------------
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): uzip_compress
+ * without the workspace argument.  Its work memory is a static device array of
+ * UZIP_NOALLOC_SCRATCH_BYTES (64 MiB) that every device loading the library
+ * holds until the process ends; the call allocates nothing (no hipMalloc or
+ * hipFree, no allocating library routine).  Inputs whose workspace
+ * (uzip_workspace_size) exceeds the scratch are rejected at once with
+ * UZIP_ERR_SCRATCH_LIMIT, nothing launched: at the default chunk sizes up to
+ * 2046 chunks, 67,043,328 values of any type.  Output bytes, size, ownership
+ * and other errors are those of uzip_compress.  All calls on one device share
+ * that device's scratch, which keeps the last call's contents: calls that
+ * overlap on one device (other streams, other threads) race and must be
+ * serialised by the caller; sequential calls on one stream are safe. */
+#define UZIP_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+uzip_status uzip_compress_noalloc(uzip_dtype dtype, const void *d_in, size_t num_elements, size_t chunk_bytes,
+                                  void *d_out, size_t out_capacity, uint64_t *d_out_size, hipStream_t stream);
 
 /* Decompress the buffer at d_in (in_bytes bytes available) holding
  * num_elements values of `dtype`, as the receiver expects them, into d_out

@@ -33,6 +33,8 @@ UZIP_ERR_CAPACITY = 2
 UZIP_ERR_CORRUPT_INPUT = 3
 UZIP_ERR_DEVICE = 4
 UZIP_ERR_UNSUPPORTED = 5
+UZIP_ERR_SCRATCH_LIMIT = 6
+UZIP_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 UZIP_PLAN_CODED = 0
 UZIP_PLAN_RAW = 1
@@ -64,6 +66,7 @@ EXPORTED = (
     "uzip_compress_batched_arbitrated",
     "uzip_compress_sampled",
     "uzip_compress_batched_sampled",
+    "uzip_compress_noalloc",
     "uzip_compress_batched_timed",
     "uzip_decompress_batched_timed",
     "uzip_status_string",
@@ -110,6 +113,8 @@ def lib() -> ctypes.CDLL:
         L.uzip_compress_batched_arbitrated.restype = i32
         L.uzip_compress_batched_arbitrated.argtypes = [i32, sz, vp, vp, sz, ctypes.POINTER(uzip_policy), vp, vp,
                                                        u64p, vp, vp, sz, vp]
+        L.uzip_compress_noalloc.restype = i32
+        L.uzip_compress_noalloc.argtypes = [i32, vp, sz, sz, vp, sz, u64p, vp]
         L.uzip_compress_batched_timed.restype = i32
         L.uzip_compress_batched_timed.argtypes = [i32, sz, vp, vp, sz, ctypes.c_uint32, ctypes.POINTER(uzip_policy),
                                                   vp, vp, u64p, vp, vp, sz, vp, vp, vp]
@@ -140,6 +145,11 @@ def uzip_compress_sampled(dtype, d_in, num_elements, chunk_bytes, d_out, out_cap
                           workspace_bytes, stream) -> int:
     return int(lib().uzip_compress_sampled(dtype, d_in, num_elements, chunk_bytes, d_out, out_capacity, d_out_size,
                                            d_workspace, workspace_bytes, stream))
+
+
+def uzip_compress_noalloc(dtype, d_in, num_elements, chunk_bytes, d_out, out_capacity, d_out_size, stream) -> int:
+    return int(lib().uzip_compress_noalloc(dtype, d_in, num_elements, chunk_bytes, d_out, out_capacity, d_out_size,
+                                           stream))
 
 
 def uzip_decompress(d_in, in_bytes, dtype, num_elements, d_out, d_status, d_workspace, workspace_bytes,

@@ -331,6 +331,18 @@ uzip_status uzip_compress(uzip_dtype dtype, const void *d_in, size_t num_element
                            d_workspace, workspace_bytes, stream);
 }
 
+uzip_status uzip_compress_noalloc(uzip_dtype dtype, const void *d_in, size_t num_elements, size_t chunk_bytes,
+                                  void *d_out, size_t out_capacity, uint64_t *d_out_size, hipStream_t stream) {
+    const uint64_t ce = chunk_elems_of(dtype, chunk_bytes);
+    if (!ce) return UZIP_ERR_INVALID_ARGUMENT;
+    const uint64_t chunks = (num_elements + ce - 1) / ce;
+    if (enc_ws(1, chunks, ce).bytes > UZIP_NOALLOC_SCRATCH_BYTES) return UZIP_ERR_SCRATCH_LIMIT;
+    void *ws = nullptr;
+    if (noalloc_scratch(&ws) != hipSuccess) return UZIP_ERR_DEVICE;
+    return compress_single(dtype, d_in, num_elements, chunk_bytes, nullptr, d_out, out_capacity, d_out_size, nullptr,
+                           ws, UZIP_NOALLOC_SCRATCH_BYTES, stream);
+}
+
 uzip_status uzip_compress_sampled(uzip_dtype dtype, const void *d_in, size_t num_elements, size_t chunk_bytes,
                                   void *d_out, size_t out_capacity, uint64_t *d_out_size, void *d_workspace,
                                   size_t workspace_bytes, hipStream_t stream) {
@@ -439,6 +451,7 @@ const char *uzip_status_string(uzip_status s) {
         case UZIP_ERR_CORRUPT_INPUT: return "corrupt compressed input";
         case UZIP_ERR_DEVICE: return "HIP launch or copy failed";
         case UZIP_ERR_UNSUPPORTED: return "unsupported";
+        case UZIP_ERR_SCRATCH_LIMIT: return "input too large for the no-allocation scratch (UZIP_NOALLOC_SCRATCH_BYTES)";
     }
     return "unknown status";
 }

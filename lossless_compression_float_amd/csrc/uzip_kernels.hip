@@ -41,6 +41,7 @@
 // and the serial per-lane rANS chain, not by the matrix cores.
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include <hip/hip_runtime.h>
@@ -2114,6 +2115,39 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
         if (h < nch && !ok && lj == 0) gstore<uint32_t>(p.status + b, 3u);
         __syncthreads();
     }
+}
+
+// ---------------------------------------------------------------------------
+// scratch of uzip_compress_noalloc: the compress workspace for callers that
+// cannot allocate device memory.  One array per device (each device that
+// loads the library holds its own copy until the process ends).  Host code
+// never names the array except in hipGetSymbolAddress: the name is a host-side
+// stand-in, not a device address.  Its device address is looked up once per
+// device, with that device current, and kept.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) uint8_t scratch[UZIP_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kScratchDevices] = {};
+}  // namespace
+
+hipError_t noalloc_scratch(void **ptr) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
 }
 
 // ---------------------------------------------------------------------------

@@ -58,6 +58,9 @@ struct ProfileEvents {
 };
 
 hipError_t launch_compress(const EncParams &ep, hipStream_t stream, const ProfileEvents *ev = nullptr);
+// device address of the current device's no-allocation scratch (looked up on
+// the first call on each device, then kept)
+hipError_t noalloc_scratch(void **ptr);
 hipError_t launch_decompress(const DecParams &vp, const DecodeParams &dp, int dtype, uint64_t max_chunks,
                              hipStream_t stream, const ProfileEvents *ev = nullptr);
 
