@@ -190,11 +190,13 @@ def main():
     dtype = ts[0].dtype
     code = uz.dtype_code(dtype)
     eb = dtype.itemsize
-    rb = {uz.UZIP_BF16: 1, uz.UZIP_FP16: 1, uz.UZIP_FP32: 3}.get(code, 0)
+    # raw (sign+mantissa) bits per value, packed back to back in the raw region
+    rbits = {uz.UZIP_BF16: 8, uz.UZIP_FP32: 24, uz.UZIP_FP16: 11, uz.UZIP_FP8_E4M3: 4, uz.UZIP_FP8_E5M2: 3}[code]
     cb = args.chunk_bytes or (262144 if code == uz.UZIP_FP32 else 65536)
     chunk_elems = cb // eb
     ns = [t.numel() for t in ts]
     n_total = sum(ns)
+    raw_region = sum((n * rbits + 7) // 8 for n in ns)
     in_bytes = n_total * eb
 
     # preallocated outputs and workspaces
@@ -301,7 +303,8 @@ def main():
             torch.equal(a.view(iv), b.view(iv)) for a, b in zip(ts, backs))
 
     def record_bytes(comp_sizes):
-        exp_offs = [((((64 + 8 * ((n + chunk_elems - 1) // chunk_elems + 1)) + 15) // 16 * 16 + rb * n) + 15) // 16 * 16
+        exp_offs = [((((64 + 8 * ((n + chunk_elems - 1) // chunk_elems + 1)) + 15) // 16 * 16 + (n * rbits + 7) // 8)
+                     + 15) // 16 * 16
                     for n in ns]
         return exp_offs, sum(s - e for s, e in zip(comp_sizes, exp_offs))
 
@@ -316,9 +319,9 @@ def main():
     decisions = [p["decision"] for p in uz.plans_as_dicts(plans)] if pol is not None else []
     # a RAW plan's k_encode only splits (k_compact writes the RAW records)
     raw_planned = sum(n for n, dcs in zip(ns, decisions) if dcs != uz.UZIP_PLAN_CODED)
-    enc_bytes = n_total * eb + n_total * rb + rec_bytes - sum(
+    enc_bytes = n_total * eb + raw_region + rec_bytes - sum(
         s - e for s, e, dcs in zip(comp_sizes, exp_offs, decisions) if dcs != uz.UZIP_PLAN_CODED)
-    dec_bytes = n_total * rb + rec_bytes + sum(64 + 8 * ((n + chunk_elems - 1) // chunk_elems + 1) for n in ns) + \
+    dec_bytes = raw_region + rec_bytes + sum(64 + 8 * ((n + chunk_elems - 1) // chunk_elems + 1) for n in ns) + \
         n_total * eb
     all_raw = pol is not None and raw_planned == n_total
     if enc_kernel_ms >= dec_kernel_ms and not all_raw:
@@ -394,8 +397,8 @@ def main():
         s_sizes = sizes.cpu().tolist()
         s_bytes = sum(s_sizes)
         _, s_rec = record_bytes(s_sizes)
-        s_enc_b = n_total * eb + n_total * rb + s_rec
-        s_dec_b = n_total * rb + s_rec + sum(64 + 8 * ((n + chunk_elems - 1) // chunk_elems + 1) for n in ns) + n_total * eb
+        s_enc_b = n_total * eb + raw_region + s_rec
+        s_dec_b = raw_region + s_rec + sum(64 + 8 * ((n + chunk_elems - 1) // chunk_elems + 1) for n in ns) + n_total * eb
         s_match = None
         if not args.no_cpu_baseline:
             import oracle

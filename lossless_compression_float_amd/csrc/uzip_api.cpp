@@ -50,7 +50,7 @@ struct EncWs {
 // record, and at least the largest RANS prefix (header, bitmap, 256
 // frequencies, states), which the encoder writes before it knows whether the
 // chunk will be stored RAW.
-EncWs enc_ws(uint64_t nbuf, uint64_t chunks, uint64_t ce) {
+EncWs enc_ws(uzip_dtype dtype, uint64_t nbuf, uint64_t chunks, uint64_t ce) {
     EncWs w{};
     uint64_t o = 0;
     w.descs = o;
@@ -61,7 +61,7 @@ EncWs enc_ws(uint64_t nbuf, uint64_t chunks, uint64_t ce) {
     o += al(chunks * 8);
     w.ticket = o;
     o += al(8);
-    w.slot_stride = std::max<uint64_t>(raw_record_bytes(ce), align16(words_offset_sampled(256)));
+    w.slot_stride = std::max<uint64_t>(raw_record_bytes(ce, sym_bits(dtype)), align16(words_offset_sampled(256)));
     w.slots = o;
     o += chunks * w.slot_stride;
     w.bytes = o + kWsAlign;  // slack: the caller's pointer need only be 16-byte aligned
@@ -96,7 +96,8 @@ uint64_t max_size(uzip_dtype dtype, uint64_t n, uint64_t ce) {
     const Layout l = layout_of(dtype, n, ce);
     if (l.chunks == 0) return l.exp_off;
     const uint64_t last = n - (l.chunks - 1) * ce;
-    return l.exp_off + (l.chunks - 1) * raw_record_bytes(ce) + raw_record_bytes(last);
+    const uint32_t sb = sym_bits(dtype);
+    return l.exp_off + (l.chunks - 1) * raw_record_bytes(ce, sb) + raw_record_bytes(last, sb);
 }
 
 static_assert(sizeof(uzip_policy) == 56 && sizeof(uzip_plan) == 32, "arbitration structs as uzip.h lays them out");
@@ -178,7 +179,7 @@ uzip_status compress_impl(uzip_dtype dtype, uint64_t ce, EncDesc *descs, uint32_
                           void *d_workspace, size_t workspace_bytes, hipStream_t stream,
                           uzip_plan *plans = nullptr, const uzip_policy *policy = nullptr, bool sampled = false,
                           const ProfileEvents *ev = nullptr) {
-    const EncWs w = enc_ws(nbuf, chunks, ce);
+    const EncWs w = enc_ws(dtype, nbuf, chunks, ce);
     if (d_workspace == nullptr || workspace_bytes < w.bytes || !aligned(d_workspace, 16))
         return UZIP_ERR_INVALID_ARGUMENT;
     uint8_t *base = ws_base(d_workspace);
@@ -312,7 +313,7 @@ size_t uzip_workspace_size(uzip_dtype dtype, size_t num_elements, size_t chunk_b
     const uint64_t ce = chunk_elems_of(dtype, chunk_bytes);
     if (!ce) return 0;
     const uint64_t chunks = (num_elements + ce - 1) / ce;
-    return (size_t)std::max(enc_ws(1, chunks, ce).bytes, dec_ws(1).bytes);
+    return (size_t)std::max(enc_ws(dtype, 1, chunks, ce).bytes, dec_ws(1).bytes);
 }
 
 size_t uzip_workspace_size_batched(uzip_dtype dtype, size_t num_buffers, const size_t *h_num_elements,
@@ -321,7 +322,7 @@ size_t uzip_workspace_size_batched(uzip_dtype dtype, size_t num_buffers, const s
     if (!ce || num_buffers == 0 || num_buffers > 0xFFFFFFFFull || h_num_elements == nullptr) return 0;
     uint64_t chunks = 0;
     for (size_t b = 0; b < num_buffers; ++b) chunks += (h_num_elements[b] + ce - 1) / ce;
-    return (size_t)std::max(enc_ws(num_buffers, chunks, ce).bytes, dec_ws(num_buffers).bytes);
+    return (size_t)std::max(enc_ws(dtype, num_buffers, chunks, ce).bytes, dec_ws(num_buffers).bytes);
 }
 
 uzip_status uzip_compress(uzip_dtype dtype, const void *d_in, size_t num_elements, size_t chunk_bytes, void *d_out,
@@ -336,7 +337,7 @@ uzip_status uzip_compress_noalloc(uzip_dtype dtype, const void *d_in, size_t num
     const uint64_t ce = chunk_elems_of(dtype, chunk_bytes);
     if (!ce) return UZIP_ERR_INVALID_ARGUMENT;
     const uint64_t chunks = (num_elements + ce - 1) / ce;
-    if (enc_ws(1, chunks, ce).bytes > UZIP_NOALLOC_SCRATCH_BYTES) return UZIP_ERR_SCRATCH_LIMIT;
+    if (enc_ws(dtype, 1, chunks, ce).bytes > UZIP_NOALLOC_SCRATCH_BYTES) return UZIP_ERR_SCRATCH_LIMIT;
     void *ws = nullptr;
     if (noalloc_scratch(&ws) != hipSuccess) return UZIP_ERR_DEVICE;
     return compress_single(dtype, d_in, num_elements, chunk_bytes, nullptr, d_out, out_capacity, d_out_size, nullptr,

@@ -30,14 +30,25 @@ constexpr uint32_t kPairTile = 64;  // chunk pairs per tile of the record-offset
 __host__ __device__ inline uint64_t align16(uint64_t v) { return (v + 15u) & ~uint64_t(15); }
 __host__ __device__ inline uint64_t align4(uint64_t v) { return (v + 3u) & ~uint64_t(3); }
 
-// bytes stored raw per value (bf16 1, fp32 3, fp16 1, fp8 0) and bytes per value
-__host__ __device__ inline uint32_t raw_bytes_per_value(int dtype) {
-    return dtype == 2 ? 3u : (dtype == 1 || dtype == 3) ? 1u : 0u;
+// Every value splits into its exponent field (the coded symbol) and its sign
+// and mantissa bits (stored raw, the sign on top).  Bits of the raw field:
+// bf16 8, fp32 24, fp16 11, fp8 e4m3fn 4, fp8 e5m2 3; bits of the symbol:
+// 8, 8, 5, 4, 5; bytes per value 2, 4, 2, 1, 1.
+__host__ __device__ inline uint32_t raw_bits(int dtype) {
+    return dtype == 1 ? 8u : dtype == 2 ? 24u : dtype == 3 ? 11u : dtype == 4 ? 4u : 3u;
 }
+__host__ __device__ inline uint32_t sym_bits(int dtype) { return dtype == 3 || dtype == 5 ? 5u : dtype == 4 ? 4u : 8u; }
 __host__ __device__ inline uint32_t elem_bytes(int dtype) { return dtype == 2 ? 4u : (dtype == 1 || dtype == 3) ? 2u : 1u; }
 
-// record bytes of a chunk stored RAW: 16-byte record header + exponents, padded
-__host__ __device__ inline uint64_t raw_record_bytes(uint64_t n_values) { return align16(kRecHeaderBytes + n_values); }
+// bytes of n fields of w bits packed back to back (value order, least
+// significant bit first): the raw region, and the body of a RAW record
+__host__ __device__ inline uint64_t packed_bytes(uint64_t n, uint32_t w) { return (n * w + 7) / 8; }
+
+// record bytes of a chunk stored RAW: 16-byte record header + the symbols
+// packed at sb bits, padded to 16 bytes
+__host__ __device__ inline uint64_t raw_record_bytes(uint64_t n_values, uint32_t sb) {
+    return align16(kRecHeaderBytes + packed_bytes(n_values, sb));
+}
 
 // offset of the 32 final states inside a RANS record (after header, 32-byte
 // presence bitmap and nsym u16 frequencies, padded to 4 bytes)
@@ -64,7 +75,7 @@ __host__ __device__ inline Layout layout_of(int dtype, uint64_t n, uint64_t chun
     Layout l;
     l.chunks = (n + chunk_elems - 1) / chunk_elems;
     l.sm_off = align16(kHeaderBytes + 8 * (l.chunks + 1));
-    l.exp_off = align16(l.sm_off + uint64_t(raw_bytes_per_value(dtype)) * n);
+    l.exp_off = align16(l.sm_off + packed_bytes(n, raw_bits(dtype)));
     return l;
 }
 

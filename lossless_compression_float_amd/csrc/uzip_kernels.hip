@@ -237,29 +237,43 @@ __device__ inline DecDesc load_dec_desc(const DecDesc *d) {
     return r;
 }
 
-// Value formats (kernel template parameter DT): 1 bf16, 2 fp32, 3 fp16, 4 fp8
-// (e4m3 and e5m2 alike; the header's dtype byte tells them apart).  EB bytes
-// per value, R bytes stored raw per value; the coded symbol is the 8-bit
-// field at bit SYM: the exponent of bf16 and fp32, the high byte of fp16
-// (sign, exponent, top 2 mantissa bits), the whole byte of fp8.
+// Value formats (kernel template parameter DT = the dtype code): 1 bf16,
+// 2 fp32, 3 fp16, 4 fp8 e4m3fn, 5 fp8 e5m2.  EB bytes per value.  The coded
+// symbol is the exponent field, SB bits at bit SYM; the raw field is the sign
+// above the mantissa bits, RB bits, and the raw fields of all values are
+// packed back to back in the raw region.  R = RB / 8 for the types whose raw
+// field is whole bytes (bf16 1, fp32 3); 0 for fp16 and fp8, whose raw fields
+// are bit-packed and whose RAW records pack their symbols at SB bits.
 template <int DT> struct Fmt;
-template <> struct Fmt<1> { static constexpr uint32_t EB = 2, R = 1, SYM = 7; };
-template <> struct Fmt<2> { static constexpr uint32_t EB = 4, R = 3, SYM = 23; };
-template <> struct Fmt<3> { static constexpr uint32_t EB = 2, R = 1, SYM = 8; };
-template <> struct Fmt<4> { static constexpr uint32_t EB = 1, R = 0, SYM = 0; };
+template <> struct Fmt<1> { static constexpr uint32_t EB = 2, R = 1, RB = 8, SB = 8, SYM = 7; };
+template <> struct Fmt<2> { static constexpr uint32_t EB = 4, R = 3, RB = 24, SB = 8, SYM = 23; };
+template <> struct Fmt<3> { static constexpr uint32_t EB = 2, R = 0, RB = 11, SB = 5, SYM = 10; };
+template <> struct Fmt<4> { static constexpr uint32_t EB = 1, R = 0, RB = 4, SB = 4, SYM = 3; };
+template <> struct Fmt<5> { static constexpr uint32_t EB = 1, R = 0, RB = 3, SB = 5, SYM = 2; };
 
 template <int DT>
 __device__ inline uint32_t exponent_of(uint32_t v) {
-    return (v >> Fmt<DT>::SYM) & 0xFFu;
+    return (v >> Fmt<DT>::SYM) & ((1u << Fmt<DT>::SB) - 1u);
 }
-// the raw field of a value (R bytes, little-endian): bf16 sign at bit 7 and 7
-// mantissa bits, fp32 sign at bit 23 and 23 mantissa bits, fp16 the low byte
+// the raw field of a value: bf16 sign at bit 7 and 7 mantissa bits, fp32 sign
+// at bit 23 and 23 mantissa bits, fp16 sign at bit 10 and 10 mantissa bits,
+// e4m3fn sign at bit 3 and 3 mantissa bits, e5m2 sign at bit 2 and 2
 template <int DT>
 __device__ inline uint32_t raw_of(uint32_t v) {
     if (DT == 1) return ((v >> 8) & 0x80u) | (v & 0x7Fu);
     if (DT == 2) return ((v >> 8) & 0x800000u) | (v & 0x7FFFFFu);
-    if (DT == 3) return v & 0xFFu;
-    return 0u;
+    if (DT == 3) return ((v >> 5) & 0x400u) | (v & 0x3FFu);
+    if (DT == 4) return ((v >> 4) & 0x8u) | (v & 0x7u);
+    return ((v >> 5) & 0x4u) | (v & 0x3u);
+}
+// inverse of the split: a value from its symbol and its raw field
+template <int DT>
+__device__ inline uint32_t join_value(uint32_t sym, uint32_t raw) {
+    if (DT == 1) return ((raw & 0x80u) << 8) | (sym << 7) | (raw & 0x7Fu);
+    if (DT == 2) return ((raw & 0x800000u) << 8) | (sym << 23) | (raw & 0x7FFFFFu);
+    if (DT == 3) return ((raw & 0x400u) << 5) | (sym << 10) | (raw & 0x3FFu);
+    if (DT == 4) return ((raw & 0x8u) << 4) | (sym << 3) | (raw & 0x7u);
+    return ((raw & 0x4u) << 5) | (sym << 2) | (raw & 0x3u);
 }
 // one value through a buffer resource (zero-extended)
 template <int DT>
@@ -282,7 +296,7 @@ __device__ inline uint32_t header_word(uint32_t k, int dtype, uint32_t chunk_ele
     switch (k) {
         case 0: return kMagic;
         case 1: return kVersion | (uint32_t(dtype) << 16) | (kProbBits << 24);
-        case 2: return kLanes | (raw_bytes_per_value(dtype) << 8) | (flags << 16);
+        case 2: return kLanes | (raw_bits(dtype) << 8) | (flags << 16);
         case 3: return chunk_elems;
         case 4: return (uint32_t)n;
         case 5: return (uint32_t)(n >> 32);
@@ -404,12 +418,46 @@ __device__ inline void copy_words(rsrc_t rslot, uint8_t *rec, uint32_t wofs, uin
     }
 }
 
-// Body of a RAW record: bytes [16, size) get the exponents of the chunk's ni
-// values (at byte in0 of the input resource), then zeros.  Whole wave,
-// wave-uniform arguments; one 16-byte unit (16 exponents) per lane.
+// Bits of a value's field packed at w bits: the w bits at bit position bit
+// of the byte string behind r (two aligned dwords, so nothing is read more
+// than 4 bytes past the dword holding the field's first bit).
+__device__ inline uint32_t packed_field(rsrc_t r, uint32_t base, uint32_t bit, uint32_t w) {
+    const uint32_t o = base + 4 * (bit >> 5);
+    const uint32_t lo = bld32(r, o);
+    const uint32_t hi = (bit & 31u) + w > 32 ? bld32(r, o + 4) : 0u;
+    return __builtin_amdgcn_alignbit(hi, lo, bit & 31u) & ((1u << w) - 1u);
+}
+
+// dword k of the w-bit packing of fields f(0) .. f(n - 1) (zeros past n)
+template <typename F>
+__device__ inline uint32_t packed_dword(uint32_t k, uint32_t n, uint32_t w, F f) {
+    uint32_t acc = 0;
+    const uint32_t i0 = 32 * k / w, i1 = (32 * k + 31) / w;
+    for (uint32_t i = i0; i <= i1 && i < n; ++i) {
+        const int sh = (int)(i * w) - (int)(32 * k);
+        const uint32_t v = f(i);
+        acc |= sh >= 0 ? v << sh : v >> -sh;
+    }
+    return acc;
+}
+
+// Body of a RAW record: bytes [16, size) get the symbols of the chunk's ni
+// values (at byte in0 of the input resource), packed at SB bits (bytes for
+// bf16 and fp32), then zeros.  Whole wave, wave-uniform arguments; bf16 and
+// fp32 one 16-byte unit (16 exponents) per lane, the others a dword per lane.
 template <int DT>
 __device__ inline void raw_exponents(rsrc_t rin, uint8_t *rec, uint32_t size, uint32_t ni, uint32_t in0, uint32_t lane) {
     constexpr uint32_t EB = Fmt<DT>::EB;
+    if constexpr (Fmt<DT>::R == 0) {
+        const uint32_t nd = (size - kRecHeaderBytes) / 4;
+        for (uint32_t k = lane; k < nd; k += 64) {
+            const uint32_t w = packed_dword(k, ni, Fmt<DT>::SB, [&](uint32_t i) {
+                return exponent_of<DT>(bld_value<DT>(rin, in0 + i * EB));
+            });
+            gstore<uint32_t>(rec + kRecHeaderBytes + 4 * k, w);
+        }
+        return;
+    }
     const uint32_t nu = (size - kRecHeaderBytes) / 16;
     for (uint32_t u = lane; u < nu; u += 64) {
         uint32_t w[16];
@@ -450,13 +498,13 @@ __device__ inline void raw_exponents(rsrc_t rin, uint8_t *rec, uint32_t size, ui
 //                four different banks: hot bins no longer serialise a wave
 //   normalise    keys of the present symbols          words [0, 512)
 //   pass 2       per-symbol coder table, 16 B/entry   words [512, 2560)
-// fp8 counts a whole byte per value, 16 per 128-bit load, with eight waves per
-// CU (a chunk holds 64 Ki values): it takes 8 sub-histograms in rows of 260
-// words (eight copies of a bin in eight banks, 16.25 KiB in all), which its
-// occupancy affords; the 2-byte types keep 10 KiB for 16 waves per CU.
+// fp8 counts 32 values per group with eight waves per CU (a chunk holds 64 Ki
+// values): it takes 8 sub-histograms in rows of 260 words (eight copies of a
+// bin in eight banks, 16.25 KiB in all), which its occupancy affords; the
+// 2-byte types keep 10 KiB for 16 waves per CU.
 template <int DT> struct EncLds {
-    static constexpr uint32_t kSubHist = DT == 4 ? 8 : 4;
-    static constexpr uint32_t kSubRow = DT == 4 ? 260 : 264;
+    static constexpr uint32_t kSubHist = Fmt<DT>::EB == 1 ? 8 : 4;
+    static constexpr uint32_t kSubRow = Fmt<DT>::EB == 1 ? 260 : 264;
     static constexpr uint32_t kWords = 2 * kSubHist * kSubRow > 2560 ? 2 * kSubHist * kSubRow : 2560;
 };
 
@@ -533,7 +581,14 @@ __global__ __launch_bounds__(64) void k_encode(EncParams p) {
 #pragma unroll
                 for (uint32_t u = 0; u < 4; ++u) {
                     if (i0[u] >= ni) continue;
-                    const uint32_t w[4] = {qv[u].x, qv[u].y, qv[u].z, qv[u].w};
+                    uint32_t w[4] = {qv[u].x, qv[u].y, qv[u].z, qv[u].w};
+                    if (i0[u] + VPL > ni) {
+                        // a vector that the chunk's end cuts: value by value (the
+                        // 128-bit load read the dword crossing the pair's end as zero)
+                        w[0] = w[1] = w[2] = w[3] = 0;
+                        for (uint32_t k = 0; i0[u] + k < ni; ++k)
+                            w[k / (4 / EB)] |= bld_value<DT>(rin, in0 + (i0[u] + k) * EB) << (8 * EB * (k % (4 / EB)));
+                    }
 #pragma unroll
                     for (uint32_t k = 0; k < VPL; ++k) {
                         const uint32_t v = EB == 4 ? w[k] : (w[k / (4 / EB)] >> (8 * EB * (k % (4 / EB)))) & ((1u << (8 * EB)) - 1u);
@@ -547,7 +602,68 @@ __global__ __launch_bounds__(64) void k_encode(EncParams p) {
                 if (i < ni) atomicAdd(&hist[exponent_of<DT>(bld_value<DT>(rin, in0 + i * EB))], 1u);
             }
         }
-    } else {
+    }
+    if constexpr (Fmt<DT>::R == 0) {
+        // ---- fp16 and fp8: raw fields bit-packed (RB bits a value), and with
+        // full tables the LDS histogram.  Lane lj takes groups gi = lj, lj + 32,
+        // ... of 32 consecutive values of its half's chunk: 32 RB bits are RB
+        // dwords of the raw region (dword-aligned: chunks hold multiples of 32
+        // values).  It loads the group (32 EB bytes, 128-bit loads), packs the
+        // 32 raw fields, counts the 32 exponents and stores the RB dwords.
+        // A group that the chunk's end cuts is read value by value (a 128-bit
+        // load crossing the end of the pair's range would read the dword
+        // holding the last values as zero); the values past the end are zero,
+        // so their bits are, and are not counted.  The resource is the pair's
+        // raw region (its base wave-uniform; half 1's chunk starts vals0 RB / 8
+        // bytes in), and the last group's dwords past it are dropped.
+        constexpr uint32_t RB = Fmt<DT>::RB;
+        const rsrc_t rraw = make_rsrc(d.out + d.sm_off + c0 * ce * RB / 8,
+                                      (uint32_t)((packed_bytes(pair_vals, RB) + 3) & ~3ull));
+        const uint32_t hraw = (h ? vals0 : 0u) * RB / 8;  // this half's chunk in rraw (vals0 = ce then)
+        const uint32_t ngroups = (ni + 31) / 32;
+        for (uint32_t gi = lj; gi < ngroups; gi += 32) {
+            uint32_t w[8 * EB];
+            if (32 * gi + 32 <= ni) {
+#pragma unroll
+                for (uint32_t u = 0; u < 2 * EB; ++u) {
+                    const uint4 qv = bld128(rin, in0 + gi * 32 * EB + 16 * u);
+                    w[4 * u] = qv.x; w[4 * u + 1] = qv.y; w[4 * u + 2] = qv.z; w[4 * u + 3] = qv.w;
+                }
+            } else {
+#pragma unroll
+                for (uint32_t u = 0; u < 8 * EB; ++u) w[u] = 0;
+                for (uint32_t k = 0; 32 * gi + k < ni; ++k)
+                    w[k * EB / 4] |= bld_value<DT>(rin, in0 + (32 * gi + k) * EB) << (8 * EB * (k % (4 / EB)));
+            }
+            uint32_t acc[RB];
+#pragma unroll
+            for (uint32_t k = 0; k < RB; ++k) acc[k] = 0;
+#pragma unroll
+            for (uint32_t k = 0; k < 32; ++k) {
+                const uint32_t v = (w[k * EB / 4] >> (8 * EB * (k % (4 / EB)))) & ((1u << (8 * EB)) - 1u);
+                if (!S && 32 * gi + k < ni) atomicAdd(&hist[exponent_of<DT>(v)], 1u);
+                const uint32_t r = raw_of<DT>(v), bit = k * RB;
+                acc[bit >> 5] |= r << (bit & 31);
+                if ((bit & 31) + RB > 32) acc[(bit >> 5) + 1] |= r >> (32 - (bit & 31));
+            }
+            const uint32_t o = hraw + gi * 4 * RB;
+            if (32 * gi + 32 <= ni) {
+#pragma unroll
+                for (uint32_t k = 0; k + 4 <= RB; k += 4)
+                    __builtin_amdgcn_raw_buffer_store_b128(u32x4{acc[k], acc[k + 1], acc[k + 2], acc[k + 3]}, rraw,
+                                                           (int)(o + 4 * k), 0, 0);
+                constexpr uint32_t k4 = RB & ~3u;
+                if constexpr (RB - k4 == 3)
+                    __builtin_amdgcn_raw_buffer_store_b96(u32x3{acc[k4], acc[k4 + 1], acc[k4 + 2]}, rraw, (int)(o + 4 * k4), 0, 0);
+                if constexpr (RB - k4 == 2)
+                    __builtin_amdgcn_raw_buffer_store_b64(u32x2{acc[k4], acc[k4 + 1]}, rraw, (int)(o + 4 * k4), 0, 0);
+                if constexpr (RB - k4 == 1) bst32(rraw, o + 4 * k4, acc[k4]);
+            } else {
+#pragma unroll
+                for (uint32_t k = 0; k < RB; ++k) bst32(rraw, o + 4 * k, acc[k]);
+            }
+        }
+    } else if constexpr (!S) {
     // ---- pass 1: split, sign+mantissa bytes to the output, LDS histogram ----
     // Main loop: iterations in which every lane of each coding half holds a
     // full 128-bit vector, with four to eight loads in flight per lane.  A half without
@@ -564,7 +680,7 @@ __global__ __launch_bounds__(64) void k_encode(EncParams p) {
         auto split = [&](const uint4 &qv, uint32_t it) __attribute__((always_inline)) {
             const uint32_t w[4] = {qv.x, qv.y, qv.z, qv.w};
             const uint32_t o = smo + it * VPI * R;
-            if (DT == 1 || DT == 3) {
+            if (DT == 1) {
                 uint32_t smw[2] = {0, 0};
 #pragma unroll
                 for (uint32_t k = 0; k < 8; ++k) {
@@ -573,9 +689,6 @@ __global__ __launch_bounds__(64) void k_encode(EncParams p) {
                     atomicAdd(&hm[exponent_of<DT>(v)], 1u);
                 }
                 __builtin_amdgcn_raw_buffer_store_b64(u32x2{smw[0], smw[1]}, rsmo, (int)o, 0, 0);
-            } else if (DT == 4) {  // the whole byte is the symbol; nothing raw
-#pragma unroll
-                for (uint32_t k = 0; k < 16; ++k) atomicAdd(&hm[(w[k >> 2] >> (8 * (k & 3))) & 0xFFu], 1u);
             } else {
                 uint32_t sm[4];
 #pragma unroll
@@ -593,8 +706,8 @@ __global__ __launch_bounds__(64) void k_encode(EncParams p) {
         // the loads are issued in asm and waited for explicitly, so that the
         // wait does not also cover the raw-byte stores: between a set's loads
         // and its wait lies only the straight-line split of the set before,
-        // with exactly one store per vector (none for fp8).
-        constexpr uint32_t kSetStores = R > 0 ? 4 : 0;
+        // with exactly one store per vector.
+        constexpr uint32_t kSetStores = 4;
         auto asm_load_set = [&](uint32_t st, u32x4(&V)[4]) __attribute__((always_inline)) {
 #pragma unroll
             for (uint32_t k = 0; k < 4; ++k) {
@@ -647,11 +760,7 @@ __global__ __launch_bounds__(64) void k_encode(EncParams p) {
                 w[k / (4 / EB)] |= bld_value<DT>(rin, o) << (8 * EB * (k % (4 / EB)));
             }
         }
-        if (DT == 4) {
-#pragma unroll
-            for (uint32_t k = 0; k < 16; ++k)
-                if (full || i0 + k < ni) atomicAdd(&hist[(w[k >> 2] >> (8 * (k & 3))) & 0xFFu], 1u);
-        } else if (DT == 1 || DT == 3) {
+        if (DT == 1) {
             uint32_t smw[2] = {0, 0};
 #pragma unroll
             for (uint32_t k = 0; k < 8; ++k) {
@@ -790,7 +899,7 @@ __global__ __launch_bounds__(64) void k_encode(EncParams p) {
     // Input values are prefetched one 8-step block ahead through the pair's
     // input resource (past the pair: zeros, never coded).
     const uint32_t nsym0 = uniform_u32(__shfl((int)nsym, 0, 64)), nsym1 = uniform_u32(__shfl((int)nsym, 32, 64));
-    const uint32_t raw0 = (uint32_t)raw_record_bytes(vals0), raw1 = (uint32_t)raw_record_bytes(vals1);
+    const uint32_t raw0 = (uint32_t)raw_record_bytes(vals0, Fmt<DT>::SB), raw1 = (uint32_t)raw_record_bytes(vals1, Fmt<DT>::SB);
     const uint32_t wofs0 = (uint32_t)(S ? words_offset_sampled(nsym0) : words_offset(nsym0));
     const uint32_t wofs1 = (uint32_t)(S ? words_offset_sampled(nsym1) : words_offset(nsym1));
     // words that fit before a record reaches its RAW size; a chunk whose table
@@ -838,7 +947,7 @@ __global__ __launch_bounds__(64) void k_encode(EncParams p) {
             act = (alive0 && vals0 > 32 * t ? half_prefix_mask(vals0 - 32 * t, 0) : 0ull) |
                   (alive1 && vals1 > 32 * t ? half_prefix_mask(vals1 - 32 * t, 1) : 0ull);
         uint32_t ex = ex_in;  // the value's exponent
-        if (!have_ex) asm("v_bfe_u32 %0, %1, %2, 8" : "=v"(ex) : "v"(v), "i"(Fmt<DT>::SYM));
+        if (!have_ex) asm("v_bfe_u32 %0, %1, %2, %3" : "=v"(ex) : "v"(v), "i"(Fmt<DT>::SYM), "i"(Fmt<DT>::SB));
         const uint4 te = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint8_t *>(tab) + (ex << 4));
         uint64_t m = lanes_lt(te.x & 0xFFFFu, x >> 20) & act;  // x >= f * 2^20
         uint32_t lo = (uint32_t)m, hi = (uint32_t)(m >> 32);
@@ -966,6 +1075,9 @@ __global__ __launch_bounds__(64) void k_encode(EncParams p) {
                 s1 = (hi1 & 0x80808080u) | (lo1 & 0x7F7F7F7Fu);
                 e0 = ((hi0 << 1) & 0xFEFEFEFEu) | ((lo0 >> 7) & 0x01010101u);
                 e1 = ((hi1 << 1) & 0xFEFEFEFEu) | ((lo1 >> 7) & 0x01010101u);
+            } else {  // fp16: the exponent is bits 2-6 of the high byte
+                e0 = (hi0 >> 2) & 0x1F1F1F1Fu;
+                e1 = (hi1 >> 2) & 0x1F1F1F1Fu;
             }
             SM[0] = s0;
             SM[1] = s1;
@@ -985,9 +1097,9 @@ __global__ __launch_bounds__(64) void k_encode(EncParams p) {
             SM[3] = sm[4] | (sm[5] << 24);
             SM[4] = (sm[5] >> 8) | (sm[6] << 16);
             SM[5] = (sm[6] >> 16) | (sm[7] << 8);
-        } else {  // fp8: the byte is the symbol, nothing raw
-            e0 = U[0].x;
-            e1 = U[0].y;
+        } else {  // fp8: bits 3-6 (e4m3fn) or 2-6 (e5m2) of each byte
+            e0 = (U[0].x >> Fmt<DT>::SYM) & (((1u << Fmt<DT>::SB) - 1u) * 0x01010101u);
+            e1 = (U[0].y >> Fmt<DT>::SYM) & (((1u << Fmt<DT>::SB) - 1u) * 0x01010101u);
         }
         asm volatile("" ::: "memory");  // (after the last block's reads of the area)
         *reinterpret_cast<u32x2 *>(stage + 8 * lj) = u32x2{e0, e1};
@@ -1184,7 +1296,8 @@ __global__ __launch_bounds__(256) void k_plan(EncParams p) {
     const uint64_t ce = p.chunk_elems;
     const Layout l = layout_of(p.dtype, n, ce);
     const uint64_t pred = l.exp_off + ceil_div_u64(n * h, 1ull << 19) + l.chunks * (words_offset(nsym) + 8);
-    const uint64_t praw = l.exp_off + (l.chunks - 1) * raw_record_bytes(ce) + raw_record_bytes(n - (l.chunks - 1) * ce);
+    const uint64_t praw = l.exp_off + (l.chunks - 1) * raw_record_bytes(ce, Fmt<DT>::SB) +
+                          raw_record_bytes(n - (l.chunks - 1) * ce, Fmt<DT>::SB);
     const uint64_t t_raw = ceil_div_u64(praw * 1000, pol.link_bytes_per_us);
     const uint64_t t_code = pol.fixed_ns + ceil_div_u64(pred * 1000, pol.link_bytes_per_us) +
                             ceil_div_u64(uint64_t(pol.exposed_encode_permil) * B, pol.encode_bytes_per_us) +
@@ -1232,13 +1345,29 @@ __global__ __launch_bounds__(256) void k_raw_frame(EncParams p) {
         const uint64_t ce = p.chunk_elems, n = uniform_u64(d.n), chunks = uniform_u64(d.chunks);
         const uint64_t c = g - uniform_u64(d.chunk_first);
         const uint32_t ni = (uint32_t)min<uint64_t>(ce, n - c * ce);
-        const uint64_t rrb = raw_record_bytes(ce), off = c * rrb;
+        const uint64_t rrb = raw_record_bytes(ce, Fmt<DT>::SB), off = c * rrb;
         uint8_t *out = d.out;
         const uint64_t exp_off = uniform_u64(d.exp_off), sm_off = uniform_u64(d.sm_off);
         const rsrc_t rin = make_rsrc(d.in + c * ce * EB, ni * EB);
         const rsrc_t rsm = make_rsrc(out + sm_off + c * ce * R, ni * R);
-        const uint32_t rbytes = (uint32_t)raw_record_bytes(ni);
+        const uint32_t rbytes = (uint32_t)raw_record_bytes(ni, Fmt<DT>::SB);
         const rsrc_t rrec = make_rsrc(out + exp_off + off, rbytes);
+        if constexpr (R == 0) {
+            // fp16 and fp8: the chunk's raw fields and its symbols, each packed
+            // (a dword per thread, built from the values it covers); the raw
+            // region's last dword may reach into the zero gap after it
+            constexpr uint32_t RB = Fmt<DT>::RB, SB = Fmt<DT>::SB;
+            uint8_t *rawp = out + sm_off + c * ce * RB / 8;
+            const uint32_t nd_raw = (uint32_t)((packed_bytes(ni, RB) + 3) / 4);
+            for (uint32_t k = t; k < nd_raw; k += 256)
+                gstore<uint32_t>(rawp + 4 * k, packed_dword(k, ni, RB, [&](uint32_t i) {
+                    return raw_of<DT>(bld_value<DT>(rin, i * EB));
+                }));
+            for (uint32_t k = t; k < (rbytes - kRecHeaderBytes) / 4; k += 256)
+                gstore<uint32_t>(out + exp_off + off + kRecHeaderBytes + 4 * k, packed_dword(k, ni, SB, [&](uint32_t i) {
+                    return exponent_of<DT>(bld_value<DT>(rin, i * EB));
+                }));
+        } else {
         const uint32_t nu = ni / 16;
         constexpr uint32_t U = 4;  // units per thread in flight
         for (uint32_t u0 = t; u0 < nu; u0 += 256 * U) {
@@ -1290,6 +1419,7 @@ __global__ __launch_bounds__(256) void k_raw_frame(EncParams p) {
             }
             __builtin_amdgcn_raw_buffer_store_b128(u32x4{ex[0], ex[1], ex[2], ex[3]}, rrec, (int)(kRecHeaderBytes + 16 * nu), 0, 0);
         }
+        }  // byte types
         if (t == 0) {
             gstore<uint4>(out + exp_off + off, make_uint4(1u, 0u, ni, rbytes));
             gstore<uint64_t>(out + kHeaderBytes + 8 * c, off);
@@ -1302,7 +1432,7 @@ __global__ __launch_bounds__(256) void k_raw_frame(EncParams p) {
             }
             if (t < 16) gstore<uint32_t>(out + 4 * t, header_word(t, p.dtype, p.chunk_elems, n, chunks, sm_off, exp_off, total));
             for (uint64_t k = kHeaderBytes + 8 * (chunks + 1) + t; k < sm_off; k += 256) gstore<uint8_t>(out + k, 0);
-            for (uint64_t k = sm_off + uint64_t(R) * n + t; k < exp_off; k += 256) gstore<uint8_t>(out + k, 0);
+            for (uint64_t k = sm_off + packed_bytes(n, Fmt<DT>::RB) + t; k < exp_off; k += 256) gstore<uint8_t>(out + k, 0);
         }
     }
 }
@@ -1323,7 +1453,8 @@ __global__ __launch_bounds__(256) void k_accept(EncParams p) {
     const EncDesc d = p.nbuf == 1 ? p.single : load_enc_desc(p.descs + bi);
     const uint64_t ce = p.chunk_elems, n = d.n, B = n * Fmt<DT>::EB;
     const Layout l = layout_of(p.dtype, n, ce);
-    const uint64_t praw = l.exp_off + (l.chunks - 1) * raw_record_bytes(ce) + raw_record_bytes(n - (l.chunks - 1) * ce);
+    const uint64_t praw = l.exp_off + (l.chunks - 1) * raw_record_bytes(ce, Fmt<DT>::SB) +
+                          raw_record_bytes(n - (l.chunks - 1) * ce, Fmt<DT>::SB);
     const uint64_t R = gload<uint64_t>(d.out_size);
     const bool accepted = R < praw && (praw - R) * 1000 >= uint64_t(p.policy.min_gain_permil) * B;
     if (!accepted) gstore<uint32_t>(&p.plans[bi].decision, UZIP_PLAN_RAW_REALIZED);
@@ -1351,7 +1482,6 @@ constexpr uint32_t kCompactPairs = 8;
 template <int DT>
 __global__ __launch_bounds__(128 * kCompactPairs) void k_compact(EncParams p) {
     constexpr uint32_t EB = Fmt<DT>::EB;
-    constexpr uint32_t R = Fmt<DT>::R;
     __shared__ uint32_t s_ticket;
     const uint32_t lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     if (threadIdx.x == 0) s_ticket = __hip_atomic_fetch_add(p.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1408,7 +1538,7 @@ __global__ __launch_bounds__(128 * kCompactPairs) void k_compact(EncParams p) {
         // words; a sampled-table record ends with its escaped exponents
         const uint32_t wofs = (uint32_t)(mode == 2 ? words_offset_sampled(nsym) : words_offset(nsym));
         for (uint32_t k = lane; k < wofs / 4; k += 64) gstore<uint32_t>(rec + 4 * k, bld32(rslot, 4 * k));
-        copy_words(rslot, rec, wofs, size, 2 * nw, (uint32_t)raw_record_bytes(ni) - 2 * nw, lane);
+        copy_words(rslot, rec, wofs, size, 2 * nw, (uint32_t)raw_record_bytes(ni, Fmt<DT>::SB) - 2 * nw, lane);
         if (mode == 2) {
             const uint32_t ne = uniform_u32(bld32(rslot, (uint32_t)esc_count_offset(nsym)));
             if (ne > 0) {
@@ -1437,7 +1567,7 @@ __global__ __launch_bounds__(128 * kCompactPairs) void k_compact(EncParams p) {
                              header_word(lane, p.dtype, p.chunk_elems, n, chunks, d.sm_off, exp_off, total, p.sampled));
         const uint64_t gap0 = kHeaderBytes + 8 * (chunks + 1);
         for (uint64_t k = gap0 + lane; k < d.sm_off; k += 64) gstore<uint8_t>(out + k, 0);
-        const uint64_t gap1 = d.sm_off + uint64_t(R) * n;
+        const uint64_t gap1 = d.sm_off + packed_bytes(n, Fmt<DT>::RB);
         for (uint64_t k = gap1 + lane; k < exp_off; k += 64) gstore<uint8_t>(out + k, 0);
     }
 }
@@ -1516,7 +1646,7 @@ __global__ void k_dec_validate(DecParams p) {
     if (ok) {
         const uint4 h0 = gload<uint4>(d.in), h1 = gload<uint4>(d.in + 16);
         const uint4 h2 = gload<uint4>(d.in + 32), h3 = gload<uint4>(d.in + 48);
-        const uint32_t r = raw_bytes_per_value(p.dtype);
+        const uint32_t r = raw_bits(p.dtype);
         // V1 magic, version, fixed coder parameters, flags (bit 0 the only
         // one defined); V2 dtype and count
         const uint32_t flags = h0.z >> 16;
@@ -1583,13 +1713,12 @@ __device__ inline uint32_t bload_sm(rsrc_t r, uint32_t off) {
     return bld8(r, off) | (bld8(r, off + 1) << 8) | (bld8(r, off + 2) << 16);
 }
 
-// inverse of the split: a value from its symbol and its raw field
+// fp16 and fp8: the raw field of the value whose bits start at bit position
+// bit of the raw region behind r (one unaligned dword: the field's 11, 4 or 3
+// bits start at most 7 bits into it)
 template <int DT>
-__device__ inline uint32_t merge_value(uint32_t ex, uint32_t smv) {
-    if (DT == 1) return ((smv & 0x80u) << 8) | (ex << 7) | (smv & 0x7Fu);
-    if (DT == 2) return ((smv & 0x800000u) << 8) | (ex << 23) | (smv & 0x7FFFFFu);
-    if (DT == 3) return (ex << 8) | (smv & 0xFFu);
-    return ex;
+__device__ inline uint32_t raw_field(rsrc_t r, uint32_t bit) {
+    return (bld32(r, bit >> 3) >> (bit & 7u)) & ((1u << Fmt<DT>::RB) - 1u);
 }
 
 // 16 values rebuilt from 16 symbol bytes E and their 16 R raw bytes S, stored
@@ -1624,7 +1753,7 @@ __device__ inline void store_unit(rsrc_t r, uint32_t off, const uint4 &E, const 
             // raw field k: bytes 3k .. 3k + 2 of w
             const uint32_t b = 3 * k, d = b >> 2;
             const uint32_t sm = __builtin_amdgcn_alignbyte(w[d + 1 < 12 ? d + 1 : 11], w[d], b & 3) & 0xFFFFFFu;
-            o[k] = merge_value<2>((e[k >> 2] >> (8 * (k & 3))) & 0xFFu, sm);
+            o[k] = join_value<2>((e[k >> 2] >> (8 * (k & 3))) & 0xFFu, sm);
         }
 #pragma unroll
         for (uint32_t q = 0; q < 4; ++q)
@@ -1640,9 +1769,10 @@ template <int DT, bool S>
 __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
     constexpr uint32_t EB = Fmt<DT>::EB;
     constexpr uint32_t R = Fmt<DT>::R;
-    // bf16 and fp16: 2-byte values with one raw byte, which share the main
-    // loop below (raw bytes by dword and bpermute, two steps per store)
-    constexpr bool kB16 = DT == 1 || DT == 3;
+    // bf16: 2-byte values with one raw byte (raw bytes by dword and
+    // bpermute, two steps per store in the main loop below)
+    constexpr bool kB16 = DT == 1;
+    constexpr uint32_t RB = Fmt<DT>::RB, SB = Fmt<DT>::SB;
     // refills found stale by the scalar refill masks and reloaded in a rare
     // branch (bf16, fp16, fp8); fp32 also loads the pair 64 words further
     constexpr bool kScalarStale = DT != 2;
@@ -1684,7 +1814,7 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
         const uint64_t a0 = uniform_u64(gload<uint64_t>(ix));
         const uint64_t a1 = uniform_u64(gload<uint64_t>(ix + 8));
         const uint64_t a2 = nch == 2 ? uniform_u64(gload<uint64_t>(ix + 16)) : a1;
-        const uint64_t rawmax = raw_record_bytes(ce);
+        const uint64_t rawmax = raw_record_bytes(ce, SB);
         // V5 for the pair's index entries: aligned, ordered, inside the records,
         // and no record longer than a full chunk's RAW record (a coarse bound
         // that keeps the 32-bit resource sizes below valid; each record is then
@@ -1712,10 +1842,10 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
             nsym = rh.x >> 16;
             nw = rh.y;
             ok = ok && (mode == 1 || mode == kCoded) && rh.z == ni && rh.w == len;
-            if (ok && mode == 1) ok = nsym == 0 && nw == 0 && len == raw_record_bytes(ni);
+            if (ok && mode == 1) ok = nsym == 0 && nw == 0 && len == raw_record_bytes(ni, SB);
             // a coded record is strictly smaller than the chunk's RAW record
             // (it would have been stored RAW otherwise); a longer one is corrupt
-            if (ok && mode == kCoded) ok = nsym >= 1 && nsym <= 256 && len < raw_record_bytes(ni);
+            if (ok && mode == kCoded) ok = nsym >= 1 && nsym <= 256 && len < raw_record_bytes(ni, SB);
             if (S && ok && mode == kCoded) {
                 ok = len >= words_offset_sampled(nsym);
                 nesc = bld32(rrec, ok ? rel + (uint32_t)esc_count_offset(nsym) : kOutOfRange);
@@ -1731,7 +1861,8 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
         const uint32_t np = __popc(pb);
         const uint32_t pre = half_excl_scan(np, lj);
         uint32_t fk[8], lsum = 0, cpre[8];
-        bool fok = true;
+        // (a table names only symbols below 2^SB, the exponent field's range)
+        bool fok = SB == 8 || 8 * lj < (1u << SB) || pb == 0;
         {
             uint32_t k2 = pre;
 #pragma unroll
@@ -1799,7 +1930,13 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
         // never consumed by a valid stream (a stream that tries fails the end
         // check offv == n_words).
         const uint32_t pair_vals = vals0 + vals1;
-        const rsrc_t rsm = make_rsrc(d.in + sm_off + c0 * ce * R, pair_vals * R);
+        // (fp16, fp8: the pair's packed raw fields, and the 3 bytes after them
+        // that a field's dword load may touch, inside the readable buffer)
+        const uint64_t rsm_at = sm_off + c0 * ce * RB / 8;
+        const rsrc_t rsm = make_rsrc(d.in + rsm_at, R > 0 ? pair_vals * R
+                                                          : (uint32_t)min<uint64_t>(packed_bytes(pair_vals, RB) + 3,
+                                                                                    d.in_bytes - rsm_at));
+        const uint32_t lanebit = ((h ? vals0 : 0u) + lj) * RB;  // fp16, fp8: bit of the lane's step-0 raw field
         const rsrc_t rout = make_rsrc(d.out + c0 * ce * EB, pair_vals * EB);
         const uint32_t sm_lane = (h ? vals0 : 0u) * R + lj * R;
         const uint32_t out_lane = rans_run ? (h ? vals0 : 0u) * EB + lj * EB : kOutOfRange;
@@ -1889,25 +2026,21 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
             const uint32_t ew0 = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)escw);
             const uint32_t ew1 = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)escw1);
             uint32_t e = ((idx >= 128 ? ew1 : ew0) >> (8 * (idx & 3u))) & 0xFFu;
-            bool bad = idx >= nesc || nsym == 256;
+            bool bad = idx >= nesc || nsym == 256 || (SB < 8 && e >= (1u << SB));
             if (tail && idx >= 256) {
                 // past the held bytes: load it, and check here that it is no sampled
                 // symbol (the bitmap byte of e's group is held by lane e >> 3 of the half)
                 e = bld8(rrec, mine && idx < nesc ? escat + idx : kOutOfRange);
                 const uint32_t pbe = (uint32_t)__builtin_amdgcn_ds_bpermute((int)(((e >> 3) | (h << 5)) << 2), (int)pb);
-                bad = bad || ((pbe >> (e & 7u)) & 1u);
+                bad = bad || ((pbe >> (e & 7u)) & 1u) || (SB < 8 && e >= (1u << SB));
             }
             escbad = escbad || (mine && bad);
             escv += h ? ehi : elo;
             uint32_t ve;
             if (DT == 1) {
                 asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(ve) : "s"(0x807Fu), "v"(sp), "v"(e << 7));
-            } else if (DT == 3) {
-                asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(ve) : "s"(0x00FFu), "v"(sp), "v"(e << 8));
-            } else if (DT == 2) {
-                ve = ((sp | ((sp & 0x800000u) << 8)) & 0x807FFFFFu) | (e << 23);
             } else {
-                ve = e;
+                ve = join_value<DT>(e, sp);
             }
             return mine ? ve : v;
         };
@@ -1983,12 +2116,17 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
                 if (S && __builtin_expect(escm != 0, 0)) v = escape_value(escm, v, sp, tail);
                 if (store) bst16(rout, out_lane + t * 32 * EB, v);
                 return v;
-            } else if (DT == 3) {
-                // the low byte from sp, the symbol (em bits 12-19) to bits 8-15
+            } else if constexpr (DT != 2) {
+                // fp16, fp8: sign (the raw field's top bit, copied to the value's
+                // top bit) and mantissa from sp, the exponent (em bits 12-19) to
+                // bit SYM; the store keeps the value's EB bytes
+                constexpr uint32_t SYM = Fmt<DT>::SYM, top = 8 * EB - 1;
+                constexpr uint32_t keep = (1u << top) | ((1u << (RB - 1)) - 1u);
+                const uint32_t spx = sp | ((sp >> (RB - 1)) << top);
                 uint32_t v;
-                asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(v) : "s"(0x00FFu), "v"(sp), "v"(em >> 4));
+                asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(v) : "s"(keep), "v"(spx), "v"(em >> (12 - SYM)));
                 if (S && __builtin_expect(escm != 0, 0)) v = escape_value(escm, v, sp, tail);
-                if (store) bst16(rout, out_lane + t * 32 * EB, v);
+                if (store) bst_value<DT>(rout, out_lane + t * 32 * EB, v);
                 return v;
             } else if (DT == 2) {
                 // sign (bit 23 of sm) to bit 31, mantissa bits 0-22, exponent to bits 23-30
@@ -1997,12 +2135,8 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
                 if (S && __builtin_expect(escm != 0, 0)) v = escape_value(escm, v, sp, tail);
                 bst32(rout, out_lane + t * 32 * EB, v);
                 return 0u;
-            } else {
-                uint32_t v = (em >> 12) & 0xFFu;  // the symbol is the value
-                if (S && __builtin_expect(escm != 0, 0)) v = escape_value(escm, v, sp, tail);
-                if (store) bst_value<DT>(rout, out_lane + t * 32 * EB, v);
-                return v;
             }
+            return 0u;
         };
         uint32_t t = 0;
         if (kB16) {
@@ -2048,12 +2182,23 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
                 D1 = bld32(rsm, smd0 + (t + 20) * 32);
                 group8(t + 8, N0, N1);
             }
-        } else if (DT == 4) {
-            // fp8: no raw bytes, one byte store per step (packing four steps
-            // into a dword through two bpermute rounds measured slower)
-            for (; t < Tmain; t += 8) {
+        } else if constexpr (R == 0) {
+            // fp16, fp8: each lane's raw field by one dword load, eight steps
+            // ahead (step t's fields of a half are 4 RB bytes further than
+            // step t - 1's); one store of EB bytes per step (packing fp8 steps
+            // into dwords through bpermute rounds measured slower)
+            constexpr int kAhead = 8;
+            const uint32_t lanebyte = lanebit >> 3, lanesh = lanebit & 7u;
+            uint32_t rq[kAhead];
 #pragma unroll
-                for (int u = 0; u < 8; ++u) step(t + u, runm, false, 0u, u & 3, true);
+            for (int u = 0; u < kAhead; ++u) rq[u] = bld32(rsm, lanebyte + u * 4 * RB);
+            for (; t < Tmain; t += kAhead) {
+#pragma unroll
+                for (int u = 0; u < kAhead; ++u) {
+                    const uint32_t sp = (rq[u] >> lanesh) & ((1u << RB) - 1u);
+                    rq[u] = bld32(rsm, lanebyte + (t + u + kAhead) * 4 * RB);
+                    step(t + u, runm, false, sp, u & 3, true);
+                }
             }
         } else {
             constexpr int kSmAhead = 8;  // sign+mantissa bytes are loaded this many steps ahead
@@ -2073,7 +2218,8 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
         for (; t < Tw; t += 8) {
             uint32_t smt[8];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) smt[u] = bload_sm<DT>(rsm, sm_lane + (t + u) * 32 * R);
+            for (int u = 0; u < 8; ++u)
+                smt[u] = R > 0 ? bload_sm<DT>(rsm, sm_lane + (t + u) * 32 * R) : raw_field<DT>(rsm, lanebit + (t + u) * 32 * RB);
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 const uint32_t tt = t + u;
@@ -2086,7 +2232,15 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
             half_mask(__ballot(rans_run && (x != kStateLow || offv != nw || (S && (escbad || escv != nesc)))), h) != 0;
         ok = ok && !endbad;
         // ---- chunks stored RAW: exponent bytes straight from the record ----
-        if (raw_run) {
+        if (R == 0 && raw_run) {
+            // fp16, fp8: the chunk's symbols (packed at SB bits after the record
+            // header) and raw fields (packed at RB bits), value by value
+            const uint32_t ob = (h ? vals0 : 0u) * EB, eo = rel + kRecHeaderBytes, vb = (h ? vals0 : 0u) * RB;
+            for (uint32_t i = lj; i < ni; i += 32) {
+                const uint32_t sym = packed_field(rrec, eo, i * SB, SB);
+                bst_value<DT>(rout, ob + i * EB, join_value<DT>(sym, raw_field<DT>(rsm, vb + i * RB)));
+            }
+        } else if (raw_run) {
             // units of 16 values: 16 exponent bytes and 16 R raw bytes in,
             // 16 EB bytes out, all 128-bit; four units per lane in flight
             const uint32_t ob = (h ? vals0 : 0u) * EB, sb = (h ? vals0 : 0u) * R, eo = rel + kRecHeaderBytes;
@@ -2108,7 +2262,7 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
                 }
             }
             for (uint32_t i = 16 * nu + lj; i < ni; i += 32) {  // the chunk's last values
-                const uint32_t v = merge_value<DT>(bld8(rrec, eo + i), bload_sm<DT>(rsm, sb + i * R));
+                const uint32_t v = join_value<DT>(bld8(rrec, eo + i), bload_sm<DT>(rsm, sb + i * R));
                 bst_value<DT>(rout, ob + i * EB, v);
             }
         }
@@ -2153,8 +2307,8 @@ hipError_t noalloc_scratch(void **ptr) {
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-// kernel template for a dtype code: bf16 1, fp32 2, fp16 3, both fp8 codes 4
-static int kernel_format(int dtype) { return dtype <= 3 ? dtype : 4; }
+// (the kernel template parameter is the dtype code, 1 to 5)
+static int kernel_format(int dtype) { return dtype; }
 
 hipError_t launch_compress(const EncParams &ep, hipStream_t stream, const ProfileEvents *ev) {
     uint64_t threads = ep.total_pairs > ep.nbuf ? ep.total_pairs : ep.nbuf;
@@ -2163,7 +2317,8 @@ hipError_t launch_compress(const EncParams &ep, hipStream_t stream, const Profil
         case 1: k_plan<1><<<dim3(ep.nbuf), dim3(256), 0, stream>>>(ep); break;
         case 2: k_plan<2><<<dim3(ep.nbuf), dim3(256), 0, stream>>>(ep); break;
         case 3: k_plan<3><<<dim3(ep.nbuf), dim3(256), 0, stream>>>(ep); break;
-        default: k_plan<4><<<dim3(ep.nbuf), dim3(256), 0, stream>>>(ep); break;
+        case 4: k_plan<4><<<dim3(ep.nbuf), dim3(256), 0, stream>>>(ep); break;
+        default: k_plan<5><<<dim3(ep.nbuf), dim3(256), 0, stream>>>(ep); break;
         }
     }
     k_prepare<<<dim3((uint32_t)((threads + 255) / 256)), dim3(256), 0, stream>>>(ep);
@@ -2176,10 +2331,12 @@ hipError_t launch_compress(const EncParams &ep, hipStream_t stream, const Profil
         case 2: k_encode<2, false><<<grid, dim3(64), 0, stream>>>(ep); break;
         case 3: k_encode<3, false><<<grid, dim3(64), 0, stream>>>(ep); break;
         case 4: k_encode<4, false><<<grid, dim3(64), 0, stream>>>(ep); break;
+        case 5: k_encode<5, false><<<grid, dim3(64), 0, stream>>>(ep); break;
         case 9: k_encode<1, true><<<grid, dim3(64), 0, stream>>>(ep); break;
         case 10: k_encode<2, true><<<grid, dim3(64), 0, stream>>>(ep); break;
         case 11: k_encode<3, true><<<grid, dim3(64), 0, stream>>>(ep); break;
-        default: k_encode<4, true><<<grid, dim3(64), 0, stream>>>(ep); break;
+        case 12: k_encode<4, true><<<grid, dim3(64), 0, stream>>>(ep); break;
+        default: k_encode<5, true><<<grid, dim3(64), 0, stream>>>(ep); break;
         }
         if (ev != nullptr) (void)hipEventRecord(ev->stop, stream);
         if (ep.plans != nullptr) {
@@ -2188,7 +2345,8 @@ hipError_t launch_compress(const EncParams &ep, hipStream_t stream, const Profil
             case 1: k_raw_frame<1><<<rgrid, dim3(256), 0, stream>>>(ep); break;
             case 2: k_raw_frame<2><<<rgrid, dim3(256), 0, stream>>>(ep); break;
             case 3: k_raw_frame<3><<<rgrid, dim3(256), 0, stream>>>(ep); break;
-            default: k_raw_frame<4><<<rgrid, dim3(256), 0, stream>>>(ep); break;
+            case 4: k_raw_frame<4><<<rgrid, dim3(256), 0, stream>>>(ep); break;
+            default: k_raw_frame<5><<<rgrid, dim3(256), 0, stream>>>(ep); break;
             }
         }
         const dim3 cgrid((uint32_t)((ep.total_pairs + kCompactPairs - 1) / kCompactPairs));
@@ -2196,7 +2354,8 @@ hipError_t launch_compress(const EncParams &ep, hipStream_t stream, const Profil
         case 1: k_compact<1><<<cgrid, dim3(128 * kCompactPairs), 0, stream>>>(ep); break;
         case 2: k_compact<2><<<cgrid, dim3(128 * kCompactPairs), 0, stream>>>(ep); break;
         case 3: k_compact<3><<<cgrid, dim3(128 * kCompactPairs), 0, stream>>>(ep); break;
-        default: k_compact<4><<<cgrid, dim3(128 * kCompactPairs), 0, stream>>>(ep); break;
+        case 4: k_compact<4><<<cgrid, dim3(128 * kCompactPairs), 0, stream>>>(ep); break;
+        default: k_compact<5><<<cgrid, dim3(128 * kCompactPairs), 0, stream>>>(ep); break;
         }
         if (ep.plans != nullptr) {
             // the realised frames' gain check, then the RAW frame of each buffer that failed it
@@ -2208,7 +2367,8 @@ hipError_t launch_compress(const EncParams &ep, hipStream_t stream, const Profil
             case 1: k_accept<1><<<agrid, dim3(256), 0, stream>>>(ep); k_raw_frame<1><<<rgrid, dim3(256), 0, stream>>>(rp); break;
             case 2: k_accept<2><<<agrid, dim3(256), 0, stream>>>(ep); k_raw_frame<2><<<rgrid, dim3(256), 0, stream>>>(rp); break;
             case 3: k_accept<3><<<agrid, dim3(256), 0, stream>>>(ep); k_raw_frame<3><<<rgrid, dim3(256), 0, stream>>>(rp); break;
-            default: k_accept<4><<<agrid, dim3(256), 0, stream>>>(ep); k_raw_frame<4><<<rgrid, dim3(256), 0, stream>>>(rp); break;
+            case 4: k_accept<4><<<agrid, dim3(256), 0, stream>>>(ep); k_raw_frame<4><<<rgrid, dim3(256), 0, stream>>>(rp); break;
+            default: k_accept<5><<<agrid, dim3(256), 0, stream>>>(ep); k_raw_frame<5><<<rgrid, dim3(256), 0, stream>>>(rp); break;
             }
         }
     }
@@ -2229,13 +2389,15 @@ hipError_t launch_decompress(const DecParams &vp, const DecodeParams &dp, int dt
         case 1: k_decode<1, false><<<dim3((uint32_t)grid), dim3(64), 0, stream>>>(dp); break;
         case 2: k_decode<2, false><<<dim3((uint32_t)grid), dim3(64), 0, stream>>>(dp); break;
         case 3: k_decode<3, false><<<dim3((uint32_t)grid), dim3(64), 0, stream>>>(dp); break;
-        default: k_decode<4, false><<<dim3((uint32_t)grid), dim3(64), 0, stream>>>(dp); break;
+        case 4: k_decode<4, false><<<dim3((uint32_t)grid), dim3(64), 0, stream>>>(dp); break;
+        default: k_decode<5, false><<<dim3((uint32_t)grid), dim3(64), 0, stream>>>(dp); break;
         }
         switch (kernel_format(dtype)) {
         case 1: k_decode<1, true><<<dim3((uint32_t)grid), dim3(64), 0, stream>>>(dp); break;
         case 2: k_decode<2, true><<<dim3((uint32_t)grid), dim3(64), 0, stream>>>(dp); break;
         case 3: k_decode<3, true><<<dim3((uint32_t)grid), dim3(64), 0, stream>>>(dp); break;
-        default: k_decode<4, true><<<dim3((uint32_t)grid), dim3(64), 0, stream>>>(dp); break;
+        case 4: k_decode<4, true><<<dim3((uint32_t)grid), dim3(64), 0, stream>>>(dp); break;
+        default: k_decode<5, true><<<dim3((uint32_t)grid), dim3(64), 0, stream>>>(dp); break;
         }
         if (ev != nullptr) (void)hipEventRecord(ev->stop, stream);
     }

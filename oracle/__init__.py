@@ -29,7 +29,9 @@ FP8_E4M3 = 4
 FP8_E5M2 = 5
 DTYPES = (BF16, FP32, FP16, FP8_E4M3, FP8_E5M2)
 _ELEM = {BF16: np.uint16, FP32: np.uint32, FP16: np.uint16, FP8_E4M3: np.uint8, FP8_E5M2: np.uint8}
-_RAW = {BF16: 1, FP32: 3, FP16: 1, FP8_E4M3: 0, FP8_E5M2: 0}
+# bits of the raw (sign+mantissa) field and of the coded exponent field
+_RAW_BITS = {BF16: 8, FP32: 24, FP16: 11, FP8_E4M3: 4, FP8_E5M2: 3}
+_SYM_BITS = {BF16: 8, FP32: 8, FP16: 5, FP8_E4M3: 4, FP8_E5M2: 5}
 OK, INVALID, CAPACITY, CORRUPT = 0, 1, 2, 3
 
 LANES = 32
@@ -109,8 +111,19 @@ def _bits(dtype: int, values) -> np.ndarray:
     return a.view(want).reshape(-1)
 
 
-def raw_bytes_per_value(dtype: int) -> int:
-    return _RAW[dtype]
+def raw_bits(dtype: int) -> int:
+    """Bits of a value's raw field (sign and mantissa)."""
+    return _RAW_BITS[dtype]
+
+
+def sym_bits(dtype: int) -> int:
+    """Bits of a value's coded symbol (its exponent field)."""
+    return _SYM_BITS[dtype]
+
+
+def packed_bytes(n: int, bits: int) -> int:
+    """Bytes that n fields of `bits` bits take packed back to back."""
+    return (n * bits + 7) // 8
 
 
 def chunk_elems(dtype: int, chunk_bytes: int = 0) -> int:
@@ -118,14 +131,15 @@ def chunk_elems(dtype: int, chunk_bytes: int = 0) -> int:
 
 
 def split(dtype: int, values):
-    """Coded bytes (n,) and raw bytes (r*n,) of each value (the exponent and the
-    sign+mantissa for bf16 and fp32)."""
+    """The exponent field of each value (one byte each, n) and the packed raw
+    fields (sign and mantissa, raw_bits(dtype) bits each, value order, least
+    significant bit first)."""
     v = _bits(dtype, values)
     n = v.size
     e = np.empty(n, np.uint8)
-    sm = np.empty(max(n * raw_bytes_per_value(dtype), 1), np.uint8)
+    sm = np.empty(max(packed_bytes(n, raw_bits(dtype)), 1), np.uint8)
     lib().orc_split(dtype, _p(v), n, _p(e), _p(sm))
-    return e, sm[: n * raw_bytes_per_value(dtype)]
+    return e, sm[: packed_bytes(n, raw_bits(dtype))]
 
 
 def merge(dtype: int, e, sm) -> np.ndarray:

@@ -26,8 +26,9 @@
  *    frame is committed when coding does not pay; Algorithm 2: the receiver
  *    validates the header before decoding.
  *  - UCCL-Zip review page, Figure 13: the payload types bfloat16, float16,
- *    float32, float8_e4m3fn and float8_e5m2.  For fp16 and fp8 the coded
- *    symbol is the byte that holds the exponent (orc_split).
+ *    float32, float8_e4m3fn and float8_e5m2.  For every type the coded symbol
+ *    is the exponent field alone (Figure 2's split) and the sign and mantissa
+ *    bits are stored raw, bit-packed (orc_split).
  *  - NCCLZ Sec. IV-C, Eq. (1) and (2), Algorithm 1: the runtime arbitration
  *    between coding and RAW from a bounded sample and a link/codec time
  *    model (orc_plan_call, orc_compress_arbitrated).
@@ -92,14 +93,47 @@ static uint64_t get64(const uint8_t *p) {
     return v;
 }
 
-/* bytes stored raw per value, and bytes per value (0: not a dtype) */
-static int orc_raw_bytes(int dtype) {
+/* Bits of a value's sign+mantissa field (stored raw) and of its exponent
+ * field (the coded symbol): bf16 1+7 and 8, fp32 1+23 and 8, fp16 1+10 and
+ * 5, fp8 e4m3fn 1+3 and 4, fp8 e5m2 1+2 and 5. */
+static int orc_raw_bits(int dtype) {
     switch (dtype) {
-    case ORC_DT_BF16: return 1;
-    case ORC_DT_FP32: return 3;
-    case ORC_DT_FP16: return 1;
-    default: return 0; /* fp8: the whole byte is coded */
+    case ORC_DT_BF16: return 8;
+    case ORC_DT_FP32: return 24;
+    case ORC_DT_FP16: return 11;
+    case ORC_DT_FP8_E4M3: return 4;
+    case ORC_DT_FP8_E5M2: return 3;
+    default: return 0;
     }
+}
+static int orc_sym_bits(int dtype) {
+    switch (dtype) {
+    case ORC_DT_FP16: case ORC_DT_FP8_E5M2: return 5;
+    case ORC_DT_FP8_E4M3: return 4;
+    default: return 8;
+    }
+}
+
+/* Bytes that n fields of w bits take when packed (see orc_put_bits). */
+static uint64_t orc_packed_bytes(uint64_t n, int w) { return (n * (uint64_t)w + 7) / 8; }
+
+/* Packing of w-bit fields, value order, least significant bit first: field i
+ * occupies bits w*i .. w*i + w - 1 of the byte string, where bit k is bit
+ * (k mod 8) of byte k / 8.  Eight-bit fields are plain bytes, 24-bit fields
+ * three bytes little-endian.  dst must be zeroed beforehand. */
+static void orc_put_bits(uint8_t *dst, uint64_t i, int w, uint32_t v) {
+    for (int b = 0; b < w; ++b) {
+        uint64_t k = i * (uint64_t)w + (uint64_t)b;
+        if ((v >> b) & 1u) dst[k >> 3] |= (uint8_t)(1u << (k & 7));
+    }
+}
+static uint32_t orc_get_bits(const uint8_t *src, uint64_t i, int w) {
+    uint32_t v = 0;
+    for (int b = 0; b < w; ++b) {
+        uint64_t k = i * (uint64_t)w + (uint64_t)b;
+        v |= (uint32_t)((src[k >> 3] >> (k & 7)) & 1u) << b;
+    }
+    return v;
 }
 static int orc_elem_bytes(int dtype) {
     switch (dtype) {
@@ -123,70 +157,69 @@ uint64_t orc_chunk_elems(int dtype, uint64_t chunk_bytes) {
 }
 
 /* ---- step 1: field split (UCCL-Zip Fig. 2) ------------------------------
- * bf16 word v: exponent e = bits 14..7; sign+mantissa byte sm keeps the sign
- * as its top bit and the 7 mantissa bits below it.
- * fp32 word v: exponent e = bits 30..23; sm is 24 bits: sign at bit 23 and
- * the 23 mantissa bits below, stored as 3 bytes little-endian.
- * fp16 and fp8 (the other types of UCCL-Zip Fig. 13; the pages give no
- * layout for them): the coded symbol is the byte that holds the exponent and
- * the remaining bytes are stored raw.  fp16 word v: e = bits 15..8 (sign, the
- * 5 exponent bits, the top 2 mantissa bits), sm = bits 7..0.  fp8 byte v:
- * e = v, nothing raw.  (Neither has a byte-aligned field of exponent bits
- * alone; the sign and mantissa bits coded along are near-uniform and cost
- * about what they would raw.) */
+ * Every value is split into its exponent field e (the coded symbol) and the
+ * rest, sign and mantissa, which is stored raw: the sign becomes the top bit
+ * of the raw field, above the mantissa bits.  The pages split every type
+ * this way (only the exponent field is compressed):
+ *   bf16 v:      e = bits 14..7  (8 bits), raw = sign << 7  | bits 6..0
+ *   fp32 v:      e = bits 30..23 (8 bits), raw = sign << 23 | bits 22..0
+ *   fp16 v:      e = bits 14..10 (5 bits), raw = sign << 10 | bits 9..0
+ *   e4m3fn v:    e = bits 6..3   (4 bits), raw = sign << 3  | bits 2..0
+ *   e5m2 v:      e = bits 6..2   (5 bits), raw = sign << 2  | bits 1..0
+ * The raw fields are packed back to back in value order (orc_put_bits): one
+ * byte per value for bf16, three bytes little-endian for fp32, 11, 4 and 3
+ * bits for fp16 and the fp8 types.  e_out receives one byte per value (the
+ * field's value); sm_out receives orc_packed_bytes(n, raw bits) bytes.
+ * NaN payloads, infinities, subnormals and signed zeros pass through
+ * unchanged: the split is a bijection of the bit pattern. */
+static void orc_fields(int dtype, uint32_t v, uint32_t *e, uint32_t *raw) {
+    switch (dtype) {
+    case ORC_DT_BF16: *e = (v >> 7) & 0xFFu; *raw = ((v >> 15) << 7) | (v & 0x7Fu); break;
+    case ORC_DT_FP32: *e = (v >> 23) & 0xFFu; *raw = ((v >> 31) << 23) | (v & 0x7FFFFFu); break;
+    case ORC_DT_FP16: *e = (v >> 10) & 0x1Fu; *raw = ((v >> 15) << 10) | (v & 0x3FFu); break;
+    case ORC_DT_FP8_E4M3: *e = (v >> 3) & 0xFu; *raw = ((v >> 7) << 3) | (v & 0x7u); break;
+    default: *e = (v >> 2) & 0x1Fu; *raw = ((v >> 7) << 2) | (v & 0x3u); break; /* e5m2 */
+    }
+}
+static uint32_t orc_join(int dtype, uint32_t e, uint32_t raw) {
+    switch (dtype) {
+    case ORC_DT_BF16: return ((raw >> 7) << 15) | (e << 7) | (raw & 0x7Fu);
+    case ORC_DT_FP32: return ((raw >> 23) << 31) | (e << 23) | (raw & 0x7FFFFFu);
+    case ORC_DT_FP16: return ((raw >> 10) << 15) | (e << 10) | (raw & 0x3FFu);
+    case ORC_DT_FP8_E4M3: return ((raw >> 3) << 7) | (e << 3) | (raw & 0x7u);
+    default: return ((raw >> 2) << 7) | (e << 2) | (raw & 0x3u);
+    }
+}
+static uint32_t orc_load(int dtype, const void *in, uint64_t i) {
+    switch (orc_elem_bytes(dtype)) {
+    case 1: return ((const uint8_t *)in)[i];
+    case 2: return ((const uint16_t *)in)[i];
+    default: return ((const uint32_t *)in)[i];
+    }
+}
+static void orc_store(int dtype, void *out, uint64_t i, uint32_t v) {
+    switch (orc_elem_bytes(dtype)) {
+    case 1: ((uint8_t *)out)[i] = (uint8_t)v; break;
+    case 2: ((uint16_t *)out)[i] = (uint16_t)v; break;
+    default: ((uint32_t *)out)[i] = v; break;
+    }
+}
+
 void orc_split(int dtype, const void *in, uint64_t n, uint8_t *e_out, uint8_t *sm_out) {
-    if (dtype == ORC_DT_FP16) {
-        const uint16_t *v = (const uint16_t *)in;
-        for (uint64_t i = 0; i < n; ++i) {
-            e_out[i] = (uint8_t)(v[i] >> 8);
-            sm_out[i] = (uint8_t)(v[i] & 0xFFu);
-        }
-    } else if (dtype == ORC_DT_FP8_E4M3 || dtype == ORC_DT_FP8_E5M2) {
-        const uint8_t *v = (const uint8_t *)in;
-        for (uint64_t i = 0; i < n; ++i) e_out[i] = v[i];
-        (void)sm_out;
-    } else if (dtype == ORC_DT_BF16) {
-        const uint16_t *v = (const uint16_t *)in;
-        for (uint64_t i = 0; i < n; ++i) {
-            uint32_t x = v[i];
-            e_out[i] = (uint8_t)((x >> 7) & 0xFFu);
-            sm_out[i] = (uint8_t)(((x >> 8) & 0x80u) | (x & 0x7Fu));
-        }
-    } else {
-        const uint32_t *v = (const uint32_t *)in;
-        for (uint64_t i = 0; i < n; ++i) {
-            uint32_t x = v[i];
-            uint32_t sm = ((x >> 8) & 0x800000u) | (x & 0x7FFFFFu);
-            e_out[i] = (uint8_t)((x >> 23) & 0xFFu);
-            sm_out[3 * i + 0] = (uint8_t)(sm & 0xFFu);
-            sm_out[3 * i + 1] = (uint8_t)((sm >> 8) & 0xFFu);
-            sm_out[3 * i + 2] = (uint8_t)(sm >> 16);
-        }
+    int w = orc_raw_bits(dtype);
+    memset(sm_out, 0, (size_t)orc_packed_bytes(n, w));
+    for (uint64_t i = 0; i < n; ++i) {
+        uint32_t e, raw;
+        orc_fields(dtype, orc_load(dtype, in, i), &e, &raw);
+        e_out[i] = (uint8_t)e;
+        orc_put_bits(sm_out, i, w, raw);
     }
 }
 
 /* inverse of orc_split */
 void orc_merge(int dtype, const uint8_t *e, const uint8_t *sm, uint64_t n, void *out) {
-    if (dtype == ORC_DT_FP16) {
-        uint16_t *v = (uint16_t *)out;
-        for (uint64_t i = 0; i < n; ++i) v[i] = (uint16_t)(((uint32_t)e[i] << 8) | sm[i]);
-    } else if (dtype == ORC_DT_FP8_E4M3 || dtype == ORC_DT_FP8_E5M2) {
-        uint8_t *v = (uint8_t *)out;
-        for (uint64_t i = 0; i < n; ++i) v[i] = e[i];
-        (void)sm;
-    } else if (dtype == ORC_DT_BF16) {
-        uint16_t *v = (uint16_t *)out;
-        for (uint64_t i = 0; i < n; ++i) {
-            uint32_t s = sm[i];
-            v[i] = (uint16_t)(((s & 0x80u) << 8) | ((uint32_t)e[i] << 7) | (s & 0x7Fu));
-        }
-    } else {
-        uint32_t *v = (uint32_t *)out;
-        for (uint64_t i = 0; i < n; ++i) {
-            uint32_t s = (uint32_t)sm[3 * i] | ((uint32_t)sm[3 * i + 1] << 8) | ((uint32_t)sm[3 * i + 2] << 16);
-            v[i] = ((s & 0x800000u) << 8) | ((uint32_t)e[i] << 23) | (s & 0x7FFFFFu);
-        }
-    }
+    int w = orc_raw_bits(dtype);
+    for (uint64_t i = 0; i < n; ++i) orc_store(dtype, out, i, orc_join(dtype, e[i], orc_get_bits(sm, i, w)));
 }
 
 /* ---- step 2: histogram of the chunk's exponents (UCCL-Zip Fig. 5(b)) ----
@@ -378,14 +411,22 @@ int orc_rans_decode(const uint32_t *states_in, const uint16_t *words, uint64_t n
 }
 
 /* ---- buffer layout ------------------------------------------------------
- * [0,64) header | [64, 64+8(C+1)) u64 rec_off[C+1] | pad | SM region at
- * sm_off = align16(64+8(C+1)), r*N bytes in value order | pad | records from
- * exp_off = align16(sm_off + r*N).  total = exp_off + rec_off[C]. */
+ * [0,64) header | [64, 64+8(C+1)) u64 rec_off[C+1] | pad | raw region at
+ * sm_off = align16(64+8(C+1)): the raw fields of all N values packed in value
+ * order, ceil(raw_bits * N / 8) bytes | pad | records from
+ * exp_off = align16(sm_off + ceil(raw_bits * N / 8)).
+ * total = exp_off + rec_off[C]. */
 static void orc_layout(int dtype, uint64_t n, uint64_t ce, uint64_t *C, uint64_t *sm_off, uint64_t *exp_off) {
     uint64_t c = (n + ce - 1) / ce;
     *C = c;
     *sm_off = orc_align16(ORC_HDR_BYTES + 8 * (c + 1));
-    *exp_off = orc_align16(*sm_off + (uint64_t)orc_raw_bytes(dtype) * n);
+    *exp_off = orc_align16(*sm_off + orc_packed_bytes(n, orc_raw_bits(dtype)));
+}
+
+/* Size of a chunk's RAW record: the 16-byte record header and the chunk's
+ * symbols packed at the type's exponent width, padded to 16 bytes. */
+static uint64_t orc_raw_record_bytes(int dtype, uint64_t ni) {
+    return orc_align16(ORC_REC_HDR + orc_packed_bytes(ni, orc_sym_bits(dtype)));
 }
 
 uint64_t orc_max_compressed_size(int dtype, uint64_t n, uint64_t chunk_bytes) {
@@ -396,13 +437,13 @@ uint64_t orc_max_compressed_size(int dtype, uint64_t n, uint64_t chunk_bytes) {
     uint64_t total = exp_off;
     for (uint64_t i = 0; i < C; ++i) {
         uint64_t ni = (i + 1 < C) ? ce : n - i * ce;
-        total += orc_align16(ORC_REC_HDR + ni);
+        total += orc_raw_record_bytes(dtype, ni);
     }
     return total;
 }
 
 /* The entropy bound of a buffer in bytes: for every chunk, its raw
- * sign+mantissa bytes plus n_i H_i / 8, where H_i is the empirical entropy
+ * sign+mantissa bits / 8 plus n_i H_i / 8, where H_i is the empirical entropy
  * (bits per value) of the chunk's coded symbols, -sum_s (c_s / n_i)
  * log2(c_s / n_i) over the chunk's histogram.  It is the size an ideal coder
  * of each chunk's symbols with the chunk's own table would reach, with no
@@ -411,12 +452,12 @@ uint64_t orc_max_compressed_size(int dtype, uint64_t n, uint64_t chunk_bytes) {
 double orc_entropy_bound(int dtype, const void *in, uint64_t n, uint64_t chunk_bytes) {
     uint64_t ce = orc_chunk_elems(dtype, chunk_bytes);
     if (ce == 0) return -1.0;
-    int r = orc_raw_bytes(dtype);
+    int w = orc_raw_bits(dtype);
     uint8_t *e = (uint8_t *)malloc((size_t)(n ? n : 1));
-    uint8_t *sm = (uint8_t *)malloc((size_t)(n * (uint64_t)r + 1));
+    uint8_t *sm = (uint8_t *)malloc((size_t)(orc_packed_bytes(n, w) + 1));
     orc_split(dtype, in, n, e, sm);
     free(sm);
-    double total = (double)r * (double)n;
+    double total = (double)w * (double)n / 8.0;
     for (uint64_t c0 = 0; c0 < n; c0 += ce) {
         uint64_t ni = n - c0 < ce ? n - c0 : ce;
         uint32_t counts[256];
@@ -433,9 +474,15 @@ double orc_entropy_bound(int dtype, const void *in, uint64_t n, uint64_t chunk_b
     return total;
 }
 
+/* The body of a RAW record: the chunk's symbols packed at sb bits. */
+static void orc_raw_body(const uint8_t *e, uint64_t ni, int sb, uint8_t *body) {
+    for (uint64_t i = 0; i < ni; ++i) orc_put_bits(body, i, sb, e[i]);
+}
+
 /* Encode one chunk's record (steps 2-4 plus the RANS/RAW choice) into rec,
- * which must hold align16(16 + ni) bytes.  Returns the record size. */
-static uint64_t orc_encode_record(const uint8_t *e, uint64_t ni, uint8_t *rec, int force_raw) {
+ * which must hold orc_raw_record_bytes bytes.  sb: the symbols' width.
+ * Returns the record size. */
+static uint64_t orc_encode_record(const uint8_t *e, uint64_t ni, int sb, uint8_t *rec, int force_raw) {
     uint32_t counts[256], f[256], c0[256], states[ORC_LANES];
     orc_histogram(e, ni, counts);
     int nsym = orc_normalize(counts, (uint32_t)ni, f);
@@ -445,7 +492,7 @@ static uint64_t orc_encode_record(const uint8_t *e, uint64_t ni, uint8_t *rec, i
     uint64_t tab_end = orc_align4(ORC_REC_HDR + 32 + 2 * (uint64_t)nsym);
     uint64_t words_at = tab_end + 4 * ORC_LANES;
     uint64_t rans_bytes = orc_align16(words_at + 2 * n_words);
-    uint64_t raw_bytes = orc_align16(ORC_REC_HDR + ni);
+    uint64_t raw_bytes = orc_align16(ORC_REC_HDR + orc_packed_bytes(ni, sb));
     uint64_t rec_bytes;
     if (!force_raw && rans_bytes < raw_bytes) {
         rec_bytes = rans_bytes;
@@ -470,7 +517,7 @@ static uint64_t orc_encode_record(const uint8_t *e, uint64_t ni, uint8_t *rec, i
         rec[0] = 1; /* mode RAW */
         put32(rec + 8, (uint32_t)ni);
         put32(rec + 12, (uint32_t)rec_bytes);
-        memcpy(rec + ORC_REC_HDR, e, (size_t)ni);
+        orc_raw_body(e, ni, sb, rec + ORC_REC_HDR);
     }
     free(words);
     return rec_bytes;
@@ -497,7 +544,7 @@ uint64_t orc_sample_counts(const uint8_t *e, uint64_t ni, uint64_t ce, uint32_t 
     return S;
 }
 
-static uint64_t orc_encode_record_sampled(const uint8_t *e, uint64_t ni, uint64_t ce, uint8_t *rec) {
+static uint64_t orc_encode_record_sampled(const uint8_t *e, uint64_t ni, uint64_t ce, int sb, uint8_t *rec) {
     uint32_t counts[256], f[256], c0[256], states[ORC_LANES];
     uint64_t S = orc_sample_counts(e, ni, ce, counts);
     int nsym = orc_normalize_sampled(counts, (uint32_t)S, f);
@@ -536,7 +583,7 @@ static uint64_t orc_encode_record_sampled(const uint8_t *e, uint64_t ni, uint64_
     uint64_t states_at = tab_end + 4, words_at = states_at + 4 * ORC_LANES;
     uint64_t esc_at = words_at + 2 * n_words;
     uint64_t coded_bytes = orc_align16(esc_at + n_esc);
-    uint64_t raw_bytes = orc_align16(ORC_REC_HDR + ni);
+    uint64_t raw_bytes = orc_align16(ORC_REC_HDR + orc_packed_bytes(ni, sb));
     uint64_t rec_bytes;
     if (coded_bytes < raw_bytes) {
         rec_bytes = coded_bytes;
@@ -563,7 +610,7 @@ static uint64_t orc_encode_record_sampled(const uint8_t *e, uint64_t ni, uint64_
         rec[0] = 1;
         put32(rec + 8, (uint32_t)ni);
         put32(rec + 12, (uint32_t)rec_bytes);
-        memcpy(rec + ORC_REC_HDR, e, (size_t)ni);
+        orc_raw_body(e, ni, sb, rec + ORC_REC_HDR);
     }
     free(m);
     free(esc);
@@ -579,11 +626,11 @@ static int orc_compress_frame(int dtype, const void *in, uint64_t n, uint64_t ch
     uint64_t ce = orc_chunk_elems(dtype, chunk_bytes);
     if (ce == 0) return ORC_INVALID;
     if (cap < orc_max_compressed_size(dtype, n, chunk_bytes)) return ORC_CAPACITY;
-    int r = orc_raw_bytes(dtype);
+    int w = orc_raw_bits(dtype), sb = orc_sym_bits(dtype);
     uint64_t C, sm_off, exp_off;
     orc_layout(dtype, n, ce, &C, &sm_off, &exp_off);
     uint8_t *e = (uint8_t *)malloc((size_t)(n ? n : 1));
-    const uint64_t sm_bytes = n * (uint64_t)r;
+    const uint64_t sm_bytes = orc_packed_bytes(n, w);
     uint8_t *sm = (uint8_t *)malloc((size_t)(sm_bytes > 0 ? sm_bytes : 1));
     orc_split(dtype, in, n, e, sm);
     memset(out, 0, (size_t)exp_off);
@@ -592,8 +639,8 @@ static int orc_compress_frame(int dtype, const void *in, uint64_t n, uint64_t ch
     put64(out + ORC_HDR_BYTES, 0);
     for (uint64_t i = 0; i < C; ++i) {
         uint64_t ni = (i + 1 < C) ? ce : n - i * ce;
-        off += sampled && !force_raw ? orc_encode_record_sampled(e + i * ce, ni, ce, out + exp_off + off)
-                                     : orc_encode_record(e + i * ce, ni, out + exp_off + off, force_raw);
+        off += sampled && !force_raw ? orc_encode_record_sampled(e + i * ce, ni, ce, sb, out + exp_off + off)
+                                     : orc_encode_record(e + i * ce, ni, sb, out + exp_off + off, force_raw);
         put64(out + ORC_HDR_BYTES + 8 * (i + 1), off);
     }
     uint64_t total = exp_off + off;
@@ -602,7 +649,7 @@ static int orc_compress_frame(int dtype, const void *in, uint64_t n, uint64_t ch
     out[6] = (uint8_t)dtype;
     out[7] = ORC_PROB_BITS;
     out[8] = ORC_LANES;
-    out[9] = (uint8_t)r;
+    out[9] = (uint8_t)w; /* raw bits per value */
     put16(out + 10, sampled ? 1u : 0u); /* flags: bit 0 = sampled tables */
     put32(out + 12, (uint32_t)ce);
     put64(out + 16, n);
@@ -714,7 +761,7 @@ int orc_plan_call(int dtype, const void *in, uint64_t n, uint64_t chunk_bytes, c
     /* the bounded sample and its statistics */
     uint64_t S = n < ORC_SAMPLE_BYTES / eb ? n : ORC_SAMPLE_BYTES / eb;
     uint8_t *e = (uint8_t *)malloc((size_t)S);
-    uint8_t *sm = (uint8_t *)malloc((size_t)(S * 3 + 1));
+    uint8_t *sm = (uint8_t *)malloc((size_t)(orc_packed_bytes(S, orc_raw_bits(dtype)) + 1));
     orc_split(dtype, in, S, e, sm);
     uint32_t counts[256];
     orc_histogram(e, S, counts);
@@ -771,9 +818,17 @@ int orc_compress_arbitrated(int dtype, const void *in, uint64_t n, uint64_t chun
 /* Decode one record into the chunk's exponents.  rec holds rec_len bytes
  * (already known to lie inside the buffer).  Checks V6-V9. */
 static int orc_decode_record_sampled(const uint8_t *rec, uint64_t rec_len, uint64_t ni, uint32_t nsym,
-                                     uint64_t n_words, uint8_t *e);
+                                     uint64_t n_words, int sb, uint8_t *e);
 
-static int orc_decode_record(const uint8_t *rec, uint64_t rec_len, uint64_t ni, uint8_t *e, int sampled) {
+/* A table names only symbols the type's exponent field can hold (below 2^sb:
+ * 32 for fp16 and e5m2, 16 for e4m3fn, all 256 for bf16 and fp32). */
+static int orc_bitmap_in_range(const uint8_t *bitmap, int sb) {
+    for (int s = 1 << sb; s < 256; ++s)
+        if ((bitmap[s >> 3] >> (s & 7)) & 1u) return 0;
+    return 1;
+}
+
+static int orc_decode_record(const uint8_t *rec, uint64_t rec_len, uint64_t ni, int sb, uint8_t *e, int sampled) {
     if (rec_len < ORC_REC_HDR) return ORC_CORRUPT;
     uint32_t mode = rec[0];
     uint32_t nsym = get16(rec + 2);
@@ -782,8 +837,9 @@ static int orc_decode_record(const uint8_t *rec, uint64_t rec_len, uint64_t ni, 
     uint64_t rec_bytes = get32(rec + 12);
     if (mode > 2 || n_values != ni || rec_bytes != rec_len) return ORC_CORRUPT;
     if (mode == 1) {
-        if (nsym != 0 || n_words != 0 || rec_len != orc_align16(ORC_REC_HDR + ni)) return ORC_CORRUPT;
-        memcpy(e, rec + ORC_REC_HDR, (size_t)ni);
+        if (nsym != 0 || n_words != 0 || rec_len != orc_align16(ORC_REC_HDR + orc_packed_bytes(ni, sb)))
+            return ORC_CORRUPT;
+        for (uint64_t i = 0; i < ni; ++i) e[i] = (uint8_t)orc_get_bits(rec + ORC_REC_HDR, i, sb);
         return ORC_OK;
     }
     /* a frame uses one kind of coded record: mode 0 (full histograms) or mode 2 (sampled) */
@@ -792,13 +848,13 @@ static int orc_decode_record(const uint8_t *rec, uint64_t rec_len, uint64_t ni, 
      * chunk's RAW record (the RAW rule, NCCLZ Sec. IV-C); one that is not is
      * rejected, so no record is ever longer than its RAW record and the
      * all-RAW size bounds every valid frame */
-    if (rec_len >= orc_align16(ORC_REC_HDR + ni)) return ORC_CORRUPT;
-    if (mode == 2) return orc_decode_record_sampled(rec, rec_len, ni, nsym, n_words, e);
+    if (rec_len >= orc_align16(ORC_REC_HDR + orc_packed_bytes(ni, sb))) return ORC_CORRUPT;
+    if (mode == 2) return orc_decode_record_sampled(rec, rec_len, ni, nsym, n_words, sb, e);
     /* RANS: bitmap, frequencies, states, words */
     if (rec_len < ORC_REC_HDR + 32) return ORC_CORRUPT;
     uint32_t pop = 0;
     for (int s = 0; s < 256; ++s) pop += (rec[16 + (s >> 3)] >> (s & 7)) & 1u;
-    if (pop != nsym || nsym < 1 || nsym > 256) return ORC_CORRUPT;
+    if (pop != nsym || nsym < 1 || nsym > 256 || !orc_bitmap_in_range(rec + 16, sb)) return ORC_CORRUPT;
     uint64_t tab_end = orc_align4(ORC_REC_HDR + 32 + 2 * (uint64_t)nsym);
     uint64_t words_at = tab_end + 4 * ORC_LANES;
     if (rec_len != orc_align16(words_at + 2 * n_words)) return ORC_CORRUPT;
@@ -831,17 +887,18 @@ static int orc_decode_record(const uint8_t *rec, uint64_t rec_len, uint64_t ni, 
  * dtype and element count, as a receiver does.  Returns ORC_OK, or
  * ORC_CORRUPT for any inconsistency; never reads outside in[0, in_bytes). */
 /* Mode 2: the sampled table, ESC in the last slot, the escape list in value
- * order.  Checks: bitmap and nsym agree (1..256), every frequency >= 1 and
- * they sum to 4095, n_esc and the words fit the record exactly, the rANS
- * stream ends as in orc_rans_decode, every escape of the list is used, and
- * no escaped byte is a sampled symbol (such a value would have been coded
- * directly). */
+ * order.  Checks: bitmap and nsym agree (1..256), no symbol beyond the
+ * exponent field's range, every frequency >= 1 and they sum to 4095, n_esc
+ * and the words fit the record exactly, the rANS stream ends as in
+ * orc_rans_decode, every escape of the list is used, and no escaped byte is a
+ * sampled symbol (such a value would have been coded directly) or beyond the
+ * exponent field's range. */
 static int orc_decode_record_sampled(const uint8_t *rec, uint64_t rec_len, uint64_t ni, uint32_t nsym,
-                                     uint64_t n_words, uint8_t *e) {
+                                     uint64_t n_words, int sb, uint8_t *e) {
     if (rec_len < ORC_REC_HDR + 32) return ORC_CORRUPT;
     uint32_t pop = 0;
     for (int s = 0; s < 256; ++s) pop += (rec[16 + (s >> 3)] >> (s & 7)) & 1u;
-    if (pop != nsym || nsym < 1 || nsym > 256) return ORC_CORRUPT;
+    if (pop != nsym || nsym < 1 || nsym > 256 || !orc_bitmap_in_range(rec + 16, sb)) return ORC_CORRUPT;
     uint64_t tab_end = orc_align4(ORC_REC_HDR + 32 + 2 * (uint64_t)nsym);
     uint64_t states_at = tab_end + 4, words_at = states_at + 4 * ORC_LANES;
     if (rec_len < words_at) return ORC_CORRUPT;
@@ -884,7 +941,7 @@ static int orc_decode_record_sampled(const uint8_t *rec, uint64_t rec_len, uint6
         if (ranks[i] < nsym) {
             e[i] = sym_of_rank[ranks[i]];
         } else {  /* ESC (only reachable when nsym < 256) */
-            if (used >= n_esc || present[esc[used]]) st = ORC_CORRUPT;
+            if (used >= n_esc || present[esc[used]] || esc[used] >= (1u << sb)) st = ORC_CORRUPT;
             else e[i] = esc[used++];
         }
     }
@@ -894,12 +951,12 @@ static int orc_decode_record_sampled(const uint8_t *rec, uint64_t rec_len, uint6
 }
 
 int orc_decompress(const uint8_t *in, uint64_t in_bytes, int dtype, uint64_t n, void *out) {
-    int r = orc_raw_bytes(dtype);
+    int w = orc_raw_bits(dtype), sb = orc_sym_bits(dtype);
     if (orc_elem_bytes(dtype) == 0) return ORC_INVALID;
     if (in_bytes < ORC_HDR_BYTES) return ORC_CORRUPT;
     /* V1: magic, version and the fixed coder parameters */
     if (get32(in) != ORC_MAGIC || get16(in + 4) != ORC_VERSION) return ORC_CORRUPT;
-    if (in[7] != ORC_PROB_BITS || in[8] != ORC_LANES || in[9] != (uint8_t)r) return ORC_CORRUPT;
+    if (in[7] != ORC_PROB_BITS || in[8] != ORC_LANES || in[9] != (uint8_t)w) return ORC_CORRUPT;
     /* flags: bit 0 = sampled tables; no other bit is defined */
     uint32_t flags = get16(in + 10);
     if (flags > 1) return ORC_CORRUPT;
@@ -927,7 +984,7 @@ int orc_decompress(const uint8_t *in, uint64_t in_bytes, int dtype, uint64_t n, 
     for (uint64_t i = 0; i < C && st == ORC_OK; ++i) {
         uint64_t ni = (i + 1 < C) ? ce : n - i * ce;
         uint64_t a = get64(in + ORC_HDR_BYTES + 8 * i), b = get64(in + ORC_HDR_BYTES + 8 * (i + 1));
-        st = orc_decode_record(in + exp_off + a, b - a, ni, e + i * ce, (int)(flags & 1u));
+        st = orc_decode_record(in + exp_off + a, b - a, ni, sb, e + i * ce, (int)(flags & 1u));
     }
     if (st == ORC_OK) orc_merge(dtype, e, in + sm_off, n, out);
     free(e);

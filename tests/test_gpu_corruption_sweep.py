@@ -102,3 +102,19 @@ def test_coded_records_not_smaller_than_raw_get_the_oracle_verdict():
         out, st = uz.decompress(torch.from_numpy(f).to(DEV), torch.bfloat16, v.size)
         torch.cuda.synchronize()
         assert (int(st.item()) == 0) == (ost == orc.OK)
+
+
+def test_symbols_beyond_the_exponent_range_get_the_oracle_verdict():
+    """fp16 frames naming a symbol no 5-bit exponent holds (in the table, or
+    as an escape byte): corrupt on the GPU as in the oracle; the unmodified
+    frames decode."""
+    from test_oracle_pins import _fp16_escape_out_of_range_frame, _fp16_moved_symbol_frame
+    for make in (_fp16_moved_symbol_frame, _fp16_escape_out_of_range_frame):
+        vals, good, bad = make()
+        for frame, want in ((good, 0), (bad, 3)):
+            assert (orc.decompress(frame, orc.FP16, vals.size)[0] == orc.OK) == (want == 0)
+            out, st = uz.decompress(torch.from_numpy(frame).to(DEV), torch.float16, vals.size)
+            torch.cuda.synchronize()
+            assert int(st.item()) == want, make.__name__
+            if want == 0:
+                assert np.array_equal(out.view(torch.int16).cpu().numpy().view(np.uint16), vals)

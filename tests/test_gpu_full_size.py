@@ -28,15 +28,15 @@ def _check_frame(b: np.ndarray, code: int, n: int, chunk_elems: int, modes=(0, 1
     """Header, index and record headers of one compressed buffer (any size);
     `modes`: the record modes the frame may hold (sampled tables: 1 and 2)."""
     C = (n + chunk_elems - 1) // chunk_elems
-    r = {orc.BF16: 1, orc.FP32: 3, orc.FP16: 1, orc.FP8_E4M3: 0, orc.FP8_E5M2: 0}[code]
+    w = orc.raw_bits(code)
     hdr = np.frombuffer(b[:64].tobytes(), dtype=np.uint64)
     assert int.from_bytes(b[0:4].tobytes(), "little") == 0x31505A55
-    assert int(b[6]) == code and int(b[7]) == 12 and int(b[8]) == 32 and int(b[9]) == r
+    assert int(b[6]) == code and int(b[7]) == 12 and int(b[8]) == 32 and int(b[9]) == w
     assert int.from_bytes(b[12:16].tobytes(), "little") == chunk_elems
     assert int(hdr[2]) == n and int(hdr[3]) == C
     sm_off, exp_off, total = int(hdr[4]), int(hdr[5]), int(hdr[6])
     assert sm_off == (64 + 8 * (C + 1) + 15) // 16 * 16
-    assert exp_off == (sm_off + r * n + 15) // 16 * 16
+    assert exp_off == (sm_off + (w * n + 7) // 8 + 15) // 16 * 16
     assert total == b.size
     idx = np.frombuffer(b[64:64 + 8 * (C + 1)].tobytes(), dtype=np.uint64).astype(np.int64)
     assert idx[0] == 0 and idx[-1] == total - exp_off

@@ -215,3 +215,23 @@ def test_corruptions_reported_as_the_oracle_reports():
     full = orc.compress(orc.BF16, bits)
     _, st = _decompress(_patch(full, 10, 1, 2), torch.bfloat16, n)
     assert st == uz.UZIP_ERR_CORRUPT_INPUT
+
+
+@pytest.mark.parametrize("tdtype", list(_ORC))
+@pytest.mark.parametrize("extra", [1, 2, 3])
+def test_sample_run_cut_by_the_buffer_end(tdtype, extra):
+    """The last chunk ends inside a sampled run, at a value that shares its
+    dword with bytes past the buffer (16,384 + 100 + extra values: run 4 of a
+    bf16/fp16 chunk, run 2 of an fp8 or fp32 chunk); the run's values up to
+    the end are counted as the oracle counts them.  The last values carry an
+    exponent no other value has, so a value read as zero changes the table."""
+    n = 16384 + 100 + extra
+    rng = np.random.default_rng(extra)
+    if tdtype in (torch.bfloat16, torch.float16, torch.float32):
+        x = rng.normal(0, 1.0, n)
+        x[-1], x[-2] = 2.0 ** 9, -(2.0 ** 9)
+        bits = workloads.bits_numpy(torch.from_numpy(x).to(tdtype))
+    else:
+        bits = workloads.bits_numpy(torch.from_numpy(rng.normal(0, 1.0, n)).to(tdtype))
+        bits[-1] = bits[-2] = 0x70 if tdtype == torch.float8_e4m3fn else 0x74  # 256 (e4m3) / 2^14 (e5m2)
+    check_sampled(bits, tdtype)

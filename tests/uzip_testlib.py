@@ -142,7 +142,7 @@ def coded_frame(sym, ftab, rans_encode):
     buf = np.zeros(total, np.uint8)
     put_to(buf, 0, 0x31505A55, 4)
     put_to(buf, 4, 1, 2)
-    buf[6], buf[7], buf[8], buf[9] = 1, 12, 32, 1
+    buf[6], buf[7], buf[8], buf[9] = 1, 12, 32, 8
     put_to(buf, 12, ce, 4)
     put_to(buf, 16, n, 8)
     put_to(buf, 24, C, 8)
