@@ -46,13 +46,12 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0
 VALUE_DTYPE = {1: "bf16", 2: "fp32", 3: "fp16", 4: "fp8_e4m3fn", 5: "fp8_e5m2"}
 # HBM bytes per launch from two rocprofv3 passes (FETCH_SIZE, then WRITE_SIZE)
-# on the gradient bucket, reads scaled by 2.000 and writes by 1.000 (what the
-# same counters read for the benchmark's plain 512 MiB device copy); the
-# kernel source they were taken on is identified by its digest, and the
-# figure is reported only while the source is unchanged.
-MEASURED_TRAFFIC_SOURCE = "bb05f26b276d"
-MEASURED_TRAFFIC = {("grad_bucket", "k_encode"): 1435844379, ("grad_bucket", "k_decode"): 897023694,
-                    ("grad_bucket:sampled", "k_encode"): 963629482, ("grad_bucket:sampled", "k_decode"): 897766720}
+# on the Llama-3-8B-shaped weight set, reads scaled by 2.000 and writes by
+# 1.000 (what the same counters read for the benchmark's plain 16.06 GB device
+# copy); the kernel source they were taken on is identified by its digest, and
+# the figure is reported only while the source is unchanged.
+MEASURED_TRAFFIC_SOURCE = "038fa82561e2"
+MEASURED_TRAFFIC = {("llama8b", "k_encode"): 42801604038, ("llama8b", "k_decode"): 26853043297}
 
 
 def kernel_source_digest() -> str:
