@@ -441,6 +441,64 @@ __device__ inline uint32_t packed_dword(uint32_t k, uint32_t n, uint32_t w, F f)
     return acc;
 }
 
+// Whole groups of 32 values of the bit-packed types: 32 fields of W bits,
+// packed LSB-first, fill exactly W dwords, so a group's fields start on a
+// dword boundary wherever the packing starts on one.  pack32 packs f into o;
+// field32 is field i of such a group (i a compile-time constant in the
+// unrolled loops below).
+template <uint32_t W>
+__device__ inline void pack32(const uint32_t (&f)[32], uint32_t (&o)[W]) {
+#pragma unroll
+    for (uint32_t d = 0; d < W; ++d) o[d] = 0;
+#pragma unroll
+    for (uint32_t i = 0; i < 32; ++i) {
+        const uint32_t b = i * W, d = b >> 5, sh = b & 31u;
+        o[d] |= f[i] << sh;
+        if (sh + W > 32) o[d + 1] |= f[i] >> (32 - sh);
+    }
+}
+template <uint32_t W>
+__device__ inline uint32_t field32(const uint32_t (&o)[W], uint32_t i) {
+    const uint32_t b = i * W, d = b >> 5, sh = b & 31u;
+    const uint32_t v = sh + W > 32 ? __builtin_amdgcn_alignbit(o[d + 1], o[d], sh) : o[d] >> sh;
+    return v & ((1u << W) - 1u);
+}
+// W consecutive dwords at a dword-aligned offset of r, in 128-bit pieces and
+// one 96-, 64- or 32-bit remainder (out of range: loads read zero, stores are
+// dropped, dword by dword)
+template <uint32_t W>
+__device__ inline void load_dwords(rsrc_t r, uint32_t off, uint32_t (&o)[W]) {
+#pragma unroll
+    for (uint32_t d = 0; d + 4 <= W; d += 4) {
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)(off + 4 * d), 0, 0);
+        o[d] = v.x; o[d + 1] = v.y; o[d + 2] = v.z; o[d + 3] = v.w;
+    }
+    constexpr uint32_t d = W & ~3u;
+    if constexpr (W - d == 3) {
+        const u32x3 v = __builtin_amdgcn_raw_buffer_load_b96(r, (int)(off + 4 * d), 0, 0);
+        o[d] = v.x; o[d + 1] = v.y; o[d + 2] = v.z;
+    } else if constexpr (W - d == 2) {
+        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)(off + 4 * d), 0, 0);
+        o[d] = v.x; o[d + 1] = v.y;
+    } else if constexpr (W - d == 1) {
+        o[d] = __builtin_amdgcn_raw_buffer_load_b32(r, (int)(off + 4 * d), 0, 0);
+    }
+}
+template <uint32_t W>
+__device__ inline void store_dwords(rsrc_t r, uint32_t off, const uint32_t (&o)[W]) {
+#pragma unroll
+    for (uint32_t d = 0; d + 4 <= W; d += 4)
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4{o[d], o[d + 1], o[d + 2], o[d + 3]}, r, (int)(off + 4 * d), 0, 0);
+    constexpr uint32_t d = W & ~3u;
+    if constexpr (W - d == 3) {
+        __builtin_amdgcn_raw_buffer_store_b96(u32x3{o[d], o[d + 1], o[d + 2]}, r, (int)(off + 4 * d), 0, 0);
+    } else if constexpr (W - d == 2) {
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2{o[d], o[d + 1]}, r, (int)(off + 4 * d), 0, 0);
+    } else if constexpr (W - d == 1) {
+        __builtin_amdgcn_raw_buffer_store_b32(o[d], r, (int)(off + 4 * d), 0, 0);
+    }
+}
+
 // Body of a RAW record: bytes [16, size) get the symbols of the chunk's ni
 // values (at byte in0 of the input resource), packed at SB bits (bytes for
 // bf16 and fp32), then zeros.  Whole wave, wave-uniform arguments; bf16 and
@@ -1353,17 +1411,37 @@ __global__ __launch_bounds__(256) void k_raw_frame(EncParams p) {
         const uint32_t rbytes = (uint32_t)raw_record_bytes(ni, Fmt<DT>::SB);
         const rsrc_t rrec = make_rsrc(out + exp_off + off, rbytes);
         if constexpr (R == 0) {
-            // fp16 and fp8: the chunk's raw fields and its symbols, each packed
-            // (a dword per thread, built from the values it covers); the raw
-            // region's last dword may reach into the zero gap after it
+            // fp16 and fp8: the chunk's raw fields and its symbols, each packed.
+            // A thread takes whole groups of 32 values (8 EB dwords in, RB raw
+            // and SB symbol dwords out, all aligned); the dwords of the
+            // chunk's ragged last group and the record's padding after the
+            // groups are built one dword per thread from the values they
+            // cover.  The raw region's last dword may reach into the zero gap
+            // after it.
             constexpr uint32_t RB = Fmt<DT>::RB, SB = Fmt<DT>::SB;
             uint8_t *rawp = out + sm_off + c * ce * RB / 8;
             const uint32_t nd_raw = (uint32_t)((packed_bytes(ni, RB) + 3) / 4);
-            for (uint32_t k = t; k < nd_raw; k += 256)
+            const rsrc_t rraw = make_rsrc(rawp, 4 * nd_raw);
+            const uint32_t ng = ni / 32;
+            for (uint32_t g = t; g < ng; g += 256) {
+                uint32_t w[8 * EB], fr[32], fs[32], orw[RB], osy[SB];
+                load_dwords<8 * EB>(rin, 32 * EB * g, w);
+#pragma unroll
+                for (uint32_t i = 0; i < 32; ++i) {
+                    const uint32_t v = (w[i * EB / 4] >> (8 * EB * (i % (4 / EB)))) & ((1u << (8 * EB)) - 1u);
+                    fr[i] = raw_of<DT>(v);
+                    fs[i] = exponent_of<DT>(v);
+                }
+                pack32<RB>(fr, orw);
+                pack32<SB>(fs, osy);
+                store_dwords<RB>(rraw, 4 * RB * g, orw);
+                store_dwords<SB>(rrec, kRecHeaderBytes + 4 * SB * g, osy);
+            }
+            for (uint32_t k = RB * ng + t; k < nd_raw; k += 256)
                 gstore<uint32_t>(rawp + 4 * k, packed_dword(k, ni, RB, [&](uint32_t i) {
                     return raw_of<DT>(bld_value<DT>(rin, i * EB));
                 }));
-            for (uint32_t k = t; k < (rbytes - kRecHeaderBytes) / 4; k += 256)
+            for (uint32_t k = SB * ng + t; k < (rbytes - kRecHeaderBytes) / 4; k += 256)
                 gstore<uint32_t>(out + exp_off + off + kRecHeaderBytes + 4 * k, packed_dword(k, ni, SB, [&](uint32_t i) {
                     return exponent_of<DT>(bld_value<DT>(rin, i * EB));
                 }));
@@ -2234,9 +2312,23 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
         // ---- chunks stored RAW: exponent bytes straight from the record ----
         if (R == 0 && raw_run) {
             // fp16, fp8: the chunk's symbols (packed at SB bits after the record
-            // header) and raw fields (packed at RB bits), value by value
+            // header) and raw fields (packed at RB bits).  A lane takes whole
+            // groups of 32 values (SB and RB aligned dwords in, 8 EB dwords of
+            // values out); the ragged last group value by value.
             const uint32_t ob = (h ? vals0 : 0u) * EB, eo = rel + kRecHeaderBytes, vb = (h ? vals0 : 0u) * RB;
-            for (uint32_t i = lj; i < ni; i += 32) {
+            const uint32_t ng = ni / 32;
+            for (uint32_t g = lj; g < ng; g += 32) {
+                uint32_t sy[SB], rw[RB], w[8 * EB];
+                load_dwords<SB>(rrec, eo + 4 * SB * g, sy);
+                load_dwords<RB>(rsm, vb / 8 + 4 * RB * g, rw);
+#pragma unroll
+                for (uint32_t k = 0; k < 8 * EB; ++k) w[k] = 0;
+#pragma unroll
+                for (uint32_t i = 0; i < 32; ++i)
+                    w[i * EB / 4] |= join_value<DT>(field32<SB>(sy, i), field32<RB>(rw, i)) << (8 * EB * (i % (4 / EB)));
+                store_dwords<8 * EB>(rout, ob + 32 * EB * g, w);
+            }
+            for (uint32_t i = 32 * ng + lj; i < ni; i += 32) {
                 const uint32_t sym = packed_field(rrec, eo, i * SB, SB);
                 bst_value<DT>(rout, ob + i * EB, join_value<DT>(sym, raw_field<DT>(rsm, vb + i * RB)));
             }

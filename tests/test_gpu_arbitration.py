@@ -83,9 +83,13 @@ def test_plan_and_frame_match_the_oracle(tdtype, link):
         assert plan["decision"] == uz.UZIP_PLAN_RAW
 
 
-@pytest.mark.parametrize("tdtype", [torch.bfloat16, torch.float32, torch.float8_e4m3fn])
-def test_raw_plan_writes_every_record_raw(tdtype):
-    bits = _workload(tdtype, 250_000, seed=4)
+@pytest.mark.parametrize("tdtype", [torch.bfloat16, torch.float32, torch.float16, torch.float8_e4m3fn,
+                                    torch.float8_e5m2])
+@pytest.mark.parametrize("n", [250_000, 100_003, 45])
+def test_raw_plan_writes_every_record_raw(tdtype, n):
+    # (the narrow types' RAW frames pack whole groups of 32 values and the
+    # ragged last group separately: sizes with and without such a group)
+    bits = _workload(tdtype, n, seed=4)
     plan, got = check_arbitrated(bits, tdtype, link_bytes_per_us=10**9)
     assert plan["decision"] == uz.UZIP_PLAN_RAW
     _, _, recs = parse_buffer(got)

@@ -59,9 +59,12 @@ def test_every_fp8_bit_pattern(fmt):
 
 
 @pytest.mark.parametrize("tdtype", [torch.float16] + FP8)
-def test_random_bits_go_raw(tdtype):
+@pytest.mark.parametrize("n", [200_000, 200_003, 70_001, 47])
+def test_random_bits_go_raw(tdtype, n):
+    # RAW records rebuilt by whole groups of 32 values, the ragged last group
+    # value by value (sizes with and without one)
     dt = np.uint16 if tdtype == torch.float16 else np.uint8
-    bits = np.random.default_rng(5).integers(0, np.iinfo(dt).max + 1, 200_000).astype(dt)
+    bits = np.random.default_rng(5).integers(0, np.iinfo(dt).max + 1, n).astype(dt)
     got = check_parity(bits, tdtype=tdtype)
     _, _, recs = parse_buffer(got)
     assert all(r["mode"] == 1 for r in recs)
