@@ -933,8 +933,9 @@ __global__ __launch_bounds__(64) void k_encode(EncParams p) {
         const uint32_t fe = esc ? 1u : f[k], ce0 = esc ? kEscSlot : cbase + cpre[k];
         const double r = fe ? enc_reciprocal(fe) : 0.0;
         const uint64_t rb = (uint64_t)__double_as_longlong(r);
-        // (f - 1) | (4096 - f) << 16: the emission threshold and the multiplier of the coding step
-        tab[lj * 8 + k] = make_uint4(((fe - 1) & 0xFFFFu) | ((kTableSize - fe) << 16), ce0, (uint32_t)rb,
+        // (16 f - 1) | (4096 - f) << 16: the emission threshold (x >= f * 2^20
+        // exactly when x >> 16 > 16 f - 1) and the multiplier of the coding step
+        tab[lj * 8 + k] = make_uint4((((fe << 4) - 1) & 0xFFFFu) | ((kTableSize - fe) << 16), ce0, (uint32_t)rb,
                                      (uint32_t)(rb >> 32));
     }
 
@@ -1007,7 +1008,7 @@ __global__ __launch_bounds__(64) void k_encode(EncParams p) {
         uint32_t ex = ex_in;  // the value's exponent
         if (!have_ex) asm("v_bfe_u32 %0, %1, %2, %3" : "=v"(ex) : "v"(v), "i"(Fmt<DT>::SYM), "i"(Fmt<DT>::SB));
         const uint4 te = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint8_t *>(tab) + (ex << 4));
-        uint64_t m = lanes_lt(te.x & 0xFFFFu, x >> 20) & act;  // x >= f * 2^20
+        uint64_t m = lanes_lt(te.x & 0xFFFFu, x >> 16) & act;  // x >= f * 2^20
         uint32_t lo = (uint32_t)m, hi = (uint32_t)(m >> 32);
         uint32_t clo = __builtin_popcount(lo), chi = __builtin_popcount(hi);
         uint64_t escm = 0;
