@@ -2264,19 +2264,33 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
         } else if constexpr (R == 0) {
             // fp16, fp8: each lane's raw field by one dword load, eight steps
             // ahead (step t's fields of a half are 4 RB bytes further than
-            // step t - 1's); one store of EB bytes per step (packing fp8 steps
-            // into dwords through bpermute rounds measured slower)
+            // step t - 1's).  fp16 leaves two steps per dword store, packed as
+            // in the bf16 loop above; fp8 stores its byte per step (packing
+            // four fp8 steps into a dword through bpermute rounds measured
+            // slower)
             constexpr int kAhead = 8;
             const uint32_t lanebyte = lanebit >> 3, lanesh = lanebit & 7u;
+            const uint32_t pk_src = ((2 * (lj & 15u)) + 32 * h) << 2;
+            const uint32_t pk_sel = lj < 16 ? 0x05040100u : 0x07060302u;
+            const uint32_t out_pair = rans_run ? (h ? vals0 : 0u) * EB + 4 * lj : kOutOfRange;
             uint32_t rq[kAhead];
 #pragma unroll
             for (int u = 0; u < kAhead; ++u) rq[u] = bld32(rsm, lanebyte + u * 4 * RB);
             for (; t < Tmain; t += kAhead) {
+                uint32_t vprev = 0;
 #pragma unroll
                 for (int u = 0; u < kAhead; ++u) {
                     const uint32_t sp = (rq[u] >> lanesh) & ((1u << RB) - 1u);
                     rq[u] = bld32(rsm, lanebyte + (t + u + kAhead) * 4 * RB);
-                    step(t + u, runm, false, sp, u & 3, true);
+                    const uint32_t v = step(t + u, runm, false, sp, u & 3, EB != 2);
+                    if (EB == 2 && (u & 1)) {
+                        const uint32_t q = __builtin_amdgcn_perm(v, vprev, 0x05040100u);
+                        const uint32_t qa = (uint32_t)__builtin_amdgcn_ds_bpermute((int)pk_src, (int)q);
+                        const uint32_t qb = (uint32_t)__builtin_amdgcn_ds_bpermute((int)(pk_src + 4), (int)q);
+                        bst32(rout, out_pair + (t + u - 1) * 64, __builtin_amdgcn_perm(qb, qa, pk_sel));
+                    } else {
+                        vprev = v;
+                    }
                 }
             }
         } else {
