@@ -90,3 +90,28 @@ def test_fp32_buffer_over_4gib():
     assert total < 0.9 * 4 * N_FP32
     del t
     torch.cuda.empty_cache()
+
+
+def test_batched_call_with_a_buffer_over_4gib():
+    """The same buffer between two small ones in one batched call: every frame
+    equals its single-buffer frame (itself checked above against the oracle
+    around byte 2^32), and the batch decodes bit for bit."""
+    big = workloads.gradient_bucket(N_BF16, device=DEV, seed=21)
+    small = [workloads.gradient_bucket(n, device=DEV, seed=s) for n, s in ((40_000, 24), (1, 25))]
+    ts = [small[0], big, small[1]]
+    bufs, sizes = uz.compress_batched(ts)
+    torch.cuda.synchronize()
+    sz = sizes.cpu().tolist()
+    for t, b, s in zip(ts, bufs, sz):
+        one, one_size = uz.compress(t)
+        torch.cuda.synchronize()
+        assert int(one_size.item()) == s
+        assert torch.equal(one[:s], b[:s])
+        del one
+    outs, status = uz.decompress_batched([b[:s] for b, s in zip(bufs, sz)], torch.bfloat16, [t.numel() for t in ts])
+    torch.cuda.synchronize()
+    assert status.cpu().tolist() == [0, 0, 0]
+    for t, o in zip(ts, outs):
+        assert torch.equal(t.view(torch.int16), o.view(torch.int16))
+    del big, bufs, outs
+    torch.cuda.empty_cache()
