@@ -41,10 +41,10 @@
  * whose size the *_workspace_size functions give.  Host arrays need only live
  * for the duration of the call: a batched call over more than one buffer
  * copies its per-buffer descriptors through a small pinned host staging area
- * that the library keeps per calling thread and device (allocated on that
- * thread's first such call, grown when a call needs more, kept until the
- * process ends), so the call never waits for work already queued on the
- * stream.  Calls enqueue work on `stream` and return without synchronising
+ * that the library keeps per calling thread and device (eight buffers of at
+ * least 64 KiB, allocated on that thread's first such call, grown when a call
+ * needs more, and kept until the process ends, also after the thread exits),
+ * so the call never waits for work already queued on the stream.  Calls enqueue work on `stream` and return without synchronising
  * it; results (d_out_size, d_status, output bytes) are valid once the
  * stream's work has completed.  Calls on different streams are independent
  * when their workspaces differ.  The library keeps no other state between
