@@ -53,7 +53,11 @@
  * Errors.  Argument errors are found on the host and returned at once, with
  * nothing launched: UZIP_ERR_INVALID_ARGUMENT (bad dtype, null or misaligned
  * pointer, chunk_bytes not a multiple of 32 values or above 2^20 values,
- * workspace too small), UZIP_ERR_CAPACITY (output capacity below
+ * workspace too small, or a compress call beyond its limits: a buffer of 2^44
+ * values or more, more than 33,554,424 (2^25 - 8) chunk pairs in one call,
+ * which keeps every launch grid within one grid dimension (at the default
+ * chunk sizes about 2.2 * 10^12 values), or an arbitrated batched call of
+ * more than 2^24 - 1 buffers), UZIP_ERR_CAPACITY (output capacity below
  * uzip_max_compressed_size).  Corrupt compressed input is found on the device
  * and reported per buffer in d_status (0 = valid, else
  * UZIP_ERR_CORRUPT_INPUT); the library never falls back to copying bytes it
@@ -98,7 +102,8 @@ typedef enum {
  * a chunk is coded only when that is strictly smaller, and a frame holding a
  * longer coded record is rejected as corrupt.  chunk_bytes is the
  * uncompressed chunk size (0 = default: 256 KiB for fp32, 64 KiB for the
- * others).  Pure host function; returns 0 for an invalid dtype or chunk size. */
+ * others).  Pure host function; returns 0 for an invalid dtype or chunk size,
+ * or a count beyond the compress limits above. */
 size_t uzip_max_compressed_size(uzip_dtype dtype, size_t num_elements, size_t chunk_bytes);
 
 /* Workspace bytes that uzip_compress or uzip_decompress needs for one buffer

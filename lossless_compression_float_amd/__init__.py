@@ -298,7 +298,7 @@ def compress(t: torch.Tensor, chunk_bytes: int = 0, out: torch.Tensor | None = N
     n = t.numel()
     cap = uzip_max_compressed_size(code, n, chunk_bytes)
     if cap == 0:
-        raise ValueError("invalid chunk_bytes %d" % chunk_bytes)
+        raise ValueError("invalid chunk_bytes %d, or %d values beyond the limits of one call" % (chunk_bytes, n))
     if out is None:
         out = torch.empty(cap, dtype=torch.uint8, device=t.device)
     if out_size is None:
@@ -398,7 +398,7 @@ def compress_arbitrated(t: torch.Tensor, pol: uzip_policy, chunk_bytes: int = 0,
     n = t.numel()
     cap = uzip_max_compressed_size(code, n, chunk_bytes)
     if cap == 0:
-        raise ValueError("invalid chunk_bytes %d" % chunk_bytes)
+        raise ValueError("invalid chunk_bytes %d, or %d values beyond the limits of one call" % (chunk_bytes, n))
     if out is None:
         out = torch.empty(cap, dtype=torch.uint8, device=t.device)
     if out_size is None:

@@ -39,6 +39,21 @@ uint64_t chunk_elems_of(uzip_dtype dtype, size_t chunk_bytes) {
     return (ce == 0 || ce > kMaxChunkElems) ? 0 : ce;
 }
 
+// Limits of one compress call, checked on the host before any size is
+// computed or anything launched: a buffer holds fewer than 2^44 values (so
+// that every byte count below is exact in 64 bits), and a call has at most
+// kMaxPairs chunk pairs, so that each launch grid (k_compact's: 1024 threads
+// per kCompactPairs = 8 pairs) stays within the 2^32 - 1 work-items of one
+// grid dimension.  The arbitrated batched calls also launch a 256-thread
+// workgroup per buffer, hence kMaxPlanBuffers.
+constexpr uint64_t kMaxElems = 1ull << 44;
+constexpr uint64_t kMaxPairs = (1ull << 25) - 8;
+constexpr uint64_t kMaxPlanBuffers = (1ull << 24) - 1;
+
+uint64_t pairs_of(uint64_t n, uint64_t ce) { return ((n + ce - 1) / ce + 1) / 2; }
+
+bool count_ok(uint64_t n, uint64_t ce) { return n < kMaxElems && pairs_of(n, ce) <= kMaxPairs; }
+
 struct EncWs {
     uint64_t descs, sizes, flags, ticket, slots, slot_stride, bytes;
 };
@@ -224,7 +239,7 @@ uzip_status compress_single(uzip_dtype dtype, const void *d_in, size_t num_eleme
                             uzip_plan *d_plan, void *d_workspace, size_t workspace_bytes, hipStream_t stream,
                             bool sampled = false) {
     const uint64_t ce = chunk_elems_of(dtype, chunk_bytes);
-    if (!ce) return UZIP_ERR_INVALID_ARGUMENT;
+    if (!ce || !count_ok(num_elements, ce)) return UZIP_ERR_INVALID_ARGUMENT;
     if (num_elements > 0 && (d_in == nullptr || !aligned(d_in, 16))) return UZIP_ERR_INVALID_ARGUMENT;
     if (d_out == nullptr || !aligned(d_out, 16) || d_out_size == nullptr || !aligned(d_out_size, 8))
         return UZIP_ERR_INVALID_ARGUMENT;
@@ -244,15 +259,18 @@ uzip_status compress_batched(uzip_dtype dtype, size_t num_buffers, const void *c
                              bool sampled = false, const ProfileEvents *ev = nullptr) {
     const uint64_t ce = chunk_elems_of(dtype, chunk_bytes);
     if (!ce || num_buffers == 0 || num_buffers > 0xFFFFFFFFull) return UZIP_ERR_INVALID_ARGUMENT;
+    if (policy != nullptr && num_buffers > kMaxPlanBuffers) return UZIP_ERR_INVALID_ARGUMENT;
     if (!h_in || !h_num_elements || !h_out || !h_out_capacity || !d_out_sizes || !aligned(d_out_sizes, 8))
         return UZIP_ERR_INVALID_ARGUMENT;
     // (kept per thread across calls: no heap allocation once it has grown)
     thread_local std::vector<EncDesc> descs;
     if (descs.size() < num_buffers) descs.resize(num_buffers);
-    uint64_t chunks = 0;
+    uint64_t chunks = 0, pairs = 0;
     for (size_t b = 0; b < num_buffers; ++b) {
         const uint64_t n = h_num_elements[b];
-        if (policy != nullptr && n >= (1ull << 44)) return UZIP_ERR_INVALID_ARGUMENT;
+        if (n >= kMaxElems) return UZIP_ERR_INVALID_ARGUMENT;
+        pairs += pairs_of(n, ce);
+        if (pairs > kMaxPairs) return UZIP_ERR_INVALID_ARGUMENT;
         if (n > 0 && (h_in[b] == nullptr || !aligned(h_in[b], 16))) return UZIP_ERR_INVALID_ARGUMENT;
         if (h_out[b] == nullptr || !aligned(h_out[b], 16)) return UZIP_ERR_INVALID_ARGUMENT;
         if (h_out_capacity[b] < max_size(dtype, n, ce)) return UZIP_ERR_CAPACITY;
@@ -306,12 +324,12 @@ extern "C" {
 
 size_t uzip_max_compressed_size(uzip_dtype dtype, size_t num_elements, size_t chunk_bytes) {
     const uint64_t ce = chunk_elems_of(dtype, chunk_bytes);
-    return ce ? (size_t)max_size(dtype, num_elements, ce) : 0;
+    return ce && count_ok(num_elements, ce) ? (size_t)max_size(dtype, num_elements, ce) : 0;
 }
 
 size_t uzip_workspace_size(uzip_dtype dtype, size_t num_elements, size_t chunk_bytes) {
     const uint64_t ce = chunk_elems_of(dtype, chunk_bytes);
-    if (!ce) return 0;
+    if (!ce || !count_ok(num_elements, ce)) return 0;
     const uint64_t chunks = (num_elements + ce - 1) / ce;
     return (size_t)std::max(enc_ws(dtype, 1, chunks, ce).bytes, dec_ws(1).bytes);
 }
@@ -320,8 +338,13 @@ size_t uzip_workspace_size_batched(uzip_dtype dtype, size_t num_buffers, const s
                                    size_t chunk_bytes) {
     const uint64_t ce = chunk_elems_of(dtype, chunk_bytes);
     if (!ce || num_buffers == 0 || num_buffers > 0xFFFFFFFFull || h_num_elements == nullptr) return 0;
-    uint64_t chunks = 0;
-    for (size_t b = 0; b < num_buffers; ++b) chunks += (h_num_elements[b] + ce - 1) / ce;
+    uint64_t chunks = 0, pairs = 0;
+    for (size_t b = 0; b < num_buffers; ++b) {
+        if (h_num_elements[b] >= kMaxElems) return 0;
+        chunks += (h_num_elements[b] + ce - 1) / ce;
+        pairs += pairs_of(h_num_elements[b], ce);
+        if (pairs > kMaxPairs) return 0;
+    }
     return (size_t)std::max(enc_ws(dtype, num_buffers, chunks, ce).bytes, dec_ws(num_buffers).bytes);
 }
 
@@ -335,7 +358,7 @@ uzip_status uzip_compress(uzip_dtype dtype, const void *d_in, size_t num_element
 uzip_status uzip_compress_noalloc(uzip_dtype dtype, const void *d_in, size_t num_elements, size_t chunk_bytes,
                                   void *d_out, size_t out_capacity, uint64_t *d_out_size, hipStream_t stream) {
     const uint64_t ce = chunk_elems_of(dtype, chunk_bytes);
-    if (!ce) return UZIP_ERR_INVALID_ARGUMENT;
+    if (!ce || !count_ok(num_elements, ce)) return UZIP_ERR_INVALID_ARGUMENT;
     const uint64_t chunks = (num_elements + ce - 1) / ce;
     if (enc_ws(dtype, 1, chunks, ce).bytes > UZIP_NOALLOC_SCRATCH_BYTES) return UZIP_ERR_SCRATCH_LIMIT;
     void *ws = nullptr;

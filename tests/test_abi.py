@@ -112,6 +112,58 @@ def test_batched_argument_errors_return_synchronously(fn):
     assert call(d_out_sizes=FAKE + 4) == uz.UZIP_ERR_INVALID_ARGUMENT
 
 
+PAIR_LIMIT = (1 << 25) - 8  # chunk pairs of one compress call (k_compact's grid: 1024 threads per 8 pairs)
+
+
+def test_counts_beyond_the_call_limits_are_rejected_on_the_host():
+    """A buffer of 2^44 values or more, or more chunk pairs in one call than
+    the launch grids can cover, is an argument error: the size functions
+    return 0 and the compress calls return at once, also for counts whose
+    byte sizes would not fit 64 bits (a size computed with wrap-around could
+    otherwise pass the capacity and workspace checks)."""
+    bf, ce = uz.UZIP_BF16, 32768
+    n_max = 2 * ce * PAIR_LIMIT  # the largest bf16 buffer at the default chunk
+    assert uz.uzip_max_compressed_size(bf, n_max, 0) == orc.max_compressed_size(bf, n_max, 0)
+    assert uz.uzip_workspace_size(bf, n_max, 0) > 0
+    assert uz.uzip_max_compressed_size(bf, n_max + 1, 0) == 0 and uz.uzip_workspace_size(bf, n_max + 1, 0) == 0
+    # at 2^20-value chunks the value limit comes first
+    assert uz.uzip_max_compressed_size(bf, (1 << 44) - 1, 1 << 21) > 0
+    for n in [1 << 44, 1 << 63, (1 << 64) - 1]:
+        for dt in [bf, uz.UZIP_FP32, uz.UZIP_FP8_E4M3]:
+            assert uz.uzip_max_compressed_size(dt, n, 0) == 0 and uz.uzip_workspace_size(dt, n, 0) == 0
+    assert uz.uzip_workspace_size_batched(bf, [2 * ce * (PAIR_LIMIT - 1), 2 * ce], 0) > 0
+    assert uz.uzip_workspace_size_batched(bf, [2 * ce * (PAIR_LIMIT - 1), 2 * ce + 1], 0) == 0
+    assert uz.uzip_workspace_size_batched(bf, [100, 1 << 44], 0) == 0
+    huge = (1 << 64) - 1
+    for n in [n_max + 1, 1 << 44, 1 << 63, huge]:
+        for fn in (uz.uzip_compress, uz.uzip_compress_sampled):
+            assert fn(bf, FAKE, n, 0, FAKE, huge, FAKE, FAKE, huge, None) == uz.UZIP_ERR_INVALID_ARGUMENT, (fn, n)
+        # (returned before the scratch's device address is looked up)
+        assert uz.uzip_compress_noalloc(bf, FAKE, n, 0, FAKE, huge, FAKE, None) == uz.UZIP_ERR_INVALID_ARGUMENT
+        assert uz.uzip_compress_arbitrated(bf, FAKE, n, 0, _policy(), FAKE, huge, FAKE, FAKE, FAKE, huge,
+                                           None) == uz.UZIP_ERR_INVALID_ARGUMENT
+    for ns in ([100, 1 << 44], [2 * ce * (PAIR_LIMIT - 1), 2 * ce + 1], [huge, 5]):
+        kw = dict(h_in=[FAKE] * len(ns), h_num_elements=ns, chunk_bytes=0, h_out=[FAKE] * len(ns),
+                  h_out_capacity=[huge] * len(ns), d_out_sizes=FAKE, d_workspace=FAKE, workspace_bytes=huge,
+                  stream=None)
+        assert uz.uzip_compress_batched(bf, **kw) == uz.UZIP_ERR_INVALID_ARGUMENT, ns
+        assert uz.uzip_compress_batched_sampled(bf, **kw) == uz.UZIP_ERR_INVALID_ARGUMENT, ns
+        assert uz.uzip_compress_batched_arbitrated(bf, policy=_policy(), d_plans=FAKE,
+                                                   **kw) == uz.UZIP_ERR_INVALID_ARGUMENT, ns
+
+
+def test_arbitrated_batch_of_too_many_buffers_is_rejected_before_its_arrays_are_read():
+    """k_plan runs a 256-thread workgroup per buffer: an arbitrated batched call
+    takes at most 2^24 - 1 buffers.  The count is checked before the host
+    arrays (here one entry long) are read."""
+    import ctypes
+    one = uz._sizes([100])
+    pol = _policy()
+    st = uz.lib().uzip_compress_batched_arbitrated(uz.UZIP_BF16, 1 << 24, one.ptr, one.ptr, 0, ctypes.byref(pol),
+                                                   one.ptr, one.ptr, FAKE, FAKE, FAKE, 1 << 40, None)
+    assert st == uz.UZIP_ERR_INVALID_ARGUMENT
+
+
 def test_status_strings():
     for s in range(6):
         assert uz.uzip_status_string(s)
