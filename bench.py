@@ -46,12 +46,18 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0
 VALUE_DTYPE = {1: "bf16", 2: "fp32", 3: "fp16", 4: "fp8_e4m3fn", 5: "fp8_e5m2"}
 # HBM bytes per launch from two rocprofv3 passes (FETCH_SIZE, then WRITE_SIZE)
-# on the Llama-3-8B-shaped weight set, reads scaled by 2.000 and writes by
-# 1.000 (what the same counters read for the benchmark's plain 16.06 GB device
-# copy); the kernel source they were taken on is identified by its digest, and
-# the figure is reported only while the source is unchanged.
+# per workload and table kind (full tables, or ":sampled"), reads scaled by
+# 2.000 and writes by 1.000 (what the same counters read for the benchmark's
+# plain device copy of the workload's size); the kernel source they were taken
+# on is identified by its digest, and a figure is reported only while the
+# source is unchanged.
 MEASURED_TRAFFIC_SOURCE = "66d8b8472a40"
-MEASURED_TRAFFIC = {("llama8b", "k_encode"): 42802712321, ("llama8b", "k_decode"): 26852914156}
+MEASURED_TRAFFIC = {
+    ("llama8b", "k_encode"): 42802712321, ("llama8b", "k_decode"): 26852914156,
+    ("llama8b:sampled", "k_encode"): 28818461550, ("llama8b:sampled", "k_decode"): 26885321688,
+    ("grad_bucket", "k_encode"): 1435831496, ("grad_bucket", "k_decode"): 896992410,
+    ("grad_bucket:sampled", "k_encode"): 963680383, ("grad_bucket:sampled", "k_decode"): 897805749,
+}
 
 
 def kernel_source_digest() -> str:
