@@ -104,8 +104,9 @@ def test_fp16_burst_of_rare_symbols():
 
 
 @pytest.mark.parametrize("tdtype,chunk_bytes", [(torch.float16, 64), (torch.float16, 2048), (torch.float16, 262144),
-                                                (torch.float8_e4m3fn, 64), (torch.float8_e4m3fn, 4096),
-                                                (torch.float8_e4m3fn, 262144), (torch.float8_e5m2, 1 << 20)])
+                                                (torch.float16, 1 << 21), (torch.float8_e4m3fn, 64),
+                                                (torch.float8_e4m3fn, 4096), (torch.float8_e4m3fn, 262144),
+                                                (torch.float8_e4m3fn, 1 << 20), (torch.float8_e5m2, 1 << 20)])
 def test_chunk_sizes(tdtype, chunk_bytes):
     n = 1_200_001
     bits = _fp16(n, seed=9) if tdtype == torch.float16 else _fp8(n, tdtype, seed=9)

@@ -86,6 +86,11 @@ def test_gradient_bucket_with_specials_has_escapes():
     (torch.float16, 150_001, 0),
     (torch.float8_e4m3fn, 200_003, 0),
     (torch.float8_e5m2, 200_003, 0),
+    # the largest chunk (2^20 values: eight runs of 16,384), then a ragged one
+    (torch.bfloat16, 1_200_001, 1 << 21),
+    (torch.float32, 1_100_003, 1 << 22),
+    (torch.float16, 1_100_001, 1 << 21),
+    (torch.float8_e4m3fn, 1_100_001, 1 << 20),
 ])
 def test_dtypes_and_chunk_sizes(tdtype, n, chunk_bytes):
     rng = np.random.default_rng(n)
