@@ -1775,16 +1775,17 @@ __global__ void k_dec_validate(DecParams p) {
 
 // LDS of one decode workgroup (two chunks), 10 KiB:
 //   s_sym [2][4096] u8   slot -> rank of its symbol among the present symbols
-//   s_rk  [2][256]  u32  rank -> (4096 - f) | symbol << 12 | c0 << 20
+//   s_rk  [2][256]  u32  rank -> (4096 - f) | c0 << 12 | symbol << 24
 // so one step costs two dependent LDS reads; fp32 adds s_slot [2][4096] u32
-// (slot -> its rank's entry, 34 KiB in all) and reads once per step.  A workgroup decodes a pair of
-// consecutive chunks of one buffer (half-wave h decodes chunk 2p + h), so the
-// record, sign+mantissa and output regions of the pair each get one buffer
-// resource.  Renormalisation words come from a register window (two 16-bit
-// words per lane: 64 words per half-wave) refilled from a load issued one step
-// earlier, off the state's dependency chain, and are fetched with ds_bpermute
-// after the ballot.  Sign+mantissa bytes are loaded 4 steps ahead.  Chunks
-// stored RAW are copied in a separate loop.
+// (slot -> its rank's entry, 34 KiB in all) and reads once per step.  The
+// symbol sits in the entry's top byte, so that byte permutes can gather the
+// symbols of several steps.  A workgroup decodes a pair of consecutive chunks
+// of one buffer (half-wave h decodes chunk 2p + h), so the record,
+// sign+mantissa and output regions of the pair each get one buffer resource.
+// Renormalisation words come from a register window (two 16-bit words per
+// lane: 64 words per half-wave) refilled from loads issued four steps ahead,
+// off the state's dependency chain, and are fetched with ds_bpermute after the
+// ballot.  Chunks stored RAW are rebuilt in a separate loop.
 template <int DT>
 __device__ inline uint32_t bload_sm(rsrc_t r, uint32_t off) {
     if (Fmt<DT>::R == 0) return 0u;
@@ -1967,17 +1968,17 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
             uint32_t k2 = pre;
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
-                if (fk[k]) s_rk[h][k2++] = (kTableSize - fk[k]) | ((lj * 8 + k) << 12) | ((cbase + cpre[k]) << 20);
+                if (fk[k]) s_rk[h][k2++] = (kTableSize - fk[k]) | ((cbase + cpre[k]) << 12) | ((lj * 8 + k) << 24);
             }
         }
         // the escape symbol: rank nsym, f = 1, slot 4095 (no owner when all 256
         // symbols are sampled: a stream reaching it is corrupt, found below)
-        if (S && coded_ok && lj == 0 && nsym < 256) s_rk[h][nsym] = (kTableSize - 1u) | (kEscSlot << 20);
+        if (S && coded_ok && lj == 0 && nsym < 256) s_rk[h][nsym] = (kTableSize - 1u) | (kEscSlot << 12);
         __syncthreads();
         if (coded_ok) {
             for (uint32_t m = 0; m < nsym + (S && nsym < 256 ? 1u : 0u); ++m) {
                 const uint32_t em = s_rk[h][m];
-                const uint32_t fs = kTableSize - (em & 0xFFFu), c0s = em >> 20;
+                const uint32_t fs = kTableSize - (em & 0xFFFu), c0s = (em >> 12) & 0xFFFu;
                 if (kDirect) {
                     for (uint32_t k = lj; k < fs; k += 32) s_slot[h][c0s + k] = em;
                 } else {
@@ -2094,9 +2095,10 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
                 escbad = escbad || (rans_run && idx < nesc && ((pbe >> (e & 7u)) & 1u));
             }
         }
-        // (called once a step's value v is built; returns it with the escaped
-        // exponent in place for the escaping lanes)
-        auto escape_value = [&](uint64_t escm, uint32_t v, uint32_t sp, bool tail) __attribute__((always_inline)) {
+        // (called once a step's table entry em is read; returns it with the
+        // escaped exponent in place of the symbol, in the top byte, for the
+        // escaping lanes)
+        auto escape_sym = [&](uint64_t escm, uint32_t em, bool tail) __attribute__((always_inline)) {
             const uint32_t elo = __builtin_popcount((uint32_t)escm), ehi = __builtin_popcount((uint32_t)(escm >> 32));
             const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(escm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)escm, 0u));
             const uint32_t idx = escv + below - (h ? elo : 0u);
@@ -2115,30 +2117,27 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
             }
             escbad = escbad || (mine && bad);
             escv += h ? ehi : elo;
-            uint32_t ve;
-            if (DT == 1) {
-                asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(ve) : "s"(0x807Fu), "v"(sp), "v"(e << 7));
-            } else {
-                ve = join_value<DT>(e, sp);
-            }
-            return mine ? ve : v;
+            return mine ? (em & 0x00FFFFFFu) | (e << 24) : em;
         };
         // One step of both half-waves.  act = lanes holding a value this step
         // (TAIL steps only: in the main loop every lane of a running half
         // holds one, and lanes of a half that is not running never reach the
         // output or the checks); par = step mod 4 (selects the refill
-        // register).  With the table entry em = g | sym << 12 | c0 << 20,
+        // register).  With the table entry em = g | c0 << 12 | sym << 24,
         // g = 4096 - f, the decode step f * (x >> 12) + (x & 4095) - c0 is
         // x - (g * (x >> 12) + c0).
-        // sp: the value's sign+mantissa, for bf16 as the byte in bytes 0 and 1
+        // sp: the value's sign+mantissa, for bf16 as the byte in bytes 0 and 1.
+        // bf16 returns the entry (escapes in place) and stores nothing unless
+        // `store` (its main loop builds and stores four steps' values at once);
+        // fp16 and fp8 return the value.
         auto step = [&](uint32_t t, uint64_t act, bool tail, uint32_t sp, int par, bool store) __attribute__((always_inline)) {
             uint32_t slot_addr;  // (x & 4095) | this half's row: the index in s_sym / s_slot
             asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(slot_addr) : "v"(x), "s"(kTableSize - 1), "v"(hsym));
-            // (sampled tables: the lanes at the escape slot; their values are
-            // patched once built, so the rare branch needs no table entry)
+            // (sampled tables: the lanes at the escape slot; their exponent is
+            // patched into the entry in a rare branch)
             const uint64_t escm = S ? lanes_eq(slot_addr, escaddr) & act : 0ull;
             const uint32_t em = kDirect ? s_slotf[slot_addr] : s_rkf[s_symf[slot_addr] | hrk];
-            const uint32_t xd = x - (__umul24(em & 0xFFFu, x >> kProbBits) + (em >> 20));
+            const uint32_t xd = x - (__umul24(em & 0xFFFu, x >> kProbBits) + ((em >> 12) & 0xFFFu));
             // (the and with act also puts the mask in registers written by the
             // scalar unit: inline asm below reads it, and the hardware needs
             // spacing between a vector compare writing scalar registers and a
@@ -2186,32 +2185,32 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
             lim += used_up ? 64u : 0u;
             NX[par] = bld32(rrec, 2 * lim + rbase);
             if (!kScalarStale) NB[par] = bld32(rrec, 2 * lim + rbase + 128);
+            const uint32_t emx = S && __builtin_expect(escm != 0, 0) ? escape_sym(escm, em, tail) : em;
             if (DT == 1) {
                 // sign (bit 7 of sm, copied to bit 15) and mantissa bits 0-6
-                // from sp, exponent (em bits 12-19) to bits 7-14; the store
+                // from sp, exponent (emx bits 24-31) to bits 7-14; the store
                 // keeps the low 16 bits
-                uint32_t v;
-                asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(v) : "s"(0x807Fu), "v"(sp), "v"(em >> 5));
-                if (S && __builtin_expect(escm != 0, 0)) v = escape_value(escm, v, sp, tail);
-                if (store) bst16(rout, out_lane + t * 32 * EB, v);
-                return v;
+                if (store) {
+                    uint32_t v;
+                    asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(v) : "s"(0x807Fu), "v"(sp), "v"(emx >> 17));
+                    bst16(rout, out_lane + t * 32 * EB, v);
+                }
+                return emx;
             } else if constexpr (DT != 2) {
                 // fp16, fp8: sign (the raw field's top bit, copied to the value's
-                // top bit) and mantissa from sp, the exponent (em bits 12-19) to
+                // top bit) and mantissa from sp, the exponent (emx bits 24-31) to
                 // bit SYM; the store keeps the value's EB bytes
                 constexpr uint32_t SYM = Fmt<DT>::SYM, top = 8 * EB - 1;
                 constexpr uint32_t keep = (1u << top) | ((1u << (RB - 1)) - 1u);
                 const uint32_t spx = sp | ((sp >> (RB - 1)) << top);
                 uint32_t v;
-                asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(v) : "s"(keep), "v"(spx), "v"(em >> (12 - SYM)));
-                if (S && __builtin_expect(escm != 0, 0)) v = escape_value(escm, v, sp, tail);
+                asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(v) : "s"(keep), "v"(spx), "v"(emx >> (24 - SYM)));
                 if (store) bst_value<DT>(rout, out_lane + t * 32 * EB, v);
                 return v;
             } else if (DT == 2) {
                 // sign (bit 23 of sm) to bit 31, mantissa bits 0-22, exponent to bits 23-30
-                const uint32_t sx = sp | ((sp & 0x800000u) << 8), ex = em << 11;
-                uint32_t v = (sx & 0x807FFFFFu) | (ex & ~0x807FFFFFu);
-                if (S && __builtin_expect(escm != 0, 0)) v = escape_value(escm, v, sp, tail);
+                const uint32_t sx = sp | ((sp & 0x800000u) << 8), ex = emx >> 1;
+                const uint32_t v = (sx & 0x807FFFFFu) | (ex & ~0x807FFFFFu);
                 bst32(rout, out_lane + t * 32 * EB, v);
                 return 0u;
             }
@@ -2219,47 +2218,56 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
         };
         uint32_t t = 0;
         if (kB16) {
-            // bf16 sign+mantissa bytes: one dword per lane per group of 4
-            // steps (the 128 bytes of the group), two groups ahead; step s of
-            // a group takes byte lj & 3 of lane 8s + lj / 4 of its half with
-            // one bpermute, and one perm copies it into bytes 0 and 1.  Every
-            // byte of a main-loop group lies inside both chunks.
-            const uint32_t smsrc = ((lj >> 2) + 32 * h) << 2;       // bpermute address of step 0 of a group
-            const uint32_t smsel = 0x0C0C0000u | ((lj & 3) * 0x0101u);
-            // Output: the values of two steps (128 bytes of the half's chunk)
-            // leave as one dword per lane: each lane packs its two values,
-            // then lane j takes the pairs of lanes 2j' and 2j' + 1 (j' = j mod
-            // 16) and keeps their first step's values (j < 16) or their
-            // second's: the dword at byte 64t + 4j.  One dword store replaces
-            // two 16-bit stores.
-            const uint32_t pk_src = ((2 * (lj & 15u)) + 32 * h) << 2;
-            const uint32_t pk_sel = lj < 16 ? 0x05040100u : 0x07060302u;
-            const uint32_t out_pair = rans_run ? (h ? vals0 : 0u) * EB + 4 * lj : kOutOfRange;
-            // two register sets alternate (16 steps per loop iteration), so no
-            // loaded register is copied
-            auto group8 = [&](uint32_t t0, uint32_t Da, uint32_t Db) __attribute__((always_inline)) {
-                uint32_t vprev = 0;
+            // bf16, four steps at a time.  A group of four steps holds 128
+            // values of each half, whose sign+mantissa bytes are 128 bytes:
+            // lane j loads dword j of them (two groups ahead), the bytes of
+            // positions 4j .. 4j + 3, that is of step j >> 3, lanes
+            // 4 (j & 7) .. 4 (j & 7) + 3; and lane j stores those four values
+            // as one 64-bit store.  Their exponents reach it in three moves:
+            // each lane packs its four steps' symbols into the bytes of one
+            // dword (entry byte 3 of each step, by v_perm); each quad of lanes
+            // transposes its 4 x 4 bytes (three DPP quad permutes and three
+            // v_perm), after which lane 4m + q holds the symbols of step q for
+            // lanes 4m .. 4m + 3; and one ds_bpermute fetches that dword from
+            // lane 4 (j & 7) + (j >> 3).  The four values are then built
+            // bytewise: low bytes (the exponent's bit 0 under the mantissa),
+            // high bytes (the sign over the exponent's bits 1-7), interleaved.
+            const uint32_t q4 = lj & 3u;
+            // transposition: from the own dword (A) and those of lanes q ^ 1 (B),
+            // q ^ 2 (C), q ^ 3 (D), lane q takes byte q of A, B, C, D in the
+            // order of their lanes; selT picks the two bytes of a pair (A, B) or
+            // (C, D), selW places the pairs
+            const uint32_t selT = q4 == 0 ? 0x0C0C0400u : q4 == 1 ? 0x0C0C0105u : q4 == 2 ? 0x0C0C0602u : 0x0C0C0307u;
+            const uint32_t selW = q4 < 2 ? 0x05040100u : 0x01000504u;
+            const int xsrc = (int)(((4 * (lj & 7u) + (lj >> 3)) | (h << 5)) << 2);
+            const uint32_t out8 = rans_run ? (h ? vals0 : 0u) * EB + 8 * lj : kOutOfRange;
+            auto group4 = [&](uint32_t t0, uint32_t S4) __attribute__((always_inline)) {
+                uint32_t e[4];
 #pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const uint32_t w = (uint32_t)__builtin_amdgcn_ds_bpermute((int)(smsrc + 32 * (u & 3)), (int)(u < 4 ? Da : Db));
-                    const uint32_t v = step(t0 + u, runm, false, __builtin_amdgcn_perm(0u, w, smsel), u & 3, false);
-                    if (u & 1) {
-                        const uint32_t q = __builtin_amdgcn_perm(v, vprev, 0x05040100u);
-                        const uint32_t qa = (uint32_t)__builtin_amdgcn_ds_bpermute((int)pk_src, (int)q);
-                        const uint32_t qb = (uint32_t)__builtin_amdgcn_ds_bpermute((int)(pk_src + 4), (int)q);
-                        bst32(rout, out_pair + (t0 + u - 1) * 64, __builtin_amdgcn_perm(qb, qa, pk_sel));
-                    } else {
-                        vprev = v;
-                    }
-                }
+                for (int u = 0; u < 4; ++u) e[u] = step(t0 + u, runm, false, 0u, u, false);
+                const uint32_t E = __builtin_amdgcn_perm(__builtin_amdgcn_perm(e[3], e[2], 0x0C0C0703u),
+                                                         __builtin_amdgcn_perm(e[1], e[0], 0x0C0C0703u), 0x05040100u);
+                const uint32_t B = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)E, 0xB1, 0xF, 0xF, true);  // quad_perm [1,0,3,2]
+                const uint32_t C = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)E, 0x4E, 0xF, 0xF, true);  // quad_perm [2,3,0,1]
+                const uint32_t D = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)E, 0x1B, 0xF, 0xF, true);  // quad_perm [3,2,1,0]
+                const uint32_t T = __builtin_amdgcn_perm(__builtin_amdgcn_perm(D, C, selT), __builtin_amdgcn_perm(B, E, selT), selW);
+                const uint32_t X = (uint32_t)__builtin_amdgcn_ds_bpermute(xsrc, (int)T);
+                uint32_t lo, hi;
+                asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(lo) : "s"(0x7F7F7F7Fu), "v"(S4), "v"(X << 7));
+                asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(hi) : "s"(0x80808080u), "v"(S4), "v"(X >> 1));
+                __builtin_amdgcn_raw_buffer_store_b64(
+                    u32x2{__builtin_amdgcn_perm(hi, lo, 0x05010400u), __builtin_amdgcn_perm(hi, lo, 0x07030602u)}, rout,
+                    (int)(out8 + t0 * 64), 0, 0);
             };
             uint32_t D0 = D0first, D1 = D1first;
             for (; t < Tmain16; t += 16) {
                 const uint32_t N0 = bld32(rsm, smd0 + (t + 8) * 32), N1 = bld32(rsm, smd0 + (t + 12) * 32);
-                group8(t, D0, D1);
+                group4(t, D0);
+                group4(t + 4, D1);
                 D0 = bld32(rsm, smd0 + (t + 16) * 32);
                 D1 = bld32(rsm, smd0 + (t + 20) * 32);
-                group8(t + 8, N0, N1);
+                group4(t + 8, N0);
+                group4(t + 12, N1);
             }
         } else if constexpr (R == 0) {
             // fp16, fp8: each lane's raw field by one dword load, eight steps
