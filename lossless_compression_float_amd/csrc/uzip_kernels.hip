@@ -2033,11 +2033,22 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
         const uint32_t nesc_w = S ? max(uniform_u32(__shfl((int)nesc, 0, 64)), uniform_u32(__shfl((int)nesc, 32, 64))) : 0u;
         const uint32_t Tmain = S && nesc_w > 256 ? 0u : min(min(F0, F1), Tw) & ~7u;
         const uint32_t Tmain16 = Tmain & ~15u;  // bf16 main loop: 16 steps per iteration
-        // bf16: this lane's sign+mantissa dword of group 0 (see the main loop),
-        // loaded before the word window so that many memory operations lie
-        // between these loads and their first use
-        const uint32_t smd0 = (h ? vals0 : 0u) + 4 * lj;
-        const uint32_t D0first = kB16 ? bld32(rsm, smd0) : 0u, D1first = kB16 ? bld32(rsm, smd0 + 128) : 0u;
+        // bf16 and fp32 (whole raw bytes): the main loop takes four steps at a
+        // time, and lane j the raw bytes of positions 4j .. 4j + 3 of a group
+        // (4 R bytes, see the main loop); groups 0 and 1 are loaded here, before
+        // the word window, so that many memory operations lie between these
+        // loads and their first use
+        constexpr bool kGroups = DT == 1 || DT == 2;
+        using SmGroup = std::conditional_t<DT == 2, u32x3, uint32_t>;
+        const uint32_t smg = ((h ? vals0 : 0u) + 4 * lj) * R;  // the lane's bytes of group 0
+        auto load_group = [&](uint32_t g) __attribute__((always_inline)) {
+            if constexpr (DT == 2) {
+                return __builtin_amdgcn_raw_buffer_load_b96(rsm, (int)(smg + 128 * R * g), 0, 0);
+            } else {
+                return kB16 ? bld32(rsm, smg + 128 * R * g) : 0u;
+            }
+        };
+        const SmGroup G0first = load_group(0), G1first = load_group(1);
         // Refill: at every step, after its own refill decision, each lane loads
         // the pair it takes at its next refill (block end lim, 32 words past
         // it, pair position 2i) into NX[t mod 4]; the load is consumed four
@@ -2127,9 +2138,9 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
         // g = 4096 - f, the decode step f * (x >> 12) + (x & 4095) - c0 is
         // x - (g * (x >> 12) + c0).
         // sp: the value's sign+mantissa, for bf16 as the byte in bytes 0 and 1.
-        // bf16 returns the entry (escapes in place) and stores nothing unless
-        // `store` (its main loop builds and stores four steps' values at once);
-        // fp16 and fp8 return the value.
+        // bf16 and fp32 return the entry (escapes in place) and store nothing
+        // unless `store` (their main loop builds and stores four steps' values
+        // at once); fp16 and fp8 return the value.
         auto step = [&](uint32_t t, uint64_t act, bool tail, uint32_t sp, int par, bool store) __attribute__((always_inline)) {
             uint32_t slot_addr;  // (x & 4095) | this half's row: the index in s_sym / s_slot
             asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(slot_addr) : "v"(x), "s"(kTableSize - 1), "v"(hsym));
@@ -2209,29 +2220,27 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
                 return v;
             } else if (DT == 2) {
                 // sign (bit 23 of sm) to bit 31, mantissa bits 0-22, exponent to bits 23-30
-                const uint32_t sx = sp | ((sp & 0x800000u) << 8), ex = emx >> 1;
-                const uint32_t v = (sx & 0x807FFFFFu) | (ex & ~0x807FFFFFu);
-                bst32(rout, out_lane + t * 32 * EB, v);
-                return 0u;
+                if (store) {
+                    const uint32_t sx = sp | ((sp & 0x800000u) << 8), ex = emx >> 1;
+                    bst32(rout, out_lane + t * 32 * EB, (sx & 0x807FFFFFu) | (ex & ~0x807FFFFFu));
+                }
+                return emx;
             }
             return 0u;
         };
         uint32_t t = 0;
-        if (kB16) {
-            // bf16, four steps at a time.  A group of four steps holds 128
-            // values of each half, whose sign+mantissa bytes are 128 bytes:
-            // lane j loads dword j of them (two groups ahead), the bytes of
-            // positions 4j .. 4j + 3, that is of step j >> 3, lanes
-            // 4 (j & 7) .. 4 (j & 7) + 3; and lane j stores those four values
-            // as one 64-bit store.  Their exponents reach it in three moves:
-            // each lane packs its four steps' symbols into the bytes of one
-            // dword (entry byte 3 of each step, by v_perm); each quad of lanes
-            // transposes its 4 x 4 bytes (three DPP quad permutes and three
-            // v_perm), after which lane 4m + q holds the symbols of step q for
-            // lanes 4m .. 4m + 3; and one ds_bpermute fetches that dword from
-            // lane 4 (j & 7) + (j >> 3).  The four values are then built
-            // bytewise: low bytes (the exponent's bit 0 under the mantissa),
-            // high bytes (the sign over the exponent's bits 1-7), interleaved.
+        if constexpr (kGroups) {
+            // bf16 and fp32, four steps at a time.  A group of four steps holds
+            // 128 values of each half; lane j takes positions 4j .. 4j + 3 of
+            // them, that is step j >> 3 of lanes 4 (j & 7) .. 4 (j & 7) + 3:
+            // their raw bytes (one 32-bit load for bf16, one 96-bit load for
+            // fp32, two groups ahead) and their one 64-bit or 128-bit store.
+            // Their exponents reach it in three moves: each lane packs its four
+            // steps' symbols into the bytes of one dword (entry byte 3 of each
+            // step, by v_perm); each quad of lanes transposes its 4 x 4 bytes
+            // (three DPP quad permutes and three v_perm), after which lane
+            // 4m + q holds the symbols of step q for lanes 4m .. 4m + 3; and one
+            // ds_bpermute fetches that dword from lane 4 (j & 7) + (j >> 3).
             const uint32_t q4 = lj & 3u;
             // transposition: from the own dword (A) and those of lanes q ^ 1 (B),
             // q ^ 2 (C), q ^ 3 (D), lane q takes byte q of A, B, C, D in the
@@ -2240,8 +2249,8 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
             const uint32_t selT = q4 == 0 ? 0x0C0C0400u : q4 == 1 ? 0x0C0C0105u : q4 == 2 ? 0x0C0C0602u : 0x0C0C0307u;
             const uint32_t selW = q4 < 2 ? 0x05040100u : 0x01000504u;
             const int xsrc = (int)(((4 * (lj & 7u) + (lj >> 3)) | (h << 5)) << 2);
-            const uint32_t out8 = rans_run ? (h ? vals0 : 0u) * EB + 8 * lj : kOutOfRange;
-            auto group4 = [&](uint32_t t0, uint32_t S4) __attribute__((always_inline)) {
+            const uint32_t outg = rans_run ? ((h ? vals0 : 0u) + 4 * lj) * EB : kOutOfRange;
+            auto group4 = [&](uint32_t t0, SmGroup S4) __attribute__((always_inline)) {
                 uint32_t e[4];
 #pragma unroll
                 for (int u = 0; u < 4; ++u) e[u] = step(t0 + u, runm, false, 0u, u, false);
@@ -2252,30 +2261,45 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
                 const uint32_t D = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)E, 0x1B, 0xF, 0xF, true);  // quad_perm [3,2,1,0]
                 const uint32_t T = __builtin_amdgcn_perm(__builtin_amdgcn_perm(D, C, selT), __builtin_amdgcn_perm(B, E, selT), selW);
                 const uint32_t X = (uint32_t)__builtin_amdgcn_ds_bpermute(xsrc, (int)T);
-                uint32_t lo, hi;
-                asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(lo) : "s"(0x7F7F7F7Fu), "v"(S4), "v"(X << 7));
-                asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(hi) : "s"(0x80808080u), "v"(S4), "v"(X >> 1));
-                __builtin_amdgcn_raw_buffer_store_b64(
-                    u32x2{__builtin_amdgcn_perm(hi, lo, 0x05010400u), __builtin_amdgcn_perm(hi, lo, 0x07030602u)}, rout,
-                    (int)(out8 + t0 * 64), 0, 0);
+                if constexpr (DT == 1) {
+                    // bytewise: low bytes (the exponent's bit 0 under the mantissa),
+                    // high bytes (the sign over the exponent's bits 1-7), interleaved
+                    uint32_t lo, hi;
+                    asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(lo) : "s"(0x7F7F7F7Fu), "v"(S4), "v"(X << 7));
+                    asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(hi) : "s"(0x80808080u), "v"(S4), "v"(X >> 1));
+                    __builtin_amdgcn_raw_buffer_store_b64(
+                        u32x2{__builtin_amdgcn_perm(hi, lo, 0x05010400u), __builtin_amdgcn_perm(hi, lo, 0x07030602u)},
+                        rout, (int)(outg + t0 * 32 * EB), 0, 0);
+                } else {
+                    // value k's raw field is bytes 3k .. 3k + 2 of the 12; one v_perm
+                    // takes them with the top one twice (the sign lands in bit 31),
+                    // and one v_bfi puts exponent byte k into bits 23-30
+                    uint32_t v0, v1, v2, v3;
+                    asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(v0) : "s"(0x807FFFFFu), "v"(__builtin_amdgcn_perm(S4.y, S4.x, 0x02020100u)), "v"(X << 23));
+                    asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(v1) : "s"(0x807FFFFFu), "v"(__builtin_amdgcn_perm(S4.y, S4.x, 0x05050403u)), "v"(X << 15));
+                    asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(v2) : "s"(0x807FFFFFu), "v"(__builtin_amdgcn_perm(S4.z, S4.y, 0x04040302u)), "v"(X << 7));
+                    asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(v3) : "s"(0x807FFFFFu), "v"(__builtin_amdgcn_perm(S4.z, S4.z, 0x03030201u)), "v"(X >> 1));
+                    __builtin_amdgcn_raw_buffer_store_b128(u32x4{v0, v1, v2, v3}, rout, (int)(outg + t0 * 32 * EB), 0, 0);
+                }
             };
-            uint32_t D0 = D0first, D1 = D1first;
+            SmGroup G0 = G0first, G1 = G1first;
             for (; t < Tmain16; t += 16) {
-                const uint32_t N0 = bld32(rsm, smd0 + (t + 8) * 32), N1 = bld32(rsm, smd0 + (t + 12) * 32);
-                group4(t, D0);
-                group4(t + 4, D1);
-                D0 = bld32(rsm, smd0 + (t + 16) * 32);
-                D1 = bld32(rsm, smd0 + (t + 20) * 32);
+                const SmGroup N0 = load_group(t / 4 + 2), N1 = load_group(t / 4 + 3);
+                group4(t, G0);
+                group4(t + 4, G1);
+                G0 = load_group(t / 4 + 4);
+                G1 = load_group(t / 4 + 5);
                 group4(t + 8, N0);
                 group4(t + 12, N1);
             }
-        } else if constexpr (R == 0) {
+        } else {
             // fp16, fp8: each lane's raw field by one dword load, eight steps
             // ahead (step t's fields of a half are 4 RB bytes further than
-            // step t - 1's).  fp16 leaves two steps per dword store, packed as
-            // in the bf16 loop above; fp8 stores its byte per step (packing
-            // four fp8 steps into a dword through bpermute rounds measured
-            // slower)
+            // step t - 1's).  fp16 leaves two steps per dword store: each lane
+            // packs its two values, two ds_bpermute give lane j the pairs of
+            // lanes 2j' and 2j' + 1 (j' = j mod 16), and one v_perm keeps the
+            // first step's halves (j < 16) or the second's; fp8 stores its byte
+            // per step
             constexpr int kAhead = 8;
             const uint32_t lanebyte = lanebit >> 3, lanesh = lanebit & 7u;
             const uint32_t pk_src = ((2 * (lj & 15u)) + 32 * h) << 2;
@@ -2299,19 +2323,6 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
                     } else {
                         vprev = v;
                     }
-                }
-            }
-        } else {
-            constexpr int kSmAhead = 8;  // sign+mantissa bytes are loaded this many steps ahead
-            uint32_t smq[kSmAhead];
-#pragma unroll
-            for (int u = 0; u < kSmAhead; ++u) smq[u] = bload_sm<DT>(rsm, sm_lane + u * 32 * R);
-            for (; t < Tmain; t += kSmAhead) {
-#pragma unroll
-                for (int u = 0; u < kSmAhead; ++u) {
-                    const uint32_t sp = smq[u];
-                    smq[u] = bload_sm<DT>(rsm, sm_lane + (t + u + kSmAhead) * 32 * R);
-                    step(t + u, runm, false, sp, u & 3, true);
                 }
             }
         }
