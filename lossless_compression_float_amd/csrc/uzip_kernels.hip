@@ -2033,19 +2033,24 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
         const uint32_t nesc_w = S ? max(uniform_u32(__shfl((int)nesc, 0, 64)), uniform_u32(__shfl((int)nesc, 32, 64))) : 0u;
         const uint32_t Tmain = S && nesc_w > 256 ? 0u : min(min(F0, F1), Tw) & ~7u;
         const uint32_t Tmain16 = Tmain & ~15u;  // bf16 main loop: 16 steps per iteration
-        // bf16 and fp32 (whole raw bytes): the main loop takes four steps at a
-        // time, and lane j the raw bytes of positions 4j .. 4j + 3 of a group
-        // (4 R bytes, see the main loop); groups 0 and 1 are loaded here, before
-        // the word window, so that many memory operations lie between these
-        // loads and their first use
-        constexpr bool kGroups = DT == 1 || DT == 2;
+        // bf16, fp32 and fp8: the main loop takes four steps at a time, and
+        // lane j the raw fields of positions 4j .. 4j + 3 of a group (4 R bytes,
+        // or 4 RB bits starting at bit gsh of byte gbyte; see the main loop);
+        // groups 0 and 1 are loaded here, before the word window, so that many
+        // memory operations lie between these loads and their first use
+        constexpr bool kGroups = DT != 3;
         using SmGroup = std::conditional_t<DT == 2, u32x3, uint32_t>;
         const uint32_t smg = ((h ? vals0 : 0u) + 4 * lj) * R;  // the lane's bytes of group 0
+        const uint32_t gbit = ((h ? vals0 : 0u) + 4 * lj) * RB, gbyte = gbit >> 3, gsh = gbit & 7u;
         auto load_group = [&](uint32_t g) __attribute__((always_inline)) {
             if constexpr (DT == 2) {
                 return __builtin_amdgcn_raw_buffer_load_b96(rsm, (int)(smg + 128 * R * g), 0, 0);
+            } else if constexpr (DT == 1) {
+                return bld32(rsm, smg + 128 * R * g);
+            } else if constexpr (kGroups) {
+                return bld32(rsm, gbyte + 16 * RB * g);  // (a group's fields: 128 RB bits)
             } else {
-                return kB16 ? bld32(rsm, smg + 128 * R * g) : 0u;
+                return 0u;
             }
         };
         const SmGroup G0first = load_group(0), G1first = load_group(1);
@@ -2138,9 +2143,9 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
         // g = 4096 - f, the decode step f * (x >> 12) + (x & 4095) - c0 is
         // x - (g * (x >> 12) + c0).
         // sp: the value's sign+mantissa, for bf16 as the byte in bytes 0 and 1.
-        // bf16 and fp32 return the entry (escapes in place) and store nothing
-        // unless `store` (their main loop builds and stores four steps' values
-        // at once); fp16 and fp8 return the value.
+        // bf16, fp32 and fp8 return the entry (escapes in place) and store
+        // nothing unless `store` (their main loop builds and stores four steps'
+        // values at once); fp16 returns the value.
         auto step = [&](uint32_t t, uint64_t act, bool tail, uint32_t sp, int par, bool store) __attribute__((always_inline)) {
             uint32_t slot_addr;  // (x & 4095) | this half's row: the index in s_sym / s_slot
             asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(slot_addr) : "v"(x), "s"(kTableSize - 1), "v"(hsym));
@@ -2210,14 +2215,17 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
             } else if constexpr (DT != 2) {
                 // fp16, fp8: sign (the raw field's top bit, copied to the value's
                 // top bit) and mantissa from sp, the exponent (emx bits 24-31) to
-                // bit SYM; the store keeps the value's EB bytes
+                // bit SYM; the store keeps the value's EB bytes.  fp8 returns the
+                // entry, as bf16 and fp32 do; fp16 returns the value
                 constexpr uint32_t SYM = Fmt<DT>::SYM, top = 8 * EB - 1;
                 constexpr uint32_t keep = (1u << top) | ((1u << (RB - 1)) - 1u);
-                const uint32_t spx = sp | ((sp >> (RB - 1)) << top);
-                uint32_t v;
-                asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(v) : "s"(keep), "v"(spx), "v"(emx >> (24 - SYM)));
-                if (store) bst_value<DT>(rout, out_lane + t * 32 * EB, v);
-                return v;
+                uint32_t v = 0;
+                if (!kGroups || store) {
+                    const uint32_t spx = sp | ((sp >> (RB - 1)) << top);
+                    asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(v) : "s"(keep), "v"(spx), "v"(emx >> (24 - SYM)));
+                    if (store) bst_value<DT>(rout, out_lane + t * 32 * EB, v);
+                }
+                return kGroups ? emx : v;
             } else if (DT == 2) {
                 // sign (bit 23 of sm) to bit 31, mantissa bits 0-22, exponent to bits 23-30
                 if (store) {
@@ -2270,7 +2278,7 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
                     __builtin_amdgcn_raw_buffer_store_b64(
                         u32x2{__builtin_amdgcn_perm(hi, lo, 0x05010400u), __builtin_amdgcn_perm(hi, lo, 0x07030602u)},
                         rout, (int)(outg + t0 * 32 * EB), 0, 0);
-                } else {
+                } else if constexpr (DT == 2) {
                     // value k's raw field is bytes 3k .. 3k + 2 of the 12; one v_perm
                     // takes them with the top one twice (the sign lands in bit 31),
                     // and one v_bfi puts exponent byte k into bits 23-30
@@ -2280,6 +2288,23 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
                     asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(v2) : "s"(0x807FFFFFu), "v"(__builtin_amdgcn_perm(S4.z, S4.y, 0x04040302u)), "v"(X << 7));
                     asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(v3) : "s"(0x807FFFFFu), "v"(__builtin_amdgcn_perm(S4.z, S4.z, 0x03030201u)), "v"(X >> 1));
                     __builtin_amdgcn_raw_buffer_store_b128(u32x4{v0, v1, v2, v3}, rout, (int)(outg + t0 * 32 * EB), 0, 0);
+                } else {
+                    // fp8: the four RB-bit fields spread to bytes, then per byte the
+                    // mantissa from the field, the exponent at bit SYM and the
+                    // field's top bit (the sign) to bit 7; one 32-bit store
+                    constexpr uint32_t SYM = Fmt<DT>::SYM;
+                    constexpr uint32_t mant4 = ((1u << (RB - 1)) - 1u) * 0x01010101u;
+                    const uint32_t F = S4 >> gsh;
+                    uint32_t Bf;
+                    if constexpr (RB == 4) {
+                        Bf = __builtin_amdgcn_perm((F >> 4) & 0x0F0Fu, F & 0x0F0Fu, 0x05010400u);
+                    } else {
+                        Bf = (F & 7u) | (((F >> 3) & 7u) << 8) | (((F >> 6) & 7u) << 16) | (((F >> 9) & 7u) << 24);
+                    }
+                    uint32_t V, W;
+                    asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(V) : "s"(mant4), "v"(Bf), "v"(X << SYM));
+                    asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(W) : "s"(0x80808080u), "v"(Bf << (8 - RB)), "v"(V));
+                    bst32(rout, outg + t0 * 32 * EB, W);
                 }
             };
             SmGroup G0 = G0first, G1 = G1first;
@@ -2293,13 +2318,12 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
                 group4(t + 12, N1);
             }
         } else {
-            // fp16, fp8: each lane's raw field by one dword load, eight steps
+            // fp16: each lane's raw field by one dword load, eight steps
             // ahead (step t's fields of a half are 4 RB bytes further than
-            // step t - 1's).  fp16 leaves two steps per dword store: each lane
-            // packs its two values, two ds_bpermute give lane j the pairs of
-            // lanes 2j' and 2j' + 1 (j' = j mod 16), and one v_perm keeps the
-            // first step's halves (j < 16) or the second's; fp8 stores its byte
-            // per step
+            // step t - 1's).  Two steps leave per dword store: each lane packs
+            // its two values, two ds_bpermute give lane j the pairs of lanes 2j'
+            // and 2j' + 1 (j' = j mod 16), and one v_perm keeps the first step's
+            // halves (j < 16) or the second's
             constexpr int kAhead = 8;
             const uint32_t lanebyte = lanebit >> 3, lanesh = lanebit & 7u;
             const uint32_t pk_src = ((2 * (lj & 15u)) + 32 * h) << 2;
