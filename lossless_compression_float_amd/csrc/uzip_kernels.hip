@@ -2033,13 +2033,12 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
         const uint32_t nesc_w = S ? max(uniform_u32(__shfl((int)nesc, 0, 64)), uniform_u32(__shfl((int)nesc, 32, 64))) : 0u;
         const uint32_t Tmain = S && nesc_w > 256 ? 0u : min(min(F0, F1), Tw) & ~7u;
         const uint32_t Tmain16 = Tmain & ~15u;  // bf16 main loop: 16 steps per iteration
-        // bf16, fp32 and fp8: the main loop takes four steps at a time, and
-        // lane j the raw fields of positions 4j .. 4j + 3 of a group (4 R bytes,
-        // or 4 RB bits starting at bit gsh of byte gbyte; see the main loop);
-        // groups 0 and 1 are loaded here, before the word window, so that many
-        // memory operations lie between these loads and their first use
-        constexpr bool kGroups = DT != 3;
-        using SmGroup = std::conditional_t<DT == 2, u32x3, uint32_t>;
+        // The main loop takes four steps at a time, and lane j the raw fields of
+        // positions 4j .. 4j + 3 of a group (4 R bytes, or 4 RB bits starting at
+        // bit gsh of byte gbyte; see the main loop); groups 0 and 1 are loaded
+        // here, before the word window, so that many memory operations lie
+        // between these loads and their first use
+        using SmGroup = std::conditional_t<DT == 2, u32x3, std::conditional_t<DT == 3, u32x2, uint32_t>>;
         const uint32_t smg = ((h ? vals0 : 0u) + 4 * lj) * R;  // the lane's bytes of group 0
         const uint32_t gbit = ((h ? vals0 : 0u) + 4 * lj) * RB, gbyte = gbit >> 3, gsh = gbit & 7u;
         auto load_group = [&](uint32_t g) __attribute__((always_inline)) {
@@ -2047,10 +2046,11 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
                 return __builtin_amdgcn_raw_buffer_load_b96(rsm, (int)(smg + 128 * R * g), 0, 0);
             } else if constexpr (DT == 1) {
                 return bld32(rsm, smg + 128 * R * g);
-            } else if constexpr (kGroups) {
-                return bld32(rsm, gbyte + 16 * RB * g);  // (a group's fields: 128 RB bits)
+            } else if constexpr (DT == 3) {
+                // 44 bits from bit gsh (0 or 4) of an unaligned byte: two dwords
+                return u32x2{bld32(rsm, gbyte + 16 * RB * g), bld32(rsm, gbyte + 16 * RB * g + 4)};
             } else {
-                return 0u;
+                return bld32(rsm, gbyte + 16 * RB * g);  // (a group's fields: 128 RB bits)
             }
         };
         const SmGroup G0first = load_group(0), G1first = load_group(1);
@@ -2143,9 +2143,8 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
         // g = 4096 - f, the decode step f * (x >> 12) + (x & 4095) - c0 is
         // x - (g * (x >> 12) + c0).
         // sp: the value's sign+mantissa, for bf16 as the byte in bytes 0 and 1.
-        // bf16, fp32 and fp8 return the entry (escapes in place) and store
-        // nothing unless `store` (their main loop builds and stores four steps'
-        // values at once); fp16 returns the value.
+        // Returns the entry (escapes in place) and stores nothing unless
+        // `store` (the main loop builds and stores four steps' values at once).
         auto step = [&](uint32_t t, uint64_t act, bool tail, uint32_t sp, int par, bool store) __attribute__((always_inline)) {
             uint32_t slot_addr;  // (x & 4095) | this half's row: the index in s_sym / s_slot
             asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(slot_addr) : "v"(x), "s"(kTableSize - 1), "v"(hsym));
@@ -2215,17 +2214,16 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
             } else if constexpr (DT != 2) {
                 // fp16, fp8: sign (the raw field's top bit, copied to the value's
                 // top bit) and mantissa from sp, the exponent (emx bits 24-31) to
-                // bit SYM; the store keeps the value's EB bytes.  fp8 returns the
-                // entry, as bf16 and fp32 do; fp16 returns the value
+                // bit SYM; the store keeps the value's EB bytes
                 constexpr uint32_t SYM = Fmt<DT>::SYM, top = 8 * EB - 1;
                 constexpr uint32_t keep = (1u << top) | ((1u << (RB - 1)) - 1u);
-                uint32_t v = 0;
-                if (!kGroups || store) {
+                if (store) {
                     const uint32_t spx = sp | ((sp >> (RB - 1)) << top);
+                    uint32_t v;
                     asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(v) : "s"(keep), "v"(spx), "v"(emx >> (24 - SYM)));
-                    if (store) bst_value<DT>(rout, out_lane + t * 32 * EB, v);
+                    bst_value<DT>(rout, out_lane + t * 32 * EB, v);
                 }
-                return kGroups ? emx : v;
+                return emx;
             } else if (DT == 2) {
                 // sign (bit 23 of sm) to bit 31, mantissa bits 0-22, exponent to bits 23-30
                 if (store) {
@@ -2237,12 +2235,13 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
             return 0u;
         };
         uint32_t t = 0;
-        if constexpr (kGroups) {
-            // bf16 and fp32, four steps at a time.  A group of four steps holds
-            // 128 values of each half; lane j takes positions 4j .. 4j + 3 of
-            // them, that is step j >> 3 of lanes 4 (j & 7) .. 4 (j & 7) + 3:
-            // their raw bytes (one 32-bit load for bf16, one 96-bit load for
-            // fp32, two groups ahead) and their one 64-bit or 128-bit store.
+        {
+            // Four steps at a time.  A group of four steps holds 128 values of
+            // each half; lane j takes positions 4j .. 4j + 3 of them, that is
+            // step j >> 3 of lanes 4 (j & 7) .. 4 (j & 7) + 3: their raw fields
+            // (one 32-bit load for bf16 and fp8, 96 bits for fp32, two unaligned
+            // dwords for fp16; two groups ahead) and their one store of 4 EB
+            // bytes.
             // Their exponents reach it in three moves: each lane packs its four
             // steps' symbols into the bytes of one dword (entry byte 3 of each
             // step, by v_perm); each quad of lanes transposes its 4 x 4 bytes
@@ -2288,6 +2287,24 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
                     asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(v2) : "s"(0x807FFFFFu), "v"(__builtin_amdgcn_perm(S4.z, S4.y, 0x04040302u)), "v"(X << 7));
                     asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(v3) : "s"(0x807FFFFFu), "v"(__builtin_amdgcn_perm(S4.z, S4.z, 0x03030201u)), "v"(X >> 1));
                     __builtin_amdgcn_raw_buffer_store_b128(u32x4{v0, v1, v2, v3}, rout, (int)(outg + t0 * 32 * EB), 0, 0);
+                } else if constexpr (DT == 3) {
+                    // fp16: two fields a dword (f0 in bits 0-10, f1 in 16-26), then
+                    // the mantissas kept, the exponent bytes of X moved to bits 10-14
+                    // and 26-30, and the fields' top bits (the signs) to bits 15, 31
+                    const uint32_t a01 = __builtin_amdgcn_alignbit(S4.y, S4.x, gsh);
+                    const uint32_t a23 = __builtin_amdgcn_alignbit(S4.y, S4.x, gsh + 22);
+                    uint32_t w[2];
+#pragma unroll
+                    for (int k = 0; k < 2; ++k) {
+                        const uint32_t a = k ? a23 : a01;
+                        uint32_t F, P, Wk;
+                        asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(F) : "s"(0x7FFu), "v"(a), "v"(a << 5));
+                        const uint32_t E = __builtin_amdgcn_perm(0u, X, k ? 0x030C020Cu : 0x010C000Cu) << 2;
+                        asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(P) : "s"(0x03FF03FFu), "v"(F), "v"(E));
+                        asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(Wk) : "s"(0x80008000u), "v"(F << 5), "v"(P));
+                        w[k] = Wk;
+                    }
+                    __builtin_amdgcn_raw_buffer_store_b64(u32x2{w[0], w[1]}, rout, (int)(outg + t0 * 32 * EB), 0, 0);
                 } else {
                     // fp8: the four RB-bit fields spread to bytes, then per byte the
                     // mantissa from the field, the exponent at bit SYM and the
@@ -2316,38 +2333,6 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
                 G1 = load_group(t / 4 + 5);
                 group4(t + 8, N0);
                 group4(t + 12, N1);
-            }
-        } else {
-            // fp16: each lane's raw field by one dword load, eight steps
-            // ahead (step t's fields of a half are 4 RB bytes further than
-            // step t - 1's).  Two steps leave per dword store: each lane packs
-            // its two values, two ds_bpermute give lane j the pairs of lanes 2j'
-            // and 2j' + 1 (j' = j mod 16), and one v_perm keeps the first step's
-            // halves (j < 16) or the second's
-            constexpr int kAhead = 8;
-            const uint32_t lanebyte = lanebit >> 3, lanesh = lanebit & 7u;
-            const uint32_t pk_src = ((2 * (lj & 15u)) + 32 * h) << 2;
-            const uint32_t pk_sel = lj < 16 ? 0x05040100u : 0x07060302u;
-            const uint32_t out_pair = rans_run ? (h ? vals0 : 0u) * EB + 4 * lj : kOutOfRange;
-            uint32_t rq[kAhead];
-#pragma unroll
-            for (int u = 0; u < kAhead; ++u) rq[u] = bld32(rsm, lanebyte + u * 4 * RB);
-            for (; t < Tmain; t += kAhead) {
-                uint32_t vprev = 0;
-#pragma unroll
-                for (int u = 0; u < kAhead; ++u) {
-                    const uint32_t sp = (rq[u] >> lanesh) & ((1u << RB) - 1u);
-                    rq[u] = bld32(rsm, lanebyte + (t + u + kAhead) * 4 * RB);
-                    const uint32_t v = step(t + u, runm, false, sp, u & 3, EB != 2);
-                    if (EB == 2 && (u & 1)) {
-                        const uint32_t q = __builtin_amdgcn_perm(v, vprev, 0x05040100u);
-                        const uint32_t qa = (uint32_t)__builtin_amdgcn_ds_bpermute((int)pk_src, (int)q);
-                        const uint32_t qb = (uint32_t)__builtin_amdgcn_ds_bpermute((int)(pk_src + 4), (int)q);
-                        bst32(rout, out_pair + (t + u - 1) * 64, __builtin_amdgcn_perm(qb, qa, pk_sel));
-                    } else {
-                        vprev = v;
-                    }
-                }
             }
         }
         // tail: the last steps of the shorter chunk and the ragged end, value by value
