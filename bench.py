@@ -51,12 +51,12 @@ VALUE_DTYPE = {1: "bf16", 2: "fp32", 3: "fp16", 4: "fp8_e4m3fn", 5: "fp8_e5m2"}
 # plain device copy of the workload's size); the kernel source they were taken
 # on is identified by its digest, and a figure is reported only while the
 # source is unchanged.
-MEASURED_TRAFFIC_SOURCE = "66d8b8472a40"
+MEASURED_TRAFFIC_SOURCE = "4bc68f7ac962"
 MEASURED_TRAFFIC = {
-    ("llama8b", "k_encode"): 42802712321, ("llama8b", "k_decode"): 26852914156,
-    ("llama8b:sampled", "k_encode"): 28818461550, ("llama8b:sampled", "k_decode"): 26885321688,
-    ("grad_bucket", "k_encode"): 1435831496, ("grad_bucket", "k_decode"): 896992410,
-    ("grad_bucket:sampled", "k_encode"): 963680383, ("grad_bucket:sampled", "k_decode"): 897805749,
+    ("llama8b", "k_encode"): 42803914419, ("llama8b", "k_decode"): 26855900471,
+    ("llama8b:sampled", "k_encode"): 28819412998, ("llama8b:sampled", "k_decode"): 26884679592,
+    ("grad_bucket", "k_encode"): 1435833071, ("grad_bucket", "k_decode"): 896966805,
+    ("grad_bucket:sampled", "k_encode"): 963674369, ("grad_bucket:sampled", "k_decode"): 897808153,
 }
 
 
