@@ -730,8 +730,11 @@ __global__ __launch_bounds__(64) void k_encode(EncParams p) {
     // without conflicts) and stores nothing: its sign+mantissa offsets lie
     // past the pair's output range.
     {
-        // (a multiple of 4 iterations, so that no step of the loop is conditional)
-        const uint32_t fullmin = min(vals0 / VPI, nch == 2 ? vals1 / VPI : 0xFFFFFFFFu) & ~3u;
+        // Sets of kSet vectors, software-pipelined (below): four, or eight for
+        // fp32, whose few waves need more loads in flight each
+        constexpr uint32_t kSet = DT == 2 ? 8u : 4u;
+        // (a multiple of kSet iterations, so that no step of the loop is conditional)
+        const uint32_t fullmin = min(vals0 / VPI, nch == 2 ? vals1 / VPI : 0xFFFFFFFFu) & ~(kSet - 1u);
         uint32_t *hm = valid ? hist : hist + 256 + lj / kSubHist;
         const rsrc_t rsmo = make_rsrc(d.out + d.sm_off + c0 * ce * R, pair_vals * R);
         const uint32_t smo = (h ? vals0 : 0u) * R + lj * VPL * R;  // this lane's first sign+mantissa byte
@@ -759,30 +762,39 @@ __global__ __launch_bounds__(64) void k_encode(EncParams p) {
                     0, 0);
             }
         };
-        // Sets of four vectors (iterations 4s .. 4s + 3), software-pipelined:
-        // the next set is loaded while a set is split.  As in the coding pass,
-        // the loads are issued in asm and waited for explicitly, so that the
-        // wait does not also cover the raw-byte stores: between a set's loads
-        // and its wait lies only the straight-line split of the set before,
-        // with exactly one store per vector.
-        constexpr uint32_t kSetStores = 4;
-        auto asm_load_set = [&](uint32_t st, u32x4(&V)[4]) __attribute__((always_inline)) {
+        // Sets of kSet vectors (iterations kSet s .. kSet s + kSet - 1),
+        // software-pipelined: the next set is loaded while a set is split.  As
+        // in the coding pass, the loads are issued in asm and waited for
+        // explicitly, so that the wait does not also cover the raw-byte stores:
+        // between a set's loads and its wait lies only the straight-line split
+        // of the set before, with exactly one store per vector.
+        constexpr uint32_t kSetStores = kSet;
+        auto asm_load_set = [&](uint32_t st, u32x4(&V)[kSet]) __attribute__((always_inline)) {
 #pragma unroll
-            for (uint32_t k = 0; k < 4; ++k) {
-                const uint32_t it = 4 * st + k;
+            for (uint32_t k = 0; k < kSet; ++k) {
+                const uint32_t it = kSet * st + k;
                 const uint32_t o = it < fullmin ? in0 + (it * VPI + lj * VPL) * EB : kOutOfRange;
                 asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen" : "=v"(V[k]) : "v"(o), "s"(rin));
             }
         };
-        auto split_set = [&](uint32_t st, const u32x4(&V)[4]) __attribute__((always_inline)) {
+        auto split_set = [&](uint32_t st, const u32x4(&V)[kSet]) __attribute__((always_inline)) {
 #pragma unroll
-            for (uint32_t k = 0; k < 4; ++k) split(make_uint4(V[k].x, V[k].y, V[k].z, V[k].w), 4 * st + k);
+            for (uint32_t k = 0; k < kSet; ++k) split(make_uint4(V[k].x, V[k].y, V[k].z, V[k].w), kSet * st + k);
         };
-#define UZIP_WAIT_SET(N, V) \
-    asm volatile("s_waitcnt vmcnt(%4)" : "+v"(V[0]), "+v"(V[1]), "+v"(V[2]), "+v"(V[3]) : "i"(N))
-        const uint32_t nsets = fullmin / 4;
+        // (the wait names every register of the set, so that none is read before it)
+#define UZIP_WAIT_SET(N, V)                                                                                        \
+    do {                                                                                                           \
+        if constexpr (kSet == 8)                                                                                   \
+            asm volatile("s_waitcnt vmcnt(%8)"                                                                     \
+                         : "+v"(V[0]), "+v"(V[1]), "+v"(V[2]), "+v"(V[3]), "+v"(V[4 % kSet]), "+v"(V[5 % kSet]), \
+                           "+v"(V[6 % kSet]), "+v"(V[7 % kSet])                                                    \
+                         : "i"(N));                                                                                \
+        else                                                                                                       \
+            asm volatile("s_waitcnt vmcnt(%4)" : "+v"(V[0]), "+v"(V[1]), "+v"(V[2]), "+v"(V[3]) : "i"(N));       \
+    } while (0)
+        const uint32_t nsets = fullmin / kSet;
         if (nsets > 0) {
-            u32x4 A[4], B[4];
+            u32x4 A[kSet], B[kSet];
             asm_vmem_fence();
             asm_load_set(0, A);
             UZIP_WAIT_SET(0, A);
