@@ -51,12 +51,12 @@ VALUE_DTYPE = {1: "bf16", 2: "fp32", 3: "fp16", 4: "fp8_e4m3fn", 5: "fp8_e5m2"}
 # plain device copy of the workload's size); the kernel source they were taken
 # on is identified by its digest, and a figure is reported only while the
 # source is unchanged.
-MEASURED_TRAFFIC_SOURCE = "4bc68f7ac962"
+MEASURED_TRAFFIC_SOURCE = "4394e6d7e284"
 MEASURED_TRAFFIC = {
-    ("llama8b", "k_encode"): 42803914419, ("llama8b", "k_decode"): 26855900471,
-    ("llama8b:sampled", "k_encode"): 28819412998, ("llama8b:sampled", "k_decode"): 26884679592,
-    ("grad_bucket", "k_encode"): 1435833071, ("grad_bucket", "k_decode"): 896966805,
-    ("grad_bucket:sampled", "k_encode"): 963674369, ("grad_bucket:sampled", "k_decode"): 897808153,
+    ("llama8b", "k_encode"): 42804218490, ("llama8b", "k_decode"): 26856009969,
+    ("llama8b:sampled", "k_encode"): 28819004878, ("llama8b:sampled", "k_decode"): 26884679722,
+    ("grad_bucket", "k_encode"): 1435828937, ("grad_bucket", "k_decode"): 896977978,
+    ("grad_bucket:sampled", "k_encode"): 963634835, ("grad_bucket:sampled", "k_decode"): 897756828,
 }
 
 
