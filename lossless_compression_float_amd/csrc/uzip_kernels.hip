@@ -1053,7 +1053,10 @@ __global__ __launch_bounds__(64) void k_encode(EncParams p) {
         asm("v_and_b32 %0, %1, %2" : "=v"(hb) : "s"(e1 - e0), "v"(hsel));
         const uint32_t kk = __builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, e0 + hb));
         bst16(rslot, vsel(m, kOutOfRange, kk << 1), x);
-        const uint32_t xs = vsel(m, x, x >> 16);
+        // (the state's select reads the compare's own result, not the masked
+        // copy: lanes outside act keep their state below, and a stopped half's
+        // state is never used)
+        const uint32_t xs = (te.x & 0xFFFFu) < (x >> 16) ? x >> 16 : x;
         const uint32_t qd = enc_quotient(xs, __hiloint2double((int)te.w, (int)te.z));
         const uint32_t xe = __umul24(qd, te.x >> 16) + (xs + te.y);  // = q * M + (xs - q * f) + c0
         // Lanes past a ragged chunk end keep their state.  Outside CAREFUL
@@ -2165,11 +2168,17 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
             const uint64_t escm = S ? lanes_eq(slot_addr, escaddr) & act : 0ull;
             const uint32_t em = kDirect ? s_slotf[slot_addr] : s_rkf[s_symf[slot_addr] | hrk];
             const uint32_t xd = x - (__umul24(em & 0xFFFu, x >> kProbBits) + ((em >> 12) & 0xFFFu));
-            // (the and with act also puts the mask in registers written by the
-            // scalar unit: inline asm below reads it, and the hardware needs
-            // spacing between a vector compare writing scalar registers and a
-            // vector read of them, which the compiler cannot see through asm)
-            const uint64_t m = lanes_lt(xd, kStateLow) & act;
+            // The lanes that take a word.  In the main loop every lane of a
+            // running half is active and the lanes of a half that is not running
+            // never reach the output or the checks, so the compare's own mask
+            // serves, with no scalar instruction on the state's dependent path;
+            // only compiler-placed instructions read it there, since the hardware
+            // needs spacing between a vector compare writing scalar registers and
+            // a vector read of them, which the compiler cannot see through inline
+            // asm.  Tail steps mask it with act on the scalar unit, and the asm
+            // selects below may read that copy.
+            const bool need = xd < kStateLow;
+            const uint64_t m = tail ? lanes_lt(xd, kStateLow) & act : __builtin_amdgcn_ballot_w64(need);
             const uint32_t lo = (uint32_t)m, hi = (uint32_t)(m >> 32);
             // the lane's word: stream position offv + rank inside the half (one mbcnt per half)
             const uint32_t kk = vsel(kHighHalf, __builtin_amdgcn_mbcnt_lo(lo, offv), __builtin_amdgcn_mbcnt_hi(hi, offv));
@@ -2179,14 +2188,11 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
             // 0-1 of xd; lanes without a word keep xd (bytes 4-7)
             uint32_t selw;
             asm("v_mad_u32_u24 %0, %1, %2, %3" : "=v"(selw) : "v"(kk & 1u), "s"(0x0202u), "v"(selbase));
-            const uint32_t xn = __builtin_amdgcn_perm(xd, wv, vsel(m, selkeep, selw));
+            const uint32_t xn = __builtin_amdgcn_perm(xd, wv, tail ? vsel(m, selkeep, selw) : (need ? selw : selkeep));
             x = tail ? vsel(act, x, xn) : xn;
             // bookkeeping in vector registers: the half's consumed count, then
-            // the lanes whose block is used up take the pairs loaded two steps ago
-            uint32_t olo, ohi;
-            asm("v_bcnt_u32_b32 %0, %1, %2" : "=v"(olo) : "s"(lo), "v"(offv));
-            asm("v_bcnt_u32_b32 %0, %1, %2" : "=v"(ohi) : "s"(hi), "v"(offv));
-            offv = vsel(kHighHalf, olo, ohi);
+            // the lanes whose block is used up take the pairs loaded four steps ago
+            offv = vsel(kHighHalf, offv + __builtin_popcount(lo), offv + __builtin_popcount(hi));
             // (plain selects: the mask comes from a vector compare, and the
             // compiler spaces its reads as the hardware requires)
             const bool used_up = offv >= lim;
