@@ -2095,6 +2095,7 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
         const uint32_t hsym = h << kProbBits, hrk = h << 8;  // this half's table rows
         const uint32_t selbase = 0x05040100u, selkeep = 0x07060504u;
         uint32_t offv = 0;  // words consumed by this half
+        const uint32_t lstate = rans_run ? kStateLow : 0u;  // main-loop renormalisation bound (0: no words)
         const uint8_t *s_symf = &s_sym[0][0];
         const uint32_t *s_rkf = &s_rk[0][0];
         const uint32_t *s_slotf = &s_slot[0][0];
@@ -2169,15 +2170,15 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
             const uint32_t em = kDirect ? s_slotf[slot_addr] : s_rkf[s_symf[slot_addr] | hrk];
             const uint32_t xd = x - (__umul24(em & 0xFFFu, x >> kProbBits) + ((em >> 12) & 0xFFFu));
             // The lanes that take a word.  In the main loop every lane of a
-            // running half is active and the lanes of a half that is not running
-            // never reach the output or the checks, so the compare's own mask
-            // serves, with no scalar instruction on the state's dependent path;
-            // only compiler-placed instructions read it there, since the hardware
+            // running half is active, and a half that is not running compares
+            // against 0 (lstate) and takes none, so the compare's own mask serves,
+            // with no scalar instruction on the state's dependent path; only
+            // compiler-placed instructions read it there, since the hardware
             // needs spacing between a vector compare writing scalar registers and
             // a vector read of them, which the compiler cannot see through inline
             // asm.  Tail steps mask it with act on the scalar unit, and the asm
             // selects below may read that copy.
-            const bool need = xd < kStateLow;
+            const bool need = xd < lstate;
             const uint64_t m = tail ? lanes_lt(xd, kStateLow) & act : __builtin_amdgcn_ballot_w64(need);
             const uint32_t lo = (uint32_t)m, hi = (uint32_t)(m >> 32);
             // the lane's word: stream position offv + rank inside the half (one mbcnt per half)
