@@ -1043,16 +1043,9 @@ __global__ __launch_bounds__(64) void k_encode(EncParams p) {
             clo = __builtin_popcount(lo);
             chi = __builtin_popcount(hi);
         }
-        // word index: end of the slot's words - (words so far + this step's) + rank in the half
-        // (r0, r1: word index just past the words still to come)
-        const uint32_t e0 = r0 - clo;
-        r1 -= chi;
-        const uint32_t e1 = r1 - clo;
-        r0 = e0;
-        uint32_t hb;  // e1 - e0 in the upper half, 0 in the lower
-        asm("v_and_b32 %0, %1, %2" : "=v"(hb) : "s"(e1 - e0), "v"(hsel));
-        const uint32_t kk = __builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, e0 + hb));
-        bst16(rslot, vsel(m, kOutOfRange, kk << 1), x);
+        // The state's chain first (select, quotient, new state), the word's
+        // place and store after it, so that the next step's chain may overlap them.
+        const uint32_t xold = x;
         // (the state's select reads the compare's own result, not the masked
         // copy: lanes outside act keep their state below, and a stopped half's
         // state is never used)
@@ -1063,6 +1056,16 @@ __global__ __launch_bounds__(64) void k_encode(EncParams p) {
         // steps every lane of a live half codes a value, and a stopped
         // half's state is never used (its chunk is stored RAW).
         x = careful ? vsel(act, x, xe) : xe;
+        // word index: end of the slot's words - (words so far + this step's) + rank in the half
+        // (r0, r1: word index just past the words still to come)
+        const uint32_t e0 = r0 - clo;
+        r1 -= chi;
+        const uint32_t e1 = r1 - clo;
+        r0 = e0;
+        uint32_t hb;  // e1 - e0 in the upper half, 0 in the lower
+        asm("v_and_b32 %0, %1, %2" : "=v"(hb) : "s"(e1 - e0), "v"(hsel));
+        const uint32_t kk = __builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, e0 + hb));
+        bst16(rslot, vsel(m, kOutOfRange, kk << 1), xold);
         if (S && careful) {  // (FAST blocks store their sign+mantissa bytes when the block is staged)
             if (R == 1) bst8(rsm2, smo2 + t * 32 * R, raw_of<DT>(v));
             if (R == 3) {
@@ -2095,6 +2098,9 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
         const uint32_t hsym = h << kProbBits, hrk = h << 8;  // this half's table rows
         const uint32_t selbase = 0x05040100u, selkeep = 0x07060504u;
         uint32_t offv = 0;  // words consumed by this half
+        // the current state's slot index and its first table read (the direct
+        // entry, or the rank), carried from step to step
+        uint32_t slot_c, first_c;
         const uint32_t lstate = rans_run ? kStateLow : 0u;  // main-loop renormalisation bound (0: no words)
         const uint8_t *s_symf = &s_sym[0][0];
         const uint32_t *s_rkf = &s_rk[0][0];
@@ -2162,12 +2168,13 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
         // Returns the entry (escapes in place) and stores nothing unless
         // `store` (the main loop builds and stores four steps' values at once).
         auto step = [&](uint32_t t, uint64_t act, bool tail, uint32_t sp, int par, bool store) __attribute__((always_inline)) {
-            uint32_t slot_addr;  // (x & 4095) | this half's row: the index in s_sym / s_slot
-            asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(slot_addr) : "v"(x), "s"(kTableSize - 1), "v"(hsym));
+            // (x & 4095) | this half's row, and its first table read (the direct
+            // entry, or the rank), both issued at the end of the step before
+            const uint32_t slot_addr = slot_c;
             // (sampled tables: the lanes at the escape slot; their exponent is
             // patched into the entry in a rare branch)
             const uint64_t escm = S ? lanes_eq(slot_addr, escaddr) & act : 0ull;
-            const uint32_t em = kDirect ? s_slotf[slot_addr] : s_rkf[s_symf[slot_addr] | hrk];
+            const uint32_t em = kDirect ? first_c : s_rkf[first_c | hrk];
             const uint32_t xd = x - (__umul24(em & 0xFFFu, x >> kProbBits) + ((em >> 12) & 0xFFFu));
             // The lanes that take a word.  In the main loop every lane of a
             // running half is active, and a half that is not running compares
@@ -2185,18 +2192,34 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
             const uint32_t kk = vsel(kHighHalf, __builtin_amdgcn_mbcnt_lo(lo, offv), __builtin_amdgcn_mbcnt_hi(hi, offv));
             // lane (kk >> 1) mod 32 of this half
             const uint32_t wv = (uint32_t)__builtin_amdgcn_ds_bpermute((int)(((kk << 1) & 124u) | lanebits), (int)P);
-            // x' = (xd << 16) | word: bytes 0-1 (kk even) or 2-3 of wv below bytes
-            // 0-1 of xd; lanes without a word keep xd (bytes 4-7)
-            uint32_t selw;
-            asm("v_mad_u32_u24 %0, %1, %2, %3" : "=v"(selw) : "v"(kk & 1u), "s"(0x0202u), "v"(selbase));
-            const uint32_t xn = __builtin_amdgcn_perm(xd, wv, tail ? vsel(m, selkeep, selw) : (need ? selw : selkeep));
-            x = tail ? vsel(act, x, xn) : xn;
-            // bookkeeping in vector registers: the half's consumed count, then
-            // the lanes whose block is used up take the pairs loaded four steps ago
+            __builtin_amdgcn_sched_barrier(0);  // (the permute issues before the bookkeeping below)
+            // bookkeeping in vector registers, split around the state's update so
+            // that the next step's table read follows that update at once: here,
+            // in the permute's shadow, the half's consumed count; after the read,
+            // the lanes whose block is used up take the pairs loaded four steps
+            // ago (the permute above has read P)
             offv = vsel(kHighHalf, offv + __builtin_popcount(lo), offv + __builtin_popcount(hi));
             // (plain selects: the mask comes from a vector compare, and the
             // compiler spaces its reads as the hardware requires)
             const bool used_up = offv >= lim;
+            // x' = (xd << 16) | word: bytes 0-1 (kk even) or 2-3 of wv below bytes
+            // 0-1 of xd; lanes without a word keep xd (bytes 4-7)
+            uint32_t selw;
+            asm("v_mad_u32_u24 %0, %1, %2, %3" : "=v"(selw) : "v"(kk & 1u), "s"(0x0202u), "v"(selbase));
+            const uint32_t sel = tail ? vsel(m, selkeep, selw) : (need ? selw : selkeep);
+            // The state's update, the next slot and its first table read issue
+            // back to back: the scheduling barriers keep everything above (the
+            // consumed count and the word select, in the permute's shadow) before
+            // them and everything below (the refill, the step's value, the
+            // group's packing) after them, in the read's shadow.  With one or two
+            // waves per SIMD (fp32, fp8) nothing else fills those shadows.
+            __builtin_amdgcn_sched_barrier(0);
+            const uint32_t xn = __builtin_amdgcn_perm(xd, wv, sel);
+            x = tail ? vsel(act, x, xn) : xn;
+            asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(slot_c) : "v"(x), "s"(kTableSize - 1), "v"(hsym));
+            first_c = kDirect ? s_slotf[slot_c] : (uint32_t)s_symf[slot_c];
+            __builtin_amdgcn_sched_barrier(0);
+            // the refill, in the read's shadow (the next step's permute reads P)
             if (kScalarStale) {
                 const uint64_t um = __builtin_amdgcn_ballot_w64(used_up);
                 const uint64_t stale = um & (R2 | R3);
@@ -2253,6 +2276,8 @@ __global__ __launch_bounds__(64) void k_decode(DecodeParams p) {
             }
             return 0u;
         };
+        asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(slot_c) : "v"(x), "s"(kTableSize - 1), "v"(hsym));
+        first_c = kDirect ? s_slotf[slot_c] : (uint32_t)s_symf[slot_c];
         uint32_t t = 0;
         {
             // Four steps at a time.  A group of four steps holds 128 values of
