@@ -708,7 +708,7 @@ def test_entropy_bound_closed_forms():
     assert orc.entropy_bound(orc.BF16, tail) == pytest.approx(ce + 64 + 64 * 2 / 8, abs=1e-6)
 
 
-def test_entropy_bound_pr1_matches_the_survey_figure():
+def test_entropy_bound_pr1_matches_the_independent_numpy_figure():
     """PR1 (1,048,576 bf16 values N(0, 0.02^2), seed 0): 0.6590 of the input,
     the figure computed independently with numpy when the workloads were
     specified."""
